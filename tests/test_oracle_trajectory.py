@@ -1,0 +1,89 @@
+"""Whole-trajectory invariants of the oracle on the tiny workload and on
+reduced-size versions of the bf16 workloads (CPU only, seconds)."""
+import numpy as np
+import pytest
+
+import oracle
+import synth
+from oracle.trajectory import run_unit, workload_cap
+
+
+def _check_traj(w, recs, n_steps):
+    cap = workload_cap(w)
+    prev_sb = None
+    for r in recs:
+        t = r["t"]
+        c = w.k_blocks if t == 0 else cap
+        sel = [i for i in r["ids"] if i >= 0]
+        assert len(sel) == min(w.k_blocks, (r["T"] + w.block_size - 1) // w.block_size)
+        assert len(r["fetch_block"]) <= c
+        held = [b for b in r["slot_block"] if b >= 0]
+        assert len(held) == len(set(held)) and len(held) <= w.n_slots
+        assert sorted(r["att_block"]) == sorted(b for b in sel if b in held)
+        assert np.all(r["last_used"][r["att_slot"]] == t)
+        if prev_sb is not None:
+            ev = set(r.get("evicted", []))
+            prev_held = {b for b in prev_sb if b >= 0} - ev
+            for b in sel:                                    # a held selected block stays
+                if b in prev_held:
+                    assert b in held
+        prev_sb = r["slot_block"]
+    assert recs[-1]["t"] == n_steps
+
+
+@pytest.mark.parametrize("h", [0, 1])
+def test_tiny_trajectory_invariants(h):
+    w = synth.TINY
+    recs = run_unit(w, 0, h, w.steps)
+    _check_traj(w, recs, w.steps)
+    # the first step appends token 1024, which opens block 64 with one token
+    assert recs[0]["T"] == 1025
+    assert len(recs) == w.steps
+
+
+def test_admission_fills_the_pool_with_the_first_selection():
+    w = synth.QWEN3_8B.with_(batch=2, prefix_tokens=16 * 300 + 5, budget_tokens=16 * 32)
+    recs = run_unit(w, 1, 3, 3)
+    r0 = recs[0]
+    assert r0["t"] == 0 and r0["T"] == w.prefix_tokens
+    assert list(r0["slot_block"]) == list(r0["ids"])      # free slots in ascending order
+    assert np.all(r0["last_used"] == 0)
+    assert list(r0["att_block"]) == list(r0["ids"])
+    _check_traj(w, recs, 3)
+
+
+def test_forced_evictions_leave_holes_that_are_refilled():
+    w = synth.QWEN3_32B.with_(batch=1, prefix_tokens=16 * 200, budget_tokens=16 * 20)
+    recs = run_unit(w, 0, 5, 6)
+    _check_traj(w, recs, 6)
+    for i in range(1, len(recs)):
+        n_prev = len(recs[i - 1]["att_block"])
+        assert len(recs[i]["evicted"]) == int(np.floor(0.1 * n_prev + 1e-9)) > 0
+
+
+def test_fetch_all_equals_dense_attention_when_budget_covers_context():
+    """Budget >= context and an uncapped fetch: every block is attended, so the
+    sparse output is dense attention over the whole context."""
+    w = synth.TINY.with_(prefix_tokens=16 * 6 + 3, budget_tokens=16 * 8, slots=8, cap=8,
+                         initial_resident_frac=0.0)
+    unit = None
+    recs = run_unit(w, 0, 1, 4, cap=8, unit=unit)
+    keys, vals = synth.unit_kv(w, 0, 1, w.prefix_tokens + 4)
+    q = oracle.to_f64(synth.queries(w), w.dtype)[0, 2:4]
+    for r in recs:
+        dense = oracle.dense_attention(q, keys, vals, w.dtype, r["T"])
+        assert np.max(np.abs(r["out"] - dense)) < 1e-12
+
+
+def test_drafts_redrawn_query_fixed():
+    w = synth.QWEN3_8B.with_(batch=1)
+    d1, d2 = synth.drafts(w, 1), synth.drafts(w, 2)
+    assert not np.array_equal(d1, d2)
+    assert np.array_equal(synth.queries(w), synth.queries(w))
+
+
+def test_unit_kv_prefix_property():
+    w = synth.LLAMA31_8B_LONG.with_(batch=1)
+    a = synth.unit_kv(w, 0, 2, 1000)
+    b = synth.unit_kv(w, 0, 2, 1200)
+    assert np.array_equal(a[0], b[0][:1000]) and np.array_equal(a[1], b[1][:1000])
