@@ -1,0 +1,243 @@
+/*
+ * liboasis -- OasisKV per-layer decode hot path on MI355X (gfx950).
+ *
+ * The full KV cache of a layer lives in pinned host memory; HBM holds, per
+ * (batch row, KV head): a min/max key summary of every KV block and a bounded
+ * pool of block slots (the sparse KV working set).  One decode step is
+ *
+ *   oasis_append_kv        write the new token (host KV, summary, resident slot)
+ *   oasis_predict          score every block against the current and draft
+ *                          queries, take the per-KV-head top-K
+ *   oasis_select_and_fetch diff the top-K against the resident slots, cap the
+ *                          fetch, pick LRU victims, gather the missing blocks
+ *                          from pinned host memory on a side stream
+ *   oasis_sparse_attn      GQA decode attention over the selected resident
+ *                          blocks
+ *
+ * Sources: the OasisKV explainer page ("OasisKV: Scaling In-Decode KV Cache
+ * Beyond HBM with Lookahead Sparse Prefetching"), Fig. 7 (CPU full KV, GPU
+ * min/max-pooled compressed keys, sparse KV working set; the draft query
+ * scans the compressed keys for the next top-K), Fig. 8 (predict -> select ->
+ * transfer per layer on streams), Fig. 9 (per-KV-head GPU block -> CPU block
+ * table), Table 2 (fetch cap by fetch ratio, LRU eviction), the explanatory
+ * diagram (diff against the GPU-resident blocks, cap the per-step transfer)
+ * and the capped-eviction glossary entry; the "KV cache offloading, week 2"
+ * study notes, section 2 (KV bytes per token) and section 3 (GQA,
+ * PagedAttention blocks).
+ *
+ * Conventions
+ *   - Every call returns an int status (OASIS_OK = 0, negative on error) and
+ *     never throws or aborts.  oasis_last_error() gives the message of the
+ *     last failing call on a handle.
+ *   - Calls that take a hipStream_t are asynchronous on that stream, like HIP
+ *     calls; pointers named *_dev are device memory owned by the caller,
+ *     16-byte aligned, contiguous, and must stay valid until the stream has
+ *     run the work.  Pointers named *_host are host memory read or written
+ *     before the call returns.
+ *   - Element type of K, V, queries and drafts is the layout's dtype
+ *     (OASIS_F32, or OASIS_BF16 as raw 16-bit patterns).  Scores and the
+ *     attention output are fp32.
+ *   - A handle is one layer.  It is not thread-safe.
+ *   - All sequences of the batch have the same length T; each append adds one
+ *     token to every sequence.
+ */
+#ifndef OASIS_H
+#define OASIS_H
+
+#include <stdint.h>
+#include <hip/hip_runtime_api.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+enum {
+    OASIS_OK = 0,
+    OASIS_E_INVAL = -1,     /* bad argument, shape or pointer */
+    OASIS_E_NOMEM = -2,     /* host or device allocation failed */
+    OASIS_E_HIP = -3,       /* a HIP runtime call failed (message in oasis_last_error) */
+    OASIS_E_CAPACITY = -4,  /* append past max_tokens */
+    OASIS_E_STATE = -5,     /* call out of order (select before predict, ...) */
+    OASIS_E_NONFINITE = -6, /* a NaN or infinite score reached the top-K */
+    OASIS_E_DEVICE = -7     /* a device-side invariant failed (see oasis_check) */
+};
+
+enum { OASIS_F32 = 0, OASIS_BF16 = 1 };
+
+typedef struct {
+    int32_t batch;          /* B */
+    int32_t num_q_heads;    /* Hq */
+    int32_t num_kv_heads;   /* Hkv; Hq % Hkv == 0, q head g uses KV head g / (Hq/Hkv) */
+    int32_t head_dim;       /* d; multiple of 8, at most 256 */
+    int32_t dtype;          /* OASIS_F32 or OASIS_BF16 */
+    int32_t max_drafts;     /* largest n_drafts passed to oasis_predict */
+    int32_t slots_per_head; /* HBM block slots per (b, KV head); 0 -> budget blocks; >= budget blocks */
+    int32_t reserved;
+    int64_t max_tokens;     /* capacity of the host KV per sequence */
+} oasis_layout;
+
+typedef struct oasis_handle oasis_t;
+
+/* Create a handle for one layer.  block_size: tokens per KV block (the
+ * paging unit, 1..64).  budget_tokens: the KV budget per (b, KV head); the
+ * top-K takes K = budget_tokens / block_size blocks.  fetch_ratio: default
+ * cap per (b, KV head) and step = max(1, floor(ratio * K)) (see
+ * oasis_cap_from_ratio), used when oasis_select_and_fetch gets cap < 0.
+ * Allocates the pinned host KV [B][Hkv][NBmax][K|V][block_size][d], the HBM
+ * summaries [B][Hkv][NBmax][max|min][d] and slot pool
+ * [B][Hkv][S][K|V][block_size][d], tables and work buffers, and one copy
+ * stream at default priority.  On success *out owns all of it. */
+int oasis_create(const oasis_layout *layout, int32_t block_size, int32_t budget_tokens,
+                 float fetch_ratio, oasis_t **out);
+
+/* Wait for all work of the handle, then free everything it owns. */
+int oasis_destroy(oasis_t *h);
+
+/* Load a prompt of len tokens per sequence (synchronous).  k_host, v_host:
+ * [B][Hkv][len][d] in the layout's dtype.  Copies them into the pinned host
+ * KV, builds every block summary on the GPU and empties the slot pool.
+ * len <= max_tokens. */
+int oasis_load_prefix(oasis_t *h, const void *k_host, const void *v_host, int64_t len);
+
+/* Set the residency tables (synchronous): slot_block_host[B][Hkv][S] (the
+ * block each slot holds, -1 = empty) and last_used_host[B][Hkv][S] (the step
+ * its block was last used).  The payload of every listed block is copied
+ * from the host KV into its slot.  A block held twice, or a block id not
+ * below the current block count, is OASIS_E_INVAL. */
+int oasis_set_state(oasis_t *h, const int32_t *slot_block_host, const int32_t *last_used_host);
+
+/* Append one token to every sequence: k_dev, v_dev [B][Hkv][d].  Writes it
+ * into the host KV, updates its block's max/min summary (a new block starts
+ * from this token, non-resident) and, if the block is resident, its slot.
+ * OASIS_E_CAPACITY when T == max_tokens. */
+int oasis_append_kv(oasis_t *h, const void *k_dev, const void *v_dev, hipStream_t stream);
+
+/* Predict the blocks of this step (OasisKV Fig. 7: the draft queries scan
+ * the min/max compressed keys).  q_dev [B][Hq][d] current query; drafts_dev
+ * [n_drafts][B][Hq][d] (may be NULL when n_drafts == 0).  Block score =
+ * max over the G query heads of the KV head's group and over {q} + drafts of
+ * sum_c max(x_c * max_c, x_c * min_c).  Then per (b, KV head) the top
+ * min(K, NB) blocks by (score desc, block id asc), -1 padded, become the
+ * selection.  block_ids_dev [B][Hkv][K] and scores_dev [B][Hkv][NBmax]
+ * (NBmax = ceil(max_tokens / block_size)) receive copies when non-NULL. */
+int oasis_predict(oasis_t *h, const void *q_dev, const void *drafts_dev, int32_t n_drafts,
+                  int32_t *block_ids_dev, float *scores_dev, hipStream_t stream);
+
+/* Replace the selection with the top-K of the given fp32 scores
+ * [B][Hkv][NBmax] (entries past the current block count are ignored).  A
+ * NaN or infinite score sets OASIS_E_NONFINITE in the device error word
+ * (oasis_check). */
+int oasis_topk_from_scores(oasis_t *h, const float *scores_dev, int32_t *block_ids_dev,
+                           hipStream_t stream);
+
+/* Diff the selection against the resident slots and fetch (OasisKV
+ * explanatory diagram, capped-eviction glossary, Table 2).  Per (b, KV head):
+ * hits keep their slot; the first min(cap, misses) misses in top-K order are
+ * fetched, into empty slots in ascending order first, then into the slots of
+ * held non-selected blocks, least recently used first (ties: lower block id);
+ * every hit and fetched block gets last_used = this step.  cap < 0 uses the
+ * handle's fetch ratio; cap is clamped to K.  The table update runs on
+ * `stream`; the host -> HBM block copies run on the handle's copy stream
+ * after it, and oasis_sparse_attn orders itself after them. */
+int oasis_select_and_fetch(oasis_t *h, int32_t cap, hipStream_t stream);
+
+/* Force blocks out of HBM (synchronous on `stream`): blocks_host
+ * [B][Hkv][max_per_unit] block ids, counts_host[B][Hkv] how many of each row
+ * to evict.  A listed block that is not resident is ignored.  Slots become
+ * empty; last_used is left as it is. */
+int oasis_evict(oasis_t *h, const int32_t *blocks_host, const int32_t *counts_host,
+                int32_t max_per_unit, hipStream_t stream);
+
+/* Sparse GQA decode attention over the attended blocks of the last
+ * select (the selected blocks that are now resident), for the current query
+ * q_dev [B][Hq][d]: out_dev[B][Hq][d] (fp32) = softmax(q.k / sqrt(d)) v over
+ * the valid tokens of those blocks; 0 when none is attended. */
+int oasis_sparse_attn(oasis_t *h, const void *q_dev, float *out_dev, hipStream_t stream);
+
+/* ---------------------------------------------------------------- inspection */
+
+enum {
+    OASIS_BUF_SUMMARY = 0,    /* dtype [B][Hkv][NBmax][2][d] (max, min) */
+    OASIS_BUF_SLOTS = 1,      /* dtype [B][Hkv][S][2][bs][d] (K, V) */
+    OASIS_BUF_HOST_KV = 2,    /* dtype [B][Hkv][NBmax][2][bs][d] */
+    OASIS_BUF_SCORES = 3,     /* f32 [B][Hkv][NBmax] (last oasis_predict) */
+    OASIS_BUF_IDS = 4,        /* i32 [B][Hkv][K] selection */
+    OASIS_BUF_SLOT_BLOCK = 5, /* i32 [B][Hkv][S] */
+    OASIS_BUF_BLOCK_SLOT = 6, /* i32 [B][Hkv][NBmax] */
+    OASIS_BUF_LAST_USED = 7,  /* i32 [B][Hkv][S] */
+    OASIS_BUF_FETCH_BLOCK = 8,/* i32 [B][Hkv][K] */
+    OASIS_BUF_FETCH_SLOT = 9, /* i32 [B][Hkv][K] */
+    OASIS_BUF_ATT_BLOCK = 10, /* i32 [B][Hkv][K]: hits (top-K order), then fetched */
+    OASIS_BUF_ATT_SLOT = 11,  /* i32 [B][Hkv][K] */
+    OASIS_BUF_COUNTS = 12,    /* i32 [B][Hkv][4]: attended, hits, fetched, misses */
+    OASIS_BUF_COUNT_
+};
+
+/* Size in bytes of an inspection buffer, or a negative status. */
+int64_t oasis_buffer_bytes(const oasis_t *h, int32_t which);
+
+/* Copy nbytes at byte offset of an inspection buffer to dst_host, after
+ * waiting for all work of the handle (synchronous). */
+int oasis_read(oasis_t *h, int32_t which, int64_t offset, int64_t nbytes, void *dst_host);
+
+typedef struct {
+    int64_t steps;            /* oasis_select_and_fetch calls */
+    int64_t hits;             /* selected blocks found resident */
+    int64_t misses;           /* selected blocks not resident */
+    int64_t fetched;          /* blocks copied host -> HBM */
+    int64_t attended;         /* blocks attended */
+    int64_t bytes_fetched;    /* fetched * 2 * block_size * d * elem bytes */
+    int64_t tokens;           /* current sequence length T */
+    int64_t reserved;
+} oasis_stats;
+
+/* Cumulative counters (synchronous). */
+int oasis_get_stats(oasis_t *h, oasis_stats *out);
+
+/* Wait for the handle's work and test the device error word: OASIS_OK,
+ * OASIS_E_NONFINITE, or OASIS_E_DEVICE (an invariant of the selection
+ * failed).  Clears the word. */
+int oasis_check(oasis_t *h);
+
+/* Per-kernel GPU time, summed over calls since timing was enabled. */
+typedef struct {
+    double ms_append, ms_score, ms_topk, ms_select, ms_gather, ms_attn, ms_combine;
+    int64_t n_append, n_score, n_topk, n_select, n_gather, n_attn, n_combine;
+} oasis_timing;
+
+/* enable != 0: bracket every kernel launch with HIP events on the stream it
+ * runs on (the copy stream for the gather); resets the sums. */
+int oasis_set_timing(oasis_t *h, int32_t enable);
+/* Synchronous: read the sums. */
+int oasis_get_timing(oasis_t *h, oasis_timing *out);
+
+/* Shape of a handle: K (top-K blocks), S (slots), NBmax, block size. */
+int oasis_get_dims(const oasis_t *h, int32_t *k_blocks, int32_t *slots, int64_t *nb_max,
+                   int32_t *block_size);
+
+/* Current number of tokens per sequence. */
+int64_t oasis_tokens(const oasis_t *h);
+
+/* The handle's copy stream (gather); for callers that order their own work
+ * after it. */
+hipStream_t oasis_copy_stream(const oasis_t *h);
+
+/* ------------------------------------------------------------------ helpers */
+
+/* "KV cache offloading, week 2", section 2: KV bytes per token =
+ * layers * 2 * KV heads * head_dim * dtype bytes. */
+uint64_t oasis_kv_bytes_per_token(int32_t layers, int32_t kv_heads, int32_t head_dim,
+                                  int32_t dtype_bytes);
+
+/* Default per-(b, KV head) cap for a fetch ratio of a K-block budget
+ * (OasisKV Table 2 sets the cap by a fetch ratio): max(1, floor(ratio * K))
+ * for ratio > 0, 0 for ratio <= 0, K for ratio >= 1. */
+int32_t oasis_cap_from_ratio(float ratio, int32_t k_blocks);
+
+const char *oasis_strerror(int status);
+const char *oasis_last_error(const oasis_t *h);
+
+#ifdef __cplusplus
+}
+#endif
+#endif /* OASIS_H */

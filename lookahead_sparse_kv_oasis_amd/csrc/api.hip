@@ -1,0 +1,710 @@
+// C-ABI of liboasis: handle, allocations, streams and kernel dispatch.
+//
+// One handle is one layer.  It owns
+//   - the pinned, device-mapped host KV [B][Hkv][NBmax][K|V][bs][d] (the CPU
+//     full KV cache of the OasisKV page's Fig. 7),
+//   - in HBM: the min/max summaries [B][Hkv][NBmax][max|min][d], the slot pool
+//     [B][Hkv][S][K|V][bs][d] (the sparse KV working set), the per-KV-head
+//     tables slot_block / block_slot / last_used (Fig. 9), scores, top-K ids,
+//     fetch and attended lists, attention partials,
+//   - a copy stream (default priority) for the host -> HBM gather, and the
+//     events that order it against the caller's stream.
+//
+// Ordering: select waits for the previous gather and attention; the gather
+// waits for select; attention, append and the next select wait for the
+// gather.  No call synchronises the host except the inspection calls.
+#include <stdarg.h>
+#include <stdio.h>
+#include <string.h>
+
+#include <algorithm>
+#include <cmath>
+#include <new>
+#include <string>
+#include <thread>
+#include <vector>
+
+#include "../../include/oasis.h"
+#include "kernels.h"
+
+using namespace oasis;
+
+namespace {
+
+enum { TM_APPEND, TM_SCORE, TM_TOPK, TM_SELECT, TM_GATHER, TM_ATTN, TM_COMBINE, TM_N };
+constexpr size_t kTimerCap = 4096;
+
+struct Timers {
+    std::vector<hipEvent_t> start, stop;
+    size_t used = 0;
+    double ms = 0.0;
+    int64_t n = 0;
+};
+
+}  // namespace
+
+struct oasis_handle {
+    Dims D{};
+    AttnPlan plan{};
+    oasis_layout L{};
+    float fetch_ratio = 0.f;
+    int device = 0;
+    bool use_mfma_score = false;
+
+    int64_t T = 0, T_prefix = 0;
+    bool predicted = false, selected = false;
+
+    void *host_kv = nullptr;      // host pointer (pinned)
+    void *host_kv_dev = nullptr;  // device view of the same memory
+    void *summ = nullptr, *slots = nullptr;
+    float *scores = nullptr;
+    int32_t *ids = nullptr, *slot_block = nullptr, *block_slot = nullptr, *last_used = nullptr;
+    int32_t *fetch_block = nullptr, *fetch_slot = nullptr, *att_block = nullptr,
+            *att_slot = nullptr, *counts = nullptr;
+    float *part_m = nullptr, *part_l = nullptr, *part_acc = nullptr;
+    uint32_t *err = nullptr;
+    DevStats *stats = nullptr;
+    int32_t *evict_buf = nullptr;
+    size_t evict_cap = 0;
+
+    hipStream_t copy = nullptr;
+    hipEvent_t ev_select = nullptr, ev_gather = nullptr, ev_attn = nullptr;
+
+    int64_t n_select = 0;
+    bool timing = false;
+    Timers tm[TM_N];
+    std::string last_error;
+};
+
+namespace {
+
+int fail(oasis_t *h, int code, const char *fmt, ...) __attribute__((format(printf, 3, 4)));
+int fail(oasis_t *h, int code, const char *fmt, ...) {
+    if (h) {
+        char buf[512];
+        va_list ap;
+        va_start(ap, fmt);
+        vsnprintf(buf, sizeof buf, fmt, ap);
+        va_end(ap);
+        h->last_error = buf;
+    }
+    return code;
+}
+
+#define HIP_OK(h, call)                                                                       \
+    do {                                                                                      \
+        hipError_t e_ = (call);                                                               \
+        if (e_ != hipSuccess)                                                                 \
+            return fail((h), OASIS_E_HIP, "%s: %s (%s:%d)", #call, hipGetErrorString(e_),    \
+                        __FILE__, __LINE__);                                                  \
+    } while (0)
+
+int64_t nb_of(const oasis_t *h) { return (h->T + h->D.bs - 1) / h->D.bs; }
+
+bool aligned16(const void *p) { return ((uintptr_t)p & 15u) == 0; }
+
+int tbegin(oasis_t *h, int cls, hipStream_t st) {
+    if (!h->timing) return OASIS_OK;
+    Timers &t = h->tm[cls];
+    if (t.used == kTimerCap) {  // fold finished pairs into the sum
+        HIP_OK(h, hipEventSynchronize(t.stop[t.used - 1]));
+        for (size_t i = 0; i < t.used; ++i) {
+            float ms = 0.f;
+            HIP_OK(h, hipEventElapsedTime(&ms, t.start[i], t.stop[i]));
+            t.ms += ms;
+        }
+        t.used = 0;
+    }
+    if (t.used == t.start.size()) {
+        hipEvent_t a, b;
+        HIP_OK(h, hipEventCreate(&a));
+        HIP_OK(h, hipEventCreate(&b));
+        t.start.push_back(a);
+        t.stop.push_back(b);
+    }
+    HIP_OK(h, hipEventRecord(t.start[t.used], st));
+    return OASIS_OK;
+}
+
+int tend(oasis_t *h, int cls, hipStream_t st) {
+    if (!h->timing) return OASIS_OK;
+    Timers &t = h->tm[cls];
+    HIP_OK(h, hipEventRecord(t.stop[t.used], st));
+    ++t.used;
+    ++t.n;
+    return OASIS_OK;
+}
+
+#define TRY(expr)                  \
+    do {                           \
+        int rc_ = (expr);          \
+        if (rc_ != OASIS_OK) return rc_; \
+    } while (0)
+
+#define LAUNCH(h, cls, st, call)                                                              \
+    do {                                                                                      \
+        TRY(tbegin((h), (cls), (st)));                                                        \
+        hipError_t e_ = (call);                                                               \
+        if (e_ != hipSuccess)                                                                 \
+            return fail((h), OASIS_E_HIP, "launch %s: %s", #call, hipGetErrorString(e_));    \
+        TRY(tend((h), (cls), (st)));                                                          \
+    } while (0)
+
+template <typename F> void parallel_for(int64_t n, F &&f) {
+    unsigned nt = std::thread::hardware_concurrency();
+    if (nt == 0) nt = 4;
+    if (nt > 16) nt = 16;
+    if (n < (int64_t)nt) nt = (unsigned)std::max<int64_t>(n, 1);
+    std::vector<std::thread> th;
+    for (unsigned w = 0; w < nt; ++w)
+        th.emplace_back([&, w] {
+            for (int64_t i = w; i < n; i += nt) f(i);
+        });
+    for (auto &t : th) t.join();
+}
+
+void free_all(oasis_t *h) {
+    (void)hipFree(h->summ);
+    (void)hipFree(h->slots);
+    (void)hipFree(h->scores);
+    (void)hipFree(h->ids);
+    (void)hipFree(h->slot_block);
+    (void)hipFree(h->block_slot);
+    (void)hipFree(h->last_used);
+    (void)hipFree(h->fetch_block);
+    (void)hipFree(h->fetch_slot);
+    (void)hipFree(h->att_block);
+    (void)hipFree(h->att_slot);
+    (void)hipFree(h->counts);
+    (void)hipFree(h->part_m);
+    (void)hipFree(h->part_l);
+    (void)hipFree(h->part_acc);
+    (void)hipFree(h->err);
+    (void)hipFree(h->stats);
+    (void)hipFree(h->evict_buf);
+    if (h->host_kv) (void)hipHostFree(h->host_kv);
+    if (h->copy) (void)hipStreamDestroy(h->copy);
+    if (h->ev_select) (void)hipEventDestroy(h->ev_select);
+    if (h->ev_gather) (void)hipEventDestroy(h->ev_gather);
+    if (h->ev_attn) (void)hipEventDestroy(h->ev_attn);
+    for (auto &t : h->tm) {
+        for (auto e : t.start) (void)hipEventDestroy(e);
+        for (auto e : t.stop) (void)hipEventDestroy(e);
+    }
+}
+
+int reset_tables(oasis_t *h) {
+    const Dims &D = h->D;
+    HIP_OK(h, hipMemset(h->slot_block, 0xFF, sizeof(int32_t) * D.units() * D.S));
+    HIP_OK(h, hipMemset(h->last_used, 0xFF, sizeof(int32_t) * D.units() * D.S));
+    HIP_OK(h, hipMemset(h->block_slot, 0xFF, sizeof(int32_t) * D.units() * D.NBmax));
+    HIP_OK(h, hipMemset(h->counts, 0, sizeof(int32_t) * D.units() * 4));
+    HIP_OK(h, hipMemset(h->fetch_block, 0xFF, sizeof(int32_t) * D.units() * D.K));
+    HIP_OK(h, hipMemset(h->fetch_slot, 0xFF, sizeof(int32_t) * D.units() * D.K));
+    HIP_OK(h, hipMemset(h->att_block, 0xFF, sizeof(int32_t) * D.units() * D.K));
+    HIP_OK(h, hipMemset(h->att_slot, 0xFF, sizeof(int32_t) * D.units() * D.K));
+    HIP_OK(h, hipMemset(h->ids, 0xFF, sizeof(int32_t) * D.units() * D.K));
+    h->predicted = h->selected = false;
+    return OASIS_OK;
+}
+
+}  // namespace
+
+// ------------------------------------------------------------------ helpers
+
+extern "C" uint64_t oasis_kv_bytes_per_token(int32_t layers, int32_t kv_heads, int32_t head_dim,
+                                             int32_t dtype_bytes) {
+    if (layers < 0 || kv_heads < 0 || head_dim < 0 || dtype_bytes < 0) return 0;
+    return (uint64_t)layers * 2u * (uint64_t)kv_heads * (uint64_t)head_dim *
+           (uint64_t)dtype_bytes;
+}
+
+extern "C" int32_t oasis_cap_from_ratio(float ratio, int32_t k_blocks) {
+    if (!(ratio > 0.f) || k_blocks <= 0) return 0;
+    if (ratio >= 1.f) return k_blocks;
+    const double c = std::floor((double)ratio * (double)k_blocks + 1e-9);
+    const int32_t cap = (int32_t)c;
+    return cap < 1 ? 1 : (cap > k_blocks ? k_blocks : cap);
+}
+
+extern "C" const char *oasis_strerror(int status) {
+    switch (status) {
+    case OASIS_OK: return "ok";
+    case OASIS_E_INVAL: return "invalid argument";
+    case OASIS_E_NOMEM: return "out of memory";
+    case OASIS_E_HIP: return "HIP runtime error";
+    case OASIS_E_CAPACITY: return "sequence capacity exceeded";
+    case OASIS_E_STATE: return "call out of order";
+    case OASIS_E_NONFINITE: return "non-finite score";
+    case OASIS_E_DEVICE: return "device invariant failed";
+    default: return "unknown status";
+    }
+}
+
+extern "C" const char *oasis_last_error(const oasis_t *h) {
+    return h ? h->last_error.c_str() : "null handle";
+}
+
+// ------------------------------------------------------------------ lifetime
+
+extern "C" int oasis_create(const oasis_layout *layout, int32_t block_size, int32_t budget_tokens,
+                            float fetch_ratio, oasis_t **out) {
+    if (!layout || !out) return OASIS_E_INVAL;
+    *out = nullptr;
+    const oasis_layout &L = *layout;
+    if (L.batch < 1 || L.num_q_heads < 1 || L.num_kv_heads < 1 ||
+        L.num_q_heads % L.num_kv_heads != 0)
+        return OASIS_E_INVAL;
+    if (L.head_dim < 8 || L.head_dim > 256 || L.head_dim % 8 != 0) return OASIS_E_INVAL;
+    if (L.dtype != OASIS_F32 && L.dtype != OASIS_BF16) return OASIS_E_INVAL;
+    if (L.max_drafts < 0 || L.max_tokens < 1) return OASIS_E_INVAL;
+    if (block_size < 1 || block_size > 64 || budget_tokens < block_size) return OASIS_E_INVAL;
+    if (!(fetch_ratio >= 0.f) || !std::isfinite(fetch_ratio)) return OASIS_E_INVAL;
+    const int K = budget_tokens / block_size;
+    const int S = L.slots_per_head > 0 ? L.slots_per_head : K;
+    const int G = L.num_q_heads / L.num_kv_heads;
+    const int64_t NBmax = (L.max_tokens + block_size - 1) / block_size;
+    if (K > 1024 || S < K || S > 8192 || NBmax > 65536) return OASIS_E_INVAL;
+    const int Q = G * (1 + L.max_drafts);
+    if ((int64_t)Q * L.head_dim * 4 > 64 * 1024) return OASIS_E_INVAL;
+
+    oasis_t *h = new (std::nothrow) oasis_t;
+    if (!h) return OASIS_E_NOMEM;
+    h->L = L;
+    h->fetch_ratio = fetch_ratio;
+    Dims &D = h->D;
+    D.B = L.batch;
+    D.Hq = L.num_q_heads;
+    D.Hkv = L.num_kv_heads;
+    D.G = G;
+    D.d = L.head_dim;
+    D.dtype = L.dtype;
+    D.bs = block_size;
+    D.K = K;
+    D.S = S;
+    D.NBmax = NBmax;
+    h->plan = plan_attention(D);
+    h->use_mfma_score = D.dtype == kBF16 && (D.d == 64 || D.d == 128 || D.d == 256) && Q <= 128;
+    if (const char *e = getenv("OASIS_SCORE_IMPL"))
+        if (!strcmp(e, "valu")) h->use_mfma_score = false;
+
+    auto bail = [&](int code) {
+        free_all(h);
+        delete h;
+        return code;
+    };
+    if (hipGetDevice(&h->device) != hipSuccess) return bail(OASIS_E_HIP);
+
+    const int64_t units = D.units();
+    const size_t e = D.esize();
+    const size_t host_bytes = (size_t)units * NBmax * D.block_elems() * e;
+    if (hipHostMalloc(&h->host_kv, host_bytes, hipHostMallocMapped) != hipSuccess)
+        return bail(OASIS_E_NOMEM);
+    if (hipHostGetDevicePointer(&h->host_kv_dev, h->host_kv, 0) != hipSuccess)
+        return bail(OASIS_E_HIP);
+    {
+        char *p = (char *)h->host_kv;
+        const size_t chunk = 64u << 20;
+        const int64_t nchunks = (int64_t)((host_bytes + chunk - 1) / chunk);
+        parallel_for(nchunks, [&](int64_t i) {
+            const size_t off = (size_t)i * chunk;
+            memset(p + off, 0, std::min(chunk, host_bytes - off));
+        });
+    }
+
+    auto dmal = [&](void **p, size_t bytes) { return hipMalloc(p, bytes ? bytes : 16) == hipSuccess; };
+    const int NS = h->plan.n_splits;
+    bool ok = dmal(&h->summ, (size_t)units * NBmax * 2 * D.d * e) &&
+              dmal(&h->slots, (size_t)units * S * D.block_elems() * e) &&
+              dmal((void **)&h->scores, sizeof(float) * units * NBmax) &&
+              dmal((void **)&h->ids, sizeof(int32_t) * units * K) &&
+              dmal((void **)&h->slot_block, sizeof(int32_t) * units * S) &&
+              dmal((void **)&h->block_slot, sizeof(int32_t) * units * NBmax) &&
+              dmal((void **)&h->last_used, sizeof(int32_t) * units * S) &&
+              dmal((void **)&h->fetch_block, sizeof(int32_t) * units * K) &&
+              dmal((void **)&h->fetch_slot, sizeof(int32_t) * units * K) &&
+              dmal((void **)&h->att_block, sizeof(int32_t) * units * K) &&
+              dmal((void **)&h->att_slot, sizeof(int32_t) * units * K) &&
+              dmal((void **)&h->counts, sizeof(int32_t) * units * 4) &&
+              dmal((void **)&h->part_m, sizeof(float) * units * NS * G) &&
+              dmal((void **)&h->part_l, sizeof(float) * units * NS * G) &&
+              dmal((void **)&h->part_acc, sizeof(float) * units * NS * G * D.d) &&
+              dmal((void **)&h->err, sizeof(uint32_t)) &&
+              dmal((void **)&h->stats, sizeof(DevStats));
+    if (!ok) return bail(OASIS_E_NOMEM);
+    if (hipMemset(h->summ, 0, (size_t)units * NBmax * 2 * D.d * e) != hipSuccess ||
+        hipMemset(h->slots, 0, (size_t)units * S * D.block_elems() * e) != hipSuccess ||
+        hipMemset(h->scores, 0, sizeof(float) * units * NBmax) != hipSuccess ||
+        hipMemset(h->err, 0, sizeof(uint32_t)) != hipSuccess ||
+        hipMemset(h->stats, 0, sizeof(DevStats)) != hipSuccess)
+        return bail(OASIS_E_HIP);
+    if (reset_tables(h) != OASIS_OK) return bail(OASIS_E_HIP);
+    if (hipStreamCreateWithFlags(&h->copy, hipStreamNonBlocking) != hipSuccess ||
+        hipEventCreateWithFlags(&h->ev_select, hipEventDisableTiming) != hipSuccess ||
+        hipEventCreateWithFlags(&h->ev_gather, hipEventDisableTiming) != hipSuccess ||
+        hipEventCreateWithFlags(&h->ev_attn, hipEventDisableTiming) != hipSuccess)
+        return bail(OASIS_E_HIP);
+    if (hipDeviceSynchronize() != hipSuccess) return bail(OASIS_E_HIP);
+    *out = h;
+    return OASIS_OK;
+}
+
+extern "C" int oasis_destroy(oasis_t *h) {
+    if (!h) return OASIS_E_INVAL;
+    (void)hipDeviceSynchronize();
+    free_all(h);
+    delete h;
+    return OASIS_OK;
+}
+
+// ------------------------------------------------------------------ setup
+
+extern "C" int oasis_load_prefix(oasis_t *h, const void *k_host, const void *v_host,
+                                 int64_t len) {
+    if (!h) return OASIS_E_INVAL;
+    if (len < 0 || len > h->L.max_tokens)
+        return fail(h, OASIS_E_CAPACITY, "prefix of %lld tokens exceeds max_tokens %lld",
+                    (long long)len, (long long)h->L.max_tokens);
+    if (len > 0 && (!k_host || !v_host)) return fail(h, OASIS_E_INVAL, "null prefix");
+    const Dims &D = h->D;
+    HIP_OK(h, hipDeviceSynchronize());
+    const size_t e = D.esize();
+    const size_t row = (size_t)D.d * e;
+    const int64_t NB = (len + D.bs - 1) / D.bs;
+    char *hk = (char *)h->host_kv;
+    parallel_for(D.units(), [&](int64_t u) {
+        const char *ks = (const char *)k_host + (size_t)u * len * row;
+        const char *vs = (const char *)v_host + (size_t)u * len * row;
+        for (int64_t j = 0; j < D.NBmax; ++j) {
+            char *blk = hk + ((size_t)u * D.NBmax + j) * D.block_elems() * e;
+            const int64_t p0 = j * D.bs;
+            const int64_t n = j < NB ? std::min<int64_t>(D.bs, len - p0) : 0;
+            if (n > 0) {
+                memcpy(blk, ks + p0 * row, n * row);
+                memcpy(blk + D.bs * row, vs + p0 * row, n * row);
+            }
+            if (n < D.bs && (j < NB || j == NB)) {  // clear rows past the prefix
+                memset(blk + n * row, 0, (D.bs - n) * row);
+                memset(blk + D.bs * row + n * row, 0, (D.bs - n) * row);
+            }
+        }
+    });
+    h->T = h->T_prefix = len;
+    HIP_OK(h, launch_summary_build(D, h->host_kv_dev, len, h->summ, h->copy));
+    HIP_OK(h, hipStreamSynchronize(h->copy));
+    TRY(reset_tables(h));
+    HIP_OK(h, hipDeviceSynchronize());
+    return OASIS_OK;
+}
+
+extern "C" int oasis_set_state(oasis_t *h, const int32_t *slot_block_host,
+                               const int32_t *last_used_host) {
+    if (!h || !slot_block_host || !last_used_host) return OASIS_E_INVAL;
+    const Dims &D = h->D;
+    const int64_t units = D.units(), NB = nb_of(h);
+    std::vector<int32_t> lb((size_t)units * D.S), ls((size_t)units * D.S), cnt((size_t)units);
+    std::vector<char> seen((size_t)NB > 0 ? (size_t)NB : 1);
+    int maxn = 0;
+    for (int64_t u = 0; u < units; ++u) {
+        std::fill(seen.begin(), seen.end(), 0);
+        int n = 0;
+        for (int s = 0; s < D.S; ++s) {
+            const int32_t b = slot_block_host[u * D.S + s];
+            if (b < -1 || b >= NB)
+                return fail(h, OASIS_E_INVAL, "unit %lld slot %d holds block %d (NB %lld)",
+                            (long long)u, s, b, (long long)NB);
+            if (b < 0) continue;
+            if (seen[b]) return fail(h, OASIS_E_INVAL, "block %d held twice in unit %lld", b, (long long)u);
+            seen[b] = 1;
+            lb[u * D.S + n] = b;
+            ls[u * D.S + n] = s;
+            ++n;
+        }
+        cnt[u] = n;
+        maxn = std::max(maxn, n);
+    }
+    HIP_OK(h, hipDeviceSynchronize());
+    HIP_OK(h, hipMemcpy(h->slot_block, slot_block_host, sizeof(int32_t) * units * D.S,
+                        hipMemcpyHostToDevice));
+    HIP_OK(h, hipMemcpy(h->last_used, last_used_host, sizeof(int32_t) * units * D.S,
+                        hipMemcpyHostToDevice));
+    HIP_OK(h, launch_rebuild_block_slot(D, h->slot_block, h->block_slot, h->copy));
+    int32_t *dlb = nullptr, *dls = nullptr, *dcnt = nullptr;
+    int rc = OASIS_OK;
+    if (hipMalloc(&dlb, sizeof(int32_t) * lb.size()) != hipSuccess ||
+        hipMalloc(&dls, sizeof(int32_t) * ls.size()) != hipSuccess ||
+        hipMalloc(&dcnt, sizeof(int32_t) * cnt.size()) != hipSuccess ||
+        hipMemcpy(dlb, lb.data(), sizeof(int32_t) * lb.size(), hipMemcpyHostToDevice) != hipSuccess ||
+        hipMemcpy(dls, ls.data(), sizeof(int32_t) * ls.size(), hipMemcpyHostToDevice) != hipSuccess ||
+        hipMemcpy(dcnt, cnt.data(), sizeof(int32_t) * cnt.size(), hipMemcpyHostToDevice) != hipSuccess ||
+        launch_gather(D, h->host_kv_dev, h->slots, dlb, dls, D.S, dcnt, 1, 0, maxn, h->copy) !=
+            hipSuccess ||
+        hipStreamSynchronize(h->copy) != hipSuccess)
+        rc = fail(h, OASIS_E_HIP, "set_state upload or payload copy failed");
+    (void)hipFree(dlb);
+    (void)hipFree(dls);
+    (void)hipFree(dcnt);
+    h->selected = false;
+    return rc;
+}
+
+// ------------------------------------------------------------------ decode step
+
+extern "C" int oasis_append_kv(oasis_t *h, const void *k_dev, const void *v_dev,
+                               hipStream_t stream) {
+    if (!h || !k_dev || !v_dev || !aligned16(k_dev) || !aligned16(v_dev))
+        return h ? fail(h, OASIS_E_INVAL, "append: null or misaligned pointer") : OASIS_E_INVAL;
+    if (h->T >= h->L.max_tokens)
+        return fail(h, OASIS_E_CAPACITY, "append: sequence already holds max_tokens = %lld",
+                    (long long)h->L.max_tokens);
+    HIP_OK(h, hipStreamWaitEvent(stream, h->ev_gather, 0));
+    HIP_OK(h, hipStreamWaitEvent(stream, h->ev_attn, 0));
+    LAUNCH(h, TM_APPEND, stream,
+           launch_append(h->D, k_dev, v_dev, h->T, h->host_kv_dev, h->summ, h->block_slot,
+                         h->slots, stream));
+    ++h->T;
+    return OASIS_OK;
+}
+
+extern "C" int oasis_predict(oasis_t *h, const void *q_dev, const void *drafts_dev,
+                             int32_t n_drafts, int32_t *block_ids_dev, float *scores_dev,
+                             hipStream_t stream) {
+    if (!h || !q_dev || !aligned16(q_dev)) return h ? fail(h, OASIS_E_INVAL, "predict: bad q") : OASIS_E_INVAL;
+    if (n_drafts < 0 || n_drafts > h->L.max_drafts)
+        return fail(h, OASIS_E_INVAL, "predict: n_drafts %d outside [0, %d]", n_drafts,
+                    h->L.max_drafts);
+    if (n_drafts > 0 && (!drafts_dev || !aligned16(drafts_dev)))
+        return fail(h, OASIS_E_INVAL, "predict: bad drafts pointer");
+    const int64_t NB = nb_of(h);
+    if (NB == 0) return fail(h, OASIS_E_STATE, "predict: no tokens loaded");
+    const Dims &D = h->D;
+    LAUNCH(h, TM_SCORE, stream,
+           launch_score(D, h->summ, q_dev, drafts_dev, n_drafts, NB, h->scores,
+                        h->use_mfma_score, stream));
+    if (scores_dev)
+        HIP_OK(h, hipMemcpyAsync(scores_dev, h->scores, sizeof(float) * D.units() * D.NBmax,
+                                 hipMemcpyDeviceToDevice, stream));
+    LAUNCH(h, TM_TOPK, stream,
+           launch_topk(D, h->scores, NB, h->ids, block_ids_dev, h->err, stream));
+    h->predicted = true;
+    return OASIS_OK;
+}
+
+extern "C" int oasis_topk_from_scores(oasis_t *h, const float *scores_dev,
+                                      int32_t *block_ids_dev, hipStream_t stream) {
+    if (!h || !scores_dev) return h ? fail(h, OASIS_E_INVAL, "topk: null scores") : OASIS_E_INVAL;
+    const int64_t NB = nb_of(h);
+    if (NB == 0) return fail(h, OASIS_E_STATE, "topk: no tokens loaded");
+    LAUNCH(h, TM_TOPK, stream,
+           launch_topk(h->D, scores_dev, NB, h->ids, block_ids_dev, h->err, stream));
+    h->predicted = true;
+    return OASIS_OK;
+}
+
+extern "C" int oasis_select_and_fetch(oasis_t *h, int32_t cap, hipStream_t stream) {
+    if (!h) return OASIS_E_INVAL;
+    if (!h->predicted) return fail(h, OASIS_E_STATE, "select before predict");
+    const Dims &D = h->D;
+    if (cap < 0) cap = oasis_cap_from_ratio(h->fetch_ratio, D.K);
+    if (cap > D.K) cap = D.K;
+    const int64_t t64 = h->T - h->T_prefix;
+    if (t64 > INT32_MAX - 1) return fail(h, OASIS_E_CAPACITY, "step index overflow");
+    HIP_OK(h, hipStreamWaitEvent(stream, h->ev_gather, 0));
+    HIP_OK(h, hipStreamWaitEvent(stream, h->ev_attn, 0));
+    LAUNCH(h, TM_SELECT, stream,
+           launch_select(D, h->ids, h->slot_block, h->last_used, h->block_slot, cap,
+                         (int32_t)t64, h->fetch_block, h->fetch_slot, h->att_block, h->att_slot,
+                         h->counts, h->stats, h->err, stream));
+    HIP_OK(h, hipEventRecord(h->ev_select, stream));
+    HIP_OK(h, hipStreamWaitEvent(h->copy, h->ev_select, 0));
+    LAUNCH(h, TM_GATHER, h->copy,
+           launch_gather(D, h->host_kv_dev, h->slots, h->fetch_block, h->fetch_slot, D.K,
+                         h->counts, 4, 2, cap, h->copy));
+    HIP_OK(h, hipEventRecord(h->ev_gather, h->copy));
+    ++h->n_select;
+    h->selected = true;
+    return OASIS_OK;
+}
+
+extern "C" int oasis_evict(oasis_t *h, const int32_t *blocks_host, const int32_t *counts_host,
+                           int32_t max_per_unit, hipStream_t stream) {
+    if (!h || !blocks_host || !counts_host || max_per_unit < 1)
+        return h ? fail(h, OASIS_E_INVAL, "evict: bad arguments") : OASIS_E_INVAL;
+    const Dims &D = h->D;
+    const size_t n = (size_t)D.units() * (max_per_unit + 1);
+    if (n > h->evict_cap) {
+        HIP_OK(h, hipDeviceSynchronize());
+        (void)hipFree(h->evict_buf);
+        h->evict_buf = nullptr;
+        HIP_OK(h, hipMalloc(&h->evict_buf, sizeof(int32_t) * n));
+        h->evict_cap = n;
+    }
+    int32_t *dblocks = h->evict_buf, *dcounts = h->evict_buf + (size_t)D.units() * max_per_unit;
+    HIP_OK(h, hipStreamWaitEvent(stream, h->ev_gather, 0));
+    HIP_OK(h, hipStreamWaitEvent(stream, h->ev_attn, 0));
+    HIP_OK(h, hipMemcpyAsync(dblocks, blocks_host, sizeof(int32_t) * D.units() * max_per_unit,
+                             hipMemcpyHostToDevice, stream));
+    HIP_OK(h, hipMemcpyAsync(dcounts, counts_host, sizeof(int32_t) * D.units(),
+                             hipMemcpyHostToDevice, stream));
+    HIP_OK(h, launch_evict(D, dblocks, dcounts, max_per_unit, h->slot_block, h->block_slot, stream));
+    HIP_OK(h, hipStreamSynchronize(stream));
+    return OASIS_OK;
+}
+
+extern "C" int oasis_sparse_attn(oasis_t *h, const void *q_dev, float *out_dev,
+                                 hipStream_t stream) {
+    if (!h || !q_dev || !out_dev || !aligned16(q_dev) || !aligned16(out_dev))
+        return h ? fail(h, OASIS_E_INVAL, "attn: null or misaligned pointer") : OASIS_E_INVAL;
+    if (!h->selected) return fail(h, OASIS_E_STATE, "attention before select");
+    const Dims &D = h->D;
+    HIP_OK(h, hipStreamWaitEvent(stream, h->ev_gather, 0));
+    LAUNCH(h, TM_ATTN, stream,
+           launch_attention(D, h->plan, q_dev, h->slots, h->att_block, h->att_slot, h->counts,
+                            h->T, h->part_m, h->part_l, h->part_acc, stream));
+    LAUNCH(h, TM_COMBINE, stream,
+           launch_combine(D, h->plan, h->part_m, h->part_l, h->part_acc, out_dev, stream));
+    HIP_OK(h, hipEventRecord(h->ev_attn, stream));
+    return OASIS_OK;
+}
+
+// ------------------------------------------------------------------ inspection
+
+extern "C" int64_t oasis_buffer_bytes(const oasis_t *h, int32_t which) {
+    if (!h) return OASIS_E_INVAL;
+    const Dims &D = h->D;
+    const int64_t u = D.units(), e = D.esize();
+    switch (which) {
+    case OASIS_BUF_SUMMARY: return u * D.NBmax * 2 * D.d * e;
+    case OASIS_BUF_SLOTS: return u * D.S * D.block_elems() * e;
+    case OASIS_BUF_HOST_KV: return u * D.NBmax * D.block_elems() * e;
+    case OASIS_BUF_SCORES: return u * D.NBmax * 4;
+    case OASIS_BUF_IDS: return u * D.K * 4;
+    case OASIS_BUF_SLOT_BLOCK: return u * D.S * 4;
+    case OASIS_BUF_BLOCK_SLOT: return u * D.NBmax * 4;
+    case OASIS_BUF_LAST_USED: return u * D.S * 4;
+    case OASIS_BUF_FETCH_BLOCK:
+    case OASIS_BUF_FETCH_SLOT:
+    case OASIS_BUF_ATT_BLOCK:
+    case OASIS_BUF_ATT_SLOT: return u * D.K * 4;
+    case OASIS_BUF_COUNTS: return u * 4 * 4;
+    default: return OASIS_E_INVAL;
+    }
+}
+
+extern "C" int oasis_read(oasis_t *h, int32_t which, int64_t offset, int64_t nbytes,
+                          void *dst_host) {
+    if (!h || !dst_host) return OASIS_E_INVAL;
+    const int64_t size = oasis_buffer_bytes(h, which);
+    if (size < 0) return fail(h, OASIS_E_INVAL, "read: unknown buffer %d", which);
+    if (offset < 0 || nbytes < 0 || offset + nbytes > size)
+        return fail(h, OASIS_E_INVAL, "read: range [%lld, +%lld) outside %lld bytes",
+                    (long long)offset, (long long)nbytes, (long long)size);
+    HIP_OK(h, hipDeviceSynchronize());
+    const void *src = nullptr;
+    switch (which) {
+    case OASIS_BUF_SUMMARY: src = h->summ; break;
+    case OASIS_BUF_SLOTS: src = h->slots; break;
+    case OASIS_BUF_HOST_KV:
+        memcpy(dst_host, (const char *)h->host_kv + offset, (size_t)nbytes);
+        return OASIS_OK;
+    case OASIS_BUF_SCORES: src = h->scores; break;
+    case OASIS_BUF_IDS: src = h->ids; break;
+    case OASIS_BUF_SLOT_BLOCK: src = h->slot_block; break;
+    case OASIS_BUF_BLOCK_SLOT: src = h->block_slot; break;
+    case OASIS_BUF_LAST_USED: src = h->last_used; break;
+    case OASIS_BUF_FETCH_BLOCK: src = h->fetch_block; break;
+    case OASIS_BUF_FETCH_SLOT: src = h->fetch_slot; break;
+    case OASIS_BUF_ATT_BLOCK: src = h->att_block; break;
+    case OASIS_BUF_ATT_SLOT: src = h->att_slot; break;
+    case OASIS_BUF_COUNTS: src = h->counts; break;
+    }
+    HIP_OK(h, hipMemcpy(dst_host, (const char *)src + offset, (size_t)nbytes,
+                        hipMemcpyDeviceToHost));
+    return OASIS_OK;
+}
+
+extern "C" int oasis_get_stats(oasis_t *h, oasis_stats *out) {
+    if (!h || !out) return OASIS_E_INVAL;
+    HIP_OK(h, hipDeviceSynchronize());
+    DevStats s;
+    HIP_OK(h, hipMemcpy(&s, h->stats, sizeof s, hipMemcpyDeviceToHost));
+    out->steps = h->n_select;
+    out->hits = (int64_t)s.hits;
+    out->misses = (int64_t)s.misses;
+    out->fetched = (int64_t)s.fetched;
+    out->attended = (int64_t)s.attended;
+    out->bytes_fetched = (int64_t)s.fetched * h->D.block_elems() * h->D.esize();
+    out->tokens = h->T;
+    out->reserved = 0;
+    return OASIS_OK;
+}
+
+extern "C" int oasis_check(oasis_t *h) {
+    if (!h) return OASIS_E_INVAL;
+    HIP_OK(h, hipDeviceSynchronize());
+    uint32_t e = 0;
+    HIP_OK(h, hipMemcpy(&e, h->err, sizeof e, hipMemcpyDeviceToHost));
+    HIP_OK(h, hipMemset(h->err, 0, sizeof e));
+    if (e & kErrNonFinite) return fail(h, OASIS_E_NONFINITE, "a NaN or infinite score reached the top-K");
+    if (e) return fail(h, OASIS_E_DEVICE, "device invariant word 0x%x", e);
+    return OASIS_OK;
+}
+
+extern "C" int oasis_set_timing(oasis_t *h, int32_t enable) {
+    if (!h) return OASIS_E_INVAL;
+    HIP_OK(h, hipDeviceSynchronize());
+    h->timing = enable != 0;
+    for (auto &t : h->tm) {
+        t.used = 0;
+        t.ms = 0.0;
+        t.n = 0;
+    }
+    return OASIS_OK;
+}
+
+extern "C" int oasis_get_timing(oasis_t *h, oasis_timing *out) {
+    if (!h || !out) return OASIS_E_INVAL;
+    HIP_OK(h, hipDeviceSynchronize());
+    double ms[TM_N];
+    int64_t n[TM_N];
+    for (int c = 0; c < TM_N; ++c) {
+        Timers &t = h->tm[c];
+        for (size_t i = 0; i < t.used; ++i) {
+            float x = 0.f;
+            HIP_OK(h, hipEventElapsedTime(&x, t.start[i], t.stop[i]));
+            t.ms += x;
+        }
+        t.used = 0;
+        ms[c] = t.ms;
+        n[c] = t.n;
+    }
+    out->ms_append = ms[TM_APPEND];
+    out->ms_score = ms[TM_SCORE];
+    out->ms_topk = ms[TM_TOPK];
+    out->ms_select = ms[TM_SELECT];
+    out->ms_gather = ms[TM_GATHER];
+    out->ms_attn = ms[TM_ATTN];
+    out->ms_combine = ms[TM_COMBINE];
+    out->n_append = n[TM_APPEND];
+    out->n_score = n[TM_SCORE];
+    out->n_topk = n[TM_TOPK];
+    out->n_select = n[TM_SELECT];
+    out->n_gather = n[TM_GATHER];
+    out->n_attn = n[TM_ATTN];
+    out->n_combine = n[TM_COMBINE];
+    return OASIS_OK;
+}
+
+extern "C" int oasis_get_dims(const oasis_t *h, int32_t *k_blocks, int32_t *slots,
+                              int64_t *nb_max, int32_t *block_size) {
+    if (!h) return OASIS_E_INVAL;
+    if (k_blocks) *k_blocks = h->D.K;
+    if (slots) *slots = h->D.S;
+    if (nb_max) *nb_max = h->D.NBmax;
+    if (block_size) *block_size = h->D.bs;
+    return OASIS_OK;
+}
+
+extern "C" int64_t oasis_tokens(const oasis_t *h) { return h ? h->T : OASIS_E_INVAL; }
+
+extern "C" hipStream_t oasis_copy_stream(const oasis_t *h) { return h ? h->copy : nullptr; }

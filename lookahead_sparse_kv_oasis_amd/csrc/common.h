@@ -1,0 +1,99 @@
+// Device-side helpers shared by the liboasis kernels (gfx950, wave64).
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+#include <type_traits>
+
+namespace oasis {
+
+enum : int { kF32 = 0, kBF16 = 1 };
+
+// Bits of the device error word.
+enum : uint32_t {
+    kErrNonFinite = 1u,   // a NaN / Inf score reached the top-K
+    kErrSelect = 2u,      // diff/cap found an inconsistent table
+    kErrSlots = 4u,       // not enough slots for the fetch (S < K misuse)
+};
+
+// Counters kept on the device, summed by oasis_get_stats.
+struct DevStats {
+    unsigned long long hits, misses, fetched, attended;
+};
+
+typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+typedef float f32x4 __attribute__((ext_vector_type(4)));
+typedef float f32x16 __attribute__((ext_vector_type(16)));
+
+__device__ __forceinline__ float bf16_bits_to_f32(uint32_t h16) {
+    return __uint_as_float(h16 << 16);
+}
+
+// Element traits: storage type and exact conversion to fp32.
+template <typename T> struct Elem;
+template <> struct Elem<float> {
+    static constexpr int kVec = 4;  // elements per 16-byte access
+    __device__ __forceinline__ static float f(float x) { return x; }
+};
+template <> struct Elem<uint16_t> {
+    static constexpr int kVec = 8;
+    __device__ __forceinline__ static float f(uint16_t x) { return bf16_bits_to_f32(x); }
+};
+
+// 16-byte vector of storage elements.
+template <typename T> struct alignas(16) Vec16 {
+    T v[16 / sizeof(T)];
+};
+
+template <typename T> __device__ __forceinline__ Vec16<T> ld16(const T *p) {
+    uint4 u = *reinterpret_cast<const uint4 *>(p);
+    return __builtin_bit_cast(Vec16<T>, u);
+}
+template <typename T> __device__ __forceinline__ void st16(T *p, const Vec16<T> &x) {
+    *reinterpret_cast<uint4 *>(p) = __builtin_bit_cast(uint4, x);
+}
+
+// Unpack 8 bf16 held in a uint4 into fp32.
+__device__ __forceinline__ void bf16x8_to_f32(const uint4 u, float *o) {
+    o[0] = __uint_as_float(u.x << 16);
+    o[1] = __uint_as_float(u.x & 0xffff0000u);
+    o[2] = __uint_as_float(u.y << 16);
+    o[3] = __uint_as_float(u.y & 0xffff0000u);
+    o[4] = __uint_as_float(u.z << 16);
+    o[5] = __uint_as_float(u.z & 0xffff0000u);
+    o[6] = __uint_as_float(u.w << 16);
+    o[7] = __uint_as_float(u.w & 0xffff0000u);
+}
+
+template <int I, int N, typename F> __device__ __forceinline__ void static_for(F &&f) {
+    if constexpr (I < N) {
+        f(std::integral_constant<int, I>{});
+        static_for<I + 1, N>(f);
+    }
+}
+
+// Wave64 reductions through cross-lane shuffles.
+__device__ __forceinline__ float wave_sum(float v) {
+#pragma unroll
+    for (int o = 32; o > 0; o >>= 1) v += __shfl_xor(v, o, 64);
+    return v;
+}
+__device__ __forceinline__ int wave_sum_i(int v) {
+#pragma unroll
+    for (int o = 32; o > 0; o >>= 1) v += __shfl_xor(v, o, 64);
+    return v;
+}
+__device__ __forceinline__ float wave_max(float v) {
+#pragma unroll
+    for (int o = 32; o > 0; o >>= 1) v = fmaxf(v, __shfl_xor(v, o, 64));
+    return v;
+}
+
+// Lanes below this one in the wave (for ordered compaction with ballots).
+__device__ __forceinline__ int lanes_below(unsigned long long mask) {
+    return __builtin_amdgcn_mbcnt_hi((uint32_t)(mask >> 32),
+                                     __builtin_amdgcn_mbcnt_lo((uint32_t)mask, 0u));
+}
+
+}  // namespace oasis

@@ -1,0 +1,73 @@
+// Host-side launchers of the liboasis kernels.  Each returns the launch's
+// hipError_t; shapes are validated by the C-ABI layer before any launch.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+#include "common.h"
+
+namespace oasis {
+
+struct Dims {
+    int B, Hq, Hkv, G, d, dtype, bs, K, S;
+    int64_t NBmax;
+    int64_t units() const { return (int64_t)B * Hkv; }
+    int esize() const { return dtype == kF32 ? 4 : 2; }
+    int64_t block_elems() const { return 2LL * bs * d; }  // K and V of one block
+};
+
+// Append token `pos` of every sequence (host KV, summary, resident slot).
+hipError_t launch_append(const Dims &D, const void *k, const void *v, int64_t pos, void *host_kv,
+                         void *summ, const int32_t *block_slot, void *slots, hipStream_t st);
+
+// Summaries of blocks [0, ceil(T/bs)) from the host KV.
+hipError_t launch_summary_build(const Dims &D, const void *host_kv, int64_t T, void *summ,
+                                hipStream_t st);
+
+// Block scores.  use_mfma selects the bf16 matrix-core kernel.
+hipError_t launch_score(const Dims &D, const void *summ, const void *q, const void *drafts,
+                        int n_drafts, int64_t NB, float *scores, bool use_mfma, hipStream_t st);
+
+// Per-unit top-K of scores[unit][0..NB).
+hipError_t launch_topk(const Dims &D, const float *scores, int64_t NB, int32_t *ids,
+                       int32_t *ids_copy, uint32_t *err, hipStream_t st);
+
+// Diff / cap / LRU per unit.
+hipError_t launch_select(const Dims &D, const int32_t *ids, int32_t *slot_block,
+                         int32_t *last_used, int32_t *block_slot, int cap, int32_t t,
+                         int32_t *fetch_block, int32_t *fetch_slot, int32_t *att_block,
+                         int32_t *att_slot, int32_t *counts, DevStats *stats, uint32_t *err,
+                         hipStream_t st);
+
+// Copy listed blocks from the host KV into their slots.  Unit u copies
+// n = counts[u * count_stride + count_index] entries of
+// (blocks, slots)[u * list_stride ...].  max_n bounds n for the grid.
+hipError_t launch_gather(const Dims &D, const void *host_kv, void *slots, const int32_t *blocks,
+                         const int32_t *slot_ids, int list_stride, const int32_t *counts,
+                         int count_stride, int count_index, int max_n, hipStream_t st);
+
+// Forced non-residency: unit u drops blocks[u * max_per_unit + i], i < counts[u].
+hipError_t launch_evict(const Dims &D, const int32_t *blocks, const int32_t *counts,
+                        int max_per_unit, int32_t *slot_block, int32_t *block_slot,
+                        hipStream_t st);
+
+// Rebuild block_slot from slot_block (after oasis_set_state).
+hipError_t launch_rebuild_block_slot(const Dims &D, const int32_t *slot_block,
+                                     int32_t *block_slot, hipStream_t st);
+
+// Split-K sparse attention partials and their combination.
+struct AttnPlan {
+    int n_splits;          // splits per unit
+    int blocks_per_wave;   // attended blocks per wave (MFMA kernel: 4 waves per split)
+    bool mfma;
+};
+AttnPlan plan_attention(const Dims &D);
+hipError_t launch_attention(const Dims &D, const AttnPlan &P, const void *q, const void *slots,
+                            const int32_t *att_block, const int32_t *att_slot,
+                            const int32_t *counts, int64_t T, float *part_m, float *part_l,
+                            float *part_acc, hipStream_t st);
+hipError_t launch_combine(const Dims &D, const AttnPlan &P, const float *part_m,
+                          const float *part_l, const float *part_acc, float *out, hipStream_t st);
+
+}  // namespace oasis

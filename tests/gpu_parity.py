@@ -1,0 +1,253 @@
+"""Helpers for the GPU parity tests: run the HIP path and the fp64 oracle on the
+same seeded inputs and compare them step by step.
+
+Tolerances (written here, used by every parity test):
+  - summaries, top-K ids, fetch lists, slot tables, recency, attended lists,
+    slot payload bytes: bit-exact;
+  - block scores: |gpu - oracle| <= 1e-4 * N_j, where N_j is the largest
+    sum over c of |x_c| * max(|max_jc|, |min_jc|) over the query rows (the
+    magnitude scale of the terms being summed; a pure relative error is
+    undefined near zero);
+  - attention output: max |gpu - oracle| <= 2e-3.
+"""
+from __future__ import annotations
+
+import numpy as np
+import torch
+
+import oracle
+import synth
+from lookahead_sparse_kv_oasis_amd import Oasis
+from lookahead_sparse_kv_oasis_amd.runner import LayerRunner, to_device
+from oracle.trajectory import initial_unit, workload_cap
+
+SCORE_TOL = 1e-4
+ATTN_TOL = 2e-3
+
+
+def log(msg):
+    print(msg, flush=True)
+
+
+def score_scale(unit: oracle.Unit, x_rows: np.ndarray) -> np.ndarray:
+    nb = unit.nb
+    amp = np.maximum(np.abs(unit.mx[:nb]), np.abs(unit.mn[:nb]))
+    return (np.abs(x_rows) @ amp.T).max(axis=0)
+
+
+def slot_payload_expected(keys, vals, blk, T, bs, dtype):
+    """Bytes a slot holding block blk must contain: valid rows, zeros past T."""
+    d = keys.shape[1]
+    dt = np.float32 if dtype == synth.F32 else np.uint16
+    out = np.zeros((2, bs, d), dt)
+    p0 = blk * bs
+    n = max(0, min(bs, T - p0))
+    out[0, :n] = keys[p0:p0 + n]
+    out[1, :n] = vals[p0:p0 + n]
+    return out
+
+
+class Parity:
+    """GPU runner + oracle units for a sample of (b, h) units of a workload."""
+
+    def __init__(self, w: synth.Workload, n_steps: int, units, layer: int = 0):
+        self.w, self.n_steps, self.units, self.layer = w, n_steps, list(units), layer
+        n_tok = w.prefix_tokens + n_steps
+        K, V = synth.layer_kv(w, n_tok, layer)
+        self.K, self.V = K, V
+        self.run = LayerRunner(w, n_steps, layer, kv=(K, V))
+        self.cap = workload_cap(w)
+        self.oru = {(b, h): initial_unit(w, b, h, n_steps, layer, kv=(K[b, h], V[b, h]))
+                    for (b, h) in self.units}
+        self.qf = oracle.to_f64(synth.queries(w, layer), w.dtype)
+        self.G = w.group
+        h = self.run.h
+        self.NBmax = h.nb_max
+        self.scores_dev = torch.empty((w.batch, w.kv_heads, self.NBmax), dtype=torch.float32,
+                                      device="cuda")
+        self.prev_att = {}
+
+    # ------------------------------------------------------------ checks
+    def check_summary(self):
+        w, h = self.w, self.run.h
+        dt = np.float32 if w.dtype == synth.F32 else np.uint16
+        per_unit = self.NBmax * 2 * w.head_dim
+        for (b, hh) in self.units:
+            u = b * w.kv_heads + hh
+            got = h.read_range("SUMMARY", u * per_unit * np.dtype(dt).itemsize,
+                               per_unit * np.dtype(dt).itemsize, dt).reshape(self.NBmax, 2, -1)
+            unit = self.oru[(b, hh)]
+            nb = unit.nb
+            exp_mx = synth.encode(unit.mx[:nb].astype(np.float32), w.dtype)
+            exp_mn = synth.encode(unit.mn[:nb].astype(np.float32), w.dtype)
+            bits = np.uint32 if w.dtype == synth.F32 else np.uint16
+            assert np.array_equal(np.ascontiguousarray(got[:nb, 0]).view(bits), exp_mx.view(bits)), \
+                f"summary max differs, unit {(b, hh)}"
+            assert np.array_equal(np.ascontiguousarray(got[:nb, 1]).view(bits), exp_mn.view(bits)), \
+                f"summary min differs, unit {(b, hh)}"
+
+    def _unit_slice(self, arr, b, hh, width):
+        u = b * self.w.kv_heads + hh
+        return arr[u * width:(u + 1) * width]
+
+    def check_state(self, t, rec):
+        w, h = self.w, self.run.h
+        K = h.k_blocks
+        S = h.slots
+        ids = h.read("IDS")
+        sb = h.read("SLOT_BLOCK")
+        lu = h.read("LAST_USED")
+        fb, fs = h.read("FETCH_BLOCK"), h.read("FETCH_SLOT")
+        ab, ast = h.read("ATT_BLOCK"), h.read("ATT_SLOT")
+        cnt = h.read("COUNTS")
+        bsl = h.read("BLOCK_SLOT")
+        for (b, hh) in self.units:
+            r = rec[(b, hh)]
+            tag = f"step {t} unit {(b, hh)}"
+            assert np.array_equal(self._unit_slice(ids, b, hh, K), r["ids"]), tag + " ids"
+            c = self._unit_slice(cnt, b, hh, 4)
+            na, nh, nf = int(c[0]), int(c[1]), int(c[2])
+            assert (na, nh, nf) == (len(r["att_block"]), r["n_hit"], len(r["fetch_block"])), \
+                tag + f" counts {(na, nh, nf)}"
+            assert np.array_equal(self._unit_slice(fb, b, hh, K)[:nf], r["fetch_block"]), tag
+            assert np.array_equal(self._unit_slice(fs, b, hh, K)[:nf], r["fetch_slot"]), tag
+            assert np.array_equal(self._unit_slice(ab, b, hh, K)[:na], r["att_block"]), tag
+            assert np.array_equal(self._unit_slice(ast, b, hh, K)[:na], r["att_slot"]), tag
+            usb = self._unit_slice(sb, b, hh, S)
+            assert np.array_equal(usb, r["slot_block"]), tag + " slot_block"
+            assert np.array_equal(self._unit_slice(lu, b, hh, S), r["last_used"]), tag + " lru"
+            ubs = self._unit_slice(bsl, b, hh, self.NBmax)
+            inv = np.full(self.NBmax, -1, np.int32)
+            held = usb >= 0
+            inv[usb[held]] = np.nonzero(held)[0]
+            assert np.array_equal(ubs, inv), tag + " block_slot is not the inverse table"
+            self.prev_att[(b, hh)] = r["att_block"]
+
+    def check_payload(self, t):
+        w, h = self.w, self.run.h
+        dt = np.float32 if w.dtype == synth.F32 else np.uint16
+        S, bs, d = h.slots, w.block_size, w.head_dim
+        per_slot = 2 * bs * d * np.dtype(dt).itemsize
+        sb = h.read("SLOT_BLOCK")
+        T = self.run.h.oasis_tokens()
+        for (b, hh) in self.units:
+            u = b * w.kv_heads + hh
+            got = h.read_range("SLOTS", u * S * per_slot, S * per_slot, dt).reshape(S, 2, bs, d)
+            usb = sb[u * S:(u + 1) * S]
+            for s in range(S):
+                if usb[s] < 0:
+                    continue
+                exp = slot_payload_expected(self.K[b, hh], self.V[b, hh], usb[s], T, bs, w.dtype)
+                assert np.array_equal(got[s], exp), \
+                    f"step {t} unit {(b, hh)} slot {s} block {usb[s]} payload differs"
+
+    def check_out(self, t, rec):
+        out = self.run.out.cpu().numpy()
+        worst = 0.0
+        for (b, hh) in self.units:
+            g0 = hh * self.G
+            got = out[b, g0:g0 + self.G].astype(np.float64)
+            err = np.max(np.abs(got - rec[(b, hh)]["out"]))
+            worst = max(worst, err)
+            assert err <= ATTN_TOL, f"step {t} unit {(b, hh)} attention max|err| {err:.3g}"
+        return worst
+
+    # ------------------------------------------------------------ stepping
+    def _oracle_step(self, t, append, cap, evictions=None):
+        rec = {}
+        worst_rel = 0.0
+        drafts = oracle.to_f64(synth.drafts(self.w, t, self.layer), self.w.dtype)
+        for (b, hh) in self.units:
+            x, cur = oracle.unit_rows(self.qf, drafts, b, hh, self.G)
+            ev = None if evictions is None else evictions[(b, hh)]
+            rec[(b, hh)] = self.oru[(b, hh)].step(t, x, cur, cap, append=append, evict_blocks=ev)
+            rec[(b, hh)]["x"] = x
+        return rec
+
+    def _compare_scores(self, t, rec):
+        gpu = self.scores_dev.cpu().numpy()
+        worst = 0.0
+        for (b, hh) in self.units:
+            unit = self.oru[(b, hh)]
+            nb = unit.nb
+            ref = rec[(b, hh)]["scores64"]
+            scale = score_scale(unit, rec[(b, hh)]["x"])
+            err = np.abs(gpu[b, hh, :nb].astype(np.float64) - ref) / scale
+            worst = max(worst, float(err.max()))
+            assert err.max() <= SCORE_TOL, f"step {t} unit {(b, hh)} score err {err.max():.3g}"
+        return gpu, worst
+
+    def _feed_oracle_scores(self, gpu, rec):
+        fed = gpu.copy()
+        for (b, hh) in self.units:
+            nb = self.oru[(b, hh)].nb
+            fed[b, hh, :nb] = rec[(b, hh)]["scores32"]
+        self.run.h.oasis_topk_from_scores(torch.from_numpy(fed).cuda())
+
+    def forced_evictions(self, t):
+        """Host-side draws of the stress workload applied to the GPU's own
+        previous attended lists (read back), same rule as the oracle."""
+        w, h = self.w, self.run.h
+        K = h.k_blocks
+        ab, cnt = h.read("ATT_BLOCK"), h.read("COUNTS")
+        draws = synth.evict_draws(w, t, self.layer)
+        blocks = np.full((w.batch, w.kv_heads, K), -1, np.int32)
+        counts = np.zeros((w.batch, w.kv_heads), np.int32)
+        per_unit = {}
+        for b in range(w.batch):
+            for hh in range(w.kv_heads):
+                u = b * w.kv_heads + hh
+                na = int(cnt[u * 4])
+                ev = synth.forced_evictions(w, ab[u * K:u * K + na], na, draws[b, hh])
+                blocks[b, hh, :len(ev)] = ev
+                counts[b, hh] = len(ev)
+                per_unit[(b, hh)] = ev
+        h.oasis_evict(blocks.reshape(w.batch * w.kv_heads, K), counts.reshape(-1))
+        out = {}
+        for key in self.units:   # the oracle's own previous attended list gives the same draw
+            prev = self.prev_att.get(key, np.zeros(0, np.int32))
+            mine = synth.forced_evictions(w, prev, len(prev), draws[key[0], key[1]])
+            assert np.array_equal(mine, per_unit[key]), f"step {t} unit {key} evictions differ"
+            out[key] = mine
+        return out
+
+    def run_all(self, check_payload_every=1, steps=None):
+        """Admission (if any) then every step, comparing after each one."""
+        w, run, h = self.w, self.run, self.run.h
+        steps = self.n_steps if steps is None else steps
+        report = dict(score_err=0.0, attn_err=0.0, steps=0)
+        self.check_summary()
+        if w.admission:
+            h.oasis_predict(run.q, run.drafts[0], w.drafts, scores=self.scores_dev)
+            torch.cuda.synchronize()
+            rec = self._oracle_step(0, append=False, cap=w.k_blocks)
+            gpu, e = self._compare_scores(0, rec)
+            self._feed_oracle_scores(gpu, rec)
+            h.oasis_select_and_fetch(w.k_blocks)
+            h.oasis_sparse_attn(run.q, run.out)
+            torch.cuda.synchronize()
+            self.check_state(0, rec)
+            self.check_payload(0)
+            report["attn_err"] = max(report["attn_err"], self.check_out(0, rec))
+        for t in range(1, steps + 1):
+            ev = None
+            if w.forced_evict_frac > 0:
+                ev = self.forced_evictions(t)
+            h.oasis_append_kv(run.app_k[t - 1], run.app_v[t - 1])
+            h.oasis_predict(run.q, run.drafts[t], w.drafts, scores=self.scores_dev)
+            torch.cuda.synchronize()
+            rec = self._oracle_step(t, append=True, cap=self.cap, evictions=ev)
+            gpu, e = self._compare_scores(t, rec)
+            report["score_err"] = max(report["score_err"], e)
+            self._feed_oracle_scores(gpu, rec)
+            h.oasis_select_and_fetch(self.cap)
+            h.oasis_sparse_attn(run.q, run.out)
+            torch.cuda.synchronize()
+            h.oasis_check()
+            self.check_state(t, rec)
+            if t % check_payload_every == 0 or t == steps:
+                self.check_payload(t)
+                self.check_summary()
+            report["attn_err"] = max(report["attn_err"], self.check_out(t, rec))
+            report["steps"] = t
+        return report
