@@ -205,9 +205,14 @@ typedef struct {
     int64_t n_append, n_score, n_topk, n_select, n_gather, n_attn, n_combine;
 } oasis_timing;
 
-/* enable != 0: bracket every kernel launch with HIP events on the stream it
- * runs on (the copy stream for the gather); resets the sums. */
-int oasis_set_timing(oasis_t *h, int32_t enable);
+/* Kernel classes for oasis_set_timing. */
+enum {
+    OASIS_TIME_APPEND = 1, OASIS_TIME_SCORE = 2, OASIS_TIME_TOPK = 4, OASIS_TIME_SELECT = 8,
+    OASIS_TIME_GATHER = 16, OASIS_TIME_ATTN = 32, OASIS_TIME_COMBINE = 64, OASIS_TIME_ALL = 127
+};
+/* mask != 0: bracket every launch of the kernel classes in mask with HIP
+ * events on the stream it runs on; 0 turns timing off.  Resets the sums. */
+int oasis_set_timing(oasis_t *h, int32_t mask);
 /* Synchronous: read the sums. */
 int oasis_get_timing(oasis_t *h, oasis_timing *out);
 

@@ -21,6 +21,8 @@ OASIS_OK, OASIS_E_INVAL, OASIS_E_NOMEM, OASIS_E_HIP = 0, -1, -2, -3
 OASIS_E_CAPACITY, OASIS_E_STATE, OASIS_E_NONFINITE, OASIS_E_DEVICE = -4, -5, -6, -7
 OASIS_F32, OASIS_BF16 = 0, 1
 
+TIME = dict(append=1, score=2, topk=4, select=8, gather=16, attn=32, combine=64, all=127)
+
 BUF = dict(SUMMARY=0, SLOTS=1, HOST_KV=2, SCORES=3, IDS=4, SLOT_BLOCK=5, BLOCK_SLOT=6,
            LAST_USED=7, FETCH_BLOCK=8, FETCH_SLOT=9, ATT_BLOCK=10, ATT_SLOT=11, COUNTS=12)
 
@@ -223,8 +225,9 @@ class Oasis:
         self._check(lib().oasis_get_stats(self.h, ctypes.byref(s)), "oasis_get_stats")
         return {n: getattr(s, n) for n, _ in oasis_stats._fields_ if n != "reserved"}
 
-    def oasis_set_timing(self, enable=True):
-        self._check(lib().oasis_set_timing(self.h, int(bool(enable))), "oasis_set_timing")
+    def oasis_set_timing(self, mask=TIME["all"]):
+        """mask: OR of TIME values (0 = off)."""
+        self._check(lib().oasis_set_timing(self.h, int(mask)), "oasis_set_timing")
 
     def oasis_get_timing(self) -> dict:
         t = oasis_timing()

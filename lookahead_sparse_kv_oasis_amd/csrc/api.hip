@@ -53,6 +53,16 @@ struct oasis_handle {
 
     int64_t T = 0, T_prefix = 0;
     bool predicted = false, selected = false;
+    // Fused mode: the blocks chosen by select are copied host -> HBM inside
+    // the next sparse attention (which reads them anyway); a call that needs
+    // the slots before that runs the standalone gather first.
+    bool fused = false;
+    bool fetch_pending = false;
+    // The top-K of the last scores has not run yet: select_and_fetch runs it
+    // fused with the select (one workgroup per unit).
+    bool topk_pending = false;
+    int64_t topk_nb = 0;
+    int last_cap = 0;
 
     void *host_kv = nullptr;      // host pointer (pinned)
     void *host_kv_dev = nullptr;  // device view of the same memory
@@ -71,7 +81,7 @@ struct oasis_handle {
     hipEvent_t ev_select = nullptr, ev_gather = nullptr, ev_attn = nullptr;
 
     int64_t n_select = 0;
-    bool timing = false;
+    int32_t timing = 0;  // mask of timed kernel classes
     Timers tm[TM_N];
     std::string last_error;
 };
@@ -104,7 +114,7 @@ int64_t nb_of(const oasis_t *h) { return (h->T + h->D.bs - 1) / h->D.bs; }
 bool aligned16(const void *p) { return ((uintptr_t)p & 15u) == 0; }
 
 int tbegin(oasis_t *h, int cls, hipStream_t st) {
-    if (!h->timing) return OASIS_OK;
+    if (!(h->timing & (1 << cls))) return OASIS_OK;
     Timers &t = h->tm[cls];
     if (t.used == kTimerCap) {  // fold finished pairs into the sum
         HIP_OK(h, hipEventSynchronize(t.stop[t.used - 1]));
@@ -127,7 +137,7 @@ int tbegin(oasis_t *h, int cls, hipStream_t st) {
 }
 
 int tend(oasis_t *h, int cls, hipStream_t st) {
-    if (!h->timing) return OASIS_OK;
+    if (!(h->timing & (1 << cls))) return OASIS_OK;
     Timers &t = h->tm[cls];
     HIP_OK(h, hipEventRecord(t.stop[t.used], st));
     ++t.used;
@@ -205,6 +215,26 @@ int reset_tables(oasis_t *h) {
     HIP_OK(h, hipMemset(h->att_slot, 0xFF, sizeof(int32_t) * D.units() * D.K));
     HIP_OK(h, hipMemset(h->ids, 0xFF, sizeof(int32_t) * D.units() * D.K));
     h->predicted = h->selected = false;
+    h->fetch_pending = false;
+    h->topk_pending = false;
+    return OASIS_OK;
+}
+
+// Run a deferred top-K on its own (when the ids are needed before a select).
+int flush_topk(oasis_t *h, hipStream_t st) {
+    if (!h->topk_pending) return OASIS_OK;
+    h->topk_pending = false;
+    LAUNCH(h, TM_TOPK, st, launch_topk(h->D, h->scores, h->topk_nb, h->ids, nullptr, h->err, st));
+    return OASIS_OK;
+}
+
+// Copy the pending fetch list host -> HBM now (fused mode only).
+int flush_fetch(oasis_t *h, hipStream_t st) {
+    if (!h->fetch_pending) return OASIS_OK;
+    h->fetch_pending = false;
+    LAUNCH(h, TM_GATHER, st,
+           launch_gather(h->D, h->host_kv_dev, h->slots, h->fetch_block, h->fetch_slot, h->D.K,
+                         h->counts, 4, 2, h->last_cap, st));
     return OASIS_OK;
 }
 
@@ -287,6 +317,9 @@ extern "C" int oasis_create(const oasis_layout *layout, int32_t block_size, int3
     h->use_mfma_score = D.dtype == kBF16 && (D.d == 64 || D.d == 128 || D.d == 256) && Q <= 128;
     if (const char *e = getenv("OASIS_SCORE_IMPL"))
         if (!strcmp(e, "valu")) h->use_mfma_score = false;
+    h->fused = h->plan.mfma;
+    if (const char *e = getenv("OASIS_GATHER"))
+        if (!strcmp(e, "stream")) h->fused = false;
 
     auto bail = [&](int code) {
         free_all(h);
@@ -313,7 +346,7 @@ extern "C" int oasis_create(const oasis_layout *layout, int32_t block_size, int3
     }
 
     auto dmal = [&](void **p, size_t bytes) { return hipMalloc(p, bytes ? bytes : 16) == hipSuccess; };
-    const int NS = h->plan.n_splits;
+    const int NS = h->plan.nsa;
     bool ok = dmal(&h->summ, (size_t)units * NBmax * 2 * D.d * e) &&
               dmal(&h->slots, (size_t)units * S * D.block_elems() * e) &&
               dmal((void **)&h->scores, sizeof(float) * units * NBmax) &&
@@ -423,6 +456,7 @@ extern "C" int oasis_set_state(oasis_t *h, const int32_t *slot_block_host,
         cnt[u] = n;
         maxn = std::max(maxn, n);
     }
+    h->fetch_pending = false;   // the tables are replaced wholesale
     HIP_OK(h, hipDeviceSynchronize());
     HIP_OK(h, hipMemcpy(h->slot_block, slot_block_host, sizeof(int32_t) * units * D.S,
                         hipMemcpyHostToDevice));
@@ -459,6 +493,7 @@ extern "C" int oasis_append_kv(oasis_t *h, const void *k_dev, const void *v_dev,
                     (long long)h->L.max_tokens);
     HIP_OK(h, hipStreamWaitEvent(stream, h->ev_gather, 0));
     HIP_OK(h, hipStreamWaitEvent(stream, h->ev_attn, 0));
+    TRY(flush_fetch(h, stream));
     LAUNCH(h, TM_APPEND, stream,
            launch_append(h->D, k_dev, v_dev, h->T, h->host_kv_dev, h->summ, h->block_slot,
                          h->slots, stream));
@@ -484,8 +519,14 @@ extern "C" int oasis_predict(oasis_t *h, const void *q_dev, const void *drafts_d
     if (scores_dev)
         HIP_OK(h, hipMemcpyAsync(scores_dev, h->scores, sizeof(float) * D.units() * D.NBmax,
                                  hipMemcpyDeviceToDevice, stream));
-    LAUNCH(h, TM_TOPK, stream,
-           launch_topk(D, h->scores, NB, h->ids, block_ids_dev, h->err, stream));
+    h->topk_nb = NB;
+    if (block_ids_dev) {
+        LAUNCH(h, TM_TOPK, stream,
+               launch_topk(D, h->scores, NB, h->ids, block_ids_dev, h->err, stream));
+        h->topk_pending = false;
+    } else {
+        h->topk_pending = true;
+    }
     h->predicted = true;
     return OASIS_OK;
 }
@@ -497,6 +538,7 @@ extern "C" int oasis_topk_from_scores(oasis_t *h, const float *scores_dev,
     if (NB == 0) return fail(h, OASIS_E_STATE, "topk: no tokens loaded");
     LAUNCH(h, TM_TOPK, stream,
            launch_topk(h->D, scores_dev, NB, h->ids, block_ids_dev, h->err, stream));
+    h->topk_pending = false;
     h->predicted = true;
     return OASIS_OK;
 }
@@ -511,16 +553,31 @@ extern "C" int oasis_select_and_fetch(oasis_t *h, int32_t cap, hipStream_t strea
     if (t64 > INT32_MAX - 1) return fail(h, OASIS_E_CAPACITY, "step index overflow");
     HIP_OK(h, hipStreamWaitEvent(stream, h->ev_gather, 0));
     HIP_OK(h, hipStreamWaitEvent(stream, h->ev_attn, 0));
-    LAUNCH(h, TM_SELECT, stream,
-           launch_select(D, h->ids, h->slot_block, h->last_used, h->block_slot, cap,
-                         (int32_t)t64, h->fetch_block, h->fetch_slot, h->att_block, h->att_slot,
-                         h->counts, h->stats, h->err, stream));
-    HIP_OK(h, hipEventRecord(h->ev_select, stream));
-    HIP_OK(h, hipStreamWaitEvent(h->copy, h->ev_select, 0));
-    LAUNCH(h, TM_GATHER, h->copy,
-           launch_gather(D, h->host_kv_dev, h->slots, h->fetch_block, h->fetch_slot, D.K,
-                         h->counts, 4, 2, cap, h->copy));
-    HIP_OK(h, hipEventRecord(h->ev_gather, h->copy));
+    TRY(flush_fetch(h, stream));
+    if (h->topk_pending) {
+        h->topk_pending = false;
+        LAUNCH(h, TM_SELECT, stream,
+               launch_topk_select(D, h->scores, h->topk_nb, h->ids, h->slot_block, h->last_used,
+                                  h->block_slot, cap, (int32_t)t64, h->fetch_block,
+                                  h->fetch_slot, h->att_block, h->att_slot, h->counts, h->stats,
+                                  h->err, stream));
+    } else {
+        LAUNCH(h, TM_SELECT, stream,
+               launch_select(D, h->ids, h->slot_block, h->last_used, h->block_slot, cap,
+                             (int32_t)t64, h->fetch_block, h->fetch_slot, h->att_block,
+                             h->att_slot, h->counts, h->stats, h->err, stream));
+    }
+    h->last_cap = cap;
+    if (h->fused) {
+        h->fetch_pending = cap > 0;
+    } else {
+        HIP_OK(h, hipEventRecord(h->ev_select, stream));
+        HIP_OK(h, hipStreamWaitEvent(h->copy, h->ev_select, 0));
+        LAUNCH(h, TM_GATHER, h->copy,
+               launch_gather(D, h->host_kv_dev, h->slots, h->fetch_block, h->fetch_slot, D.K,
+                             h->counts, 4, 2, cap, h->copy));
+        HIP_OK(h, hipEventRecord(h->ev_gather, h->copy));
+    }
     ++h->n_select;
     h->selected = true;
     return OASIS_OK;
@@ -542,6 +599,7 @@ extern "C" int oasis_evict(oasis_t *h, const int32_t *blocks_host, const int32_t
     int32_t *dblocks = h->evict_buf, *dcounts = h->evict_buf + (size_t)D.units() * max_per_unit;
     HIP_OK(h, hipStreamWaitEvent(stream, h->ev_gather, 0));
     HIP_OK(h, hipStreamWaitEvent(stream, h->ev_attn, 0));
+    TRY(flush_fetch(h, stream));
     HIP_OK(h, hipMemcpyAsync(dblocks, blocks_host, sizeof(int32_t) * D.units() * max_per_unit,
                              hipMemcpyHostToDevice, stream));
     HIP_OK(h, hipMemcpyAsync(dcounts, counts_host, sizeof(int32_t) * D.units(),
@@ -558,11 +616,22 @@ extern "C" int oasis_sparse_attn(oasis_t *h, const void *q_dev, float *out_dev,
     if (!h->selected) return fail(h, OASIS_E_STATE, "attention before select");
     const Dims &D = h->D;
     HIP_OK(h, hipStreamWaitEvent(stream, h->ev_gather, 0));
+    int mode = 0, nsf = 0;
+    if (h->fetch_pending) {
+        if (h->plan.mfma) {
+            mode = 1;
+            nsf = attention_fetch_splits(D, h->plan, h->last_cap);
+            h->fetch_pending = false;
+        } else {
+            TRY(flush_fetch(h, stream));
+        }
+    }
     LAUNCH(h, TM_ATTN, stream,
-           launch_attention(D, h->plan, q_dev, h->slots, h->att_block, h->att_slot, h->counts,
-                            h->T, h->part_m, h->part_l, h->part_acc, stream));
+           launch_attention(D, h->plan, mode, nsf, q_dev, h->slots, h->host_kv_dev, h->att_block,
+                            h->att_slot, h->counts, h->T, h->part_m, h->part_l, h->part_acc,
+                            stream));
     LAUNCH(h, TM_COMBINE, stream,
-           launch_combine(D, h->plan, h->part_m, h->part_l, h->part_acc, out_dev, stream));
+           launch_combine(D, h->plan, nsf, h->part_m, h->part_l, h->part_acc, out_dev, stream));
     HIP_OK(h, hipEventRecord(h->ev_attn, stream));
     return OASIS_OK;
 }
@@ -600,6 +669,11 @@ extern "C" int oasis_read(oasis_t *h, int32_t which, int64_t offset, int64_t nby
         return fail(h, OASIS_E_INVAL, "read: range [%lld, +%lld) outside %lld bytes",
                     (long long)offset, (long long)nbytes, (long long)size);
     HIP_OK(h, hipDeviceSynchronize());
+    if (h->fetch_pending || (h->topk_pending && which == OASIS_BUF_IDS)) {
+        TRY(flush_fetch(h, h->copy));
+        if (which == OASIS_BUF_IDS) TRY(flush_topk(h, h->copy));
+        HIP_OK(h, hipStreamSynchronize(h->copy));
+    }
     const void *src = nullptr;
     switch (which) {
     case OASIS_BUF_SUMMARY: src = h->summ; break;
@@ -650,10 +724,10 @@ extern "C" int oasis_check(oasis_t *h) {
     return OASIS_OK;
 }
 
-extern "C" int oasis_set_timing(oasis_t *h, int32_t enable) {
+extern "C" int oasis_set_timing(oasis_t *h, int32_t mask) {
     if (!h) return OASIS_E_INVAL;
     HIP_OK(h, hipDeviceSynchronize());
-    h->timing = enable != 0;
+    h->timing = mask & OASIS_TIME_ALL;
     for (auto &t : h->tm) {
         t.used = 0;
         t.ms = 0.0;

@@ -24,8 +24,9 @@ template <typename T, int EPL>
 __global__ __launch_bounds__(64) void attn_generic_kernel(
     const T *__restrict__ q, const T *__restrict__ slots, const int32_t *__restrict__ att_block,
     const int32_t *__restrict__ att_slot, const int32_t *__restrict__ counts, int64_t T_, int Hq,
-    int Hkv, int G, int d, int K, int S, int bs, int bps, int n_splits, float scale_log2,
-    float *__restrict__ part_m, float *__restrict__ part_l, float *__restrict__ part_acc) {
+    int Hkv, int G, int d, int K, int S, int bs, int bps, int nsa, int split_off,
+    float scale_log2, float *__restrict__ part_m, float *__restrict__ part_l,
+    float *__restrict__ part_acc) {
     const int lane = threadIdx.x;
     const int split = blockIdx.x, h = blockIdx.y, b = blockIdx.z;
     const int64_t u = (int64_t)b * Hkv + h;
@@ -69,7 +70,7 @@ __global__ __launch_bounds__(64) void attn_generic_kernel(
                 m = mn;
             }
         }
-        const int64_t pi = (u * n_splits + split) * G + g;
+        const int64_t pi = (u * nsa + split_off + split) * G + g;
 #pragma unroll
         for (int e = 0; e < EPL; ++e) {
             const int c = lane + 64 * e;
@@ -91,81 +92,72 @@ template <int g> __device__ __forceinline__ float row_bcast(float x) {
                                            false));
 }
 
-// Four waves per (split, unit); wave w takes attended entries
-// split * 4 * BPW + w + 4 i.  Per 16-token block:
+// Per 16-token block of one unit, in one wave:
 //   S^T = K . Q^T on v_mfma_f32_16x16x32_bf16 (tokens are the M rows, the G
 //   heads of the group the N columns, zero-padded to 16).  Lane l supplies
-//   token / head l % 16 and the 32 consecutive dimensions 32 (l / 16) ...,
-//   8 per MFMA step, so every lane reads one contiguous 64-byte piece of its
-//   key row.  The accumulator of lane l holds head l % 16 for tokens
+//   token / head l % 16 and, at step c, the dimensions 32 c + 8 (l / 16) ...
+//   (8 of them), so the four lanes of a key row read 64 contiguous bytes per
+//   step.  The accumulator of lane l holds head l % 16 for tokens
 //   4 (l / 16) + r, r < 4.
 //   P V on the vector ALU in fp32: lane l owns tokens 4 (l / 16) + r and the
 //   8 dimensions 8 (l % 16) ...; the probabilities of head g for its tokens
 //   sit in lane 16 (l / 16) + g of the same 16-lane row, so a DPP row
 //   broadcast delivers them.
-template <int G, int BPW>
-__global__ __launch_bounds__(256) void attn_mfma_kernel(
-    const uint16_t *__restrict__ q, const uint16_t *__restrict__ slots,
-    const int32_t *__restrict__ att_block, const int32_t *__restrict__ att_slot,
-    const int32_t *__restrict__ counts, int64_t T_, int Hq, int Hkv, int K, int S, int n_splits,
-    float scale_log2, float *__restrict__ part_m, float *__restrict__ part_l,
-    float *__restrict__ part_acc) {
-    constexpr int D = 128, BS = 16;
-    __shared__ float sm_m[4][16], sm_l[4][16];
-    __shared__ float sm_acc[4][G][D];
-
-    const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
-    const int split = blockIdx.x, h = blockIdx.y, b = blockIdx.z;
-    const int64_t u = (int64_t)b * Hkv + h;
-    const int n_att = counts[u * 4];
-    const int col = lane & 15, kg = lane >> 4;
-
+template <int G> struct AttnWave {
+    static constexpr int D = 128, BS = 16, BLK = 2 * BS * D;
+    int col, kg, koff, voff;
     bf16x8 qb[4];
-    {
-        const uint16_t *qr = q + ((int64_t)b * Hq + h * G + (col < G ? col : 0)) * D + 32 * kg;
+    float m, lsum;
+    float acc[G][8];
+
+    // Lane roles; must run before the first load.
+    __device__ __forceinline__ void lanes() {
+        const int lane = threadIdx.x & 63;
+        col = lane & 15;
+        kg = lane >> 4;
+        koff = col * D + 8 * kg;
+        voff = BS * D + 4 * kg * D + 8 * col;
+    }
+    // Queries of unit (b, h) and a cleared softmax state.
+    __device__ __forceinline__ void init(const uint16_t *q, int64_t b, int Hq, int h) {
+        const uint16_t *qr = q + (b * Hq + h * G + (col < G ? col : 0)) * D + 8 * kg;
 #pragma unroll
         for (int i = 0; i < 4; ++i) {
-            uint4 w = *reinterpret_cast<const uint4 *>(qr + 8 * i);
+            uint4 w = *reinterpret_cast<const uint4 *>(qr + 32 * i);
             if (col >= G) w = make_uint4(0, 0, 0, 0);
             qb[i] = __builtin_bit_cast(bf16x8, w);
         }
+        reset();
     }
-
-    float m = -INFINITY, lsum = 0.f;
-    float acc[G][8];
+    __device__ __forceinline__ void reset() {
+        m = -INFINITY;
+        lsum = 0.f;
 #pragma unroll
-    for (int g = 0; g < G; ++g)
+        for (int g = 0; g < G; ++g)
 #pragma unroll
-        for (int e = 0; e < 8; ++e) acc[g][e] = 0.f;
-
-    const int e0 = split * 4 * BPW + wave;
-#pragma unroll 1
-    for (int bi = 0; bi < BPW; ++bi) {
-        const int e = e0 + 4 * bi;
-        if (e >= n_att) break;
-        const int32_t blk = att_block[u * K + e], slot = att_slot[u * K + e];
-        const int64_t first = (int64_t)blk * BS;
-        const int valid = (int)((T_ - first) < BS ? (T_ - first) : BS);
-        const uint16_t *kp = slots + (u * S + slot) * 2 * (int64_t)BS * D;
-        const uint16_t *vp = kp + BS * D;
-
-        bf16x8 ka[4];
-        const uint16_t *kr = kp + col * D + 32 * kg;
+            for (int e = 0; e < 8; ++e) acc[g][e] = 0.f;
+    }
+    __device__ __forceinline__ void load(uint4 (&kk)[4], uint4 (&vv)[4], const uint16_t *p) const {
 #pragma unroll
-        for (int i = 0; i < 4; ++i)
-            ka[i] = __builtin_bit_cast(bf16x8, *reinterpret_cast<const uint4 *>(kr + 8 * i));
-        uint4 vr[4];
+        for (int i = 0; i < 4; ++i) kk[i] = gload16(p + koff + 32 * i);
 #pragma unroll
-        for (int r = 0; r < 4; ++r) {
-            vr[r] = *reinterpret_cast<const uint4 *>(vp + (4 * kg + r) * D + 8 * col);
-            if (4 * kg + r >= valid) vr[r] = make_uint4(0, 0, 0, 0);
-        }
-
+        for (int r = 0; r < 4; ++r) vv[r] = gload16(p + voff + r * D);
+    }
+    __device__ __forceinline__ void store(uint16_t *p, const uint4 (&kk)[4],
+                                          const uint4 (&vv)[4]) const {
+#pragma unroll
+        for (int c = 0; c < 4; ++c) gstore16(p + koff + 32 * c, kk[c]);
+#pragma unroll
+        for (int r = 0; r < 4; ++r) gstore16(p + voff + r * D, vv[r]);
+    }
+    // Online-softmax update with one block of `valid` tokens.
+    __device__ __forceinline__ void block(const uint4 (&kk)[4], const uint4 (&vv)[4], int valid,
+                                          float scale_log2) {
         f32x4 s4 = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-        for (int i = 0; i < 4; ++i)
-            s4 = __builtin_amdgcn_mfma_f32_16x16x32_bf16(ka[i], qb[i], s4, 0, 0, 0);
-
+        for (int c = 0; c < 4; ++c)
+            s4 = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, kk[c]), qb[c],
+                                                         s4, 0, 0, 0);
         float sr[4];
 #pragma unroll
         for (int r = 0; r < 4; ++r) sr[r] = (4 * kg + r < valid) ? s4[r] * scale_log2 : -INFINITY;
@@ -180,65 +172,217 @@ __global__ __launch_bounds__(256) void attn_mfma_kernel(
         for (int r = 0; r < 4; ++r) p[r] = live ? exp2f(sr[r] - mn) : 0.f;
         lsum = lsum * alpha + ((p[0] + p[1]) + (p[2] + p[3]));
         m = mn;
-
-        float vf[4][8];
-#pragma unroll
-        for (int r = 0; r < 4; ++r) bf16x8_to_f32(vr[r], vf[r]);
-
+        // rescale, then add the block's four value rows one at a time (the
+        // rows past T are zeroed: their probability is 0 but the bytes may be
+        // anything)
         static_for<0, G>([&](auto gi) {
             constexpr int g = decltype(gi)::value;
             const float ag = row_bcast<g>(alpha);
-            float pg[4];
 #pragma unroll
-            for (int r = 0; r < 4; ++r) pg[r] = row_bcast<g>(p[r]);
-#pragma unroll
-            for (int e = 0; e < 8; ++e) {
-                float a = acc[g][e] * ag;
-#pragma unroll
-                for (int r = 0; r < 4; ++r) a += pg[r] * vf[r][e];
-                acc[g][e] = a;
-            }
+            for (int e = 0; e < 8; ++e) acc[g][e] *= ag;
         });
-    }
-
-    // reduce over the four token groups of the wave
-    lsum += __shfl_xor(lsum, 16, 64);
-    lsum += __shfl_xor(lsum, 32, 64);
 #pragma unroll
-    for (int g = 0; g < G; ++g)
+        for (int r = 0; r < 4; ++r) {
+            const uint32_t keep = (4 * kg + r < valid) ? 0xFFFFFFFFu : 0u;
+            float vf[8];
+            bf16x8_to_f32(make_uint4(vv[r].x & keep, vv[r].y & keep, vv[r].z & keep,
+                                     vv[r].w & keep),
+                          vf);
+            static_for<0, G>([&](auto gi) {
+                constexpr int g = decltype(gi)::value;
+                const float pg = row_bcast<g>(p[r]);
 #pragma unroll
-        for (int e = 0; e < 8; ++e) {
-            float a = acc[g][e];
-            a += __shfl_xor(a, 16, 64);
-            a += __shfl_xor(a, 32, 64);
-            acc[g][e] = a;
+                for (int e = 0; e < 8; ++e) acc[g][e] += pg * vf[e];
+            });
         }
-    if (kg == 0) {
+    }
+    // Sum the four token groups; lanes with kg == 0 then hold the wave's acc.
+    __device__ __forceinline__ void reduce() {
+        lsum += __shfl_xor(lsum, 16, 64);
+        lsum += __shfl_xor(lsum, 32, 64);
 #pragma unroll
         for (int g = 0; g < G; ++g)
 #pragma unroll
-            for (int e = 0; e < 8; ++e) sm_acc[wave][g][8 * col + e] = acc[g][e];
-        sm_m[wave][col] = m;
-        sm_l[wave][col] = lsum;
+            for (int e = 0; e < 8; ++e) {
+                float a = acc[g][e];
+                a += __shfl_xor(a, 16, 64);
+                a += __shfl_xor(a, 32, 64);
+                acc[g][e] = a;
+            }
+    }
+    // Write this wave's (reduced) state as partial pi0 + g.
+    __device__ __forceinline__ void write_partial(int64_t pi0, float *part_m, float *part_l,
+                                                  float *part_acc) const {
+        if (kg == 0) {
+#pragma unroll
+            for (int g = 0; g < G; ++g) {
+                float4 *dst = reinterpret_cast<float4 *>(part_acc + (pi0 + g) * D + 8 * col);
+                dst[0] = make_float4(acc[g][0], acc[g][1], acc[g][2], acc[g][3]);
+                dst[1] = make_float4(acc[g][4], acc[g][5], acc[g][6], acc[g][7]);
+            }
+            if (col < G) {
+                part_m[pi0 + col] = m;
+                part_l[pi0 + col] = lsum;
+            }
+        }
+    }
+};
+
+__device__ __forceinline__ int block_valid(int64_t T, int32_t blk) {
+    const int64_t first = (int64_t)blk * 16;
+    return (int)((T - first) < 16 ? (T - first) : 16);
+}
+
+// Grid (1-D, 256 threads = 4 waves per workgroup):
+//   workgroups [0, n_fetch_wg): fetch waves (mode 1 only).  Item i of unit u,
+//     i < cap, is the i-th block fetched for u this step (attended entry
+//     n_hit + i).  Wave f takes items f, f + F, ... (F = 4 n_fetch_wg): it
+//     reads the block from the pinned host KV over the host link, writes it
+//     into its slot (the copy later steps will hit), attends to it from
+//     registers and writes partial i of the unit; an item past the unit's
+//     fetch count writes an empty partial.  A few such waves keep the host
+//     link saturated while holding only a small share of the CU slots.
+//   workgroups after that: hit workgroups, ns1 per unit; wave w of split s
+//     takes entries 4 BPW s + w + 4 j, j < BPW, of [0, n_end) (n_end = n_hit
+//     in mode 1, n_att in mode 0) from their slots; the four waves are merged
+//     in LDS into partial nsf_max + s.
+template <int G, int BPW>
+__global__ __launch_bounds__(256) void attn_mfma_kernel(
+    const uint16_t *__restrict__ q, uint16_t *__restrict__ slots,
+    const uint16_t *__restrict__ host_kv, const int32_t *__restrict__ att_block,
+    const int32_t *__restrict__ att_slot, const int32_t *__restrict__ counts, int64_t T_, int Hq,
+    int Hkv, int K, int S, int64_t NBmax, int mode, int cap, int n_fetch_wg, int nsf_max,
+    int ns1, int nsa, int64_t units, float scale_log2, float *__restrict__ part_m,
+    float *__restrict__ part_l, float *__restrict__ part_acc) {
+    using W = AttnWave<G>;
+    constexpr int D = W::D;
+    // wave-uniform, so per-wave metadata comes through scalar loads
+    const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+    W st;
+    st.lanes();
+
+    if ((int64_t)blockIdx.x < n_fetch_wg) {
+        const int64_t F = 4LL * n_fetch_wg;
+        const int64_t n_items = units * cap;
+        int64_t it = (int64_t)blockIdx.x * 4 + wave;
+        int64_t cur_u = -1;
+        uint4 kr[2][4], vr[2][4];
+        // item -> (unit, i, entry); returns the source block pointer or null
+        auto locate = [&](int64_t item, int64_t &u, int &i, int32_t &blk, int32_t &slot) -> bool {
+            u = item / cap;
+            i = (int)(item % cap);
+            const int n_hit = __builtin_amdgcn_readfirstlane(counts[u * 4 + 1]);
+            const int n_att = __builtin_amdgcn_readfirstlane(counts[u * 4 + 0]);
+            if (n_hit + i >= n_att) return false;
+            blk = __builtin_amdgcn_readfirstlane(att_block[u * K + n_hit + i]);
+            slot = __builtin_amdgcn_readfirstlane(att_slot[u * K + n_hit + i]);
+            return true;
+        };
+        int64_t u0;
+        int i0;
+        int32_t blk0 = 0, slot0 = 0;
+        bool have0 = it < n_items && locate(it, u0, i0, blk0, slot0);
+        if (it < n_items && have0) st.load(kr[0], vr[0], host_kv + (u0 * NBmax + blk0) * W::BLK);
+        int buf = 0;
+        for (; it < n_items; it += F) {
+            // prefetch the next item while this one is processed
+            const int64_t nx = it + F;
+            int64_t u1 = 0;
+            int i1 = 0;
+            int32_t blk1 = 0, slot1 = 0;
+            const bool have1 = nx < n_items && locate(nx, u1, i1, blk1, slot1);
+            if (have1) {
+                if (buf == 0) st.load(kr[1], vr[1], host_kv + (u1 * NBmax + blk1) * W::BLK);
+                else st.load(kr[0], vr[0], host_kv + (u1 * NBmax + blk1) * W::BLK);
+            }
+            __builtin_amdgcn_sched_barrier(0);  // keep the prefetch ahead of the compute
+            if (u0 != cur_u) {
+                const int64_t b = u0 / Hkv;
+                st.init(q, b, Hq, (int)(u0 % Hkv));
+                cur_u = u0;
+            } else {
+                st.reset();
+            }
+            if (have0) {
+                uint16_t *dst = slots + (u0 * S + slot0) * (int64_t)W::BLK;
+                if (buf == 0) {
+                    st.store(dst, kr[0], vr[0]);
+                    st.block(kr[0], vr[0], block_valid(T_, blk0), scale_log2);
+                } else {
+                    st.store(dst, kr[1], vr[1]);
+                    st.block(kr[1], vr[1], block_valid(T_, blk0), scale_log2);
+                }
+            }
+            st.reduce();
+            st.write_partial((u0 * nsa + i0) * G, part_m, part_l, part_acc);
+            u0 = u1;
+            i0 = i1;
+            blk0 = blk1;
+            slot0 = slot1;
+            have0 = have1;
+            buf ^= 1;
+        }
+        return;
+    }
+
+    __shared__ float sm_m[4][16], sm_l[4][16];
+    __shared__ float sm_acc[4][G][D];
+    const int64_t g = (int64_t)blockIdx.x - n_fetch_wg;
+    const int64_t u = g / ns1;
+    const int s = (int)(g % ns1);
+    const int e_end = __builtin_amdgcn_readfirstlane(mode == 1 ? counts[u * 4 + 1] : counts[u * 4 + 0]);
+    const int e_first = 4 * BPW * s + wave;
+    st.init(q, u / Hkv, Hq, (int)(u % Hkv));
+    const int ne = e_first >= e_end ? 0 : (e_end - e_first + 3) / 4 < BPW ? (e_end - e_first + 3) / 4 : BPW;
+
+    uint4 kr[2][4], vr[2][4];
+    int32_t blk_cur = 0;
+    if (ne > 0) {
+        blk_cur = __builtin_amdgcn_readfirstlane(att_block[u * K + e_first]);
+        const int32_t sl = __builtin_amdgcn_readfirstlane(att_slot[u * K + e_first]);
+        st.load(kr[0], vr[0], slots + (u * S + sl) * (int64_t)W::BLK);
+    }
+#pragma unroll
+    for (int j = 0; j < BPW; ++j) {
+        if (j >= ne) break;
+        int32_t blk_nx = 0;
+        if (j + 1 < ne) {
+            const int e = e_first + 4 * (j + 1);
+            blk_nx = __builtin_amdgcn_readfirstlane(att_block[u * K + e]);
+            const int32_t sl = __builtin_amdgcn_readfirstlane(att_slot[u * K + e]);
+            st.load(kr[(j + 1) & 1], vr[(j + 1) & 1], slots + (u * S + sl) * (int64_t)W::BLK);
+        }
+        __builtin_amdgcn_sched_barrier(0);  // keep the prefetch ahead of the compute
+        st.block(kr[j & 1], vr[j & 1], block_valid(T_, blk_cur), scale_log2);
+        blk_cur = blk_nx;
+    }
+    st.reduce();
+    if (st.kg == 0) {
+#pragma unroll
+        for (int gg = 0; gg < G; ++gg)
+#pragma unroll
+            for (int e = 0; e < 8; ++e) sm_acc[wave][gg][8 * st.col + e] = st.acc[gg][e];
+        sm_m[wave][st.col] = st.m;
+        sm_l[wave][st.col] = st.lsum;
     }
     __syncthreads();
 
-    // merge the four waves into this split's partial
+    // merge the four waves into this workgroup's partial
     for (int idx = threadIdx.x; idx < G * D; idx += 256) {
-        const int g = idx / D, c = idx % D;
+        const int gg = idx / D, c = idx % D;
         float M = -INFINITY;
 #pragma unroll
-        for (int w = 0; w < 4; ++w) M = fmaxf(M, sm_m[w][g]);
+        for (int w = 0; w < 4; ++w) M = fmaxf(M, sm_m[w][gg]);
         float a = 0.f, L = 0.f;
         if (M != -INFINITY) {
 #pragma unroll
             for (int w = 0; w < 4; ++w) {
-                const float wt = exp2f(sm_m[w][g] - M);
-                a += wt * sm_acc[w][g][c];
-                L += wt * sm_l[w][g];
+                const float wt = exp2f(sm_m[w][gg] - M);
+                a += wt * sm_acc[w][gg][c];
+                L += wt * sm_l[w][gg];
             }
         }
-        const int64_t pi = (u * n_splits + split) * G + g;
+        const int64_t pi = (u * nsa + nsf_max + s) * G + gg;
         part_acc[pi * D + c] = a;
         if (c == 0) {
             part_m[pi] = M;
@@ -249,29 +393,35 @@ __global__ __launch_bounds__(256) void attn_mfma_kernel(
 
 // ---------------------------------------------------------------- combine
 
-// One workgroup per (b, query head); thread c owns output dimension c.
+// One workgroup per (b, query head); thread c owns output dimension c.  The
+// partials of a unit are splits [0, n_a) and [off_b, off_b + n_b) of nsa.
 __global__ __launch_bounds__(256) void combine_kernel(const float *__restrict__ part_m,
                                                       const float *__restrict__ part_l,
                                                       const float *__restrict__ part_acc,
                                                       float *__restrict__ out, int Hq, int Hkv,
-                                                      int G, int d, int n_splits) {
+                                                      int G, int d, int nsa, int n_a, int off_b,
+                                                      int n_b) {
     const int qh = blockIdx.x, b = blockIdx.y;
     const int h = qh / G, g = qh % G;
     const int64_t u = (int64_t)b * Hkv + h;
-    const int64_t base = u * n_splits * G + g;  // partial index of split s: base + s * G
+    const int n = n_a + n_b;
+    auto pidx = [&](int i) -> int64_t {
+        const int s = i < n_a ? i : off_b + (i - n_a);
+        return (u * nsa + s) * G + g;
+    };
     float M = -INFINITY;
-    for (int s = 0; s < n_splits; ++s) M = fmaxf(M, part_m[base + (int64_t)s * G]);
+    for (int i = 0; i < n; ++i) M = fmaxf(M, part_m[pidx(i)]);
     float L = 0.f;
     if (M != -INFINITY)
-        for (int s = 0; s < n_splits; ++s) {
-            const int64_t pi = base + (int64_t)s * G;
+        for (int i = 0; i < n; ++i) {
+            const int64_t pi = pidx(i);
             L += exp2f(part_m[pi] - M) * part_l[pi];
         }
     for (int c = threadIdx.x; c < d; c += blockDim.x) {
         float a = 0.f;
         if (M != -INFINITY)
-            for (int s = 0; s < n_splits; ++s) {
-                const int64_t pi = base + (int64_t)s * G;
+            for (int i = 0; i < n; ++i) {
+                const int64_t pi = pidx(i);
                 a += exp2f(part_m[pi] - M) * part_acc[pi * d + c];
             }
         out[((int64_t)b * Hq + qh) * d + c] = (L > 0.f) ? a / L : 0.f;
@@ -294,63 +444,82 @@ AttnPlan plan_attention(const Dims &D) {
         int bpw = 8;
         while (bpw > 1 && units * ((D.K + 4 * bpw - 1) / (4 * bpw)) < 1024) bpw /= 2;
         P.blocks_per_wave = bpw;
-        P.n_splits = (D.K + 4 * bpw - 1) / (4 * bpw);
+        P.ns1 = (D.K + 4 * bpw - 1) / (4 * bpw);
+        P.nsf_max = D.K;
     } else {
         int bps = 8;
         while (bps > 1 && units * ((D.K + bps - 1) / bps) < 1024) bps /= 2;
         P.blocks_per_wave = bps;
-        P.n_splits = (D.K + bps - 1) / bps;
+        P.ns1 = (D.K + bps - 1) / bps;
+        P.nsf_max = 0;
     }
+    P.nsa = P.nsf_max + P.ns1;
     return P;
+}
+
+int attention_fetch_splits(const Dims &D, const AttnPlan &P, int cap) {
+    if (!P.mfma || cap <= 0) return 0;
+    return cap > D.K ? D.K : cap;
+}
+
+// Fetch workgroups for a fused launch: about four items per wave, enough
+// waves in flight to cover the host link's latency, and never more than a
+// small share of the chip.
+static int fetch_workgroups(int64_t items) {
+    int64_t waves = (items + 3) / 4;
+    if (waves < 64) waves = 64;
+    if (waves > 512) waves = 512;
+    int64_t wgs = (waves + 3) / 4;
+    const int64_t max_useful = (items + 3) / 4;
+    if (wgs > max_useful) wgs = max_useful;
+    return (int)(wgs < 1 ? 1 : wgs);
 }
 
 template <int G>
 static void launch_mfma_g(const AttnPlan &P, dim3 grid, hipStream_t st, const uint16_t *q,
-                          const uint16_t *slots, const int32_t *ab, const int32_t *as,
-                          const int32_t *counts, int64_t T, const Dims &D, float sc, float *pm,
-                          float *pl, float *pa) {
+                          uint16_t *slots, const uint16_t *host_kv, const int32_t *ab,
+                          const int32_t *as, const int32_t *counts, int64_t T, const Dims &D,
+                          int mode, int cap, int n_fetch_wg, float sc, float *pm, float *pl,
+                          float *pa) {
+#define OASIS_ATTN(BPW)                                                                        \
+    hipLaunchKernelGGL((attn_mfma_kernel<G, BPW>), grid, dim3(256), 0, st, q, slots, host_kv,  \
+                       ab, as, counts, T, D.Hq, D.Hkv, D.K, D.S, D.NBmax, mode, cap,           \
+                       n_fetch_wg, P.nsf_max, P.ns1, P.nsa, D.units(), sc, pm, pl, pa)
     switch (P.blocks_per_wave) {
-    case 1:
-        hipLaunchKernelGGL((attn_mfma_kernel<G, 1>), grid, dim3(256), 0, st, q, slots, ab, as,
-                           counts, T, D.Hq, D.Hkv, D.K, D.S, P.n_splits, sc, pm, pl, pa);
-        break;
-    case 2:
-        hipLaunchKernelGGL((attn_mfma_kernel<G, 2>), grid, dim3(256), 0, st, q, slots, ab, as,
-                           counts, T, D.Hq, D.Hkv, D.K, D.S, P.n_splits, sc, pm, pl, pa);
-        break;
-    case 4:
-        hipLaunchKernelGGL((attn_mfma_kernel<G, 4>), grid, dim3(256), 0, st, q, slots, ab, as,
-                           counts, T, D.Hq, D.Hkv, D.K, D.S, P.n_splits, sc, pm, pl, pa);
-        break;
-    default:
-        hipLaunchKernelGGL((attn_mfma_kernel<G, 8>), grid, dim3(256), 0, st, q, slots, ab, as,
-                           counts, T, D.Hq, D.Hkv, D.K, D.S, P.n_splits, sc, pm, pl, pa);
-        break;
+    case 1: OASIS_ATTN(1); break;
+    case 2: OASIS_ATTN(2); break;
+    case 4: OASIS_ATTN(4); break;
+    default: OASIS_ATTN(8); break;
     }
+#undef OASIS_ATTN
 }
 
-hipError_t launch_attention(const Dims &D, const AttnPlan &P, const void *q, const void *slots,
-                            const int32_t *att_block, const int32_t *att_slot,
-                            const int32_t *counts, int64_t T, float *part_m, float *part_l,
-                            float *part_acc, hipStream_t st) {
+hipError_t launch_attention(const Dims &D, const AttnPlan &P, int mode, int nsf, const void *q,
+                            void *slots, const void *host_kv, const int32_t *att_block,
+                            const int32_t *att_slot, const int32_t *counts, int64_t T,
+                            float *part_m, float *part_l, float *part_acc, hipStream_t st) {
     const float sc = kLog2e / sqrtf((float)D.d);
-    dim3 grid((unsigned)P.n_splits, D.Hkv, D.B);
     if (P.mfma) {
-        const uint16_t *qq = (const uint16_t *)q, *sl = (const uint16_t *)slots;
+        if (mode == 0) nsf = 0;
+        const int n_fetch_wg = nsf > 0 ? fetch_workgroups(D.units() * nsf) : 0;
+        dim3 grid((unsigned)(n_fetch_wg + D.units() * P.ns1));
+        const uint16_t *qq = (const uint16_t *)q, *hk = (const uint16_t *)host_kv;
+        uint16_t *sl = (uint16_t *)slots;
         switch (D.G) {
-        case 1: launch_mfma_g<1>(P, grid, st, qq, sl, att_block, att_slot, counts, T, D, sc, part_m, part_l, part_acc); break;
-        case 2: launch_mfma_g<2>(P, grid, st, qq, sl, att_block, att_slot, counts, T, D, sc, part_m, part_l, part_acc); break;
-        case 4: launch_mfma_g<4>(P, grid, st, qq, sl, att_block, att_slot, counts, T, D, sc, part_m, part_l, part_acc); break;
-        case 8: launch_mfma_g<8>(P, grid, st, qq, sl, att_block, att_slot, counts, T, D, sc, part_m, part_l, part_acc); break;
-        default: launch_mfma_g<16>(P, grid, st, qq, sl, att_block, att_slot, counts, T, D, sc, part_m, part_l, part_acc); break;
+        case 1: launch_mfma_g<1>(P, grid, st, qq, sl, hk, att_block, att_slot, counts, T, D, mode, nsf, n_fetch_wg, sc, part_m, part_l, part_acc); break;
+        case 2: launch_mfma_g<2>(P, grid, st, qq, sl, hk, att_block, att_slot, counts, T, D, mode, nsf, n_fetch_wg, sc, part_m, part_l, part_acc); break;
+        case 4: launch_mfma_g<4>(P, grid, st, qq, sl, hk, att_block, att_slot, counts, T, D, mode, nsf, n_fetch_wg, sc, part_m, part_l, part_acc); break;
+        case 8: launch_mfma_g<8>(P, grid, st, qq, sl, hk, att_block, att_slot, counts, T, D, mode, nsf, n_fetch_wg, sc, part_m, part_l, part_acc); break;
+        default: launch_mfma_g<16>(P, grid, st, qq, sl, hk, att_block, att_slot, counts, T, D, mode, nsf, n_fetch_wg, sc, part_m, part_l, part_acc); break;
         }
         return hipGetLastError();
     }
+    dim3 grid((unsigned)P.ns1, D.Hkv, D.B);
     const int epl = (D.d + 63) / 64;
 #define OASIS_GENERIC(TT, E)                                                                     \
     hipLaunchKernelGGL((attn_generic_kernel<TT, E>), grid, dim3(64), 0, st, (const TT *)q,       \
                        (const TT *)slots, att_block, att_slot, counts, T, D.Hq, D.Hkv, D.G, D.d, \
-                       D.K, D.S, D.bs, P.blocks_per_wave, P.n_splits, sc, part_m, part_l,        \
+                       D.K, D.S, D.bs, P.blocks_per_wave, P.nsa, P.nsf_max, sc, part_m, part_l,  \
                        part_acc)
     if (D.dtype == kF32) {
         if (epl == 1) OASIS_GENERIC(float, 1);
@@ -365,11 +534,12 @@ hipError_t launch_attention(const Dims &D, const AttnPlan &P, const void *q, con
     return hipGetLastError();
 }
 
-hipError_t launch_combine(const Dims &D, const AttnPlan &P, const float *part_m,
+hipError_t launch_combine(const Dims &D, const AttnPlan &P, int nsf, const float *part_m,
                           const float *part_l, const float *part_acc, float *out,
                           hipStream_t st) {
     hipLaunchKernelGGL(combine_kernel, dim3(D.Hq, D.B), dim3(D.d <= 256 ? D.d : 256), 0, st,
-                       part_m, part_l, part_acc, out, D.Hq, D.Hkv, D.G, D.d, P.n_splits);
+                       part_m, part_l, part_acc, out, D.Hq, D.Hkv, D.G, D.d, P.nsa, nsf,
+                       P.nsf_max, P.ns1);
     return hipGetLastError();
 }
 

@@ -54,6 +54,19 @@ template <typename T> __device__ __forceinline__ void st16(T *p, const Vec16<T> 
     *reinterpret_cast<uint4 *>(p) = __builtin_bit_cast(uint4, x);
 }
 
+// 16-byte global-memory access through an explicit global address space, so
+// pointers picked at run time (slot or pinned host block) still compile to
+// global_load / global_store rather than flat accesses.
+typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+__device__ __forceinline__ uint4 gload16(const void *p) {
+    const u32x4 v = *(const __attribute__((address_space(1))) u32x4 *)p;
+    return make_uint4(v.x, v.y, v.z, v.w);
+}
+__device__ __forceinline__ void gstore16(void *p, uint4 v) {
+    const u32x4 w = {v.x, v.y, v.z, v.w};
+    *(__attribute__((address_space(1))) u32x4 *)p = w;
+}
+
 // Unpack 8 bf16 held in a uint4 into fp32.
 __device__ __forceinline__ void bf16x8_to_f32(const uint4 u, float *o) {
     o[0] = __uint_as_float(u.x << 16);
@@ -88,6 +101,30 @@ __device__ __forceinline__ float wave_max(float v) {
 #pragma unroll
     for (int o = 32; o > 0; o >>= 1) v = fmaxf(v, __shfl_xor(v, o, 64));
     return v;
+}
+
+// Wave64 reductions of 32-bit integers through DPP: an inclusive scan inside
+// each 16-lane row (row_shr 1, 2, 4, 8), then the four row totals are read
+// from lanes 15, 31, 47, 63.  The result is wave-uniform.
+template <typename Op> __device__ __forceinline__ uint32_t wave_reduce_u32(uint32_t v, uint32_t id, Op op) {
+    v = op(v, (uint32_t)__builtin_amdgcn_update_dpp((int)id, (int)v, 0x111, 0xF, 0xF, false));
+    v = op(v, (uint32_t)__builtin_amdgcn_update_dpp((int)id, (int)v, 0x112, 0xF, 0xF, false));
+    v = op(v, (uint32_t)__builtin_amdgcn_update_dpp((int)id, (int)v, 0x114, 0xF, 0xF, false));
+    v = op(v, (uint32_t)__builtin_amdgcn_update_dpp((int)id, (int)v, 0x118, 0xF, 0xF, false));
+    const uint32_t r0 = (uint32_t)__builtin_amdgcn_readlane((int)v, 15);
+    const uint32_t r1 = (uint32_t)__builtin_amdgcn_readlane((int)v, 31);
+    const uint32_t r2 = (uint32_t)__builtin_amdgcn_readlane((int)v, 47);
+    const uint32_t r3 = (uint32_t)__builtin_amdgcn_readlane((int)v, 63);
+    return op(op(r0, r1), op(r2, r3));
+}
+__device__ __forceinline__ uint32_t wave_add_u32(uint32_t v) {
+    return wave_reduce_u32(v, 0u, [](uint32_t a, uint32_t b) { return a + b; });
+}
+__device__ __forceinline__ uint32_t wave_max_u32(uint32_t v) {
+    return wave_reduce_u32(v, 0u, [](uint32_t a, uint32_t b) { return a > b ? a : b; });
+}
+__device__ __forceinline__ uint32_t wave_min_u32(uint32_t v) {
+    return wave_reduce_u32(v, 0xFFFFFFFFu, [](uint32_t a, uint32_t b) { return a < b ? a : b; });
 }
 
 // Lanes below this one in the wave (for ordered compaction with ballots).

@@ -16,7 +16,7 @@
 
 namespace oasis {
 
-typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+
 
 template <int PER_THREAD>
 __global__ __launch_bounds__(256) void gather_kernel(const u32x4 *__restrict__ host_kv,

@@ -47,6 +47,14 @@ hipError_t launch_gather(const Dims &D, const void *host_kv, void *slots, const 
                          const int32_t *slot_ids, int list_stride, const int32_t *counts,
                          int count_stride, int count_index, int max_n, hipStream_t st);
 
+// Top-K and diff / cap / LRU of every unit in one kernel (the ids are also
+// written to ids).
+hipError_t launch_topk_select(const Dims &D, const float *scores, int64_t NB, int32_t *ids,
+                              int32_t *slot_block, int32_t *last_used, int32_t *block_slot,
+                              int cap, int32_t t, int32_t *fetch_block, int32_t *fetch_slot,
+                              int32_t *att_block, int32_t *att_slot, int32_t *counts,
+                              DevStats *stats, uint32_t *err, hipStream_t st);
+
 // Forced non-residency: unit u drops blocks[u * max_per_unit + i], i < counts[u].
 hipError_t launch_evict(const Dims &D, const int32_t *blocks, const int32_t *counts,
                         int max_per_unit, int32_t *slot_block, int32_t *block_slot,
@@ -56,18 +64,28 @@ hipError_t launch_evict(const Dims &D, const int32_t *blocks, const int32_t *cou
 hipError_t launch_rebuild_block_slot(const Dims &D, const int32_t *slot_block,
                                      int32_t *block_slot, hipStream_t st);
 
-// Split-K sparse attention partials and their combination.
+// Split-K sparse attention partials and their combination.  Partials of a
+// unit are indexed [0, nsa): fetch splits at [0, nsf), hit splits at
+// [nsf_max, nsf_max + ns1).
 struct AttnPlan {
-    int n_splits;          // splits per unit
-    int blocks_per_wave;   // attended blocks per wave (MFMA kernel: 4 waves per split)
-    bool mfma;
+    bool mfma;             // bf16, d = 128, block 16, G in {1, 2, 4, 8, 16}
+    int blocks_per_wave;   // hit entries per wave (MFMA: 4 waves per split)
+    int ns1;               // hit splits per unit
+    int nsf_max;           // fetch splits per unit at cap = K (MFMA only)
+    int nsa;               // partial stride per unit
 };
 AttnPlan plan_attention(const Dims &D);
-hipError_t launch_attention(const Dims &D, const AttnPlan &P, const void *q, const void *slots,
-                            const int32_t *att_block, const int32_t *att_slot,
-                            const int32_t *counts, int64_t T, float *part_m, float *part_l,
-                            float *part_acc, hipStream_t st);
-hipError_t launch_combine(const Dims &D, const AttnPlan &P, const float *part_m,
-                          const float *part_l, const float *part_acc, float *out, hipStream_t st);
+// Fetch splits for a cap (fused mode), 0 when the kernel cannot fuse.
+int attention_fetch_splits(const Dims &D, const AttnPlan &P, int cap);
+// mode 0: every attended entry from its slot.  mode 1 (MFMA only): entries
+// [n_hit, n_att) are read from the host KV and written into their slots in
+// the same kernel, using nsf fetch splits.
+hipError_t launch_attention(const Dims &D, const AttnPlan &P, int mode, int nsf, const void *q,
+                            void *slots, const void *host_kv, const int32_t *att_block,
+                            const int32_t *att_slot, const int32_t *counts, int64_t T,
+                            float *part_m, float *part_l, float *part_acc, hipStream_t st);
+hipError_t launch_combine(const Dims &D, const AttnPlan &P, int nsf, const float *part_m,
+                          const float *part_l, const float *part_acc, float *out,
+                          hipStream_t st);
 
 }  // namespace oasis

@@ -96,6 +96,11 @@ __global__ __launch_bounds__(256) void score_mfma_kernel(const uint16_t *__restr
                                                          int B, int Hq, int Hkv, int G,
                                                          int64_t NBmax, int64_t NB) {
     constexpr int NI = D / 8;  // MFMA steps: 16 k each, 8 from each half
+    // One tile of 32 summaries is 16 KB per wave.  With one query tile the
+    // next tile is loaded while the current one is multiplied (two register
+    // buffers); with more query tiles the registers hold a single buffer whose
+    // loads are all issued before the first multiply.
+    constexpr bool kDouble = QT == 1;
     const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
     const int h = blockIdx.y, b = blockIdx.z;
     const int64_t u = (int64_t)b * Hkv + h;
@@ -121,15 +126,16 @@ __global__ __launch_bounds__(256) void score_mfma_kernel(const uint16_t *__restr
     const int64_t ntiles = (NB + 31) / 32;
     const uint16_t *base = summ + u * NBmax * 2 * D + half * D;
     float *out = scores + u * NBmax;
-    for (int64_t tile = (int64_t)blockIdx.x * 4 + wave; tile < ntiles;
-         tile += (int64_t)gridDim.x * 4) {
+    const int64_t stride = (int64_t)gridDim.x * 4;
+
+    auto load = [&](bf16x8(&bv)[NI], int64_t tile) {
         const int64_t j = tile * 32 + m;
-        const int64_t jj = j < NB ? j : NB - 1;
-        const uint16_t *src = base + jj * 2 * D;
-        bf16x8 bv[NI];
+        const uint16_t *src = base + (j < NB ? j : NB - 1) * 2 * D;
 #pragma unroll
         for (int i = 0; i < NI; ++i)
             bv[i] = __builtin_bit_cast(bf16x8, *reinterpret_cast<const uint4 *>(src + 8 * i));
+    };
+    auto compute = [&](const bf16x8(&bv)[NI], int64_t tile) {
         float best = -INFINITY;
 #pragma unroll
         for (int t = 0; t < QT; ++t) {
@@ -141,7 +147,35 @@ __global__ __launch_bounds__(256) void score_mfma_kernel(const uint16_t *__restr
             for (int r = 0; r < 16; ++r) best = fmaxf(best, acc[r]);
         }
         best = fmaxf(best, __shfl_xor(best, 32, 64));
+        const int64_t j = tile * 32 + m;
         if (half == 0 && j < NB) out[j] = best;
+    };
+
+    int64_t t0 = (int64_t)blockIdx.x * 4 + wave;
+    if (t0 >= ntiles) return;
+    if constexpr (kDouble) {
+        bf16x8 ba[NI], bb[NI];
+        load(ba, t0);
+        while (true) {
+            const int64_t t1 = t0 + stride;
+            if (t1 < ntiles) load(bb, t1);
+            __builtin_amdgcn_sched_barrier(0);
+            compute(ba, t0);
+            if (t1 >= ntiles) break;
+            const int64_t t2 = t1 + stride;
+            if (t2 < ntiles) load(ba, t2);
+            __builtin_amdgcn_sched_barrier(0);
+            compute(bb, t1);
+            if (t2 >= ntiles) break;
+            t0 = t2;
+        }
+    } else {
+        bf16x8 bv[NI];
+        for (; t0 < ntiles; t0 += stride) {
+            load(bv, t0);
+            __builtin_amdgcn_sched_barrier(0);
+            compute(bv, t0);
+        }
     }
 }
 

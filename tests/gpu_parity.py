@@ -251,3 +251,102 @@ class Parity:
             report["attn_err"] = max(report["attn_err"], self.check_out(t, rec))
             report["steps"] = t
         return report
+
+
+class FreeRunning(Parity):
+    """The GPU runs on its own scores with the fused top-K + select.  Each step
+    is checked kernel by kernel: scores against the oracle's, the ids against
+    the oracle top-K of the GPU's own fp32 scores, the select outputs against
+    the oracle select applied to the GPU's previous tables, and the attention
+    against the oracle attention over the GPU's attended list."""
+
+    def _tables(self):
+        h = self.run.h
+        S = h.slots
+        sb, lu = h.read("SLOT_BLOCK"), h.read("LAST_USED")
+        return {(b, hh): (self._unit_slice(sb, b, hh, S).copy(),
+                          self._unit_slice(lu, b, hh, S).copy()) for (b, hh) in self.units}
+
+    def run_free(self, steps=None, check_payload_every=8):
+        w, run, h = self.w, self.run, self.run.h
+        steps = self.n_steps if steps is None else steps
+        K = h.k_blocks
+        report = dict(score_err=0.0, attn_err=0.0, steps=0, fetched=0)
+        if w.admission:
+            run.admission()
+            torch.cuda.synchronize()
+            for (b, hh) in self.units:
+                self.oru[(b, hh)].slot_block[:] = -1
+        prev = self._tables()
+        draft_cache = {}
+        for t in range(1, steps + 1):
+            if w.forced_evict_frac > 0:
+                ab, cnt = h.read("ATT_BLOCK"), h.read("COUNTS")
+                draws = synth.evict_draws(w, t, self.layer)
+                blocks = np.full((w.batch * w.kv_heads, K), -1, np.int32)
+                counts = np.zeros(w.batch * w.kv_heads, np.int32)
+                for u in range(w.batch * w.kv_heads):
+                    na = int(cnt[u * 4])
+                    ev = synth.forced_evictions(w, ab[u * K:u * K + na], na,
+                                                draws[u // w.kv_heads, u % w.kv_heads])
+                    blocks[u, :len(ev)] = ev
+                    counts[u] = len(ev)
+                    key = (u // w.kv_heads, u % w.kv_heads)
+                    if key in prev:
+                        sb0 = prev[key][0]
+                        for blk in ev:
+                            sb0[sb0 == blk] = -1
+                h.oasis_evict(blocks, counts)
+            h.oasis_append_kv(run.app_k[t - 1], run.app_v[t - 1])
+            h.oasis_predict(run.q, run.drafts[t], w.drafts, scores=self.scores_dev)
+            h.oasis_select_and_fetch(self.cap)
+            h.oasis_sparse_attn(run.q, run.out)
+            torch.cuda.synchronize()
+            h.oasis_check()
+            gpu_scores = self.scores_dev.cpu().numpy()
+            ids = h.read("IDS")
+            fb, fs = h.read("FETCH_BLOCK"), h.read("FETCH_SLOT")
+            ab, ast = h.read("ATT_BLOCK"), h.read("ATT_SLOT")
+            cnt = h.read("COUNTS")
+            out = run.out.cpu().numpy()
+            drafts = oracle.to_f64(synth.drafts(w, t, self.layer), w.dtype)
+            now = self._tables()
+            for (b, hh) in self.units:
+                tag = f"free step {t} unit {(b, hh)}"
+                unit = self.oru[(b, hh)]
+                unit.append()
+                x, cur = oracle.unit_rows(self.qf, drafts, b, hh, self.G)
+                ref = unit.score(x)
+                nb = unit.nb
+                err = np.abs(gpu_scores[b, hh, :nb].astype(np.float64) - ref) / score_scale(unit, x)
+                report["score_err"] = max(report["score_err"], float(err.max()))
+                assert err.max() <= SCORE_TOL, tag + f" score err {err.max():.3g}"
+                exp_ids = oracle.topk(gpu_scores[b, hh, :nb], K)
+                got_ids = self._unit_slice(ids, b, hh, K)
+                assert np.array_equal(got_ids, exp_ids), tag + " ids"
+                sb0, lu0 = prev[(b, hh)]
+                r = oracle.select(sb0.copy(), lu0.copy(), exp_ids, self.cap, t)
+                sb_exp, lu_exp = sb0.copy(), lu0.copy()
+                oracle.select(sb_exp, lu_exp, exp_ids, self.cap, t)
+                c = self._unit_slice(cnt, b, hh, 4)
+                na, nh, nf = int(c[0]), int(c[1]), int(c[2])
+                assert (na, nh, nf) == (len(r["att_block"]), r["n_hit"], len(r["fetch_block"])), tag
+                assert np.array_equal(self._unit_slice(fb, b, hh, K)[:nf], r["fetch_block"]), tag
+                assert np.array_equal(self._unit_slice(fs, b, hh, K)[:nf], r["fetch_slot"]), tag
+                assert np.array_equal(self._unit_slice(ab, b, hh, K)[:na], r["att_block"]), tag
+                assert np.array_equal(self._unit_slice(ast, b, hh, K)[:na], r["att_slot"]), tag
+                assert np.array_equal(now[(b, hh)][0], sb_exp), tag + " slot_block"
+                assert np.array_equal(now[(b, hh)][1], lu_exp), tag + " last_used"
+                exp_out = oracle.attention(cur, unit.keys, unit.vals, w.dtype, w.block_size,
+                                           unit.T, r["att_block"])
+                g0 = hh * self.G
+                e = float(np.max(np.abs(out[b, g0:g0 + self.G].astype(np.float64) - exp_out)))
+                report["attn_err"] = max(report["attn_err"], e)
+                assert e <= ATTN_TOL, tag + f" attention err {e:.3g}"
+                report["fetched"] += nf
+            if t % check_payload_every == 0 or t == steps:
+                self.check_payload(t)
+                self.check_summary()
+            prev = now
+            report["steps"] = t
+        return report

@@ -47,3 +47,55 @@ def test_group_sizes_reduced_context(q_heads, kv_heads):
     units = [(0, 0), (1, kv_heads - 1)]
     p = Parity(w, 6, units)
     log(f"G={q_heads // kv_heads}: {p.run_all()}")
+
+
+# ------------------------------------------------------------------ full-size workloads
+# Every step of the workload through the C-ABI at its real shape, compared on a
+# sample of (batch row, KV head) units that the oracle recomputes one by one.
+
+def test_qwen3_8b_layer_full_size_sampled_units():
+    Parity, log = _parity()
+    w = synth.QWEN3_8B
+    p = Parity(w, w.steps, [(0, 0), (17, 5), (31, 7)])
+    rep = p.run_all(check_payload_every=8)
+    log(f"{w.name}: {rep}")
+
+
+def test_llama31_8b_long_context_full_size_sampled_units():
+    Parity, log = _parity()
+    w = synth.LLAMA31_8B_LONG
+    p = Parity(w, w.steps, [(0, 3), (5, 0), (7, 7)])
+    rep = p.run_all(check_payload_every=8)
+    log(f"{w.name}: {rep}")
+
+
+def test_qwen3_32b_forced_eviction_full_size_sampled_units():
+    Parity, log = _parity()
+    w = synth.QWEN3_32B
+    p = Parity(w, w.steps, [(0, 0), (9, 4), (15, 7)])
+    rep = p.run_all(check_payload_every=16)
+    log(f"{w.name}: {rep}")
+
+
+# ------------------------------------------------------------------ free-running
+# The GPU selects on its own scores with the fused top-K + select kernel;
+# every step is checked against the oracle functions applied to its state.
+
+def test_tiny_workload_free_running():
+    from tests.gpu_parity import FreeRunning, log
+    w = synth.TINY
+    log(f"tiny free: {FreeRunning(w, w.steps, [(0, 0), (0, 1)]).run_free()}")
+
+
+def test_qwen3_8b_layer_free_running_sampled_units():
+    from tests.gpu_parity import FreeRunning, log
+    w = synth.QWEN3_8B
+    rep = FreeRunning(w, 24, [(0, 0), (13, 2), (31, 7)]).run_free(check_payload_every=8)
+    log(f"{w.name} free: {rep}")
+
+
+def test_qwen3_32b_free_running_with_forced_evictions():
+    from tests.gpu_parity import FreeRunning, log
+    w = synth.QWEN3_32B
+    rep = FreeRunning(w, 16, [(0, 0), (7, 5), (15, 7)]).run_free(check_payload_every=4)
+    log(f"{w.name} free: {rep}")
