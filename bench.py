@@ -110,6 +110,9 @@ def main():
                     choices=sorted(_workloads()))
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-h2d-peak", action="store_true")
+    ap.add_argument("--copy-calibration", type=int, default=0, metavar="MIB",
+                    help="only run a plain device-to-device copy of this many MiB five times "
+                         "(reference for the HBM byte counters) and exit")
     ap.add_argument("--no-kernel-timing", action="store_true",
                     help="skip the per-kernel HIP events (roofline fields become null)")
     args = ap.parse_args()
@@ -120,6 +123,16 @@ def main():
 
     import numpy as np
     import torch
+
+    if args.copy_calibration:
+        n = args.copy_calibration << 20
+        src = torch.ones(n, dtype=torch.uint8, device="cuda")
+        dst = torch.empty_like(src)
+        for _ in range(5):
+            dst.copy_(src)
+        torch.cuda.synchronize()
+        print(json.dumps({"copy_calibration_bytes": n, "launches": 5}))
+        return
 
     import synth
     from lookahead_sparse_kv_oasis_amd.runner import LayerRunner

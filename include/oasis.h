@@ -71,7 +71,8 @@ typedef struct {
     int32_t head_dim;       /* d; multiple of 8, at most 256 */
     int32_t dtype;          /* OASIS_F32 or OASIS_BF16 */
     int32_t max_drafts;     /* largest n_drafts passed to oasis_predict */
-    int32_t slots_per_head; /* HBM block slots per (b, KV head); 0 -> budget blocks; >= budget blocks */
+    int32_t slots_per_head; /* HBM block slots per (b, KV head); 0 -> budget blocks;
+                               budget blocks <= slots <= 2048 */
     int32_t reserved;
     int64_t max_tokens;     /* capacity of the host KV per sequence */
 } oasis_layout;
@@ -80,7 +81,8 @@ typedef struct oasis_handle oasis_t;
 
 /* Create a handle for one layer.  block_size: tokens per KV block (the
  * paging unit, 1..64).  budget_tokens: the KV budget per (b, KV head); the
- * top-K takes K = budget_tokens / block_size blocks.  fetch_ratio: default
+ * top-K takes K = budget_tokens / block_size blocks (1..1024).  At most
+ * 65536 blocks per sequence.  fetch_ratio: default
  * cap per (b, KV head) and step = max(1, floor(ratio * K)) (see
  * oasis_cap_from_ratio), used when oasis_select_and_fetch gets cap < 0.
  * Allocates the pinned host KV [B][Hkv][NBmax][K|V][block_size][d], the HBM

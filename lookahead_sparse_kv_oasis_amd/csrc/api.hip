@@ -294,7 +294,7 @@ extern "C" int oasis_create(const oasis_layout *layout, int32_t block_size, int3
     const int S = L.slots_per_head > 0 ? L.slots_per_head : K;
     const int G = L.num_q_heads / L.num_kv_heads;
     const int64_t NBmax = (L.max_tokens + block_size - 1) / block_size;
-    if (K > 1024 || S < K || S > 8192 || NBmax > 65536) return OASIS_E_INVAL;
+    if (K > 1024 || S < K || S > 2048 || NBmax > 65536) return OASIS_E_INVAL;
     const int Q = G * (1 + L.max_drafts);
     if ((int64_t)Q * L.head_dim * 4 > 64 * 1024) return OASIS_E_INVAL;
 

@@ -79,7 +79,8 @@ AttnPlan plan_attention(const Dims &D);
 int attention_fetch_splits(const Dims &D, const AttnPlan &P, int cap);
 // mode 0: every attended entry from its slot.  mode 1 (MFMA only): entries
 // [n_hit, n_att) are read from the host KV and written into their slots in
-// the same kernel, using nsf fetch splits.
+// the same kernel, using nsf fetch splits.  launch_combine merges the
+// partials into the output.
 hipError_t launch_attention(const Dims &D, const AttnPlan &P, int mode, int nsf, const void *q,
                             void *slots, const void *host_kv, const int32_t *att_block,
                             const int32_t *att_slot, const int32_t *counts, int64_t T,

@@ -13,6 +13,9 @@
 // For bf16 that contraction runs on the matrix cores: x+ and x- are exact
 // bf16 values, bf16 x bf16 products are exact in fp32, and the fp32
 // accumulation is the only rounding.
+#include <stdlib.h>
+#include <string.h>
+
 #include "kernels.h"
 
 namespace oasis {
@@ -179,6 +182,109 @@ __global__ __launch_bounds__(256) void score_mfma_kernel(const uint16_t *__restr
     }
 }
 
+// LDS-staged variant (D = 128, one query tile).  A wave's tile of 32 block
+// summaries is 16 KB of contiguous HBM; it is read with fully coalesced
+// 16-byte loads (1 KB per instruction) into registers, written to a
+// wave-private LDS buffer whose 512-byte rows are padded to 528 bytes (so the
+// operand reads below hit 16 distinct banks per 16 lanes), and read back in
+// the MFMA operand layout.  The next tile's global loads are in flight while
+// the current tile is multiplied.
+constexpr int kScoreRowPad = 528;                  // bytes per padded summary row
+constexpr int kScoreTileLds = 32 * kScoreRowPad;   // bytes per wave
+
+__global__ __launch_bounds__(256) void score_mfma_lds_kernel(const uint16_t *__restrict__ summ,
+                                                             const uint16_t *__restrict__ q,
+                                                             const uint16_t *__restrict__ drafts,
+                                                             int n_drafts,
+                                                             float *__restrict__ scores, int B,
+                                                             int Hq, int Hkv, int G,
+                                                             int64_t NBmax, int64_t NB) {
+    constexpr int D = 128, NI = D / 8;
+    extern __shared__ __attribute__((aligned(16))) unsigned char score_lds[];
+    const int lane = threadIdx.x & 63;
+    const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+    const int h = blockIdx.y, b = blockIdx.z;
+    const int64_t u = (int64_t)b * Hkv + h;
+    const int Q = G * (1 + n_drafts);
+    const int m = lane & 31, half = lane >> 5;
+    unsigned char *buf = score_lds + wave * kScoreTileLds;
+
+    bf16x8 a[NI];
+    {
+        int r = m;
+        if (r >= Q) r = 0;
+        const int src = r / G, g = r % G;
+        const uint16_t *x = src == 0
+                                ? q + ((int64_t)b * Hq + h * G + g) * D
+                                : drafts + (((int64_t)(src - 1) * B + b) * Hq + h * G + g) * D;
+#pragma unroll
+        for (int i = 0; i < NI; ++i) {
+            const uint4 w = *reinterpret_cast<const uint4 *>(x + 8 * i);
+            a[i] = __builtin_bit_cast(bf16x8, keep_sign(w, half != 0));
+        }
+    }
+
+    const int64_t ntiles = (NB + 31) / 32;
+    const unsigned char *base = reinterpret_cast<const unsigned char *>(summ + u * NBmax * 2 * D);
+    const int64_t ubytes = NB * 2 * D * 2;  // valid summary bytes of this unit
+    float *out = scores + u * NBmax;
+    const int64_t stride = (int64_t)gridDim.x * 4;
+
+    // coalesced: instruction k, lane l -> tile byte 1024 k + 16 l
+    auto gload = [&](uint4 (&r)[16], int64_t tile) {
+        const int64_t t0 = tile * 32 * 512;
+#pragma unroll
+        for (int k = 0; k < 16; ++k) {
+            int64_t off = t0 + 1024 * k + 16 * lane;
+            if (off >= ubytes) off = ubytes - 16;  // ragged last tile: stay in bounds
+            r[k] = gload16(base + off);
+        }
+    };
+    auto lds_store = [&](const uint4 (&r)[16]) {
+#pragma unroll
+        for (int k = 0; k < 16; ++k) {
+            const int o = 1024 * k + 16 * lane;
+            *reinterpret_cast<uint4 *>(buf + (o >> 9) * kScoreRowPad + (o & 511)) = r[k];
+        }
+    };
+    auto compute = [&](int64_t tile) {
+        f32x16 acc = {};
+        const unsigned char *row = buf + m * kScoreRowPad + half * 256;
+#pragma unroll
+        for (int i = 0; i < NI; ++i) {
+            const uint4 w = *reinterpret_cast<const uint4 *>(row + 16 * i);
+            acc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a[i], __builtin_bit_cast(bf16x8, w), acc,
+                                                          0, 0, 0);
+        }
+        float best = acc[0];
+#pragma unroll
+        for (int r = 1; r < 16; ++r) best = fmaxf(best, acc[r]);
+        best = fmaxf(best, __shfl_xor(best, 32, 64));
+        const int64_t j = tile * 32 + m;
+        if (half == 0 && j < NB) out[j] = best;
+    };
+    auto wave_lds_sync = [] {
+        __builtin_amdgcn_fence(__ATOMIC_SEQ_CST, "workgroup");
+        __builtin_amdgcn_wave_barrier();
+    };
+
+    int64_t t = (int64_t)blockIdx.x * 4 + wave;
+    if (t >= ntiles) return;
+    uint4 r[16];
+    gload(r, t);
+    while (true) {
+        lds_store(r);
+        wave_lds_sync();
+        const int64_t nx = t + stride;
+        if (nx < ntiles) gload(r, nx);
+        __builtin_amdgcn_sched_barrier(0);
+        compute(t);
+        wave_lds_sync();  // all lanes done reading before the next store
+        if (nx >= ntiles) break;
+        t = nx;
+    }
+}
+
 template <int D>
 static void launch_mfma(int QT, dim3 grid, hipStream_t st, const uint16_t *summ,
                         const uint16_t *q, const uint16_t *dr, int nd, float *scores,
@@ -200,6 +306,10 @@ static void launch_mfma(int QT, dim3 grid, hipStream_t st, const uint16_t *summ,
 hipError_t launch_score(const Dims &D, const void *summ, const void *q, const void *drafts,
                         int n_drafts, int64_t NB, float *scores, bool use_mfma, hipStream_t st) {
     if (NB <= 0) return hipSuccess;
+    static const bool lds_staged = [] {
+        const char *e = getenv("OASIS_SCORE_IMPL");
+        return !(e && !strcmp(e, "mfma_direct"));
+    }();
     const int Q = D.G * (1 + n_drafts);
     if (use_mfma) {
         const int QT = (Q + 31) / 32;
@@ -211,6 +321,11 @@ hipError_t launch_score(const Dims &D, const void *summ, const void *q, const vo
         dim3 grid((unsigned)per_unit, D.Hkv, D.B);
         const uint16_t *s = (const uint16_t *)summ, *qq = (const uint16_t *)q,
                        *dr = (const uint16_t *)drafts;
+        if (D.d == 128 && QT == 1 && lds_staged) {
+            hipLaunchKernelGGL(score_mfma_lds_kernel, grid, dim3(256), 4 * kScoreTileLds, st, s, qq,
+                               dr, n_drafts, scores, D.B, D.Hq, D.Hkv, D.G, D.NBmax, NB);
+            return hipGetLastError();
+        }
         if (D.d == 64)
             launch_mfma<64>(QT, grid, st, s, qq, dr, n_drafts, scores, D, NB);
         else if (D.d == 128)

@@ -67,17 +67,26 @@ __device__ __forceinline__ int block_excl_scan(int v, int *sh) {
 
 // Top-K of one unit's scores s[0..NB) into out[0..K) (and out2, out_lds when
 // not null), -1 padded.  Called by every thread of an NT-thread workgroup.
+//
+// Radix select on the order keys: below the common high bits of the largest
+// and smallest key, 8 bits per pass, an LDS histogram of the keys still in
+// play picks the digit holding the K'-th largest key; it stops as soon as a
+// digit's bin holds exactly the keys still needed.  If the bits run out first
+// the bin is one key value tau and the lowest ids among the keys equal to tau
+// fill the rest.
 template <int NT, int CMAX>
 __device__ void topk_unit(const float *__restrict__ s, int NB, int K, int32_t *__restrict__ out,
                           int32_t *__restrict__ out2, int32_t *out_lds,
                           uint32_t *__restrict__ err) {
     constexpr int NW = NT / 64;
-    __shared__ uint32_t red[2][NW];
+    __shared__ uint32_t hist[2][256];
     __shared__ uint32_t red_mx[NW], red_mn[NW];
-    __shared__ int scan_a[NW], scan_b[NW];
-    __shared__ int gt_total;
-    __shared__ uint32_t ckey[kTopkMaxK];
-    __shared__ int32_t cid[kTopkMaxK];
+    __shared__ int pick[2][3];  // digit, keys above the digit's bin, keys in the bin
+    __shared__ int wave_cnt[NW];
+    __shared__ int scan_a[NW];
+    __shared__ __attribute__((aligned(16))) uint32_t ckey[kTopkMaxK];
+    __shared__ __attribute__((aligned(16))) int32_t cid[kTopkMaxK];
+    __shared__ int rank_sh[kTopkMaxK];
 
     const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
     const int Kp = K < NB ? K : NB;
@@ -112,6 +121,7 @@ __device__ void topk_unit(const float *__restrict__ s, int NB, int K, int32_t *_
         red_mx[wave] = lmx;
         red_mn[wave] = lmn;
     }
+    for (int i = tid; i < Kp; i += NT) rank_sh[i] = 0;
     __syncthreads();
     uint32_t kmax = 0u, kmin = 0xFFFFFFFFu;
 #pragma unroll
@@ -120,113 +130,148 @@ __device__ void topk_unit(const float *__restrict__ s, int NB, int K, int32_t *_
         kmin = red_mn[w] < kmin ? red_mn[w] : kmin;
     }
 
-    // Every key lies in [kmin, kmax] and so shares their common high bits; the
-    // K'-th largest key tau is built below that prefix, one bit at a time,
-    // keeping #{key >= tau} >= K'.  Stop as soon as exactly K' keys qualify.
+    // bits at and above `hi` are fixed to those of `prefix`; `need` keys are
+    // still to be taken among the keys that match them
     const uint32_t diff = kmax ^ kmin;
-    const int top = diff ? 31 - __builtin_clz(diff) : -1;
-    uint32_t tau = top < 0 ? kmax : (top == 31 ? 0u : (kmax & ~((2u << top) - 1u)));
+    int hi = diff ? 32 - __builtin_clz(diff) : 0;
+    uint32_t prefix = hi >= 32 ? 0u : (kmax & ~((1u << hi) - 1u));
+    int need = Kp;
     bool exact = false;
-    int pass = 0;
-    for (int bit = top; bit >= 0; --bit, ++pass) {
-        const uint32_t cand = tau | (1u << bit);
-        uint32_t cnt = 0;
-#pragma unroll
-        for (int i = 0; i < CMAX; ++i) cnt += key[i] >= cand ? 1u : 0u;
-        cnt = wave_add_u32(cnt);
-        if (lane == 0) red[pass & 1][wave] = cnt;
+    int cur = 0;
+    while (hi > 0 && !exact) {
+        const int width = hi < 8 ? hi : 8;
+        const int sh = hi - width;
+        const uint32_t fixed = hi >= 32 ? 0u : ~((1u << hi) - 1u);
+        for (int i = tid; i < 256; i += NT) hist[cur][i] = 0u;
         __syncthreads();
-        cnt = 0;
-#pragma unroll
-        for (int w = 0; w < NW; ++w) cnt += red[pass & 1][w];
-        if ((int)cnt >= Kp) {
-            tau = cand;
-            if ((int)cnt == Kp) {
-                exact = true;
-                break;
-            }
-        }
-    }
-
-    // Taken: keys above tau, plus the lowest-id keys equal to tau up to K'.
-    int take_eq = 0, eq_before = 0;
-    if (!exact) {
-        int gt = 0, eq = 0;
 #pragma unroll
         for (int i = 0; i < CMAX; ++i) {
             const int id = begin + i;
-            const bool valid = i < C && id < NB;
-            gt += (valid && key[i] > tau) ? 1 : 0;
-            eq += (valid && key[i] == tau) ? 1 : 0;
+            if (i < C && id < NB && (key[i] & fixed) == prefix)
+                atomicAdd(&hist[cur][(key[i] >> sh) & ((1u << width) - 1u)], 1u);
+        }
+        __syncthreads();
+        if (wave == 0) {
+            // suffix sums over the 256 bins, four per lane, highest digit first
+            uint32_t h[4];
+#pragma unroll
+            for (int j = 0; j < 4; ++j) h[j] = hist[cur][4 * lane + j];
+            const uint32_t mine = h[0] + h[1] + h[2] + h[3];
+            uint32_t suf = mine;  // lanes >= this one
+#pragma unroll
+            for (int o = 1; o < 64; o <<= 1) {
+                const uint32_t y = __shfl_down(suf, o, 64);
+                if (lane + o < 64) suf += y;
+            }
+            uint32_t above = suf - mine;
+#pragma unroll
+            for (int j = 3; j >= 0; --j) {
+                if (above < (uint32_t)need && above + h[j] >= (uint32_t)need) {
+                    pick[cur][0] = 4 * lane + j;
+                    pick[cur][1] = (int)above;
+                    pick[cur][2] = (int)h[j];
+                }
+                above += h[j];
+            }
+        }
+        __syncthreads();
+        const int digit = pick[cur][0];
+        need -= pick[cur][1];
+        prefix |= (uint32_t)digit << sh;
+        hi = sh;
+        exact = pick[cur][2] == need;
+        cur ^= 1;
+    }
+    // selection: keys >= prefix when exact; otherwise keys > tau = prefix and
+    // the `need` lowest-id keys equal to tau
+    const uint32_t tau = prefix;
+    int eq_before = 0;
+    if (!exact) {
+        int eq = 0;
+#pragma unroll
+        for (int i = 0; i < CMAX; ++i) {
+            const int id = begin + i;
+            eq += (i < C && id < NB && key[i] == tau) ? 1 : 0;
         }
         eq_before = block_excl_scan<NT>(eq, scan_a);
-        const int gt_before = block_excl_scan<NT>(gt, scan_b);
-        // total of gt: last thread's exclusive prefix plus its own count
-        if (tid == NT - 1) gt_total = gt_before + gt;
-        __syncthreads();
-        take_eq = Kp - gt_total;
     }
-    int take_local = 0;
+    bool take[CMAX];
+    int my_takes = 0;
     {
         int eq_seen = 0;
 #pragma unroll
         for (int i = 0; i < CMAX; ++i) {
             const int id = begin + i;
+            bool t = false;
             if (i < C && id < NB) {
-                bool take;
                 if (exact) {
-                    take = key[i] >= tau;
+                    t = key[i] >= tau;
                 } else {
-                    take = key[i] > tau;
+                    t = key[i] > tau;
                     if (key[i] == tau) {
-                        take = eq_before + eq_seen < take_eq;
+                        t = eq_before + eq_seen < need;
                         ++eq_seen;
                     }
                 }
-                take_local += take ? 1 : 0;
             }
+            take[i] = t;
+            my_takes += t ? 1 : 0;
         }
     }
-    __syncthreads();  // scan_a is reused below
-    int pos = block_excl_scan<NT>(take_local, scan_a);
-    {
-        int eq_seen = 0;
+    // compaction: wave bases through LDS, lane positions through ballots
+    const uint32_t wt = wave_add_u32((uint32_t)my_takes);
+    if (lane == 0) wave_cnt[wave] = (int)wt;
+    __syncthreads();
+    int pos = 0;
+    for (int w = 0; w < wave; ++w) pos += wave_cnt[w];
 #pragma unroll
-        for (int i = 0; i < CMAX; ++i) {
-            const int id = begin + i;
-            if (i < C && id < NB) {
-                bool take;
-                if (exact) {
-                    take = key[i] >= tau;
-                } else {
-                    take = key[i] > tau;
-                    if (key[i] == tau) {
-                        take = eq_before + eq_seen < take_eq;
-                        ++eq_seen;
-                    }
-                }
-                if (take && pos < kTopkMaxK) {
-                    ckey[pos] = key[i];
-                    cid[pos] = id;
-                    ++pos;
-                }
+    for (int i = 0; i < CMAX; ++i) {
+        const unsigned long long b = __ballot(take[i]);
+        if (take[i]) {
+            const int p = pos + lanes_below(b);
+            if (p < kTopkMaxK) {
+                ckey[p] = key[i];
+                cid[p] = begin + i;
             }
         }
+        pos += __popcll(b);
     }
     __syncthreads();
 
-    // place each winner by counting the winners that order before it
-    for (int i = tid; i < Kp; i += NT) {
+    // place each winner by counting the winners that order before it; two
+    // threads share a winner when there are enough threads
+    const int parts = (NT >= 2 * Kp) ? 2 : 1;
+    const int span = (Kp + parts - 1) / parts;
+    for (int idx = tid; idx < Kp * parts; idx += NT) {
+        const int i = idx % Kp, part = idx / Kp;
         const uint32_t ki = ckey[i];
         const int32_t ii = cid[i];
+        auto before = [&](uint32_t kj, int32_t ij) { return (kj > ki || (kj == ki && ij < ii)) ? 1 : 0; };
+        int j = part * span;
+        const int j1 = (j + span) < Kp ? (j + span) : Kp;
         int rank = 0;
-        for (int j = 0; j < Kp; ++j) {
-            const uint32_t kj = ckey[j];
-            rank += (kj > ki || (kj == ki && cid[j] < ii)) ? 1 : 0;
+        for (; j < j1 && (j & 3); ++j) rank += before(ckey[j], cid[j]);
+#pragma unroll 4
+        for (; j + 8 <= j1; j += 8) {
+            const uint4 ka = *reinterpret_cast<const uint4 *>(ckey + j);
+            const uint4 kb = *reinterpret_cast<const uint4 *>(ckey + j + 4);
+            const int4 ia = *reinterpret_cast<const int4 *>(cid + j);
+            const int4 ib = *reinterpret_cast<const int4 *>(cid + j + 4);
+            rank += before(ka.x, ia.x) + before(ka.y, ia.y) + before(ka.z, ia.z) +
+                    before(ka.w, ia.w) + before(kb.x, ib.x) + before(kb.y, ib.y) +
+                    before(kb.z, ib.z) + before(kb.w, ib.w);
         }
-        out[rank] = ii;
-        if (out2) out2[rank] = ii;
-        if (out_lds) out_lds[rank] = ii;
+        for (; j < j1; ++j) rank += before(ckey[j], cid[j]);
+        if (parts == 1) rank_sh[i] = rank;
+        else atomicAdd(&rank_sh[i], rank);
+    }
+    __syncthreads();
+    for (int i = tid; i < Kp; i += NT) {
+        const int32_t id = cid[i];
+        const int r = rank_sh[i];
+        out[r] = id;
+        if (out2) out2[r] = id;
+        if (out_lds) out_lds[r] = id;
     }
     for (int i = Kp + tid; i < K; i += NT) {
         out[i] = -1;
@@ -245,10 +290,23 @@ __global__ __launch_bounds__(NT) void topk_kernel(const float *__restrict__ scor
                         nullptr, err);
 }
 
+// Hash of a block id for the LDS residency table.
+__device__ __forceinline__ uint32_t block_hash(int32_t blk) {
+    return ((uint32_t)blk * 2654435761u) >> 8;
+}
+
 // LDS ordering between lanes of one wave.
 __device__ __forceinline__ void wave_sync() {
     __builtin_amdgcn_fence(__ATOMIC_SEQ_CST, "workgroup");
     __builtin_amdgcn_wave_barrier();
+}
+
+// Slots of the LDS residency hash: a power of two of at least twice S, so a
+// probe sequence always meets an empty slot.
+__host__ __device__ constexpr int hash_size(int S) {
+    int h = 64;
+    while (h < 2 * S) h *= 2;
+    return h;
 }
 
 // Bytes of LDS scratch select_unit needs.
@@ -269,7 +327,8 @@ __device__ void select_unit(int64_t u, const int32_t *sel, const int32_t *sb_in,
                             int32_t *__restrict__ fetch_block, int32_t *__restrict__ fetch_slot,
                             int32_t *__restrict__ att_block, int32_t *__restrict__ att_slot,
                             int32_t *__restrict__ counts, DevStats *stats, uint32_t *err,
-                            int32_t *sh) {
+                            int32_t *sh, const int32_t *hkey, const int32_t *hval,
+                            uint32_t hmask) {
     int32_t *hit_blk = sh;             // [K]
     int32_t *hit_slot = hit_blk + K;   // [K]
     int32_t *miss_blk = hit_slot + K;  // [K]
@@ -290,7 +349,23 @@ __device__ void select_unit(int64_t u, const int32_t *sel, const int32_t *sb_in,
     for (int base = 0; base < K; base += 64) {
         const int i = base + lane;
         const int32_t id = i < K ? sel[i] : -1;
-        const int32_t s = id >= 0 ? bs[id] : -1;
+        int32_t s = -1;
+        if (id >= 0) {
+            if (hkey) {  // LDS hash of the resident blocks: linear probing
+                uint32_t hh = block_hash(id) & hmask;
+                while (true) {
+                    const int32_t k = hkey[hh];
+                    if (k == id) {
+                        s = hval[hh];
+                        break;
+                    }
+                    if (k < 0) break;
+                    hh = (hh + 1) & hmask;
+                }
+            } else {
+                s = bs[id];
+            }
+        }
         const bool hit = id >= 0 && s >= 0;
         const bool miss = id >= 0 && s < 0;
         const unsigned long long hb = __ballot(hit), mb = __ballot(miss);
@@ -325,7 +400,29 @@ __device__ void select_unit(int64_t u, const int32_t *sel, const int32_t *sb_in,
     }
     wave_sync();
     const int need = n - nfree;
-    if (need > 0) {
+    if (need > 0 && need <= 16 && S <= 256) {
+        // pick the `need` least-recent victims by repeated wave minimum over
+        // (last_used, block) keys held in registers (at most 4 per lane)
+        unsigned long long mine[4];
+#pragma unroll
+        for (int k = 0; k < 4; ++k) mine[k] = (lane + 64 * k < S) ? vkey[lane + 64 * k] : ~0ull;
+        for (int r = 0; r < need; ++r) {
+            unsigned long long lo = mine[0];
+#pragma unroll
+            for (int k = 1; k < 4; ++k) lo = mine[k] < lo ? mine[k] : lo;
+            const uint32_t hi_min = wave_min_u32((uint32_t)(lo >> 32));
+            const uint32_t lo_min = wave_min_u32((uint32_t)(lo >> 32) == hi_min ? (uint32_t)lo
+                                                                                : 0xFFFFFFFFu);
+            const unsigned long long best = ((unsigned long long)hi_min << 32) | lo_min;
+            if (best == ~0ull) break;  // fewer victims than needed: reported below
+#pragma unroll
+            for (int k = 0; k < 4; ++k)
+                if (mine[k] == best) {
+                    cand[nfree + r] = lane + 64 * k;
+                    mine[k] = ~0ull;
+                }
+        }
+    } else if (need > 0) {
         for (int s = lane; s < S; s += 64) {
             const unsigned long long k = vkey[s];
             if (k == ~0ull) continue;
@@ -391,7 +488,7 @@ __global__ __launch_bounds__(64) void select_kernel(
     const int64_t u = blockIdx.x;
     select_unit(u, ids + u * K, slot_block + u * S, last_used + u * S, slot_block, last_used,
                 block_slot, K, S, NBmax, cap, t, fetch_block, fetch_slot, att_block, att_slot,
-                counts, stats, err, sh);
+                counts, stats, err, sh, nullptr, nullptr, 0u);
 }
 
 // Top-K and select of one unit in one workgroup.
@@ -405,20 +502,34 @@ __global__ __launch_bounds__(NT) void topk_select_kernel(
     int32_t *__restrict__ counts, DevStats *stats, uint32_t *err) {
     extern __shared__ __attribute__((aligned(16))) int32_t sh[];
     const int64_t u = blockIdx.x;
+    const int K4 = (K + 3) & ~3, S4 = (S + 3) & ~3;
+    const int HS = hash_size(S);
     int32_t *sel_lds = sh;                 // [K]
-    int32_t *sb_lds = sel_lds + K;         // [S]
-    int32_t *lu_lds = sb_lds + S;          // [S]
-    int32_t *scratch = lu_lds + S + ((K + 2 * S) & 1);  // 8-byte aligned
+    int32_t *sb_lds = sel_lds + K4;        // [S]
+    int32_t *lu_lds = sb_lds + S4;         // [S]
+    int32_t *hkey = lu_lds + S4;           // [HS] resident block -> slot
+    int32_t *hval = hkey + HS;             // [HS]
+    int32_t *scratch = hval + HS;          // 16-byte aligned
+    for (int i = threadIdx.x; i < HS; i += NT) hkey[i] = -1;
+    __syncthreads();
+    // tables into LDS and the resident blocks into the hash, while the top-K
+    // below still waits for its scores
     for (int s = threadIdx.x; s < S; s += NT) {
-        sb_lds[s] = slot_block[u * S + s];
+        const int32_t blk = slot_block[u * S + s];
+        sb_lds[s] = blk;
         lu_lds[s] = last_used[u * S + s];
+        if (blk >= 0) {
+            uint32_t hh = block_hash(blk) & (uint32_t)(HS - 1);
+            while (atomicCAS(&hkey[hh], -1, blk) != -1) hh = (hh + 1) & (uint32_t)(HS - 1);
+            hval[hh] = s;
+        }
     }
     topk_unit<NT, CMAX>(scores + u * NBmax, NB, K, ids + u * K, nullptr, sel_lds, err);
     __syncthreads();
     if (threadIdx.x < 64)
         select_unit(u, sel_lds, sb_lds, lu_lds, slot_block, last_used, block_slot, K, S, NBmax,
                     cap, t, fetch_block, fetch_slot, att_block, att_slot, counts, stats, err,
-                    scratch);
+                    scratch, hkey, hval, (uint32_t)(HS - 1));
 }
 
 __global__ __launch_bounds__(64) void evict_kernel(const int32_t *__restrict__ blocks,
@@ -493,8 +604,15 @@ hipError_t launch_topk_select(const Dims &D, const float *scores, int64_t NB, in
                               int32_t *att_block, int32_t *att_slot, int32_t *counts,
                               DevStats *stats, uint32_t *err, hipStream_t st) {
     dim3 grid((unsigned)D.units());
-    const size_t lds = sizeof(int32_t) * ((size_t)D.K + 2 * (size_t)D.S + 1) +
+    const size_t lds = sizeof(int32_t) * ((size_t)((D.K + 3) & ~3) + 2 * (size_t)((D.S + 3) & ~3) +
+                                          2 * (size_t)hash_size(D.S)) +
                        select_lds_bytes(D.K, D.S);
+    if (lds > 64 * 1024) {  // large pools: the two kernels one after the other
+        hipError_t e = launch_topk(D, scores, NB, ids, nullptr, err, st);
+        if (e != hipSuccess) return e;
+        return launch_select(D, ids, slot_block, last_used, block_slot, cap, t, fetch_block,
+                             fetch_slot, att_block, att_slot, counts, stats, err, st);
+    }
 #define OASIS_TS(NT_, CM_)                                                                      \
     hipLaunchKernelGGL((topk_select_kernel<NT_, CM_>), grid, dim3(NT_), lds, st, scores,      \
                        (int)NB, ids, slot_block, last_used, block_slot, D.K, D.S, D.NBmax, cap, \
