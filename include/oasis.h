@@ -190,7 +190,8 @@ typedef struct {
     int64_t attended;         /* blocks attended */
     int64_t bytes_fetched;    /* fetched * 2 * block_size * d * elem bytes */
     int64_t tokens;           /* current sequence length T */
-    int64_t reserved;
+    int64_t fetch_fused;      /* 1: blocks are copied host -> HBM inside oasis_sparse_attn's
+                                 kernel; 0: by a copy kernel on the handle's copy stream */
 } oasis_stats;
 
 /* Cumulative counters (synchronous). */

@@ -53,7 +53,7 @@ class oasis_layout(ctypes.Structure):
 class oasis_stats(ctypes.Structure):
     _fields_ = [(n, ctypes.c_int64) for n in
                 ("steps", "hits", "misses", "fetched", "attended", "bytes_fetched", "tokens",
-                 "reserved")]
+                 "fetch_fused")]
 
 
 class oasis_timing(ctypes.Structure):
@@ -223,7 +223,7 @@ class Oasis:
     def oasis_get_stats(self) -> dict:
         s = oasis_stats()
         self._check(lib().oasis_get_stats(self.h, ctypes.byref(s)), "oasis_get_stats")
-        return {n: getattr(s, n) for n, _ in oasis_stats._fields_ if n != "reserved"}
+        return {n: getattr(s, n) for n, _ in oasis_stats._fields_}
 
     def oasis_set_timing(self, mask=TIME["all"]):
         """mask: OR of TIME values (0 = off)."""

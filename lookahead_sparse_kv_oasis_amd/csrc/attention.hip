@@ -482,7 +482,7 @@ static void launch_mfma_g(const AttnPlan &P, dim3 grid, hipStream_t st, const ui
                           int mode, int cap, int n_fetch_wg, float sc, float *pm, float *pl,
                           float *pa) {
 #define OASIS_ATTN(BPW)                                                                        \
-    hipLaunchKernelGGL((attn_mfma_kernel<G, BPW>), grid, dim3(256), 0, st, q, slots, host_kv,  \
+    OASIS_LAUNCH((attn_mfma_kernel<G, BPW>), grid, dim3(256), 0, st, q, slots, host_kv,  \
                        ab, as, counts, T, D.Hq, D.Hkv, D.K, D.S, D.NBmax, mode, cap,           \
                        n_fetch_wg, P.nsf_max, P.ns1, P.nsa, D.units(), sc, pm, pl, pa)
     switch (P.blocks_per_wave) {
@@ -517,7 +517,7 @@ hipError_t launch_attention(const Dims &D, const AttnPlan &P, int mode, int nsf,
     dim3 grid((unsigned)P.ns1, D.Hkv, D.B);
     const int epl = (D.d + 63) / 64;
 #define OASIS_GENERIC(TT, E)                                                                     \
-    hipLaunchKernelGGL((attn_generic_kernel<TT, E>), grid, dim3(64), 0, st, (const TT *)q,       \
+    OASIS_LAUNCH((attn_generic_kernel<TT, E>), grid, dim3(64), 0, st, (const TT *)q,       \
                        (const TT *)slots, att_block, att_slot, counts, T, D.Hq, D.Hkv, D.G, D.d, \
                        D.K, D.S, D.bs, P.blocks_per_wave, P.nsa, P.nsf_max, sc, part_m, part_l,  \
                        part_acc)
@@ -537,7 +537,7 @@ hipError_t launch_attention(const Dims &D, const AttnPlan &P, int mode, int nsf,
 hipError_t launch_combine(const Dims &D, const AttnPlan &P, int nsf, const float *part_m,
                           const float *part_l, const float *part_acc, float *out,
                           hipStream_t st) {
-    hipLaunchKernelGGL(combine_kernel, dim3(D.Hq, D.B), dim3(D.d <= 256 ? D.d : 256), 0, st,
+    OASIS_LAUNCH(combine_kernel, dim3(D.Hq, D.B), dim3(D.d <= 256 ? D.d : 256), 0, st,
                        part_m, part_l, part_acc, out, D.Hq, D.Hkv, D.G, D.d, P.nsa, nsf,
                        P.nsf_max, P.ns1);
     return hipGetLastError();

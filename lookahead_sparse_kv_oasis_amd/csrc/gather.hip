@@ -57,15 +57,15 @@ hipError_t launch_gather(const Dims &D, const void *host_kv, void *slots, const 
     const int block_vec = (int)(D.block_elems() * D.esize() / 16);
     dim3 grid((unsigned)max_n, (unsigned)D.units());
     if (block_vec <= 256)
-        hipLaunchKernelGGL(gather_kernel<1>, grid, dim3(256), 0, st, (const u32x4 *)host_kv,
+        OASIS_LAUNCH(gather_kernel<1>, grid, dim3(256), 0, st, (const u32x4 *)host_kv,
                            (u32x4 *)slots, blocks, slot_ids, list_stride, counts, count_stride,
                            count_index, D.NBmax, D.S, block_vec);
     else if (block_vec <= 512)
-        hipLaunchKernelGGL(gather_kernel<2>, grid, dim3(256), 0, st, (const u32x4 *)host_kv,
+        OASIS_LAUNCH(gather_kernel<2>, grid, dim3(256), 0, st, (const u32x4 *)host_kv,
                            (u32x4 *)slots, blocks, slot_ids, list_stride, counts, count_stride,
                            count_index, D.NBmax, D.S, block_vec);
     else
-        hipLaunchKernelGGL(gather_kernel<4>, grid, dim3(256), 0, st, (const u32x4 *)host_kv,
+        OASIS_LAUNCH(gather_kernel<4>, grid, dim3(256), 0, st, (const u32x4 *)host_kv,
                            (u32x4 *)slots, blocks, slot_ids, list_stride, counts, count_stride,
                            count_index, D.NBmax, D.S, block_vec);
     return hipGetLastError();

@@ -2,12 +2,32 @@
 // hipError_t; shapes are validated by the C-ABI layer before any launch.
 #pragma once
 
+#include <hip/hip_ext.h>
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
 #include "common.h"
 
 namespace oasis {
+
+// Timing events for the next launch: when set, the launch carries them in its
+// dispatch packet (start/stop timestamps of the kernel itself, no extra
+// packets on the stream).  Set and cleared by the C-ABI layer around one
+// launcher call; one thread drives a handle.
+struct LaunchEvents {
+    hipEvent_t start = nullptr, stop = nullptr;
+};
+extern thread_local LaunchEvents g_launch_events;
+
+#define OASIS_LAUNCH(kernel, grid, block, lds, stream, ...)                                       \
+    do {                                                                                         \
+        if (::oasis::g_launch_events.start)                                                      \
+            hipExtLaunchKernelGGL(kernel, grid, block, lds, stream,                              \
+                                  ::oasis::g_launch_events.start,                                \
+                                  ::oasis::g_launch_events.stop, 0, __VA_ARGS__);                \
+        else                                                                                     \
+            hipLaunchKernelGGL(kernel, grid, block, lds, stream, __VA_ARGS__);                   \
+    } while (0)
 
 struct Dims {
     int B, Hq, Hkv, G, d, dtype, bs, K, S;

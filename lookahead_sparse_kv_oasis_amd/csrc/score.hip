@@ -290,16 +290,16 @@ static void launch_mfma(int QT, dim3 grid, hipStream_t st, const uint16_t *summ,
                         const uint16_t *q, const uint16_t *dr, int nd, float *scores,
                         const Dims &Dm, int64_t NB) {
     if (QT == 1)
-        hipLaunchKernelGGL((score_mfma_kernel<D, 1>), grid, dim3(256), 0, st, summ, q, dr, nd,
+        OASIS_LAUNCH((score_mfma_kernel<D, 1>), grid, dim3(256), 0, st, summ, q, dr, nd,
                            scores, Dm.B, Dm.Hq, Dm.Hkv, Dm.G, Dm.NBmax, NB);
     else if (QT == 2)
-        hipLaunchKernelGGL((score_mfma_kernel<D, 2>), grid, dim3(256), 0, st, summ, q, dr, nd,
+        OASIS_LAUNCH((score_mfma_kernel<D, 2>), grid, dim3(256), 0, st, summ, q, dr, nd,
                            scores, Dm.B, Dm.Hq, Dm.Hkv, Dm.G, Dm.NBmax, NB);
     else if (QT == 3)
-        hipLaunchKernelGGL((score_mfma_kernel<D, 3>), grid, dim3(256), 0, st, summ, q, dr, nd,
+        OASIS_LAUNCH((score_mfma_kernel<D, 3>), grid, dim3(256), 0, st, summ, q, dr, nd,
                            scores, Dm.B, Dm.Hq, Dm.Hkv, Dm.G, Dm.NBmax, NB);
     else
-        hipLaunchKernelGGL((score_mfma_kernel<D, 4>), grid, dim3(256), 0, st, summ, q, dr, nd,
+        OASIS_LAUNCH((score_mfma_kernel<D, 4>), grid, dim3(256), 0, st, summ, q, dr, nd,
                            scores, Dm.B, Dm.Hq, Dm.Hkv, Dm.G, Dm.NBmax, NB);
 }
 
@@ -322,7 +322,7 @@ hipError_t launch_score(const Dims &D, const void *summ, const void *q, const vo
         const uint16_t *s = (const uint16_t *)summ, *qq = (const uint16_t *)q,
                        *dr = (const uint16_t *)drafts;
         if (D.d == 128 && QT == 1 && lds_staged) {
-            hipLaunchKernelGGL(score_mfma_lds_kernel, grid, dim3(256), 4 * kScoreTileLds, st, s, qq,
+            OASIS_LAUNCH(score_mfma_lds_kernel, grid, dim3(256), 4 * kScoreTileLds, st, s, qq,
                                dr, n_drafts, scores, D.B, D.Hq, D.Hkv, D.G, D.NBmax, NB);
             return hipGetLastError();
         }
@@ -337,11 +337,11 @@ hipError_t launch_score(const Dims &D, const void *summ, const void *q, const vo
     dim3 grid((unsigned)((NB + 63) / 64), D.Hkv, D.B), block(64);
     const size_t lds = (size_t)Q * D.d * sizeof(float);
     if (D.dtype == kF32)
-        hipLaunchKernelGGL(score_valu_kernel<float>, grid, block, lds, st, (const float *)summ,
+        OASIS_LAUNCH(score_valu_kernel<float>, grid, block, lds, st, (const float *)summ,
                            (const float *)q, (const float *)drafts, n_drafts, scores, D.B, D.Hq,
                            D.Hkv, D.G, D.d, D.NBmax, NB);
     else
-        hipLaunchKernelGGL(score_valu_kernel<uint16_t>, grid, block, lds, st,
+        OASIS_LAUNCH(score_valu_kernel<uint16_t>, grid, block, lds, st,
                            (const uint16_t *)summ, (const uint16_t *)q,
                            (const uint16_t *)drafts, n_drafts, scores, D.B, D.Hq, D.Hkv, D.G,
                            D.d, D.NBmax, NB);

@@ -575,7 +575,7 @@ hipError_t launch_topk(const Dims &D, const float *scores, int64_t NB, int32_t *
                        int32_t *ids_copy, uint32_t *err, hipStream_t st) {
     dim3 grid((unsigned)D.units());
 #define OASIS_TOPK(NT_, CM_)                                                                    \
-    hipLaunchKernelGGL((topk_kernel<NT_, CM_>), grid, dim3(NT_), 0, st, scores, D.NBmax,      \
+    OASIS_LAUNCH((topk_kernel<NT_, CM_>), grid, dim3(NT_), 0, st, scores, D.NBmax,      \
                        (int)NB, D.K, ids, ids_copy, err)
     if (NB <= 256 * 64) {
         OASIS_CMAX_DISPATCH(256, (NB + 255) / 256, OASIS_TOPK);
@@ -591,7 +591,7 @@ hipError_t launch_select(const Dims &D, const int32_t *ids, int32_t *slot_block,
                          int32_t *fetch_block, int32_t *fetch_slot, int32_t *att_block,
                          int32_t *att_slot, int32_t *counts, DevStats *stats, uint32_t *err,
                          hipStream_t st) {
-    hipLaunchKernelGGL(select_kernel, dim3((unsigned)D.units()), dim3(64),
+    OASIS_LAUNCH(select_kernel, dim3((unsigned)D.units()), dim3(64),
                        select_lds_bytes(D.K, D.S), st, ids, slot_block, last_used, block_slot,
                        D.K, D.S, D.NBmax, cap, t, fetch_block, fetch_slot, att_block, att_slot,
                        counts, stats, err);
@@ -614,7 +614,7 @@ hipError_t launch_topk_select(const Dims &D, const float *scores, int64_t NB, in
                              fetch_slot, att_block, att_slot, counts, stats, err, st);
     }
 #define OASIS_TS(NT_, CM_)                                                                      \
-    hipLaunchKernelGGL((topk_select_kernel<NT_, CM_>), grid, dim3(NT_), lds, st, scores,      \
+    OASIS_LAUNCH((topk_select_kernel<NT_, CM_>), grid, dim3(NT_), lds, st, scores,      \
                        (int)NB, ids, slot_block, last_used, block_slot, D.K, D.S, D.NBmax, cap, \
                        t, fetch_block, fetch_slot, att_block, att_slot, counts, stats, err)
     if (NB <= 256 * 64) {
@@ -629,7 +629,7 @@ hipError_t launch_topk_select(const Dims &D, const float *scores, int64_t NB, in
 hipError_t launch_evict(const Dims &D, const int32_t *blocks, const int32_t *counts,
                         int max_per_unit, int32_t *slot_block, int32_t *block_slot,
                         hipStream_t st) {
-    hipLaunchKernelGGL(evict_kernel, dim3((unsigned)D.units()), dim3(64), 0, st, blocks, counts,
+    OASIS_LAUNCH(evict_kernel, dim3((unsigned)D.units()), dim3(64), 0, st, blocks, counts,
                        max_per_unit, slot_block, block_slot, D.S, D.NBmax);
     return hipGetLastError();
 }
@@ -637,7 +637,7 @@ hipError_t launch_evict(const Dims &D, const int32_t *blocks, const int32_t *cou
 hipError_t launch_rebuild_block_slot(const Dims &D, const int32_t *slot_block,
                                      int32_t *block_slot, hipStream_t st) {
     // one workgroup per unit so the clear is ordered before the fill
-    hipLaunchKernelGGL(rebuild_block_slot_kernel, dim3(1, (unsigned)D.units()), dim3(256), 0, st,
+    OASIS_LAUNCH(rebuild_block_slot_kernel, dim3(1, (unsigned)D.units()), dim3(256), 0, st,
                        slot_block, block_slot, D.S, D.NBmax);
     return hipGetLastError();
 }

@@ -90,11 +90,11 @@ hipError_t launch_append(const Dims &D, const void *k, const void *v, int64_t po
                          void *summ, const int32_t *block_slot, void *slots, hipStream_t st) {
     dim3 grid((unsigned)D.units()), block(64);
     if (D.dtype == kF32)
-        hipLaunchKernelGGL(append_kernel<float>, grid, block, 0, st, (const float *)k,
+        OASIS_LAUNCH(append_kernel<float>, grid, block, 0, st, (const float *)k,
                            (const float *)v, pos, (float *)host_kv, (float *)summ, block_slot,
                            (float *)slots, D.d, D.bs, D.S, D.NBmax);
     else
-        hipLaunchKernelGGL(append_kernel<uint16_t>, grid, block, 0, st, (const uint16_t *)k,
+        OASIS_LAUNCH(append_kernel<uint16_t>, grid, block, 0, st, (const uint16_t *)k,
                            (const uint16_t *)v, pos, (uint16_t *)host_kv, (uint16_t *)summ,
                            block_slot, (uint16_t *)slots, D.d, D.bs, D.S, D.NBmax);
     return hipGetLastError();
@@ -109,11 +109,11 @@ hipError_t launch_summary_build(const Dims &D, const void *host_kv, int64_t T, v
     int64_t blocks = (total + 255) / 256;
     if (blocks > 65536) blocks = 65536;
     if (D.dtype == kF32)
-        hipLaunchKernelGGL(summary_build_kernel<float>, dim3((unsigned)blocks), dim3(256), 0, st,
+        OASIS_LAUNCH(summary_build_kernel<float>, dim3((unsigned)blocks), dim3(256), 0, st,
                            (const float *)host_kv, T, (float *)summ, D.d, D.bs, D.NBmax, NB,
                            D.units());
     else
-        hipLaunchKernelGGL(summary_build_kernel<uint16_t>, dim3((unsigned)blocks), dim3(256), 0,
+        OASIS_LAUNCH(summary_build_kernel<uint16_t>, dim3((unsigned)blocks), dim3(256), 0,
                            st, (const uint16_t *)host_kv, T, (uint16_t *)summ, D.d, D.bs,
                            D.NBmax, NB, D.units());
     return hipGetLastError();
