@@ -67,7 +67,7 @@ def stored_traffic(kernel: str, workload: str):
 
 def _workloads():
     import synth
-    return {w.name: w for w in synth.WORKLOADS[:4]}
+    return {w.name: w for w in synth.WORKLOADS}
 
 
 def pinned_h2d_peak_gbps(nbytes=1 << 30, reps=5):
@@ -151,6 +151,15 @@ def main():
                          "(reference for the HBM byte counters) and exit")
     ap.add_argument("--no-kernel-timing", action="store_true",
                     help="skip the per-kernel HIP events (roofline fields become null)")
+    ap.add_argument("--schedule", default="overlap", choices=["overlap", "serial", "both"],
+                    help="multi-layer workloads: prediction/selection of later layers on a "
+                         "second stream under earlier layers' attention, or one stream")
+    ap.add_argument("--data-layers", type=int, default=2,
+                    help="multi-layer workloads: distinct host KV buffers the layers alias")
+    ap.add_argument("--fetch-ratio", default=None,
+                    help="override the workload's fetch ratio ('all' = cap K)")
+    ap.add_argument("--sweep", action="store_true",
+                    help="multi-layer workloads: one line per fetch ratio of the sweep")
     args = ap.parse_args()
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
         print("bench.py measures one GPU only: the decode path has no cross-GPU exchange and "
@@ -174,6 +183,12 @@ def main():
     from lookahead_sparse_kv_oasis_amd.runner import LayerRunner
 
     w = _workloads()[args.workload]
+    if w.layers > 1:
+        bench_model(args, w)
+        return
+    if args.fetch_ratio is not None:
+        w = w.with_(fetch_ratio=1.0 if args.fetch_ratio == "all" else float(args.fetch_ratio),
+                    cap=0)
     n_steps = args.warmup + args.steps
     t_setup = time.perf_counter()
     run = LayerRunner(w, n_steps)
@@ -293,6 +308,119 @@ def main():
         print("# cpu baseline (oracle) ...", file=sys.stderr, flush=True)
         line["cpu_baseline"] = cpu_baseline(w)
     print(json.dumps(line), flush=True)
+
+
+def bench_model(args, w):
+    """All layers of a multi-layer workload per step through oasis_decode_layers."""
+    import numpy as np
+    import torch
+
+    import synth
+    from lookahead_sparse_kv_oasis_amd import TIME, cap_from_ratio
+    from lookahead_sparse_kv_oasis_amd.runner import ModelRunner
+
+    n_steps = args.warmup + args.steps
+    if n_steps > w.steps:
+        w = w.with_(steps=n_steps)
+    t_setup = time.perf_counter()
+    log = lambda m: print("# " + m, file=sys.stderr, flush=True)
+    mr = ModelRunner(w, n_steps, data_layers=args.data_layers, log=log)
+    log(f"setup {time.perf_counter() - t_setup:.1f}s: {w.name}, {w.layers} layers on "
+        f"{mr.H} host KV buffers, {n_steps} steps")
+    if args.sweep:
+        ratios = synth.FETCH_RATIO_SWEEP
+    elif args.fetch_ratio is not None:
+        ratios = [None if args.fetch_ratio == "all" else float(args.fetch_ratio)]
+    else:
+        ratios = [w.fetch_ratio]
+    schedules = ["overlap", "serial"] if args.schedule == "both" else [args.schedule]
+    stream = torch.cuda.current_stream()
+    side = torch.cuda.Stream()
+    h2d = None if args.no_h2d_peak else pinned_h2d_peak_gbps()
+    cpu = None if args.no_cpu_baseline else cpu_baseline(w.with_(layers=1))
+    e, d, bs = w.elem_bytes, w.head_dim, w.block_size
+    units = w.batch * w.kv_heads
+    blk_bytes = 2 * bs * d * e
+    q_bytes = w.batch * w.q_heads * d * e
+    L = w.layers
+    first = True
+    for ratio in ratios:
+        cap = w.k_blocks if ratio is None else cap_from_ratio(ratio, w.k_blocks)
+        res = {}
+        for sched in schedules:
+            sd = side if sched == "overlap" else None
+            if not first:
+                mr.reset()
+            first = False
+            mr.admission(stream, sd)
+            for t in range(1, args.warmup + 1):
+                mr.step(t, stream, sd, cap)
+            torch.cuda.synchronize()
+            s0 = [h.oasis_get_stats() for h in mr.handles]
+            for h in mr.handles:
+                h.oasis_set_timing(0 if args.no_kernel_timing else TIME["score"] | TIME["attn"])
+            torch.cuda.synchronize()
+            t0 = time.perf_counter()
+            for t in range(args.warmup + 1, n_steps + 1):
+                mr.step(t, stream, sd, cap)
+            torch.cuda.synchronize()
+            dt = time.perf_counter() - t0
+            s1 = [h.oasis_get_stats() for h in mr.handles]
+            tms = [h.oasis_get_timing() for h in mr.handles]
+            for h in mr.handles:
+                h.oasis_check()
+                h.oasis_set_timing(0)
+            fetched = sum(b["fetched"] - a["fetched"] for a, b in zip(s0, s1)) / args.steps
+            attended = sum(b["attended"] - a["attended"] for a, b in zip(s0, s1)) / args.steps
+            res[sched] = dict(dt=dt, fetched=fetched, attended=attended, tms=tms)
+            log(f"ratio {ratio} cap {cap} {sched}: {dt / args.steps * 1e3:.3f} ms/step")
+        main_sched = schedules[0]
+        r = res[main_sched]
+        K = args.steps
+        dt = r["dt"]
+        nb_avg = np.mean([w.blocks_at(w.prefix_tokens + t)
+                          for t in range(args.warmup + 1, n_steps + 1)])
+        score_bytes = units * nb_avg * 2 * d * e + q_bytes * (1 + w.drafts) + units * nb_avg * 4
+        roof = None
+        if not args.no_kernel_timing:
+            n_sc = sum(tm["n_score"] for tm in r["tms"])
+            ms_score = sum(tm["ms_score"] for tm in r["tms"]) / max(n_sc, 1)
+            n_at = sum(tm["n_attn"] for tm in r["tms"])
+            ms_attn = sum(tm["ms_attn"] for tm in r["tms"]) / max(n_at, 1)
+            score_gbps = score_bytes / (ms_score * 1e-3) / 1e9
+            roof = {"bound": "hbm", "kernel": "oasis_score", "achieved": score_gbps,
+                    "peak": HBM_PEAK_GBPS, "unit": "GB/s", "frac": score_gbps / HBM_PEAK_GBPS,
+                    "traffic": None, "per_launch_bytes": score_bytes, "avg_ms": ms_score,
+                    "attn_avg_ms": ms_attn}
+        link_gbps = r["fetched"] * blk_bytes / (dt / K) / 1e9
+        line = {
+            "metric": METRIC,
+            "value": L * K / dt,
+            "unit": "layer-steps/s",
+            "n_gpus": 1, "steps": K, "warmup": args.warmup,
+            "ms_per_step": dt / K * 1e3,
+            "higher_is_better": True, "scaling": "weak", "vs_baseline": None,
+            "dtype": "bf16" if w.dtype == synth.BF16 else "f32", "data": "synthetic",
+            "config": {"workload": w.name, "layers": L, "batch": w.batch,
+                       "q_heads": w.q_heads, "kv_heads": w.kv_heads, "head_dim": d,
+                       "context": w.prefix_tokens, "block_size": bs,
+                       "budget_tokens": w.budget_tokens, "drafts": w.drafts,
+                       "fetch_ratio": "all" if ratio is None else ratio,
+                       "cap_per_kv_head": cap, "schedule": main_sched,
+                       "host_kv_buffers": mr.H},
+            "model_steps_per_s": K / dt,
+            "roofline": roof,
+            "host_link": {"achieved_gbps_step_avg": link_gbps, "pinned_h2d_peak_gbps": h2d,
+                          "blocks_per_step": r["fetched"],
+                          "bytes_per_step": r["fetched"] * blk_bytes},
+            "attended_blocks_per_step": r["attended"],
+            "cpu_baseline": cpu,
+        }
+        if "serial" in res and main_sched != "serial":
+            line["serial_ms_per_step"] = res["serial"]["dt"] / K * 1e3
+            line["overlap_speedup"] = res["serial"]["dt"] / dt
+        print(json.dumps(line), flush=True)
+    mr.close()
 
 
 if __name__ == "__main__":

@@ -92,13 +92,30 @@ typedef struct oasis_handle oasis_t;
 int oasis_create(const oasis_layout *layout, int32_t block_size, int32_t budget_tokens,
                  float fetch_ratio, oasis_t **out);
 
+/* Create a handle for a layer whose KV data is identical to owner's, using
+ * owner's pinned host KV instead of allocating its own (the host buffer is
+ * reference counted and lives until the last handle using it is destroyed).
+ * For models whose full host KV exceeds host memory, layers can be aliased
+ * onto a few distinct host buffers.  batch, num_kv_heads, head_dim, dtype,
+ * block_size and the block capacity (max_tokens rounded up to blocks) must
+ * equal owner's, else OASIS_E_INVAL; everything in HBM (summaries, slots,
+ * tables) is the new handle's own.  Every handle of a buffer must be given
+ * the same appended tokens, since they all write them into the buffer. */
+int oasis_create_shared(const oasis_layout *layout, int32_t block_size, int32_t budget_tokens,
+                        float fetch_ratio, const oasis_t *owner, oasis_t **out);
+
 /* Wait for all work of the handle, then free everything it owns. */
 int oasis_destroy(oasis_t *h);
 
 /* Load a prompt of len tokens per sequence (synchronous).  k_host, v_host:
  * [B][Hkv][len][d] in the layout's dtype.  Copies them into the pinned host
  * KV, builds every block summary on the GPU and empties the slot pool.
- * len <= max_tokens. */
+ * len <= max_tokens.  With k_host == v_host == NULL the host KV keeps the
+ * prompt the last load wrote into it (OASIS_E_STATE unless that prompt had
+ * len tokens) and the handle starts over from it; this is how a handle
+ * sharing a buffer gets its prompt.  Either form clears every host row past
+ * len that a load or an append wrote, so all handles of a shared buffer must
+ * be reloaded before their next step. */
 int oasis_load_prefix(oasis_t *h, const void *k_host, const void *v_host, int64_t len);
 
 /* Set the residency tables (synchronous): slot_block_host[B][Hkv][S] (the
@@ -139,8 +156,10 @@ int oasis_topk_from_scores(oasis_t *h, const float *scores_dev, int32_t *block_i
  * held non-selected blocks, least recently used first (ties: lower block id);
  * every hit and fetched block gets last_used = this step.  cap < 0 uses the
  * handle's fetch ratio; cap is clamped to K.  The table update runs on
- * `stream`; the host -> HBM block copies run on the handle's copy stream
- * after it, and oasis_sparse_attn orders itself after them. */
+ * `stream`.  The host -> HBM block copies run inside the next
+ * oasis_sparse_attn's kernel (bf16 layouts), or on the handle's copy stream
+ * after the update; any call that needs the slots earlier (append, evict,
+ * select, reading SLOTS) makes the copy first. */
 int oasis_select_and_fetch(oasis_t *h, int32_t cap, hipStream_t stream);
 
 /* Force blocks out of HBM (synchronous on `stream`): blocks_host
@@ -155,6 +174,32 @@ int oasis_evict(oasis_t *h, const int32_t *blocks_host, const int32_t *counts_ho
  * q_dev [B][Hq][d]: out_dev[B][Hq][d] (fp32) = softmax(q.k / sqrt(d)) v over
  * the valid tokens of those blocks; 0 when none is attended. */
 int oasis_sparse_attn(oasis_t *h, const void *q_dev, float *out_dev, hipStream_t stream);
+
+/* ---------------------------------------------------------------- layer pipeline */
+
+typedef struct {
+    const void *k_new;   /* [B][Hkv][d] token to append, or NULL: no append */
+    const void *v_new;   /* [B][Hkv][d], NULL exactly when k_new is */
+    const void *q;       /* [B][Hq][d] current query */
+    const void *drafts;  /* [n_drafts][B][Hq][d], or NULL when n_drafts == 0 */
+    float *out;          /* [B][Hq][d] fp32 attention output */
+} oasis_layer_io;
+
+/* One decode step over the n_layers layers of a model (OasisKV page,
+ * Fig. 8: predict, select and transfer per layer, overlapped with compute):
+ * per layer, in order, append (when io[l].k_new), predict with the deferred
+ * top-K, select_and_fetch(cap) and sparse_attn, with the same semantics as
+ * those calls.  With side != stream, append/predict/select of every layer
+ * run on `side` and each layer's attention on `stream` after that layer's
+ * select, so later layers' prediction and selection overlap earlier layers'
+ * attention and host fetch; `stream` then waits for `side` before the call
+ * returns.  side == stream runs everything on `stream` one layer after the
+ * other.  Both give bit-identical results.  The handles must be distinct.
+ * On error no further call is issued (work already queued still runs and
+ * `stream` still joins `side`), and oasis_last_error(layers[0]) names the
+ * failing layer. */
+int oasis_decode_layers(oasis_t *const *layers, const oasis_layer_io *io, int32_t n_layers,
+                        int32_t n_drafts, int32_t cap, hipStream_t stream, hipStream_t side);
 
 /* ---------------------------------------------------------------- inspection */
 

@@ -27,7 +27,8 @@ BUF = dict(SUMMARY=0, SLOTS=1, HOST_KV=2, SCORES=3, IDS=4, SLOT_BLOCK=5, BLOCK_S
            LAST_USED=7, FETCH_BLOCK=8, FETCH_SLOT=9, ATT_BLOCK=10, ATT_SLOT=11, COUNTS=12)
 
 EXPORTS = [
-    "oasis_create", "oasis_destroy", "oasis_load_prefix", "oasis_set_state",
+    "oasis_create", "oasis_create_shared", "oasis_destroy", "oasis_load_prefix",
+    "oasis_set_state", "oasis_decode_layers",
     "oasis_append_kv", "oasis_predict", "oasis_topk_from_scores", "oasis_select_and_fetch",
     "oasis_evict", "oasis_sparse_attn", "oasis_buffer_bytes", "oasis_read", "oasis_get_stats",
     "oasis_check", "oasis_set_timing", "oasis_get_timing", "oasis_get_dims", "oasis_tokens",
@@ -48,6 +49,11 @@ class oasis_layout(ctypes.Structure):
                 ("dtype", ctypes.c_int32), ("max_drafts", ctypes.c_int32),
                 ("slots_per_head", ctypes.c_int32), ("reserved", ctypes.c_int32),
                 ("max_tokens", ctypes.c_int64)]
+
+
+class oasis_layer_io(ctypes.Structure):
+    _fields_ = [("k_new", ctypes.c_void_p), ("v_new", ctypes.c_void_p), ("q", ctypes.c_void_p),
+                ("drafts", ctypes.c_void_p), ("out", ctypes.c_void_p)]
 
 
 class oasis_stats(ctypes.Structure):
@@ -78,6 +84,11 @@ def lib():
         sig = {
             "oasis_create": (ctypes.c_int, [ctypes.POINTER(oasis_layout), i32, i32, f32,
                                             ctypes.POINTER(ctypes.c_void_p)]),
+            "oasis_create_shared": (ctypes.c_int, [ctypes.POINTER(oasis_layout), i32, i32, f32,
+                                                   H, ctypes.POINTER(ctypes.c_void_p)]),
+            "oasis_decode_layers": (ctypes.c_int, [ctypes.POINTER(ctypes.c_void_p),
+                                                   ctypes.POINTER(oasis_layer_io), i32, i32, i32,
+                                                   vp, vp]),
             "oasis_destroy": (ctypes.c_int, [H]),
             "oasis_load_prefix": (ctypes.c_int, [H, vp, vp, i64]),
             "oasis_set_state": (ctypes.c_int, [H, vp, vp]),
@@ -145,15 +156,23 @@ class Oasis:
 
     def __init__(self, batch, num_q_heads, num_kv_heads, head_dim, dtype, max_drafts,
                  max_tokens, block_size=16, budget_tokens=2048, fetch_ratio=0.02,
-                 slots_per_head=0):
+                 slots_per_head=0, share_host_with: "Oasis | None" = None):
+        """share_host_with: another handle whose host KV this layer reuses
+        (oasis_create_shared); otherwise oasis_create."""
         L = lib()
         self.layout = oasis_layout(batch, num_q_heads, num_kv_heads, head_dim, dtype,
                                    max_drafts, slots_per_head, 0, max_tokens)
         h = ctypes.c_void_p()
-        rc = L.oasis_create(ctypes.byref(self.layout), block_size, budget_tokens, fetch_ratio,
-                            ctypes.byref(h))
+        if share_host_with is None:
+            rc = L.oasis_create(ctypes.byref(self.layout), block_size, budget_tokens,
+                                fetch_ratio, ctypes.byref(h))
+            what = "oasis_create"
+        else:
+            rc = L.oasis_create_shared(ctypes.byref(self.layout), block_size, budget_tokens,
+                                       fetch_ratio, share_host_with.h, ctypes.byref(h))
+            what = "oasis_create_shared"
         if rc != OASIS_OK:
-            raise OasisError(rc, "oasis_create: " + L.oasis_strerror(rc).decode())
+            raise OasisError(rc, f"{what}: " + L.oasis_strerror(rc).decode())
         self.h = h
         k, s, nb, bs = ctypes.c_int32(), ctypes.c_int32(), ctypes.c_int64(), ctypes.c_int32()
         L.oasis_get_dims(h, ctypes.byref(k), ctypes.byref(s), ctypes.byref(nb), ctypes.byref(bs))
@@ -181,7 +200,9 @@ class Oasis:
             pass
 
     # -- C-ABI calls
-    def oasis_load_prefix(self, k_host: np.ndarray, v_host: np.ndarray, length: int):
+    def oasis_load_prefix(self, k_host: np.ndarray | None, v_host: np.ndarray | None,
+                          length: int):
+        """k_host = v_host = None: start over from the prompt already in the host KV."""
         self._check(lib().oasis_load_prefix(self.h, _ptr(k_host), _ptr(v_host), length),
                     "oasis_load_prefix")
 
@@ -255,3 +276,30 @@ class Oasis:
         self._check(lib().oasis_read(self.h, BUF[which], offset, nbytes, out.ctypes.data),
                     "oasis_read")
         return out
+
+
+class LayerStep:
+    """Argument block of oasis_decode_layers for a fixed list of layer handles.
+
+    set(l, ...) stores the device pointers of layer l's inputs and output;
+    run() issues one decode step over all layers."""
+
+    def __init__(self, layers):
+        self.layers = list(layers)
+        n = len(self.layers)
+        self._h = (ctypes.c_void_p * n)(*[x.h for x in self.layers])
+        self._io = (oasis_layer_io * n)()
+
+    def set(self, l, k_new, v_new, q, drafts, out):
+        io = self._io[l]
+        io.k_new, io.v_new = _ptr(k_new), _ptr(v_new)
+        io.q, io.drafts, io.out = _ptr(q), _ptr(drafts), _ptr(out)
+
+    def run(self, n_drafts, cap, stream=None, side=None):
+        """side=None runs every layer on `stream` in order; a different stream
+        overlaps prediction/selection with attention."""
+        st = _stream(stream)
+        sd = st if side is None else _stream(side)
+        rc = lib().oasis_decode_layers(self._h, self._io, len(self.layers), n_drafts, cap, st, sd)
+        if rc != OASIS_OK:
+            self.layers[0]._check(rc, "oasis_decode_layers")

@@ -10,15 +10,21 @@
 //   - a copy stream (default priority) for the host -> HBM gather, and the
 //     events that order it against the caller's stream.
 //
+// Handles of layers whose KV is identical may share one host KV buffer
+// (oasis_create_shared); the buffer is reference counted.
+//
 // Ordering: select waits for the previous gather and attention; the gather
 // waits for select; attention, append and the next select wait for the
-// gather.  No call synchronises the host except the inspection calls.
+// gather; attention waits for the select.  A wait is issued only when the
+// producing call ran on another stream (one stream is in order by itself).
+// No call synchronises the host except the inspection calls.
 #include <stdarg.h>
 #include <stdio.h>
 #include <string.h>
 
 #include <algorithm>
 #include <cmath>
+#include <memory>
 #include <new>
 #include <string>
 #include <thread>
@@ -41,6 +47,25 @@ struct Timers {
     size_t used = 0;
     double ms = 0.0;
     int64_t n = 0;
+};
+
+// Pinned, device-mapped host KV; shared by the handles created from one owner.
+struct HostKV {
+    void *host = nullptr;
+    void *dev = nullptr;
+    size_t bytes = 0;
+    int64_t loaded = -1;   // tokens per sequence written by the last prompt load
+    int64_t high = 0;      // rows per sequence below which a load or an append wrote
+    ~HostKV() {
+        if (host) (void)hipHostFree(host);
+    }
+};
+
+// An event with the stream its last record went to.
+struct Mark {
+    hipEvent_t ev = nullptr;
+    hipStream_t st = nullptr;
+    bool set = false;
 };
 
 }  // namespace
@@ -66,7 +91,8 @@ struct oasis_handle {
     int64_t topk_nb = 0;
     int last_cap = 0;
 
-    void *host_kv = nullptr;      // host pointer (pinned)
+    std::shared_ptr<HostKV> hkv;
+    void *host_kv = nullptr;      // host pointer (pinned), hkv->host
     void *host_kv_dev = nullptr;  // device view of the same memory
     void *summ = nullptr, *slots = nullptr;
     float *scores = nullptr;
@@ -80,7 +106,8 @@ struct oasis_handle {
     size_t evict_cap = 0;
 
     hipStream_t copy = nullptr;
-    hipEvent_t ev_select = nullptr, ev_gather = nullptr, ev_attn = nullptr;
+    Mark m_select, m_gather, m_attn;
+    hipEvent_t ev_fork = nullptr, ev_join = nullptr;   // oasis_decode_layers
 
     int64_t n_select = 0;
     int32_t timing = 0;  // mask of timed kernel classes
@@ -128,6 +155,21 @@ void fold_timer(Timers &t) {
 }
 
 bool aligned16(const void *p) { return ((uintptr_t)p & 15u) == 0; }
+
+// Record m on st.
+int mark(oasis_t *h, Mark &m, hipStream_t st) {
+    HIP_OK(h, hipEventRecord(m.ev, st));
+    m.st = st;
+    m.set = true;
+    return OASIS_OK;
+}
+
+// Make st wait for the work behind m when it was recorded on another stream.
+int after(oasis_t *h, hipStream_t st, const Mark &m) {
+    if (!m.set || m.st == st) return OASIS_OK;
+    HIP_OK(h, hipStreamWaitEvent(st, m.ev, 0));
+    return OASIS_OK;
+}
 
 int tbegin(oasis_t *h, int cls, hipStream_t st) {
     (void)st;
@@ -205,11 +247,10 @@ void free_all(oasis_t *h) {
     (void)hipFree(h->err);
     (void)hipFree(h->stats);
     (void)hipFree(h->evict_buf);
-    if (h->host_kv) (void)hipHostFree(h->host_kv);
+    h->hkv.reset();
     if (h->copy) (void)hipStreamDestroy(h->copy);
-    if (h->ev_select) (void)hipEventDestroy(h->ev_select);
-    if (h->ev_gather) (void)hipEventDestroy(h->ev_gather);
-    if (h->ev_attn) (void)hipEventDestroy(h->ev_attn);
+    for (hipEvent_t e : {h->m_select.ev, h->m_gather.ev, h->m_attn.ev, h->ev_fork, h->ev_join})
+        if (e) (void)hipEventDestroy(e);
     for (auto &t : h->tm) {
         for (auto e : t.start) (void)hipEventDestroy(e);
         for (auto e : t.stop) (void)hipEventDestroy(e);
@@ -290,8 +331,10 @@ extern "C" const char *oasis_last_error(const oasis_t *h) {
 
 // ------------------------------------------------------------------ lifetime
 
-extern "C" int oasis_create(const oasis_layout *layout, int32_t block_size, int32_t budget_tokens,
-                            float fetch_ratio, oasis_t **out) {
+namespace {
+
+int create_handle(const oasis_layout *layout, int32_t block_size, int32_t budget_tokens,
+                  float fetch_ratio, const oasis_t *owner, oasis_t **out) {
     if (!layout || !out) return OASIS_E_INVAL;
     *out = nullptr;
     const oasis_layout &L = *layout;
@@ -344,19 +387,30 @@ extern "C" int oasis_create(const oasis_layout *layout, int32_t block_size, int3
     const int64_t units = D.units();
     const size_t e = D.esize();
     const size_t host_bytes = (size_t)units * NBmax * D.block_elems() * e;
-    if (hipHostMalloc(&h->host_kv, host_bytes, hipHostMallocMapped) != hipSuccess)
-        return bail(OASIS_E_NOMEM);
-    if (hipHostGetDevicePointer(&h->host_kv_dev, h->host_kv, 0) != hipSuccess)
-        return bail(OASIS_E_HIP);
-    {
-        char *p = (char *)h->host_kv;
+    if (owner) {
+        const oasis_layout &O = owner->L;
+        if (O.batch != L.batch || O.num_kv_heads != L.num_kv_heads || O.head_dim != L.head_dim ||
+            O.dtype != L.dtype || owner->D.bs != block_size || owner->D.NBmax != NBmax ||
+            owner->device != h->device || !owner->hkv || owner->hkv->bytes != host_bytes)
+            return bail(OASIS_E_INVAL);
+        h->hkv = owner->hkv;
+    } else {
+        auto hk = std::make_shared<HostKV>();
+        if (hipHostMalloc(&hk->host, host_bytes, hipHostMallocMapped) != hipSuccess)
+            return bail(OASIS_E_NOMEM);
+        hk->bytes = host_bytes;
+        if (hipHostGetDevicePointer(&hk->dev, hk->host, 0) != hipSuccess) return bail(OASIS_E_HIP);
+        char *p = (char *)hk->host;
         const size_t chunk = 64u << 20;
         const int64_t nchunks = (int64_t)((host_bytes + chunk - 1) / chunk);
         parallel_for(nchunks, [&](int64_t i) {
             const size_t off = (size_t)i * chunk;
             memset(p + off, 0, std::min(chunk, host_bytes - off));
         });
+        h->hkv = std::move(hk);
     }
+    h->host_kv = h->hkv->host;
+    h->host_kv_dev = h->hkv->dev;
 
     auto dmal = [&](void **p, size_t bytes) { return hipMalloc(p, bytes ? bytes : 16) == hipSuccess; };
     const int NS = h->plan.nsa;
@@ -386,13 +440,32 @@ extern "C" int oasis_create(const oasis_layout *layout, int32_t block_size, int3
         return bail(OASIS_E_HIP);
     if (reset_tables(h) != OASIS_OK) return bail(OASIS_E_HIP);
     if (hipStreamCreateWithFlags(&h->copy, hipStreamNonBlocking) != hipSuccess ||
-        hipEventCreateWithFlags(&h->ev_select, hipEventDisableTiming) != hipSuccess ||
-        hipEventCreateWithFlags(&h->ev_gather, hipEventDisableTiming) != hipSuccess ||
-        hipEventCreateWithFlags(&h->ev_attn, hipEventDisableTiming) != hipSuccess)
+        hipEventCreateWithFlags(&h->m_select.ev, hipEventDisableTiming) != hipSuccess ||
+        hipEventCreateWithFlags(&h->m_gather.ev, hipEventDisableTiming) != hipSuccess ||
+        hipEventCreateWithFlags(&h->m_attn.ev, hipEventDisableTiming) != hipSuccess ||
+        hipEventCreateWithFlags(&h->ev_fork, hipEventDisableTiming) != hipSuccess ||
+        hipEventCreateWithFlags(&h->ev_join, hipEventDisableTiming) != hipSuccess)
         return bail(OASIS_E_HIP);
     if (hipDeviceSynchronize() != hipSuccess) return bail(OASIS_E_HIP);
     *out = h;
     return OASIS_OK;
+}
+
+}  // namespace
+
+extern "C" int oasis_create(const oasis_layout *layout, int32_t block_size, int32_t budget_tokens,
+                            float fetch_ratio, oasis_t **out) {
+    return create_handle(layout, block_size, budget_tokens, fetch_ratio, nullptr, out);
+}
+
+extern "C" int oasis_create_shared(const oasis_layout *layout, int32_t block_size,
+                                   int32_t budget_tokens, float fetch_ratio, const oasis_t *owner,
+                                   oasis_t **out) {
+    if (!owner) {
+        if (out) *out = nullptr;
+        return OASIS_E_INVAL;
+    }
+    return create_handle(layout, block_size, budget_tokens, fetch_ratio, owner, out);
 }
 
 extern "C" int oasis_destroy(oasis_t *h) {
@@ -411,30 +484,42 @@ extern "C" int oasis_load_prefix(oasis_t *h, const void *k_host, const void *v_h
     if (len < 0 || len > h->L.max_tokens)
         return fail(h, OASIS_E_CAPACITY, "prefix of %lld tokens exceeds max_tokens %lld",
                     (long long)len, (long long)h->L.max_tokens);
-    if (len > 0 && (!k_host || !v_host)) return fail(h, OASIS_E_INVAL, "null prefix");
+    const bool reuse = !k_host && !v_host;
+    HostKV &hkv = *h->hkv;
+    if (reuse && hkv.loaded != len)
+        return fail(h, OASIS_E_STATE,
+                    "prefix reuse: the host KV holds a prompt of %lld tokens, not %lld",
+                    (long long)hkv.loaded, (long long)len);
+    if (!reuse && len > 0 && (!k_host || !v_host)) return fail(h, OASIS_E_INVAL, "null prefix");
     const Dims &D = h->D;
     HIP_OK(h, hipDeviceSynchronize());
     const size_t e = D.esize();
     const size_t row = (size_t)D.d * e;
     const int64_t NB = (len + D.bs - 1) / D.bs;
+    // Rows past the prompt are cleared up to the end of its next block and up
+    // to the highest row any append wrote, so slots never carry stale tokens.
+    const int64_t clear_to = std::min<int64_t>(std::max<int64_t>((NB + 1) * D.bs, hkv.high),
+                                               D.NBmax * D.bs);
     char *hk = (char *)h->host_kv;
     parallel_for(D.units(), [&](int64_t u) {
-        const char *ks = (const char *)k_host + (size_t)u * len * row;
-        const char *vs = (const char *)v_host + (size_t)u * len * row;
-        for (int64_t j = 0; j < D.NBmax; ++j) {
+        const char *ks = reuse ? nullptr : (const char *)k_host + (size_t)u * len * row;
+        const char *vs = reuse ? nullptr : (const char *)v_host + (size_t)u * len * row;
+        for (int64_t j = 0; j * D.bs < clear_to; ++j) {
             char *blk = hk + ((size_t)u * D.NBmax + j) * D.block_elems() * e;
             const int64_t p0 = j * D.bs;
             const int64_t n = j < NB ? std::min<int64_t>(D.bs, len - p0) : 0;
-            if (n > 0) {
+            if (n > 0 && !reuse) {
                 memcpy(blk, ks + p0 * row, n * row);
                 memcpy(blk + D.bs * row, vs + p0 * row, n * row);
             }
-            if (n < D.bs && (j < NB || j == NB)) {  // clear rows past the prefix
+            if (n < D.bs) {
                 memset(blk + n * row, 0, (D.bs - n) * row);
                 memset(blk + D.bs * row + n * row, 0, (D.bs - n) * row);
             }
         }
     });
+    hkv.loaded = len;
+    hkv.high = len;
     h->T = h->T_prefix = len;
     HIP_OK(h, launch_summary_build(D, h->host_kv_dev, len, h->summ, h->copy));
     HIP_OK(h, hipStreamSynchronize(h->copy));
@@ -504,13 +589,14 @@ extern "C" int oasis_append_kv(oasis_t *h, const void *k_dev, const void *v_dev,
     if (h->T >= h->L.max_tokens)
         return fail(h, OASIS_E_CAPACITY, "append: sequence already holds max_tokens = %lld",
                     (long long)h->L.max_tokens);
-    HIP_OK(h, hipStreamWaitEvent(stream, h->ev_gather, 0));
-    HIP_OK(h, hipStreamWaitEvent(stream, h->ev_attn, 0));
+    TRY(after(h, stream, h->m_gather));
+    TRY(after(h, stream, h->m_attn));
     TRY(flush_fetch(h, stream));
     LAUNCH(h, TM_APPEND, stream,
            launch_append(h->D, k_dev, v_dev, h->T, h->host_kv_dev, h->summ, h->block_slot,
                          h->slots, stream));
     ++h->T;
+    h->hkv->high = std::max(h->hkv->high, h->T);
     return OASIS_OK;
 }
 
@@ -564,8 +650,8 @@ extern "C" int oasis_select_and_fetch(oasis_t *h, int32_t cap, hipStream_t strea
     if (cap > D.K) cap = D.K;
     const int64_t t64 = h->T - h->T_prefix;
     if (t64 > INT32_MAX - 1) return fail(h, OASIS_E_CAPACITY, "step index overflow");
-    HIP_OK(h, hipStreamWaitEvent(stream, h->ev_gather, 0));
-    HIP_OK(h, hipStreamWaitEvent(stream, h->ev_attn, 0));
+    TRY(after(h, stream, h->m_gather));
+    TRY(after(h, stream, h->m_attn));
     TRY(flush_fetch(h, stream));
     if (h->topk_pending) {
         h->topk_pending = false;
@@ -581,15 +667,15 @@ extern "C" int oasis_select_and_fetch(oasis_t *h, int32_t cap, hipStream_t strea
                              h->att_slot, h->counts, h->stats, h->err, stream));
     }
     h->last_cap = cap;
+    TRY(mark(h, h->m_select, stream));
     if (h->fused) {
         h->fetch_pending = cap > 0;
     } else {
-        HIP_OK(h, hipEventRecord(h->ev_select, stream));
-        HIP_OK(h, hipStreamWaitEvent(h->copy, h->ev_select, 0));
+        TRY(after(h, h->copy, h->m_select));
         LAUNCH(h, TM_GATHER, h->copy,
                launch_gather(D, h->host_kv_dev, h->slots, h->fetch_block, h->fetch_slot, D.K,
                              h->counts, 4, 2, cap, h->copy));
-        HIP_OK(h, hipEventRecord(h->ev_gather, h->copy));
+        TRY(mark(h, h->m_gather, h->copy));
     }
     ++h->n_select;
     h->selected = true;
@@ -610,8 +696,8 @@ extern "C" int oasis_evict(oasis_t *h, const int32_t *blocks_host, const int32_t
         h->evict_cap = n;
     }
     int32_t *dblocks = h->evict_buf, *dcounts = h->evict_buf + (size_t)D.units() * max_per_unit;
-    HIP_OK(h, hipStreamWaitEvent(stream, h->ev_gather, 0));
-    HIP_OK(h, hipStreamWaitEvent(stream, h->ev_attn, 0));
+    TRY(after(h, stream, h->m_gather));
+    TRY(after(h, stream, h->m_attn));
     TRY(flush_fetch(h, stream));
     HIP_OK(h, hipMemcpyAsync(dblocks, blocks_host, sizeof(int32_t) * D.units() * max_per_unit,
                              hipMemcpyHostToDevice, stream));
@@ -628,7 +714,8 @@ extern "C" int oasis_sparse_attn(oasis_t *h, const void *q_dev, float *out_dev,
         return h ? fail(h, OASIS_E_INVAL, "attn: null or misaligned pointer") : OASIS_E_INVAL;
     if (!h->selected) return fail(h, OASIS_E_STATE, "attention before select");
     const Dims &D = h->D;
-    HIP_OK(h, hipStreamWaitEvent(stream, h->ev_gather, 0));
+    TRY(after(h, stream, h->m_select));
+    TRY(after(h, stream, h->m_gather));
     int mode = 0, nsf = 0;
     if (h->fetch_pending) {
         if (h->plan.mfma) {
@@ -645,8 +732,66 @@ extern "C" int oasis_sparse_attn(oasis_t *h, const void *q_dev, float *out_dev,
                             stream));
     LAUNCH(h, TM_COMBINE, stream,
            launch_combine(D, h->plan, nsf, h->part_m, h->part_l, h->part_acc, out_dev, stream));
-    HIP_OK(h, hipEventRecord(h->ev_attn, stream));
+    TRY(mark(h, h->m_attn, stream));
     return OASIS_OK;
+}
+
+// ------------------------------------------------------------------ layer pipeline
+
+// One decode step over the layers of a model.  With side != stream, the
+// append / predict / select of every layer go to `side` in layer order and
+// each layer's attention goes to `stream` once that layer's select is done,
+// so prediction and selection of later layers run under the attention (and
+// its fused host fetch) of earlier ones (OasisKV page, Fig. 8: predict,
+// select and transfer per layer overlapped with compute).  Per-layer
+// ordering across steps comes from the handles' own marks.
+extern "C" int oasis_decode_layers(oasis_t *const *layers, const oasis_layer_io *io,
+                                   int32_t n_layers, int32_t n_drafts, int32_t cap,
+                                   hipStream_t stream, hipStream_t side) {
+    if (!layers || !io || n_layers < 1) return OASIS_E_INVAL;
+    for (int32_t l = 0; l < n_layers; ++l) {
+        if (!layers[l]) return OASIS_E_INVAL;
+        for (int32_t m = 0; m < l; ++m)
+            if (layers[m] == layers[l])
+                return fail(layers[l], OASIS_E_INVAL, "decode_layers: handle %d repeats %d", l, m);
+        if ((io[l].k_new == nullptr) != (io[l].v_new == nullptr))
+            return fail(layers[l], OASIS_E_INVAL, "decode_layers: layer %d has k without v", l);
+    }
+    oasis_t *h0 = layers[0];
+    const bool overlap = side != stream;
+    if (overlap) {
+        HIP_OK(h0, hipEventRecord(h0->ev_fork, stream));
+        HIP_OK(h0, hipStreamWaitEvent(side, h0->ev_fork, 0));
+    }
+    hipStream_t pre = overlap ? side : stream;
+    int rc = OASIS_OK, bad = -1;
+    // All pre-attention work is queued first: the side stream runs ahead of
+    // the attention stream by as many layers as it can.
+    for (int32_t l = 0; l < n_layers && rc == OASIS_OK; ++l) {
+        oasis_t *h = layers[l];
+        if (io[l].k_new) rc = oasis_append_kv(h, io[l].k_new, io[l].v_new, pre);
+        if (rc == OASIS_OK)
+            rc = oasis_predict(h, io[l].q, io[l].drafts, n_drafts, nullptr, nullptr, pre);
+        if (rc == OASIS_OK) rc = oasis_select_and_fetch(h, cap, pre);
+        if (rc == OASIS_OK && !overlap) rc = oasis_sparse_attn(h, io[l].q, io[l].out, stream);
+        if (rc != OASIS_OK) bad = l;
+    }
+    if (overlap) {
+        for (int32_t l = 0; l < n_layers && rc == OASIS_OK; ++l) {
+            rc = oasis_sparse_attn(layers[l], io[l].q, io[l].out, stream);
+            if (rc != OASIS_OK) bad = l;
+        }
+        // Join: the caller's stream sees the side stream's work even where a
+        // call failed half way.
+        if (hipEventRecord(h0->ev_join, side) != hipSuccess ||
+            hipStreamWaitEvent(stream, h0->ev_join, 0) != hipSuccess)
+            return rc != OASIS_OK ? rc : fail(h0, OASIS_E_HIP, "decode_layers: join failed");
+    }
+    if (bad > 0) {
+        const std::string msg = layers[bad]->last_error;
+        fail(h0, rc, "decode_layers: layer %d: %s", bad, msg.c_str());
+    }
+    return rc;
 }
 
 // ------------------------------------------------------------------ inspection

@@ -77,3 +77,98 @@ class LayerRunner:
 def _cap_from_ratio(ratio, k):
     from . import cap_from_ratio
     return cap_from_ratio(ratio, k)
+
+
+class ModelRunner:
+    """All layers of a multi-layer workload, stepped by oasis_decode_layers.
+
+    Layer l's K, V and current query are those of data layer
+    ``synth.data_layer(w, l, data_layers)``: layers of one data layer share a
+    pinned host KV (oasis_create_shared) so that the model fits host memory,
+    and receive the same appended tokens.  Each layer has its own HBM state
+    (summaries, slot pool, tables) and its own draft noise, so selections
+    differ between layers.
+    """
+
+    def __init__(self, w: synth.Workload, n_steps: int, data_layers: int = 2,
+                 device: str = "cuda", cap: int | None = None, threads: int = 16, log=None):
+        from . import LayerStep
+        self.w, self.n_steps = w, n_steps
+        self.n_layers = w.layers
+        self.H = max(1, min(data_layers, w.layers))
+        self.T0 = w.prefix_tokens
+        n_tok = self.T0 + n_steps
+        self.cap = cap if cap is not None else (
+            w.cap if w.cap > 0 else _cap_from_ratio(w.fetch_ratio, w.k_blocks))
+        dt = OASIS_F32 if w.dtype == synth.F32 else OASIS_BF16
+        mk = lambda owner=None: Oasis(w.batch, w.q_heads, w.kv_heads, w.head_dim, dt, w.drafts,
+                                      n_tok, block_size=w.block_size,
+                                      budget_tokens=w.budget_tokens, fetch_ratio=w.fetch_ratio,
+                                      slots_per_head=w.n_slots, share_host_with=owner)
+        self.handles = [None] * self.n_layers
+        self.app_k, self.app_v, self.q = [], [], []
+        for g in range(self.H):
+            if log:
+                log(f"generating data layer {g} of {self.H}")
+            Kp, Vp, Ka, Va = synth.layer_kv_split(w, self.T0, n_steps, g, threads)
+            owner = mk()
+            owner.oasis_load_prefix(Kp, Vp, self.T0)
+            del Kp, Vp
+            self.app_k.append(to_device(Ka, device))
+            self.app_v.append(to_device(Va, device))
+            del Ka, Va
+            self.q.append(to_device(synth.queries(w, g), device))
+            for l in range(g, self.n_layers, self.H):
+                if l == g:
+                    self.handles[l] = owner
+                else:
+                    h = mk(owner)
+                    h.oasis_load_prefix(None, None, self.T0)
+                    self.handles[l] = h
+        # draft queries of every (step, layer): [steps + 1][layers] device tensors
+        from concurrent.futures import ThreadPoolExecutor
+        keys = [(t, l) for t in range(n_steps + 1) for l in range(self.n_layers)]
+        with ThreadPoolExecutor(threads) as ex:
+            host = list(ex.map(lambda k: synth.drafts(w, k[0], k[1], self.group_of(k[1])), keys))
+        flat = [to_device(a, device) for a in host]
+        del host
+        self.drafts = [flat[t * self.n_layers:(t + 1) * self.n_layers]
+                       for t in range(n_steps + 1)]
+        self.out = torch.empty((self.n_layers, w.batch, w.q_heads, w.head_dim),
+                               dtype=torch.float32, device=device)
+        self.step_args = LayerStep(self.handles)
+        self.t = 0
+
+    def group_of(self, l: int) -> int:
+        return synth.data_layer(self.w, l, self.H)
+
+    def reset(self):
+        """Every layer starts over from the prompt (synchronous)."""
+        for h in self.handles:
+            h.oasis_load_prefix(None, None, self.T0)
+        self.t = 0
+
+    def _fill(self, t: int):
+        a = self.step_args
+        for l in range(self.n_layers):
+            g = self.group_of(l)
+            k = self.app_k[g][t - 1] if t > 0 else None
+            v = self.app_v[g][t - 1] if t > 0 else None
+            a.set(l, k, v, self.q[g], self.drafts[t][l], self.out[l])
+
+    def admission(self, stream=None, side=None):
+        """Untimed step 0 on every layer: select on the prompt, fetch it all."""
+        self._fill(0)
+        self.step_args.run(self.w.drafts, self.w.k_blocks, stream=stream, side=side)
+
+    def step(self, t: int, stream=None, side=None, cap: int | None = None):
+        """Decode step t (1-based) over all layers; side=None serialises."""
+        self._fill(t)
+        self.step_args.run(self.w.drafts, self.cap if cap is None else cap, stream=stream,
+                           side=side)
+        self.t = t
+
+    def close(self):
+        for h in self.handles[::-1]:
+            if h is not None:
+                h.close()

@@ -21,6 +21,7 @@ in place of model activations, which are not available.
 from __future__ import annotations
 
 import dataclasses
+import functools
 from concurrent.futures import ThreadPoolExecutor
 
 import numpy as np
@@ -153,9 +154,17 @@ def queries(w: Workload, layer: int = 0) -> np.ndarray:
     return encode(x, w.dtype)
 
 
-def drafts(w: Workload, step: int, layer: int = 0) -> np.ndarray:
-    """Draft queries [D][b][g][d] = q + N(0, sigma^2), redrawn every step."""
-    q = decode_f32(queries(w, layer), w.dtype)
+@functools.lru_cache(maxsize=8)
+def _queries_f32(w: Workload, layer: int) -> np.ndarray:
+    return decode_f32(queries(w, layer), w.dtype)
+
+
+def drafts(w: Workload, step: int, layer: int = 0, q_layer: int | None = None) -> np.ndarray:
+    """Draft queries [D][b][g][d] = q + N(0, sigma^2), redrawn every step.
+
+    q is layer q_layer's query (default: the same layer); the noise stream is
+    layer's own."""
+    q = _queries_f32(w, layer if q_layer is None else q_layer)
     g = _rng(w, layer, _DRAFT, step)
     noise = g.standard_normal((w.drafts, w.batch, w.q_heads, w.head_dim), dtype=np.float32)
     return encode(q[None] + np.float32(w.draft_sigma) * noise, w.dtype)
@@ -220,6 +229,37 @@ def layer_kv(w: Workload, n_tokens: int, layer: int = 0, threads: int = 8):
     with ThreadPoolExecutor(threads) as ex:
         list(ex.map(one, range(w.batch * w.kv_heads)))
     return K, V
+
+
+def layer_kv_split(w: Workload, n_prefix: int, n_append: int, layer: int = 0,
+                   threads: int = 8):
+    """The same draws as layer_kv(w, n_prefix + n_append, layer), split into
+    the prompt K, V [B][Hkv][n_prefix][d] and the appended tokens
+    [n_append][B][Hkv][d] (one slab per decode step)."""
+    dt = np.float32 if w.dtype == F32 else np.uint16
+    d = w.head_dim
+    Kp = np.empty((w.batch, w.kv_heads, n_prefix, d), dtype=dt)
+    Vp = np.empty_like(Kp)
+    Ka = np.empty((n_append, w.batch, w.kv_heads, d), dtype=dt)
+    Va = np.empty_like(Ka)
+    u = heavy_direction(w, layer)
+
+    def one(idx):
+        b, h = divmod(idx, w.kv_heads)
+        k, v = unit_kv(w, b, h, n_prefix + n_append, layer, u[b, h])
+        Kp[b, h], Vp[b, h] = k[:n_prefix], v[:n_prefix]
+        Ka[:, b, h], Va[:, b, h] = k[n_prefix:], v[n_prefix:]
+
+    with ThreadPoolExecutor(threads) as ex:
+        list(ex.map(one, range(w.batch * w.kv_heads)))
+    return Kp, Vp, Ka, Va
+
+
+def data_layer(w: Workload, layer: int, data_layers: int) -> int:
+    """Multi-layer workloads whose full host KV does not fit host memory
+    alias layer l's K, V and current query onto data layer l mod data_layers;
+    each layer keeps its own draft noise."""
+    return layer % max(1, min(data_layers, w.layers))
 
 
 # ---------------------------------------------------------------- residency / eviction draws

@@ -260,12 +260,70 @@ class FreeRunning(Parity):
     the oracle select applied to the GPU's previous tables, and the attention
     against the oracle attention over the GPU's attended list."""
 
+    q_layer = None   # layer whose query the drafts perturb (None: self.layer)
+
     def _tables(self):
         h = self.run.h
         S = h.slots
         sb, lu = h.read("SLOT_BLOCK"), h.read("LAST_USED")
         return {(b, hh): (self._unit_slice(sb, b, hh, S).copy(),
                           self._unit_slice(lu, b, hh, S).copy()) for (b, hh) in self.units}
+
+    def after_admission(self):
+        """Admission ran on the GPU: the oracle units only track the KV and
+        scores from here (selection is checked against the GPU's tables)."""
+        for (b, hh) in self.units:
+            self.oru[(b, hh)].slot_block[:] = -1
+        return self._tables()
+
+    def verify_step(self, t, prev, report, gpu_scores, cap, check_payload=False):
+        """Check step t of the handle against the oracle; returns its tables."""
+        w, h = self.w, self.run.h
+        K = h.k_blocks
+        ids = h.read("IDS")
+        fb, fs = h.read("FETCH_BLOCK"), h.read("FETCH_SLOT")
+        ab, ast = h.read("ATT_BLOCK"), h.read("ATT_SLOT")
+        cnt = h.read("COUNTS")
+        out = self.run.out.cpu().numpy()
+        drafts = oracle.to_f64(synth.drafts(w, t, self.layer, self.q_layer), w.dtype)
+        now = self._tables()
+        for (b, hh) in self.units:
+            tag = f"free step {t} layer {self.layer} unit {(b, hh)}"
+            unit = self.oru[(b, hh)]
+            unit.append()
+            x, cur = oracle.unit_rows(self.qf, drafts, b, hh, self.G)
+            ref = unit.score(x)
+            nb = unit.nb
+            err = np.abs(gpu_scores[b, hh, :nb].astype(np.float64) - ref) / score_scale(unit, x)
+            report["score_err"] = max(report["score_err"], float(err.max()))
+            assert err.max() <= SCORE_TOL, tag + f" score err {err.max():.3g}"
+            exp_ids = oracle.topk(gpu_scores[b, hh, :nb], K)
+            got_ids = self._unit_slice(ids, b, hh, K)
+            assert np.array_equal(got_ids, exp_ids), tag + " ids"
+            sb0, lu0 = prev[(b, hh)]
+            sb_exp, lu_exp = sb0.copy(), lu0.copy()
+            r = oracle.select(sb_exp, lu_exp, exp_ids, cap, t)
+            c = self._unit_slice(cnt, b, hh, 4)
+            na, nh, nf = int(c[0]), int(c[1]), int(c[2])
+            assert (na, nh, nf) == (len(r["att_block"]), r["n_hit"], len(r["fetch_block"])), tag
+            assert np.array_equal(self._unit_slice(fb, b, hh, K)[:nf], r["fetch_block"]), tag
+            assert np.array_equal(self._unit_slice(fs, b, hh, K)[:nf], r["fetch_slot"]), tag
+            assert np.array_equal(self._unit_slice(ab, b, hh, K)[:na], r["att_block"]), tag
+            assert np.array_equal(self._unit_slice(ast, b, hh, K)[:na], r["att_slot"]), tag
+            assert np.array_equal(now[(b, hh)][0], sb_exp), tag + " slot_block"
+            assert np.array_equal(now[(b, hh)][1], lu_exp), tag + " last_used"
+            exp_out = oracle.attention(cur, unit.keys, unit.vals, w.dtype, w.block_size,
+                                       unit.T, r["att_block"])
+            g0 = hh * self.G
+            e = float(np.max(np.abs(out[b, g0:g0 + self.G].astype(np.float64) - exp_out)))
+            report["attn_err"] = max(report["attn_err"], e)
+            assert e <= ATTN_TOL, tag + f" attention err {e:.3g}"
+            report["fetched"] += nf
+        if check_payload:
+            self.check_payload(t)
+            self.check_summary()
+        report["steps"] = t
+        return now
 
     def run_free(self, steps=None, check_payload_every=8):
         w, run, h = self.w, self.run, self.run.h
@@ -275,10 +333,9 @@ class FreeRunning(Parity):
         if w.admission:
             run.admission()
             torch.cuda.synchronize()
-            for (b, hh) in self.units:
-                self.oru[(b, hh)].slot_block[:] = -1
-        prev = self._tables()
-        draft_cache = {}
+            prev = self.after_admission()
+        else:
+            prev = self._tables()
         for t in range(1, steps + 1):
             if w.forced_evict_frac > 0:
                 ab, cnt = h.read("ATT_BLOCK"), h.read("COUNTS")
@@ -303,50 +360,42 @@ class FreeRunning(Parity):
             h.oasis_sparse_attn(run.q, run.out)
             torch.cuda.synchronize()
             h.oasis_check()
-            gpu_scores = self.scores_dev.cpu().numpy()
-            ids = h.read("IDS")
-            fb, fs = h.read("FETCH_BLOCK"), h.read("FETCH_SLOT")
-            ab, ast = h.read("ATT_BLOCK"), h.read("ATT_SLOT")
-            cnt = h.read("COUNTS")
-            out = run.out.cpu().numpy()
-            drafts = oracle.to_f64(synth.drafts(w, t, self.layer), w.dtype)
-            now = self._tables()
-            for (b, hh) in self.units:
-                tag = f"free step {t} unit {(b, hh)}"
-                unit = self.oru[(b, hh)]
-                unit.append()
-                x, cur = oracle.unit_rows(self.qf, drafts, b, hh, self.G)
-                ref = unit.score(x)
-                nb = unit.nb
-                err = np.abs(gpu_scores[b, hh, :nb].astype(np.float64) - ref) / score_scale(unit, x)
-                report["score_err"] = max(report["score_err"], float(err.max()))
-                assert err.max() <= SCORE_TOL, tag + f" score err {err.max():.3g}"
-                exp_ids = oracle.topk(gpu_scores[b, hh, :nb], K)
-                got_ids = self._unit_slice(ids, b, hh, K)
-                assert np.array_equal(got_ids, exp_ids), tag + " ids"
-                sb0, lu0 = prev[(b, hh)]
-                r = oracle.select(sb0.copy(), lu0.copy(), exp_ids, self.cap, t)
-                sb_exp, lu_exp = sb0.copy(), lu0.copy()
-                oracle.select(sb_exp, lu_exp, exp_ids, self.cap, t)
-                c = self._unit_slice(cnt, b, hh, 4)
-                na, nh, nf = int(c[0]), int(c[1]), int(c[2])
-                assert (na, nh, nf) == (len(r["att_block"]), r["n_hit"], len(r["fetch_block"])), tag
-                assert np.array_equal(self._unit_slice(fb, b, hh, K)[:nf], r["fetch_block"]), tag
-                assert np.array_equal(self._unit_slice(fs, b, hh, K)[:nf], r["fetch_slot"]), tag
-                assert np.array_equal(self._unit_slice(ab, b, hh, K)[:na], r["att_block"]), tag
-                assert np.array_equal(self._unit_slice(ast, b, hh, K)[:na], r["att_slot"]), tag
-                assert np.array_equal(now[(b, hh)][0], sb_exp), tag + " slot_block"
-                assert np.array_equal(now[(b, hh)][1], lu_exp), tag + " last_used"
-                exp_out = oracle.attention(cur, unit.keys, unit.vals, w.dtype, w.block_size,
-                                           unit.T, r["att_block"])
-                g0 = hh * self.G
-                e = float(np.max(np.abs(out[b, g0:g0 + self.G].astype(np.float64) - exp_out)))
-                report["attn_err"] = max(report["attn_err"], e)
-                assert e <= ATTN_TOL, tag + f" attention err {e:.3g}"
-                report["fetched"] += nf
-            if t % check_payload_every == 0 or t == steps:
-                self.check_payload(t)
-                self.check_summary()
-            prev = now
-            report["steps"] = t
+            prev = self.verify_step(t, prev, report, self.scores_dev.cpu().numpy(), self.cap,
+                                    check_payload=(t % check_payload_every == 0 or t == steps))
         return report
+
+
+class PipelineLayer(FreeRunning):
+    """Free-running checks of one layer of a ModelRunner (oasis_decode_layers).
+
+    The layer's K, V and query come from its data layer; its drafts from its
+    own noise stream around that query."""
+
+    def __init__(self, mr, layer: int, units, unit_kv: dict):
+        from types import SimpleNamespace
+        w = mr.w
+        self.w, self.n_steps, self.units = w, mr.n_steps, list(units)
+        self.layer, self.q_layer = layer, mr.group_of(layer)
+        h = mr.handles[layer]
+        self.run = SimpleNamespace(h=h, out=mr.out[layer])
+        self.cap = mr.cap
+        self.K = {k: kv[0] for k, kv in unit_kv.items()}
+        self.V = {k: kv[1] for k, kv in unit_kv.items()}
+        self.oru = {k: initial_unit(w, k[0], k[1], mr.n_steps, self.q_layer, kv=unit_kv[k])
+                    for k in self.units}
+        self.qf = oracle.to_f64(synth.queries(w, self.q_layer), w.dtype)
+        self.G = w.group
+        self.NBmax = h.nb_max
+        self.prev_att = {}
+
+    def scores(self):
+        w = self.w
+        return self.run.h.read("SCORES", np.float32).reshape(w.batch, w.kv_heads, self.NBmax)
+
+
+def pipeline_unit_kv(mr, layer, units):
+    """Oracle-side K, V of sampled units of a ModelRunner layer (its data layer's draws)."""
+    w, g = mr.w, mr.group_of(layer)
+    n_tok = w.prefix_tokens + mr.n_steps
+    u = synth.heavy_direction(w, g)
+    return {k: synth.unit_kv(w, k[0], k[1], n_tok, g, u[k[0], k[1]]) for k in units}

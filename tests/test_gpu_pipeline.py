@@ -1,0 +1,140 @@
+"""Multi-layer decode through oasis_decode_layers: layers sharing a host KV,
+prediction/selection overlapped with attention on a second stream.
+
+  - the overlapped schedule gives bit-identical outputs, tables and slot
+    payloads to the serial one;
+  - sampled (layer, unit) pairs of the 36-layer Qwen3-8B model at full size
+    are checked step by step against the oracle (free-running checks:
+    scores 1e-4, ids / select / tables bit-exact, attention 2e-3);
+  - the fetch-all cap and a restart from the shared prompt (the fetch-ratio
+    sweep) keep those checks.
+"""
+import numpy as np
+import pytest
+import torch
+
+import synth
+
+pytestmark = pytest.mark.gpu
+
+
+@pytest.fixture(scope="module", autouse=True)
+def _gpu():
+    assert torch.cuda.is_available(), "GPU tests need a GPU"
+    import lookahead_sparse_kv_oasis_amd as L
+    L.lib()
+
+
+def _log(msg):
+    print(msg, flush=True)
+
+
+SMALL = synth.QWEN3_8B_36L.with_(batch=4, prefix_tokens=16 * 300 + 5, layers=6, steps=10,
+                                 budget_tokens=16 * 64)
+
+STATE_BUFS = ["IDS", "SLOT_BLOCK", "BLOCK_SLOT", "LAST_USED", "FETCH_BLOCK", "FETCH_SLOT",
+              "ATT_BLOCK", "ATT_SLOT", "COUNTS"]
+
+
+def _runner(w, steps, data_layers=2, **kw):
+    from lookahead_sparse_kv_oasis_amd.runner import ModelRunner
+    return ModelRunner(w, steps, data_layers=data_layers, threads=8, log=_log, **kw)
+
+
+def test_overlapped_schedule_matches_serial_bitwise():
+    w = SMALL
+    a = _runner(w, w.steps)
+    b = _runner(w, w.steps)
+    side = torch.cuda.Stream()
+    a.admission(side=side)
+    b.admission()
+    for t in range(1, w.steps + 1):
+        a.step(t, side=side)
+        b.step(t)
+        torch.cuda.synchronize()
+        assert torch.equal(a.out, b.out), f"step {t}: outputs differ"
+    for l in range(w.layers):
+        ha, hb = a.handles[l], b.handles[l]
+        for buf in STATE_BUFS:
+            assert np.array_equal(ha.read(buf), hb.read(buf)), f"layer {l} {buf}"
+        assert np.array_equal(ha.read("SLOTS", np.uint8), hb.read("SLOTS", np.uint8)), \
+            f"layer {l} slot payloads"
+        sa, sb = ha.oasis_get_stats(), hb.oasis_get_stats()
+        assert {k: sa[k] for k in ("hits", "misses", "fetched")} == \
+            {k: sb[k] for k in ("hits", "misses", "fetched")}
+        ha.oasis_check()
+    # layers of one data layer share the host KV and differ in their selections
+    assert np.array_equal(a.handles[0].read("HOST_KV", np.uint8),
+                          a.handles[2].read("HOST_KV", np.uint8))
+    assert not np.array_equal(a.handles[0].read("IDS"), a.handles[2].read("IDS"))
+    a.close()
+    b.close()
+
+
+def _check_layers(mr, layers, units, steps, side, cap=None, check_payload_every=4):
+    from tests.gpu_parity import PipelineLayer, pipeline_unit_kv
+    checks = [PipelineLayer(mr, l, units, pipeline_unit_kv(mr, l, units)) for l in layers]
+    cap = mr.cap if cap is None else cap
+    reports = [dict(score_err=0.0, attn_err=0.0, steps=0, fetched=0) for _ in checks]
+    mr.admission(side=side)
+    torch.cuda.synchronize()
+    prev = [c.after_admission() for c in checks]
+    for t in range(1, steps + 1):
+        mr.step(t, side=side, cap=cap)
+        torch.cuda.synchronize()
+        for i, c in enumerate(checks):
+            c.run.h.oasis_check()
+            prev[i] = c.verify_step(t, prev[i], reports[i], c.scores(), cap,
+                                    check_payload=(t % check_payload_every == 0 or t == steps))
+    return reports
+
+
+def test_reduced_model_against_oracle_and_fetch_all_restart():
+    w = SMALL
+    mr = _runner(w, w.steps)
+    side = torch.cuda.Stream()
+    units = [(0, 0), (3, 7), (1, 4)]
+    rep = _check_layers(mr, [0, 3, 5], units, w.steps, side)
+    _log(f"reduced model, cap {mr.cap}: {rep}")
+    # restart every layer from the shared prompt with the fetch-all cap
+    mr.reset()
+    rep = _check_layers(mr, [1, 4], units, w.steps, side, cap=w.k_blocks)
+    _log(f"reduced model, fetch all: {rep}")
+    mr.close()
+
+
+def test_decode_layers_rejects_bad_arguments():
+    from lookahead_sparse_kv_oasis_amd import LayerStep, OasisError, Oasis, OASIS_BF16
+    w = SMALL.with_(layers=2, steps=2)
+    mr = _runner(w, 2)
+    bad = LayerStep([mr.handles[0], mr.handles[0]])
+    for l in range(2):
+        bad.set(l, None, None, mr.q[0], mr.drafts[1][0], mr.out[0])
+    with pytest.raises(OasisError):
+        bad.run(w.drafts, 2)
+    half = LayerStep(mr.handles)
+    for l in range(2):
+        half.set(l, mr.app_k[0][0], None, mr.q[0], mr.drafts[1][l], mr.out[l])
+    with pytest.raises(OasisError):
+        half.run(w.drafts, 2)
+    # a shared handle must match the owner's host layout
+    with pytest.raises(OasisError):
+        Oasis(w.batch + 1, w.q_heads, w.kv_heads, w.head_dim, OASIS_BF16, w.drafts,
+              w.prefix_tokens + 2, share_host_with=mr.handles[0])
+    # reuse of the host prompt needs the same length
+    with pytest.raises(OasisError):
+        mr.handles[1].oasis_load_prefix(None, None, w.prefix_tokens - 1)
+    mr.close()
+
+
+@pytest.mark.slow
+def test_qwen3_8b_36_layers_full_size_sampled_layers():
+    """The 36-layer model at batch 64 and 64K context (two data layers),
+    overlapped schedule, fetch ratio 0.02."""
+    w = synth.QWEN3_8B_36L
+    mr = _runner(w, w.steps)
+    side = torch.cuda.Stream()
+    rep = _check_layers(mr, [0, 19, 35], [(0, 0), (37, 3), (63, 7)], w.steps, side,
+                        check_payload_every=8)
+    _log(f"{w.name}: {rep}")
+    mr.close()
