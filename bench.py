@@ -8,8 +8,9 @@ memory and block summaries in HBM) before the timed region.
 
 Prints one JSON line.  `value` is decode layer-steps/s; the roofline object
 is for the dominant HBM kernel, with its algorithmic bytes per launch divided
-by its average launch time from HIP events recorded on its stream during the
-timed region.  The CPU baseline is the fp64 oracle timed on a bounded sample
+by its average launch time from HIP events attached to its dispatches on its
+stream during the timed region (one launch in --timing-period, spread evenly
+over the region, so that the events barely disturb the measured throughput).  The CPU baseline is the fp64 oracle timed on a bounded sample
 of the same workload on the host cores.
 """
 from __future__ import annotations
@@ -87,33 +88,39 @@ def pinned_h2d_peak_gbps(nbytes=1 << 30, reps=5):
     return best
 
 
-def cpu_baseline(w, target_s=15.0, max_threads=16):
-    """The fp64 oracle (as it stands) on a bounded sample of the workload:
-    a few (b, KV head) units stepped through the same decode steps on a pool
-    of host threads.  Extrapolated to whole-layer steps/s."""
+def cpu_baseline(w, target_s=12.0, max_threads=16):
+    """The fp64 oracle (as it stands) on a bounded sample of the workload: up
+    to 64 (b, KV head) units stepped through the same decode steps (appended
+    tokens continue the seeded draws past the workload's step count) on a pool
+    of host threads, sized from a one-step calibration to about target_s of
+    wall time.  Extrapolated to whole-layer steps/s."""
     from concurrent.futures import ThreadPoolExecutor
-
-    import numpy as np
 
     import oracle
     import synth
     from oracle.trajectory import initial_unit, workload_cap
 
     threads = min(max_threads, len(os.sched_getaffinity(0)))
-    n_units = threads
+    units_all = w.batch * w.kv_heads
+    n_units = min(units_all, 64)
     cap = workload_cap(w)
     qf = oracle.to_f64(synth.queries(w), w.dtype)
-    units = [(i % w.batch, (i * 7) % w.kv_heads) for i in range(n_units)]
+    units = [divmod((i * 37) % units_all, w.kv_heads) for i in range(n_units)]
     # calibrate: one unit, two steps
-    probe = initial_unit(w, *units[0], 64)
-    dr = oracle.to_f64(synth.drafts(w, 1), w.dtype)
-    x, cur = oracle.unit_rows(qf, dr, *units[0], w.group)
-    t0 = time.perf_counter()
-    probe.step(1, x, cur, cap)
-    one = time.perf_counter() - t0
-    steps = int(max(2, min(64, target_s / max(one, 1e-6))))
-    us = [initial_unit(w, b, h, steps, kv=None) for (b, h) in units]
-    drafts = [oracle.to_f64(synth.drafts(w, t), w.dtype) for t in range(1, steps + 1)]
+    probe = initial_unit(w, *units[0], 2)
+    one = []
+    for t in (1, 2):
+        x, cur = oracle.unit_rows(qf, oracle.to_f64(synth.drafts(w, t), w.dtype), *units[0],
+                                  w.group)
+        t0 = time.perf_counter()
+        probe.step(t, x, cur, cap)
+        one.append(time.perf_counter() - t0)
+    per = min(one)
+    steps = int(max(2, min(1024, target_s * threads / max(per * n_units, 1e-9))))
+    with ThreadPoolExecutor(threads) as ex:
+        us = list(ex.map(lambda bh: initial_unit(w, bh[0], bh[1], steps), units))
+        drafts = list(ex.map(lambda t: oracle.to_f64(synth.drafts(w, t), w.dtype),
+                             range(1, steps + 1)))
 
     def run(i):
         b, h = units[i]
@@ -127,13 +134,13 @@ def cpu_baseline(w, target_s=15.0, max_threads=16):
     dt = time.perf_counter() - t0
     unit_steps_per_s = n_units * steps / dt
     return {
-        "value": unit_steps_per_s / (w.batch * w.kv_heads),
+        "value": unit_steps_per_s / units_all,
         "unit": "layer-steps/s",
         "cores": threads,
         "kind": "oracle",
-        "sample": f"{n_units} of {w.batch * w.kv_heads} (batch row, KV head) units x {steps} "
-                  f"decode steps of {w.name} (append, fp64 score, top-K, select, attention), "
-                  f"{dt:.1f} s wall on {threads} threads, scaled to one whole-layer step",
+        "sample": f"{n_units} of {units_all} (batch row, KV head) units x {steps} decode steps "
+                  f"of {w.name} (append, fp64 score, top-K, select, attention), {dt:.1f} s "
+                  f"wall on {threads} threads, scaled to one whole-layer step",
     }
 
 
@@ -151,6 +158,9 @@ def main():
                          "(reference for the HBM byte counters) and exit")
     ap.add_argument("--no-kernel-timing", action="store_true",
                     help="skip the per-kernel HIP events (roofline fields become null)")
+    ap.add_argument("--timing-period", type=int, default=4,
+                    help="attach HIP events to one launch in this many of each timed kernel "
+                         "(spread over the timed region)")
     ap.add_argument("--schedule", default="overlap", choices=["overlap", "serial", "both"],
                     help="multi-layer workloads: prediction/selection of later layers on a "
                          "second stream under earlier layers' attention, or one stream")
@@ -158,6 +168,8 @@ def main():
                     help="multi-layer workloads: distinct host KV buffers the layers alias")
     ap.add_argument("--fetch-ratio", default=None,
                     help="override the workload's fetch ratio ('all' = cap K)")
+    ap.add_argument("--layers", type=int, default=None,
+                    help="override the workload's layer count (1 = the single-layer path)")
     ap.add_argument("--sweep", action="store_true",
                     help="multi-layer workloads: one line per fetch ratio of the sweep")
     args = ap.parse_args()
@@ -183,6 +195,8 @@ def main():
     from lookahead_sparse_kv_oasis_amd.runner import LayerRunner
 
     w = _workloads()[args.workload]
+    if args.layers is not None:
+        w = w.with_(layers=args.layers)
     if w.layers > 1:
         bench_model(args, w)
         return
@@ -207,6 +221,7 @@ def main():
     # itself unperturbed
     h.oasis_set_timing(0 if args.no_kernel_timing else
                        TIME["score"] | TIME["attn"] | (0 if stats0["fetch_fused"] else TIME["gather"]))
+    h.oasis_set_timing_period(args.timing_period)
 
     torch.cuda.synchronize()
     t0 = time.perf_counter()
@@ -302,6 +317,8 @@ def main():
                       "blocks_per_step": fetched, "bytes_per_step": fetched * blk_bytes},
         "kernels_avg_ms": {"score": ms_score, "attn": ms_attn,
                            **({} if fused else {"gather": ms_gather})},
+        "timed_launches": {"score": tm["n_score"], "attn": tm["n_attn"],
+                           "period": args.timing_period},
         "attended_blocks_per_step": attended,
     }
     if not args.no_cpu_baseline:
@@ -359,10 +376,12 @@ def bench_model(args, w):
             s0 = [h.oasis_get_stats() for h in mr.handles]
             for h in mr.handles:
                 h.oasis_set_timing(0 if args.no_kernel_timing else TIME["score"] | TIME["attn"])
+                h.oasis_set_timing_period(args.timing_period)
             torch.cuda.synchronize()
             t0 = time.perf_counter()
             for t in range(args.warmup + 1, n_steps + 1):
                 mr.step(t, stream, sd, cap)
+            t_issue = time.perf_counter() - t0
             torch.cuda.synchronize()
             dt = time.perf_counter() - t0
             s1 = [h.oasis_get_stats() for h in mr.handles]
@@ -373,7 +392,13 @@ def bench_model(args, w):
             fetched = sum(b["fetched"] - a["fetched"] for a, b in zip(s0, s1)) / args.steps
             attended = sum(b["attended"] - a["attended"] for a, b in zip(s0, s1)) / args.steps
             res[sched] = dict(dt=dt, fetched=fetched, attended=attended, tms=tms)
-            log(f"ratio {ratio} cap {cap} {sched}: {dt / args.steps * 1e3:.3f} ms/step")
+            n_sc = max(1, sum(tm["n_score"] for tm in tms))
+            n_at = max(1, sum(tm["n_attn"] for tm in tms))
+            log(f"ratio {ratio} cap {cap} {sched}: {dt / args.steps * 1e3:.3f} ms/step, "
+                f"host issue {t_issue / args.steps * 1e3:.3f} ms/step, score "
+                f"{sum(tm['ms_score'] for tm in tms) / n_sc * 1e3:.1f} us, attn "
+                f"{sum(tm['ms_attn'] for tm in tms) / n_at * 1e3:.1f} us per launch, "
+                f"{fetched:.0f} blocks fetched/step")
         main_sched = schedules[0]
         r = res[main_sched]
         K = args.steps

@@ -263,6 +263,13 @@ enum {
 int oasis_set_timing(oasis_t *h, int32_t mask);
 /* Synchronous: read the sums. */
 int oasis_get_timing(oasis_t *h, oasis_timing *out);
+/* Bracket only one launch in `period` of each timed class with events (the
+ * first, then every period-th); the others run as untimed launches.  Events
+ * attached to a dispatch cost a few microseconds of the following work, so a
+ * period above 1 measures average kernel times with less disturbance of the
+ * stream.  Default 1; OASIS_E_INVAL for period < 1.  Does not reset the sums;
+ * oasis_set_timing restarts the count. */
+int oasis_set_timing_period(oasis_t *h, int32_t period);
 
 /* Shape of a handle: K (top-K blocks), S (slots), NBmax, block size. */
 int oasis_get_dims(const oasis_t *h, int32_t *k_blocks, int32_t *slots, int64_t *nb_max,

@@ -31,7 +31,7 @@ EXPORTS = [
     "oasis_set_state", "oasis_decode_layers",
     "oasis_append_kv", "oasis_predict", "oasis_topk_from_scores", "oasis_select_and_fetch",
     "oasis_evict", "oasis_sparse_attn", "oasis_buffer_bytes", "oasis_read", "oasis_get_stats",
-    "oasis_check", "oasis_set_timing", "oasis_get_timing", "oasis_get_dims", "oasis_tokens",
+    "oasis_check", "oasis_set_timing", "oasis_set_timing_period", "oasis_get_timing", "oasis_get_dims", "oasis_tokens",
     "oasis_copy_stream", "oasis_kv_bytes_per_token", "oasis_cap_from_ratio", "oasis_strerror",
     "oasis_last_error",
 ]
@@ -103,6 +103,7 @@ def lib():
             "oasis_get_stats": (ctypes.c_int, [H, ctypes.POINTER(oasis_stats)]),
             "oasis_check": (ctypes.c_int, [H]),
             "oasis_set_timing": (ctypes.c_int, [H, i32]),
+            "oasis_set_timing_period": (ctypes.c_int, [H, i32]),
             "oasis_get_timing": (ctypes.c_int, [H, ctypes.POINTER(oasis_timing)]),
             "oasis_get_dims": (ctypes.c_int, [H, ctypes.POINTER(i32), ctypes.POINTER(i32),
                                               ctypes.POINTER(i64), ctypes.POINTER(i32)]),
@@ -249,6 +250,10 @@ class Oasis:
     def oasis_set_timing(self, mask=TIME["all"]):
         """mask: OR of TIME values (0 = off)."""
         self._check(lib().oasis_set_timing(self.h, int(mask)), "oasis_set_timing")
+
+    def oasis_set_timing_period(self, period: int):
+        """Time one launch in `period` of each timed kernel class."""
+        self._check(lib().oasis_set_timing_period(self.h, int(period)), "oasis_set_timing_period")
 
     def oasis_get_timing(self) -> dict:
         t = oasis_timing()

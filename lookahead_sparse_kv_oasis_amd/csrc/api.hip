@@ -47,6 +47,8 @@ struct Timers {
     size_t used = 0;
     double ms = 0.0;
     int64_t n = 0;
+    int64_t seq = 0;      // launches seen since timing was set
+    bool active = false;  // the current launch carries events
 };
 
 // Pinned, device-mapped host KV; shared by the handles created from one owner.
@@ -111,6 +113,7 @@ struct oasis_handle {
 
     int64_t n_select = 0;
     int32_t timing = 0;  // mask of timed kernel classes
+    int32_t timing_period = 1;  // time one launch in this many per class
     Timers tm[TM_N];
     std::string last_error;
 };
@@ -175,6 +178,8 @@ int tbegin(oasis_t *h, int cls, hipStream_t st) {
     (void)st;
     if (!(h->timing & (1 << cls))) return OASIS_OK;
     Timers &t = h->tm[cls];
+    t.active = (t.seq++ % h->timing_period) == 0;
+    if (!t.active) return OASIS_OK;
     if (t.used == kTimerCap) {  // fold finished pairs into the sum
         HIP_OK(h, hipEventSynchronize(t.stop[t.used - 1]));
         fold_timer(t);
@@ -194,8 +199,10 @@ int tbegin(oasis_t *h, int cls, hipStream_t st) {
 int tend(oasis_t *h, int cls, hipStream_t st) {
     (void)st;
     if (!(h->timing & (1 << cls))) return OASIS_OK;
-    g_launch_events = LaunchEvents{};
     Timers &t = h->tm[cls];
+    if (!t.active) return OASIS_OK;
+    g_launch_events = LaunchEvents{};
+    t.active = false;
     ++t.used;
     return OASIS_OK;
 }
@@ -890,7 +897,15 @@ extern "C" int oasis_set_timing(oasis_t *h, int32_t mask) {
         t.used = 0;
         t.ms = 0.0;
         t.n = 0;
+        t.seq = 0;
+        t.active = false;
     }
+    return OASIS_OK;
+}
+
+extern "C" int oasis_set_timing_period(oasis_t *h, int32_t period) {
+    if (!h || period < 1) return h ? fail(h, OASIS_E_INVAL, "timing period %d < 1", period) : OASIS_E_INVAL;
+    h->timing_period = period;
     return OASIS_OK;
 }
 

@@ -179,3 +179,21 @@ def test_stats_count_fetches_and_hits():
     assert admission <= st["fetched"] <= admission + 4 * units * r.cap
     assert st["hits"] + st["misses"] == 5 * units * w.k_blocks
     assert st["bytes_fetched"] == st["fetched"] * 2 * 16 * 128 * 2
+
+
+def test_sampled_kernel_timing_counts_one_launch_per_period():
+    from lookahead_sparse_kv_oasis_amd import TIME, OasisError
+    from lookahead_sparse_kv_oasis_amd.runner import LayerRunner
+    w = synth.QWEN3_8B.with_(batch=1, prefix_tokens=16 * 200)
+    r = LayerRunner(w, 7)
+    r.admission()
+    r.h.oasis_set_timing(TIME["score"] | TIME["attn"])
+    r.h.oasis_set_timing_period(3)
+    for t in range(1, 8):
+        r.step(t)
+    tm = r.h.oasis_get_timing()
+    # launches 0, 3 and 6 of each class carry events
+    assert tm["n_score"] == 3 and tm["n_attn"] == 3 and tm["n_append"] == 0
+    assert tm["ms_score"] > 0 and tm["ms_attn"] > 0
+    with pytest.raises(OasisError):
+        r.h.oasis_set_timing_period(0)
