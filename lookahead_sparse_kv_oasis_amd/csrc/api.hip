@@ -380,6 +380,7 @@ int create_handle(const oasis_layout *layout, int32_t block_size, int32_t budget
     h->use_mfma_score = D.dtype == kBF16 && (D.d == 64 || D.d == 128 || D.d == 256) && Q <= 128;
     if (const char *e = getenv("OASIS_SCORE_IMPL"))
         if (!strcmp(e, "valu")) h->use_mfma_score = false;
+    D.tiled = h->use_mfma_score;  // the matrix-core score reads the tiled summary layout
     h->fused = h->plan.mfma;
     if (const char *e = getenv("OASIS_GATHER"))
         if (!strcmp(e, "stream")) h->fused = false;
@@ -421,7 +422,8 @@ int create_handle(const oasis_layout *layout, int32_t block_size, int32_t budget
 
     auto dmal = [&](void **p, size_t bytes) { return hipMalloc(p, bytes ? bytes : 16) == hipSuccess; };
     const int NS = h->plan.nsa;
-    bool ok = dmal(&h->summ, (size_t)units * NBmax * 2 * D.d * e) &&
+    const size_t summ_bytes = (size_t)units * D.summ_unit_elems() * e;
+    bool ok = dmal(&h->summ, summ_bytes) &&
               dmal(&h->slots, (size_t)units * S * D.block_elems() * e) &&
               dmal((void **)&h->scores, sizeof(float) * units * NBmax) &&
               dmal((void **)&h->ids, sizeof(int32_t) * units * K) &&
@@ -439,7 +441,7 @@ int create_handle(const oasis_layout *layout, int32_t block_size, int32_t budget
               dmal((void **)&h->err, sizeof(uint32_t)) &&
               dmal((void **)&h->stats, sizeof(DevStats));
     if (!ok) return bail(OASIS_E_NOMEM);
-    if (hipMemset(h->summ, 0, (size_t)units * NBmax * 2 * D.d * e) != hipSuccess ||
+    if (hipMemset(h->summ, 0, summ_bytes) != hipSuccess ||
         hipMemset(h->slots, 0, (size_t)units * S * D.block_elems() * e) != hipSuccess ||
         hipMemset(h->scores, 0, sizeof(float) * units * NBmax) != hipSuccess ||
         hipMemset(h->err, 0, sizeof(uint32_t)) != hipSuccess ||
@@ -621,7 +623,7 @@ extern "C" int oasis_predict(oasis_t *h, const void *q_dev, const void *drafts_d
     const Dims &D = h->D;
     LAUNCH(h, TM_SCORE, stream,
            launch_score(D, h->summ, q_dev, drafts_dev, n_drafts, NB, h->scores,
-                        h->use_mfma_score, stream));
+                        stream));
     if (scores_dev)
         HIP_OK(h, hipMemcpyAsync(scores_dev, h->scores, sizeof(float) * D.units() * D.NBmax,
                                  hipMemcpyDeviceToDevice, stream));
@@ -825,6 +827,35 @@ extern "C" int64_t oasis_buffer_bytes(const oasis_t *h, int32_t which) {
     }
 }
 
+namespace {
+
+// Block-major bytes [offset, offset + nbytes) of a tiled summary: the units the
+// range touches are copied whole and reordered on the host.
+int read_tiled_summary(oasis_t *h, int64_t offset, int64_t nbytes, char *dst) {
+    const Dims &D = h->D;
+    const size_t e = D.esize();
+    const int64_t logical_unit = D.NBmax * 2 * D.d * (int64_t)e;
+    if (nbytes == 0) return OASIS_OK;
+    std::vector<uint16_t> tiled((size_t)D.summ_unit_elems());
+    std::vector<uint16_t> plain((size_t)(D.NBmax * 2 * D.d));
+    for (int64_t u = offset / logical_unit; u <= (offset + nbytes - 1) / logical_unit; ++u) {
+        HIP_OK(h, hipMemcpy(tiled.data(), (const uint16_t *)h->summ + u * D.summ_unit_elems(),
+                            tiled.size() * sizeof(uint16_t), hipMemcpyDeviceToHost));
+        for (int64_t j = 0; j < D.NBmax; ++j)
+            for (int half = 0; half < 2; ++half)
+                for (int c = 0; c < D.d; c += 8)
+                    memcpy(&plain[(size_t)(j * 2 * D.d + half * D.d + c)],
+                           &tiled[(size_t)summ_offset(true, D.d, j, half, c)], 16);
+        const int64_t lo = std::max(offset, u * logical_unit);
+        const int64_t hi = std::min(offset + nbytes, (u + 1) * logical_unit);
+        memcpy(dst + (lo - offset), (const char *)plain.data() + (lo - u * logical_unit),
+               (size_t)(hi - lo));
+    }
+    return OASIS_OK;
+}
+
+}  // namespace
+
 extern "C" int oasis_read(oasis_t *h, int32_t which, int64_t offset, int64_t nbytes,
                           void *dst_host) {
     if (!h || !dst_host) return OASIS_E_INVAL;
@@ -841,7 +872,10 @@ extern "C" int oasis_read(oasis_t *h, int32_t which, int64_t offset, int64_t nby
     }
     const void *src = nullptr;
     switch (which) {
-    case OASIS_BUF_SUMMARY: src = h->summ; break;
+    case OASIS_BUF_SUMMARY:
+        if (h->D.tiled) return read_tiled_summary(h, offset, nbytes, (char *)dst_host);
+        src = h->summ;
+        break;
     case OASIS_BUF_SLOTS: src = h->slots; break;
     case OASIS_BUF_HOST_KV:
         memcpy(dst_host, (const char *)h->host_kv + offset, (size_t)nbytes);

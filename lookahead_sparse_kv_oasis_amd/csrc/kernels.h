@@ -32,10 +32,26 @@ extern thread_local LaunchEvents g_launch_events;
 struct Dims {
     int B, Hq, Hkv, G, d, dtype, bs, K, S;
     int64_t NBmax;
+    // Summary layout.  Block-major: [unit][block][max | min][d].  Tiled (bf16
+    // with the matrix-core score): per unit, tiles of 32 blocks, each tile
+    // [k-step i < d / 8][lane < 64][8 elements], where lane l holds block
+    // 32 t + l % 32, maxima for l < 32 and minima for l >= 32, dims 8i..8i+8:
+    // the B-operand order of v_mfma_f32_32x32x16_bf16, so one k-step of a
+    // tile is one contiguous 1 KB load of a wave.
+    bool tiled = false;
     int64_t units() const { return (int64_t)B * Hkv; }
     int esize() const { return dtype == kF32 ? 4 : 2; }
     int64_t block_elems() const { return 2LL * bs * d; }  // K and V of one block
+    int64_t summ_tiles() const { return (NBmax + 31) / 32; }
+    int64_t summ_unit_elems() const { return tiled ? summ_tiles() * 64LL * d : NBmax * 2LL * d; }
 };
+
+// Element offset of dims [c, c + 8) of the maxima (half 0) or minima (half 1)
+// of block j in a unit's summary region (see Dims).
+__host__ __device__ inline int64_t summ_offset(bool tiled, int d, int64_t j, int half, int c) {
+    if (!tiled) return j * 2LL * d + (int64_t)half * d + c;
+    return (j >> 5) * 64LL * d + (int64_t)(c >> 3) * 512 + (int64_t)(half * 32 + (int)(j & 31)) * 8;
+}
 
 // Append token `pos` of every sequence (host KV, summary, resident slot).
 hipError_t launch_append(const Dims &D, const void *k, const void *v, int64_t pos, void *host_kv,
@@ -45,9 +61,10 @@ hipError_t launch_append(const Dims &D, const void *k, const void *v, int64_t po
 hipError_t launch_summary_build(const Dims &D, const void *host_kv, int64_t T, void *summ,
                                 hipStream_t st);
 
-// Block scores.  use_mfma selects the bf16 matrix-core kernel.
+// Block scores: the bf16 matrix-core kernel on a tiled summary, the VALU
+// kernel on a block-major one.
 hipError_t launch_score(const Dims &D, const void *summ, const void *q, const void *drafts,
-                        int n_drafts, int64_t NB, float *scores, bool use_mfma, hipStream_t st);
+                        int n_drafts, int64_t NB, float *scores, hipStream_t st);
 
 // Per-unit top-K of scores[unit][0..NB).
 hipError_t launch_topk(const Dims &D, const float *scores, int64_t NB, int32_t *ids,

@@ -5,7 +5,8 @@
 // A block's summary is, per dimension, the largest and smallest key value over
 // the block's valid tokens.  Both kernels keep the first of equal values
 // (strict comparisons in token order), so a summary is a bit-exact copy of
-// existing key elements.
+// existing key elements.  The summary region of a unit is block-major or tiled
+// (the matrix-core operand order), see Dims; summ_offset addresses both.
 #include "kernels.h"
 
 namespace oasis {
@@ -18,23 +19,26 @@ __global__ __launch_bounds__(64) void append_kernel(const T *__restrict__ k,
                                                     T *host_kv, T *summ,
                                                     const int32_t *__restrict__ block_slot,
                                                     T *slots, int d, int bs, int S,
-                                                    int64_t NBmax) {
+                                                    int64_t NBmax, bool tiled,
+                                                    int64_t unit_elems) {
     constexpr int V = Elem<T>::kVec;
     const int64_t u = blockIdx.x;
     const int64_t j = pos / bs;
     const int o = (int)(pos % bs);
     const int32_t s = block_slot[u * NBmax + j];
     T *hk = host_kv + ((u * NBmax + j) * 2 * bs + o) * (int64_t)d;
-    T *sm = summ + (u * NBmax + j) * 2 * (int64_t)d;
+    T *su = summ + u * unit_elems;
     for (int c = threadIdx.x * V; c < d; c += blockDim.x * V) {
+        T *smx = su + summ_offset(tiled, d, j, 0, c);
+        T *smn = su + summ_offset(tiled, d, j, 1, c);
         const Vec16<T> kk = ld16(k + u * d + c);
         const Vec16<T> vv = ld16(v + u * d + c);
         st16(hk + c, kk);
         st16(hk + (int64_t)bs * d + c, vv);
         Vec16<T> mx = kk, mn = kk;
         if (o != 0) {
-            mx = ld16(sm + c);
-            mn = ld16(sm + d + c);
+            mx = ld16(smx);
+            mn = ld16(smn);
 #pragma unroll
             for (int e = 0; e < V; ++e) {
                 const float x = Elem<T>::f(kk.v[e]);
@@ -42,8 +46,8 @@ __global__ __launch_bounds__(64) void append_kernel(const T *__restrict__ k,
                 if (x < Elem<T>::f(mn.v[e])) mn.v[e] = kk.v[e];
             }
         }
-        st16(sm + c, mx);
-        st16(sm + d + c, mn);
+        st16(smx, mx);
+        st16(smn, mn);
         if (s >= 0) {  // write-through into the resident copy of the block
             T *sl = slots + ((u * S + s) * 2 * bs + o) * (int64_t)d;
             st16(sl + c, kk);
@@ -57,7 +61,8 @@ template <typename T>
 __global__ __launch_bounds__(256) void summary_build_kernel(const T *host_kv, int64_t T_,
                                                             T *summ, int d, int bs,
                                                             int64_t NBmax, int64_t NB,
-                                                            int64_t units) {
+                                                            int64_t units, bool tiled,
+                                                            int64_t unit_elems) {
     constexpr int V = Elem<T>::kVec;
     const int chunks = d / V;
     const int64_t total = units * NB * chunks;
@@ -80,9 +85,9 @@ __global__ __launch_bounds__(256) void summary_build_kernel(const T *host_kv, in
                 if (f < Elem<T>::f(mn.v[e])) mn.v[e] = x.v[e];
             }
         }
-        T *dst = summ + (u * NBmax + j) * 2 * (int64_t)d + c;
-        st16(dst, mx);
-        st16(dst + d, mn);
+        T *su = summ + u * unit_elems;
+        st16(su + summ_offset(tiled, d, j, 0, c), mx);
+        st16(su + summ_offset(tiled, d, j, 1, c), mn);
     }
 }
 
@@ -92,11 +97,13 @@ hipError_t launch_append(const Dims &D, const void *k, const void *v, int64_t po
     if (D.dtype == kF32)
         OASIS_LAUNCH(append_kernel<float>, grid, block, 0, st, (const float *)k,
                            (const float *)v, pos, (float *)host_kv, (float *)summ, block_slot,
-                           (float *)slots, D.d, D.bs, D.S, D.NBmax);
+                           (float *)slots, D.d, D.bs, D.S, D.NBmax, D.tiled,
+                           D.summ_unit_elems());
     else
         OASIS_LAUNCH(append_kernel<uint16_t>, grid, block, 0, st, (const uint16_t *)k,
                            (const uint16_t *)v, pos, (uint16_t *)host_kv, (uint16_t *)summ,
-                           block_slot, (uint16_t *)slots, D.d, D.bs, D.S, D.NBmax);
+                           block_slot, (uint16_t *)slots, D.d, D.bs, D.S, D.NBmax, D.tiled,
+                           D.summ_unit_elems());
     return hipGetLastError();
 }
 
@@ -111,11 +118,11 @@ hipError_t launch_summary_build(const Dims &D, const void *host_kv, int64_t T, v
     if (D.dtype == kF32)
         OASIS_LAUNCH(summary_build_kernel<float>, dim3((unsigned)blocks), dim3(256), 0, st,
                            (const float *)host_kv, T, (float *)summ, D.d, D.bs, D.NBmax, NB,
-                           D.units());
+                           D.units(), D.tiled, D.summ_unit_elems());
     else
         OASIS_LAUNCH(summary_build_kernel<uint16_t>, dim3((unsigned)blocks), dim3(256), 0,
                            st, (const uint16_t *)host_kv, T, (uint16_t *)summ, D.d, D.bs,
-                           D.NBmax, NB, D.units());
+                           D.NBmax, NB, D.units(), D.tiled, D.summ_unit_elems());
     return hipGetLastError();
 }
 

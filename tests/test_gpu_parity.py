@@ -49,6 +49,17 @@ def test_group_sizes_reduced_context(q_heads, kv_heads):
     log(f"G={q_heads // kv_heads}: {p.run_all()}")
 
 
+@pytest.mark.parametrize("head_dim", [64, 256])
+def test_head_dims_reduced_context(head_dim):
+    """bf16 at d = 64 and 256: the tiled summary layout and the matrix-core
+    score at the other tile sizes (8 KB and 32 KB per 32 blocks)."""
+    Parity, log = _parity()
+    w = synth.QWEN3_8B.with_(batch=2, head_dim=head_dim, prefix_tokens=16 * 200 + 3,
+                             budget_tokens=16 * 64)
+    p = Parity(w, 5, [(0, 0), (1, 7)])
+    log(f"d={head_dim}: {p.run_all()}")
+
+
 # ------------------------------------------------------------------ full-size workloads
 # Every step of the workload through the C-ABI at its real shape, compared on a
 # sample of (batch row, KV head) units that the oracle recomputes one by one.
