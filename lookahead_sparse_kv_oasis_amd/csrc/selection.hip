@@ -74,8 +74,27 @@ __device__ __forceinline__ int block_excl_scan(int v, int *sh) {
 // digit's bin holds exactly the keys still needed.  If the bits run out first
 // the bin is one key value tau and the lowest ids among the keys equal to tau
 // fill the rest.
+// One thread's share of a unit's scores: C = ceil(NB / NT) consecutive block
+// ids starting at tid * C, as order keys.  Loaded first so that the loads
+// overlap whatever the caller does before topk_unit.
+template <int CMAX> struct TopkKeys {
+    uint32_t key[CMAX];
+    float raw[CMAX];
+};
+
 template <int NT, int CMAX>
-__device__ void topk_unit(const float *__restrict__ s, int NB, int K, int32_t *__restrict__ out,
+__device__ __forceinline__ void topk_load(const float *__restrict__ s, int NB, TopkKeys<CMAX> &k) {
+    const int C = (NB + NT - 1) / NT;
+    const int begin = threadIdx.x * C;
+#pragma unroll
+    for (int i = 0; i < CMAX; ++i) {
+        const int id = begin + i;
+        k.raw[i] = (i < C && id < NB) ? s[id] : 0.f;
+    }
+}
+
+template <int NT, int CMAX>
+__device__ void topk_unit(TopkKeys<CMAX> &kk, int NB, int K, int32_t *__restrict__ out,
                           int32_t *__restrict__ out2, int32_t *out_lds,
                           uint32_t *__restrict__ err) {
     constexpr int NW = NT / 64;
@@ -101,14 +120,14 @@ __device__ void topk_unit(const float *__restrict__ s, int NB, int K, int32_t *_
 
     const int C = (NB + NT - 1) / NT;
     const int begin = tid * C;
-    uint32_t key[CMAX];
+    uint32_t *key = kk.key;
     bool bad = false;
     uint32_t lmx = 0u, lmn = 0xFFFFFFFFu;
 #pragma unroll
     for (int i = 0; i < CMAX; ++i) {
         const int id = begin + i;
         const bool valid = i < C && id < NB;
-        key[i] = valid ? order_key(s[id], bad) : 0u;
+        key[i] = valid ? order_key(kk.raw[i], bad) : 0u;
         if (valid) {
             lmx = key[i] > lmx ? key[i] : lmx;
             lmn = key[i] < lmn ? key[i] : lmn;
@@ -238,6 +257,62 @@ __device__ void topk_unit(const float *__restrict__ s, int NB, int K, int32_t *_
     }
     __syncthreads();
 
+    if (Kp <= 128) {
+        // one wave sorts the winners: 64-bit composites (key, ~id) in
+        // descending order are (score desc, id asc); two per lane, element
+        // e * 64 + lane, bitonic network, cross-lane pairs by shuffles
+        if (wave == 0) {
+            unsigned long long v[2];
+#pragma unroll
+            for (int e = 0; e < 2; ++e) {
+                const int i = e * 64 + lane;
+                v[e] = i < Kp ? ((unsigned long long)ckey[i] << 32) | (uint32_t)~(uint32_t)cid[i]
+                              : 0ull;  // sorts last: no finite score has key 0
+            }
+#pragma unroll
+            for (int k = 2; k <= 128; k <<= 1) {
+#pragma unroll
+                for (int j = k >> 1; j > 0; j >>= 1) {
+                    if (j == 64) {  // partner is the lane's other element
+                        // element 0 has bit 64 clear: it keeps the larger
+                        // value when the block (bit k = 128) sorts descending
+                        const unsigned long long a = v[0], b = v[1];
+                        v[0] = a > b ? a : b;
+                        v[1] = a > b ? b : a;
+                    } else {
+#pragma unroll
+                        for (int e = 0; e < 2; ++e) {
+                            const int i = e * 64 + lane;
+                            const unsigned long long o = __shfl_xor(v[e], j, 64);
+                            // descending overall: the pair's lower index keeps the
+                            // larger value in blocks with (i & k) == 0
+                            const bool lower = (i & j) == 0;
+                            const bool desc = (i & k) == 0;
+                            const bool keep_max = lower == desc;
+                            v[e] = keep_max ? (v[e] > o ? v[e] : o) : (v[e] < o ? v[e] : o);
+                        }
+                    }
+                }
+            }
+#pragma unroll
+            for (int e = 0; e < 2; ++e) {
+                const int r = e * 64 + lane;
+                if (r < Kp) {
+                    const int32_t id = (int32_t)~(uint32_t)v[e];
+                    out[r] = id;
+                    if (out2) out2[r] = id;
+                    if (out_lds) out_lds[r] = id;
+                }
+            }
+        }
+        for (int i = Kp + tid; i < K; i += NT) {
+            out[i] = -1;
+            if (out2) out2[i] = -1;
+            if (out_lds) out_lds[i] = -1;
+        }
+        return;
+    }
+
     // place each winner by counting the winners that order before it; two
     // threads share a winner when there are enough threads
     const int parts = (NT >= 2 * Kp) ? 2 : 1;
@@ -286,8 +361,10 @@ __global__ __launch_bounds__(NT) void topk_kernel(const float *__restrict__ scor
                                                   int32_t *__restrict__ ids_copy,
                                                   uint32_t *__restrict__ err) {
     const int64_t u = blockIdx.x;
-    topk_unit<NT, CMAX>(scores + u * NBmax, NB, K, ids + u * K, ids_copy ? ids_copy + u * K : nullptr,
-                        nullptr, err);
+    TopkKeys<CMAX> kk;
+    topk_load<NT, CMAX>(scores + u * NBmax, NB, kk);
+    topk_unit<NT, CMAX>(kk, NB, K, ids + u * K, ids_copy ? ids_copy + u * K : nullptr, nullptr,
+                        err);
 }
 
 // Hash of a block id for the LDS residency table.
@@ -510,6 +587,9 @@ __global__ __launch_bounds__(NT) void topk_select_kernel(
     int32_t *hkey = lu_lds + S4;           // [HS] resident block -> slot
     int32_t *hval = hkey + HS;             // [HS]
     int32_t *scratch = hval + HS;          // 16-byte aligned
+    // the scores are read while the tables below are read and hashed
+    TopkKeys<CMAX> kk;
+    topk_load<NT, CMAX>(scores + u * NBmax, NB, kk);
     for (int i = threadIdx.x; i < HS; i += NT) hkey[i] = -1;
     __syncthreads();
     // tables into LDS and the resident blocks into the hash, while the top-K
@@ -524,7 +604,7 @@ __global__ __launch_bounds__(NT) void topk_select_kernel(
             hval[hh] = s;
         }
     }
-    topk_unit<NT, CMAX>(scores + u * NBmax, NB, K, ids + u * K, nullptr, sel_lds, err);
+    topk_unit<NT, CMAX>(kk, NB, K, ids + u * K, nullptr, sel_lds, err);
     __syncthreads();
     if (threadIdx.x < 64)
         select_unit(u, sel_lds, sb_lds, lu_lds, slot_block, last_used, block_slot, K, S, NBmax,
