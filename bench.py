@@ -210,23 +210,31 @@ def main():
     stream = torch.cuda.current_stream()
     print(f"# setup {time.perf_counter() - t_setup:.1f}s: {w.name}, {n_steps} steps",
           file=sys.stderr, flush=True)
-    if w.admission:
-        run.admission(stream)
-    for t in range(1, args.warmup + 1):
-        run.step(t, stream)
+    rec = None
+    if w.lookahead:
+        # [OASIS] Fig. 8 ordering; the warmup steps also measure prediction recall
+        rec = warmup_ahead_with_recall(run, args.warmup, stream)
+        step = run.step_ahead
+    else:
+        if w.admission:
+            run.admission(stream)
+        for t in range(1, args.warmup + 1):
+            run.step(t, stream)
+        step = run.step
     torch.cuda.synchronize()
     stats0 = h.oasis_get_stats()
     from lookahead_sparse_kv_oasis_amd import TIME
     # events only around the two HBM kernels of the metric, to keep the step
     # itself unperturbed
     h.oasis_set_timing(0 if args.no_kernel_timing else
-                       TIME["score"] | TIME["attn"] | (0 if stats0["fetch_fused"] else TIME["gather"]))
+                       TIME["score"] | TIME["attn"] |
+                       (0 if stats0["fetch_fused"] and not w.lookahead else TIME["gather"]))
     h.oasis_set_timing_period(args.timing_period)
 
     torch.cuda.synchronize()
     t0 = time.perf_counter()
     for t in range(args.warmup + 1, n_steps + 1):
-        run.step(t, stream)
+        step(t, stream)
     torch.cuda.synchronize()
     dt = time.perf_counter() - t0
 
@@ -260,7 +268,9 @@ def main():
     score_gbps = score_bytes / (ms_score * 1e-3) / 1e9
     attn_gbps = attn_bytes / (ms_attn * 1e-3) / 1e9
     hbm_gbps = (score_bytes + attn_bytes) / ((ms_score + ms_attn + ms_comb) * 1e-3) / 1e9
-    fused = bool(stats1["fetch_fused"])
+    # in the lookahead order the next append copies the fetched blocks with the
+    # standalone gather kernel, so the attention kernel does no host reads
+    fused = bool(stats1["fetch_fused"]) and not w.lookahead
     # with the fetch fused into the attention kernel the host-link transfer
     # runs inside it: its rate is bounded below by bytes / attention time
     g_ms = ms_attn if fused else ms_gather
@@ -321,10 +331,45 @@ def main():
                            "period": args.timing_period},
         "attended_blocks_per_step": attended,
     }
+    if rec is not None:
+        line["ordering"] = "lookahead"
+        line["recall"] = rec
     if not args.no_cpu_baseline:
         print("# cpu baseline (oracle) ...", file=sys.stderr, flush=True)
         line["cpu_baseline"] = cpu_baseline(w)
     print(json.dumps(line), flush=True)
+
+
+def warmup_ahead_with_recall(run, warmup, stream):
+    """Admission and `warmup` lookahead steps of a LayerRunner; each step also
+    scores the step's own query to get the exact top-K (untimed), giving the
+    recall of the drafts' prediction (made one step earlier) and of the
+    previous query's exact top-K ([OASIS] Fig. 4, synthetic analog)."""
+    import numpy as np
+    import torch
+
+    from lookahead_sparse_kv_oasis_amd.runner import exact_ids, predicted_ids, recall
+
+    h, w = run.h, run.w
+    buf = torch.empty(w.batch * w.kv_heads * w.k_blocks, dtype=torch.int32, device="cuda")
+    run.admission_ahead(stream)
+    torch.cuda.synchronize()
+    r_ahead, r_prev, prev = [], [], None
+    for t in range(1, warmup + 1):
+        pred = predicted_ids(h)
+        h.oasis_append_kv(run.app_k[t - 1], run.app_v[t - 1], stream=stream)
+        ex = exact_ids(h, run.q_steps[t], buf, stream)
+        r_ahead.append(recall(pred, ex))
+        if prev is not None:
+            r_prev.append(recall(prev, ex))
+        prev = ex
+        h.oasis_sparse_attn(run.q_steps[t], run.out, stream=stream)
+        h.oasis_predict(None, run.drafts[t], w.drafts, stream=stream)
+        h.oasis_select_and_fetch(run.cap, stream=stream)
+    return {"drafts": float(np.mean(r_ahead)) if r_ahead else None,
+            "previous_query": float(np.mean(r_prev)) if r_prev else None,
+            "steps": warmup, "what": "mean over units and steps of |predicted top-K ∩ exact "
+                                     "top-K of the step's own query| / K"}
 
 
 def bench_model(args, w):
@@ -353,6 +398,7 @@ def bench_model(args, w):
     schedules = ["overlap", "serial"] if args.schedule == "both" else [args.schedule]
     stream = torch.cuda.current_stream()
     side = torch.cuda.Stream()
+    xfer = torch.cuda.Stream()
     h2d = None if args.no_h2d_peak else pinned_h2d_peak_gbps()
     cpu = None if args.no_cpu_baseline else cpu_baseline(w.with_(layers=1))
     e, d, bs = w.elem_bytes, w.head_dim, w.block_size
@@ -369,9 +415,17 @@ def bench_model(args, w):
             if not first:
                 mr.reset()
             first = False
-            mr.admission(stream, sd)
+            if w.lookahead:
+                sd2 = side if sched == "overlap" else stream
+                xf = xfer if sched == "overlap" else stream
+                mr.admission_ahead(stream, sd2, xf)
+                mstep = (lambda t, sd2=sd2, xf=xf:
+                         mr.step_ahead(t, stream, sd2, xf, cap))
+            else:
+                mr.admission(stream, sd)
+                mstep = lambda t, sd=sd: mr.step(t, stream, sd, cap)
             for t in range(1, args.warmup + 1):
-                mr.step(t, stream, sd, cap)
+                mstep(t)
             torch.cuda.synchronize()
             s0 = [h.oasis_get_stats() for h in mr.handles]
             for h in mr.handles:
@@ -380,7 +434,7 @@ def bench_model(args, w):
             torch.cuda.synchronize()
             t0 = time.perf_counter()
             for t in range(args.warmup + 1, n_steps + 1):
-                mr.step(t, stream, sd, cap)
+                mstep(t)
             t_issue = time.perf_counter() - t0
             torch.cuda.synchronize()
             dt = time.perf_counter() - t0
@@ -432,6 +486,7 @@ def bench_model(args, w):
                        "budget_tokens": w.budget_tokens, "drafts": w.drafts,
                        "fetch_ratio": "all" if ratio is None else ratio,
                        "cap_per_kv_head": cap, "schedule": main_sched,
+                       "ordering": "lookahead" if w.lookahead else "within step",
                        "host_kv_buffers": mr.H},
             "model_steps_per_s": K / dt,
             "roofline": roof,

@@ -132,10 +132,11 @@ int oasis_set_state(oasis_t *h, const int32_t *slot_block_host, const int32_t *l
 int oasis_append_kv(oasis_t *h, const void *k_dev, const void *v_dev, hipStream_t stream);
 
 /* Predict the blocks of this step (OasisKV Fig. 7: the draft queries scan
- * the min/max compressed keys).  q_dev [B][Hq][d] current query; drafts_dev
- * [n_drafts][B][Hq][d] (may be NULL when n_drafts == 0).  Block score =
- * max over the G query heads of the KV head's group and over {q} + drafts of
- * sum_c max(x_c * max_c, x_c * min_c).  Then per (b, KV head) the top
+ * the min/max compressed keys).  q_dev [B][Hq][d] current query, or NULL to
+ * predict from the drafts alone (the lookahead ordering of Fig. 8; needs
+ * n_drafts >= 1); drafts_dev [n_drafts][B][Hq][d] (may be NULL when n_drafts
+ * == 0).  Block score = max over the G query heads of the KV head's group and
+ * over {q} + drafts of sum_c max(x_c * max_c, x_c * min_c).  Then per (b, KV head) the top
  * min(K, NB) blocks by (score desc, block id asc), -1 padded, become the
  * selection.  block_ids_dev [B][Hkv][K] and scores_dev [B][Hkv][NBmax]
  * (NBmax = ceil(max_tokens / block_size)) receive copies when non-NULL. */
@@ -200,6 +201,25 @@ typedef struct {
  * failing layer. */
 int oasis_decode_layers(oasis_t *const *layers, const oasis_layer_io *io, int32_t n_layers,
                         int32_t n_drafts, int32_t cap, hipStream_t stream, hipStream_t side);
+
+/* One decode step over the layers in the lookahead order (OasisKV page,
+ * Fig. 8: the draft query of step t drives top-K prediction, KV selection and
+ * KV transfer before the layer's attention at step t+1).  Per layer l, in
+ * order: on `stream`, append io[l].k_new/v_new (when not NULL) and, when the
+ * layer has selected before and io[l].q and io[l].out are not NULL, attend
+ * with io[l].q over the set the previous call selected; then on `side`,
+ * predict from io[l].drafts alone (n_drafts >= 1) and select_and_fetch(cap);
+ * the selected misses are copied host -> HBM on `xfer`.  The next call's
+ * append and attention of that layer wait for the copy; the call itself does
+ * not: `stream` does not wait for `side` or `xfer`, so transfers run under
+ * the attention of the following layers.  Synchronize all three streams (or
+ * the device) before reusing the call's inputs.  Call it with every q = NULL
+ * and cap = K for the admission step (predict and fetch only).  The handles
+ * must be distinct; on error no further call is issued and
+ * oasis_last_error(layers[0]) names the failing layer. */
+int oasis_decode_layers_ahead(oasis_t *const *layers, const oasis_layer_io *io,
+                              int32_t n_layers, int32_t n_drafts, int32_t cap,
+                              hipStream_t stream, hipStream_t side, hipStream_t xfer);
 
 /* ---------------------------------------------------------------- inspection */
 

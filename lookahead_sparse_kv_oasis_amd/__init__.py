@@ -28,7 +28,7 @@ BUF = dict(SUMMARY=0, SLOTS=1, HOST_KV=2, SCORES=3, IDS=4, SLOT_BLOCK=5, BLOCK_S
 
 EXPORTS = [
     "oasis_create", "oasis_create_shared", "oasis_destroy", "oasis_load_prefix",
-    "oasis_set_state", "oasis_decode_layers",
+    "oasis_set_state", "oasis_decode_layers", "oasis_decode_layers_ahead",
     "oasis_append_kv", "oasis_predict", "oasis_topk_from_scores", "oasis_select_and_fetch",
     "oasis_evict", "oasis_sparse_attn", "oasis_buffer_bytes", "oasis_read", "oasis_get_stats",
     "oasis_check", "oasis_set_timing", "oasis_set_timing_period", "oasis_get_timing", "oasis_get_dims", "oasis_tokens",
@@ -89,6 +89,9 @@ def lib():
             "oasis_decode_layers": (ctypes.c_int, [ctypes.POINTER(ctypes.c_void_p),
                                                    ctypes.POINTER(oasis_layer_io), i32, i32, i32,
                                                    vp, vp]),
+            "oasis_decode_layers_ahead": (ctypes.c_int, [ctypes.POINTER(ctypes.c_void_p),
+                                                         ctypes.POINTER(oasis_layer_io), i32, i32,
+                                                         i32, vp, vp, vp]),
             "oasis_destroy": (ctypes.c_int, [H]),
             "oasis_load_prefix": (ctypes.c_int, [H, vp, vp, i64]),
             "oasis_set_state": (ctypes.c_int, [H, vp, vp]),
@@ -308,3 +311,10 @@ class LayerStep:
         rc = lib().oasis_decode_layers(self._h, self._io, len(self.layers), n_drafts, cap, st, sd)
         if rc != OASIS_OK:
             self.layers[0]._check(rc, "oasis_decode_layers")
+
+    def run_ahead(self, n_drafts, cap, stream, side, xfer):
+        """oasis_decode_layers_ahead: the lookahead ordering on three streams."""
+        rc = lib().oasis_decode_layers_ahead(self._h, self._io, len(self.layers), n_drafts, cap,
+                                             _stream(stream), _stream(side), _stream(xfer))
+        if rc != OASIS_OK:
+            self.layers[0]._check(rc, "oasis_decode_layers_ahead")

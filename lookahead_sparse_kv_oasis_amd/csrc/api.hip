@@ -108,7 +108,7 @@ struct oasis_handle {
     size_t evict_cap = 0;
 
     hipStream_t copy = nullptr;
-    Mark m_select, m_gather, m_attn;
+    Mark m_append, m_select, m_gather, m_attn;
     hipEvent_t ev_fork = nullptr, ev_join = nullptr;   // oasis_decode_layers
 
     int64_t n_select = 0;
@@ -256,7 +256,8 @@ void free_all(oasis_t *h) {
     (void)hipFree(h->evict_buf);
     h->hkv.reset();
     if (h->copy) (void)hipStreamDestroy(h->copy);
-    for (hipEvent_t e : {h->m_select.ev, h->m_gather.ev, h->m_attn.ev, h->ev_fork, h->ev_join})
+    for (hipEvent_t e : {h->m_append.ev, h->m_select.ev, h->m_gather.ev, h->m_attn.ev, h->ev_fork,
+                         h->ev_join})
         if (e) (void)hipEventDestroy(e);
     for (auto &t : h->tm) {
         for (auto e : t.start) (void)hipEventDestroy(e);
@@ -449,6 +450,7 @@ int create_handle(const oasis_layout *layout, int32_t block_size, int32_t budget
         return bail(OASIS_E_HIP);
     if (reset_tables(h) != OASIS_OK) return bail(OASIS_E_HIP);
     if (hipStreamCreateWithFlags(&h->copy, hipStreamNonBlocking) != hipSuccess ||
+        hipEventCreateWithFlags(&h->m_append.ev, hipEventDisableTiming) != hipSuccess ||
         hipEventCreateWithFlags(&h->m_select.ev, hipEventDisableTiming) != hipSuccess ||
         hipEventCreateWithFlags(&h->m_gather.ev, hipEventDisableTiming) != hipSuccess ||
         hipEventCreateWithFlags(&h->m_attn.ev, hipEventDisableTiming) != hipSuccess ||
@@ -606,13 +608,16 @@ extern "C" int oasis_append_kv(oasis_t *h, const void *k_dev, const void *v_dev,
                          h->slots, stream));
     ++h->T;
     h->hkv->high = std::max(h->hkv->high, h->T);
+    TRY(mark(h, h->m_append, stream));
     return OASIS_OK;
 }
 
 extern "C" int oasis_predict(oasis_t *h, const void *q_dev, const void *drafts_dev,
                              int32_t n_drafts, int32_t *block_ids_dev, float *scores_dev,
                              hipStream_t stream) {
-    if (!h || !q_dev || !aligned16(q_dev)) return h ? fail(h, OASIS_E_INVAL, "predict: bad q") : OASIS_E_INVAL;
+    if (!h) return OASIS_E_INVAL;
+    if ((q_dev && !aligned16(q_dev)) || (!q_dev && n_drafts < 1))
+        return fail(h, OASIS_E_INVAL, "predict: bad q (null q needs at least one draft)");
     if (n_drafts < 0 || n_drafts > h->L.max_drafts)
         return fail(h, OASIS_E_INVAL, "predict: n_drafts %d outside [0, %d]", n_drafts,
                     h->L.max_drafts);
@@ -621,6 +626,7 @@ extern "C" int oasis_predict(oasis_t *h, const void *q_dev, const void *drafts_d
     const int64_t NB = nb_of(h);
     if (NB == 0) return fail(h, OASIS_E_STATE, "predict: no tokens loaded");
     const Dims &D = h->D;
+    TRY(after(h, stream, h->m_append));
     LAUNCH(h, TM_SCORE, stream,
            launch_score(D, h->summ, q_dev, drafts_dev, n_drafts, NB, h->scores,
                         stream));
@@ -651,7 +657,12 @@ extern "C" int oasis_topk_from_scores(oasis_t *h, const float *scores_dev,
     return OASIS_OK;
 }
 
-extern "C" int oasis_select_and_fetch(oasis_t *h, int32_t cap, hipStream_t stream) {
+namespace {
+
+// Select, then copy the fetched blocks: inside the next attention when the
+// handle fuses the fetch and `gst` is null, else eagerly on `gst` (the copy
+// stream when null).
+int select_impl(oasis_t *h, int32_t cap, hipStream_t stream, bool eager, hipStream_t gst) {
     if (!h) return OASIS_E_INVAL;
     if (!h->predicted) return fail(h, OASIS_E_STATE, "select before predict");
     const Dims &D = h->D;
@@ -677,18 +688,25 @@ extern "C" int oasis_select_and_fetch(oasis_t *h, int32_t cap, hipStream_t strea
     }
     h->last_cap = cap;
     TRY(mark(h, h->m_select, stream));
-    if (h->fused) {
+    if (h->fused && !eager) {
         h->fetch_pending = cap > 0;
-    } else {
-        TRY(after(h, h->copy, h->m_select));
-        LAUNCH(h, TM_GATHER, h->copy,
+    } else if (cap > 0) {
+        hipStream_t g = gst ? gst : h->copy;
+        TRY(after(h, g, h->m_select));
+        LAUNCH(h, TM_GATHER, g,
                launch_gather(D, h->host_kv_dev, h->slots, h->fetch_block, h->fetch_slot, D.K,
-                             h->counts, 4, 2, cap, h->copy));
-        TRY(mark(h, h->m_gather, h->copy));
+                             h->counts, 4, 2, cap, g));
+        TRY(mark(h, h->m_gather, g));
     }
     ++h->n_select;
     h->selected = true;
     return OASIS_OK;
+}
+
+}  // namespace
+
+extern "C" int oasis_select_and_fetch(oasis_t *h, int32_t cap, hipStream_t stream) {
+    return select_impl(h, cap, stream, false, nullptr);
 }
 
 extern "C" int oasis_evict(oasis_t *h, const int32_t *blocks_host, const int32_t *counts_host,
@@ -799,6 +817,53 @@ extern "C" int oasis_decode_layers(oasis_t *const *layers, const oasis_layer_io 
     if (bad > 0) {
         const std::string msg = layers[bad]->last_error;
         fail(h0, rc, "decode_layers: layer %d: %s", bad, msg.c_str());
+    }
+    return rc;
+}
+
+// One decode step over the layers in the lookahead order (OasisKV page,
+// Fig. 8): per layer, the new token is appended and the current query attends
+// over the set the previous call selected (on `stream`); then the drafts alone
+// predict the next step's set, which is selected (on `side`) and copied host
+// -> HBM (on `xfer`).  Nothing waits for the copies until that layer's next
+// attention, so each transfer has the rest of the step to land.
+extern "C" int oasis_decode_layers_ahead(oasis_t *const *layers, const oasis_layer_io *io,
+                                         int32_t n_layers, int32_t n_drafts, int32_t cap,
+                                         hipStream_t stream, hipStream_t side,
+                                         hipStream_t xfer) {
+    if (!layers || !io || n_layers < 1) return OASIS_E_INVAL;
+    if (n_drafts < 1) return fail(layers[0], OASIS_E_INVAL, "decode_layers_ahead: no drafts");
+    for (int32_t l = 0; l < n_layers; ++l) {
+        if (!layers[l]) return OASIS_E_INVAL;
+        for (int32_t m = 0; m < l; ++m)
+            if (layers[m] == layers[l])
+                return fail(layers[l], OASIS_E_INVAL, "decode_layers_ahead: handle %d repeats %d",
+                            l, m);
+        if ((io[l].k_new == nullptr) != (io[l].v_new == nullptr))
+            return fail(layers[l], OASIS_E_INVAL, "decode_layers_ahead: layer %d has k without v",
+                        l);
+        if (!io[l].drafts)
+            return fail(layers[l], OASIS_E_INVAL, "decode_layers_ahead: layer %d has no drafts", l);
+    }
+    oasis_t *h0 = layers[0];
+    // side and xfer see the caller's earlier work
+    HIP_OK(h0, hipEventRecord(h0->ev_fork, stream));
+    HIP_OK(h0, hipStreamWaitEvent(side, h0->ev_fork, 0));
+    HIP_OK(h0, hipStreamWaitEvent(xfer, h0->ev_fork, 0));
+    int rc = OASIS_OK, bad = -1;
+    for (int32_t l = 0; l < n_layers && rc == OASIS_OK; ++l) {
+        oasis_t *h = layers[l];
+        if (io[l].k_new) rc = oasis_append_kv(h, io[l].k_new, io[l].v_new, stream);
+        if (rc == OASIS_OK && h->selected && io[l].q && io[l].out)
+            rc = oasis_sparse_attn(h, io[l].q, io[l].out, stream);
+        if (rc == OASIS_OK)
+            rc = oasis_predict(h, nullptr, io[l].drafts, n_drafts, nullptr, nullptr, side);
+        if (rc == OASIS_OK) rc = select_impl(h, cap, side, true, xfer);
+        if (rc != OASIS_OK) bad = l;
+    }
+    if (bad > 0) {
+        const std::string msg = layers[bad]->last_error;
+        fail(h0, rc, "decode_layers_ahead: layer %d: %s", bad, msg.c_str());
     }
     return rc;
 }

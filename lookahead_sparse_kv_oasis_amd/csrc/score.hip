@@ -27,16 +27,17 @@ template <typename T>
 __global__ __launch_bounds__(64) void score_valu_kernel(const T *__restrict__ summ,
                                                         const T *__restrict__ q,
                                                         const T *__restrict__ drafts,
-                                                        int n_drafts, float *__restrict__ scores,
+                                                        int n_drafts, int qskip,
+                                                        float *__restrict__ scores,
                                                         int B, int Hq, int Hkv, int G, int d,
                                                         int64_t NBmax, int64_t NB) {
     constexpr int V = Elem<T>::kVec;
     extern __shared__ float xs[];  // [Q][d]
     const int h = blockIdx.y, b = blockIdx.z;
     const int64_t u = (int64_t)b * Hkv + h;
-    const int Q = G * (1 + n_drafts);
+    const int Q = G * (1 - qskip + n_drafts);
     for (int i = threadIdx.x; i < Q * d; i += blockDim.x) {
-        const int r = i / d, c = i % d, src = r / G, g = r % G;
+        const int r = i / d, c = i % d, src = r / G + qskip, g = r % G;
         const T *row = src == 0 ? q + ((int64_t)b * Hq + h * G + g) * d
                                 : drafts + (((int64_t)(src - 1) * B + b) * Hq + h * G + g) * d;
         xs[i] = Elem<T>::f(row[c]);
@@ -102,7 +103,7 @@ template <int D, int QT>
 __global__ __launch_bounds__(256) void score_tiled_kernel(const uint16_t *__restrict__ summ,
                                                           const uint16_t *__restrict__ q,
                                                           const uint16_t *__restrict__ drafts,
-                                                          int n_drafts,
+                                                          int n_drafts, int qskip,
                                                           float *__restrict__ scores, int B,
                                                           int Hq, int Hkv, int G,
                                                           int64_t unit_elems, int64_t NBmax,
@@ -115,7 +116,7 @@ __global__ __launch_bounds__(256) void score_tiled_kernel(const uint16_t *__rest
     const int64_t u = blockIdx.x / per_unit;
     const int64_t chunk = blockIdx.x % per_unit;
     const int h = (int)(u % Hkv), b = (int)(u / Hkv);
-    const int Q = G * (1 + n_drafts);
+    const int Q = G * (1 - qskip + n_drafts);
     const int m = lane & 31, half = lane >> 5;
     const int64_t ntiles = (NB + 31) / 32;
     const int64_t t_begin = chunk * tiles_per_wg;
@@ -137,7 +138,7 @@ __global__ __launch_bounds__(256) void score_tiled_kernel(const uint16_t *__rest
     for (int qt = 0; qt < QT; ++qt) {
         int r = 32 * qt + m;
         if (r >= Q) r = 0;
-        const int src = r / G, g = r % G;
+        const int src = r / G + qskip, g = r % G;
         const uint16_t *x = src == 0
                                 ? q + ((int64_t)b * Hq + h * G + g) * D
                                 : drafts + (((int64_t)(src - 1) * B + b) * Hq + h * G + g) * D;
@@ -172,10 +173,11 @@ __global__ __launch_bounds__(256) void score_tiled_kernel(const uint16_t *__rest
 
 template <int D>
 static void launch_tiled(int QT, dim3 grid, size_t lds, hipStream_t st, const uint16_t *summ,
-                         const uint16_t *q, const uint16_t *dr, int nd, float *scores,
+                         const uint16_t *q, const uint16_t *dr, int nd, int qskip, float *scores,
                          const Dims &Dm, int64_t NB, int per_unit, int tpw) {
 #define OASIS_SCORE_T(QT_)                                                                      \
-    OASIS_LAUNCH((score_tiled_kernel<D, QT_>), grid, dim3(256), lds, st, summ, q, dr, nd, scores, \
+    OASIS_LAUNCH((score_tiled_kernel<D, QT_>), grid, dim3(256), lds, st, summ, q, dr, nd, qskip,  \
+                 scores,                                                                       \
                  Dm.B, Dm.Hq, Dm.Hkv, Dm.G, Dm.summ_unit_elems(), Dm.NBmax, NB, per_unit, tpw)
     if (QT == 1) OASIS_SCORE_T(1);
     else if (QT == 2) OASIS_SCORE_T(2);
@@ -187,7 +189,8 @@ static void launch_tiled(int QT, dim3 grid, size_t lds, hipStream_t st, const ui
 hipError_t launch_score(const Dims &D, const void *summ, const void *q, const void *drafts,
                         int n_drafts, int64_t NB, float *scores, hipStream_t st) {
     if (NB <= 0) return hipSuccess;
-    const int Q = D.G * (1 + n_drafts);
+    const int qskip = q ? 0 : 1;  // no current query: the drafts alone
+    const int Q = D.G * (1 - qskip + n_drafts);
     if (D.tiled) {
         const int QT = (Q + 31) / 32;
         const int64_t ntiles = (NB + 31) / 32;
@@ -202,22 +205,23 @@ hipError_t launch_score(const Dims &D, const void *summ, const void *q, const vo
         const uint16_t *s = (const uint16_t *)summ, *qq = (const uint16_t *)q,
                        *dr = (const uint16_t *)drafts;
         if (D.d == 64)
-            launch_tiled<64>(QT, grid, lds, st, s, qq, dr, n_drafts, scores, D, NB, (int)per_unit, (int)tpw);
+            launch_tiled<64>(QT, grid, lds, st, s, qq, dr, n_drafts, qskip, scores, D, NB, (int)per_unit, (int)tpw);
         else if (D.d == 128)
-            launch_tiled<128>(QT, grid, lds, st, s, qq, dr, n_drafts, scores, D, NB, (int)per_unit, (int)tpw);
+            launch_tiled<128>(QT, grid, lds, st, s, qq, dr, n_drafts, qskip, scores, D, NB, (int)per_unit, (int)tpw);
         else
-            launch_tiled<256>(QT, grid, lds, st, s, qq, dr, n_drafts, scores, D, NB, (int)per_unit, (int)tpw);
+            launch_tiled<256>(QT, grid, lds, st, s, qq, dr, n_drafts, qskip, scores, D, NB, (int)per_unit, (int)tpw);
         return hipGetLastError();
     }
     dim3 grid((unsigned)((NB + 63) / 64), D.Hkv, D.B), block(64);
     const size_t lds = sizeof(float) * Q * D.d;
     if (D.dtype == kF32)
         OASIS_LAUNCH(score_valu_kernel<float>, grid, block, lds, st, (const float *)summ,
-                     (const float *)q, (const float *)drafts, n_drafts, scores, D.B, D.Hq,
+                     (const float *)q, (const float *)drafts, n_drafts, qskip, scores, D.B, D.Hq,
                      D.Hkv, D.G, D.d, D.NBmax, NB);
     else
         OASIS_LAUNCH(score_valu_kernel<uint16_t>, grid, block, lds, st, (const uint16_t *)summ,
-                     (const uint16_t *)q, (const uint16_t *)drafts, n_drafts, scores, D.B, D.Hq,
+                     (const uint16_t *)q, (const uint16_t *)drafts, n_drafts, qskip, scores, D.B,
+                     D.Hq,
                      D.Hkv, D.G, D.d, D.NBmax, NB);
     return hipGetLastError();
 }

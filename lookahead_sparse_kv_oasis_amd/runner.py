@@ -42,6 +42,10 @@ class LayerRunner:
         self.app_v = to_device(np.ascontiguousarray(V[:, :, self.T0:].transpose(2, 0, 1, 3)), device)
         del K, V
         self.q = to_device(synth.queries(w, layer), device)
+        # current query per step (the same tensor unless the workload drifts)
+        self.q_steps = ([to_device(synth.query_at(w, t, layer), device)
+                         for t in range(n_steps + 1)] if w.query_drift else
+                        [self.q] * (n_steps + 1))
         self.drafts = [to_device(synth.drafts(w, t, layer), device) for t in range(n_steps + 1)]
         self.out = torch.empty((w.batch, w.q_heads, w.head_dim), dtype=torch.float32,
                                device=device)
@@ -64,13 +68,32 @@ class LayerRunner:
         instead of the library's own (parity runs)."""
         h = self.h
         h.oasis_append_kv(self.app_k[t - 1], self.app_v[t - 1], stream=stream)
-        h.oasis_predict(self.q, self.drafts[t], self.w.drafts, stream=stream)
+        q = self.q_steps[t]
+        h.oasis_predict(q, self.drafts[t], self.w.drafts, stream=stream)
         if scores_hook is not None:
             s = scores_hook(t)
             if s is not None:
                 h.oasis_topk_from_scores(s, stream=stream)
         h.oasis_select_and_fetch(self.cap, stream=stream)
-        h.oasis_sparse_attn(self.q, self.out, stream=stream)
+        h.oasis_sparse_attn(q, self.out, stream=stream)
+        self.t = t
+
+    # ---- lookahead ordering ([OASIS] Fig. 8)
+    def admission_ahead(self, stream=None):
+        """Untimed step 0: the step-0 drafts select (cap = K) the set that step
+        1 attends over."""
+        h = self.h
+        h.oasis_predict(None, self.drafts[0], self.w.drafts, stream=stream)
+        h.oasis_select_and_fetch(self.w.k_blocks, stream=stream)
+
+    def step_ahead(self, t: int, stream=None, cap: int | None = None):
+        """Step t: append token T0 + t - 1, attend with the step-t query over
+        the set step t-1 selected, then select step t+1's set from the drafts."""
+        h = self.h
+        h.oasis_append_kv(self.app_k[t - 1], self.app_v[t - 1], stream=stream)
+        h.oasis_sparse_attn(self.q_steps[t], self.out, stream=stream)
+        h.oasis_predict(None, self.drafts[t], self.w.drafts, stream=stream)
+        h.oasis_select_and_fetch(self.cap if cap is None else cap, stream=stream)
         self.t = t
 
 
@@ -106,7 +129,7 @@ class ModelRunner:
                                       budget_tokens=w.budget_tokens, fetch_ratio=w.fetch_ratio,
                                       slots_per_head=w.n_slots, share_host_with=owner)
         self.handles = [None] * self.n_layers
-        self.app_k, self.app_v, self.q = [], [], []
+        self.app_k, self.app_v, self.q, self.q_steps = [], [], [], []
         for g in range(self.H):
             if log:
                 log(f"generating data layer {g} of {self.H}")
@@ -118,6 +141,9 @@ class ModelRunner:
             self.app_v.append(to_device(Va, device))
             del Ka, Va
             self.q.append(to_device(synth.queries(w, g), device))
+            self.q_steps.append([to_device(synth.query_at(w, t, g), device)
+                                 for t in range(n_steps + 1)] if w.query_drift else
+                                [self.q[-1]] * (n_steps + 1))
             for l in range(g, self.n_layers, self.H):
                 if l == g:
                     self.handles[l] = owner
@@ -154,7 +180,7 @@ class ModelRunner:
             g = self.group_of(l)
             k = self.app_k[g][t - 1] if t > 0 else None
             v = self.app_v[g][t - 1] if t > 0 else None
-            a.set(l, k, v, self.q[g], self.drafts[t][l], self.out[l])
+            a.set(l, k, v, self.q_steps[g][t], self.drafts[t][l], self.out[l])
 
     def admission(self, stream=None, side=None):
         """Untimed step 0 on every layer: select on the prompt, fetch it all."""
@@ -168,7 +194,47 @@ class ModelRunner:
                            side=side)
         self.t = t
 
+    # ---- lookahead ordering ([OASIS] Fig. 8): oasis_decode_layers_ahead
+    def admission_ahead(self, stream, side, xfer):
+        """Untimed step 0: every layer's step-0 drafts select (cap = K) and
+        fetch the set its step-1 attention uses."""
+        a = self.step_args
+        for l in range(self.n_layers):
+            a.set(l, None, None, None, self.drafts[0][l], None)
+        a.run_ahead(self.w.drafts, self.w.k_blocks, stream, side, xfer)
+
+    def step_ahead(self, t: int, stream, side, xfer, cap: int | None = None):
+        a = self.step_args
+        for l in range(self.n_layers):
+            g = self.group_of(l)
+            a.set(l, self.app_k[g][t - 1], self.app_v[g][t - 1], self.q_steps[g][t],
+                  self.drafts[t][l], self.out[l])
+        a.run_ahead(self.w.drafts, self.cap if cap is None else cap, stream, side, xfer)
+        self.t = t
+
     def close(self):
         for h in self.handles[::-1]:
             if h is not None:
                 h.close()
+
+
+# ---- prediction quality of the lookahead ordering ([OASIS] Fig. 4, Fig. 6)
+
+def predicted_ids(h) -> np.ndarray:
+    """The handle's current selection (ids) as [units][K]."""
+    return h.read("IDS").reshape(-1, h.k_blocks)
+
+
+def exact_ids(h, q, buf: torch.Tensor, stream=None) -> np.ndarray:
+    """Top-K ids of the current query alone ([units][K]).  Leaves the handle's
+    scores and ids changed: call it where the next predict recomputes them."""
+    h.oasis_predict(q, None, 0, block_ids=buf, stream=stream)
+    torch.cuda.synchronize()
+    return buf.cpu().numpy().reshape(-1, h.k_blocks)
+
+
+def recall(pred: np.ndarray, exact: np.ndarray) -> float:
+    """Mean over units of |pred ∩ exact| / |exact| (ids -1 are padding)."""
+    hit = (pred[:, :, None] == exact[:, None, :]) & (exact[:, None, :] >= 0)
+    n = np.maximum((exact >= 0).sum(axis=1), 1)
+    return float((hit.any(axis=1).sum(axis=1) / n).mean())

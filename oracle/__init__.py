@@ -257,6 +257,28 @@ class Unit:
         return rec
 
 
+    def step_ahead(self, t, x_rows, q_rows, cap, append=True, scores32=None, attend=True):
+        """One decode step in the lookahead order ([OASIS] Fig. 8): token t is
+        appended; the current query attends over the blocks that the previous
+        step selected (self.att); then the draft rows x_rows are scored and the
+        top-K, diff, cap and LRU choose the set for the next step's attention.
+        attend=False (the untimed admission step) skips the attention."""
+        if append:
+            self.append()
+        att = getattr(self, "att", np.zeros(0, np.int32))
+        out = (attention(q_rows, self.keys, self.vals, self.dtype, self.bs, self.T, att)
+               if attend else None)
+        s64 = self.score(x_rows)
+        s32 = s64.astype(np.float32) if scores32 is None else np.asarray(scores32, np.float32)
+        ids = topk(s32, self.K)
+        sel = select(self.slot_block, self.last_used, ids, cap, t)
+        self.att = sel["att_block"]
+        rec = dict(t=t, T=self.T, scores64=s64, scores32=s32, ids=ids, out=out, attended=att,
+                   slot_block=self.slot_block.copy(), last_used=self.last_used.copy())
+        rec.update(sel)
+        return rec
+
+
 def unit_rows(q, drafts_t, b, h, group):
     """Query rows of one unit: the G group heads of the current query, then of
     every draft (scoring), and the current query alone (attention)."""
@@ -264,3 +286,9 @@ def unit_rows(q, drafts_t, b, h, group):
     cur = q[b, g0:g1]
     rows = [cur] + [drafts_t[i, b, g0:g1] for i in range(drafts_t.shape[0])]
     return np.concatenate(rows, axis=0), cur
+
+
+def draft_rows(drafts_t, b, h, group):
+    """Scoring rows of one unit from the drafts alone (lookahead prediction)."""
+    g0, g1 = h * group, (h + 1) * group
+    return np.concatenate([drafts_t[i, b, g0:g1] for i in range(drafts_t.shape[0])], axis=0)

@@ -14,7 +14,7 @@ from __future__ import annotations
 import numpy as np
 
 import synth
-from . import Unit, cap_from_ratio, to_f64, unit_rows
+from . import Unit, cap_from_ratio, draft_rows, to_f64, unit_rows
 
 
 def workload_cap(w: synth.Workload) -> int:
@@ -57,4 +57,24 @@ def run_unit(w: synth.Workload, b: int, h: int, n_steps: int, layer: int = 0, ca
         rec["evicted"] = ev if ev is not None else np.zeros(0, np.int32)
         recs.append(rec)
         prev_att = rec["att_block"]
+    return recs
+
+
+def run_unit_ahead(w: synth.Workload, b: int, h: int, n_steps: int, layer: int = 0, cap=None,
+                   kv=None, unit: Unit | None = None):
+    """Lookahead trajectory ([OASIS] Fig. 8) of one unit: an admission step 0
+    selects (cap = K) from the step-0 drafts; step t appends token t, attends
+    with the step-t query over the set chosen at step t-1, and selects the
+    set for step t+1 from the step-t drafts alone."""
+    if unit is None:
+        unit = initial_unit(w, b, h, n_steps, layer, kv)
+    cap = workload_cap(w) if cap is None else cap
+    recs = []
+    x = draft_rows(to_f64(synth.drafts(w, 0, layer), w.dtype), b, h, w.group)
+    recs.append(unit.step_ahead(0, x, None, w.k_blocks, append=False, attend=False))
+    for t in range(1, n_steps + 1):
+        q = to_f64(synth.query_at(w, t, layer), w.dtype)
+        cur = q[b, h * w.group:(h + 1) * w.group]
+        x = draft_rows(to_f64(synth.drafts(w, t, layer), w.dtype), b, h, w.group)
+        recs.append(unit.step_ahead(t, x, cur, cap))
     return recs

@@ -30,7 +30,7 @@ F32 = 0
 BF16 = 1
 
 # stream kinds
-_K, _V, _Q, _DRAFT, _HEAVY, _RESID, _EVICT = 1, 2, 3, 4, 5, 6, 7
+_K, _V, _Q, _DRAFT, _HEAVY, _RESID, _EVICT, _QDRIFT = 1, 2, 3, 4, 5, 6, 7, 8
 
 
 @dataclasses.dataclass(frozen=True)
@@ -60,6 +60,12 @@ class Workload:
     admission: bool = True    # uncapped step 0 fills the pool with the step-0 selection
     initial_resident_frac: float = 0.0
     layers: int = 1
+    # Lookahead workloads: the current query drifts between steps (AR(1) around
+    # the step-0 query: e_t = rho e_{t-1} + sqrt(1 - rho^2) query_drift xi_t)
+    # and the drafts of step t are centred on the next step's query.
+    query_drift: float = 0.0
+    drift_rho: float = 0.9
+    lookahead: bool = False
     seed: int = 0
 
     @property
@@ -109,7 +115,19 @@ QWEN3_8B_36L = Workload(
     dtype=BF16, prefix_tokens=65536, steps=32, heavy_frac=0.05, heavy_amp=2.0,
     fetch_ratio=0.02, layers=36)
 
-WORKLOADS = [TINY, QWEN3_8B, LLAMA31_8B_LONG, QWEN3_32B, QWEN3_8B_36L]
+# Lookahead ordering ([OASIS] Fig. 8): the drafts of step t predict the set for
+# step t+1's attention.  Queries drift (AR(1), stationary std 0.5 per element,
+# rho 0.9, so about 0.22 change per step) and the drafts sit 0.1 around the next
+# query, so the previous query and the drafts are both imperfect predictors.
+QWEN3_8B_AHEAD = QWEN3_8B.with_(name="qwen3_8b_layer_b32_t32k_bf16_lookahead",
+                                query_drift=0.5, drift_rho=0.9, draft_sigma=0.1,
+                                lookahead=True)
+QWEN3_8B_36L_AHEAD = QWEN3_8B_36L.with_(name="qwen3_8b_36layer_b64_t64k_bf16_lookahead",
+                                        query_drift=0.5, drift_rho=0.9, draft_sigma=0.1,
+                                        lookahead=True)
+
+WORKLOADS = [TINY, QWEN3_8B, LLAMA31_8B_LONG, QWEN3_32B, QWEN3_8B_36L, QWEN3_8B_AHEAD,
+             QWEN3_8B_36L_AHEAD]
 FETCH_RATIO_SWEEP = [0.01, 0.02, 0.05, 0.10, 0.20, None]   # None = fetch all
 
 
@@ -159,12 +177,38 @@ def _queries_f32(w: Workload, layer: int) -> np.ndarray:
     return decode_f32(queries(w, layer), w.dtype)
 
 
+@functools.lru_cache(maxsize=8)
+def _drift(w: Workload, layer: int, upto: int) -> tuple:
+    """Deviations e_0 .. e_upto of the drifting query (e_0 = 0), fp32."""
+    shape = (w.batch, w.q_heads, w.head_dim)
+    e = [np.zeros(shape, np.float32)]
+    c = np.float32(np.sqrt(1.0 - w.drift_rho ** 2) * w.query_drift)
+    for t in range(1, upto + 1):
+        xi = _rng(w, layer, _QDRIFT, t).standard_normal(shape, dtype=np.float32)
+        e.append(np.float32(w.drift_rho) * e[-1] + c * xi)
+    return tuple(e)
+
+
+def query_at(w: Workload, step: int, layer: int = 0) -> np.ndarray:
+    """Current query of decode step `step` in storage dtype: the step-0 query,
+    plus the AR(1) deviation of a lookahead workload."""
+    if w.query_drift == 0.0 or step == 0:
+        return queries(w, layer)
+    e = _drift(w, layer, max(step, w.steps + 1))[step]
+    return encode(_queries_f32(w, layer) + e, w.dtype)
+
+
 def drafts(w: Workload, step: int, layer: int = 0, q_layer: int | None = None) -> np.ndarray:
     """Draft queries [D][b][g][d] = q + N(0, sigma^2), redrawn every step.
 
-    q is layer q_layer's query (default: the same layer); the noise stream is
-    layer's own."""
-    q = _queries_f32(w, layer if q_layer is None else q_layer)
+    q is layer q_layer's query (default: the same layer) at this step, or at
+    the next step for a lookahead workload (the draft tokens approximate the
+    query that comes next); the noise stream is layer's own."""
+    ql = layer if q_layer is None else q_layer
+    if w.lookahead or w.query_drift != 0.0:
+        q = decode_f32(query_at(w, step + 1 if w.lookahead else step, ql), w.dtype)
+    else:
+        q = _queries_f32(w, ql)
     g = _rng(w, layer, _DRAFT, step)
     noise = g.standard_normal((w.drafts, w.batch, w.q_heads, w.head_dim), dtype=np.float32)
     return encode(q[None] + np.float32(w.draft_sigma) * noise, w.dtype)

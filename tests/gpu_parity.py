@@ -365,7 +365,94 @@ class FreeRunning(Parity):
         return report
 
 
-class PipelineLayer(FreeRunning):
+class AheadRunning(FreeRunning):
+    """Lookahead ordering ([OASIS] Fig. 8) on one layer, free running: step t
+    appends, attends with the step-t query over the set step t-1 selected, and
+    selects step t+1's set from the drafts alone.  Checked per step: the draft
+    scores against the oracle's, the ids against the oracle top-K of the
+    GPU's own fp32 scores, the select against the oracle select on the GPU's
+    previous tables, and the attention against the oracle attention over the
+    previously selected (and checked) list."""
+
+    def _draft_rows(self, t, b, hh):
+        d = oracle.to_f64(synth.drafts(self.w, t, self.layer, self.q_layer), self.w.dtype)
+        return oracle.draft_rows(d, b, hh, self.G)
+
+    def verify_ahead(self, t, prev, prev_att, report, cap, check_payload=False):
+        w, h = self.w, self.run.h
+        K = h.k_blocks
+        gpu_scores = h.read("SCORES", np.float32).reshape(w.batch, w.kv_heads, self.NBmax)
+        ids = h.read("IDS")
+        fb, fs = h.read("FETCH_BLOCK"), h.read("FETCH_SLOT")
+        ab, ast = h.read("ATT_BLOCK"), h.read("ATT_SLOT")
+        cnt = h.read("COUNTS")
+        out = self.run.out.cpu().numpy()
+        q = oracle.to_f64(synth.query_at(w, t, self.q_layer if self.q_layer is not None
+                                         else self.layer), w.dtype)
+        now = self._tables()
+        att_now = {}
+        for (b, hh) in self.units:
+            tag = f"lookahead step {t} layer {self.layer} unit {(b, hh)}"
+            unit = self.oru[(b, hh)]
+            if t > 0:
+                unit.append()
+                cur = q[b, hh * self.G:(hh + 1) * self.G]
+                exp_out = oracle.attention(cur, unit.keys, unit.vals, w.dtype, w.block_size,
+                                           unit.T, prev_att[(b, hh)])
+                g0 = hh * self.G
+                e = float(np.max(np.abs(out[b, g0:g0 + self.G].astype(np.float64) - exp_out)))
+                report["attn_err"] = max(report["attn_err"], e)
+                assert e <= ATTN_TOL, tag + f" attention err {e:.3g}"
+            x = self._draft_rows(t, b, hh)
+            nb = unit.nb
+            ref = unit.score(x)
+            err = np.abs(gpu_scores[b, hh, :nb].astype(np.float64) - ref) / score_scale(unit, x)
+            report["score_err"] = max(report["score_err"], float(err.max()))
+            assert err.max() <= SCORE_TOL, tag + f" score err {err.max():.3g}"
+            exp_ids = oracle.topk(gpu_scores[b, hh, :nb], K)
+            assert np.array_equal(self._unit_slice(ids, b, hh, K), exp_ids), tag + " ids"
+            sb0, lu0 = prev[(b, hh)]
+            sb_exp, lu_exp = sb0.copy(), lu0.copy()
+            r = oracle.select(sb_exp, lu_exp, exp_ids, cap, t)
+            c = self._unit_slice(cnt, b, hh, 4)
+            na, nh, nf = int(c[0]), int(c[1]), int(c[2])
+            assert (na, nh, nf) == (len(r["att_block"]), r["n_hit"], len(r["fetch_block"])), tag
+            assert np.array_equal(self._unit_slice(fb, b, hh, K)[:nf], r["fetch_block"]), tag
+            assert np.array_equal(self._unit_slice(fs, b, hh, K)[:nf], r["fetch_slot"]), tag
+            assert np.array_equal(self._unit_slice(ab, b, hh, K)[:na], r["att_block"]), tag
+            assert np.array_equal(self._unit_slice(ast, b, hh, K)[:na], r["att_slot"]), tag
+            assert np.array_equal(now[(b, hh)][0], sb_exp), tag + " slot_block"
+            assert np.array_equal(now[(b, hh)][1], lu_exp), tag + " last_used"
+            att_now[(b, hh)] = r["att_block"].copy()
+            report["fetched"] += nf
+        if check_payload:
+            self.check_payload(t)
+            self.check_summary()
+        report["steps"] = t
+        return now, att_now
+
+    def run_ahead(self, steps=None, check_payload_every=4):
+        w, run = self.w, self.run
+        steps = self.n_steps if steps is None else steps
+        report = dict(score_err=0.0, attn_err=0.0, steps=0, fetched=0)
+        empty = {k: (np.full(run.h.slots, -1, np.int32), np.full(run.h.slots, -1, np.int32))
+                 for k in self.units}
+        for k in self.units:
+            self.oru[k].slot_block[:] = -1
+        run.admission_ahead()
+        torch.cuda.synchronize()
+        prev, att = self.verify_ahead(0, empty, None, report, w.k_blocks)
+        for t in range(1, steps + 1):
+            run.step_ahead(t)
+            torch.cuda.synchronize()
+            run.h.oasis_check()
+            prev, att = self.verify_ahead(t, prev, att, report, self.cap,
+                                          check_payload=(t % check_payload_every == 0 or
+                                                         t == steps))
+        return report
+
+
+class PipelineLayer(AheadRunning):
     """Free-running checks of one layer of a ModelRunner (oasis_decode_layers).
 
     The layer's K, V and query come from its data layer; its drafts from its

@@ -110,3 +110,58 @@ def test_qwen3_32b_free_running_with_forced_evictions():
     w = synth.QWEN3_32B
     rep = FreeRunning(w, 16, [(0, 0), (7, 5), (15, 7)]).run_free(check_payload_every=4)
     log(f"{w.name} free: {rep}")
+
+
+# ------------------------------------------------------------------ lookahead ordering
+
+def test_lookahead_ordering_reduced_context():
+    """[OASIS] Fig. 8 ordering on one layer: attention at step t over the set
+    step t-1 predicted from its drafts alone."""
+    from tests.gpu_parity import AheadRunning, log
+    w = synth.QWEN3_8B_AHEAD.with_(batch=2, prefix_tokens=16 * 300 + 7, budget_tokens=16 * 64)
+    p = AheadRunning(w, 10, [(0, 0), (1, 7), (0, 4)])
+    log(f"lookahead reduced: {p.run_ahead()}")
+
+
+def test_lookahead_ordering_full_size_sampled_units():
+    from tests.gpu_parity import AheadRunning, log
+    w = synth.QWEN3_8B_AHEAD
+    p = AheadRunning(w, w.steps, [(0, 0), (17, 5), (31, 7)])
+    log(f"{w.name}: {p.run_ahead(check_payload_every=16)}")
+
+
+def test_lookahead_recall_measurement():
+    """Recall of the drafts' prediction and of the previous query's top-K
+    against the exact top-K of the step's own query; the exact ids are checked
+    against the oracle top-K of the GPU's scores for sampled units."""
+    from lookahead_sparse_kv_oasis_amd.runner import LayerRunner, exact_ids, predicted_ids, recall
+    from tests.gpu_parity import log
+    w = synth.QWEN3_8B_AHEAD.with_(batch=4, prefix_tokens=16 * 400 + 3, budget_tokens=16 * 64)
+    n = 8
+    run = LayerRunner(w, n)
+    h = run.h
+    buf = torch.empty(w.batch * w.kv_heads * w.k_blocks, dtype=torch.int32, device="cuda")
+    run.admission_ahead()
+    torch.cuda.synchronize()
+    prev_exact = None
+    r_ahead, r_prev = [], []
+    K = h.k_blocks
+    for t in range(1, n + 1):
+        pred = predicted_ids(h)
+        h.oasis_append_kv(run.app_k[t - 1], run.app_v[t - 1])
+        ex = exact_ids(h, run.q_steps[t], buf)
+        scores = h.read("SCORES", np.float32).reshape(w.batch * w.kv_heads, -1)
+        nb = w.blocks_at(w.prefix_tokens + t)
+        for u in (0, 9, w.batch * w.kv_heads - 1):
+            assert np.array_equal(ex[u], oracle.topk(scores[u, :nb], K)), f"step {t} unit {u}"
+        r_ahead.append(recall(pred, ex))
+        if prev_exact is not None:
+            r_prev.append(recall(prev_exact, ex))
+        prev_exact = ex
+        h.oasis_sparse_attn(run.q_steps[t], run.out)
+        h.oasis_predict(None, run.drafts[t], w.drafts)
+        h.oasis_select_and_fetch(run.cap)
+    torch.cuda.synchronize()
+    a, p = float(np.mean(r_ahead)), float(np.mean(r_prev))
+    log(f"recall of the exact next top-K: drafts {a:.3f}, previous query {p:.3f}")
+    assert 0.0 < a <= 1.0 and 0.0 < p <= 1.0

@@ -138,3 +138,45 @@ def test_qwen3_8b_36_layers_full_size_sampled_layers():
                         check_payload_every=8)
     _log(f"{w.name}: {rep}")
     mr.close()
+
+
+AHEAD_SMALL = synth.QWEN3_8B_36L_AHEAD.with_(batch=4, prefix_tokens=16 * 300 + 5, layers=5,
+                                             steps=8, budget_tokens=16 * 64)
+
+
+def test_lookahead_executor_against_oracle_and_one_stream():
+    """oasis_decode_layers_ahead on three streams: sampled layers checked step by
+    step against the oracle's lookahead ordering, and every output, table and
+    slot bit-identical to the same calls on one stream."""
+    from tests.gpu_parity import PipelineLayer, pipeline_unit_kv
+    w = AHEAD_SMALL
+    a = _runner(w, w.steps)
+    b = _runner(w, w.steps)
+    cur = torch.cuda.current_stream()
+    side, xfer = torch.cuda.Stream(), torch.cuda.Stream()
+    units = [(0, 0), (3, 7), (2, 5)]
+    checks = [PipelineLayer(a, l, units, pipeline_unit_kv(a, l, units)) for l in (0, 2, 4)]
+    reps = [dict(score_err=0.0, attn_err=0.0, steps=0, fetched=0) for _ in checks]
+    for c in checks:
+        for k in units:
+            c.oru[k].slot_block[:] = -1
+    empty = {k: (np.full(a.handles[0].slots, -1, np.int32),
+                 np.full(a.handles[0].slots, -1, np.int32)) for k in units}
+    a.admission_ahead(cur, side, xfer)
+    b.admission_ahead(cur, cur, cur)
+    torch.cuda.synchronize()
+    state = [c.verify_ahead(0, empty, None, r, w.k_blocks) for c, r in zip(checks, reps)]
+    for t in range(1, w.steps + 1):
+        a.step_ahead(t, cur, side, xfer)
+        b.step_ahead(t, cur, cur, cur)
+        torch.cuda.synchronize()
+        assert torch.equal(a.out, b.out), f"step {t}: outputs differ"
+        state = [c.verify_ahead(t, prev, att, r, a.cap, check_payload=(t % 4 == 0))
+                 for c, r, (prev, att) in zip(checks, reps, state)]
+    for l in range(w.layers):
+        for buf in STATE_BUFS:
+            assert np.array_equal(a.handles[l].read(buf), b.handles[l].read(buf)), f"{l} {buf}"
+        a.handles[l].oasis_check()
+    _log(f"lookahead executor: {reps}")
+    a.close()
+    b.close()

@@ -87,3 +87,63 @@ def test_unit_kv_prefix_property():
     a = synth.unit_kv(w, 0, 2, 1000)
     b = synth.unit_kv(w, 0, 2, 1200)
     assert np.array_equal(a[0], b[0][:1000]) and np.array_equal(a[1], b[1][:1000])
+
+
+# ------------------------------------------------------------------ lookahead ordering
+
+def _ahead_small(**kw):
+    return synth.QWEN3_8B_AHEAD.with_(batch=1, prefix_tokens=16 * 6 + 14, budget_tokens=16 * 16,
+                                      **kw)
+
+
+def test_lookahead_attends_the_previous_steps_selection():
+    """Fig. 8 ordering: step t's attention runs over exactly the blocks that
+    step t-1 selected, and a capped step never fetches more than the cap."""
+    from oracle.trajectory import run_unit_ahead
+    w = synth.QWEN3_8B_AHEAD.with_(batch=1, prefix_tokens=16 * 300 + 5, budget_tokens=16 * 32)
+    recs = run_unit_ahead(w, 0, 5, 8)
+    assert recs[0]["out"] is None and len(recs[0]["attended"]) == 0
+    for prev, r in zip(recs, recs[1:]):
+        assert np.array_equal(r["attended"], prev["att_block"])
+        assert len(r["fetch_block"]) <= workload_cap(w)
+        held = set(int(b) for b in r["slot_block"] if b >= 0)
+        # the set attended at step t+1 is held after step t's select
+        assert set(int(b) for b in r["att_block"]) <= held
+
+
+def test_lookahead_with_whole_context_budget_is_dense_attention_minus_the_newest_block():
+    """Budget and cap covering every block: the attended set at step t is every
+    block that existed at step t-1.  When token t lands in an existing block
+    that is the whole context (dense attention over T tokens); when token t
+    opens a new block, that block was not there to be predicted, so the output
+    is dense attention over the first T - 1 tokens."""
+    from oracle.trajectory import run_unit_ahead
+    w = _ahead_small(cap=16)
+    n = 6
+    recs = run_unit_ahead(w, 0, 2, n, cap=16)
+    keys, vals = synth.unit_kv(w, 0, 2, w.prefix_tokens + n)
+    opened = 0
+    for r in recs[1:]:
+        q = oracle.to_f64(synth.query_at(w, r["t"]), w.dtype)[0, 2 * w.group:3 * w.group]
+        T = r["T"]
+        new_block = (T - 1) % w.block_size == 0
+        opened += new_block
+        dense = oracle.dense_attention(q, keys, vals, w.dtype, T - 1 if new_block else T)
+        assert np.max(np.abs(r["out"] - dense)) < 1e-12
+    assert opened >= 1   # the prompt ends 2 tokens before a block boundary
+
+
+def test_lookahead_query_drift_and_drafts_follow_the_next_query():
+    """The lookahead workload's queries drift between steps and its drafts are
+    centred on the next step's query (so they predict it better than the
+    previous query does)."""
+    w = synth.QWEN3_8B_AHEAD.with_(batch=2)
+    f = lambda a: synth.decode_f32(a, w.dtype).astype(np.float64)
+    q = [f(synth.query_at(w, t)) for t in range(4)]
+    d1 = f(synth.drafts(w, 1))
+    assert np.array_equal(q[0], f(synth.queries(w)))
+    assert 0.15 < np.std(q[2] - q[1]) < 0.3
+    assert np.std(d1 - q[2][None]) < 0.5 * np.std(q[1] - q[2])
+    # non-lookahead workloads keep a fixed query
+    w0 = synth.QWEN3_8B.with_(batch=2)
+    assert np.array_equal(synth.query_at(w0, 5), synth.queries(w0))
