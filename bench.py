@@ -170,6 +170,9 @@ def main():
                     help="override the workload's fetch ratio ('all' = cap K)")
     ap.add_argument("--layers", type=int, default=None,
                     help="override the workload's layer count (1 = the single-layer path)")
+    ap.add_argument("--correct-cap", type=int, default=0,
+                    help="lookahead workloads: decode-time miss correction with this cap per "
+                         "(b, KV head) and step (0: attention over the prefetched set)")
     ap.add_argument("--sweep", action="store_true",
                     help="multi-layer workloads: one line per fetch ratio of the sweep")
     args = ap.parse_args()
@@ -213,8 +216,11 @@ def main():
     rec = None
     if w.lookahead:
         # [OASIS] Fig. 8 ordering; the warmup steps also measure prediction recall
-        rec = warmup_ahead_with_recall(run, args.warmup, stream)
-        step = run.step_ahead
+        rec = warmup_ahead_with_recall(run, args.warmup, stream, args.correct_cap)
+        if args.correct_cap > 0:
+            step = lambda t, st: run.step_corrected(t, args.correct_cap, st)
+        else:
+            step = run.step_ahead
     else:
         if w.admission:
             run.admission(stream)
@@ -333,6 +339,7 @@ def main():
     }
     if rec is not None:
         line["ordering"] = "lookahead"
+        line["config"]["correct_cap"] = args.correct_cap
         line["recall"] = rec
     if not args.no_cpu_baseline:
         print("# cpu baseline (oracle) ...", file=sys.stderr, flush=True)
@@ -340,7 +347,7 @@ def main():
     print(json.dumps(line), flush=True)
 
 
-def warmup_ahead_with_recall(run, warmup, stream):
+def warmup_ahead_with_recall(run, warmup, stream, cap_correct=0):
     """Admission and `warmup` lookahead steps of a LayerRunner; each step also
     scores the step's own query to get the exact top-K (untimed), giving the
     recall of the drafts' prediction (made one step earlier) and of the
@@ -355,6 +362,7 @@ def warmup_ahead_with_recall(run, warmup, stream):
     run.admission_ahead(stream)
     torch.cuda.synchronize()
     r_ahead, r_prev, prev = [], [], None
+    miss, left = [], []
     for t in range(1, warmup + 1):
         pred = predicted_ids(h)
         h.oasis_append_kv(run.app_k[t - 1], run.app_v[t - 1], stream=stream)
@@ -363,13 +371,24 @@ def warmup_ahead_with_recall(run, warmup, stream):
         if prev is not None:
             r_prev.append(recall(prev, ex))
         prev = ex
+        if cap_correct > 0:
+            # the exact ids are the selection now: correct with them
+            h.oasis_select_and_fetch(cap_correct, stream=stream)
+            c = h.read("COUNTS").reshape(-1, 4)
+            miss.append(float(c[:, 3].mean()) / w.k_blocks)
+            left.append(float(np.maximum(c[:, 3] - cap_correct, 0).mean()) / w.k_blocks)
         h.oasis_sparse_attn(run.q_steps[t], run.out, stream=stream)
         h.oasis_predict(None, run.drafts[t], w.drafts, stream=stream)
         h.oasis_select_and_fetch(run.cap, stream=stream)
-    return {"drafts": float(np.mean(r_ahead)) if r_ahead else None,
-            "previous_query": float(np.mean(r_prev)) if r_prev else None,
-            "steps": warmup, "what": "mean over units and steps of |predicted top-K ∩ exact "
-                                     "top-K of the step's own query| / K"}
+    out = {"drafts": float(np.mean(r_ahead)) if r_ahead else None,
+           "previous_query": float(np.mean(r_prev)) if r_prev else None,
+           "steps": warmup, "what": "mean over units and steps of |predicted top-K ∩ exact "
+                                    "top-K of the step's own query| / K"}
+    if cap_correct > 0:
+        out["decode_time_miss_rate"] = float(np.mean(miss)) if miss else None
+        out["left_after_correction"] = float(np.mean(left)) if left else None
+        out["correct_cap"] = cap_correct
+    return out
 
 
 def bench_model(args, w):
@@ -420,7 +439,7 @@ def bench_model(args, w):
                 xf = xfer if sched == "overlap" else stream
                 mr.admission_ahead(stream, sd2, xf)
                 mstep = (lambda t, sd2=sd2, xf=xf:
-                         mr.step_ahead(t, stream, sd2, xf, cap))
+                         mr.step_ahead(t, stream, sd2, xf, cap, args.correct_cap))
             else:
                 mr.admission(stream, sd)
                 mstep = lambda t, sd=sd: mr.step(t, stream, sd, cap)
@@ -487,6 +506,7 @@ def bench_model(args, w):
                        "fetch_ratio": "all" if ratio is None else ratio,
                        "cap_per_kv_head": cap, "schedule": main_sched,
                        "ordering": "lookahead" if w.lookahead else "within step",
+                       "correct_cap": args.correct_cap if w.lookahead else None,
                        "host_kv_buffers": mr.H},
             "model_steps_per_s": K / dt,
             "roofline": roof,

@@ -214,12 +214,19 @@ int oasis_decode_layers(oasis_t *const *layers, const oasis_layer_io *io, int32_
  * not: `stream` does not wait for `side` or `xfer`, so transfers run under
  * the attention of the following layers.  Synchronize all three streams (or
  * the device) before reusing the call's inputs.  Call it with every q = NULL
- * and cap = K for the admission step (predict and fetch only).  The handles
- * must be distinct; on error no further call is issued and
+ * and cap = K for the admission step (predict and fetch only).
+ * cap_correct > 0 adds decode-time miss correction (the corrective transfers
+ * the OasisKV page lists among its limits): before attending, each layer
+ * scores its current query alone, selects that top-K with cap_correct (the
+ * blocks the earlier prediction missed are fetched synchronously, on
+ * `stream`), and attends over it; the drafts' prefetch for the next step
+ * follows as above.  cap_correct = 0: attention over the prefetched set.
+ * The handles must be distinct; on error no further call is issued and
  * oasis_last_error(layers[0]) names the failing layer. */
 int oasis_decode_layers_ahead(oasis_t *const *layers, const oasis_layer_io *io,
                               int32_t n_layers, int32_t n_drafts, int32_t cap,
-                              hipStream_t stream, hipStream_t side, hipStream_t xfer);
+                              int32_t cap_correct, hipStream_t stream, hipStream_t side,
+                              hipStream_t xfer);
 
 /* ---------------------------------------------------------------- inspection */
 

@@ -91,7 +91,7 @@ def lib():
                                                    vp, vp]),
             "oasis_decode_layers_ahead": (ctypes.c_int, [ctypes.POINTER(ctypes.c_void_p),
                                                          ctypes.POINTER(oasis_layer_io), i32, i32,
-                                                         i32, vp, vp, vp]),
+                                                         i32, i32, vp, vp, vp]),
             "oasis_destroy": (ctypes.c_int, [H]),
             "oasis_load_prefix": (ctypes.c_int, [H, vp, vp, i64]),
             "oasis_set_state": (ctypes.c_int, [H, vp, vp]),
@@ -312,9 +312,11 @@ class LayerStep:
         if rc != OASIS_OK:
             self.layers[0]._check(rc, "oasis_decode_layers")
 
-    def run_ahead(self, n_drafts, cap, stream, side, xfer):
-        """oasis_decode_layers_ahead: the lookahead ordering on three streams."""
+    def run_ahead(self, n_drafts, cap, stream, side, xfer, cap_correct=0):
+        """oasis_decode_layers_ahead: the lookahead ordering on three streams
+        (cap_correct > 0: with decode-time miss correction)."""
         rc = lib().oasis_decode_layers_ahead(self._h, self._io, len(self.layers), n_drafts, cap,
-                                             _stream(stream), _stream(side), _stream(xfer))
+                                             cap_correct, _stream(stream), _stream(side),
+                                             _stream(xfer))
         if rc != OASIS_OK:
             self.layers[0]._check(rc, "oasis_decode_layers_ahead")

@@ -627,6 +627,7 @@ extern "C" int oasis_predict(oasis_t *h, const void *q_dev, const void *drafts_d
     if (NB == 0) return fail(h, OASIS_E_STATE, "predict: no tokens loaded");
     const Dims &D = h->D;
     TRY(after(h, stream, h->m_append));
+    TRY(after(h, stream, h->m_select));  // the previous select reads the scores
     LAUNCH(h, TM_SCORE, stream,
            launch_score(D, h->summ, q_dev, drafts_dev, n_drafts, NB, h->scores,
                         stream));
@@ -829,8 +830,8 @@ extern "C" int oasis_decode_layers(oasis_t *const *layers, const oasis_layer_io 
 // attention, so each transfer has the rest of the step to land.
 extern "C" int oasis_decode_layers_ahead(oasis_t *const *layers, const oasis_layer_io *io,
                                          int32_t n_layers, int32_t n_drafts, int32_t cap,
-                                         hipStream_t stream, hipStream_t side,
-                                         hipStream_t xfer) {
+                                         int32_t cap_correct, hipStream_t stream,
+                                         hipStream_t side, hipStream_t xfer) {
     if (!layers || !io || n_layers < 1) return OASIS_E_INVAL;
     if (n_drafts < 1) return fail(layers[0], OASIS_E_INVAL, "decode_layers_ahead: no drafts");
     for (int32_t l = 0; l < n_layers; ++l) {
@@ -854,8 +855,14 @@ extern "C" int oasis_decode_layers_ahead(oasis_t *const *layers, const oasis_lay
     for (int32_t l = 0; l < n_layers && rc == OASIS_OK; ++l) {
         oasis_t *h = layers[l];
         if (io[l].k_new) rc = oasis_append_kv(h, io[l].k_new, io[l].v_new, stream);
-        if (rc == OASIS_OK && h->selected && io[l].q && io[l].out)
-            rc = oasis_sparse_attn(h, io[l].q, io[l].out, stream);
+        const bool attend = h->selected && io[l].q && io[l].out;
+        if (rc == OASIS_OK && attend && cap_correct > 0) {
+            // decode-time miss correction: the current query's own top-K, its
+            // missing blocks fetched now (inside the attention when fused)
+            rc = oasis_predict(h, io[l].q, nullptr, 0, nullptr, nullptr, stream);
+            if (rc == OASIS_OK) rc = select_impl(h, cap_correct, stream, !h->fused, stream);
+        }
+        if (rc == OASIS_OK && attend) rc = oasis_sparse_attn(h, io[l].q, io[l].out, stream);
         if (rc == OASIS_OK)
             rc = oasis_predict(h, nullptr, io[l].drafts, n_drafts, nullptr, nullptr, side);
         if (rc == OASIS_OK) rc = select_impl(h, cap, side, true, xfer);

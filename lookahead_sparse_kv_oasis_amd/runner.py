@@ -96,6 +96,19 @@ class LayerRunner:
         h.oasis_select_and_fetch(self.cap if cap is None else cap, stream=stream)
         self.t = t
 
+    def step_corrected(self, t: int, cap_correct: int, stream=None, cap: int | None = None):
+        """Lookahead step with decode-time miss correction: append; the step-t
+        query's own top-K selected with cap_correct (missed blocks fetched
+        now); attention over it; then the drafts prefetch step t+1's set."""
+        h = self.h
+        h.oasis_append_kv(self.app_k[t - 1], self.app_v[t - 1], stream=stream)
+        h.oasis_predict(self.q_steps[t], None, 0, stream=stream)
+        h.oasis_select_and_fetch(cap_correct, stream=stream)
+        h.oasis_sparse_attn(self.q_steps[t], self.out, stream=stream)
+        h.oasis_predict(None, self.drafts[t], self.w.drafts, stream=stream)
+        h.oasis_select_and_fetch(self.cap if cap is None else cap, stream=stream)
+        self.t = t
+
 
 def _cap_from_ratio(ratio, k):
     from . import cap_from_ratio
@@ -203,13 +216,15 @@ class ModelRunner:
             a.set(l, None, None, None, self.drafts[0][l], None)
         a.run_ahead(self.w.drafts, self.w.k_blocks, stream, side, xfer)
 
-    def step_ahead(self, t: int, stream, side, xfer, cap: int | None = None):
+    def step_ahead(self, t: int, stream, side, xfer, cap: int | None = None,
+                   cap_correct: int = 0):
         a = self.step_args
         for l in range(self.n_layers):
             g = self.group_of(l)
             a.set(l, self.app_k[g][t - 1], self.app_v[g][t - 1], self.q_steps[g][t],
                   self.drafts[t][l], self.out[l])
-        a.run_ahead(self.w.drafts, self.cap if cap is None else cap, stream, side, xfer)
+        a.run_ahead(self.w.drafts, self.cap if cap is None else cap, stream, side, xfer,
+                    cap_correct)
         self.t = t
 
     def close(self):

@@ -279,6 +279,33 @@ class Unit:
         return rec
 
 
+    def step_corrected(self, t, q_rows, cap_correct, x_draft_rows, cap, append=True):
+        """One decode step with decode-time miss correction (the corrective
+        transfers the OasisKV page names among its limits) on top of the
+        lookahead prefetch: token t is appended; the current query alone is
+        scored and its top-K selected with cap_correct (the blocks the earlier
+        prediction missed are fetched now, synchronously); the current query
+        attends over that set; then the drafts alone select (cap) the set to
+        prefetch for step t+1.  Both selects use recency t."""
+        if append:
+            self.append()
+        e64 = self.score(q_rows)
+        e32 = e64.astype(np.float32)
+        exact = topk(e32, self.K)
+        corr = select(self.slot_block, self.last_used, exact, cap_correct, t)
+        out = attention(q_rows, self.keys, self.vals, self.dtype, self.bs, self.T,
+                        corr["att_block"])
+        s64 = self.score(x_draft_rows)
+        s32 = s64.astype(np.float32)
+        ids = topk(s32, self.K)
+        pre = select(self.slot_block, self.last_used, ids, cap, t)
+        self.att = pre["att_block"]
+        return dict(t=t, T=self.T, exact_scores64=e64, exact_scores32=e32, exact_ids=exact,
+                    correction=corr, out=out, scores64=s64, scores32=s32, ids=ids,
+                    prefetch=pre, slot_block=self.slot_block.copy(),
+                    last_used=self.last_used.copy())
+
+
 def unit_rows(q, drafts_t, b, h, group):
     """Query rows of one unit: the G group heads of the current query, then of
     every draft (scoring), and the current query alone (attention)."""

@@ -78,3 +78,23 @@ def run_unit_ahead(w: synth.Workload, b: int, h: int, n_steps: int, layer: int =
         x = draft_rows(to_f64(synth.drafts(w, t, layer), w.dtype), b, h, w.group)
         recs.append(unit.step_ahead(t, x, cur, cap))
     return recs
+
+
+def run_unit_corrected(w: synth.Workload, b: int, h: int, n_steps: int, cap_correct: int,
+                       layer: int = 0, cap=None, kv=None, unit: Unit | None = None):
+    """Lookahead prefetch plus decode-time miss correction for one unit: the
+    admission step prefetches (cap = K) from the step-0 drafts; each step
+    then corrects with the current query's exact top-K (cap_correct) before
+    attending, and prefetches the next step's set from its drafts (cap)."""
+    if unit is None:
+        unit = initial_unit(w, b, h, n_steps, layer, kv)
+    cap = workload_cap(w) if cap is None else cap
+    recs = []
+    x = draft_rows(to_f64(synth.drafts(w, 0, layer), w.dtype), b, h, w.group)
+    recs.append(unit.step_ahead(0, x, None, w.k_blocks, append=False, attend=False))
+    for t in range(1, n_steps + 1):
+        q = to_f64(synth.query_at(w, t, layer), w.dtype)
+        cur = q[b, h * w.group:(h + 1) * w.group]
+        x = draft_rows(to_f64(synth.drafts(w, t, layer), w.dtype), b, h, w.group)
+        recs.append(unit.step_corrected(t, cur, cap_correct, x, cap))
+    return recs

@@ -486,3 +486,93 @@ def pipeline_unit_kv(mr, layer, units):
     n_tok = w.prefix_tokens + mr.n_steps
     u = synth.heavy_direction(w, g)
     return {k: synth.unit_kv(w, k[0], k[1], n_tok, g, u[k[0], k[1]]) for k in units}
+
+
+class CorrectedRunning(AheadRunning):
+    """Lookahead prefetch plus decode-time miss correction on one layer, run
+    phase by phase: each step's correction (the step query's own top-K,
+    cap_correct), its attention, and the drafts' prefetch are each checked
+    against the oracle on the GPU's own scores and previous tables."""
+
+    def _phase(self, t, prev, rows_of, cap, report, name):
+        w, h = self.w, self.run.h
+        K = h.k_blocks
+        gpu_scores = h.read("SCORES", np.float32).reshape(w.batch, w.kv_heads, self.NBmax)
+        ids = h.read("IDS")
+        fb, fs = h.read("FETCH_BLOCK"), h.read("FETCH_SLOT")
+        ab, ast = h.read("ATT_BLOCK"), h.read("ATT_SLOT")
+        cnt = h.read("COUNTS")
+        now = self._tables()
+        att, misses = {}, 0
+        for (b, hh) in self.units:
+            tag = f"{name} step {t} unit {(b, hh)}"
+            unit = self.oru[(b, hh)]
+            x = rows_of(b, hh)
+            nb = unit.nb
+            ref = unit.score(x)
+            err = np.abs(gpu_scores[b, hh, :nb].astype(np.float64) - ref) / score_scale(unit, x)
+            report["score_err"] = max(report["score_err"], float(err.max()))
+            assert err.max() <= SCORE_TOL, tag + f" score err {err.max():.3g}"
+            exp_ids = oracle.topk(gpu_scores[b, hh, :nb], K)
+            assert np.array_equal(self._unit_slice(ids, b, hh, K), exp_ids), tag + " ids"
+            sb_exp, lu_exp = prev[(b, hh)][0].copy(), prev[(b, hh)][1].copy()
+            r = oracle.select(sb_exp, lu_exp, exp_ids, cap, t)
+            c = self._unit_slice(cnt, b, hh, 4)
+            na, nh, nf, nm = int(c[0]), int(c[1]), int(c[2]), int(c[3])
+            n_sel = int((exp_ids >= 0).sum())
+            assert (na, nh, nf, nm) == (len(r["att_block"]), r["n_hit"], len(r["fetch_block"]),
+                                        n_sel - r["n_hit"]), tag
+            assert np.array_equal(self._unit_slice(fb, b, hh, K)[:nf], r["fetch_block"]), tag
+            assert np.array_equal(self._unit_slice(fs, b, hh, K)[:nf], r["fetch_slot"]), tag
+            assert np.array_equal(self._unit_slice(ab, b, hh, K)[:na], r["att_block"]), tag
+            assert np.array_equal(self._unit_slice(ast, b, hh, K)[:na], r["att_slot"]), tag
+            assert np.array_equal(now[(b, hh)][0], sb_exp), tag + " slot_block"
+            assert np.array_equal(now[(b, hh)][1], lu_exp), tag + " last_used"
+            att[(b, hh)] = r["att_block"].copy()
+            misses += nm
+        report[name + "_misses"] = report.get(name + "_misses", 0) + misses
+        return now, att
+
+    def run_corrected(self, cap_correct, steps=None, check_payload_every=4):
+        w, run, h = self.w, self.run, self.run.h
+        steps = self.n_steps if steps is None else steps
+        report = dict(score_err=0.0, attn_err=0.0, steps=0, fetched=0)
+        empty = {k: (np.full(h.slots, -1, np.int32), np.full(h.slots, -1, np.int32))
+                 for k in self.units}
+        for k in self.units:
+            self.oru[k].slot_block[:] = -1
+        run.admission_ahead()
+        torch.cuda.synchronize()
+        prev, _ = self.verify_ahead(0, empty, None, report, w.k_blocks)
+        for t in range(1, steps + 1):
+            q = oracle.to_f64(synth.query_at(w, t, self.layer), w.dtype)
+            cur = {k: q[k[0], k[1] * self.G:(k[1] + 1) * self.G] for k in self.units}
+            h.oasis_append_kv(run.app_k[t - 1], run.app_v[t - 1])
+            for k in self.units:
+                self.oru[k].append()
+            h.oasis_predict(run.q_steps[t], None, 0)
+            h.oasis_select_and_fetch(cap_correct)
+            torch.cuda.synchronize()
+            prev, att = self._phase(t, prev, lambda b, hh: cur[(b, hh)], cap_correct, report,
+                                    "correction")
+            h.oasis_sparse_attn(run.q_steps[t], run.out)
+            torch.cuda.synchronize()
+            out = run.out.cpu().numpy()
+            for (b, hh) in self.units:
+                unit = self.oru[(b, hh)]
+                exp = oracle.attention(cur[(b, hh)], unit.keys, unit.vals, w.dtype, w.block_size,
+                                       unit.T, att[(b, hh)])
+                g0 = hh * self.G
+                e = float(np.max(np.abs(out[b, g0:g0 + self.G].astype(np.float64) - exp)))
+                report["attn_err"] = max(report["attn_err"], e)
+                assert e <= ATTN_TOL, f"corrected step {t} unit {(b, hh)} attention err {e:.3g}"
+            h.oasis_predict(None, run.drafts[t], w.drafts)
+            h.oasis_select_and_fetch(self.cap)
+            torch.cuda.synchronize()
+            h.oasis_check()
+            prev, _ = self._phase(t, prev, lambda b, hh: self._draft_rows(t, b, hh), self.cap,
+                                  report, "prefetch")
+            if t % check_payload_every == 0 or t == steps:
+                self.check_payload(t)
+            report["steps"] = t
+        return report

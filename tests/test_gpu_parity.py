@@ -165,3 +165,15 @@ def test_lookahead_recall_measurement():
     a, p = float(np.mean(r_ahead)), float(np.mean(r_prev))
     log(f"recall of the exact next top-K: drafts {a:.3f}, previous query {p:.3f}")
     assert 0.0 < a <= 1.0 and 0.0 < p <= 1.0
+
+
+# ------------------------------------------------------------------ decode-time miss correction
+
+def test_miss_correction_reduced_context():
+    """Lookahead prefetch plus decode-time miss correction, phase by phase
+    against the oracle (cap_correct = 3 and the unbounded correction)."""
+    from tests.gpu_parity import CorrectedRunning, log
+    w = synth.QWEN3_8B_AHEAD.with_(batch=2, prefix_tokens=16 * 300 + 7, budget_tokens=16 * 64)
+    for cc in (3, w.k_blocks):
+        p = CorrectedRunning(w, 8, [(0, 0), (1, 7), (0, 4)])
+        log(f"correction cap {cc}: {p.run_corrected(cc)}")

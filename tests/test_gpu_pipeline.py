@@ -180,3 +180,30 @@ def test_lookahead_executor_against_oracle_and_one_stream():
     _log(f"lookahead executor: {reps}")
     a.close()
     b.close()
+
+
+def test_lookahead_executor_with_miss_correction_matches_one_stream():
+    """oasis_decode_layers_ahead with cap_correct: three streams bit-identical to
+    one, and every layer's output equal to the single-layer corrected calls."""
+    from lookahead_sparse_kv_oasis_amd.runner import LayerRunner
+    w = AHEAD_SMALL.with_(layers=3)
+    a = _runner(w, w.steps)
+    b = _runner(w, w.steps)
+    single = LayerRunner(w.with_(layers=1), w.steps, layer=0)
+    cur = torch.cuda.current_stream()
+    side, xfer = torch.cuda.Stream(), torch.cuda.Stream()
+    a.admission_ahead(cur, side, xfer)
+    b.admission_ahead(cur, cur, cur)
+    single.admission_ahead()
+    for t in range(1, w.steps + 1):
+        a.step_ahead(t, cur, side, xfer, cap_correct=4)
+        b.step_ahead(t, cur, cur, cur, cap_correct=4)
+        single.step_corrected(t, 4)
+        torch.cuda.synchronize()
+        assert torch.equal(a.out, b.out), f"step {t}: outputs differ"
+        assert torch.equal(a.out[0], single.out), f"step {t}: layer 0 differs from one layer"
+    for l in range(w.layers):
+        for buf in STATE_BUFS:
+            assert np.array_equal(a.handles[l].read(buf), b.handles[l].read(buf)), f"{l} {buf}"
+    a.close()
+    b.close()

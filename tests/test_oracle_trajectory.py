@@ -147,3 +147,39 @@ def test_lookahead_query_drift_and_drafts_follow_the_next_query():
     # non-lookahead workloads keep a fixed query
     w0 = synth.QWEN3_8B.with_(batch=2)
     assert np.array_equal(synth.query_at(w0, 5), synth.queries(w0))
+
+
+# ------------------------------------------------------------------ decode-time miss correction
+
+def test_correction_with_whole_context_budget_is_dense_attention():
+    """Budget covering every block and an unbounded correction: the corrected
+    set is every block, so the output is dense attention over all T tokens
+    (the newest block included, unlike the plain lookahead order)."""
+    from oracle.trajectory import run_unit_corrected
+    w = _ahead_small(cap=2)
+    n = 6
+    recs = run_unit_corrected(w, 0, 1, n, cap_correct=16, cap=2)
+    keys, vals = synth.unit_kv(w, 0, 1, w.prefix_tokens + n)
+    for r in recs[1:]:
+        q = oracle.to_f64(synth.query_at(w, r["t"]), w.dtype)[0, w.group:2 * w.group]
+        dense = oracle.dense_attention(q, keys, vals, w.dtype, r["T"])
+        assert np.max(np.abs(r["out"] - dense)) < 1e-12
+        assert len(r["correction"]["att_block"]) == (r["T"] + 15) // 16
+
+
+def test_correction_fetches_at_most_its_cap_and_attends_the_exact_hits():
+    """The corrective select fetches at most cap_correct of the exact top-K's
+    missing blocks; attention covers exactly the exact top-K blocks held after
+    it; the prefetch that follows fetches at most the prefetch cap."""
+    from oracle.trajectory import run_unit_corrected
+    w = synth.QWEN3_8B_AHEAD.with_(batch=1, prefix_tokens=16 * 300 + 5, budget_tokens=16 * 32)
+    recs = run_unit_corrected(w, 0, 6, 10, cap_correct=3, cap=2)
+    for r in recs[1:]:
+        c, p = r["correction"], r["prefetch"]
+        assert len(c["fetch_block"]) <= 3 and len(p["fetch_block"]) <= 2
+        exact = [int(i) for i in r["exact_ids"] if i >= 0]
+        assert c["n_hit"] + len(c["fetch_block"]) == len(c["att_block"])
+        assert set(int(b) for b in c["att_block"]) <= set(exact)
+        # a miss beyond the correction cap is the only reason to skip an exact block
+        n_miss = len(exact) - c["n_hit"]
+        assert len(exact) - len(c["att_block"]) == max(0, n_miss - 3)
