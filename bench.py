@@ -247,6 +247,9 @@ def main():
     tm = h.oasis_get_timing()
     stats1 = h.oasis_get_stats()
     h.oasis_check()
+    verify = None
+    if run.h.layout.dtype == 1 and w.head_dim == 128 and w.block_size == 16 and not w.lookahead:
+        verify = time_verify(run, w)
     K = args.steps
     e = w.elem_bytes
     units = w.batch * w.kv_heads
@@ -337,6 +340,10 @@ def main():
                            "period": args.timing_period},
         "attended_blocks_per_step": attended,
     }
+    if verify is not None:
+        verify["attended_blocks"] = attended
+        verify["hbm_gbps"] = (verify["passes"] * attended * blk_bytes) / (verify["avg_ms"] * 1e-3) / 1e9
+        line["verify_attention"] = verify
     if rec is not None:
         line["ordering"] = "lookahead"
         line["config"]["correct_cap"] = args.correct_cap
@@ -345,6 +352,44 @@ def main():
         print("# cpu baseline (oracle) ...", file=sys.stderr, flush=True)
         line["cpu_baseline"] = cpu_baseline(w)
     print(json.dumps(line), flush=True)
+
+
+def time_verify(run, w, calls=20):
+    """Attention over the normal and draft query sets together (after the timed
+    region; synthetic draft-token K/V): average call time with events on the
+    caller's stream, and the number of passes over the attended KV."""
+    import numpy as np
+    import torch
+
+    import synth
+    from lookahead_sparse_kv_oasis_amd.runner import to_device
+
+    D = w.drafts
+    rng = np.random.default_rng(11)
+    shape = (D, w.batch, w.kv_heads, w.head_dim)
+    kd = to_device(synth.encode(rng.standard_normal(shape).astype(np.float32), w.dtype))
+    vd = to_device(synth.encode(rng.standard_normal(shape).astype(np.float32), w.dtype))
+    out = torch.empty((1 + D, w.batch, w.q_heads, w.head_dim), dtype=torch.float32,
+                      device="cuda")
+    t = run.t
+    run.h.oasis_sparse_attn_verify(run.q, run.drafts[t], D, kd, vd, out)
+    torch.cuda.synchronize()
+    a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    a.record()
+    for _ in range(calls):
+        run.h.oasis_sparse_attn_verify(run.q, run.drafts[t], D, kd, vd, out)
+    b.record()
+    torch.cuda.synchronize()
+    rows = w.group * (1 + D)
+    passes, r = 0, rows
+    while r > 0:
+        g = 16
+        while g > r:
+            g //= 2
+        r -= g
+        passes += 1
+    return {"avg_ms": a.elapsed_time(b) / calls, "query_sets": 1 + D, "rows_per_kv_head": rows,
+            "passes": passes, "calls": calls}
 
 
 def warmup_ahead_with_recall(run, warmup, stream, cap_correct=0):

@@ -176,6 +176,21 @@ int oasis_evict(oasis_t *h, const int32_t *blocks_host, const int32_t *counts_ho
  * the valid tokens of those blocks; 0 when none is attended. */
 int oasis_sparse_attn(oasis_t *h, const void *q_dev, float *out_dev, hipStream_t stream);
 
+/* Attention over the normal and draft queries together (OasisKV page, Fig. 7
+ * right: the attention kernel runs the normal and draft queries over the
+ * sparse KV), as speculative decoding verifies drafts.  q_dev [B][Hq][d] is
+ * the current query (position T-1); drafts_dev [n_drafts][B][Hq][d] the draft
+ * queries, draft j at position T-1+j; k_drafts_dev / v_drafts_dev
+ * [n_drafts][B][Hkv][d] the draft tokens' keys and values (not appended to
+ * the cache).  out_dev [1+n_drafts][B][Hq][d] fp32: set 0 = oasis_sparse_attn
+ * of q; set j attends over the attended blocks of the last select (tokens
+ * < T) and draft tokens 1..j (causal).  Fetches pending from the last select
+ * are copied first.  bf16 layouts with d = 128 and block_size 16 only
+ * (OASIS_E_INVAL otherwise); allocates its scratch on first use. */
+int oasis_sparse_attn_verify(oasis_t *h, const void *q_dev, const void *drafts_dev,
+                             int32_t n_drafts, const void *k_drafts_dev,
+                             const void *v_drafts_dev, float *out_dev, hipStream_t stream);
+
 /* ---------------------------------------------------------------- layer pipeline */
 
 typedef struct {

@@ -30,7 +30,7 @@ EXPORTS = [
     "oasis_create", "oasis_create_shared", "oasis_destroy", "oasis_load_prefix",
     "oasis_set_state", "oasis_decode_layers", "oasis_decode_layers_ahead",
     "oasis_append_kv", "oasis_predict", "oasis_topk_from_scores", "oasis_select_and_fetch",
-    "oasis_evict", "oasis_sparse_attn", "oasis_buffer_bytes", "oasis_read", "oasis_get_stats",
+    "oasis_evict", "oasis_sparse_attn", "oasis_sparse_attn_verify", "oasis_buffer_bytes", "oasis_read", "oasis_get_stats",
     "oasis_check", "oasis_set_timing", "oasis_set_timing_period", "oasis_get_timing", "oasis_get_dims", "oasis_tokens",
     "oasis_copy_stream", "oasis_kv_bytes_per_token", "oasis_cap_from_ratio", "oasis_strerror",
     "oasis_last_error",
@@ -101,6 +101,7 @@ def lib():
             "oasis_select_and_fetch": (ctypes.c_int, [H, i32, vp]),
             "oasis_evict": (ctypes.c_int, [H, vp, vp, i32, vp]),
             "oasis_sparse_attn": (ctypes.c_int, [H, vp, vp, vp]),
+            "oasis_sparse_attn_verify": (ctypes.c_int, [H, vp, vp, i32, vp, vp, vp, vp]),
             "oasis_buffer_bytes": (i64, [H, i32]),
             "oasis_read": (ctypes.c_int, [H, i32, i64, i64, vp]),
             "oasis_get_stats": (ctypes.c_int, [H, ctypes.POINTER(oasis_stats)]),
@@ -241,6 +242,13 @@ class Oasis:
     def oasis_sparse_attn(self, q, out, stream=None):
         self._check(lib().oasis_sparse_attn(self.h, _ptr(q), _ptr(out), _stream(stream)),
                     "oasis_sparse_attn")
+
+    def oasis_sparse_attn_verify(self, q, drafts, n_drafts, k_drafts, v_drafts, out,
+                                 stream=None):
+        self._check(lib().oasis_sparse_attn_verify(self.h, _ptr(q), _ptr(drafts), n_drafts,
+                                                   _ptr(k_drafts), _ptr(v_drafts), _ptr(out),
+                                                   _stream(stream)),
+                    "oasis_sparse_attn_verify")
 
     def oasis_check(self):
         self._check(lib().oasis_check(self.h), "oasis_check")

@@ -106,6 +106,9 @@ struct oasis_handle {
     DevStats *stats = nullptr;
     int32_t *evict_buf = nullptr;
     size_t evict_cap = 0;
+    // verification attention: packed query rows and per-row partials
+    void *vq = nullptr;
+    float *vpart_m = nullptr, *vpart_l = nullptr, *vpart_acc = nullptr;
 
     hipStream_t copy = nullptr;
     Mark m_append, m_select, m_gather, m_attn;
@@ -254,6 +257,10 @@ void free_all(oasis_t *h) {
     (void)hipFree(h->err);
     (void)hipFree(h->stats);
     (void)hipFree(h->evict_buf);
+    (void)hipFree(h->vq);
+    (void)hipFree(h->vpart_m);
+    (void)hipFree(h->vpart_l);
+    (void)hipFree(h->vpart_acc);
     h->hkv.reset();
     if (h->copy) (void)hipStreamDestroy(h->copy);
     for (hipEvent_t e : {h->m_append.ev, h->m_select.ev, h->m_gather.ev, h->m_attn.ev, h->ev_fork,
@@ -760,6 +767,43 @@ extern "C" int oasis_sparse_attn(oasis_t *h, const void *q_dev, float *out_dev,
                             stream));
     LAUNCH(h, TM_COMBINE, stream,
            launch_combine(D, h->plan, nsf, h->part_m, h->part_l, h->part_acc, out_dev, stream));
+    TRY(mark(h, h->m_attn, stream));
+    return OASIS_OK;
+}
+
+extern "C" int oasis_sparse_attn_verify(oasis_t *h, const void *q_dev, const void *drafts_dev,
+                                        int32_t n_drafts, const void *k_drafts_dev,
+                                        const void *v_drafts_dev, float *out_dev,
+                                        hipStream_t stream) {
+    if (!h) return OASIS_E_INVAL;
+    if (!q_dev || !out_dev || !aligned16(q_dev) || !aligned16(out_dev))
+        return fail(h, OASIS_E_INVAL, "verify: null or misaligned q / out");
+    if (n_drafts < 0 || n_drafts > h->L.max_drafts)
+        return fail(h, OASIS_E_INVAL, "verify: n_drafts %d outside [0, %d]", n_drafts,
+                    h->L.max_drafts);
+    if (n_drafts > 0 && (!drafts_dev || !k_drafts_dev || !v_drafts_dev || !aligned16(drafts_dev)))
+        return fail(h, OASIS_E_INVAL, "verify: null drafts or draft K/V");
+    if (!h->plan.mfma)
+        return fail(h, OASIS_E_INVAL, "verify: needs the bf16, d = 128, block 16 layout");
+    if (!h->selected) return fail(h, OASIS_E_STATE, "verify attention before select");
+    const Dims &D = h->D;
+    if (!h->vq) {  // sized for max_drafts on first use
+        const int M = verify_rows(D, h->L.max_drafts);
+        const size_t rows = (size_t)D.units() * M;
+        if (hipMalloc(&h->vq, rows * 128 * sizeof(uint16_t)) != hipSuccess ||
+            hipMalloc((void **)&h->vpart_m, rows * h->plan.ns1 * sizeof(float)) != hipSuccess ||
+            hipMalloc((void **)&h->vpart_l, rows * h->plan.ns1 * sizeof(float)) != hipSuccess ||
+            hipMalloc((void **)&h->vpart_acc, rows * h->plan.ns1 * 128 * sizeof(float)) !=
+                hipSuccess)
+            return fail(h, OASIS_E_NOMEM, "verify: scratch allocation failed");
+    }
+    TRY(after(h, stream, h->m_select));
+    TRY(after(h, stream, h->m_gather));
+    TRY(flush_fetch(h, stream));  // every attended block resident before the passes
+    // several launches: not a class of the per-kernel timers
+    HIP_OK(h, launch_verify(D, h->plan, n_drafts, q_dev, drafts_dev, k_drafts_dev, v_drafts_dev,
+                            h->slots, h->att_block, h->att_slot, h->counts, h->T, h->vq,
+                            h->vpart_m, h->vpart_l, h->vpart_acc, out_dev, stream));
     TRY(mark(h, h->m_attn, stream));
     return OASIS_OK;
 }

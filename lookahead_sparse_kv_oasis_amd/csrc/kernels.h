@@ -122,6 +122,16 @@ hipError_t launch_attention(const Dims &D, const AttnPlan &P, int mode, int nsf,
                             void *slots, const void *host_kv, const int32_t *att_block,
                             const int32_t *att_slot, const int32_t *counts, int64_t T,
                             float *part_m, float *part_l, float *part_acc, hipStream_t st);
+// Verification attention (normal and draft query sets together, causal over
+// the draft tokens): rows per unit, and the whole pass (pack, one block
+// attention per chunk of rows, combine).  bf16, d = 128, bs = 16.
+int verify_rows(const Dims &D, int n_drafts);
+hipError_t launch_verify(const Dims &D, const AttnPlan &P, int n_drafts, const void *q,
+                         const void *drafts, const void *kd, const void *vd, void *slots,
+                         const int32_t *att_block, const int32_t *att_slot,
+                         const int32_t *counts, int64_t T, void *qpack, float *vpart_m,
+                         float *vpart_l, float *vpart_acc, float *out, hipStream_t st);
+
 hipError_t launch_combine(const Dims &D, const AttnPlan &P, int nsf, const float *part_m,
                           const float *part_l, const float *part_acc, float *out,
                           hipStream_t st);

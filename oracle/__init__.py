@@ -306,6 +306,38 @@ class Unit:
                     last_used=self.last_used.copy())
 
 
+def attention_verify(q_sets, keys, vals, dtype: int, bs: int, T: int, blocks, k_drafts, v_drafts):
+    """Attention over the normal and draft queries together ([OASIS] Fig. 7,
+    right), plain fp64.  q_sets [1 + D][G][d]: set 0 is the current query
+    (position T - 1), set j the j-th draft (position T - 1 + j).  Set j attends
+    over the valid tokens of the attended blocks plus draft tokens 1..j
+    (k_drafts / v_drafts [D][d], exact values): causal within the drafts.
+    Returns [1 + D][G][d]."""
+    keys, vals = _storage(keys, dtype), _storage(vals, dtype)
+    kf = np.asarray(k_drafts, np.float64)
+    vf = np.asarray(v_drafts, np.float64)
+    toks = []
+    for blk in np.asarray(blocks, np.int64):
+        p0 = int(blk) * bs
+        toks.extend(range(p0, min(p0 + bs, T)))
+    toks = np.asarray(toks, np.int64)
+    k_ctx = to_f64(keys[toks], dtype) if len(toks) else np.zeros((0, keys.shape[1]))
+    v_ctx = to_f64(vals[toks], dtype) if len(toks) else np.zeros((0, vals.shape[1]))
+    q_sets = np.asarray(q_sets, np.float64)
+    d = q_sets.shape[-1]
+    out = np.zeros(q_sets.shape, np.float64)
+    for j in range(q_sets.shape[0]):
+        kk = np.concatenate([k_ctx, kf[:j]], axis=0)
+        vv = np.concatenate([v_ctx, vf[:j]], axis=0)
+        if kk.shape[0] == 0:
+            continue
+        lg = q_sets[j] @ kk.T / np.sqrt(d)
+        lg -= lg.max(axis=1, keepdims=True)
+        p = np.exp(lg)
+        out[j] = (p @ vv) / p.sum(axis=1, keepdims=True)
+    return out
+
+
 def unit_rows(q, drafts_t, b, h, group):
     """Query rows of one unit: the G group heads of the current query, then of
     every draft (scoring), and the current query alone (attention)."""

@@ -177,3 +177,52 @@ def test_miss_correction_reduced_context():
     for cc in (3, w.k_blocks):
         p = CorrectedRunning(w, 8, [(0, 0), (1, 7), (0, 4)])
         log(f"correction cap {cc}: {p.run_corrected(cc)}")
+
+
+# ------------------------------------------------------------------ verification attention
+
+@pytest.mark.parametrize("q_heads,n_steps", [(32, 4), (64, 3)])
+def test_verification_attention_against_oracle(q_heads, n_steps):
+    """Normal and draft queries together with causal draft tokens ([OASIS]
+    Fig. 7 right) after each step of the free-running path: every set of
+    sampled units against the oracle over the GPU's attended list; set 0
+    equal to oasis_sparse_attn up to summation order."""
+    from lookahead_sparse_kv_oasis_amd.runner import LayerRunner, to_device
+    from tests.gpu_parity import ATTN_TOL, log
+    w = synth.QWEN3_8B.with_(batch=3, q_heads=q_heads, prefix_tokens=16 * 300 + 9,
+                             budget_tokens=16 * 64)
+    run = LayerRunner(w, n_steps)
+    h = run.h
+    D, B, Hkv, d, G = w.drafts, w.batch, w.kv_heads, w.head_dim, w.group
+    rng = np.random.default_rng(7)
+    out = torch.empty((1 + D, B, w.q_heads, d), dtype=torch.float32, device="cuda")
+    run.admission()
+    worst = 0.0
+    units = [(0, 0), (1, 5), (2, 7)]
+    kv = {k: synth.unit_kv(w, k[0], k[1], w.prefix_tokens + n_steps) for k in units}
+    qf = oracle.to_f64(synth.queries(w), w.dtype)
+    for t in range(1, n_steps + 1):
+        run.step(t)
+        kd = synth.encode(rng.standard_normal((D, B, Hkv, d)).astype(np.float32), w.dtype)
+        vd = synth.encode(rng.standard_normal((D, B, Hkv, d)).astype(np.float32), w.dtype)
+        h.oasis_sparse_attn_verify(run.q, run.drafts[t], D, to_device(kd), to_device(vd), out)
+        torch.cuda.synchronize()
+        got = out.cpu().numpy()
+        # set 0 is the plain attention, summed in other splits (fetched blocks
+        # are read from their slots here, inside the fetch waves there)
+        assert np.max(np.abs(got[0] - run.out.cpu().numpy())) < 1e-5, f"step {t}: set 0"
+        ab, cnt = h.read("ATT_BLOCK"), h.read("COUNTS")
+        dr = oracle.to_f64(synth.drafts(w, t), w.dtype)
+        T = w.prefix_tokens + t
+        for (b, hh) in units:
+            u = b * Hkv + hh
+            att = ab[u * w.k_blocks:u * w.k_blocks + int(cnt[u * 4])]
+            g0 = hh * G
+            sets = np.stack([qf[b, g0:g0 + G]] + [dr[i, b, g0:g0 + G] for i in range(D)])
+            exp = oracle.attention_verify(sets, kv[(b, hh)][0], kv[(b, hh)][1], w.dtype,
+                                          w.block_size, T, att, oracle.to_f64(kd[:, b, hh], w.dtype),
+                                          oracle.to_f64(vd[:, b, hh], w.dtype))
+            e = float(np.max(np.abs(got[:, b, g0:g0 + G].astype(np.float64) - exp)))
+            worst = max(worst, e)
+            assert e <= ATTN_TOL, f"step {t} unit {(b, hh)} verify err {e:.3g}"
+    log(f"verify G={G}: max err {worst:.3g}")

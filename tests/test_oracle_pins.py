@@ -321,3 +321,49 @@ def test_attention_ignores_tokens_past_T():
     a = oracle.attention(q, K1, V1, synth.F32, bs, 6, np.array([0, 1], np.int32))
     b = oracle.attention(q, K2, V2, synth.F32, bs, 6, np.array([0, 1], np.int32))
     assert np.array_equal(a, b)
+
+
+# ------------------------------------------------------------------ verification attention
+
+def _verify_case(seed, dtype=None):
+    rng = np.random.default_rng(seed)
+    d, bs, G, D = 32, 16, 2, 3
+    T = 16 * 5 + 7
+    dt = synth.BF16 if dtype is None else dtype
+    keys = synth.encode(rng.standard_normal((T + 4, d)).astype(np.float32), dt)
+    vals = synth.encode(rng.standard_normal((T + 4, d)).astype(np.float32), dt)
+    kd = synth.encode(rng.standard_normal((D, d)).astype(np.float32), dt)
+    vd = synth.encode(rng.standard_normal((D, d)).astype(np.float32), dt)
+    q = rng.standard_normal((1 + D, G, d))
+    return keys, vals, kd, vd, q, T, bs, dt
+
+
+def test_verify_attention_over_every_block_is_dense_attention_of_the_extended_sequence():
+    """Every block attended: query set j sees the T context tokens and draft
+    tokens 1..j, so each set equals dense attention over the context with the
+    first j draft tokens appended (the independent dense routine)."""
+    keys, vals, kd, vd, q, T, bs, dt = _verify_case(1)
+    nb = (T + bs - 1) // bs
+    out = oracle.attention_verify(q, keys, vals, dt, bs, T, np.arange(nb), oracle.to_f64(kd, dt),
+                                  oracle.to_f64(vd, dt))
+    for j in range(q.shape[0]):
+        ke = np.concatenate([keys[:T], kd[:j]], axis=0)
+        ve = np.concatenate([vals[:T], vd[:j]], axis=0)
+        dense = oracle.dense_attention(q[j], ke, ve, dt, T + j)
+        assert np.max(np.abs(out[j] - dense)) < 1e-12
+
+
+def test_verify_attention_set_zero_is_the_sparse_attention_and_drafts_are_causal():
+    """Set 0 (the current query) ignores the draft tokens: it equals the plain
+    sparse attention; changing draft token j changes only sets >= j."""
+    keys, vals, kd, vd, q, T, bs, dt = _verify_case(2)
+    blocks = np.array([4, 1, 3], np.int32)
+    kf, vf = oracle.to_f64(kd, dt), oracle.to_f64(vd, dt)
+    out = oracle.attention_verify(q, keys, vals, dt, bs, T, blocks, kf, vf)
+    plain = oracle.attention(q[0], keys, vals, dt, bs, T, blocks)
+    assert np.max(np.abs(out[0] - plain)) < 1e-12
+    kf2 = kf.copy()
+    kf2[1] += 1.0                       # draft token 2
+    out2 = oracle.attention_verify(q, keys, vals, dt, bs, T, blocks, kf2, vf)
+    assert np.array_equal(out[:2], out2[:2])
+    assert np.all(np.abs(out[2:] - out2[2:]).max(axis=(1, 2)) > 0)
