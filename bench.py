@@ -32,9 +32,10 @@ PCIE_GEN5_X16_GBPS = 64.0   # host link, one direction
 
 
 KERNEL_SOURCES = {
-    "oasis_score": ["score.hip"],
+    "oasis_score": ["score.hip", "score_tile.h"],
     "oasis_sparse_attn": ["attention.hip"],
     "oasis_topk_select": ["selection.hip"],
+    "oasis_score_topk_select": ["selection.hip", "score_tile.h"],
 }
 
 
@@ -173,6 +174,8 @@ def main():
     ap.add_argument("--correct-cap", type=int, default=0,
                     help="lookahead workloads: decode-time miss correction with this cap per "
                          "(b, KV head) and step (0: attention over the prefetched set)")
+    ap.add_argument("--fuse-score-topk", action="store_true",
+                    help="score, top-K and select in one kernel where the shape allows")
     ap.add_argument("--sweep", action="store_true",
                     help="multi-layer workloads: one line per fetch ratio of the sweep")
     args = ap.parse_args()
@@ -210,6 +213,8 @@ def main():
     t_setup = time.perf_counter()
     run = LayerRunner(w, n_steps)
     h = run.h
+    if args.fuse_score_topk:
+        h.oasis_set_score_topk_fusion(True)
     stream = torch.cuda.current_stream()
     print(f"# setup {time.perf_counter() - t_setup:.1f}s: {w.name}, {n_steps} steps",
           file=sys.stderr, flush=True)
@@ -294,8 +299,10 @@ def main():
     link_gbps = h2d if h2d is not None else PCIE_GEN5_X16_GBPS
     attn_link_bound = fused and fetched * blk_bytes / (link_gbps * 1e9) >= attn_bytes / 6.5e12
     if ms_score >= ms_attn or attn_link_bound:
-        dom = dict(kernel="oasis_score", achieved=score_gbps, per_launch_bytes=score_bytes,
-                   avg_ms=ms_score)
+        # with the fusion on, the score class times the fused score + top-K +
+        # select kernel, whose HBM bytes are the score's plus the small tables
+        dom = dict(kernel="oasis_score_topk_select" if args.fuse_score_topk else "oasis_score",
+                   achieved=score_gbps, per_launch_bytes=score_bytes, avg_ms=ms_score)
     else:
         dom = dict(kernel="oasis_sparse_attn", achieved=attn_gbps, per_launch_bytes=attn_bytes,
                    avg_ms=ms_attn)
@@ -318,7 +325,8 @@ def main():
                    "kv_heads": w.kv_heads, "head_dim": w.head_dim,
                    "context": w.prefix_tokens, "block_size": bs,
                    "budget_tokens": w.budget_tokens, "drafts": w.drafts,
-                   "fetch_ratio": w.fetch_ratio, "cap_per_kv_head": run.cap},
+                   "fetch_ratio": w.fetch_ratio, "cap_per_kv_head": run.cap,
+                   "fuse_score_topk": bool(args.fuse_score_topk)},
         "hbm_gbps_score_attn": hbm_gbps,
         "roofline": {"bound": "hbm", "kernel": dom["kernel"], "achieved": dom["achieved"],
                      "peak": HBM_PEAK_GBPS, "unit": "GB/s",
@@ -451,6 +459,9 @@ def bench_model(args, w):
     t_setup = time.perf_counter()
     log = lambda m: print("# " + m, file=sys.stderr, flush=True)
     mr = ModelRunner(w, n_steps, data_layers=args.data_layers, log=log)
+    if args.fuse_score_topk:
+        for h in mr.handles:
+            h.oasis_set_score_topk_fusion(True)
     log(f"setup {time.perf_counter() - t_setup:.1f}s: {w.name}, {w.layers} layers on "
         f"{mr.H} host KV buffers, {n_steps} steps")
     if args.sweep:

@@ -313,6 +313,29 @@ int oasis_get_timing(oasis_t *h, oasis_timing *out);
  * oasis_set_timing restarts the count. */
 int oasis_set_timing_period(oasis_t *h, int32_t period);
 
+/* Attended set (OasisKV page, Fig. 7: attention over the sparse KV working
+ * set).  Off (default): the selected blocks held after the step, listed as
+ * the hits in top-K order, then the fetched blocks.  On: every block held
+ * after the step, listed as the hits, then the held blocks that were neither
+ * selected nor evicted (slot order), then the fetched blocks; the two agree
+ * when every selected block is held and S = K.  Residency, recency and the
+ * fetch are the same either way.  The ATT_BLOCK / ATT_SLOT lists hold K
+ * entries per KV head, so on needs S <= K (OASIS_E_INVAL otherwise).  Takes
+ * effect at the next oasis_select_and_fetch. */
+int oasis_set_attend_all_resident(oasis_t *h, int32_t on);
+
+/* Score + top-K + select fusion (on != 0; off by default).  While on, an
+ * oasis_predict that asks for neither ids nor scores is deferred: the next
+ * oasis_select_and_fetch scores every block, takes the top-K and selects in
+ * one kernel, one workgroup per (b, KV head), the scores staying in LDS (a
+ * copy still lands in the SCORES buffer).  Applies to tiled bf16 layouts with
+ * d = 128, at least 256 (b, KV head) units and at most 8192 blocks; other
+ * shapes run the separate kernels.  While a predict is deferred its q and
+ * drafts must stay valid until the select; an oasis_append_kv, or a read of
+ * the IDS or SCORES buffer, in between runs the deferred score on its own
+ * first.  The results are the same as without fusion. */
+int oasis_set_score_topk_fusion(oasis_t *h, int32_t on);
+
 /* Shape of a handle: K (top-K blocks), S (slots), NBmax, block size. */
 int oasis_get_dims(const oasis_t *h, int32_t *k_blocks, int32_t *slots, int64_t *nb_max,
                    int32_t *block_size);

@@ -31,7 +31,8 @@ EXPORTS = [
     "oasis_set_state", "oasis_decode_layers", "oasis_decode_layers_ahead",
     "oasis_append_kv", "oasis_predict", "oasis_topk_from_scores", "oasis_select_and_fetch",
     "oasis_evict", "oasis_sparse_attn", "oasis_sparse_attn_verify", "oasis_buffer_bytes", "oasis_read", "oasis_get_stats",
-    "oasis_check", "oasis_set_timing", "oasis_set_timing_period", "oasis_get_timing", "oasis_get_dims", "oasis_tokens",
+    "oasis_check", "oasis_set_timing", "oasis_set_timing_period",
+    "oasis_set_score_topk_fusion", "oasis_set_attend_all_resident", "oasis_get_timing", "oasis_get_dims", "oasis_tokens",
     "oasis_copy_stream", "oasis_kv_bytes_per_token", "oasis_cap_from_ratio", "oasis_strerror",
     "oasis_last_error",
 ]
@@ -108,6 +109,8 @@ def lib():
             "oasis_check": (ctypes.c_int, [H]),
             "oasis_set_timing": (ctypes.c_int, [H, i32]),
             "oasis_set_timing_period": (ctypes.c_int, [H, i32]),
+            "oasis_set_score_topk_fusion": (ctypes.c_int, [H, i32]),
+            "oasis_set_attend_all_resident": (ctypes.c_int, [H, i32]),
             "oasis_get_timing": (ctypes.c_int, [H, ctypes.POINTER(oasis_timing)]),
             "oasis_get_dims": (ctypes.c_int, [H, ctypes.POINTER(i32), ctypes.POINTER(i32),
                                               ctypes.POINTER(i64), ctypes.POINTER(i32)]),
@@ -261,6 +264,16 @@ class Oasis:
     def oasis_set_timing(self, mask=TIME["all"]):
         """mask: OR of TIME values (0 = off)."""
         self._check(lib().oasis_set_timing(self.h, int(mask)), "oasis_set_timing")
+
+    def oasis_set_score_topk_fusion(self, on: bool):
+        """Fuse score, top-K and select into one kernel (when the shape allows)."""
+        self._check(lib().oasis_set_score_topk_fusion(self.h, int(bool(on))),
+                    "oasis_set_score_topk_fusion")
+
+    def oasis_set_attend_all_resident(self, on: bool):
+        """Attend every block held after the step instead of the selected ones."""
+        self._check(lib().oasis_set_attend_all_resident(self.h, int(bool(on))),
+                    "oasis_set_attend_all_resident")
 
     def oasis_set_timing_period(self, period: int):
         """Time one launch in `period` of each timed kernel class."""

@@ -91,6 +91,12 @@ struct oasis_handle {
     // fused with the select (one workgroup per unit).
     bool topk_pending = false;
     int64_t topk_nb = 0;
+    // Score + top-K + select fusion (opt-in): predict records its query rows
+    // and the next select scores, ranks and selects in one kernel.
+    bool fuse_score = false;
+    bool score_pending = false;
+    const void *score_q = nullptr, *score_drafts = nullptr;
+    int score_nd = 0;
     int last_cap = 0;
 
     std::shared_ptr<HostKV> hkv;
@@ -286,11 +292,25 @@ int reset_tables(oasis_t *h) {
     h->predicted = h->selected = false;
     h->fetch_pending = false;
     h->topk_pending = false;
+    h->score_pending = false;
+    return OASIS_OK;
+}
+
+// Run a deferred score on its own (when the scores are needed before a select).
+int flush_score(oasis_t *h, hipStream_t st) {
+    if (!h->score_pending) return OASIS_OK;
+    h->score_pending = false;
+    TRY(after(h, st, h->m_append));
+    TRY(after(h, st, h->m_select));
+    LAUNCH(h, TM_SCORE, st,
+           launch_score(h->D, h->summ, h->score_q, h->score_drafts, h->score_nd, h->topk_nb,
+                        h->scores, st));
     return OASIS_OK;
 }
 
 // Run a deferred top-K on its own (when the ids are needed before a select).
 int flush_topk(oasis_t *h, hipStream_t st) {
+    TRY(flush_score(h, st));
     if (!h->topk_pending) return OASIS_OK;
     h->topk_pending = false;
     LAUNCH(h, TM_TOPK, st, launch_topk(h->D, h->scores, h->topk_nb, h->ids, nullptr, h->err, st));
@@ -610,6 +630,7 @@ extern "C" int oasis_append_kv(oasis_t *h, const void *k_dev, const void *v_dev,
     TRY(after(h, stream, h->m_gather));
     TRY(after(h, stream, h->m_attn));
     TRY(flush_fetch(h, stream));
+    TRY(flush_score(h, stream));  // a deferred predict scores the summaries before this token
     LAUNCH(h, TM_APPEND, stream,
            launch_append(h->D, k_dev, v_dev, h->T, h->host_kv_dev, h->summ, h->block_slot,
                          h->slots, stream));
@@ -635,6 +656,18 @@ extern "C" int oasis_predict(oasis_t *h, const void *q_dev, const void *drafts_d
     const Dims &D = h->D;
     TRY(after(h, stream, h->m_append));
     TRY(after(h, stream, h->m_select));  // the previous select reads the scores
+    h->score_pending = false;
+    if (h->fuse_score && !block_ids_dev && !scores_dev &&
+        score_topk_fusable(D, NB, D.G * ((q_dev ? 1 : 0) + n_drafts))) {
+        h->score_pending = true;  // scored by the next select's fused kernel
+        h->score_q = q_dev;
+        h->score_drafts = drafts_dev;
+        h->score_nd = n_drafts;
+        h->topk_nb = NB;
+        h->topk_pending = true;
+        h->predicted = true;
+        return OASIS_OK;
+    }
     LAUNCH(h, TM_SCORE, stream,
            launch_score(D, h->summ, q_dev, drafts_dev, n_drafts, NB, h->scores,
                         stream));
@@ -661,6 +694,7 @@ extern "C" int oasis_topk_from_scores(oasis_t *h, const float *scores_dev,
     LAUNCH(h, TM_TOPK, stream,
            launch_topk(h->D, scores_dev, NB, h->ids, block_ids_dev, h->err, stream));
     h->topk_pending = false;
+    h->score_pending = false;
     h->predicted = true;
     return OASIS_OK;
 }
@@ -681,7 +715,19 @@ int select_impl(oasis_t *h, int32_t cap, hipStream_t stream, bool eager, hipStre
     TRY(after(h, stream, h->m_gather));
     TRY(after(h, stream, h->m_attn));
     TRY(flush_fetch(h, stream));
-    if (h->topk_pending) {
+    if (h->score_pending) {
+        // the deferred predict's orderings, on this stream
+        TRY(after(h, stream, h->m_append));
+        TRY(after(h, stream, h->m_select));
+        h->score_pending = false;
+        h->topk_pending = false;
+        LAUNCH(h, TM_SCORE, stream,
+               launch_score_topk_select(D, h->summ, h->score_q, h->score_drafts, h->score_nd,
+                                        h->topk_nb, h->scores, h->ids, h->slot_block,
+                                        h->last_used, h->block_slot, cap, (int32_t)t64,
+                                        h->fetch_block, h->fetch_slot, h->att_block,
+                                        h->att_slot, h->counts, h->stats, h->err, stream));
+    } else if (h->topk_pending) {
         h->topk_pending = false;
         LAUNCH(h, TM_SELECT, stream,
                launch_topk_select(D, h->scores, h->topk_nb, h->ids, h->slot_block, h->last_used,
@@ -981,9 +1027,11 @@ extern "C" int oasis_read(oasis_t *h, int32_t which, int64_t offset, int64_t nby
         return fail(h, OASIS_E_INVAL, "read: range [%lld, +%lld) outside %lld bytes",
                     (long long)offset, (long long)nbytes, (long long)size);
     HIP_OK(h, hipDeviceSynchronize());
-    if (h->fetch_pending || (h->topk_pending && which == OASIS_BUF_IDS)) {
+    if (h->fetch_pending || (h->topk_pending && which == OASIS_BUF_IDS) ||
+        (h->score_pending && which == OASIS_BUF_SCORES)) {
         TRY(flush_fetch(h, h->copy));
         if (which == OASIS_BUF_IDS) TRY(flush_topk(h, h->copy));
+        if (which == OASIS_BUF_SCORES) TRY(flush_score(h, h->copy));
         HIP_OK(h, hipStreamSynchronize(h->copy));
     }
     const void *src = nullptr;
@@ -1049,6 +1097,26 @@ extern "C" int oasis_set_timing(oasis_t *h, int32_t mask) {
         t.n = 0;
         t.seq = 0;
         t.active = false;
+    }
+    return OASIS_OK;
+}
+
+extern "C" int oasis_set_attend_all_resident(oasis_t *h, int32_t on) {
+    if (!h) return OASIS_E_INVAL;
+    if (on && h->D.S > h->D.K)
+        return fail(h, OASIS_E_INVAL,
+                    "attend_all_resident: %d slots per KV head exceed the %d-entry attended list",
+                    h->D.S, h->D.K);
+    h->D.attend_all = on != 0;
+    return OASIS_OK;
+}
+
+extern "C" int oasis_set_score_topk_fusion(oasis_t *h, int32_t on) {
+    if (!h) return OASIS_E_INVAL;
+    h->fuse_score = on != 0;
+    if (!h->fuse_score && h->score_pending) {
+        TRY(flush_score(h, h->copy));
+        HIP_OK(h, hipStreamSynchronize(h->copy));
     }
     return OASIS_OK;
 }

@@ -238,15 +238,15 @@ __device__ __forceinline__ int block_valid(int64_t T, int32_t blk) {
 // Grid (1-D, 256 threads = 4 waves per workgroup):
 //   workgroups [0, n_fetch_wg): fetch waves (mode 1 only).  Item i of unit u,
 //     i < cap, is the i-th block fetched for u this step (attended entry
-//     n_hit + i).  Wave f takes items f, f + F, ... (F = 4 n_fetch_wg): it
+//     n_att - n_fetch + i: the fetched blocks end the list).  Wave f takes items f, f + F, ... (F = 4 n_fetch_wg): it
 //     reads the block from the pinned host KV over the host link, writes it
 //     into its slot (the copy later steps will hit), attends to it from
 //     registers and writes partial i of the unit; an item past the unit's
 //     fetch count writes an empty partial.  A few such waves keep the host
 //     link saturated while holding only a small share of the CU slots.
 //   workgroups after that: hit workgroups, ns1 per unit; wave w of split s
-//     takes entries 4 BPW s + w + 4 j, j < BPW, of [0, n_end) (n_end = n_hit
-//     in mode 1, n_att in mode 0) from their slots; the four waves are merged
+//     takes entries 4 BPW s + w + 4 j, j < BPW, of [0, n_end) (n_end =
+//     n_att - n_fetch in mode 1, n_att in mode 0) from their slots; the four waves are merged
 //     in LDS into partial nsf_max + s.
 template <int G, int BPW>
 __global__ __launch_bounds__(256) void attn_mfma_kernel(
@@ -273,11 +273,12 @@ __global__ __launch_bounds__(256) void attn_mfma_kernel(
         auto locate = [&](int64_t item, int64_t &u, int &i, int32_t &blk, int32_t &slot) -> bool {
             u = item / cap;
             i = (int)(item % cap);
-            const int n_hit = __builtin_amdgcn_readfirstlane(counts[u * 4 + 1]);
             const int n_att = __builtin_amdgcn_readfirstlane(counts[u * 4 + 0]);
-            if (n_hit + i >= n_att) return false;
-            blk = __builtin_amdgcn_readfirstlane(att_block[u * K + n_hit + i]);
-            slot = __builtin_amdgcn_readfirstlane(att_slot[u * K + n_hit + i]);
+            const int n_fetch = __builtin_amdgcn_readfirstlane(counts[u * 4 + 2]);
+            if (i >= n_fetch) return false;
+            const int e = n_att - n_fetch + i;  // the fetched blocks end the list
+            blk = __builtin_amdgcn_readfirstlane(att_block[u * K + e]);
+            slot = __builtin_amdgcn_readfirstlane(att_slot[u * K + e]);
             return true;
         };
         int64_t u0;
@@ -332,7 +333,8 @@ __global__ __launch_bounds__(256) void attn_mfma_kernel(
     const int64_t g = (int64_t)blockIdx.x - n_fetch_wg;
     const int64_t u = g / ns1;
     const int s = (int)(g % ns1);
-    const int e_end = __builtin_amdgcn_readfirstlane(mode == 1 ? counts[u * 4 + 1] : counts[u * 4 + 0]);
+    const int e_end = __builtin_amdgcn_readfirstlane(
+        mode == 1 ? counts[u * 4 + 0] - counts[u * 4 + 2] : counts[u * 4 + 0]);
     const int e_first = 4 * BPW * s + wave;
     st.init(q, u / Hkv, Hq, (int)(u % Hkv));
     const int ne = e_first >= e_end ? 0 : (e_end - e_first + 3) / 4 < BPW ? (e_end - e_first + 3) / 4 : BPW;

@@ -39,6 +39,9 @@ struct Dims {
     // the B-operand order of v_mfma_f32_32x32x16_bf16, so one k-step of a
     // tile is one contiguous 1 KB load of a wave.
     bool tiled = false;
+    // Attended set: the selected blocks now held (false), or every block held
+    // after the step (true; needs S <= K so the list fits K entries).
+    bool attend_all = false;
     int64_t units() const { return (int64_t)B * Hkv; }
     int esize() const { return dtype == kF32 ? 4 : 2; }
     int64_t block_elems() const { return 2LL * bs * d; }  // K and V of one block
@@ -86,6 +89,18 @@ hipError_t launch_gather(const Dims &D, const void *host_kv, void *slots, const 
 
 // Top-K and diff / cap / LRU of every unit in one kernel (the ids are also
 // written to ids).
+// Score, top-K and select fused in one workgroup per unit (tiled bf16
+// summaries, d = 128, at least 256 units, NB <= 8192); score_topk_fusable
+// says whether a shape qualifies.
+bool score_topk_fusable(const Dims &D, int64_t NB, int n_rows);
+hipError_t launch_score_topk_select(const Dims &D, const void *summ, const void *q,
+                                    const void *drafts, int n_drafts, int64_t NB, float *scores,
+                                    int32_t *ids, int32_t *slot_block, int32_t *last_used,
+                                    int32_t *block_slot, int cap, int32_t t,
+                                    int32_t *fetch_block, int32_t *fetch_slot,
+                                    int32_t *att_block, int32_t *att_slot, int32_t *counts,
+                                    DevStats *stats, uint32_t *err, hipStream_t st);
+
 hipError_t launch_topk_select(const Dims &D, const float *scores, int64_t NB, int32_t *ids,
                               int32_t *slot_block, int32_t *last_used, int32_t *block_slot,
                               int cap, int32_t t, int32_t *fetch_block, int32_t *fetch_slot,

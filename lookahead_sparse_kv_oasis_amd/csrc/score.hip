@@ -17,6 +17,7 @@
 #include <string.h>
 
 #include "kernels.h"
+#include "score_tile.h"
 
 namespace oasis {
 
@@ -74,25 +75,7 @@ __global__ __launch_bounds__(64) void score_valu_kernel(const T *__restrict__ su
 }
 
 // ---------------------------------------------------------------- MFMA, bf16
-
-// v_mfma_f32_32x32x16_bf16 operand layout (wave64): lane l supplies row
-// (A) / column (B) l % 32 and 8 consecutive k of the 16-k step, k-half
-// l / 32.  The k order inside the contraction is free as long as A and B
-// agree, so k-half 0 carries x+ against the block maxima and k-half 1 carries
-// x- against the block minima.  The tiled summary layout (Dims) stores each
-// k-step of a 32-block tile in exactly this lane order, so a wave reads one
-// k-step with one fully coalesced 1 KB load and feeds it to the matrix core
-// straight from its registers.  Query rows past Q repeat row 0, so the max
-// over all 32 accumulator rows needs no mask.  Output column of lane l is
-// block l % 32; lanes l and l ^ 32 hold the two halves of its rows.
-__device__ __forceinline__ uint4 keep_sign(uint4 w, bool negative) {
-    auto one = [&](uint32_t x) -> uint32_t {
-        const uint32_t s = (x >> 15) & 0x00010001u;  // sign bit of each bf16
-        const uint32_t neg = s * 0xFFFFu;             // 0xFFFF per negative element
-        return negative ? (x & neg) : (x & ~neg);
-    };
-    return make_uint4(one(w.x), one(w.y), one(w.z), one(w.w));
-}
+// (operand layout and sign split: score_tile.h)
 
 // One workgroup (4 waves) per contiguous range of tiles_per_wg tiles of one
 // unit; the waves take the range's tiles in turn, one tile (16 KB at d = 128)
@@ -109,60 +92,24 @@ __global__ __launch_bounds__(256) void score_tiled_kernel(const uint16_t *__rest
                                                           int64_t unit_elems, int64_t NBmax,
                                                           int64_t NB, int per_unit,
                                                           int tiles_per_wg) {
-    constexpr int NI = D / 8;  // k-steps: 16 k each, 8 from each half
     extern __shared__ float tile_best[];  // [tiles_per_wg][32]
-    const int lane = threadIdx.x & 63;
     const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
     const int64_t u = blockIdx.x / per_unit;
     const int64_t chunk = blockIdx.x % per_unit;
     const int h = (int)(u % Hkv), b = (int)(u / Hkv);
-    const int Q = G * (1 - qskip + n_drafts);
-    const int m = lane & 31, half = lane >> 5;
     const int64_t ntiles = (NB + 31) / 32;
     const int64_t t_begin = chunk * tiles_per_wg;
     const int64_t t_end = t_begin + tiles_per_wg < ntiles ? t_begin + tiles_per_wg : ntiles;
     if (t_begin >= t_end) return;  // whole workgroup
-    const uint16_t *ubase = summ + u * unit_elems + 8 * lane;
-
-    bf16x8 bv[NI];
-    auto load = [&](int64_t tile) {
-        const uint16_t *src = ubase + tile * 64 * D;
-#pragma unroll
-        for (int i = 0; i < NI; ++i) bv[i] = __builtin_bit_cast(bf16x8, gload16(src + 512 * i));
-    };
+    ScoreTiles<D, QT> st;
+    st.setup(summ, u, unit_elems);
     int64_t t = t_begin + wave;
-    if (t < t_end) load(t);  // in flight while the query rows are read
-
-    bf16x8 a[QT][NI];
-#pragma unroll
-    for (int qt = 0; qt < QT; ++qt) {
-        int r = 32 * qt + m;
-        if (r >= Q) r = 0;
-        const int src = r / G + qskip, g = r % G;
-        const uint16_t *x = src == 0
-                                ? q + ((int64_t)b * Hq + h * G + g) * D
-                                : drafts + (((int64_t)(src - 1) * B + b) * Hq + h * G + g) * D;
-#pragma unroll
-        for (int i = 0; i < NI; ++i) {
-            const uint4 w = *reinterpret_cast<const uint4 *>(x + 8 * i);
-            a[qt][i] = __builtin_bit_cast(bf16x8, keep_sign(w, half != 0));
-        }
-    }
-
+    if (t < t_end) st.load(t);  // in flight while the query rows are read
+    st.rows(q, drafts, n_drafts, qskip, B, Hq, G, b, h);
     for (; t < t_end; t += 4) {
-        float best = -INFINITY;
-#pragma unroll
-        for (int qt = 0; qt < QT; ++qt) {
-            f32x16 acc = {};
-#pragma unroll
-            for (int i = 0; i < NI; ++i)
-                acc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a[qt][i], bv[i], acc, 0, 0, 0);
-#pragma unroll
-            for (int r = 0; r < 16; ++r) best = fmaxf(best, acc[r]);
-        }
-        best = fmaxf(best, __shfl_xor(best, 32, 64));
-        if (half == 0) tile_best[(t - t_begin) * 32 + m] = best;
-        if (t + 4 < t_end) load(t + 4);
+        const float best = st.best();
+        if (st.half == 0) tile_best[(t - t_begin) * 32 + st.m] = best;
+        if (t + 4 < t_end) st.load(t + 4);
     }
     __syncthreads();
     const int64_t j0 = t_begin * 32;

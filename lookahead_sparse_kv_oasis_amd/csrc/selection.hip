@@ -26,14 +26,17 @@
 //            are not selected, least recently used first, ties to the lower
 //            block id;
 //   every hit and every fetched block gets last_used = t.
-// The attended list is the hits followed by the fetched blocks.  One wave
-// does it: ordered compactions use ballots; victims are ranked by counting
+// The attended list is the hits followed by the fetched blocks; under the
+// attend-all reading (every block held after the step) the held blocks that
+// were neither selected nor evicted come between them, in slot order.  One
+// wave does it: ordered compactions use ballots; victims are ranked by counting
 // smaller (last_used, block) keys, exact because held block ids are distinct.
 //
 // The fused kernel runs both for a unit in one workgroup: the slot tables are
 // copied into LDS while the top-K runs, and the winners go straight from LDS
 // into the select.
 #include "kernels.h"
+#include "score_tile.h"
 
 namespace oasis {
 
@@ -405,7 +408,7 @@ __device__ void select_unit(int64_t u, const int32_t *sel, const int32_t *sb_in,
                             int32_t *__restrict__ att_block, int32_t *__restrict__ att_slot,
                             int32_t *__restrict__ counts, DevStats *stats, uint32_t *err,
                             int32_t *sh, const int32_t *hkey, const int32_t *hval,
-                            uint32_t hmask) {
+                            uint32_t hmask, int attend_all) {
     int32_t *hit_blk = sh;             // [K]
     int32_t *hit_slot = hit_blk + K;   // [K]
     int32_t *miss_blk = hit_slot + K;  // [K]
@@ -525,6 +528,23 @@ __device__ void select_unit(int64_t u, const int32_t *sel, const int32_t *sb_in,
         const int32_t old = sb_in[s];
         if (old >= 0) bs[old] = -1;
     }
+    // attend-all reading: the held blocks that stay and were not selected
+    int nr = 0;
+    if (attend_all) {
+        for (int i = lane; i < n; i += 64) selected[cand[i]] = 2;  // refilled
+        wave_sync();
+        for (int base = 0; base < S; base += 64) {
+            const int s = base + lane;
+            const bool keep = s < S && sb_in[s] >= 0 && selected[s] == 0;
+            const unsigned long long kb = __ballot(keep);
+            if (keep) {
+                const int p = nh + nr + lanes_below(kb);
+                ab[p] = sb_in[s];
+                as[p] = s;
+            }
+            nr += __popcll(kb);
+        }
+    }
     wave_sync();
     for (int i = lane; i < n; i += 64) {
         const int s = cand[i];
@@ -534,8 +554,8 @@ __device__ void select_unit(int64_t u, const int32_t *sel, const int32_t *sb_in,
         lu[s] = t;
         fb[i] = blk;
         fs[i] = s;
-        ab[nh + i] = blk;
-        as[nh + i] = s;
+        ab[nh + nr + i] = blk;
+        as[nh + nr + i] = s;
     }
     for (int i = lane; i < nh; i += 64) {
         lu[hit_slot[i]] = t;
@@ -543,14 +563,14 @@ __device__ void select_unit(int64_t u, const int32_t *sel, const int32_t *sb_in,
         as[i] = hit_slot[i];
     }
     if (lane == 0) {
-        counts[u * 4 + 0] = nh + n;
+        counts[u * 4 + 0] = nh + nr + n;
         counts[u * 4 + 1] = nh;
         counts[u * 4 + 2] = n;
         counts[u * 4 + 3] = nm;
         atomicAdd(&stats->hits, (unsigned long long)nh);
         atomicAdd(&stats->misses, (unsigned long long)nm);
         atomicAdd(&stats->fetched, (unsigned long long)n);
-        atomicAdd(&stats->attended, (unsigned long long)(nh + n));
+        atomicAdd(&stats->attended, (unsigned long long)(nh + nr + n));
     }
 }
 
@@ -560,12 +580,12 @@ __global__ __launch_bounds__(64) void select_kernel(
     int64_t NBmax, int cap, int32_t t, int32_t *__restrict__ fetch_block,
     int32_t *__restrict__ fetch_slot, int32_t *__restrict__ att_block,
     int32_t *__restrict__ att_slot, int32_t *__restrict__ counts, DevStats *stats,
-    uint32_t *err) {
+    uint32_t *err, int attend_all) {
     extern __shared__ __attribute__((aligned(16))) int32_t sh[];
     const int64_t u = blockIdx.x;
     select_unit(u, ids + u * K, slot_block + u * S, last_used + u * S, slot_block, last_used,
                 block_slot, K, S, NBmax, cap, t, fetch_block, fetch_slot, att_block, att_slot,
-                counts, stats, err, sh, nullptr, nullptr, 0u);
+                counts, stats, err, sh, nullptr, nullptr, 0u, attend_all);
 }
 
 // Top-K and select of one unit in one workgroup.
@@ -576,7 +596,7 @@ __global__ __launch_bounds__(NT) void topk_select_kernel(
     int32_t *__restrict__ block_slot, int K, int S, int64_t NBmax, int cap, int32_t t,
     int32_t *__restrict__ fetch_block, int32_t *__restrict__ fetch_slot,
     int32_t *__restrict__ att_block, int32_t *__restrict__ att_slot,
-    int32_t *__restrict__ counts, DevStats *stats, uint32_t *err) {
+    int32_t *__restrict__ counts, DevStats *stats, uint32_t *err, int attend_all) {
     extern __shared__ __attribute__((aligned(16))) int32_t sh[];
     const int64_t u = blockIdx.x;
     const int K4 = (K + 3) & ~3, S4 = (S + 3) & ~3;
@@ -609,7 +629,80 @@ __global__ __launch_bounds__(NT) void topk_select_kernel(
     if (threadIdx.x < 64)
         select_unit(u, sel_lds, sb_lds, lu_lds, slot_block, last_used, block_slot, K, S, NBmax,
                     cap, t, fetch_block, fetch_slot, att_block, att_slot, counts, stats, err,
-                    scratch, hkey, hval, (uint32_t)(HS - 1));
+                    scratch, hkey, hval, (uint32_t)(HS - 1), attend_all);
+}
+
+// Score, top-K and select of one unit in one workgroup (4 waves): the unit's
+// tiles are scored into LDS (the slot tables are hashed meanwhile), copied out
+// for inspection, and the top-K and select run on the LDS copy: no score round
+// trip through HBM and one launch instead of two.  The summary read is the
+// same as the score kernel's.
+template <int D, int QT, int CMAX>
+__global__ __launch_bounds__(256) void score_topk_select_kernel(
+    const uint16_t *__restrict__ summ, const uint16_t *__restrict__ q,
+    const uint16_t *__restrict__ drafts, int n_drafts, int qskip, float *__restrict__ scores,
+    int B, int Hq, int Hkv, int G, int64_t unit_elems, int NB, int32_t *__restrict__ ids,
+    int32_t *__restrict__ slot_block, int32_t *__restrict__ last_used,
+    int32_t *__restrict__ block_slot, int K, int S, int64_t NBmax, int cap, int32_t t,
+    int32_t *__restrict__ fetch_block, int32_t *__restrict__ fetch_slot,
+    int32_t *__restrict__ att_block, int32_t *__restrict__ att_slot,
+    int32_t *__restrict__ counts, DevStats *stats, uint32_t *err, int attend_all) {
+    constexpr int NT = 256;
+    extern __shared__ __attribute__((aligned(16))) int32_t sh[];
+    const int64_t u = blockIdx.x;
+    const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+    const int K4 = (K + 3) & ~3, S4 = (S + 3) & ~3;
+    const int HS = hash_size(S);
+    int32_t *sel_lds = sh;                 // [K]
+    int32_t *sb_lds = sel_lds + K4;        // [S]
+    int32_t *lu_lds = sb_lds + S4;         // [S]
+    int32_t *hkey = lu_lds + S4;           // [HS]
+    int32_t *hval = hkey + HS;             // [HS]
+    int32_t *scratch = hval + HS;          // 16-byte aligned
+    float *sc = reinterpret_cast<float *>(scratch + ((select_lds_bytes(K, S) + 15) / 16) * 4);
+    const int h = (int)(u % Hkv), b = (int)(u / Hkv);
+    const int ntiles = (NB + 31) / 32;
+
+    ScoreTiles<D, QT> st;
+    st.setup(summ, u, unit_elems);
+    int tile = wave;
+    if (tile < ntiles) st.load(tile);  // in flight while the tables are hashed
+    for (int i = threadIdx.x; i < HS; i += NT) hkey[i] = -1;
+    __syncthreads();
+    for (int s = threadIdx.x; s < S; s += NT) {
+        const int32_t blk = slot_block[u * S + s];
+        sb_lds[s] = blk;
+        lu_lds[s] = last_used[u * S + s];
+        if (blk >= 0) {
+            uint32_t hh = block_hash(blk) & (uint32_t)(HS - 1);
+            while (atomicCAS(&hkey[hh], -1, blk) != -1) hh = (hh + 1) & (uint32_t)(HS - 1);
+            hval[hh] = s;
+        }
+    }
+    st.rows(q, drafts, n_drafts, qskip, B, Hq, G, b, h);
+    for (; tile < ntiles; tile += 4) {
+        const float best = st.best();
+        if (st.half == 0) sc[tile * 32 + st.m] = best;
+        if (tile + 4 < ntiles) st.load(tile + 4);
+    }
+    __syncthreads();
+    for (int j = threadIdx.x; j < NB; j += NT) scores[u * NBmax + j] = sc[j];
+    TopkKeys<CMAX> kk;
+    {
+        const int C = (NB + NT - 1) / NT;
+        const int begin = threadIdx.x * C;
+#pragma unroll
+        for (int i = 0; i < CMAX; ++i) {
+            const int id = begin + i;
+            kk.raw[i] = (i < C && id < NB) ? sc[id] : 0.f;
+        }
+    }
+    topk_unit<NT, CMAX>(kk, NB, K, ids + u * K, nullptr, sel_lds, err);
+    __syncthreads();
+    if (threadIdx.x < 64)
+        select_unit(u, sel_lds, sb_lds, lu_lds, slot_block, last_used, block_slot, K, S, NBmax,
+                    cap, t, fetch_block, fetch_slot, att_block, att_slot, counts, stats, err,
+                    scratch, hkey, hval, (uint32_t)(HS - 1), attend_all);
 }
 
 __global__ __launch_bounds__(64) void evict_kernel(const int32_t *__restrict__ blocks,
@@ -674,7 +767,7 @@ hipError_t launch_select(const Dims &D, const int32_t *ids, int32_t *slot_block,
     OASIS_LAUNCH(select_kernel, dim3((unsigned)D.units()), dim3(64),
                        select_lds_bytes(D.K, D.S), st, ids, slot_block, last_used, block_slot,
                        D.K, D.S, D.NBmax, cap, t, fetch_block, fetch_slot, att_block, att_slot,
-                       counts, stats, err);
+                       counts, stats, err, D.attend_all ? 1 : 0);
     return hipGetLastError();
 }
 
@@ -696,13 +789,64 @@ hipError_t launch_topk_select(const Dims &D, const float *scores, int64_t NB, in
 #define OASIS_TS(NT_, CM_)                                                                      \
     OASIS_LAUNCH((topk_select_kernel<NT_, CM_>), grid, dim3(NT_), lds, st, scores,      \
                        (int)NB, ids, slot_block, last_used, block_slot, D.K, D.S, D.NBmax, cap, \
-                       t, fetch_block, fetch_slot, att_block, att_slot, counts, stats, err)
+                       t, fetch_block, fetch_slot, att_block, att_slot, counts, stats, err,      \
+                       D.attend_all ? 1 : 0)
     if (NB <= 256 * 64) {
         OASIS_CMAX_DISPATCH(256, (NB + 255) / 256, OASIS_TS);
     } else {
         OASIS_CMAX_DISPATCH(1024, (NB + 1023) / 1024, OASIS_TS);
     }
 #undef OASIS_TS
+    return hipGetLastError();
+}
+
+static size_t fused_lds_bytes(const Dims &D, int64_t NB) {
+    const size_t ints = (size_t)((D.K + 3) & ~3) + 2 * (size_t)((D.S + 3) & ~3) +
+                        2 * (size_t)hash_size(D.S);
+    return sizeof(int32_t) * ints + ((select_lds_bytes(D.K, D.S) + 15) / 16) * 16 +
+           sizeof(float) * 32 * (size_t)((NB + 31) / 32);
+}
+
+bool score_topk_fusable(const Dims &D, int64_t NB, int n_rows) {
+    // one workgroup per unit must still fill the GPU, and the unit's scores
+    // must fit in LDS next to the select's tables
+    return D.tiled && D.d == 128 && n_rows <= 128 && D.units() >= 256 && NB >= 1 &&
+           NB <= 8192 && fused_lds_bytes(D, NB) <= 64 * 1024;
+}
+
+hipError_t launch_score_topk_select(const Dims &D, const void *summ, const void *q,
+                                    const void *drafts, int n_drafts, int64_t NB, float *scores,
+                                    int32_t *ids, int32_t *slot_block, int32_t *last_used,
+                                    int32_t *block_slot, int cap, int32_t t,
+                                    int32_t *fetch_block, int32_t *fetch_slot,
+                                    int32_t *att_block, int32_t *att_slot, int32_t *counts,
+                                    DevStats *stats, uint32_t *err, hipStream_t st) {
+    const int qskip = q ? 0 : 1;
+    const int Q = D.G * (1 - qskip + n_drafts);
+    if (!score_topk_fusable(D, NB, Q)) return hipErrorInvalidValue;
+    const int QT = (Q + 31) / 32;
+    const size_t lds = fused_lds_bytes(D, NB);
+    const int C = (int)((NB + 255) / 256);
+    const dim3 grid((unsigned)D.units());
+#define OASIS_STS(QT_, CM_)                                                                      \
+    OASIS_LAUNCH((score_topk_select_kernel<128, QT_, CM_>), grid, dim3(256), lds, st,            \
+                 (const uint16_t *)summ, (const uint16_t *)q, (const uint16_t *)drafts, n_drafts, \
+                 qskip, scores, D.B, D.Hq, D.Hkv, D.G, D.summ_unit_elems(), (int)NB, ids,         \
+                 slot_block, last_used, block_slot, D.K, D.S, D.NBmax, cap, t, fetch_block,       \
+                 fetch_slot, att_block, att_slot, counts, stats, err, D.attend_all ? 1 : 0)
+#define OASIS_STS_C(QT_)                   \
+    do {                                   \
+        if (C <= 4) OASIS_STS(QT_, 4);     \
+        else if (C <= 8) OASIS_STS(QT_, 8); \
+        else if (C <= 16) OASIS_STS(QT_, 16); \
+        else OASIS_STS(QT_, 32);           \
+    } while (0)
+    if (QT == 1) OASIS_STS_C(1);
+    else if (QT == 2) OASIS_STS_C(2);
+    else if (QT == 3) OASIS_STS_C(3);
+    else OASIS_STS_C(4);
+#undef OASIS_STS_C
+#undef OASIS_STS
     return hipGetLastError();
 }
 

@@ -64,7 +64,7 @@ def lib():
         L.orc_topk.argtypes = [fp, i64, i32, ip]
         L.orc_select.restype = ctypes.c_int
         L.orc_select.argtypes = [ip, ip, i32, ip, i32, i32, ctypes.c_int32,
-                                 ip, ip, ip, ip, ip, ip, ip]
+                                 ip, ip, ip, ip, ip, ip, ip, i32]
         L.orc_attention.restype = None
         L.orc_attention.argtypes = [dp, i32, vp, vp, i32, i32, i32, i64, ip, i32, dp]
         L.orc_dense_attention.restype = None
@@ -144,21 +144,26 @@ def topk(s32: np.ndarray, k: int) -> np.ndarray:
     return ids
 
 
-def select(slot_block: np.ndarray, last_used: np.ndarray, ids: np.ndarray, cap: int, t: int):
-    """Diff / cap / LRU for one unit; updates slot_block and last_used in place."""
+def select(slot_block: np.ndarray, last_used: np.ndarray, ids: np.ndarray, cap: int, t: int,
+           attend_all: bool = False):
+    """Diff / cap / LRU for one unit; updates slot_block and last_used in place.
+
+    attend_all: the attended list is every block held after the step (hits,
+    then the other held blocks in slot order, then the fetched ones) instead
+    of the selected blocks now held."""
     S = slot_block.shape[0]
     K = ids.shape[0]
     assert slot_block.dtype == np.int32 and last_used.dtype == np.int32
     ids = np.ascontiguousarray(ids, np.int32)
     fb = np.full(max(cap, 1), -1, np.int32)
     fs = np.full(max(cap, 1), -1, np.int32)
-    ab = np.full(K, -1, np.int32)
-    ast = np.full(K, -1, np.int32)
+    ab = np.full(max(K, S), -1, np.int32)
+    ast = np.full(max(K, S), -1, np.int32)
     nf, na, nh = (ctypes.c_int32(0) for _ in range(3))
     I = ctypes.c_int32
     rc = lib().orc_select(_p(slot_block, I), _p(last_used, I), S, _p(ids, I), K, cap, t,
                           _p(fb, I), _p(fs, I), ctypes.byref(nf), _p(ab, I), _p(ast, I),
-                          ctypes.byref(na), ctypes.byref(nh))
+                          ctypes.byref(na), ctypes.byref(nh), int(bool(attend_all)))
     if rc != 0:
         raise ValueError("invalid residency state")
     return dict(fetch_block=fb[:nf.value].copy(), fetch_slot=fs[:nf.value].copy(),

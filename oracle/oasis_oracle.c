@@ -207,11 +207,17 @@ static int by_lru(const void *pa, const void *pb)
  * Outputs: fetch_block/fetch_slot[0..n-1]; the attended list (READING: the
  * attention runs over the selected blocks now held) = hits in top-K order
  * followed by the fetched blocks, as block ids and their slots.
+ * attend_all != 0 takes the other reading of the attended set, every block
+ * held after the step: the hits, then the held blocks that were not
+ * selected (kept, not evicted) in slot order, then the fetched blocks;
+ * att_block / att_slot then need room for max(K, S) entries.  Residency and
+ * recency are the same under both readings.
  * Returns 0, or -1 on an invalid state (a block held twice, not enough
  * slots). */
 int orc_select(int32_t *slot_block, int32_t *last_used, int S, const int32_t *ids, int K,
                int cap, int32_t t, int32_t *fetch_block, int32_t *fetch_slot, int32_t *n_fetch,
-               int32_t *att_block, int32_t *att_slot, int32_t *n_att, int32_t *n_hit)
+               int32_t *att_block, int32_t *att_slot, int32_t *n_att, int32_t *n_hit,
+               int attend_all)
 {
     int32_t *hit_slot = malloc(sizeof(int32_t) * (size_t)(K > 0 ? K : 1));
     int32_t *miss = malloc(sizeof(int32_t) * (size_t)(K > 0 ? K : 1));
@@ -286,12 +292,33 @@ int orc_select(int32_t *slot_block, int32_t *last_used, int S, const int32_t *id
         last_used[s] = t;
         fetch_block[i] = miss[i];
         fetch_slot[i] = s;
-        att_block[nh + i] = miss[i];
-        att_slot[nh + i] = s;
+    }
+    int na = nh;
+    if (attend_all) {
+        for (int s = 0; s < S; ++s) {
+            if (slot_block[s] < 0)
+                continue;
+            int listed = 0;
+            for (int i = 0; i < nh; ++i)
+                if (hit_slot[i] == s)
+                    listed = 1;
+            for (int i = 0; i < n; ++i)
+                if (cand[i] == s)
+                    listed = 1;
+            if (!listed) {
+                att_block[na] = slot_block[s];
+                att_slot[na] = s;
+                ++na;
+            }
+        }
+    }
+    for (int i = 0; i < n; ++i) {
+        att_block[na + i] = miss[i];
+        att_slot[na + i] = cand[i];
     }
     *n_fetch = n;
     *n_hit = nh;
-    *n_att = nh + n;
+    *n_att = na + n;
 out:
     free(hit_slot);
     free(miss);

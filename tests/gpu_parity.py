@@ -261,6 +261,7 @@ class FreeRunning(Parity):
     against the oracle attention over the GPU's attended list."""
 
     q_layer = None   # layer whose query the drafts perturb (None: self.layer)
+    attend_all = False  # attended set: every block held after the step
 
     def _tables(self):
         h = self.run.h
@@ -302,7 +303,7 @@ class FreeRunning(Parity):
             assert np.array_equal(got_ids, exp_ids), tag + " ids"
             sb0, lu0 = prev[(b, hh)]
             sb_exp, lu_exp = sb0.copy(), lu0.copy()
-            r = oracle.select(sb_exp, lu_exp, exp_ids, cap, t)
+            r = oracle.select(sb_exp, lu_exp, exp_ids, cap, t, attend_all=self.attend_all)
             c = self._unit_slice(cnt, b, hh, 4)
             na, nh, nf = int(c[0]), int(c[1]), int(c[2])
             assert (na, nh, nf) == (len(r["att_block"]), r["n_hit"], len(r["fetch_block"])), tag
@@ -325,11 +326,19 @@ class FreeRunning(Parity):
         report["steps"] = t
         return now
 
-    def run_free(self, steps=None, check_payload_every=8):
+    def run_free(self, steps=None, check_payload_every=8, fuse=False, attend_all=False):
+        """fuse: score, top-K and select in one kernel (the scores are then
+        read back from the handle's SCORES buffer).  attend_all: attend every
+        block held after each step."""
         w, run, h = self.w, self.run, self.run.h
         steps = self.n_steps if steps is None else steps
         K = h.k_blocks
         report = dict(score_err=0.0, attn_err=0.0, steps=0, fetched=0)
+        if fuse:
+            h.oasis_set_score_topk_fusion(True)
+        if attend_all:
+            h.oasis_set_attend_all_resident(True)
+            self.attend_all = True
         if w.admission:
             run.admission()
             torch.cuda.synchronize()
@@ -355,12 +364,15 @@ class FreeRunning(Parity):
                             sb0[sb0 == blk] = -1
                 h.oasis_evict(blocks, counts)
             h.oasis_append_kv(run.app_k[t - 1], run.app_v[t - 1])
-            h.oasis_predict(run.q, run.drafts[t], w.drafts, scores=self.scores_dev)
+            h.oasis_predict(run.q, run.drafts[t], w.drafts,
+                            scores=None if fuse else self.scores_dev)
             h.oasis_select_and_fetch(self.cap)
             h.oasis_sparse_attn(run.q, run.out)
             torch.cuda.synchronize()
             h.oasis_check()
-            prev = self.verify_step(t, prev, report, self.scores_dev.cpu().numpy(), self.cap,
+            sc = (h.read("SCORES", np.float32).reshape(w.batch, w.kv_heads, self.NBmax) if fuse
+                  else self.scores_dev.cpu().numpy())
+            prev = self.verify_step(t, prev, report, sc, self.cap,
                                     check_payload=(t % check_payload_every == 0 or t == steps))
         return report
 
@@ -413,7 +425,7 @@ class AheadRunning(FreeRunning):
             assert np.array_equal(self._unit_slice(ids, b, hh, K), exp_ids), tag + " ids"
             sb0, lu0 = prev[(b, hh)]
             sb_exp, lu_exp = sb0.copy(), lu0.copy()
-            r = oracle.select(sb_exp, lu_exp, exp_ids, cap, t)
+            r = oracle.select(sb_exp, lu_exp, exp_ids, cap, t, attend_all=self.attend_all)
             c = self._unit_slice(cnt, b, hh, 4)
             na, nh, nf = int(c[0]), int(c[1]), int(c[2])
             assert (na, nh, nf) == (len(r["att_block"]), r["n_hit"], len(r["fetch_block"])), tag
@@ -516,7 +528,7 @@ class CorrectedRunning(AheadRunning):
             exp_ids = oracle.topk(gpu_scores[b, hh, :nb], K)
             assert np.array_equal(self._unit_slice(ids, b, hh, K), exp_ids), tag + " ids"
             sb_exp, lu_exp = prev[(b, hh)][0].copy(), prev[(b, hh)][1].copy()
-            r = oracle.select(sb_exp, lu_exp, exp_ids, cap, t)
+            r = oracle.select(sb_exp, lu_exp, exp_ids, cap, t, attend_all=self.attend_all)
             c = self._unit_slice(cnt, b, hh, 4)
             na, nh, nf, nm = int(c[0]), int(c[1]), int(c[2]), int(c[3])
             n_sel = int((exp_ids >= 0).sum())

@@ -226,3 +226,131 @@ def test_verification_attention_against_oracle(q_heads, n_steps):
             worst = max(worst, e)
             assert e <= ATTN_TOL, f"step {t} unit {(b, hh)} verify err {e:.3g}"
     log(f"verify G={G}: max err {worst:.3g}")
+
+
+# ------------------------------------------------------------------ score + top-K + select fusion
+
+def _state(h, bufs=("IDS", "SLOT_BLOCK", "BLOCK_SLOT", "LAST_USED", "FETCH_BLOCK",
+                    "FETCH_SLOT", "ATT_BLOCK", "ATT_SLOT", "COUNTS")):
+    return {b: h.read(b) for b in bufs}
+
+
+def test_score_topk_fusion_bit_identical_full_size():
+    """Qwen3-8B layer at batch 32 and 32K context: with the fused kernel every
+    step's scores, ids, tables, slot payloads and outputs equal the separate
+    kernels' bit for bit; a read of the ids or the scores between predict and
+    select runs the deferred work on its own and changes nothing."""
+    from lookahead_sparse_kv_oasis_amd import TIME
+    from lookahead_sparse_kv_oasis_amd.runner import LayerRunner
+    from tests.gpu_parity import log
+    w = synth.QWEN3_8B
+    n = 10
+    a, b = LayerRunner(w, n), LayerRunner(w, n)
+    a.h.oasis_set_score_topk_fusion(True)
+    a.h.oasis_set_timing(TIME["all"])
+    a.admission()
+    b.admission()
+    for t in range(1, n + 1):
+        for r in (a, b):
+            r.h.oasis_append_kv(r.app_k[t - 1], r.app_v[t - 1])
+            r.h.oasis_predict(r.q_steps[t], r.drafts[t], w.drafts)
+        if t == 3:
+            assert np.array_equal(a.h.read("IDS"), b.h.read("IDS")), "ids read before select"
+        if t == 5:
+            assert np.array_equal(a.h.read("SCORES", np.float32), b.h.read("SCORES", np.float32))
+        for r in (a, b):
+            r.h.oasis_select_and_fetch(r.cap)
+            r.h.oasis_sparse_attn(r.q_steps[t], r.out)
+        torch.cuda.synchronize()
+        assert torch.equal(a.out, b.out), f"step {t}: outputs differ"
+        sa, sb = _state(a.h), _state(b.h)
+        for k in sa:
+            assert np.array_equal(sa[k], sb[k]), f"step {t}: {k} differs"
+        assert np.array_equal(a.h.read("SCORES", np.float32), b.h.read("SCORES", np.float32)), \
+            f"step {t}: scores differ"
+        if t % 5 == 0:
+            assert np.array_equal(a.h.read("SLOTS", np.uint8), b.h.read("SLOTS", np.uint8)), \
+                f"step {t}: slot payloads differ"
+    tm = a.h.oasis_get_timing()
+    # steps 3 and 5 ran the separate kernels, the admission and the rest fused
+    assert tm["n_select"] == 2 and tm["n_score"] == n + 1, tm
+    log(f"fused score+top-K+select: {n} steps bit-identical, timing {tm}")
+    a.h.oasis_check()
+
+
+def test_score_topk_fusion_free_running_against_oracle():
+    """The fused kernel checked step by step against the oracle (scores 1e-4,
+    ids, select and tables bit-exact, attention 2e-3) on sampled units."""
+    from tests.gpu_parity import FreeRunning, log
+    w = synth.QWEN3_8B
+    rep = FreeRunning(w, 12, [(0, 0), (13, 2), (31, 7)]).run_free(check_payload_every=6,
+                                                                   fuse=True)
+    log(f"{w.name} fused free: {rep}")
+
+
+def test_score_topk_fusion_lookahead_executor():
+    """The three-stream lookahead executor (Fig. 8 ordering) with fusion on
+    every layer: outputs and tables bit-identical to the same run without."""
+    from lookahead_sparse_kv_oasis_amd.runner import ModelRunner
+    from tests.gpu_parity import log
+    w = synth.QWEN3_8B_36L_AHEAD.with_(batch=32, prefix_tokens=16 * 200 + 5, layers=3, steps=6,
+                                       budget_tokens=16 * 64)
+    a = ModelRunner(w, w.steps, data_layers=1, threads=8, log=log)
+    b = ModelRunner(w, w.steps, data_layers=1, threads=8, log=log)
+    for h in a.handles:
+        h.oasis_set_score_topk_fusion(True)
+    cur = torch.cuda.current_stream()
+    side, xfer = torch.cuda.Stream(), torch.cuda.Stream()
+    a.admission_ahead(cur, side, xfer)
+    b.admission_ahead(cur, side, xfer)
+    for t in range(1, w.steps + 1):
+        a.step_ahead(t, cur, side, xfer, cap_correct=4 if t % 2 else 0)
+        b.step_ahead(t, cur, side, xfer, cap_correct=4 if t % 2 else 0)
+        torch.cuda.synchronize()
+        assert torch.equal(a.out, b.out), f"step {t}: outputs differ"
+    for l in range(w.layers):
+        sa, sb = _state(a.handles[l]), _state(b.handles[l])
+        for k in sa:
+            assert np.array_equal(sa[k], sb[k]), f"layer {l} {k}"
+        a.handles[l].oasis_check()
+    a.close()
+    b.close()
+
+
+# ------------------------------------------------------------------ attend-all reading
+
+def test_attend_all_resident_tiny_free_running():
+    """fp32 path with slots = K: every held block attended, checked against
+    the oracle's attend-all select and attention over that list."""
+    from tests.gpu_parity import FreeRunning, log
+    w = synth.TINY.with_(slots=8)
+    rep = FreeRunning(w, w.steps, [(0, 0), (0, 1)]).run_free(attend_all=True)
+    log(f"tiny attend-all: {rep}")
+
+
+def test_attend_all_resident_rejects_more_slots_than_budget():
+    from lookahead_sparse_kv_oasis_amd import OasisError
+    from lookahead_sparse_kv_oasis_amd.runner import LayerRunner
+    run = LayerRunner(synth.TINY, 2)  # 32 slots per KV head, K = 8
+    with pytest.raises(OasisError):
+        run.h.oasis_set_attend_all_resident(True)
+    run.h.oasis_set_attend_all_resident(False)
+
+
+def test_attend_all_resident_forced_evictions_full_size():
+    """Qwen3-32B layer with forced evictions, so fewer than S blocks are held
+    and some held blocks are not selected: the attended lists and the fused
+    fetch + attention over them against the oracle."""
+    from tests.gpu_parity import FreeRunning, log
+    w = synth.QWEN3_32B
+    rep = FreeRunning(w, 12, [(0, 0), (7, 5), (15, 7)]).run_free(check_payload_every=6,
+                                                                  attend_all=True)
+    log(f"{w.name} attend-all: {rep}")
+
+
+def test_attend_all_resident_with_fusion_full_size():
+    from tests.gpu_parity import FreeRunning, log
+    w = synth.QWEN3_8B
+    rep = FreeRunning(w, 8, [(0, 0), (13, 2), (31, 7)]).run_free(check_payload_every=4, fuse=True,
+                                                                  attend_all=True)
+    log(f"{w.name} attend-all fused: {rep}")

@@ -210,6 +210,24 @@ def test_select_reproduces_hand_worked_lru_trace():
         assert list(sb) == st["slot_block"] and list(lu) == st["last_used"], st["t"]
 
 
+def test_select_attend_all_reading_on_hand_worked_trace():
+    """The attend-every-held-block reading on the same trace: the attended
+    lists of the worked example, and residency, recency and fetches equal to
+    the default reading's at every step."""
+    g = json.load(open(os.path.join(GOLD, "lru_trace.json")))
+    sb = np.array(g["initial"]["slot_block"], np.int32)
+    lu = np.array(g["initial"]["last_used"], np.int32)
+    for st in g["steps"]:
+        ids = np.array(st["ids"], np.int32)
+        r = oracle.select(sb, lu, ids, g["cap"], st["t"], attend_all=True)
+        assert list(r["att_block"]) == st["att_block_all"], st["t"]
+        assert list(r["att_slot"]) == st["att_slot_all"], st["t"]
+        for key in ("fetch_block", "fetch_slot"):
+            assert list(r[key]) == st[key], (st["t"], key)
+        assert r["n_hit"] == st["n_hit"]
+        assert list(sb) == st["slot_block"] and list(lu) == st["last_used"], st["t"]
+
+
 def _check_select_invariants(sb0, lu0, sb, lu, ids, cap, t, r):
     sel = [i for i in ids if i >= 0]
     held0 = {b for b in sb0 if b >= 0}
@@ -253,6 +271,45 @@ def test_select_invariants_random(seed):
         sb0, lu0 = sb.copy(), lu.copy()
         r = oracle.select(sb, lu, ids, cap, t)
         _check_select_invariants(sb0, lu0, sb, lu, ids, cap, t, r)
+
+
+@pytest.mark.parametrize("seed", range(20))
+def test_select_attend_all_invariants_random(seed):
+    """Attend-all reading: the list is the hits in top-K order, then every
+    other held block in slot order, then the fetched blocks; it names each
+    held block once with its slot; the state update is the default's; with
+    S = K and an uncapped fetch it is the default attended set."""
+    rng = _rng(900 + seed)
+    nb = int(rng.integers(2, 40))
+    k = int(rng.integers(1, min(nb, 10) + 1))
+    S = k if seed % 2 else int(rng.integers(k, k + 8))
+    cap = k if seed % 4 == 1 else int(rng.integers(0, k + 2))
+    sb = np.full(S, -1, np.int32)
+    lu = np.full(S, -1, np.int32)
+    nres = int(rng.integers(0, min(S, nb) + 1))
+    sb[rng.choice(S, nres, replace=False)] = rng.choice(nb, nres, replace=False)
+    lu[:] = rng.integers(-1, 5, S)
+    for t in range(5, 12):
+        s = rng.integers(0, 6, nb).astype(np.float32)
+        ids = oracle.topk(s, k)
+        sb_d, lu_d = sb.copy(), lu.copy()
+        rd = oracle.select(sb_d, lu_d, ids, cap, t)
+        ra = oracle.select(sb, lu, ids, cap, t, attend_all=True)
+        assert np.array_equal(sb, sb_d) and np.array_equal(lu, lu_d)
+        assert np.array_equal(ra["fetch_block"], rd["fetch_block"])
+        assert np.array_equal(ra["fetch_slot"], rd["fetch_slot"])
+        nh, nf = rd["n_hit"], len(rd["fetch_block"])
+        att, ats = list(ra["att_block"]), list(ra["att_slot"])
+        assert att[:nh] == list(rd["att_block"][:nh])               # hits, top-K order
+        assert att[len(att) - nf:] == list(rd["fetch_block"])       # fetched last
+        rest = ats[nh:len(ats) - nf]
+        assert rest == sorted(rest)                                  # others in slot order
+        held = {int(b): s_ for s_, b in enumerate(sb) if b >= 0}
+        assert sorted(att) == sorted(held) and len(att) == len(set(att))
+        for b, s_ in zip(att, ats):
+            assert held[b] == s_
+        if S == k and {int(b) for b in ids if b >= 0} <= set(held):
+            assert sorted(att) == sorted(rd["att_block"])
 
 
 def test_select_rejects_duplicate_residency():
