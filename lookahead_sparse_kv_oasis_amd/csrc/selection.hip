@@ -632,13 +632,13 @@ __global__ __launch_bounds__(NT) void topk_select_kernel(
                     scratch, hkey, hval, (uint32_t)(HS - 1), attend_all);
 }
 
-// Score, top-K and select of one unit in one workgroup (4 waves): the unit's
+// Score, top-K and select of one unit in one workgroup (NT / 64 waves): the unit's
 // tiles are scored into LDS (the slot tables are hashed meanwhile), copied out
 // for inspection, and the top-K and select run on the LDS copy: no score round
 // trip through HBM and one launch instead of two.  The summary read is the
 // same as the score kernel's.
-template <int D, int QT, int CMAX>
-__global__ __launch_bounds__(256) void score_topk_select_kernel(
+template <int D, int QT, int CMAX, int NT>
+__global__ __launch_bounds__(NT) void score_topk_select_kernel(
     const uint16_t *__restrict__ summ, const uint16_t *__restrict__ q,
     const uint16_t *__restrict__ drafts, int n_drafts, int qskip, float *__restrict__ scores,
     int B, int Hq, int Hkv, int G, int64_t unit_elems, int NB, int32_t *__restrict__ ids,
@@ -647,7 +647,7 @@ __global__ __launch_bounds__(256) void score_topk_select_kernel(
     int32_t *__restrict__ fetch_block, int32_t *__restrict__ fetch_slot,
     int32_t *__restrict__ att_block, int32_t *__restrict__ att_slot,
     int32_t *__restrict__ counts, DevStats *stats, uint32_t *err, int attend_all) {
-    constexpr int NT = 256;
+    constexpr int NW = NT / 64;
     extern __shared__ __attribute__((aligned(16))) int32_t sh[];
     const int64_t u = blockIdx.x;
     const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
@@ -680,10 +680,10 @@ __global__ __launch_bounds__(256) void score_topk_select_kernel(
         }
     }
     st.rows(q, drafts, n_drafts, qskip, B, Hq, G, b, h);
-    for (; tile < ntiles; tile += 4) {
+    for (; tile < ntiles; tile += NW) {
         const float best = st.best();
         if (st.half == 0) sc[tile * 32 + st.m] = best;
-        if (tile + 4 < ntiles) st.load(tile + 4);
+        if (tile + NW < ntiles) st.load(tile + NW);
     }
     __syncthreads();
     for (int j = threadIdx.x; j < NB; j += NT) scores[u * NBmax + j] = sc[j];
@@ -735,13 +735,25 @@ __global__ __launch_bounds__(256) void rebuild_block_slot_kernel(
         }
 }
 
-#define OASIS_CMAX_DISPATCH(NT, C, LAUNCH)          \
-    do {                                             \
-        if ((C) <= 4) LAUNCH(NT, 4);                 \
-        else if ((C) <= 8) LAUNCH(NT, 8);            \
-        else if ((C) <= 16) LAUNCH(NT, 16);          \
-        else if ((C) <= 32) LAUNCH(NT, 32);          \
-        else LAUNCH(NT, 64);                         \
+// Workgroup size and per-thread key capacity of the top-K for NB blocks.
+// Each thread holds C = ceil(NB / NT) keys in registers; the loops run over
+// the compiled capacity CMAX, and their cost follows CMAX rather than C
+// (measured: 2,049 blocks take 7.0 us with 256 threads x 16 keys, 6.0 us with
+// 1,024 x 4; 8,193 blocks 19 us with 256 x 64, 10.6 us with 1,024 x 16).  So
+// the thread count grows first and C fits a power of two.  NB <= 65,536.
+static int topk_threads(int64_t NB) { return NB <= 1024 ? 256 : NB <= 2048 ? 512 : 1024; }
+
+#define OASIS_TOPK_DISPATCH(NB, LAUNCH)                        \
+    do {                                                       \
+        const int nt_ = topk_threads(NB);                      \
+        const int64_t c_ = ((NB) + nt_ - 1) / nt_;             \
+        if (nt_ == 256) LAUNCH(256, 4);                        \
+        else if (nt_ == 512) LAUNCH(512, 4);                   \
+        else if (c_ <= 4) LAUNCH(1024, 4);                     \
+        else if (c_ <= 8) LAUNCH(1024, 8);                     \
+        else if (c_ <= 16) LAUNCH(1024, 16);                   \
+        else if (c_ <= 32) LAUNCH(1024, 32);                   \
+        else LAUNCH(1024, 64);                                 \
     } while (0)
 
 hipError_t launch_topk(const Dims &D, const float *scores, int64_t NB, int32_t *ids,
@@ -750,11 +762,7 @@ hipError_t launch_topk(const Dims &D, const float *scores, int64_t NB, int32_t *
 #define OASIS_TOPK(NT_, CM_)                                                                    \
     OASIS_LAUNCH((topk_kernel<NT_, CM_>), grid, dim3(NT_), 0, st, scores, D.NBmax,      \
                        (int)NB, D.K, ids, ids_copy, err)
-    if (NB <= 256 * 64) {
-        OASIS_CMAX_DISPATCH(256, (NB + 255) / 256, OASIS_TOPK);
-    } else {
-        OASIS_CMAX_DISPATCH(1024, (NB + 1023) / 1024, OASIS_TOPK);
-    }
+    OASIS_TOPK_DISPATCH(NB, OASIS_TOPK);
 #undef OASIS_TOPK
     return hipGetLastError();
 }
@@ -791,11 +799,7 @@ hipError_t launch_topk_select(const Dims &D, const float *scores, int64_t NB, in
                        (int)NB, ids, slot_block, last_used, block_slot, D.K, D.S, D.NBmax, cap, \
                        t, fetch_block, fetch_slot, att_block, att_slot, counts, stats, err,      \
                        D.attend_all ? 1 : 0)
-    if (NB <= 256 * 64) {
-        OASIS_CMAX_DISPATCH(256, (NB + 255) / 256, OASIS_TS);
-    } else {
-        OASIS_CMAX_DISPATCH(1024, (NB + 1023) / 1024, OASIS_TS);
-    }
+    OASIS_TOPK_DISPATCH(NB, OASIS_TS);
 #undef OASIS_TS
     return hipGetLastError();
 }
@@ -826,26 +830,38 @@ hipError_t launch_score_topk_select(const Dims &D, const void *summ, const void 
     if (!score_topk_fusable(D, NB, Q)) return hipErrorInvalidValue;
     const int QT = (Q + 31) / 32;
     const size_t lds = fused_lds_bytes(D, NB);
-    const int C = (int)((NB + 255) / 256);
     const dim3 grid((unsigned)D.units());
-#define OASIS_STS(QT_, CM_)                                                                      \
-    OASIS_LAUNCH((score_topk_select_kernel<128, QT_, CM_>), grid, dim3(256), lds, st,            \
+    // 8 waves once the keys outgrow 8 per thread, where the query rows leave
+    // the registers for it (at most two 32-row MFMA tiles)
+    const int nt = (QT <= 2 && NB > 2048) ? 512 : 256;
+    const int C = (int)((NB + nt - 1) / nt);
+#define OASIS_STS(QT_, CM_, NT_)                                                                 \
+    OASIS_LAUNCH((score_topk_select_kernel<128, QT_, CM_, NT_>), grid, dim3(NT_), lds, st,       \
                  (const uint16_t *)summ, (const uint16_t *)q, (const uint16_t *)drafts, n_drafts, \
                  qskip, scores, D.B, D.Hq, D.Hkv, D.G, D.summ_unit_elems(), (int)NB, ids,         \
                  slot_block, last_used, block_slot, D.K, D.S, D.NBmax, cap, t, fetch_block,       \
                  fetch_slot, att_block, att_slot, counts, stats, err, D.attend_all ? 1 : 0)
-#define OASIS_STS_C(QT_)                   \
-    do {                                   \
-        if (C <= 4) OASIS_STS(QT_, 4);     \
-        else if (C <= 8) OASIS_STS(QT_, 8); \
-        else if (C <= 16) OASIS_STS(QT_, 16); \
-        else OASIS_STS(QT_, 32);           \
+#define OASIS_STS_SMALL(QT_)                         \
+    do {                                             \
+        if (nt == 512) {                             \
+            if (C <= 8) OASIS_STS(QT_, 8, 512);      \
+            else OASIS_STS(QT_, 16, 512);            \
+        } else if (C <= 4) OASIS_STS(QT_, 4, 256);   \
+        else OASIS_STS(QT_, 8, 256);                 \
     } while (0)
-    if (QT == 1) OASIS_STS_C(1);
-    else if (QT == 2) OASIS_STS_C(2);
-    else if (QT == 3) OASIS_STS_C(3);
-    else OASIS_STS_C(4);
-#undef OASIS_STS_C
+#define OASIS_STS_LARGE(QT_)                  \
+    do {                                      \
+        if (C <= 4) OASIS_STS(QT_, 4, 256);   \
+        else if (C <= 8) OASIS_STS(QT_, 8, 256); \
+        else if (C <= 16) OASIS_STS(QT_, 16, 256); \
+        else OASIS_STS(QT_, 32, 256);         \
+    } while (0)
+    if (QT == 1) OASIS_STS_SMALL(1);
+    else if (QT == 2) OASIS_STS_SMALL(2);
+    else if (QT == 3) OASIS_STS_LARGE(3);
+    else OASIS_STS_LARGE(4);
+#undef OASIS_STS_LARGE
+#undef OASIS_STS_SMALL
 #undef OASIS_STS
     return hipGetLastError();
 }
