@@ -176,6 +176,8 @@ def main():
                          "(b, KV head) and step (0: attention over the prefetched set)")
     ap.add_argument("--fuse-score-topk", action="store_true",
                     help="score, top-K and select in one kernel where the shape allows")
+    ap.add_argument("--no-fused-leg", action="store_true",
+                    help="single layers: skip the second timed leg with score, top-K and select fused")
     ap.add_argument("--sweep", action="store_true",
                     help="multi-layer workloads: one line per fetch ratio of the sweep")
     args = ap.parse_args()
@@ -209,7 +211,13 @@ def main():
     if args.fetch_ratio is not None:
         w = w.with_(fetch_ratio=1.0 if args.fetch_ratio == "all" else float(args.fetch_ratio),
                     cap=0)
-    n_steps = args.warmup + args.steps
+    # a second timed leg on the same handle, with score, top-K and select in
+    # one kernel, where that kernel applies (tiled bf16 d = 128, >= 256 units)
+    fused_leg = (not args.fuse_score_topk and not args.no_fused_leg and not w.lookahead and
+                 not args.no_kernel_timing and w.dtype == synth.BF16 and w.head_dim == 128 and
+                 w.batch * w.kv_heads >= 256)
+    n_main = args.warmup + args.steps
+    n_steps = n_main + (args.steps if fused_leg else 0)
     t_setup = time.perf_counter()
     run = LayerRunner(w, n_steps)
     h = run.h
@@ -244,7 +252,7 @@ def main():
 
     torch.cuda.synchronize()
     t0 = time.perf_counter()
-    for t in range(args.warmup + 1, n_steps + 1):
+    for t in range(args.warmup + 1, n_main + 1):
         step(t, stream)
     torch.cuda.synchronize()
     dt = time.perf_counter() - t0
@@ -261,7 +269,7 @@ def main():
     d, bs = w.head_dim, w.block_size
     blk_bytes = 2 * bs * d * e
     # algorithmic bytes per launch
-    nb_avg = np.mean([w.blocks_at(w.prefix_tokens + t) for t in range(args.warmup + 1, n_steps + 1)])
+    nb_avg = np.mean([w.blocks_at(w.prefix_tokens + t) for t in range(args.warmup + 1, n_main + 1)])
     q_bytes = w.batch * w.q_heads * d * e
     score_bytes = units * nb_avg * 2 * d * e + q_bytes * (1 + w.drafts) + units * nb_avg * 4
     attended = (stats1["attended"] - stats0["attended"]) / K
@@ -348,6 +356,28 @@ def main():
                            "period": args.timing_period},
         "attended_blocks_per_step": attended,
     }
+    if fused_leg:
+        h.oasis_set_score_topk_fusion(True)
+        h.oasis_set_timing(TIME["score"] | TIME["select"])
+        h.oasis_set_timing_period(args.timing_period)
+        torch.cuda.synchronize()
+        t0 = time.perf_counter()
+        for t in range(n_main + 1, n_steps + 1):
+            step(t, stream)
+        torch.cuda.synchronize()
+        dt2 = time.perf_counter() - t0
+        tm2 = h.oasis_get_timing()
+        h.oasis_check()
+        if tm2["n_select"] == 0 and tm2["n_score"] > 0:
+            ms_f = tm2["ms_score"] / tm2["n_score"]
+            f_gbps = score_bytes / (ms_f * 1e-3) / 1e9
+            line["fused_score_topk"] = {
+                "value": K / dt2, "ms_per_step": dt2 / K * 1e3,
+                "kernel": "oasis_score_topk_select", "avg_ms": ms_f,
+                "achieved_gbps": f_gbps, "frac": f_gbps / HBM_PEAK_GBPS,
+                "traffic": stored_traffic("oasis_score_topk_select", w.name),
+                "steps": K, "note": "same handle, the K steps after the main timed region, "
+                "score + top-K + select in one kernel (bit-identical results)"}
     if verify is not None:
         verify["attended_blocks"] = attended
         verify["hbm_gbps"] = (verify["passes"] * attended * blk_bytes) / (verify["avg_ms"] * 1e-3) / 1e9

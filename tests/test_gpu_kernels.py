@@ -32,8 +32,11 @@ def _zeros_prefix(h, T, d, batch=1, hkv=1, dtype=np.float32):
     h.oasis_load_prefix(z, z, T)
 
 
-@pytest.mark.parametrize("nb,k,seed", [(1, 8, 0), (5, 8, 1), (300, 128, 2), (2052, 128, 3),
-                                       (8196, 128, 4), (20000, 256, 5), (4096, 1024, 6)])
+# block counts across the workgroup shapes (256 / 512 / 1,024 threads, 4 to 64
+# keys per thread), the largest pool, and K above the one-wave sort
+@pytest.mark.parametrize("nb,k,seed", [(1, 8, 0), (5, 8, 1), (300, 128, 2), (1500, 128, 8),
+                                       (2048, 64, 9), (2052, 128, 3), (8196, 128, 4),
+                                       (20000, 256, 5), (4096, 1024, 6), (65536, 128, 7)])
 def test_topk_matches_oracle_with_ties(nb, k, seed):
     bs, d, units = 16, 8, 3
     h = _handle(batch=units, hq=1, hkv=1, d=d, max_tokens=nb * bs, budget=k * bs)

@@ -354,3 +354,27 @@ def test_attend_all_resident_with_fusion_full_size():
     rep = FreeRunning(w, 8, [(0, 0), (13, 2), (31, 7)]).run_free(check_payload_every=4, fuse=True,
                                                                   attend_all=True)
     log(f"{w.name} attend-all fused: {rep}")
+
+
+@pytest.mark.parametrize("q_heads,drafts,prefix", [(128, 4, 16 * 300 + 5), (128, 7, 16 * 300 + 5),
+                                                   (128, 4, 16 * 2100 + 3)])
+def test_score_topk_fusion_query_row_tiles(q_heads, drafts, prefix):
+    """G = 16 with 5 and 8 query sets (80 and 128 rows: three and four 32-row
+    tiles per unit), short and 2,100-block contexts: fused equals separate."""
+    from lookahead_sparse_kv_oasis_amd.runner import LayerRunner
+    w = synth.QWEN3_8B.with_(q_heads=q_heads, drafts=drafts, prefix_tokens=prefix)
+    n = 4
+    a, b = LayerRunner(w, n), LayerRunner(w, n)
+    a.h.oasis_set_score_topk_fusion(True)
+    for r in (a, b):
+        r.admission()
+    for t in range(1, n + 1):
+        for r in (a, b):
+            r.step(t)
+        torch.cuda.synchronize()
+        assert torch.equal(a.out, b.out), f"step {t}: outputs differ"
+        assert np.array_equal(a.h.read("SCORES", np.float32), b.h.read("SCORES", np.float32))
+        sa, sb = _state(a.h), _state(b.h)
+        for k in sa:
+            assert np.array_equal(sa[k], sb[k]), f"step {t}: {k} differs"
+    a.h.oasis_check()
