@@ -467,13 +467,13 @@ int create_handle(const oasis_layout *layout, int32_t block_size, int32_t budget
               dmal((void **)&h->part_l, sizeof(float) * units * NS * G) &&
               dmal((void **)&h->part_acc, sizeof(float) * units * NS * G * D.d) &&
               dmal((void **)&h->err, sizeof(uint32_t)) &&
-              dmal((void **)&h->stats, sizeof(DevStats));
+              dmal((void **)&h->stats, sizeof(DevStats) * units);
     if (!ok) return bail(OASIS_E_NOMEM);
     if (hipMemset(h->summ, 0, summ_bytes) != hipSuccess ||
         hipMemset(h->slots, 0, (size_t)units * S * D.block_elems() * e) != hipSuccess ||
         hipMemset(h->scores, 0, sizeof(float) * units * NBmax) != hipSuccess ||
         hipMemset(h->err, 0, sizeof(uint32_t)) != hipSuccess ||
-        hipMemset(h->stats, 0, sizeof(DevStats)) != hipSuccess)
+        hipMemset(h->stats, 0, sizeof(DevStats) * units) != hipSuccess)
         return bail(OASIS_E_HIP);
     if (reset_tables(h) != OASIS_OK) return bail(OASIS_E_HIP);
     if (hipStreamCreateWithFlags(&h->copy, hipStreamNonBlocking) != hipSuccess ||
@@ -1063,8 +1063,16 @@ extern "C" int oasis_read(oasis_t *h, int32_t which, int64_t offset, int64_t nby
 extern "C" int oasis_get_stats(oasis_t *h, oasis_stats *out) {
     if (!h || !out) return OASIS_E_INVAL;
     HIP_OK(h, hipDeviceSynchronize());
-    DevStats s;
-    HIP_OK(h, hipMemcpy(&s, h->stats, sizeof s, hipMemcpyDeviceToHost));
+    std::vector<DevStats> rows((size_t)h->D.units());
+    HIP_OK(h, hipMemcpy(rows.data(), h->stats, sizeof(DevStats) * rows.size(),
+                        hipMemcpyDeviceToHost));
+    DevStats s{};
+    for (const DevStats &r : rows) {
+        s.hits += r.hits;
+        s.misses += r.misses;
+        s.fetched += r.fetched;
+        s.attended += r.attended;
+    }
     out->steps = h->n_select;
     out->hits = (int64_t)s.hits;
     out->misses = (int64_t)s.misses;

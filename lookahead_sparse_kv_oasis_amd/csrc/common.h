@@ -17,7 +17,8 @@ enum : uint32_t {
     kErrSlots = 4u,       // not enough slots for the fetch (S < K misuse)
 };
 
-// Counters kept on the device, summed by oasis_get_stats.
+// Counters kept on the device, one row per (b, KV head) unit, summed over the
+// units by oasis_get_stats.
 struct DevStats {
     unsigned long long hits, misses, fetched, attended;
 };

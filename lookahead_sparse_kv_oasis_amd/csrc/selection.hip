@@ -52,6 +52,46 @@ __device__ __forceinline__ uint32_t order_key(float f, bool &bad) {
     return (b & 0x80000000u) ? ~b : (b | 0x80000000u);
 }
 
+// Lane (lane ^ J)'s value.  J < 16 stays inside a 16-lane row and goes
+// through DPP: quad_perm [1,0,3,2] and [2,3,0,1] for 1 and 2, row_shl:4 /
+// row_shr:4 chosen by lane bit 2 for 4, row_ror:8 for 8.  J = 16, 32 use a
+// cross-lane shuffle.
+template <int J> __device__ __forceinline__ uint32_t lane_xor_u32(uint32_t v) {
+    const int x = (int)v;
+    if constexpr (J == 1) {
+        return (uint32_t)__builtin_amdgcn_update_dpp(0, x, 0xB1, 0xF, 0xF, false);
+    } else if constexpr (J == 2) {
+        return (uint32_t)__builtin_amdgcn_update_dpp(0, x, 0x4E, 0xF, 0xF, false);
+    } else if constexpr (J == 4) {
+        const int up = __builtin_amdgcn_update_dpp(0, x, 0x104, 0xF, 0xF, false);  // lane + 4
+        const int dn = __builtin_amdgcn_update_dpp(0, x, 0x114, 0xF, 0xF, false);  // lane - 4
+        return (uint32_t)((threadIdx.x & 4) ? dn : up);
+    } else if constexpr (J == 8) {
+        return (uint32_t)__builtin_amdgcn_update_dpp(0, x, 0x128, 0xF, 0xF, false);
+    } else {
+        return (uint32_t)__shfl_xor(x, J, 64);
+    }
+}
+template <int J> __device__ __forceinline__ unsigned long long lane_xor_u64(unsigned long long v) {
+    const uint32_t lo = lane_xor_u32<J>((uint32_t)v), hi = lane_xor_u32<J>((uint32_t)(v >> 32));
+    return ((unsigned long long)hi << 32) | lo;
+}
+
+// Inclusive suffix sum over the lanes of a wave (lane l: sum of lanes >= l):
+// row_shl 1, 2, 4, 8 inside each 16-lane row, then the totals of the rows
+// above, read from their first lanes.
+__device__ __forceinline__ uint32_t wave_suffix_sum_u32(uint32_t v) {
+    v += (uint32_t)__builtin_amdgcn_update_dpp(0, (int)v, 0x101, 0xF, 0xF, false);
+    v += (uint32_t)__builtin_amdgcn_update_dpp(0, (int)v, 0x102, 0xF, 0xF, false);
+    v += (uint32_t)__builtin_amdgcn_update_dpp(0, (int)v, 0x104, 0xF, 0xF, false);
+    v += (uint32_t)__builtin_amdgcn_update_dpp(0, (int)v, 0x108, 0xF, 0xF, false);
+    const uint32_t t1 = (uint32_t)__builtin_amdgcn_readlane((int)v, 16);
+    const uint32_t t2 = (uint32_t)__builtin_amdgcn_readlane((int)v, 32);
+    const uint32_t t3 = (uint32_t)__builtin_amdgcn_readlane((int)v, 48);
+    const int row = (threadIdx.x & 63) >> 4;
+    return v + (row < 1 ? t1 : 0u) + (row < 2 ? t2 : 0u) + (row < 3 ? t3 : 0u);
+}
+
 template <int NT>
 __device__ __forceinline__ int block_excl_scan(int v, int *sh) {
     const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
@@ -144,6 +184,7 @@ __device__ void topk_unit(TopkKeys<CMAX> &kk, int NB, int K, int32_t *__restrict
         red_mn[wave] = lmn;
     }
     for (int i = tid; i < Kp; i += NT) rank_sh[i] = 0;
+    for (int i = tid; i < 256; i += NT) hist[0][i] = 0u;
     __syncthreads();
     uint32_t kmax = 0u, kmin = 0xFFFFFFFFu;
 #pragma unroll
@@ -164,14 +205,15 @@ __device__ void topk_unit(TopkKeys<CMAX> &kk, int NB, int K, int32_t *__restrict
         const int width = hi < 8 ? hi : 8;
         const int sh = hi - width;
         const uint32_t fixed = hi >= 32 ? 0u : ~((1u << hi) - 1u);
-        for (int i = tid; i < 256; i += NT) hist[cur][i] = 0u;
-        __syncthreads();
+        // hist[cur] was cleared before the previous barrier; the other
+        // buffer, read by the previous pass's scan, is cleared for the next
 #pragma unroll
         for (int i = 0; i < CMAX; ++i) {
             const int id = begin + i;
             if (i < C && id < NB && (key[i] & fixed) == prefix)
                 atomicAdd(&hist[cur][(key[i] >> sh) & ((1u << width) - 1u)], 1u);
         }
+        for (int i = tid; i < 256; i += NT) hist[cur ^ 1][i] = 0u;
         __syncthreads();
         if (wave == 0) {
             // suffix sums over the 256 bins, four per lane, highest digit first
@@ -179,12 +221,7 @@ __device__ void topk_unit(TopkKeys<CMAX> &kk, int NB, int K, int32_t *__restrict
 #pragma unroll
             for (int j = 0; j < 4; ++j) h[j] = hist[cur][4 * lane + j];
             const uint32_t mine = h[0] + h[1] + h[2] + h[3];
-            uint32_t suf = mine;  // lanes >= this one
-#pragma unroll
-            for (int o = 1; o < 64; o <<= 1) {
-                const uint32_t y = __shfl_down(suf, o, 64);
-                if (lane + o < 64) suf += y;
-            }
+            const uint32_t suf = wave_suffix_sum_u32(mine);  // lanes >= this one
             uint32_t above = suf - mine;
 #pragma unroll
             for (int j = 3; j >= 0; --j) {
@@ -263,7 +300,8 @@ __device__ void topk_unit(TopkKeys<CMAX> &kk, int NB, int K, int32_t *__restrict
     if (Kp <= 128) {
         // one wave sorts the winners: 64-bit composites (key, ~id) in
         // descending order are (score desc, id asc); two per lane, element
-        // e * 64 + lane, bitonic network, cross-lane pairs by shuffles
+        // e * 64 + lane, bitonic network, cross-lane pairs through DPP and
+        // shuffles
         if (wave == 0) {
             unsigned long long v[2];
 #pragma unroll
@@ -272,11 +310,13 @@ __device__ void topk_unit(TopkKeys<CMAX> &kk, int NB, int K, int32_t *__restrict
                 v[e] = i < Kp ? ((unsigned long long)ckey[i] << 32) | (uint32_t)~(uint32_t)cid[i]
                               : 0ull;  // sorts last: no finite score has key 0
             }
-#pragma unroll
-            for (int k = 2; k <= 128; k <<= 1) {
-#pragma unroll
-                for (int j = k >> 1; j > 0; j >>= 1) {
-                    if (j == 64) {  // partner is the lane's other element
+            // k = 2^kk is the size of the sorted runs being merged, j = 2^jj the
+            // compare distance; distances below 16 exchange through DPP
+            static_for<1, 8>([&](auto kkI) {
+                constexpr int kk = decltype(kkI)::value, k = 1 << kk;
+                static_for<0, kk>([&](auto tI) {
+                    constexpr int j = 1 << (kk - 1 - decltype(tI)::value);
+                    if constexpr (j == 64) {  // partner is the lane's other element
                         // element 0 has bit 64 clear: it keeps the larger
                         // value when the block (bit k = 128) sorts descending
                         const unsigned long long a = v[0], b = v[1];
@@ -286,7 +326,7 @@ __device__ void topk_unit(TopkKeys<CMAX> &kk, int NB, int K, int32_t *__restrict
 #pragma unroll
                         for (int e = 0; e < 2; ++e) {
                             const int i = e * 64 + lane;
-                            const unsigned long long o = __shfl_xor(v[e], j, 64);
+                            const unsigned long long o = lane_xor_u64<j>(v[e]);
                             // descending overall: the pair's lower index keeps the
                             // larger value in blocks with (i & k) == 0
                             const bool lower = (i & j) == 0;
@@ -295,8 +335,8 @@ __device__ void topk_unit(TopkKeys<CMAX> &kk, int NB, int K, int32_t *__restrict
                             v[e] = keep_max ? (v[e] > o ? v[e] : o) : (v[e] < o ? v[e] : o);
                         }
                     }
-                }
-            }
+                });
+            });
 #pragma unroll
             for (int e = 0; e < 2; ++e) {
                 const int r = e * 64 + lane;
@@ -567,10 +607,14 @@ __device__ void select_unit(int64_t u, const int32_t *sel, const int32_t *sb_in,
         counts[u * 4 + 1] = nh;
         counts[u * 4 + 2] = n;
         counts[u * 4 + 3] = nm;
-        atomicAdd(&stats->hits, (unsigned long long)nh);
-        atomicAdd(&stats->misses, (unsigned long long)nm);
-        atomicAdd(&stats->fetched, (unsigned long long)n);
-        atomicAdd(&stats->attended, (unsigned long long)(nh + nr + n));
+        // the unit's own counters: one workgroup per unit and the handle's
+        // selects run in order, so no atomics (1,024 same-address atomics per
+        // launch at 256 units held the kernel's end for microseconds)
+        DevStats &su = stats[u];
+        su.hits += (unsigned long long)nh;
+        su.misses += (unsigned long long)nm;
+        su.fetched += (unsigned long long)n;
+        su.attended += (unsigned long long)(nh + nr + n);
     }
 }
 
