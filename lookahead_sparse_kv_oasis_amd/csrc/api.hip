@@ -119,6 +119,11 @@ struct oasis_handle {
     hipStream_t copy = nullptr;
     Mark m_append, m_select, m_gather, m_attn;
     hipEvent_t ev_fork = nullptr, ev_join = nullptr;   // oasis_decode_layers
+    // The marks are recorded only once the handle's work has used two
+    // streams; until then stream order is all the ordering there is.
+    bool multi = false;
+    bool have_last = false;
+    hipStream_t last_st = nullptr;
 
     int64_t n_select = 0;
     int32_t timing = 0;  // mask of timed kernel classes
@@ -170,9 +175,31 @@ bool aligned16(const void *p) { return ((uintptr_t)p & 15u) == 0; }
 
 // Record m on st.
 int mark(oasis_t *h, Mark &m, hipStream_t st) {
+    if (!h->multi) return OASIS_OK;  // one stream so far: nothing waits across streams
     HIP_OK(h, hipEventRecord(m.ev, st));
     m.st = st;
     m.set = true;
+    return OASIS_OK;
+}
+
+// Note that the handle's next work goes to st.  The first time that differs
+// from the stream used so far, every mark is recorded there (covering all the
+// work queued until now) and from then on each step records its marks.  A
+// record costs the GPU a few microseconds before the next kernel, so a caller
+// that keeps a handle on one stream pays for none.  The synchronous internal
+// uses of the copy stream (prompt load, state set, reads) follow a device
+// synchronization and end with one, so they do not count.
+int use_stream(oasis_t *h, hipStream_t st) {
+    if (h->multi) return OASIS_OK;
+    if (!h->have_last) {
+        h->have_last = true;
+        h->last_st = st;
+        return OASIS_OK;
+    }
+    if (st == h->last_st) return OASIS_OK;
+    h->multi = true;
+    for (Mark *m : {&h->m_append, &h->m_select, &h->m_gather, &h->m_attn})
+        if (int rc = mark(h, *m, h->last_st)) return rc;
     return OASIS_OK;
 }
 
@@ -476,13 +503,19 @@ int create_handle(const oasis_layout *layout, int32_t block_size, int32_t budget
         hipMemset(h->stats, 0, sizeof(DevStats) * units) != hipSuccess)
         return bail(OASIS_E_HIP);
     if (reset_tables(h) != OASIS_OK) return bail(OASIS_E_HIP);
+    // The ordering events are only waited on by other streams of this GPU,
+    // never by the host, and every kernel already ends with a device-wide
+    // release of its writes.  Without the flag each record performed a
+    // system-scope cache writeback and invalidate that left the GPU idle for
+    // about 5.7 us before the next kernel (three records per decode step).
+    constexpr unsigned kMarkFlags = hipEventDisableTiming | hipEventDisableSystemFence;
     if (hipStreamCreateWithFlags(&h->copy, hipStreamNonBlocking) != hipSuccess ||
-        hipEventCreateWithFlags(&h->m_append.ev, hipEventDisableTiming) != hipSuccess ||
-        hipEventCreateWithFlags(&h->m_select.ev, hipEventDisableTiming) != hipSuccess ||
-        hipEventCreateWithFlags(&h->m_gather.ev, hipEventDisableTiming) != hipSuccess ||
-        hipEventCreateWithFlags(&h->m_attn.ev, hipEventDisableTiming) != hipSuccess ||
-        hipEventCreateWithFlags(&h->ev_fork, hipEventDisableTiming) != hipSuccess ||
-        hipEventCreateWithFlags(&h->ev_join, hipEventDisableTiming) != hipSuccess)
+        hipEventCreateWithFlags(&h->m_append.ev, kMarkFlags) != hipSuccess ||
+        hipEventCreateWithFlags(&h->m_select.ev, kMarkFlags) != hipSuccess ||
+        hipEventCreateWithFlags(&h->m_gather.ev, kMarkFlags) != hipSuccess ||
+        hipEventCreateWithFlags(&h->m_attn.ev, kMarkFlags) != hipSuccess ||
+        hipEventCreateWithFlags(&h->ev_fork, kMarkFlags) != hipSuccess ||
+        hipEventCreateWithFlags(&h->ev_join, kMarkFlags) != hipSuccess)
         return bail(OASIS_E_HIP);
     if (hipDeviceSynchronize() != hipSuccess) return bail(OASIS_E_HIP);
     *out = h;
@@ -627,6 +660,7 @@ extern "C" int oasis_append_kv(oasis_t *h, const void *k_dev, const void *v_dev,
     if (h->T >= h->L.max_tokens)
         return fail(h, OASIS_E_CAPACITY, "append: sequence already holds max_tokens = %lld",
                     (long long)h->L.max_tokens);
+    TRY(use_stream(h, stream));
     TRY(after(h, stream, h->m_gather));
     TRY(after(h, stream, h->m_attn));
     TRY(flush_fetch(h, stream));
@@ -654,6 +688,7 @@ extern "C" int oasis_predict(oasis_t *h, const void *q_dev, const void *drafts_d
     const int64_t NB = nb_of(h);
     if (NB == 0) return fail(h, OASIS_E_STATE, "predict: no tokens loaded");
     const Dims &D = h->D;
+    TRY(use_stream(h, stream));
     TRY(after(h, stream, h->m_append));
     TRY(after(h, stream, h->m_select));  // the previous select reads the scores
     h->score_pending = false;
@@ -691,6 +726,7 @@ extern "C" int oasis_topk_from_scores(oasis_t *h, const float *scores_dev,
     if (!h || !scores_dev) return h ? fail(h, OASIS_E_INVAL, "topk: null scores") : OASIS_E_INVAL;
     const int64_t NB = nb_of(h);
     if (NB == 0) return fail(h, OASIS_E_STATE, "topk: no tokens loaded");
+    TRY(use_stream(h, stream));
     LAUNCH(h, TM_TOPK, stream,
            launch_topk(h->D, scores_dev, NB, h->ids, block_ids_dev, h->err, stream));
     h->topk_pending = false;
@@ -712,6 +748,7 @@ int select_impl(oasis_t *h, int32_t cap, hipStream_t stream, bool eager, hipStre
     if (cap > D.K) cap = D.K;
     const int64_t t64 = h->T - h->T_prefix;
     if (t64 > INT32_MAX - 1) return fail(h, OASIS_E_CAPACITY, "step index overflow");
+    TRY(use_stream(h, stream));
     TRY(after(h, stream, h->m_gather));
     TRY(after(h, stream, h->m_attn));
     TRY(flush_fetch(h, stream));
@@ -746,6 +783,7 @@ int select_impl(oasis_t *h, int32_t cap, hipStream_t stream, bool eager, hipStre
         h->fetch_pending = cap > 0;
     } else if (cap > 0) {
         hipStream_t g = gst ? gst : h->copy;
+        TRY(use_stream(h, g));
         TRY(after(h, g, h->m_select));
         LAUNCH(h, TM_GATHER, g,
                launch_gather(D, h->host_kv_dev, h->slots, h->fetch_block, h->fetch_slot, D.K,
@@ -777,6 +815,7 @@ extern "C" int oasis_evict(oasis_t *h, const int32_t *blocks_host, const int32_t
         h->evict_cap = n;
     }
     int32_t *dblocks = h->evict_buf, *dcounts = h->evict_buf + (size_t)D.units() * max_per_unit;
+    TRY(use_stream(h, stream));
     TRY(after(h, stream, h->m_gather));
     TRY(after(h, stream, h->m_attn));
     TRY(flush_fetch(h, stream));
@@ -795,6 +834,7 @@ extern "C" int oasis_sparse_attn(oasis_t *h, const void *q_dev, float *out_dev,
         return h ? fail(h, OASIS_E_INVAL, "attn: null or misaligned pointer") : OASIS_E_INVAL;
     if (!h->selected) return fail(h, OASIS_E_STATE, "attention before select");
     const Dims &D = h->D;
+    TRY(use_stream(h, stream));
     TRY(after(h, stream, h->m_select));
     TRY(after(h, stream, h->m_gather));
     int mode = 0, nsf = 0;
@@ -843,6 +883,7 @@ extern "C" int oasis_sparse_attn_verify(oasis_t *h, const void *q_dev, const voi
                 hipSuccess)
             return fail(h, OASIS_E_NOMEM, "verify: scratch allocation failed");
     }
+    TRY(use_stream(h, stream));
     TRY(after(h, stream, h->m_select));
     TRY(after(h, stream, h->m_gather));
     TRY(flush_fetch(h, stream));  // every attended block resident before the passes
@@ -938,9 +979,11 @@ extern "C" int oasis_decode_layers_ahead(oasis_t *const *layers, const oasis_lay
     }
     oasis_t *h0 = layers[0];
     // side and xfer see the caller's earlier work
-    HIP_OK(h0, hipEventRecord(h0->ev_fork, stream));
-    HIP_OK(h0, hipStreamWaitEvent(side, h0->ev_fork, 0));
-    HIP_OK(h0, hipStreamWaitEvent(xfer, h0->ev_fork, 0));
+    if (side != stream || xfer != stream) {
+        HIP_OK(h0, hipEventRecord(h0->ev_fork, stream));
+        if (side != stream) HIP_OK(h0, hipStreamWaitEvent(side, h0->ev_fork, 0));
+        if (xfer != stream) HIP_OK(h0, hipStreamWaitEvent(xfer, h0->ev_fork, 0));
+    }
     int rc = OASIS_OK, bad = -1;
     for (int32_t l = 0; l < n_layers && rc == OASIS_OK; ++l) {
         oasis_t *h = layers[l];
@@ -1123,6 +1166,7 @@ extern "C" int oasis_set_score_topk_fusion(oasis_t *h, int32_t on) {
     if (!h) return OASIS_E_INVAL;
     h->fuse_score = on != 0;
     if (!h->fuse_score && h->score_pending) {
+        HIP_OK(h, hipDeviceSynchronize());  // the work the deferred score follows
         TRY(flush_score(h, h->copy));
         HIP_OK(h, hipStreamSynchronize(h->copy));
     }

@@ -207,3 +207,30 @@ def test_lookahead_executor_with_miss_correction_matches_one_stream():
             assert np.array_equal(a.handles[l].read(buf), b.handles[l].read(buf)), f"{l} {buf}"
     a.close()
     b.close()
+
+
+def test_handle_moving_to_a_second_stream_midway_matches_one_stream():
+    """A handle driven on one stream records no ordering events; when its
+    predict / select move to a second stream at step 4 (and back for the
+    attention), the first cross-stream call orders everything queued before
+    it: outputs and tables stay bit-identical to the all-one-stream run."""
+    from lookahead_sparse_kv_oasis_amd.runner import LayerRunner
+    w = synth.QWEN3_8B.with_(batch=4, prefix_tokens=16 * 300 + 5, budget_tokens=16 * 64)
+    n = 8
+    a, b = LayerRunner(w, n), LayerRunner(w, n)
+    cur, s2 = torch.cuda.current_stream(), torch.cuda.Stream()
+    a.admission()
+    b.admission()
+    for t in range(1, n + 1):
+        for r, other in ((a, s2 if t >= 4 else cur), (b, cur)):
+            h = r.h
+            h.oasis_append_kv(r.app_k[t - 1], r.app_v[t - 1], stream=cur)
+            h.oasis_predict(r.q_steps[t], r.drafts[t], w.drafts, stream=other)
+            h.oasis_select_and_fetch(r.cap, stream=other)
+            h.oasis_sparse_attn(r.q_steps[t], r.out, stream=cur)
+        torch.cuda.synchronize()
+        assert torch.equal(a.out, b.out), f"step {t}: outputs differ"
+    for buf in STATE_BUFS:
+        assert np.array_equal(a.h.read(buf), b.h.read(buf)), buf
+    assert np.array_equal(a.h.read("SLOTS", np.uint8), b.h.read("SLOTS", np.uint8))
+    a.h.oasis_check()
