@@ -378,3 +378,32 @@ def test_score_topk_fusion_query_row_tiles(q_heads, drafts, prefix):
         for k in sa:
             assert np.array_equal(sa[k], sb[k]), f"step {t}: {k} differs"
     a.h.oasis_check()
+
+
+# ------------------------------------------------------------------ degenerate and large pools
+
+def test_free_running_cap_zero_attends_hits_only():
+    """Cap 0 after an admission: nothing is fetched, the attended list is the
+    held selected blocks, and the attention runs over those alone."""
+    from tests.gpu_parity import FreeRunning, log
+    w = synth.QWEN3_8B.with_(batch=2, prefix_tokens=16 * 300 + 7, budget_tokens=16 * 64)
+    p = FreeRunning(w, 5, [(0, 0), (1, 7)])
+    p.cap = 0
+    rep = p.run_free()
+    log(f"cap 0: {rep}")
+    assert rep["fetched"] == 0
+
+
+@pytest.mark.parametrize("slots", [300, 2048])
+def test_free_running_full_slot_pools(slots):
+    """S > K slots per KV head, every slot held from the start: the admission
+    and every capped fetch evict, and with more than 256 slots the victims are
+    ranked by counting.  300 slots keep the tables in the top-K + select
+    kernel's LDS; 2,048 (the largest pool) do not, and the top-K and select
+    run as two kernels."""
+    from tests.gpu_parity import FreeRunning, log
+    w = synth.QWEN3_8B.with_(batch=2, prefix_tokens=16 * 2100 + 3, slots=slots,
+                             initial_resident_frac=1.0)
+    p = FreeRunning(w, 6, [(0, 0), (1, 5)])
+    rep = p.run_free()
+    log(f"{slots}-slot pool: {rep}")
