@@ -145,6 +145,14 @@ template <int G> struct AttnWave {
 #pragma unroll
         for (int r = 0; r < 4; ++r) vv[r] = gload16(p + voff + r * D);
     }
+    // The same from a resident slot in HBM, streamed (read once per step).
+    __device__ __forceinline__ void load_nt(uint4 (&kk)[4], uint4 (&vv)[4],
+                                            const uint16_t *p) const {
+#pragma unroll
+        for (int i = 0; i < 4; ++i) kk[i] = gload16_nt(p + koff + 32 * i);
+#pragma unroll
+        for (int r = 0; r < 4; ++r) vv[r] = gload16_nt(p + voff + r * D);
+    }
     __device__ __forceinline__ void store(uint16_t *p, const uint4 (&kk)[4],
                                           const uint4 (&vv)[4]) const {
 #pragma unroll
@@ -344,7 +352,7 @@ __global__ __launch_bounds__(256) void attn_mfma_kernel(
     if (ne > 0) {
         blk_cur = __builtin_amdgcn_readfirstlane(att_block[u * K + e_first]);
         const int32_t sl = __builtin_amdgcn_readfirstlane(att_slot[u * K + e_first]);
-        st.load(kr[0], vr[0], slots + (u * S + sl) * (int64_t)W::BLK);
+        st.load_nt(kr[0], vr[0], slots + (u * S + sl) * (int64_t)W::BLK);
     }
 #pragma unroll
     for (int j = 0; j < BPW; ++j) {
@@ -354,7 +362,7 @@ __global__ __launch_bounds__(256) void attn_mfma_kernel(
             const int e = e_first + 4 * (j + 1);
             blk_nx = __builtin_amdgcn_readfirstlane(att_block[u * K + e]);
             const int32_t sl = __builtin_amdgcn_readfirstlane(att_slot[u * K + e]);
-            st.load(kr[(j + 1) & 1], vr[(j + 1) & 1], slots + (u * S + sl) * (int64_t)W::BLK);
+            st.load_nt(kr[(j + 1) & 1], vr[(j + 1) & 1], slots + (u * S + sl) * (int64_t)W::BLK);
         }
         __builtin_amdgcn_sched_barrier(0);  // keep the prefetch ahead of the compute
         st.block(kr[j & 1], vr[j & 1], block_valid(T_, blk_cur), scale_log2);

@@ -43,7 +43,7 @@ template <int D, int QT> struct ScoreTiles {
     __device__ __forceinline__ void load(int64_t tile) {
         const uint16_t *src = ubase + tile * 64 * D;
 #pragma unroll
-        for (int i = 0; i < NI; ++i) bv[i] = __builtin_bit_cast(bf16x8, gload16(src + 512 * i));
+        for (int i = 0; i < NI; ++i) bv[i] = __builtin_bit_cast(bf16x8, gload16_nt(src + 512 * i));
     }
     // Rows: G heads x {current query (unless qskip), drafts}, sign-split.
     __device__ __forceinline__ void rows(const uint16_t *q, const uint16_t *drafts, int n_drafts,
