@@ -107,6 +107,8 @@ template <int g> __device__ __forceinline__ float row_bcast(float x) {
 //   broadcast delivers them.
 template <int G> struct AttnWave {
     static constexpr int D = 128, BS = 16, BLK = 2 * BS * D;
+    static constexpr int kStage = 8;  // LDS staging per wave (unused here)
+    uint16_t *vst = nullptr;
     int col, kg, koff, voff;
     bf16x8 qb[4];
     float m, lsum;
@@ -236,6 +238,161 @@ template <int G> struct AttnWave {
             }
         }
     }
+    // This wave's (reduced) state into LDS for the workgroup's merge.
+    __device__ __forceinline__ void stash(float (*sacc)[D], float *sm, float *sl) const {
+        if (kg == 0) {
+#pragma unroll
+            for (int g = 0; g < G; ++g)
+#pragma unroll
+                for (int e = 0; e < 8; ++e) sacc[g][8 * col + e] = acc[g][e];
+            sm[col] = m;
+            sl[col] = lsum;
+        }
+    }
+};
+
+// 16 heads per KV head (and the 16-row chunks of the verification
+// attention): P V on the matrix cores as well, v_mfma_f32_16x16x16_bf16 per
+// 16 output dimensions.  The probabilities of S^T already sit in the A-operand
+// order (lane l: head l % 16, tokens 4 (l / 16) + r); each is split into a
+// bf16 high part and the bf16 of the remainder, two products whose sum keeps
+// the relative error near 2^-16.  The B operand (lane l: dimension 16 n +
+// l % 16, tokens 4 (l / 16) + r) comes from the block's V rows staged in
+// LDS, rows past the valid tokens zeroed.  The output O[head][dim] sits in 8
+// accumulators per lane (lane l: dimension 16 n + l % 16, heads 4 (l / 16) +
+// r), 32 registers instead of the 128 the vector-ALU form needs for 16
+// heads, which had left one wave per SIMD.
+template <int G> struct AttnWaveM {
+    static_assert(G == 16, "16 heads fill the matrix rows");
+    static constexpr int D = 128, BS = 16, BLK = 2 * BS * D;
+    static constexpr int kStage = BS * D;  // bf16 elements staged per wave
+    int col, kg, koff, voff;
+    bf16x8 qb[4];
+    float m, lsum;
+    f32x4 o[8];
+    uint16_t *vst = nullptr;  // this wave's staging area in LDS
+
+    __device__ __forceinline__ void lanes() {
+        const int lane = threadIdx.x & 63;
+        col = lane & 15;
+        kg = lane >> 4;
+        koff = col * D + 8 * kg;
+        voff = BS * D + 4 * kg * D + 8 * col;
+    }
+    __device__ __forceinline__ void init(const uint16_t *q, int64_t b, int Hq, int h) {
+        const uint16_t *qr = q + (b * Hq + h * G + col) * D + 8 * kg;
+#pragma unroll
+        for (int i = 0; i < 4; ++i)
+            qb[i] = __builtin_bit_cast(bf16x8, *reinterpret_cast<const uint4 *>(qr + 32 * i));
+        reset();
+    }
+    __device__ __forceinline__ void reset() {
+        m = -INFINITY;
+        lsum = 0.f;
+#pragma unroll
+        for (int n = 0; n < 8; ++n) o[n] = f32x4{0.f, 0.f, 0.f, 0.f};
+    }
+    __device__ __forceinline__ void load(uint4 (&kk)[4], uint4 (&vv)[4], const uint16_t *p) const {
+#pragma unroll
+        for (int i = 0; i < 4; ++i) kk[i] = gload16(p + koff + 32 * i);
+#pragma unroll
+        for (int r = 0; r < 4; ++r) vv[r] = gload16(p + voff + r * D);
+    }
+    __device__ __forceinline__ void load_nt(uint4 (&kk)[4], uint4 (&vv)[4],
+                                            const uint16_t *p) const {
+#pragma unroll
+        for (int i = 0; i < 4; ++i) kk[i] = gload16_nt(p + koff + 32 * i);
+#pragma unroll
+        for (int r = 0; r < 4; ++r) vv[r] = gload16_nt(p + voff + r * D);
+    }
+    __device__ __forceinline__ void store(uint16_t *p, const uint4 (&kk)[4],
+                                          const uint4 (&vv)[4]) const {
+#pragma unroll
+        for (int c = 0; c < 4; ++c) gstore16(p + koff + 32 * c, kk[c]);
+#pragma unroll
+        for (int r = 0; r < 4; ++r) gstore16(p + voff + r * D, vv[r]);
+    }
+    __device__ __forceinline__ void block(const uint4 (&kk)[4], const uint4 (&vv)[4], int valid,
+                                          float scale_log2) {
+        f32x4 s4 = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+        for (int c = 0; c < 4; ++c)
+            s4 = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, kk[c]), qb[c],
+                                                         s4, 0, 0, 0);
+        float sr[4];
+#pragma unroll
+        for (int r = 0; r < 4; ++r) sr[r] = (4 * kg + r < valid) ? s4[r] * scale_log2 : -INFINITY;
+        float bm = fmaxf(fmaxf(sr[0], sr[1]), fmaxf(sr[2], sr[3]));
+        bm = fmaxf(bm, __shfl_xor(bm, 16, 64));
+        bm = fmaxf(bm, __shfl_xor(bm, 32, 64));
+        const float mn = fmaxf(m, bm);
+        const bool live = mn != -INFINITY;
+        const float alpha = live ? exp2f(m - mn) : 1.f;
+        float p[4];
+#pragma unroll
+        for (int r = 0; r < 4; ++r) p[r] = live ? exp2f(sr[r] - mn) : 0.f;
+        lsum = lsum * alpha + ((p[0] + p[1]) + (p[2] + p[3]));
+        m = mn;
+        // rescale the rows of O (heads 4 kg + r); head h's factor is in lane h
+#pragma unroll
+        for (int r = 0; r < 4; ++r) {
+            const float ar = __shfl(alpha, 4 * kg + r, 64);
+#pragma unroll
+            for (int n = 0; n < 8; ++n) o[n][r] *= ar;
+        }
+        // stage V (rows past the valid tokens zeroed: probability 0, bytes
+        // possibly anything); the previous block's reads are done first
+        wave_sync();
+#pragma unroll
+        for (int r = 0; r < 4; ++r) {
+            const uint4 w = (4 * kg + r < valid) ? vv[r] : make_uint4(0, 0, 0, 0);
+            *reinterpret_cast<uint4 *>(vst + (4 * kg + r) * D + 8 * col) = w;
+        }
+        wave_sync();
+        // P as bf16 high part + bf16 of the remainder
+        s16x4 ahi, alo;
+#pragma unroll
+        for (int r = 0; r < 4; ++r) {
+            const uint32_t hb = __float_as_uint(p[r]) & 0xFFFF0000u;
+            const float rest = p[r] - __uint_as_float(hb);
+            ahi[r] = (short)(hb >> 16);
+            alo[r] = (short)(__float_as_uint(rest) >> 16);
+        }
+#pragma unroll
+        for (int n = 0; n < 8; ++n) {
+            s16x4 bv;
+#pragma unroll
+            for (int r = 0; r < 4; ++r) bv[r] = (short)vst[(4 * kg + r) * D + 16 * n + col];
+            o[n] = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(ahi, bv, o[n], 0, 0, 0);
+            o[n] = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(alo, bv, o[n], 0, 0, 0);
+        }
+    }
+    // Sum the four token groups of lsum; O already holds all the tokens.
+    __device__ __forceinline__ void reduce() {
+        lsum += __shfl_xor(lsum, 16, 64);
+        lsum += __shfl_xor(lsum, 32, 64);
+    }
+    __device__ __forceinline__ void write_partial(int64_t pi0, float *part_m, float *part_l,
+                                                  float *part_acc) const {
+#pragma unroll
+        for (int n = 0; n < 8; ++n)
+#pragma unroll
+            for (int r = 0; r < 4; ++r) part_acc[(pi0 + 4 * kg + r) * D + 16 * n + col] = o[n][r];
+        if (kg == 0) {
+            part_m[pi0 + col] = m;
+            part_l[pi0 + col] = lsum;
+        }
+    }
+    __device__ __forceinline__ void stash(float (*sacc)[D], float *sm, float *sl) const {
+#pragma unroll
+        for (int n = 0; n < 8; ++n)
+#pragma unroll
+            for (int r = 0; r < 4; ++r) sacc[4 * kg + r][16 * n + col] = o[n][r];
+        if (kg == 0) {
+            sm[col] = m;
+            sl[col] = lsum;
+        }
+    }
 };
 
 __device__ __forceinline__ int block_valid(int64_t T, int32_t blk) {
@@ -264,12 +421,14 @@ __global__ __launch_bounds__(256) void attn_mfma_kernel(
     int Hkv, int K, int S, int64_t NBmax, int mode, int cap, int n_fetch_wg, int nsf_max,
     int ns1, int nsa, int64_t units, float scale_log2, float *__restrict__ part_m,
     float *__restrict__ part_l, float *__restrict__ part_acc) {
-    using W = AttnWave<G>;
+    using W = std::conditional_t<G == 16, AttnWaveM<G>, AttnWave<G>>;
     constexpr int D = W::D;
+    __shared__ __attribute__((aligned(16))) uint16_t vstage[4][W::kStage];
     // wave-uniform, so per-wave metadata comes through scalar loads
     const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
     W st;
     st.lanes();
+    st.vst = vstage[wave];
 
     if ((int64_t)blockIdx.x < n_fetch_wg) {
         const int64_t F = 4LL * n_fetch_wg;
@@ -369,14 +528,7 @@ __global__ __launch_bounds__(256) void attn_mfma_kernel(
         blk_cur = blk_nx;
     }
     st.reduce();
-    if (st.kg == 0) {
-#pragma unroll
-        for (int gg = 0; gg < G; ++gg)
-#pragma unroll
-            for (int e = 0; e < 8; ++e) sm_acc[wave][gg][8 * st.col + e] = st.acc[gg][e];
-        sm_m[wave][st.col] = st.m;
-        sm_l[wave][st.col] = st.lsum;
-    }
+    st.stash(sm_acc[wave], sm_m[wave], sm_l[wave]);
     __syncthreads();
 
     // merge the four waves into this workgroup's partial

@@ -26,6 +26,13 @@ struct DevStats {
 typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
 typedef float f32x4 __attribute__((ext_vector_type(4)));
 typedef float f32x16 __attribute__((ext_vector_type(16)));
+typedef short s16x4 __attribute__((ext_vector_type(4)));  // 4 bf16 bit patterns
+
+// LDS ordering between lanes of one wave.
+__device__ __forceinline__ void wave_sync() {
+    __builtin_amdgcn_fence(__ATOMIC_SEQ_CST, "workgroup");
+    __builtin_amdgcn_wave_barrier();
+}
 
 __device__ __forceinline__ float bf16_bits_to_f32(uint32_t h16) {
     return __uint_as_float(h16 << 16);

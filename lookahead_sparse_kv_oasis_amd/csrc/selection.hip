@@ -415,12 +415,6 @@ __device__ __forceinline__ uint32_t block_hash(int32_t blk) {
     return ((uint32_t)blk * 2654435761u) >> 8;
 }
 
-// LDS ordering between lanes of one wave.
-__device__ __forceinline__ void wave_sync() {
-    __builtin_amdgcn_fence(__ATOMIC_SEQ_CST, "workgroup");
-    __builtin_amdgcn_wave_barrier();
-}
-
 // Slots of the LDS residency hash: a power of two of at least twice S, so a
 // probe sequence always meets an empty slot.
 __host__ __device__ constexpr int hash_size(int S) {
