@@ -557,6 +557,9 @@ __global__ __launch_bounds__(256) void attn_mfma_kernel(
 
 // ---------------------------------------------------------------- combine
 
+// Partials merged from registers when there are at most this many.
+constexpr int kCombineRegs = 24;
+
 // One workgroup per (b, query head); thread c owns output dimension c.  The
 // partials of a unit are splits [0, n_a) and [off_b, off_b + n_b) of nsa.
 __global__ __launch_bounds__(256) void combine_kernel(const float *__restrict__ part_m,
@@ -573,6 +576,40 @@ __global__ __launch_bounds__(256) void combine_kernel(const float *__restrict__ 
         const int s = i < n_a ? i : off_b + (i - n_a);
         return (u * nsa + s) * G + g;
     };
+    if (n <= kCombineRegs && (int)blockDim.x >= d) {
+        // every load issued up front (one round trip), then the same sums in
+        // the same order as below
+        const int c = threadIdx.x;
+        float pm[kCombineRegs], pl[kCombineRegs], pa[kCombineRegs];
+#pragma unroll
+        for (int i = 0; i < kCombineRegs; ++i) {
+            pm[i] = -INFINITY;
+            pl[i] = 0.f;
+            pa[i] = 0.f;
+            if (i < n) {
+                const int64_t pi = pidx(i);
+                pm[i] = part_m[pi];
+                pl[i] = part_l[pi];
+                if (c < d) pa[i] = part_acc[pi * d + c];
+            }
+        }
+        float M = -INFINITY;
+#pragma unroll
+        for (int i = 0; i < kCombineRegs; ++i) M = fmaxf(M, pm[i]);
+        float L = 0.f, a = 0.f;
+        if (M != -INFINITY) {
+#pragma unroll
+            for (int i = 0; i < kCombineRegs; ++i) {
+                if (i < n) {
+                    const float wgt = exp2f(pm[i] - M);
+                    L += wgt * pl[i];
+                    a += wgt * pa[i];
+                }
+            }
+        }
+        if (c < d) out[((int64_t)b * Hq + qh) * d + c] = (L > 0.f) ? a / L : 0.f;
+        return;
+    }
     float M = -INFINITY;
     for (int i = 0; i < n; ++i) M = fmaxf(M, part_m[pidx(i)]);
     float L = 0.f;

@@ -423,6 +423,16 @@ __host__ __device__ constexpr int hash_size(int S) {
     return h;
 }
 
+// Resident-block lookup in LDS: up to this many blocks a direct table
+// slot_of[block] (int16, S <= 2048), one read per lookup; past it a hash of
+// the resident blocks with linear probing.
+constexpr int64_t kDirectMax = 16384;
+
+// 32-bit words of LDS the lookup table takes (16-byte multiple).
+__host__ __device__ constexpr int table_ints(int S, int64_t NB) {
+    return NB <= kDirectMax ? (int)(((NB + 7) / 8) * 4) : 2 * hash_size(S);
+}
+
 // Bytes of LDS scratch select_unit needs.
 __host__ __device__ constexpr size_t select_lds_bytes(int K, int S) {
     return sizeof(int32_t) * (3 * (size_t)K + 2 * (size_t)S + 2) +
@@ -441,8 +451,8 @@ __device__ void select_unit(int64_t u, const int32_t *sel, const int32_t *sb_in,
                             int32_t *__restrict__ fetch_block, int32_t *__restrict__ fetch_slot,
                             int32_t *__restrict__ att_block, int32_t *__restrict__ att_slot,
                             int32_t *__restrict__ counts, DevStats *stats, uint32_t *err,
-                            int32_t *sh, const int32_t *hkey, const int32_t *hval,
-                            uint32_t hmask, int attend_all) {
+                            int32_t *sh, const int16_t *slot_of, const int32_t *hkey,
+                            const int32_t *hval, uint32_t hmask, int attend_all) {
     int32_t *hit_blk = sh;             // [K]
     int32_t *hit_slot = hit_blk + K;   // [K]
     int32_t *miss_blk = hit_slot + K;  // [K]
@@ -465,7 +475,9 @@ __device__ void select_unit(int64_t u, const int32_t *sel, const int32_t *sb_in,
         const int32_t id = i < K ? sel[i] : -1;
         int32_t s = -1;
         if (id >= 0) {
-            if (hkey) {  // LDS hash of the resident blocks: linear probing
+            if (slot_of) {  // LDS table of the resident blocks
+                s = slot_of[id];
+            } else if (hkey) {  // LDS hash of the resident blocks: linear probing
                 uint32_t hh = block_hash(id) & hmask;
                 while (true) {
                     const int32_t k = hkey[hh];
@@ -623,7 +635,7 @@ __global__ __launch_bounds__(64) void select_kernel(
     const int64_t u = blockIdx.x;
     select_unit(u, ids + u * K, slot_block + u * S, last_used + u * S, slot_block, last_used,
                 block_slot, K, S, NBmax, cap, t, fetch_block, fetch_slot, att_block, att_slot,
-                counts, stats, err, sh, nullptr, nullptr, 0u, attend_all);
+                counts, stats, err, sh, nullptr, nullptr, nullptr, 0u, attend_all);
 }
 
 // Top-K and select of one unit in one workgroup.
@@ -642,13 +654,21 @@ __global__ __launch_bounds__(NT) void topk_select_kernel(
     int32_t *sel_lds = sh;                 // [K]
     int32_t *sb_lds = sel_lds + K4;        // [S]
     int32_t *lu_lds = sb_lds + S4;         // [S]
-    int32_t *hkey = lu_lds + S4;           // [HS] resident block -> slot
-    int32_t *hval = hkey + HS;             // [HS]
-    int32_t *scratch = hval + HS;          // 16-byte aligned
+    // resident block -> slot: a direct table, or a hash past kDirectMax blocks
+    const bool direct = NB <= kDirectMax;
+    int32_t *tab = lu_lds + S4;
+    int16_t *slot_of = direct ? reinterpret_cast<int16_t *>(tab) : nullptr;
+    int32_t *hkey = direct ? nullptr : tab;    // [HS]
+    int32_t *hval = direct ? nullptr : tab + HS;
+    int32_t *scratch = tab + table_ints(S, NB);  // 16-byte aligned
     // the scores are read while the tables below are read and hashed
     TopkKeys<CMAX> kk;
     topk_load<NT, CMAX>(scores + u * NBmax, NB, kk);
-    for (int i = threadIdx.x; i < HS; i += NT) hkey[i] = -1;
+    if (direct) {
+        for (int i = threadIdx.x; i < NB; i += NT) slot_of[i] = -1;
+    } else {
+        for (int i = threadIdx.x; i < HS; i += NT) hkey[i] = -1;
+    }
     __syncthreads();
     // tables into LDS and the resident blocks into the hash, while the top-K
     // below still waits for its scores
@@ -656,10 +676,14 @@ __global__ __launch_bounds__(NT) void topk_select_kernel(
         const int32_t blk = slot_block[u * S + s];
         sb_lds[s] = blk;
         lu_lds[s] = last_used[u * S + s];
-        if (blk >= 0) {
-            uint32_t hh = block_hash(blk) & (uint32_t)(HS - 1);
-            while (atomicCAS(&hkey[hh], -1, blk) != -1) hh = (hh + 1) & (uint32_t)(HS - 1);
-            hval[hh] = s;
+        if (blk >= 0 && blk < NB) {  // blocks past NB are never selected
+            if (direct) {
+                slot_of[blk] = (int16_t)s;
+            } else {
+                uint32_t hh = block_hash(blk) & (uint32_t)(HS - 1);
+                while (atomicCAS(&hkey[hh], -1, blk) != -1) hh = (hh + 1) & (uint32_t)(HS - 1);
+                hval[hh] = s;
+            }
         }
     }
     topk_unit<NT, CMAX>(kk, NB, K, ids + u * K, nullptr, sel_lds, err);
@@ -667,7 +691,7 @@ __global__ __launch_bounds__(NT) void topk_select_kernel(
     if (threadIdx.x < 64)
         select_unit(u, sel_lds, sb_lds, lu_lds, slot_block, last_used, block_slot, K, S, NBmax,
                     cap, t, fetch_block, fetch_slot, att_block, att_slot, counts, stats, err,
-                    scratch, hkey, hval, (uint32_t)(HS - 1), attend_all);
+                    scratch, slot_of, hkey, hval, (uint32_t)(HS - 1), attend_all);
 }
 
 // Score, top-K and select of one unit in one workgroup (NT / 64 waves): the unit's
@@ -694,9 +718,13 @@ __global__ __launch_bounds__(NT) void score_topk_select_kernel(
     int32_t *sel_lds = sh;                 // [K]
     int32_t *sb_lds = sel_lds + K4;        // [S]
     int32_t *lu_lds = sb_lds + S4;         // [S]
-    int32_t *hkey = lu_lds + S4;           // [HS]
-    int32_t *hval = hkey + HS;             // [HS]
-    int32_t *scratch = hval + HS;          // 16-byte aligned
+    // resident block -> slot: a direct table, or a hash past kDirectMax blocks
+    const bool direct = NB <= kDirectMax;
+    int32_t *tab = lu_lds + S4;
+    int16_t *slot_of = direct ? reinterpret_cast<int16_t *>(tab) : nullptr;
+    int32_t *hkey = direct ? nullptr : tab;    // [HS]
+    int32_t *hval = direct ? nullptr : tab + HS;
+    int32_t *scratch = tab + table_ints(S, NB);  // 16-byte aligned
     float *sc = reinterpret_cast<float *>(scratch + ((select_lds_bytes(K, S) + 15) / 16) * 4);
     const int h = (int)(u % Hkv), b = (int)(u / Hkv);
     const int ntiles = (NB + 31) / 32;
@@ -705,16 +733,24 @@ __global__ __launch_bounds__(NT) void score_topk_select_kernel(
     st.setup(summ, u, unit_elems);
     int tile = wave;
     if (tile < ntiles) st.load(tile);  // in flight while the tables are hashed
-    for (int i = threadIdx.x; i < HS; i += NT) hkey[i] = -1;
+    if (direct) {
+        for (int i = threadIdx.x; i < NB; i += NT) slot_of[i] = -1;
+    } else {
+        for (int i = threadIdx.x; i < HS; i += NT) hkey[i] = -1;
+    }
     __syncthreads();
     for (int s = threadIdx.x; s < S; s += NT) {
         const int32_t blk = slot_block[u * S + s];
         sb_lds[s] = blk;
         lu_lds[s] = last_used[u * S + s];
-        if (blk >= 0) {
-            uint32_t hh = block_hash(blk) & (uint32_t)(HS - 1);
-            while (atomicCAS(&hkey[hh], -1, blk) != -1) hh = (hh + 1) & (uint32_t)(HS - 1);
-            hval[hh] = s;
+        if (blk >= 0 && blk < NB) {  // blocks past NB are never selected
+            if (direct) {
+                slot_of[blk] = (int16_t)s;
+            } else {
+                uint32_t hh = block_hash(blk) & (uint32_t)(HS - 1);
+                while (atomicCAS(&hkey[hh], -1, blk) != -1) hh = (hh + 1) & (uint32_t)(HS - 1);
+                hval[hh] = s;
+            }
         }
     }
     st.rows(q, drafts, n_drafts, qskip, B, Hq, G, b, h);
@@ -740,7 +776,7 @@ __global__ __launch_bounds__(NT) void score_topk_select_kernel(
     if (threadIdx.x < 64)
         select_unit(u, sel_lds, sb_lds, lu_lds, slot_block, last_used, block_slot, K, S, NBmax,
                     cap, t, fetch_block, fetch_slot, att_block, att_slot, counts, stats, err,
-                    scratch, hkey, hval, (uint32_t)(HS - 1), attend_all);
+                    scratch, slot_of, hkey, hval, (uint32_t)(HS - 1), attend_all);
 }
 
 __global__ __launch_bounds__(64) void evict_kernel(const int32_t *__restrict__ blocks,
@@ -824,7 +860,7 @@ hipError_t launch_topk_select(const Dims &D, const float *scores, int64_t NB, in
                               DevStats *stats, uint32_t *err, hipStream_t st) {
     dim3 grid((unsigned)D.units());
     const size_t lds = sizeof(int32_t) * ((size_t)((D.K + 3) & ~3) + 2 * (size_t)((D.S + 3) & ~3) +
-                                          2 * (size_t)hash_size(D.S)) +
+                                          (size_t)table_ints(D.S, NB)) +
                        select_lds_bytes(D.K, D.S);
     if (lds > 64 * 1024) {  // large pools: the two kernels one after the other
         hipError_t e = launch_topk(D, scores, NB, ids, nullptr, err, st);
@@ -844,7 +880,7 @@ hipError_t launch_topk_select(const Dims &D, const float *scores, int64_t NB, in
 
 static size_t fused_lds_bytes(const Dims &D, int64_t NB) {
     const size_t ints = (size_t)((D.K + 3) & ~3) + 2 * (size_t)((D.S + 3) & ~3) +
-                        2 * (size_t)hash_size(D.S);
+                        (size_t)table_ints(D.S, NB);
     return sizeof(int32_t) * ints + ((select_lds_bytes(D.K, D.S) + 15) / 16) * 16 +
            sizeof(float) * 32 * (size_t)((NB + 31) / 32);
 }
