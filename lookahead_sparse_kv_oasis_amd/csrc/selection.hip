@@ -661,7 +661,7 @@ __global__ __launch_bounds__(NT) void topk_select_kernel(
     int32_t *hkey = direct ? nullptr : tab;    // [HS]
     int32_t *hval = direct ? nullptr : tab + HS;
     int32_t *scratch = tab + table_ints(S, NB);  // 16-byte aligned
-    // the scores are read while the tables below are read and hashed
+    // the scores are read while the tables below are read and indexed
     TopkKeys<CMAX> kk;
     topk_load<NT, CMAX>(scores + u * NBmax, NB, kk);
     if (direct) {
@@ -670,7 +670,7 @@ __global__ __launch_bounds__(NT) void topk_select_kernel(
         for (int i = threadIdx.x; i < HS; i += NT) hkey[i] = -1;
     }
     __syncthreads();
-    // tables into LDS and the resident blocks into the hash, while the top-K
+    // tables into LDS and the resident blocks into the lookup table, while the top-K
     // below still waits for its scores
     for (int s = threadIdx.x; s < S; s += NT) {
         const int32_t blk = slot_block[u * S + s];
@@ -695,7 +695,7 @@ __global__ __launch_bounds__(NT) void topk_select_kernel(
 }
 
 // Score, top-K and select of one unit in one workgroup (NT / 64 waves): the unit's
-// tiles are scored into LDS (the slot tables are hashed meanwhile), copied out
+// tiles are scored into LDS (the slot tables are indexed meanwhile), copied out
 // for inspection, and the top-K and select run on the LDS copy: no score round
 // trip through HBM and one launch instead of two.  The summary read is the
 // same as the score kernel's.
@@ -732,7 +732,7 @@ __global__ __launch_bounds__(NT) void score_topk_select_kernel(
     ScoreTiles<D, QT> st;
     st.setup(summ, u, unit_elems);
     int tile = wave;
-    if (tile < ntiles) st.load(tile);  // in flight while the tables are hashed
+    if (tile < ntiles) st.load(tile);  // in flight while the tables are indexed
     if (direct) {
         for (int i = threadIdx.x; i < NB; i += NT) slot_of[i] = -1;
     } else {

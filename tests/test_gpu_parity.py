@@ -407,3 +407,13 @@ def test_free_running_full_slot_pools(slots):
     p = FreeRunning(w, 6, [(0, 0), (1, 5)])
     rep = p.run_free()
     log(f"{slots}-slot pool: {rep}")
+
+
+def test_free_running_past_the_direct_lookup_table():
+    """More than 16,384 blocks per KV head (272K tokens): the select's
+    resident-block lookup falls back to the LDS hash; checked step by step
+    against the oracle on sampled units."""
+    from tests.gpu_parity import FreeRunning, log
+    w = synth.QWEN3_8B.with_(batch=1, prefix_tokens=16 * 17000 + 5)
+    rep = FreeRunning(w, 4, [(0, 0), (0, 5)]).run_free(check_payload_every=4)
+    log(f"17,000-block context: {rep}")
