@@ -242,12 +242,15 @@ def main():
         step = run.step
     torch.cuda.synchronize()
     stats0 = h.oasis_get_stats()
+    # with miss correction the prefetch select's blocks are copied by the
+    # standalone gather (the next select rewrites the fetch list first)
+    correcting = w.lookahead and args.correct_cap > 0
     from lookahead_sparse_kv_oasis_amd import TIME
     # events only around the two HBM kernels of the metric, to keep the step
     # itself unperturbed
     h.oasis_set_timing(0 if args.no_kernel_timing else
                        TIME["score"] | TIME["attn"] |
-                       (0 if stats0["fetch_fused"] and not w.lookahead else TIME["gather"]))
+                       (0 if stats0["fetch_fused"] and not correcting else TIME["gather"]))
     h.oasis_set_timing_period(args.timing_period)
 
     torch.cuda.synchronize()
@@ -290,9 +293,9 @@ def main():
     score_gbps = score_bytes / (ms_score * 1e-3) / 1e9
     attn_gbps = attn_bytes / (ms_attn * 1e-3) / 1e9
     hbm_gbps = (score_bytes + attn_bytes) / ((ms_score + ms_attn + ms_comb) * 1e-3) / 1e9
-    # in the lookahead order the next append copies the fetched blocks with the
-    # standalone gather kernel, so the attention kernel does no host reads
-    fused = bool(stats1["fetch_fused"]) and not w.lookahead
+    # the fetch runs inside the next attention, in the lookahead order too
+    # (the append before it leaves it pending)
+    fused = bool(stats1["fetch_fused"]) and not correcting
     # with the fetch fused into the attention kernel the host-link transfer
     # runs inside it: its rate is bounded below by bytes / attention time
     g_ms = ms_attn if fused else ms_gather

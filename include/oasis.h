@@ -159,8 +159,9 @@ int oasis_topk_from_scores(oasis_t *h, const float *scores_dev, int32_t *block_i
  * handle's fetch ratio; cap is clamped to K.  The table update runs on
  * `stream`.  The host -> HBM block copies run inside the next
  * oasis_sparse_attn's kernel (bf16 layouts), or on the handle's copy stream
- * after the update; any call that needs the slots earlier (append, evict,
- * select, reading SLOTS) makes the copy first. */
+ * after the update; any call that needs the slots earlier (evict, select,
+ * reading SLOTS) makes the copy first.  An append in between leaves the copy
+ * pending: the copy then takes the whole host block, appended token included. */
 int oasis_select_and_fetch(oasis_t *h, int32_t cap, hipStream_t stream);
 
 /* Force blocks out of HBM (synchronous on `stream`): blocks_host

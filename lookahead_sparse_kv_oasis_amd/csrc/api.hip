@@ -84,7 +84,9 @@ struct oasis_handle {
     bool predicted = false, selected = false;
     // Fused mode: the blocks chosen by select are copied host -> HBM inside
     // the next sparse attention (which reads them anyway); a call that needs
-    // the slots before that runs the standalone gather first.
+    // the slots before that (evict, select, reads) runs the standalone gather
+    // first.  An append does not: the later copy takes its token from the
+    // host KV.
     bool fused = false;
     bool fetch_pending = false;
     // The top-K of the last scores has not run yet: select_and_fetch runs it
@@ -663,7 +665,12 @@ extern "C" int oasis_append_kv(oasis_t *h, const void *k_dev, const void *v_dev,
     TRY(use_stream(h, stream));
     TRY(after(h, stream, h->m_gather));
     TRY(after(h, stream, h->m_attn));
-    TRY(flush_fetch(h, stream));
+    // A fetch left pending by the last select stays pending: it copies whole
+    // host blocks later on this stream, after this token is in the host KV, so
+    // a fetched block's slot ends up with the token whether or not the write-
+    // through below reaches it first.  In the lookahead order (append, attend,
+    // predict, select) the next attention thus streams its hits from HBM
+    // while its fetch waves read the host link.
     TRY(flush_score(h, stream));  // a deferred predict scores the summaries before this token
     LAUNCH(h, TM_APPEND, stream,
            launch_append(h->D, k_dev, v_dev, h->T, h->host_kv_dev, h->summ, h->block_slot,

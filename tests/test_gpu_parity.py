@@ -130,6 +130,21 @@ def test_lookahead_ordering_full_size_sampled_units():
     log(f"{w.name}: {p.run_ahead(check_payload_every=16)}")
 
 
+def test_lookahead_append_into_a_block_whose_fetch_is_pending():
+    """Budget and cap covering every block.  Admission fetches the partly
+    filled tail block, and a block opened at step 12 is fetched by that step's
+    select; in both cases the next append writes its token into the block
+    while the copy is still pending (it runs inside the next attention).  The
+    attention over that block and the slot payloads must hold the token."""
+    from tests.gpu_parity import AheadRunning, log
+    w = synth.QWEN3_8B_AHEAD.with_(batch=2, prefix_tokens=16 * 40 + 5, budget_tokens=16 * 48,
+                                   cap=48)
+    p = AheadRunning(w, 16, [(0, 0), (1, 7), (0, 4)])
+    rep = p.run_ahead(check_payload_every=1)
+    log(f"lookahead, fetch all, appends into pending fetches: {rep}")
+    assert rep["fetched"] > 0
+
+
 def test_lookahead_recall_measurement():
     """Recall of the drafts' prediction and of the previous query's top-K
     against the exact top-K of the step's own query; the exact ids are checked
