@@ -10,13 +10,47 @@
 //
 // A few waves stream the whole list: wave w copies items w, w + W, ... of the
 // units x max_n (unit, i) pairs (item i of a unit exists when i < its count),
-// each block with 16-byte loads of 8 per lane issued before the stores.  Host
-// reads by shader loads run best with about 64 waves in flight (about 55 GB/s);
-// one workgroup per block (thousands of waves) lowers the link rate and takes
-// CU slots from the kernels running beside the copy.
+// in chunks of 8 16-byte loads per lane (8 KB).  A wave keeps two chunks in
+// flight: the next chunk's list entries are read (scalar loads) and its host
+// loads issued before the current chunk is stored, so neither the list reads
+// nor the slot stores leave the host link idle.  Host reads by shader loads
+// run best with about 64 waves in flight (about 55 GB/s alone); one workgroup
+// per block (thousands of waves) lowers the link rate and takes CU slots from
+// the kernels running beside the copy.
 #include "kernels.h"
 
 namespace oasis {
+
+namespace {
+
+constexpr int kChunk = 64 * 8;  // 16-byte vectors per wave chunk
+
+struct GatherCursor {
+    const u32x4 *src;
+    u32x4 *dst;
+    int64_t item;
+    int c0;
+};
+
+__device__ __forceinline__ void load_chunk(u32x4 (&r)[8], const GatherCursor &g, int block_vec,
+                                           int lane) {
+#pragma unroll
+    for (int k = 0; k < 8; ++k) {
+        const int c = g.c0 + k * 64 + lane;
+        if (c < block_vec) r[k] = __builtin_nontemporal_load(g.src + c);
+    }
+}
+
+__device__ __forceinline__ void store_chunk(const u32x4 (&r)[8], const GatherCursor &g,
+                                            int block_vec, int lane) {
+#pragma unroll
+    for (int k = 0; k < 8; ++k) {
+        const int c = g.c0 + k * 64 + lane;
+        if (c < block_vec) g.dst[c] = r[k];
+    }
+}
+
+}  // namespace
 
 __global__ __launch_bounds__(256) void gather_kernel(const u32x4 *__restrict__ host_kv,
                                                      u32x4 *__restrict__ slots,
@@ -28,31 +62,54 @@ __global__ __launch_bounds__(256) void gather_kernel(const u32x4 *__restrict__ h
                                                      int64_t NBmax, int S, int block_vec,
                                                      int max_n, int64_t units) {
     const int lane = threadIdx.x & 63;
+    const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
     const int64_t W = (int64_t)gridDim.x * 4;
     const int64_t n_items = units * max_n;
-    for (int64_t item = (int64_t)blockIdx.x * 4 + (threadIdx.x >> 6); item < n_items;
-         item += W) {
-        const int64_t u = item / max_n;
-        const int i = (int)(item % max_n);
-        const int n = counts[u * count_stride + count_index];
-        if (i >= n) continue;
-        const int32_t blk = blocks[u * list_stride + i];
-        const int32_t s = slot_ids[u * list_stride + i];
-        const u32x4 *src = host_kv + (u * NBmax + blk) * (int64_t)block_vec;
-        u32x4 *dst = slots + (u * S + s) * (int64_t)block_vec;
-        for (int c0 = 0; c0 < block_vec; c0 += 64 * 8) {
-            u32x4 r[8];
-#pragma unroll
-            for (int k = 0; k < 8; ++k) {
-                const int c = c0 + k * 64 + lane;
-                if (c < block_vec) r[k] = __builtin_nontemporal_load(src + c);
-            }
-#pragma unroll
-            for (int k = 0; k < 8; ++k) {
-                const int c = c0 + k * 64 + lane;
-                if (c < block_vec) dst[c] = r[k];
-            }
+    // The first existing item at or after `item` (stride W): fills g and
+    // returns true, or returns false when the list is exhausted.
+    auto seek = [&](int64_t item, GatherCursor &g) -> bool {
+        for (; item < n_items; item += W) {
+            const int64_t u = item / max_n;
+            const int i = (int)(item % max_n);
+            const int n = __builtin_amdgcn_readfirstlane(counts[u * count_stride + count_index]);
+            if (i >= n) continue;
+            const int32_t blk = __builtin_amdgcn_readfirstlane(blocks[u * list_stride + i]);
+            const int32_t s = __builtin_amdgcn_readfirstlane(slot_ids[u * list_stride + i]);
+            g.src = host_kv + (u * NBmax + blk) * (int64_t)block_vec;
+            g.dst = slots + (u * S + s) * (int64_t)block_vec;
+            g.item = item;
+            g.c0 = 0;
+            return true;
         }
+        return false;
+    };
+    // The chunk after g: the next chunk of the same block, else the next item.
+    auto advance = [&](const GatherCursor &g, GatherCursor &nx) -> bool {
+        if (g.c0 + kChunk < block_vec) {
+            nx = g;
+            nx.c0 = g.c0 + kChunk;
+            return true;
+        }
+        return seek(g.item + W, nx);
+    };
+    GatherCursor cur, nx;
+    if (!seek((int64_t)blockIdx.x * 4 + wave, cur)) return;
+    u32x4 ra[8], rb[8];
+    load_chunk(ra, cur, block_vec, lane);
+    // two register buffers in turn, so a chunk in flight is never copied
+    for (;;) {
+        bool more = advance(cur, nx);
+        if (more) load_chunk(rb, nx, block_vec, lane);
+        __builtin_amdgcn_sched_barrier(0);  // the next chunk's loads go out first
+        store_chunk(ra, cur, block_vec, lane);
+        if (!more) break;
+        cur = nx;
+        more = advance(cur, nx);
+        if (more) load_chunk(ra, nx, block_vec, lane);
+        __builtin_amdgcn_sched_barrier(0);
+        store_chunk(rb, cur, block_vec, lane);
+        if (!more) break;
+        cur = nx;
     }
 }
 
