@@ -30,9 +30,11 @@
  *     never throws or aborts.  oasis_last_error() gives the message of the
  *     last failing call on a handle.
  *   - Calls that take a hipStream_t are asynchronous on that stream, like HIP
- *     calls; pointers named *_dev are device memory owned by the caller,
- *     16-byte aligned, contiguous, and must stay valid until the stream has
- *     run the work.  Pointers named *_host are host memory read or written
+ *     calls.  The calls of one handle may use different streams: each waits
+ *     for the handle's earlier work it depends on (HIP events, recorded only
+ *     once a handle has used two streams).  Pointers named *_dev are device
+ *     memory owned by the caller, 16-byte aligned, contiguous, and must stay
+ *     valid until the stream has run the work.  Pointers named *_host are host memory read or written
  *     before the call returns.
  *   - Element type of K, V, queries and drafts is the layout's dtype
  *     (OASIS_F32, or OASIS_BF16 as raw 16-bit patterns).  Scores and the

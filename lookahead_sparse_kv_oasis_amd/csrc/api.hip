@@ -15,8 +15,10 @@
 //
 // Ordering: select waits for the previous gather and attention; the gather
 // waits for select; attention, append and the next select wait for the
-// gather; attention waits for the select.  A wait is issued only when the
-// producing call ran on another stream (one stream is in order by itself).
+// gather; attention and append wait for the select.  A select, an append or
+// a new predict also waits for score / top-K kernels that a predict queued on
+// another stream.  A wait is issued only when the producing call ran on
+// another stream (one stream is in order by itself).
 // No call synchronises the host except the inspection calls.
 #include <stdarg.h>
 #include <stdio.h>
@@ -120,6 +122,15 @@ struct oasis_handle {
 
     hipStream_t copy = nullptr;
     Mark m_append, m_select, m_gather, m_attn;
+    // The last score / top-K kernels launched outside a select (predict,
+    // topk_from_scores, a flushed deferred score) and not yet ordered by a
+    // select on their stream: a call on another stream that reads or
+    // rewrites their inputs or outputs waits for them (after_predict).  The
+    // event is recorded only then, so a caller that keeps predict and select
+    // on one stream pays for no record.
+    bool pred_open = false, pred_marked = false;
+    hipStream_t pred_st = nullptr;
+    hipEvent_t ev_predict = nullptr;
     hipEvent_t ev_fork = nullptr, ev_join = nullptr;   // oasis_decode_layers
     // The marks are recorded only once the handle's work has used two
     // streams; until then stream order is all the ordering there is.
@@ -299,7 +310,7 @@ void free_all(oasis_t *h) {
     h->hkv.reset();
     if (h->copy) (void)hipStreamDestroy(h->copy);
     for (hipEvent_t e : {h->m_append.ev, h->m_select.ev, h->m_gather.ev, h->m_attn.ev, h->ev_fork,
-                         h->ev_join})
+                         h->ev_join, h->ev_predict})
         if (e) (void)hipEventDestroy(e);
     for (auto &t : h->tm) {
         for (auto e : t.start) (void)hipEventDestroy(e);
@@ -325,15 +336,37 @@ int reset_tables(oasis_t *h) {
     return OASIS_OK;
 }
 
+// Score / top-K kernels were just queued on st outside a select.
+void open_predict(oasis_t *h, hipStream_t st) {
+    h->pred_open = true;
+    h->pred_marked = false;
+    h->pred_st = st;
+}
+
+// Make st wait for the open score / top-K kernels when they were queued on
+// another stream.  The event is recorded on their stream now: it covers them
+// and whatever was queued there after them.
+int after_predict(oasis_t *h, hipStream_t st) {
+    if (!h->pred_open || h->pred_st == st) return OASIS_OK;
+    if (!h->pred_marked) {
+        HIP_OK(h, hipEventRecord(h->ev_predict, h->pred_st));
+        h->pred_marked = true;
+    }
+    HIP_OK(h, hipStreamWaitEvent(st, h->ev_predict, 0));
+    return OASIS_OK;
+}
+
 // Run a deferred score on its own (when the scores are needed before a select).
 int flush_score(oasis_t *h, hipStream_t st) {
     if (!h->score_pending) return OASIS_OK;
     h->score_pending = false;
     TRY(after(h, st, h->m_append));
     TRY(after(h, st, h->m_select));
+    TRY(after_predict(h, st));
     LAUNCH(h, TM_SCORE, st,
            launch_score(h->D, h->summ, h->score_q, h->score_drafts, h->score_nd, h->topk_nb,
                         h->scores, st));
+    open_predict(h, st);
     return OASIS_OK;
 }
 
@@ -342,7 +375,9 @@ int flush_topk(oasis_t *h, hipStream_t st) {
     TRY(flush_score(h, st));
     if (!h->topk_pending) return OASIS_OK;
     h->topk_pending = false;
+    TRY(after_predict(h, st));
     LAUNCH(h, TM_TOPK, st, launch_topk(h->D, h->scores, h->topk_nb, h->ids, nullptr, h->err, st));
+    open_predict(h, st);
     return OASIS_OK;
 }
 
@@ -517,7 +552,8 @@ int create_handle(const oasis_layout *layout, int32_t block_size, int32_t budget
         hipEventCreateWithFlags(&h->m_gather.ev, kMarkFlags) != hipSuccess ||
         hipEventCreateWithFlags(&h->m_attn.ev, kMarkFlags) != hipSuccess ||
         hipEventCreateWithFlags(&h->ev_fork, kMarkFlags) != hipSuccess ||
-        hipEventCreateWithFlags(&h->ev_join, kMarkFlags) != hipSuccess)
+        hipEventCreateWithFlags(&h->ev_join, kMarkFlags) != hipSuccess ||
+        hipEventCreateWithFlags(&h->ev_predict, kMarkFlags) != hipSuccess)
         return bail(OASIS_E_HIP);
     if (hipDeviceSynchronize() != hipSuccess) return bail(OASIS_E_HIP);
     *out = h;
@@ -665,6 +701,7 @@ extern "C" int oasis_append_kv(oasis_t *h, const void *k_dev, const void *v_dev,
     TRY(use_stream(h, stream));
     TRY(after(h, stream, h->m_gather));
     TRY(after(h, stream, h->m_attn));
+    TRY(after(h, stream, h->m_select));  // and the score the select ranked
     // A fetch left pending by the last select stays pending: it copies whole
     // host blocks later on this stream, after this token is in the host KV, so
     // a fetched block's slot ends up with the token whether or not the write-
@@ -672,6 +709,7 @@ extern "C" int oasis_append_kv(oasis_t *h, const void *k_dev, const void *v_dev,
     // predict, select) the next attention thus streams its hits from HBM
     // while its fetch waves read the host link.
     TRY(flush_score(h, stream));  // a deferred predict scores the summaries before this token
+    TRY(after_predict(h, stream));  // a score on another stream may still read the summaries
     LAUNCH(h, TM_APPEND, stream,
            launch_append(h->D, k_dev, v_dev, h->T, h->host_kv_dev, h->summ, h->block_slot,
                          h->slots, stream));
@@ -698,6 +736,7 @@ extern "C" int oasis_predict(oasis_t *h, const void *q_dev, const void *drafts_d
     TRY(use_stream(h, stream));
     TRY(after(h, stream, h->m_append));
     TRY(after(h, stream, h->m_select));  // the previous select reads the scores
+    TRY(after_predict(h, stream));       // an earlier score writes the same buffers
     h->score_pending = false;
     if (h->fuse_score && !block_ids_dev && !scores_dev &&
         score_topk_fusable(D, NB, D.G * ((q_dev ? 1 : 0) + n_drafts))) {
@@ -724,6 +763,7 @@ extern "C" int oasis_predict(oasis_t *h, const void *q_dev, const void *drafts_d
     } else {
         h->topk_pending = true;
     }
+    open_predict(h, stream);
     h->predicted = true;
     return OASIS_OK;
 }
@@ -734,8 +774,11 @@ extern "C" int oasis_topk_from_scores(oasis_t *h, const float *scores_dev,
     const int64_t NB = nb_of(h);
     if (NB == 0) return fail(h, OASIS_E_STATE, "topk: no tokens loaded");
     TRY(use_stream(h, stream));
+    TRY(after(h, stream, h->m_select));  // the previous select reads the ids
+    TRY(after_predict(h, stream));
     LAUNCH(h, TM_TOPK, stream,
            launch_topk(h->D, scores_dev, NB, h->ids, block_ids_dev, h->err, stream));
+    open_predict(h, stream);
     h->topk_pending = false;
     h->score_pending = false;
     h->predicted = true;
@@ -758,6 +801,7 @@ int select_impl(oasis_t *h, int32_t cap, hipStream_t stream, bool eager, hipStre
     TRY(use_stream(h, stream));
     TRY(after(h, stream, h->m_gather));
     TRY(after(h, stream, h->m_attn));
+    TRY(after_predict(h, stream));  // the scores / ids it ranks and reads
     TRY(flush_fetch(h, stream));
     if (h->score_pending) {
         // the deferred predict's orderings, on this stream
@@ -785,6 +829,9 @@ int select_impl(oasis_t *h, int32_t cap, hipStream_t stream, bool eager, hipStre
                              h->att_slot, h->counts, h->stats, h->err, stream));
     }
     h->last_cap = cap;
+    // From here stream order after the select (and its mark) covers the
+    // predict's kernels.
+    h->pred_open = false;
     TRY(mark(h, h->m_select, stream));
     if (h->fused && !eager) {
         h->fetch_pending = cap > 0;

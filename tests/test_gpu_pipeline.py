@@ -234,3 +234,32 @@ def test_handle_moving_to_a_second_stream_midway_matches_one_stream():
         assert np.array_equal(a.h.read(buf), b.h.read(buf)), buf
     assert np.array_equal(a.h.read("SLOTS", np.uint8), b.h.read("SLOTS", np.uint8))
     a.h.oasis_check()
+
+
+def test_predict_on_another_stream_than_its_select_and_append():
+    """Predict on one stream while append, select and attention run on the
+    other, swapping the two streams every step: the select, the next append
+    and the next predict wait for the score kernels queued on the other
+    stream, so outputs, tables and slot payloads equal a one-stream run bit
+    for bit."""
+    from lookahead_sparse_kv_oasis_amd.runner import LayerRunner
+    w = synth.QWEN3_8B.with_(batch=8, prefix_tokens=16 * 1000 + 5, budget_tokens=16 * 64)
+    n = 8
+    a, b = LayerRunner(w, n), LayerRunner(w, n)
+    cur, s2 = torch.cuda.current_stream(), torch.cuda.Stream()
+    a.admission()
+    b.admission()
+    for t in range(1, n + 1):
+        ps, ss = (s2, cur) if t % 2 else (cur, s2)
+        for r, (p_st, s_st) in ((a, (ps, ss)), (b, (cur, cur))):
+            h = r.h
+            h.oasis_append_kv(r.app_k[t - 1], r.app_v[t - 1], stream=s_st)
+            h.oasis_predict(r.q_steps[t], r.drafts[t], w.drafts, stream=p_st)
+            h.oasis_select_and_fetch(r.cap, stream=s_st)
+            h.oasis_sparse_attn(r.q_steps[t], r.out, stream=s_st)
+        torch.cuda.synchronize()
+        assert torch.equal(a.out, b.out), f"step {t}: outputs differ"
+    for buf in STATE_BUFS:
+        assert np.array_equal(a.h.read(buf), b.h.read(buf)), buf
+    assert np.array_equal(a.h.read("SLOTS", np.uint8), b.h.read("SLOTS", np.uint8))
+    a.h.oasis_check()
