@@ -60,6 +60,30 @@ def test_head_dims_reduced_context(head_dim):
     log(f"d={head_dim}: {p.run_all()}")
 
 
+@pytest.mark.parametrize("block_size,budget_blocks", [(1, 48), (8, 64), (64, 16)])
+def test_block_sizes_reduced_context(block_size, budget_blocks):
+    """bf16, d = 128 at block sizes other than 16: the matrix-core score on
+    summaries of 1, 8 or 64 tokens, the generic attention kernel and the
+    eager gather on the copy stream (the fused fetch needs 16-token blocks).
+    One-token blocks are the degenerate case where a block's score is the
+    exact largest dot product of its key with the query rows."""
+    Parity, log = _parity()
+    w = synth.QWEN3_8B.with_(batch=2, block_size=block_size,
+                             prefix_tokens=block_size * 120 + block_size // 2 + 1,
+                             budget_tokens=block_size * budget_blocks)
+    p = Parity(w, 6, [(0, 0), (1, 7)])
+    log(f"block size {block_size}: {p.run_all()}")
+
+
+def test_tiny_workload_one_token_blocks():
+    """fp32 with one-token blocks: the VALU score, block-major summaries and
+    the generic attention at the smallest block."""
+    Parity, log = _parity()
+    w = synth.TINY.with_(block_size=1, prefix_tokens=200, budget_tokens=8, slots=16)
+    p = Parity(w, 8, [(0, 0), (0, 1)])
+    log(f"tiny, one-token blocks: {p.run_all()}")
+
+
 # ------------------------------------------------------------------ full-size workloads
 # Every step of the workload through the C-ABI at its real shape, compared on a
 # sample of (batch row, KV head) units that the oracle recomputes one by one.
