@@ -89,6 +89,37 @@ def pinned_h2d_peak_gbps(nbytes=1 << 30, reps=5):
     return best
 
 
+def hbm_read_peak(nbytes=2 << 30, reps=5):
+    """The box's streaming-read rate of HBM: oasis_stream_read over a buffer
+    eight times the 256 MB last-level cache, best of `reps` launches for each
+    of a few grid sizes (HIP events on the launching stream).  Returns
+    {"gbps", "workgroups", "bytes"}."""
+    import torch
+    from lookahead_sparse_kv_oasis_amd import stream_read
+    buf = torch.empty(nbytes // 4, dtype=torch.int32, device="cuda")
+    buf.fill_(0x01020304)
+    best = (0.0, 0)
+    for wgs in (1024, 2048, 4096, 8192, 16384, 32768):
+        sink = torch.empty(wgs, dtype=torch.int32, device="cuda")
+        stream_read(buf, sink, wgs)   # warm the code path
+        mine = 0.0
+        for _ in range(reps):
+            a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            a.record()
+            stream_read(buf, sink, wgs)
+            b.record()
+            b.synchronize()
+            gbps = nbytes / (a.elapsed_time(b) * 1e-3) / 1e9
+            mine = max(mine, gbps)
+            if gbps > best[0]:
+                best = (gbps, wgs)
+        print(f"# HBM streaming read, {wgs} workgroups: {mine:.0f} GB/s", file=sys.stderr,
+              flush=True)
+    torch.cuda.synchronize()
+    del buf
+    return {"gbps": best[0], "workgroups": best[1], "bytes": nbytes}
+
+
 def cpu_baseline(w, target_s=12.0, max_threads=16):
     """The fp64 oracle (as it stands) on a bounded sample of the workload: up
     to 64 (b, KV head) units stepped through the same decode steps (appended
@@ -154,6 +185,8 @@ def main():
                     choices=sorted(_workloads()))
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-h2d-peak", action="store_true")
+    ap.add_argument("--no-read-peak", action="store_true",
+                    help="skip the HBM streaming-read measurement (2 GiB, a few launches)")
     ap.add_argument("--copy-calibration", type=int, default=0, metavar="MIB",
                     help="only run a plain device-to-device copy of this many MiB five times "
                          "(reference for the HBM byte counters) and exit")
@@ -301,14 +334,17 @@ def main():
     g_ms = ms_attn if fused else ms_gather
     gather_gbps = fetched * blk_bytes / (g_ms * 1e-3) / 1e9 if g_ms > 0 else None
     h2d = None if args.no_h2d_peak else pinned_h2d_peak_gbps()
+    rpk = None if args.no_read_peak else hbm_read_peak()
     # The roofline kernel is the one with the most HBM time among the kernels
     # bound by HBM.  With the fetch fused in, the attention kernel's time is
     # set by the host link whenever the capped fetch outlasts its HBM stream
     # (fetched bytes at the pinned-copy rate >= its HBM bytes at the box's
-    # streaming-read rate, 6.5 TB/s measured); it is then reported under
-    # host_link instead.
+    # streaming-read rate, measured here, else 6.5 TB/s); it is then reported
+    # under host_link instead.
     link_gbps = h2d if h2d is not None else PCIE_GEN5_X16_GBPS
-    attn_link_bound = fused and fetched * blk_bytes / (link_gbps * 1e9) >= attn_bytes / 6.5e12
+    read_gbps = rpk["gbps"] if rpk else 6500.0
+    attn_link_bound = (fused and fetched * blk_bytes / (link_gbps * 1e9) >=
+                       attn_bytes / (read_gbps * 1e9))
     if ms_score >= ms_attn or attn_link_bound:
         # with the fusion on, the score class times the fused score + top-K +
         # select kernel, whose HBM bytes are the score's plus the small tables
@@ -342,10 +378,14 @@ def main():
         "roofline": {"bound": "hbm", "kernel": dom["kernel"], "achieved": dom["achieved"],
                      "peak": HBM_PEAK_GBPS, "unit": "GB/s",
                      "frac": dom["achieved"] / HBM_PEAK_GBPS, "traffic": traffic,
-                     "per_launch_bytes": dom["per_launch_bytes"], "avg_ms": dom["avg_ms"]},
+                     "per_launch_bytes": dom["per_launch_bytes"], "avg_ms": dom["avg_ms"],
+                     "measured_read_peak_gbps": rpk["gbps"] if rpk else None,
+                     "frac_of_measured_read_peak":
+                         dom["achieved"] / rpk["gbps"] if rpk else None},
         "attention": {"kernel": "oasis_sparse_attn", "avg_ms": ms_attn,
                       "hbm_bytes_per_launch": attn_bytes, "hbm_gbps": attn_gbps,
                       "hbm_frac": attn_gbps / HBM_PEAK_GBPS,
+                      "hbm_frac_of_measured_read_peak": attn_gbps / rpk["gbps"] if rpk else None,
                       "bound": "host_link" if attn_link_bound else "hbm",
                       "traffic": stored_traffic("oasis_sparse_attn", w.name)},
         "host_link": {"kernel": "oasis_sparse_attn (fused fetch)" if fused else "oasis_gather",
@@ -358,6 +398,7 @@ def main():
         "timed_launches": {"score": tm["n_score"], "attn": tm["n_attn"],
                            "period": args.timing_period},
         "attended_blocks_per_step": attended,
+        "hbm_read_peak": rpk,
     }
     if fused_leg:
         h.oasis_set_score_topk_fusion(True)
@@ -508,6 +549,7 @@ def bench_model(args, w):
     side = torch.cuda.Stream()
     xfer = torch.cuda.Stream()
     h2d = None if args.no_h2d_peak else pinned_h2d_peak_gbps()
+    rpk = None if args.no_read_peak else hbm_read_peak()
     cpu = None if args.no_cpu_baseline else cpu_baseline(w.with_(layers=1))
     e, d, bs = w.elem_bytes, w.head_dim, w.block_size
     units = w.batch * w.kv_heads
@@ -578,7 +620,9 @@ def bench_model(args, w):
             roof = {"bound": "hbm", "kernel": "oasis_score", "achieved": score_gbps,
                     "peak": HBM_PEAK_GBPS, "unit": "GB/s", "frac": score_gbps / HBM_PEAK_GBPS,
                     "traffic": None, "per_launch_bytes": score_bytes, "avg_ms": ms_score,
-                    "attn_avg_ms": ms_attn}
+                    "attn_avg_ms": ms_attn,
+                    "measured_read_peak_gbps": rpk["gbps"] if rpk else None,
+                    "frac_of_measured_read_peak": score_gbps / rpk["gbps"] if rpk else None}
         link_gbps = r["fetched"] * blk_bytes / (dt / K) / 1e9
         line = {
             "metric": METRIC,

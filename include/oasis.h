@@ -357,6 +357,18 @@ hipStream_t oasis_copy_stream(const oasis_t *h);
 uint64_t oasis_kv_bytes_per_token(int32_t layers, int32_t kv_heads, int32_t head_dim,
                                   int32_t dtype_bytes);
 
+/* Measurement helper: read `bytes` of device memory at buf_dev (16-byte
+ * aligned, bytes a positive multiple of 16) once, with `workgroups`
+ * workgroups (1..65536) of 256 threads streaming 16 KB pieces in turn, on
+ * `stream`.  sink_dev [workgroups] receives, per workgroup, the XOR of the
+ * 32-bit words it read, so the XOR over sink equals the XOR of the buffer's
+ * words.  Timed over a buffer larger than the last-level cache it gives the
+ * box's streaming-read rate of HBM, the practical ceiling of the summary
+ * scan and of the attention over resident slots.  OASIS_E_INVAL on bad
+ * arguments; no handle needed. */
+int oasis_stream_read(const void *buf_dev, int64_t bytes, uint32_t *sink_dev, int32_t workgroups,
+                      hipStream_t stream);
+
 /* Default per-(b, KV head) cap for a fetch ratio of a K-block budget
  * (OasisKV Table 2 sets the cap by a fetch ratio): max(1, floor(ratio * K))
  * for ratio > 0, 0 for ratio <= 0, K for ratio >= 1. */

@@ -33,7 +33,8 @@ EXPORTS = [
     "oasis_evict", "oasis_sparse_attn", "oasis_sparse_attn_verify", "oasis_buffer_bytes", "oasis_read", "oasis_get_stats",
     "oasis_check", "oasis_set_timing", "oasis_set_timing_period",
     "oasis_set_score_topk_fusion", "oasis_set_attend_all_resident", "oasis_get_timing", "oasis_get_dims", "oasis_tokens",
-    "oasis_copy_stream", "oasis_kv_bytes_per_token", "oasis_cap_from_ratio", "oasis_strerror",
+    "oasis_copy_stream", "oasis_stream_read", "oasis_kv_bytes_per_token", "oasis_cap_from_ratio",
+    "oasis_strerror",
     "oasis_last_error",
 ]
 
@@ -116,6 +117,7 @@ def lib():
                                               ctypes.POINTER(i64), ctypes.POINTER(i32)]),
             "oasis_tokens": (i64, [H]),
             "oasis_copy_stream": (vp, [H]),
+            "oasis_stream_read": (ctypes.c_int, [vp, i64, vp, i32, vp]),
             "oasis_kv_bytes_per_token": (ctypes.c_uint64, [i32, i32, i32, i32]),
             "oasis_cap_from_ratio": (i32, [f32, i32]),
             "oasis_strerror": (ctypes.c_char_p, [ctypes.c_int]),
@@ -153,6 +155,16 @@ def _stream(stream):
 
 def kv_bytes_per_token(layers, kv_heads, head_dim, dtype_bytes) -> int:
     return int(lib().oasis_kv_bytes_per_token(layers, kv_heads, head_dim, dtype_bytes))
+
+
+def stream_read(buf, sink, workgroups: int, stream=None) -> None:
+    """oasis_stream_read: one streaming read of the device tensor `buf`;
+    sink (uint32 / int32 device tensor of `workgroups` entries) receives the
+    per-workgroup XOR of the words read."""
+    nbytes = buf.numel() * buf.element_size()
+    rc = lib().oasis_stream_read(_ptr(buf), nbytes, _ptr(sink), workgroups, _stream(stream))
+    if rc != OASIS_OK:
+        raise OasisError(rc, "oasis_stream_read")
 
 
 def cap_from_ratio(ratio, k_blocks) -> int:

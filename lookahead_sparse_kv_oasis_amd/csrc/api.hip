@@ -33,6 +33,7 @@
 #include <vector>
 
 #include "../../include/oasis.h"
+#include "bandwidth.h"
 #include "kernels.h"
 
 using namespace oasis;
@@ -400,6 +401,16 @@ extern "C" uint64_t oasis_kv_bytes_per_token(int32_t layers, int32_t kv_heads, i
     if (layers < 0 || kv_heads < 0 || head_dim < 0 || dtype_bytes < 0) return 0;
     return (uint64_t)layers * 2u * (uint64_t)kv_heads * (uint64_t)head_dim *
            (uint64_t)dtype_bytes;
+}
+
+extern "C" int oasis_stream_read(const void *buf_dev, int64_t bytes, uint32_t *sink_dev,
+                                 int32_t workgroups, hipStream_t stream) {
+    if (!buf_dev || !sink_dev || !aligned16(buf_dev) || bytes <= 0 || bytes % 16 != 0 ||
+        workgroups < 1 || workgroups > 65536)
+        return OASIS_E_INVAL;
+    return launch_stream_read(buf_dev, bytes, sink_dev, workgroups, stream) == hipSuccess
+               ? OASIS_OK
+               : OASIS_E_HIP;
 }
 
 extern "C" int32_t oasis_cap_from_ratio(float ratio, int32_t k_blocks) {

@@ -200,3 +200,18 @@ def test_sampled_kernel_timing_counts_one_launch_per_period():
     assert tm["ms_score"] > 0 and tm["ms_attn"] > 0
     with pytest.raises(OasisError):
         r.h.oasis_set_timing_period(0)
+
+
+@pytest.mark.parametrize("nbytes,wgs", [(16, 1), (16 * 1007, 3), (64 << 20, 300),
+                                        ((64 << 20) + 16 * 5, 2048)])
+def test_stream_read_folds_every_word_of_the_buffer(nbytes, wgs):
+    """The streaming-read helper behind the measured HBM read peak: the XOR of
+    its per-workgroup words equals the XOR of the buffer, for ragged sizes and
+    for more workgroups than 16 KB pieces."""
+    from lookahead_sparse_kv_oasis_amd import stream_read
+    host = np.random.default_rng(nbytes).integers(0, 2**32, size=nbytes // 4, dtype=np.uint32)
+    buf = torch.from_numpy(host.view(np.int32)).cuda()
+    sink = torch.zeros(wgs, dtype=torch.int32, device="cuda")
+    stream_read(buf, sink, wgs)
+    torch.cuda.synchronize()
+    assert np.bitwise_xor.reduce(sink.cpu().numpy().view(np.uint32)) == np.bitwise_xor.reduce(host)

@@ -77,3 +77,14 @@ def test_create_rejects_bad_layouts_without_touching_the_gpu():
     assert lib.oasis_create(ctypes.byref(lay), 16, 128, -1.0, ctypes.byref(h)) == L.OASIS_E_INVAL
     assert lib.oasis_create(None, 16, 128, 0.02, ctypes.byref(h)) == L.OASIS_E_INVAL
     assert lib.oasis_destroy(None) == L.OASIS_E_INVAL
+
+
+def test_stream_read_rejects_bad_arguments_without_touching_the_gpu():
+    """Argument checks happen before any launch (the pointers here are never
+    dereferenced)."""
+    import lookahead_sparse_kv_oasis_amd as L
+    f = L.lib().oasis_stream_read
+    for buf, nbytes, sink, wgs in [(None, 16, 64, 1), (64, 16, None, 1), (72, 16, 64, 1),
+                                   (64, 0, 64, 1), (64, 24, 64, 1), (64, 16, 64, 0),
+                                   (64, 16, 64, 65537)]:
+        assert f(buf, nbytes, sink, wgs, None) == L.OASIS_E_INVAL, (buf, nbytes, sink, wgs)
