@@ -89,35 +89,55 @@ def pinned_h2d_peak_gbps(nbytes=1 << 30, reps=5):
     return best
 
 
-def hbm_read_peak(nbytes=2 << 30, reps=5):
-    """The box's streaming-read rate of HBM: oasis_stream_read over a buffer
-    eight times the 256 MB last-level cache, best of `reps` launches for each
-    of a few grid sizes (HIP events on the launching stream).  Returns
-    {"gbps", "workgroups", "bytes"}."""
+def hbm_read_peak(same_sizes=(), nbytes=2 << 30, reps=5):
+    """The box's streaming-read rate of HBM with oasis_stream_read.
+
+    "gbps": a buffer eight times the 256 MB last-level cache read once, best
+    of `reps` launches for each of a few grid sizes.  "same_size": for each
+    byte count in same_sizes (the per-launch bytes of a kernel), a buffer of
+    that size read once right after the large buffer has evicted the cache,
+    best of `reps`: a plain read of the same bytes, with the same launch ramp
+    and drain as the kernel it is compared with.  HIP events on the launching
+    stream."""
     import torch
     from lookahead_sparse_kv_oasis_amd import stream_read
-    buf = torch.empty(nbytes // 4, dtype=torch.int32, device="cuda")
-    buf.fill_(0x01020304)
+    big = torch.empty(nbytes // 4, dtype=torch.int32, device="cuda")
+    big.fill_(0x01020304)
+    sinks = {w: torch.empty(w, dtype=torch.int32, device="cuda")
+             for w in (1024, 2048, 4096, 8192, 16384, 32768)}
+
+    def timed(buf, wgs, flush):
+        if flush:
+            stream_read(big, sinks[8192], 8192)
+        a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        a.record()
+        stream_read(buf, sinks[wgs], wgs)
+        b.record()
+        b.synchronize()
+        return a.elapsed_time(b) * 1e-3
+
     best = (0.0, 0)
-    for wgs in (1024, 2048, 4096, 8192, 16384, 32768):
-        sink = torch.empty(wgs, dtype=torch.int32, device="cuda")
-        stream_read(buf, sink, wgs)   # warm the code path
-        mine = 0.0
-        for _ in range(reps):
-            a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-            a.record()
-            stream_read(buf, sink, wgs)
-            b.record()
-            b.synchronize()
-            gbps = nbytes / (a.elapsed_time(b) * 1e-3) / 1e9
-            mine = max(mine, gbps)
-            if gbps > best[0]:
-                best = (gbps, wgs)
+    for wgs in sinks:
+        stream_read(big, sinks[wgs], wgs)   # warm the code path
+        mine = max(nbytes / timed(big, wgs, False) / 1e9 for _ in range(reps))
+        if mine > best[0]:
+            best = (mine, wgs)
         print(f"# HBM streaming read, {wgs} workgroups: {mine:.0f} GB/s", file=sys.stderr,
               flush=True)
+    out = {"gbps": best[0], "workgroups": best[1], "bytes": nbytes, "same_size": {}}
+    for n in same_sizes:
+        n16 = int(n) // 16 * 16
+        buf = torch.empty(n16 // 4, dtype=torch.int32, device="cuda")
+        buf.fill_(1)
+        g = max(n16 / timed(buf, wgs, True) / 1e9 for wgs in (1024, 4096, 8192)
+                for _ in range(reps))
+        out["same_size"][str(int(n))] = g
+        print(f"# HBM streaming read of {n16 / 1e6:.1f} MB after a cache flush: {g:.0f} GB/s",
+              file=sys.stderr, flush=True)
+        del buf
+    del big, sinks
     torch.cuda.synchronize()
-    del buf
-    return {"gbps": best[0], "workgroups": best[1], "bytes": nbytes}
+    return out
 
 
 def cpu_baseline(w, target_s=12.0, max_threads=16):
@@ -334,7 +354,7 @@ def main():
     g_ms = ms_attn if fused else ms_gather
     gather_gbps = fetched * blk_bytes / (g_ms * 1e-3) / 1e9 if g_ms > 0 else None
     h2d = None if args.no_h2d_peak else pinned_h2d_peak_gbps()
-    rpk = None if args.no_read_peak else hbm_read_peak()
+    rpk = None if args.no_read_peak else hbm_read_peak((score_bytes, attn_bytes))
     # The roofline kernel is the one with the most HBM time among the kernels
     # bound by HBM.  With the fetch fused in, the attention kernel's time is
     # set by the host link whenever the capped fetch outlasts its HBM stream
@@ -354,6 +374,9 @@ def main():
         dom = dict(kernel="oasis_sparse_attn", achieved=attn_gbps, per_launch_bytes=attn_bytes,
                    avg_ms=ms_attn)
     traffic = stored_traffic(dom["kernel"], w.name)
+
+    def same(n):
+        return rpk["same_size"].get(str(int(n))) if rpk else None
 
     line = {
         "metric": METRIC,
@@ -381,11 +404,15 @@ def main():
                      "per_launch_bytes": dom["per_launch_bytes"], "avg_ms": dom["avg_ms"],
                      "measured_read_peak_gbps": rpk["gbps"] if rpk else None,
                      "frac_of_measured_read_peak":
-                         dom["achieved"] / rpk["gbps"] if rpk else None},
+                         dom["achieved"] / rpk["gbps"] if rpk else None,
+                     "same_size_read_gbps": same(dom["per_launch_bytes"]),
+                     "frac_of_same_size_read": (dom["achieved"] / same(dom["per_launch_bytes"])
+                                                if rpk else None)},
         "attention": {"kernel": "oasis_sparse_attn", "avg_ms": ms_attn,
                       "hbm_bytes_per_launch": attn_bytes, "hbm_gbps": attn_gbps,
                       "hbm_frac": attn_gbps / HBM_PEAK_GBPS,
                       "hbm_frac_of_measured_read_peak": attn_gbps / rpk["gbps"] if rpk else None,
+                      "same_size_read_gbps": same(attn_bytes),
                       "bound": "host_link" if attn_link_bound else "hbm",
                       "traffic": stored_traffic("oasis_sparse_attn", w.name)},
         "host_link": {"kernel": "oasis_sparse_attn (fused fetch)" if fused else "oasis_gather",
