@@ -694,11 +694,11 @@ __global__ __launch_bounds__(NT) void topk_select_kernel(
                     scratch, slot_of, hkey, hval, (uint32_t)(HS - 1), attend_all);
 }
 
-// Score, top-K and select of one unit in one workgroup (NT / 64 waves): the unit's
-// tiles are scored into LDS (the slot tables are indexed meanwhile), copied out
-// for inspection, and the top-K and select run on the LDS copy: no score round
-// trip through HBM and one launch instead of two.  The summary read is the
-// same as the score kernel's.
+// Score, top-K and select of one unit in one workgroup (NT / 64 waves): the
+// unit's tiles are scored into LDS by the first nws waves (the slot tables are
+// indexed meanwhile), copied out for inspection, and the top-K and select run
+// on the LDS copy: no score round trip through HBM and one launch instead of
+// two.  The summary read is the same as the score kernel's.
 template <int D, int QT, int CMAX, int NT>
 __global__ __launch_bounds__(NT) void score_topk_select_kernel(
     const uint16_t *__restrict__ summ, const uint16_t *__restrict__ q,
@@ -708,7 +708,7 @@ __global__ __launch_bounds__(NT) void score_topk_select_kernel(
     int32_t *__restrict__ block_slot, int K, int S, int64_t NBmax, int cap, int32_t t,
     int32_t *__restrict__ fetch_block, int32_t *__restrict__ fetch_slot,
     int32_t *__restrict__ att_block, int32_t *__restrict__ att_slot,
-    int32_t *__restrict__ counts, DevStats *stats, uint32_t *err, int attend_all) {
+    int32_t *__restrict__ counts, DevStats *stats, uint32_t *err, int attend_all, int nws) {
     constexpr int NW = NT / 64;
     extern __shared__ __attribute__((aligned(16))) int32_t sh[];
     const int64_t u = blockIdx.x;
@@ -729,9 +729,10 @@ __global__ __launch_bounds__(NT) void score_topk_select_kernel(
     const int h = (int)(u % Hkv), b = (int)(u / Hkv);
     const int ntiles = (NB + 31) / 32;
 
+    const int NWS = nws < NW ? nws : NW;
     ScoreTiles<D, QT> st;
     st.setup(summ, u, unit_elems);
-    int tile = wave;
+    int tile = wave < NWS ? wave : ntiles;
     if (tile < ntiles) st.load(tile);  // in flight while the tables are indexed
     if (direct) {
         for (int i = threadIdx.x; i < NB; i += NT) slot_of[i] = -1;
@@ -753,11 +754,13 @@ __global__ __launch_bounds__(NT) void score_topk_select_kernel(
             }
         }
     }
-    st.rows(q, drafts, n_drafts, qskip, B, Hq, G, b, h);
-    for (; tile < ntiles; tile += NW) {
-        const float best = st.best();
-        if (st.half == 0) sc[tile * 32 + st.m] = best;
-        if (tile + NW < ntiles) st.load(tile + NW);
+    if (wave < NWS) {
+        st.rows(q, drafts, n_drafts, qskip, B, Hq, G, b, h);
+        for (; tile < ntiles; tile += NWS) {
+            const float best = st.best();
+            if (st.half == 0) sc[tile * 32 + st.m] = best;
+            if (tile + NWS < ntiles) st.load(tile + NWS);
+        }
     }
     __syncthreads();
     for (int j = threadIdx.x; j < NB; j += NT) scores[u * NBmax + j] = sc[j];
@@ -908,13 +911,22 @@ hipError_t launch_score_topk_select(const Dims &D, const void *summ, const void 
     // 8 waves once the keys outgrow 8 per thread, where the query rows leave
     // the registers for it (at most two 32-row MFMA tiles)
     const int nt = (QT <= 2 && NB > 2048) ? 512 : 256;
+    // Scoring waves: with one workgroup per CU, four (one 16 KB tile stream
+    // per SIMD, as in the score kernel) read the summaries faster than eight
+    // (51.6 against 53.6 us on the Qwen3-8B layer); with two or more per CU
+    // every wave scores (10.30 against 10.83 ms per 36-layer step, where the
+    // kernel shares the GPU with other layers' attention).
+    int dev = 0, cus = 256;
+    if (hipGetDevice(&dev) == hipSuccess)
+        (void)hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev);
+    const int nws = D.units() <= cus ? 4 : nt / 64;
     const int C = (int)((NB + nt - 1) / nt);
 #define OASIS_STS(QT_, CM_, NT_)                                                                 \
     OASIS_LAUNCH((score_topk_select_kernel<128, QT_, CM_, NT_>), grid, dim3(NT_), lds, st,       \
                  (const uint16_t *)summ, (const uint16_t *)q, (const uint16_t *)drafts, n_drafts, \
                  qskip, scores, D.B, D.Hq, D.Hkv, D.G, D.summ_unit_elems(), (int)NB, ids,         \
                  slot_block, last_used, block_slot, D.K, D.S, D.NBmax, cap, t, fetch_block,       \
-                 fetch_slot, att_block, att_slot, counts, stats, err, D.attend_all ? 1 : 0)
+                 fetch_slot, att_block, att_slot, counts, stats, err, D.attend_all ? 1 : 0, nws)
 #define OASIS_STS_SMALL(QT_)                         \
     do {                                             \
         if (nt == 512) {                             \
