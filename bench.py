@@ -229,6 +229,8 @@ def main():
                          "(b, KV head) and step (0: attention over the prefetched set)")
     ap.add_argument("--fuse-score-topk", action="store_true",
                     help="score, top-K and select in one kernel where the shape allows")
+    ap.add_argument("--no-split-leg", action="store_true",
+                    help="skip the leg that copies fetched blocks with the gather kernel")
     ap.add_argument("--no-fused-leg", action="store_true",
                     help="single layers: skip the second timed leg with score, top-K and select fused")
     ap.add_argument("--sweep", action="store_true",
@@ -269,8 +271,12 @@ def main():
     fused_leg = (not args.fuse_score_topk and not args.no_fused_leg and not w.lookahead and
                  not args.no_kernel_timing and w.dtype == synth.BF16 and w.head_dim == 128 and
                  w.batch * w.kv_heads >= 256)
+    # a third leg with the fetch as its own kernel, so that score and attention
+    # are timed as pure HBM kernels and the host-link copy on its own
+    split_leg = fused_leg and not args.no_split_leg
     n_main = args.warmup + args.steps
-    n_steps = n_main + (args.steps if fused_leg else 0)
+    n_fused_end = n_main + (args.steps if fused_leg else 0)
+    n_steps = n_fused_end + (args.steps if split_leg else 0)
     t_setup = time.perf_counter()
     run = LayerRunner(w, n_steps)
     h = run.h
@@ -433,7 +439,7 @@ def main():
         h.oasis_set_timing_period(args.timing_period)
         torch.cuda.synchronize()
         t0 = time.perf_counter()
-        for t in range(n_main + 1, n_steps + 1):
+        for t in range(n_main + 1, n_fused_end + 1):
             step(t, stream)
         torch.cuda.synchronize()
         dt2 = time.perf_counter() - t0
@@ -449,6 +455,44 @@ def main():
                 "traffic": stored_traffic("oasis_score_topk_select", w.name),
                 "steps": K, "note": "same handle, the K steps after the main timed region, "
                 "score + top-K + select in one kernel (bit-identical results)"}
+    if split_leg:
+        h.oasis_set_score_topk_fusion(False)
+        h.oasis_set_fetch_in_attention(False)
+        h.oasis_set_timing(TIME["score"] | TIME["attn"] | TIME["gather"])
+        h.oasis_set_timing_period(args.timing_period)
+        st0 = h.oasis_get_stats()
+        torch.cuda.synchronize()
+        t0 = time.perf_counter()
+        for t in range(n_fused_end + 1, n_steps + 1):
+            step(t, stream)
+        torch.cuda.synchronize()
+        dt3 = time.perf_counter() - t0
+        tm3 = h.oasis_get_timing()
+        st1 = h.oasis_get_stats()
+        h.oasis_check()
+        h.oasis_set_fetch_in_attention(True)
+        if min(tm3["n_score"], tm3["n_attn"], tm3["n_gather"]) > 0:
+            s3 = tm3["ms_score"] / tm3["n_score"]
+            a3 = tm3["ms_attn"] / tm3["n_attn"]
+            g3 = tm3["ms_gather"] / tm3["n_gather"]
+            att3 = (st1["attended"] - st0["attended"]) / K
+            f3 = (st1["fetched"] - st0["fetched"]) / K
+            ab3 = att3 * blk_bytes + q_bytes + w.batch * w.q_heads * d * 4
+            sa3 = (score_bytes + ab3) / ((s3 + a3) * 1e-3) / 1e9
+            g_gbps = f3 * blk_bytes / (g3 * 1e-3) / 1e9
+            line["split_fetch"] = {
+                "value": K / dt3, "ms_per_step": dt3 / K * 1e3,
+                "score_attn_hbm_gbps": sa3, "score_attn_frac": sa3 / HBM_PEAK_GBPS,
+                "score_attn_frac_of_measured_read_peak": sa3 / rpk["gbps"] if rpk else None,
+                "score_avg_ms": s3, "attn_avg_ms": a3,
+                "attn_hbm_gbps": ab3 / (a3 * 1e-3) / 1e9,
+                "gather_avg_ms": g3, "gather_gbps": g_gbps,
+                "gather_frac_of_pinned_h2d": g_gbps / h2d if h2d else None,
+                "steps": K, "note": "same handle, the K steps after the fused leg, fetched "
+                "blocks copied by the gather kernel on the copy stream (the same "
+                "selections and payloads; outputs equal up to the split-K merge order): "
+                "score and attention timed as pure HBM kernels, the copy on its own; "
+                "slower per step than the copy inside the attention"}
     if verify is not None:
         verify["attended_blocks"] = attended
         verify["hbm_gbps"] = (verify["passes"] * attended * blk_bytes) / (verify["avg_ms"] * 1e-3) / 1e9

@@ -339,6 +339,20 @@ int oasis_set_attend_all_resident(oasis_t *h, int32_t on);
  * first.  The results are the same as without fusion. */
 int oasis_set_score_topk_fusion(oasis_t *h, int32_t on);
 
+/* Where the blocks chosen by oasis_select_and_fetch are copied host -> HBM
+ * (OasisKV explanatory diagram: only the missing blocks are transferred).
+ * on != 0: inside the next oasis_sparse_attn's kernel, whose fetch waves read
+ * the host link while its other workgroups attend to the resident blocks;
+ * the default where the attention runs on the matrix cores (bf16, d = 128,
+ * block 16).  on == 0: by the gather kernel on the handle's copy stream right
+ * after the select; the attention then waits for the copy.  Selections,
+ * tables and slot payloads are the same either way; the attention output
+ * differs only by the order of its fp32 split-K merge (inside the attention
+ * each fetched block is a partial of its own).  A copy still pending is made
+ * before the switch (synchronous).  OASIS_E_INVAL when on is asked for
+ * another layout. */
+int oasis_set_fetch_in_attention(oasis_t *h, int32_t on);
+
 /* Shape of a handle: K (top-K blocks), S (slots), NBmax, block size. */
 int oasis_get_dims(const oasis_t *h, int32_t *k_blocks, int32_t *slots, int64_t *nb_max,
                    int32_t *block_size);

@@ -32,7 +32,7 @@ EXPORTS = [
     "oasis_append_kv", "oasis_predict", "oasis_topk_from_scores", "oasis_select_and_fetch",
     "oasis_evict", "oasis_sparse_attn", "oasis_sparse_attn_verify", "oasis_buffer_bytes", "oasis_read", "oasis_get_stats",
     "oasis_check", "oasis_set_timing", "oasis_set_timing_period",
-    "oasis_set_score_topk_fusion", "oasis_set_attend_all_resident", "oasis_get_timing", "oasis_get_dims", "oasis_tokens",
+    "oasis_set_score_topk_fusion", "oasis_set_fetch_in_attention", "oasis_set_attend_all_resident", "oasis_get_timing", "oasis_get_dims", "oasis_tokens",
     "oasis_copy_stream", "oasis_stream_read", "oasis_kv_bytes_per_token", "oasis_cap_from_ratio",
     "oasis_strerror",
     "oasis_last_error",
@@ -111,6 +111,7 @@ def lib():
             "oasis_set_timing": (ctypes.c_int, [H, i32]),
             "oasis_set_timing_period": (ctypes.c_int, [H, i32]),
             "oasis_set_score_topk_fusion": (ctypes.c_int, [H, i32]),
+            "oasis_set_fetch_in_attention": (ctypes.c_int, [H, i32]),
             "oasis_set_attend_all_resident": (ctypes.c_int, [H, i32]),
             "oasis_get_timing": (ctypes.c_int, [H, ctypes.POINTER(oasis_timing)]),
             "oasis_get_dims": (ctypes.c_int, [H, ctypes.POINTER(i32), ctypes.POINTER(i32),
@@ -276,6 +277,12 @@ class Oasis:
     def oasis_set_timing(self, mask=TIME["all"]):
         """mask: OR of TIME values (0 = off)."""
         self._check(lib().oasis_set_timing(self.h, int(mask)), "oasis_set_timing")
+
+    def oasis_set_fetch_in_attention(self, on: bool):
+        """Copy fetched blocks inside the next attention (True) or with the
+        gather kernel on the copy stream right after the select (False)."""
+        self._check(lib().oasis_set_fetch_in_attention(self.h, int(bool(on))),
+                    "oasis_set_fetch_in_attention")
 
     def oasis_set_score_topk_fusion(self, on: bool):
         """Fuse score, top-K and select into one kernel (when the shape allows)."""

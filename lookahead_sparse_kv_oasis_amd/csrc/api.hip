@@ -1238,6 +1238,20 @@ extern "C" int oasis_set_score_topk_fusion(oasis_t *h, int32_t on) {
     return OASIS_OK;
 }
 
+extern "C" int oasis_set_fetch_in_attention(oasis_t *h, int32_t on) {
+    if (!h) return OASIS_E_INVAL;
+    if (on && !h->plan.mfma)
+        return fail(h, OASIS_E_INVAL,
+                    "fetch in attention: needs the bf16, d = 128, block 16 layout");
+    if (h->fetch_pending) {
+        HIP_OK(h, hipDeviceSynchronize());  // the select the copy follows
+        TRY(flush_fetch(h, h->copy));
+        HIP_OK(h, hipStreamSynchronize(h->copy));
+    }
+    h->fused = on != 0;
+    return OASIS_OK;
+}
+
 extern "C" int oasis_set_timing_period(oasis_t *h, int32_t period) {
     if (!h || period < 1) return h ? fail(h, OASIS_E_INVAL, "timing period %d < 1", period) : OASIS_E_INVAL;
     h->timing_period = period;

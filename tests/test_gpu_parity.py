@@ -317,6 +317,57 @@ def test_score_topk_fusion_bit_identical_full_size():
     a.h.oasis_check()
 
 
+def test_fetch_outside_the_attention_bit_identical_full_size():
+    """Qwen3-8B layer at full size: fetched blocks copied by the gather kernel
+    on the copy stream (fetch-in-attention off from the start, or switched
+    off and on again with a copy pending) give the same tables, selections
+    and slot payloads, bit for bit, as the copy inside the attention kernel.
+    The attention output differs only by rounding: inside the attention each
+    fetched block is its own split-K partial, with the gather every block is
+    read from its slot by the hit workgroups, so the fp32 merge order
+    differs."""
+    from lookahead_sparse_kv_oasis_amd import OasisError, OASIS_E_INVAL, TIME
+    from lookahead_sparse_kv_oasis_amd.runner import LayerRunner
+    from tests.gpu_parity import log
+    w = synth.QWEN3_8B
+    n = 8
+    a, b, c = LayerRunner(w, n), LayerRunner(w, n), LayerRunner(w, n)
+    a.h.oasis_set_fetch_in_attention(False)
+    a.h.oasis_set_timing(TIME["gather"] | TIME["attn"])
+    for r in (a, b, c):
+        r.admission()
+    for t in range(1, n + 1):
+        for r in (a, b, c):
+            r.h.oasis_append_kv(r.app_k[t - 1], r.app_v[t - 1])
+            r.h.oasis_predict(r.q_steps[t], r.drafts[t], w.drafts)
+            r.h.oasis_select_and_fetch(r.cap)
+        if t in (3, 6):   # c switches with its copy pending
+            c.h.oasis_set_fetch_in_attention(t == 6)
+        for r in (a, b, c):
+            r.h.oasis_sparse_attn(r.q_steps[t], r.out)
+        torch.cuda.synchronize()
+        for r in (a, c):
+            err = float((r.out - b.out).abs().max())
+            assert err <= 1e-5, f"step {t}: outputs differ by {err:.3g}"
+            sr, sb = _state(r.h), _state(b.h)
+            for k in sb:
+                assert np.array_equal(sr[k], sb[k]), f"step {t}: {k} differs"
+        if t % 4 == 0:
+            pb = b.h.read("SLOTS", np.uint8)
+            for r in (a, c):
+                assert np.array_equal(r.h.read("SLOTS", np.uint8), pb), f"step {t}: payloads"
+    tm = a.h.oasis_get_timing()
+    assert tm["n_gather"] == n + 1 and tm["n_attn"] == n + 1, tm   # admission included
+    log(f"fetch outside the attention: {n} steps bit-identical, timing {tm}")
+    for r in (a, b, c):
+        r.h.oasis_check()
+    f32 = LayerRunner(synth.TINY, 1)
+    with pytest.raises(OasisError) as e:
+        f32.h.oasis_set_fetch_in_attention(True)   # fp32 attention has no fetch waves
+    assert e.value.status == OASIS_E_INVAL
+    f32.h.oasis_set_fetch_in_attention(False)
+
+
 def test_score_topk_fusion_free_running_against_oracle():
     """The fused kernel checked step by step against the oracle (scores 1e-4,
     ids, select and tables bit-exact, attention 2e-3) on sampled units."""
