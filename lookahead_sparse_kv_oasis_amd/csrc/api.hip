@@ -15,10 +15,10 @@
 //
 // Ordering: select waits for the previous gather and attention; the gather
 // waits for select; attention, append and the next select wait for the
-// gather; attention and append wait for the select.  A select, an append or
-// a new predict also waits for score / top-K kernels that a predict queued on
-// another stream.  A wait is issued only when the producing call ran on
-// another stream (one stream is in order by itself).
+// gather; attention, append and evict wait for the select.  A select, an
+// append or a new predict also waits for score / top-K kernels that a
+// predict queued on another stream.  A wait is issued only when the
+// producing call ran on another stream (one stream is in order by itself).
 // No call synchronises the host except the inspection calls.
 #include <stdarg.h>
 #include <stdio.h>
@@ -883,6 +883,7 @@ extern "C" int oasis_evict(oasis_t *h, const int32_t *blocks_host, const int32_t
     TRY(use_stream(h, stream));
     TRY(after(h, stream, h->m_gather));
     TRY(after(h, stream, h->m_attn));
+    TRY(after(h, stream, h->m_select));  // a select on another stream rewrites the same tables
     TRY(flush_fetch(h, stream));
     HIP_OK(h, hipMemcpyAsync(dblocks, blocks_host, sizeof(int32_t) * D.units() * max_per_unit,
                              hipMemcpyHostToDevice, stream));
