@@ -237,8 +237,9 @@ def main():
                     help="multi-layer workloads: one line per fetch ratio of the sweep")
     args = ap.parse_args()
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
-        print("bench.py measures one GPU only: the decode path has no cross-GPU exchange and "
-              "this build runs on a single MI355X; use --gpus 1.", file=sys.stderr)
+        print("bench.py measures one GPU only: every (batch row, KV head) unit of the decode "
+              "path is independent, so several GPUs would each run this same measurement on "
+              "their own share; use --gpus 1.", file=sys.stderr)
         sys.exit(2)
 
     import numpy as np
