@@ -240,8 +240,8 @@ def test_predict_on_another_stream_than_its_select_and_append():
     """Predict on one stream while append, select and attention run on the
     other, swapping the two streams every step: the select, the next append
     and the next predict wait for the score kernels queued on the other
-    stream, so outputs, tables and slot payloads equal a one-stream run bit
-    for bit."""
+    stream, and an evict on the predict's stream waits for the select, so
+    outputs, tables and slot payloads equal a one-stream run bit for bit."""
     from lookahead_sparse_kv_oasis_amd.runner import LayerRunner
     w = synth.QWEN3_8B.with_(batch=8, prefix_tokens=16 * 1000 + 5, budget_tokens=16 * 64)
     n = 8
@@ -249,6 +249,7 @@ def test_predict_on_another_stream_than_its_select_and_append():
     cur, s2 = torch.cuda.current_stream(), torch.cuda.Stream()
     a.admission()
     b.admission()
+    units = w.batch * w.kv_heads
     for t in range(1, n + 1):
         ps, ss = (s2, cur) if t % 2 else (cur, s2)
         for r, (p_st, s_st) in ((a, (ps, ss)), (b, (cur, cur))):
@@ -257,8 +258,16 @@ def test_predict_on_another_stream_than_its_select_and_append():
             h.oasis_predict(r.q_steps[t], r.drafts[t], w.drafts, stream=p_st)
             h.oasis_select_and_fetch(r.cap, stream=s_st)
             h.oasis_sparse_attn(r.q_steps[t], r.out, stream=s_st)
+            if t == 4:
+                # step 3's first attended block of every unit forced out, on
+                # the stream that did not run this step's select (nothing
+                # synchronises in between)
+                h.oasis_evict(prev_att[id(r)], np.ones(units, np.int32), stream=p_st)
         torch.cuda.synchronize()
         assert torch.equal(a.out, b.out), f"step {t}: outputs differ"
+        if t == 3:
+            prev_att = {id(r): r.h.read("ATT_BLOCK").reshape(units, -1)[:, :1].copy()
+                        for r in (a, b)}
     for buf in STATE_BUFS:
         assert np.array_equal(a.h.read(buf), b.h.read(buf)), buf
     assert np.array_equal(a.h.read("SLOTS", np.uint8), b.h.read("SLOTS", np.uint8))
