@@ -15,9 +15,9 @@
 //
 // Ordering: select waits for the previous gather and attention; the gather
 // waits for select; attention, append and the next select wait for the
-// gather; attention, append and evict wait for the select.  A select, an
-// append or a new predict also waits for score / top-K kernels that a
-// predict queued on another stream.  A wait is issued only when the
+// gather; attention, append and evict wait for the select; attention waits
+// for the last append.  A select, an append or a new predict also waits for
+// score / top-K kernels that a predict queued on another stream.  A wait is issued only when the
 // producing call ran on another stream (one stream is in order by itself).
 // No call synchronises the host except the inspection calls.
 #include <stdarg.h>
@@ -903,6 +903,9 @@ extern "C" int oasis_sparse_attn(oasis_t *h, const void *q_dev, float *out_dev,
     TRY(use_stream(h, stream));
     TRY(after(h, stream, h->m_select));
     TRY(after(h, stream, h->m_gather));
+    // the last append: its write-through into resident slots, and the host
+    // token a pending fetch copies
+    TRY(after(h, stream, h->m_append));
     int mode = 0, nsf = 0;
     if (h->fetch_pending) {
         if (h->plan.mfma) {
@@ -952,6 +955,7 @@ extern "C" int oasis_sparse_attn_verify(oasis_t *h, const void *q_dev, const voi
     TRY(use_stream(h, stream));
     TRY(after(h, stream, h->m_select));
     TRY(after(h, stream, h->m_gather));
+    TRY(after(h, stream, h->m_append));  // the last token, written through into its slot
     TRY(flush_fetch(h, stream));  // every attended block resident before the passes
     // several launches: not a class of the per-kernel timers
     HIP_OK(h, launch_verify(D, h->plan, n_drafts, q_dev, drafts_dev, k_drafts_dev, v_drafts_dev,

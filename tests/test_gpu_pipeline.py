@@ -272,3 +272,35 @@ def test_predict_on_another_stream_than_its_select_and_append():
         assert np.array_equal(a.h.read(buf), b.h.read(buf)), buf
     assert np.array_equal(a.h.read("SLOTS", np.uint8), b.h.read("SLOTS", np.uint8))
     a.h.oasis_check()
+
+
+def test_lookahead_append_and_attention_on_different_streams():
+    """Lookahead order with each step's append on one stream and its
+    attention, predict and select on the other (swapped every step), nothing
+    synchronising in between.  Budget and cap cover every block, so the
+    blocks a pending fetch copies include the one the append writes: the
+    attention waits for the append's write-through and for the host token its
+    fetch reads, and outputs, tables and slot payloads equal a one-stream run
+    bit for bit."""
+    from lookahead_sparse_kv_oasis_amd.runner import LayerRunner
+    w = synth.QWEN3_8B_AHEAD.with_(batch=2, prefix_tokens=16 * 40 + 5, budget_tokens=16 * 48,
+                                   cap=48)
+    n = 16
+    a, b = LayerRunner(w, n), LayerRunner(w, n)
+    cur, s2 = torch.cuda.current_stream(), torch.cuda.Stream()
+    a.admission_ahead()
+    b.admission_ahead()
+    for t in range(1, n + 1):
+        st_app, st_rest = (cur, s2) if t % 2 else (s2, cur)
+        h = a.h
+        h.oasis_append_kv(a.app_k[t - 1], a.app_v[t - 1], stream=st_app)
+        h.oasis_sparse_attn(a.q_steps[t], a.out, stream=st_rest)
+        h.oasis_predict(None, a.drafts[t], w.drafts, stream=st_rest)
+        h.oasis_select_and_fetch(a.cap, stream=st_rest)
+        b.step_ahead(t)
+        torch.cuda.synchronize()
+        assert torch.equal(a.out, b.out), f"step {t}: outputs differ"
+    for buf in STATE_BUFS:
+        assert np.array_equal(a.h.read(buf), b.h.read(buf)), buf
+    assert np.array_equal(a.h.read("SLOTS", np.uint8), b.h.read("SLOTS", np.uint8))
+    a.h.oasis_check()
