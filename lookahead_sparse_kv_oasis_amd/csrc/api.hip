@@ -15,9 +15,10 @@
 //
 // Ordering: select waits for the previous gather and attention; the gather
 // waits for select; attention, append and the next select wait for the
-// gather; attention, append and evict wait for the select; attention waits
-// for the last append.  A select, an append or a new predict also waits for
-// score / top-K kernels that a predict queued on another stream.  A wait is issued only when the
+// gather; attention, append and evict wait for the select; attention and
+// select wait for the last append; attention waits for the previous
+// attention.  A select, an append or a new predict also waits for score /
+// top-K kernels that a predict queued on another stream.  A wait is issued only when the
 // producing call ran on another stream (one stream is in order by itself).
 // No call synchronises the host except the inspection calls.
 #include <stdarg.h>
@@ -812,6 +813,7 @@ int select_impl(oasis_t *h, int32_t cap, hipStream_t stream, bool eager, hipStre
     TRY(use_stream(h, stream));
     TRY(after(h, stream, h->m_gather));
     TRY(after(h, stream, h->m_attn));
+    TRY(after(h, stream, h->m_append));  // it reads the block -> slot table the select rewrites
     TRY(after_predict(h, stream));  // the scores / ids it ranks and reads
     TRY(flush_fetch(h, stream));
     if (h->score_pending) {
@@ -906,6 +908,8 @@ extern "C" int oasis_sparse_attn(oasis_t *h, const void *q_dev, float *out_dev,
     // the last append: its write-through into resident slots, and the host
     // token a pending fetch copies
     TRY(after(h, stream, h->m_append));
+    // the previous attention: the same partials, and the slots its fetch wrote
+    TRY(after(h, stream, h->m_attn));
     int mode = 0, nsf = 0;
     if (h->fetch_pending) {
         if (h->plan.mfma) {

@@ -304,3 +304,37 @@ def test_lookahead_append_and_attention_on_different_streams():
         assert np.array_equal(a.h.read(buf), b.h.read(buf)), buf
     assert np.array_equal(a.h.read("SLOTS", np.uint8), b.h.read("SLOTS", np.uint8))
     a.h.oasis_check()
+
+
+def test_select_after_append_and_attention_twice_on_other_streams():
+    """Per step: append and predict on one stream, a second append on the
+    other, the select back on the first (it waits for that append, whose
+    write-through reads the block -> slot table the select rewrites), then
+    one attention on each stream: the first copies the fetched blocks, the
+    second waits for it (same partials, the slots it wrote).  Outputs, tables
+    and slot payloads equal the same calls on one stream bit for bit."""
+    from lookahead_sparse_kv_oasis_amd.runner import LayerRunner
+    w = synth.QWEN3_8B.with_(batch=4, prefix_tokens=16 * 300 + 5, budget_tokens=16 * 64)
+    n = 6
+    a, b = LayerRunner(w, 2 * n), LayerRunner(w, 2 * n)
+    out2 = {id(a): torch.empty_like(a.out), id(b): torch.empty_like(b.out)}
+    cur, s2 = torch.cuda.current_stream(), torch.cuda.Stream()
+    a.admission()
+    b.admission()
+    for t in range(1, n + 1):
+        k = 2 * (t - 1)
+        for r, other in ((a, s2), (b, cur)):
+            h = r.h
+            h.oasis_append_kv(r.app_k[k], r.app_v[k], stream=cur)
+            h.oasis_predict(r.q_steps[t], r.drafts[t], w.drafts, stream=cur)
+            h.oasis_append_kv(r.app_k[k + 1], r.app_v[k + 1], stream=other)
+            h.oasis_select_and_fetch(r.cap, stream=cur)
+            h.oasis_sparse_attn(r.q_steps[t], r.out, stream=other)
+            h.oasis_sparse_attn(r.q_steps[t], out2[id(r)], stream=cur)
+        torch.cuda.synchronize()
+        assert torch.equal(a.out, b.out), f"step {t}: first attention differs"
+        assert torch.equal(out2[id(a)], out2[id(b)]), f"step {t}: second attention differs"
+    for buf in STATE_BUFS:
+        assert np.array_equal(a.h.read(buf), b.h.read(buf)), buf
+    assert np.array_equal(a.h.read("SLOTS", np.uint8), b.h.read("SLOTS", np.uint8))
+    a.h.oasis_check()
