@@ -140,12 +140,14 @@ def hbm_read_peak(same_sizes=(), nbytes=2 << 30, reps=5):
     return out
 
 
-def cpu_baseline(w, target_s=12.0, max_threads=16):
+def cpu_baseline(w, target_s=12.0, max_threads=16, bytes_per_step=None):
     """The fp64 oracle (as it stands) on a bounded sample of the workload: up
     to 64 (b, KV head) units stepped through the same decode steps (appended
     tokens continue the seeded draws past the workload's step count) on a pool
     of host threads, sized from a one-step calibration to about target_s of
-    wall time.  Extrapolated to whole-layer steps/s."""
+    wall time.  Extrapolated to whole-layer steps/s; with bytes_per_step (the
+    algorithmic score + attention bytes of one layer step) also as an
+    effective GB/s.  phase_share: each phase's share of the oracle's time."""
     from concurrent.futures import ThreadPoolExecutor
 
     import oracle
@@ -174,22 +176,32 @@ def cpu_baseline(w, target_s=12.0, max_threads=16):
         drafts = list(ex.map(lambda t: oracle.to_f64(synth.drafts(w, t), w.dtype),
                              range(1, steps + 1)))
 
+    phases = [dict() for _ in range(n_units)]
+
     def run(i):
         b, h = units[i]
         for t in range(1, steps + 1):
             x, cur = oracle.unit_rows(qf, drafts[t - 1], b, h, w.group)
-            us[i].step(t, x, cur, cap)
+            us[i].step(t, x, cur, cap, phase_times=phases[i])
 
     t0 = time.perf_counter()
     with ThreadPoolExecutor(threads) as ex:
         list(ex.map(run, range(n_units)))
     dt = time.perf_counter() - t0
     unit_steps_per_s = n_units * steps / dt
+    total = {}
+    for p in phases:
+        for k, v in p.items():
+            total[k] = total.get(k, 0.0) + v
+    tsum = sum(total.values()) or 1.0
+    value = unit_steps_per_s / units_all
     return {
-        "value": unit_steps_per_s / units_all,
+        "value": value,
         "unit": "layer-steps/s",
         "cores": threads,
         "kind": "oracle",
+        "effective_gbps": value * bytes_per_step / 1e9 if bytes_per_step else None,
+        "phase_share": {k: v / tsum for k, v in total.items()},
         "sample": f"{n_units} of {units_all} (batch row, KV head) units x {steps} decode steps "
                   f"of {w.name} (append, fp64 score, top-K, select, attention), {dt:.1f} s "
                   f"wall on {threads} threads, scaled to one whole-layer step",
@@ -504,7 +516,7 @@ def main():
         line["recall"] = rec
     if not args.no_cpu_baseline:
         print("# cpu baseline (oracle) ...", file=sys.stderr, flush=True)
-        line["cpu_baseline"] = cpu_baseline(w)
+        line["cpu_baseline"] = cpu_baseline(w, bytes_per_step=score_bytes + attn_bytes)
     print(json.dumps(line), flush=True)
 
 

@@ -21,6 +21,7 @@ import ctypes
 import math
 import os
 import subprocess
+import time
 
 import numpy as np
 
@@ -196,6 +197,21 @@ def dense_attention(q: np.ndarray, keys: np.ndarray, vals: np.ndarray, dtype: in
 
 # ------------------------------------------------------------ one unit
 
+class _PhaseClock:
+    """Adds the wall time since the previous lap to phase_times[name]; does
+    nothing when phase_times is None (timing only, no effect on results)."""
+
+    def __init__(self, phase_times):
+        self.d = phase_times
+        self.t = time.perf_counter() if phase_times is not None else 0.0
+
+    def lap(self, name):
+        if self.d is not None:
+            now = time.perf_counter()
+            self.d[name] = self.d.get(name, 0.0) + (now - self.t)
+            self.t = now
+
+
 class Unit:
     """Decode-step state of one (batch row, KV head) unit.
 
@@ -240,22 +256,31 @@ class Unit:
     def score(self, x_rows) -> np.ndarray:
         return score(self.mx[:self.nb], self.mn[:self.nb], x_rows)
 
-    def step(self, t, x_rows, q_rows, cap, append=True, evict_blocks=None, scores32=None):
+    def step(self, t, x_rows, q_rows, cap, append=True, evict_blocks=None, scores32=None,
+             phase_times=None):
         """One decode step.  Returns a record of every intermediate result.
 
         scores32: if given, the fp32 scores to select on (parity hook);
         otherwise the oracle's own fp64 scores rounded to fp32.
+        phase_times: if given, a dict to which the wall time of each phase
+        (append, score, topk, select, attention) is added.
         """
+        clock = _PhaseClock(phase_times)
         if evict_blocks is not None and len(evict_blocks):
             self.evict(evict_blocks)
         if append:
             self.append()
+        clock.lap("append")
         s64 = self.score(x_rows)
+        clock.lap("score")
         s32 = s64.astype(np.float32) if scores32 is None else np.asarray(scores32, np.float32)
         ids = topk(s32, self.K)
+        clock.lap("topk")
         sel = select(self.slot_block, self.last_used, ids, cap, t)
+        clock.lap("select")
         out = attention(q_rows, self.keys, self.vals, self.dtype, self.bs, self.T,
                         sel["att_block"])
+        clock.lap("attention")
         rec = dict(t=t, T=self.T, scores64=s64, scores32=s32, ids=ids, out=out,
                    slot_block=self.slot_block.copy(), last_used=self.last_used.copy())
         rec.update(sel)
