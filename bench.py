@@ -318,10 +318,10 @@ def main():
     # standalone gather (the next select rewrites the fetch list first)
     correcting = w.lookahead and args.correct_cap > 0
     from lookahead_sparse_kv_oasis_amd import TIME
-    # events only around the two HBM kernels of the metric, to keep the step
-    # itself unperturbed
+    # events only around the kernels of the metric (score, attention and the
+    # combine of its partials), sampled, to keep the step itself unperturbed
     h.oasis_set_timing(0 if args.no_kernel_timing else
-                       TIME["score"] | TIME["attn"] |
+                       TIME["score"] | TIME["attn"] | TIME["combine"] |
                        (0 if stats0["fetch_fused"] and not correcting else TIME["gather"]))
     h.oasis_set_timing_period(args.timing_period)
 
@@ -439,7 +439,7 @@ def main():
                       "frac": (gather_gbps / h2d) if (gather_gbps and h2d) else None,
                       "pcie_gen5_x16_gbps": PCIE_GEN5_X16_GBPS,
                       "blocks_per_step": fetched, "bytes_per_step": fetched * blk_bytes},
-        "kernels_avg_ms": {"score": ms_score, "attn": ms_attn,
+        "kernels_avg_ms": {"score": ms_score, "attn": ms_attn, "combine": ms_comb,
                            **({} if fused else {"gather": ms_gather})},
         "timed_launches": {"score": tm["n_score"], "attn": tm["n_attn"],
                            "period": args.timing_period},
@@ -471,7 +471,7 @@ def main():
     if split_leg:
         h.oasis_set_score_topk_fusion(False)
         h.oasis_set_fetch_in_attention(False)
-        h.oasis_set_timing(TIME["score"] | TIME["attn"] | TIME["gather"])
+        h.oasis_set_timing(TIME["score"] | TIME["attn"] | TIME["combine"] | TIME["gather"])
         h.oasis_set_timing_period(args.timing_period)
         st0 = h.oasis_get_stats()
         torch.cuda.synchronize()
@@ -491,7 +491,8 @@ def main():
             att3 = (st1["attended"] - st0["attended"]) / K
             f3 = (st1["fetched"] - st0["fetched"]) / K
             ab3 = att3 * blk_bytes + q_bytes + w.batch * w.q_heads * d * 4
-            sa3 = (score_bytes + ab3) / ((s3 + a3) * 1e-3) / 1e9
+            c3 = tm3["ms_combine"] / max(tm3["n_combine"], 1)
+            sa3 = (score_bytes + ab3) / ((s3 + a3 + c3) * 1e-3) / 1e9
             g_gbps = f3 * blk_bytes / (g3 * 1e-3) / 1e9
             line["split_fetch"] = {
                 "value": K / dt3, "ms_per_step": dt3 / K * 1e3,
