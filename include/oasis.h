@@ -90,7 +90,11 @@ typedef struct oasis_handle oasis_t;
  * Allocates the pinned host KV [B][Hkv][NBmax][K|V][block_size][d], the HBM
  * summaries [B][Hkv][NBmax][max|min][d] and slot pool
  * [B][Hkv][S][K|V][block_size][d], tables and work buffers, and one copy
- * stream at default priority.  On success *out owns all of it. */
+ * stream at default priority.  On success *out owns all of it.
+ * Environment, read here: OASIS_SCORE_IMPL=valu keeps bf16 summaries
+ * block-major and scores them on the vector ALU instead of the matrix cores;
+ * OASIS_GATHER=stream starts the handle with the fetch outside the attention
+ * (as oasis_set_fetch_in_attention(h, 0)). */
 int oasis_create(const oasis_layout *layout, int32_t block_size, int32_t budget_tokens,
                  float fetch_ratio, oasis_t **out);
 
