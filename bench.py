@@ -10,8 +10,14 @@ Prints one JSON line.  `value` is decode layer-steps/s; the roofline object
 is for the dominant HBM kernel, with its algorithmic bytes per launch divided
 by its average launch time from HIP events attached to its dispatches on its
 stream during the timed region (one launch in --timing-period, spread evenly
-over the region, so that the events barely disturb the measured throughput).  The CPU baseline is the fp64 oracle timed on a bounded sample
-of the same workload on the host cores.
+over the region, so that the events barely disturb the measured throughput).
+Its fractions are against the 8 TB/s spec, the box's measured streaming-read
+rate (2 GiB) and a cold plain read of the kernel's own bytes.  Two more legs
+on the same handle follow the main one: score + top-K + select fused into one
+kernel, and the fetch copied by the gather kernel instead of inside the
+attention (score and attention then timed as pure HBM kernels, the copy on
+its own).  The CPU baseline is the fp64 oracle timed on a bounded sample of
+the same workload on the host cores.
 """
 from __future__ import annotations
 
