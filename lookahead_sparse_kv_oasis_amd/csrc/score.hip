@@ -104,12 +104,29 @@ __global__ __launch_bounds__(256) void score_tiled_kernel(const uint16_t *__rest
     ScoreTiles<D, QT> st;
     st.setup(summ, u, unit_elems);
     int64_t t = t_begin + wave;
+    // A wave that owns one tile more than the fewest (65 tiles over 4 waves:
+    // 17, 16, 16, 16) loads that last tile now into a second buffer, so it
+    // costs no extra round trip at the end, where every other wave would wait
+    // for it.  One 32-row query tile only: the registers allow it there.
+    const int64_t mine = t < t_end ? (t_end - t + 3) / 4 : 0;
+    const bool extra = QT == 1 && mine >= 2 && mine > (t_end - t_begin) / 4;
+    const int64_t t_stop = extra ? t + 4 * (mine - 1) : t_end;
+    bf16x8 bx[ScoreTiles<D, QT>::NI];
     if (t < t_end) st.load(t);  // in flight while the query rows are read
+    if constexpr (QT == 1) {
+        if (extra) st.load_to(bx, t_stop);
+    }
     st.rows(q, drafts, n_drafts, qskip, B, Hq, G, b, h);
-    for (; t < t_end; t += 4) {
+    for (; t < t_stop; t += 4) {
         const float best = st.best();
         if (st.half == 0) tile_best[(t - t_begin) * 32 + st.m] = best;
-        if (t + 4 < t_end) st.load(t + 4);
+        if (t + 4 < t_stop) st.load(t + 4);
+    }
+    if constexpr (QT == 1) {
+        if (extra) {
+            const float best = st.best_of(bx);
+            if (st.half == 0) tile_best[(t_stop - t_begin) * 32 + st.m] = best;
+        }
     }
     __syncthreads();
     const int64_t j0 = t_begin * 32;

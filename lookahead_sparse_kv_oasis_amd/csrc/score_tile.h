@@ -40,11 +40,12 @@ template <int D, int QT> struct ScoreTiles {
         half = lane >> 5;
         ubase = summ + u * unit_elems + 8 * lane;
     }
-    __device__ __forceinline__ void load(int64_t tile) {
+    __device__ __forceinline__ void load_to(bf16x8 (&dst)[NI], int64_t tile) const {
         const uint16_t *src = ubase + tile * 64 * D;
 #pragma unroll
-        for (int i = 0; i < NI; ++i) bv[i] = __builtin_bit_cast(bf16x8, gload16_nt(src + 512 * i));
+        for (int i = 0; i < NI; ++i) dst[i] = __builtin_bit_cast(bf16x8, gload16_nt(src + 512 * i));
     }
+    __device__ __forceinline__ void load(int64_t tile) { load_to(bv, tile); }
     // Rows: G heads x {current query (unless qskip), drafts}, sign-split.
     __device__ __forceinline__ void rows(const uint16_t *q, const uint16_t *drafts, int n_drafts,
                                          int qskip, int B, int Hq, int G, int b, int h) {
@@ -64,20 +65,21 @@ template <int D, int QT> struct ScoreTiles {
             }
         }
     }
-    // Score of block m of the loaded tile (valid in lanes with half == 0).
-    __device__ __forceinline__ float best() const {
+    // Score of block m of tile `tl` (valid in lanes with half == 0).
+    __device__ __forceinline__ float best_of(const bf16x8 (&tl)[NI]) const {
         float b = -INFINITY;
 #pragma unroll
         for (int qt = 0; qt < QT; ++qt) {
             f32x16 acc = {};
 #pragma unroll
             for (int i = 0; i < NI; ++i)
-                acc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a[qt][i], bv[i], acc, 0, 0, 0);
+                acc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a[qt][i], tl[i], acc, 0, 0, 0);
 #pragma unroll
             for (int r = 0; r < 16; ++r) b = fmaxf(b, acc[r]);
         }
         return fmaxf(b, __shfl_xor(b, 32, 64));
     }
+    __device__ __forceinline__ float best() const { return best_of(bv); }
 };
 
 }  // namespace oasis
