@@ -413,11 +413,8 @@ __device__ __forceinline__ int block_valid(int64_t T, int32_t blk) {
 //     takes entries 4 BPW s + w + 4 j, j < BPW, of [0, n_end) (n_end =
 //     n_att - n_fetch in mode 1, n_att in mode 0) from their slots; the four waves are merged
 //     in LDS into partial nsf_max + s.
-// Three waves per SIMD for the 16-head form: it fits them without spilling
-// (165 VGPRs); the other forms keep the compiler's choice (two).
 template <int G, int BPW>
-__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(G == 16 ? 3 : 1))) void
-attn_mfma_kernel(
+__global__ __launch_bounds__(256) void attn_mfma_kernel(
     const uint16_t *__restrict__ q, uint16_t *__restrict__ slots,
     const uint16_t *__restrict__ host_kv, const int32_t *__restrict__ att_block,
     const int32_t *__restrict__ att_slot, const int32_t *__restrict__ counts, int64_t T_, int Hq,
@@ -509,25 +506,26 @@ attn_mfma_kernel(
     st.init(q, u / Hkv, Hq, (int)(u % Hkv));
     const int ne = e_first >= e_end ? 0 : (e_end - e_first + 3) / 4 < BPW ? (e_end - e_first + 3) / 4 : BPW;
 
-    // every list entry of this wave read up front (one round trip), so no
-    // block's loads wait for its entry behind the previous block's compute
-    int32_t blk[BPW], sl[BPW];
-#pragma unroll
-    for (int j = 0; j < BPW; ++j) {
-        const int e = j < ne ? e_first + 4 * j : 0;  // entries past ne: read, never used
-        blk[j] = __builtin_amdgcn_readfirstlane(att_block[u * K + e]);
-        sl[j] = __builtin_amdgcn_readfirstlane(att_slot[u * K + e]);
-    }
     uint4 kr[2][4], vr[2][4];
-    if (ne > 0) st.load_nt(kr[0], vr[0], slots + (u * S + sl[0]) * (int64_t)W::BLK);
+    int32_t blk_cur = 0;
+    if (ne > 0) {
+        blk_cur = __builtin_amdgcn_readfirstlane(att_block[u * K + e_first]);
+        const int32_t sl = __builtin_amdgcn_readfirstlane(att_slot[u * K + e_first]);
+        st.load_nt(kr[0], vr[0], slots + (u * S + sl) * (int64_t)W::BLK);
+    }
 #pragma unroll
     for (int j = 0; j < BPW; ++j) {
         if (j >= ne) break;
-        if (j + 1 < ne)
-            st.load_nt(kr[(j + 1) & 1], vr[(j + 1) & 1],
-                       slots + (u * S + sl[j + 1]) * (int64_t)W::BLK);
+        int32_t blk_nx = 0;
+        if (j + 1 < ne) {
+            const int e = e_first + 4 * (j + 1);
+            blk_nx = __builtin_amdgcn_readfirstlane(att_block[u * K + e]);
+            const int32_t sl = __builtin_amdgcn_readfirstlane(att_slot[u * K + e]);
+            st.load_nt(kr[(j + 1) & 1], vr[(j + 1) & 1], slots + (u * S + sl) * (int64_t)W::BLK);
+        }
         __builtin_amdgcn_sched_barrier(0);  // keep the prefetch ahead of the compute
-        st.block(kr[j & 1], vr[j & 1], block_valid(T_, blk[j]), scale_log2);
+        st.block(kr[j & 1], vr[j & 1], block_valid(T_, blk_cur), scale_log2);
+        blk_cur = blk_nx;
     }
     st.reduce();
     st.stash(sm_acc[wave], sm_m[wave], sm_l[wave]);

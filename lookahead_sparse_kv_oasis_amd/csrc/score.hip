@@ -82,7 +82,7 @@ __global__ __launch_bounds__(64) void score_valu_kernel(const T *__restrict__ su
 // in flight per wave.  Each tile's 32 scores go to LDS and the range is
 // written out in one coalesced pass at the end: scattered 128-byte score
 // stores between the summary reads cost about a tenth of the HBM rate.
-template <int D, int QT>
+template <int D, int QT, bool XT>
 __global__ __launch_bounds__(256) void score_tiled_kernel(const uint16_t *__restrict__ summ,
                                                           const uint16_t *__restrict__ q,
                                                           const uint16_t *__restrict__ drafts,
@@ -104,16 +104,18 @@ __global__ __launch_bounds__(256) void score_tiled_kernel(const uint16_t *__rest
     ScoreTiles<D, QT> st;
     st.setup(summ, u, unit_elems);
     int64_t t = t_begin + wave;
-    // A wave that owns one tile more than the fewest (65 tiles over 4 waves:
-    // 17, 16, 16, 16) loads that last tile now into a second buffer, so it
-    // costs no extra round trip at the end, where every other wave would wait
-    // for it.  One 32-row query tile only: the registers allow it there.
+    // XT: a wave that owns one tile more than the fewest (65 tiles over 4
+    // waves: 17, 16, 16, 16) loads that last tile now into a second buffer,
+    // so it costs no extra round trip at the end, where every other wave
+    // would wait for it.  The buffer takes 64 more registers per lane, which
+    // leave no room beside the kernel for another kernel's waves, so it is
+    // used where each CU holds one workgroup and nothing else runs there.
     const int64_t mine = t < t_end ? (t_end - t + 3) / 4 : 0;
-    const bool extra = QT == 1 && mine >= 2 && mine > (t_end - t_begin) / 4;
+    const bool extra = XT && mine >= 2 && mine > (t_end - t_begin) / 4;
     const int64_t t_stop = extra ? t + 4 * (mine - 1) : t_end;
-    bf16x8 bx[ScoreTiles<D, QT>::NI];
+    bf16x8 bx[XT ? ScoreTiles<D, QT>::NI : 1];
     if (t < t_end) st.load(t);  // in flight while the query rows are read
-    if constexpr (QT == 1) {
+    if constexpr (XT) {
         if (extra) st.load_to(bx, t_stop);
     }
     st.rows(q, drafts, n_drafts, qskip, B, Hq, G, b, h);
@@ -122,7 +124,7 @@ __global__ __launch_bounds__(256) void score_tiled_kernel(const uint16_t *__rest
         if (st.half == 0) tile_best[(t - t_begin) * 32 + st.m] = best;
         if (t + 4 < t_stop) st.load(t + 4);
     }
-    if constexpr (QT == 1) {
+    if constexpr (XT) {
         if (extra) {
             const float best = st.best_of(bx);
             if (st.half == 0) tile_best[(t_stop - t_begin) * 32 + st.m] = best;
@@ -136,17 +138,19 @@ __global__ __launch_bounds__(256) void score_tiled_kernel(const uint16_t *__rest
 }
 
 template <int D>
-static void launch_tiled(int QT, dim3 grid, size_t lds, hipStream_t st, const uint16_t *summ,
-                         const uint16_t *q, const uint16_t *dr, int nd, int qskip, float *scores,
-                         const Dims &Dm, int64_t NB, int per_unit, int tpw) {
-#define OASIS_SCORE_T(QT_)                                                                      \
-    OASIS_LAUNCH((score_tiled_kernel<D, QT_>), grid, dim3(256), lds, st, summ, q, dr, nd, qskip,  \
-                 scores,                                                                       \
-                 Dm.B, Dm.Hq, Dm.Hkv, Dm.G, Dm.summ_unit_elems(), Dm.NBmax, NB, per_unit, tpw)
-    if (QT == 1) OASIS_SCORE_T(1);
-    else if (QT == 2) OASIS_SCORE_T(2);
-    else if (QT == 3) OASIS_SCORE_T(3);
-    else OASIS_SCORE_T(4);
+static void launch_tiled(int QT, bool xt, dim3 grid, size_t lds, hipStream_t st,
+                         const uint16_t *summ, const uint16_t *q, const uint16_t *dr, int nd,
+                         int qskip, float *scores, const Dims &Dm, int64_t NB, int per_unit,
+                         int tpw) {
+#define OASIS_SCORE_T(QT_, XT_)                                                                 \
+    OASIS_LAUNCH((score_tiled_kernel<D, QT_, XT_>), grid, dim3(256), lds, st, summ, q, dr, nd,    \
+                 qskip, scores, Dm.B, Dm.Hq, Dm.Hkv, Dm.G, Dm.summ_unit_elems(), Dm.NBmax, NB,    \
+                 per_unit, tpw)
+    if (QT == 1 && xt) OASIS_SCORE_T(1, true);
+    else if (QT == 1) OASIS_SCORE_T(1, false);
+    else if (QT == 2) OASIS_SCORE_T(2, false);
+    else if (QT == 3) OASIS_SCORE_T(3, false);
+    else OASIS_SCORE_T(4, false);
 #undef OASIS_SCORE_T
 }
 
@@ -168,12 +172,20 @@ hipError_t launch_score(const Dims &D, const void *summ, const void *q, const vo
         const size_t lds = sizeof(float) * 32 * (size_t)tpw;
         const uint16_t *s = (const uint16_t *)summ, *qq = (const uint16_t *)q,
                        *dr = (const uint16_t *)drafts;
+        // the extra-tile buffer where each CU holds at most one workgroup
+        int dev = 0, cus = 256;
+        if (hipGetDevice(&dev) == hipSuccess)
+            (void)hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev);
+        const bool xt = (int64_t)grid.x <= cus;
         if (D.d == 64)
-            launch_tiled<64>(QT, grid, lds, st, s, qq, dr, n_drafts, qskip, scores, D, NB, (int)per_unit, (int)tpw);
+            launch_tiled<64>(QT, xt, grid, lds, st, s, qq, dr, n_drafts, qskip, scores, D, NB,
+                             (int)per_unit, (int)tpw);
         else if (D.d == 128)
-            launch_tiled<128>(QT, grid, lds, st, s, qq, dr, n_drafts, qskip, scores, D, NB, (int)per_unit, (int)tpw);
+            launch_tiled<128>(QT, xt, grid, lds, st, s, qq, dr, n_drafts, qskip, scores, D, NB,
+                              (int)per_unit, (int)tpw);
         else
-            launch_tiled<256>(QT, grid, lds, st, s, qq, dr, n_drafts, qskip, scores, D, NB, (int)per_unit, (int)tpw);
+            launch_tiled<256>(QT, xt, grid, lds, st, s, qq, dr, n_drafts, qskip, scores, D, NB,
+                              (int)per_unit, (int)tpw);
         return hipGetLastError();
     }
     dim3 grid((unsigned)((NB + 63) / 64), D.Hkv, D.B), block(64);

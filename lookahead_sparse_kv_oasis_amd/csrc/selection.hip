@@ -699,7 +699,7 @@ __global__ __launch_bounds__(NT) void topk_select_kernel(
 // indexed meanwhile), copied out for inspection, and the top-K and select run
 // on the LDS copy: no score round trip through HBM and one launch instead of
 // two.  The summary read is the same as the score kernel's.
-template <int D, int QT, int CMAX, int NT>
+template <int D, int QT, int CMAX, int NT, bool XT>
 __global__ __launch_bounds__(NT) void score_topk_select_kernel(
     const uint16_t *__restrict__ summ, const uint16_t *__restrict__ q,
     const uint16_t *__restrict__ drafts, int n_drafts, int qskip, float *__restrict__ scores,
@@ -733,7 +733,17 @@ __global__ __launch_bounds__(NT) void score_topk_select_kernel(
     ScoreTiles<D, QT> st;
     st.setup(summ, u, unit_elems);
     int tile = wave < NWS ? wave : ntiles;
+    // XT, as in the score kernel: a wave owning one tile more than the fewest
+    // loads that last tile now into a second buffer (with one workgroup per
+    // CU only: the buffer's registers would keep other kernels' waves off)
+    const int mine = tile < ntiles ? (ntiles - tile + NWS - 1) / NWS : 0;
+    const bool extra = XT && mine >= 2 && mine > ntiles / NWS;
+    const int t_stop = extra ? tile + NWS * (mine - 1) : ntiles;
+    bf16x8 bx[XT ? ScoreTiles<D, QT>::NI : 1];
     if (tile < ntiles) st.load(tile);  // in flight while the tables are indexed
+    if constexpr (XT) {
+        if (extra) st.load_to(bx, t_stop);
+    }
     if (direct) {
         for (int i = threadIdx.x; i < NB; i += NT) slot_of[i] = -1;
     } else {
@@ -756,10 +766,16 @@ __global__ __launch_bounds__(NT) void score_topk_select_kernel(
     }
     if (wave < NWS) {
         st.rows(q, drafts, n_drafts, qskip, B, Hq, G, b, h);
-        for (; tile < ntiles; tile += NWS) {
+        for (; tile < t_stop; tile += NWS) {
             const float best = st.best();
             if (st.half == 0) sc[tile * 32 + st.m] = best;
-            if (tile + NWS < ntiles) st.load(tile + NWS);
+            if (tile + NWS < t_stop) st.load(tile + NWS);
+        }
+        if constexpr (XT) {
+            if (extra) {
+                const float best = st.best_of(bx);
+                if (st.half == 0) sc[t_stop * 32 + st.m] = best;
+            }
         }
     }
     __syncthreads();
@@ -921,12 +937,18 @@ hipError_t launch_score_topk_select(const Dims &D, const void *summ, const void 
         (void)hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev);
     const int nws = D.units() <= cus ? 4 : nt / 64;
     const int C = (int)((NB + nt - 1) / nt);
-#define OASIS_STS(QT_, CM_, NT_)                                                                 \
-    OASIS_LAUNCH((score_topk_select_kernel<128, QT_, CM_, NT_>), grid, dim3(NT_), lds, st,       \
+    const bool xt = nws == 4 && QT == 1;  // one workgroup per CU
+#define OASIS_STS_X(QT_, CM_, NT_, XT_)                                                          \
+    OASIS_LAUNCH((score_topk_select_kernel<128, QT_, CM_, NT_, XT_>), grid, dim3(NT_), lds, st,  \
                  (const uint16_t *)summ, (const uint16_t *)q, (const uint16_t *)drafts, n_drafts, \
                  qskip, scores, D.B, D.Hq, D.Hkv, D.G, D.summ_unit_elems(), (int)NB, ids,         \
                  slot_block, last_used, block_slot, D.K, D.S, D.NBmax, cap, t, fetch_block,       \
                  fetch_slot, att_block, att_slot, counts, stats, err, D.attend_all ? 1 : 0, nws)
+#define OASIS_STS(QT_, CM_, NT_)                                                                 \
+    do {                                                                                         \
+        if (QT_ == 1 && xt) OASIS_STS_X(QT_, CM_, NT_, true);                                    \
+        else OASIS_STS_X(QT_, CM_, NT_, false);                                                  \
+    } while (0)
 #define OASIS_STS_SMALL(QT_)                         \
     do {                                             \
         if (nt == 512) {                             \
@@ -949,6 +971,7 @@ hipError_t launch_score_topk_select(const Dims &D, const void *summ, const void 
 #undef OASIS_STS_LARGE
 #undef OASIS_STS_SMALL
 #undef OASIS_STS
+#undef OASIS_STS_X
     return hipGetLastError();
 }
 
