@@ -337,8 +337,8 @@ class Unit:
 
 
 def attention_verify(q_sets, keys, vals, dtype: int, bs: int, T: int, blocks, k_drafts, v_drafts):
-    """Attention over the normal and draft queries together ([OASIS] Fig. 7,
-    right), plain fp64.  q_sets [1 + D][G][d]: set 0 is the current query
+    """Verification attention ([OASIS] Fig. 7, right): the current query and
+    each draft query over the sparse KV in one pass, plain fp64.  q_sets [1 + D][G][d]: set 0 is the current query
     (position T - 1), set j the j-th draft (position T - 1 + j).  Set j attends
     over the valid tokens of the attended blocks plus draft tokens 1..j
     (k_drafts / v_drafts [D][d], exact values): causal within the drafts.

@@ -94,8 +94,8 @@ int orc_block_summary(const void *keys, int dtype, int64_t T, int d, int bs, int
 
 /* ---------------------------------------------------------------- score */
 
-/* [OASIS] Fig. 7: the draft query scans the compressed (min/max pooled) keys
- * to predict the next step's top-K blocks.
+/* [OASIS] Fig. 7: the next step's top-K blocks are predicted from the
+ * min/max-pooled key summaries, scored against the draft queries.
  * READING (score rule): the block score for one query row x is the largest
  * value x.k can take over the block's per-dimension box [mn, mx], i.e.
  * sum_c max(x_c*mx_c, x_c*mn_c).

@@ -61,6 +61,62 @@ def test_forced_evictions_leave_holes_that_are_refilled():
         assert len(recs[i]["evicted"]) == int(np.floor(0.1 * n_prev + 1e-9)) > 0
 
 
+def test_evict_empties_the_slots_and_the_next_select_refills_them_first():
+    """Unit.evict, pinned by a hand-worked case (R8: empty slots are filled
+    first, in ascending order, before any LRU victim).  Four slots hold blocks
+    5, 2, 7, 9 with recency 3, 1, 2, 0.  Evicting 2 and 9 empties slots 1 and
+    3 and leaves recency alone.  Selecting [11, 12, 13, 5] with cap 3 then
+    fetches 11 -> slot 1 and 12 -> slot 3 (the holes, ascending), and 13 ->
+    slot 2, the least recent held block not selected (7 at step 2; 5 is a
+    hit).  A no-op evict would hand slot 1 to the LRU victim 2 instead."""
+    w = synth.TINY.with_(prefix_tokens=16 * 14, budget_tokens=16 * 4, slots=4,
+                         initial_resident_frac=0.0)
+    keys, vals = synth.unit_kv(w, 0, 0, w.prefix_tokens)
+    unit = oracle.Unit(keys, vals, w.dtype, w.block_size, w.prefix_tokens, 4, 4,
+                       slot_block=[5, 2, 7, 9], last_used=[3, 1, 2, 0])
+    unit.evict(np.array([2, 9], np.int32))
+    assert unit.slot_block.tolist() == [5, -1, 7, -1]
+    assert unit.last_used.tolist() == [3, 1, 2, 0]
+    unit.evict(np.array([4], np.int32))          # not held: nothing changes
+    assert unit.slot_block.tolist() == [5, -1, 7, -1]
+    r = oracle.select(unit.slot_block, unit.last_used, np.array([11, 12, 13, 5], np.int32), 3, 4)
+    assert r["fetch_block"].tolist() == [11, 12, 13]
+    assert r["fetch_slot"].tolist() == [1, 3, 2]
+    assert r["att_block"].tolist() == [5, 11, 12, 13] and r["n_hit"] == 1
+    assert unit.slot_block.tolist() == [5, 11, 13, 12]
+    assert unit.last_used.tolist() == [4, 4, 4, 4]
+
+
+def test_forced_evictions_are_gone_at_the_next_select():
+    """Along the GQA-8 stress trajectory, every forced-out block is absent
+    when the next select runs: if it is held after that step, the step fetched
+    it again (it is in the fetch list, not among the hits), and the evicted
+    blocks' slots are empty slots, which the select fills first."""
+    w = synth.QWEN3_32B.with_(batch=1, prefix_tokens=16 * 200, budget_tokens=16 * 20)
+    recs = run_unit(w, 0, 5, 8)
+    seen = 0
+    for i in range(1, len(recs)):
+        ev = set(int(b) for b in recs[i]["evicted"])
+        assert ev
+        prev_sb = recs[i - 1]["slot_block"]
+        holes = sorted(int(s) for s in np.nonzero(np.isin(prev_sb, list(ev)))[0])
+        # empty at the select: the new holes and any slot a capped step left empty
+        empty = sorted(set(holes) | set(int(s) for s in np.nonzero(prev_sb < 0)[0]))
+        hits = set(int(b) for b in recs[i]["att_block"][:recs[i]["n_hit"]])
+        fetched = [int(b) for b in recs[i]["fetch_block"]]
+        assert not (ev & hits), f"step {i}: an evicted block counted as a hit"
+        for b in ev:
+            if b in recs[i]["slot_block"]:
+                assert b in fetched
+        # the first fetches go to the empty slots, ascending, holes included
+        nf = len(fetched)
+        assert [int(s) for s in recs[i]["fetch_slot"][:min(nf, len(empty))]] == \
+            empty[:min(nf, len(empty))]
+        assert len(holes) == len(ev)   # every forced-out block was held
+        seen += len(ev & set(fetched))
+    assert seen > 0   # some evicted blocks were selected again and re-fetched
+
+
 def test_fetch_all_equals_dense_attention_when_budget_covers_context():
     """Budget >= context and an uncapped fetch: every block is attended, so the
     sparse output is dense attention over the whole context."""
