@@ -16,8 +16,8 @@
  *
  * Sources: the OasisKV explainer page ("OasisKV: Scaling In-Decode KV Cache
  * Beyond HBM with Lookahead Sparse Prefetching"), Fig. 7 (CPU full KV, GPU
- * min/max-pooled compressed keys, sparse KV working set; the draft query
- * scans the compressed keys for the next top-K), Fig. 8 (predict -> select ->
+ * min/max-pooled compressed keys, sparse KV working set; drafts score the
+ * pooled keys to pick the next top-K), Fig. 8 (predict -> select ->
  * transfer per layer on streams), Fig. 9 (per-KV-head GPU block -> CPU block
  * table), Table 2 (fetch cap by fetch ratio, LRU eviction), the explanatory
  * diagram (diff against the GPU-resident blocks, cap the per-step transfer)
@@ -113,16 +113,19 @@ int oasis_create_shared(const oasis_layout *layout, int32_t block_size, int32_t 
 /* Wait for all work of the handle, then free everything it owns. */
 int oasis_destroy(oasis_t *h);
 
-/* Load a prompt of len tokens per sequence (synchronous).  k_host, v_host:
+/* Load a prompt of len tokens per sequence.  k_host, v_host:
  * [B][Hkv][len][d] in the layout's dtype.  Copies them into the pinned host
- * KV, builds every block summary on the GPU and empties the slot pool.
+ * KV, builds every block summary on the GPU (on `stream`) and empties the
+ * slot pool; returns once all of it is done (synchronous: the host arrays
+ * may be reused at once).
  * len <= max_tokens.  With k_host == v_host == NULL the host KV keeps the
  * prompt the last load wrote into it (OASIS_E_STATE unless that prompt had
  * len tokens) and the handle starts over from it; this is how a handle
  * sharing a buffer gets its prompt.  Either form clears every host row past
  * len that a load or an append wrote, so all handles of a shared buffer must
  * be reloaded before their next step. */
-int oasis_load_prefix(oasis_t *h, const void *k_host, const void *v_host, int64_t len);
+int oasis_load_prefix(oasis_t *h, const void *k_host, const void *v_host, int64_t len,
+                      hipStream_t stream);
 
 /* Set the residency tables (synchronous): slot_block_host[B][Hkv][S] (the
  * block each slot holds, -1 = empty) and last_used_host[B][Hkv][S] (the step
@@ -156,6 +159,10 @@ int oasis_predict(oasis_t *h, const void *q_dev, const void *drafts_dev, int32_t
 int oasis_topk_from_scores(oasis_t *h, const float *scores_dev, int32_t *block_ids_dev,
                            hipStream_t stream);
 
+/* Value of oasis_select_and_fetch's `copy` that leaves the host -> HBM copy
+ * where the handle puts it (see oasis_set_fetch_in_attention). */
+#define OASIS_COPY_DEFAULT ((hipStream_t)(intptr_t)-1)
+
 /* Diff the selection against the resident slots and fetch (OasisKV
  * explanatory diagram, capped-eviction glossary, Table 2).  Per (b, KV head):
  * hits keep their slot; the first min(cap, misses) misses in top-K order are
@@ -163,12 +170,20 @@ int oasis_topk_from_scores(oasis_t *h, const float *scores_dev, int32_t *block_i
  * held non-selected blocks, least recently used first (ties: lower block id);
  * every hit and fetched block gets last_used = this step.  cap < 0 uses the
  * handle's fetch ratio; cap is clamped to K.  The table update runs on
- * `stream`.  The host -> HBM block copies run inside the next
- * oasis_sparse_attn's kernel (bf16 layouts), or on the handle's copy stream
- * after the update; any call that needs the slots earlier (evict, select,
- * reading SLOTS) makes the copy first.  An append in between leaves the copy
- * pending: the copy then takes the whole host block, appended token included. */
-int oasis_select_and_fetch(oasis_t *h, int32_t cap, hipStream_t stream);
+ * `stream` (the compute stream).
+ * copy: the stream of the host -> HBM block copies (OasisKV Fig. 8: the
+ * transfer on a stream of its own).  A stream: the gather kernel copies the
+ * fetched blocks there right after the table update (it waits for `stream`),
+ * and the next call that reads the slots (attention, append, select, evict)
+ * waits for it.  OASIS_COPY_DEFAULT: the handle's own placement, by default
+ * inside the next oasis_sparse_attn's kernel (bf16, d = 128, block 16:
+ * fetch waves read the host blocks while the other workgroups attend to the
+ * hits, which measured faster than a separate copy the attention waits for),
+ * else the handle's copy stream.  A copy left for the attention is made
+ * earlier by any call that needs the slots first (evict, select, reading
+ * SLOTS, verify); an append in between leaves it pending, and the copy then
+ * takes the whole host block, appended token included. */
+int oasis_select_and_fetch(oasis_t *h, int32_t cap, hipStream_t stream, hipStream_t copy);
 
 /* Force blocks out of HBM (synchronous on `stream`): blocks_host
  * [B][Hkv][max_per_unit] block ids, counts_host[B][Hkv] how many of each row
@@ -177,15 +192,29 @@ int oasis_select_and_fetch(oasis_t *h, int32_t cap, hipStream_t stream);
 int oasis_evict(oasis_t *h, const int32_t *blocks_host, const int32_t *counts_host,
                 int32_t max_per_unit, hipStream_t stream);
 
+/* Forced non-residency from seeded draws, on the device (asynchronous on
+ * `stream`): per (b, KV head), floor(fraction * n) entries of the attended
+ * list of the last select (n entries) leave HBM, the entries i whose
+ * draws_dev[b][Hkv][i] are smallest (ties: lower i); their slots become
+ * empty, last_used is left as it is.  draws_dev [B][Hkv][K] fp64 device
+ * memory, 8-byte aligned, i < n read; fraction in [0, 1].  The count is
+ * floor(fraction * n + 1e-9) with the product and the sum each rounded.
+ * This is the stress of decode-time misses (the OasisKV page lists
+ * mispredicted, non-resident blocks among its limits) as a timed-step
+ * operation: no host synchronisation, later calls on other streams wait
+ * for it.  OASIS_E_STATE before the first select. */
+int oasis_evict_attended(oasis_t *h, const double *draws_dev, double fraction,
+                         hipStream_t stream);
+
 /* Sparse GQA decode attention over the attended blocks of the last
  * select (the selected blocks that are now resident), for the current query
  * q_dev [B][Hq][d]: out_dev[B][Hq][d] (fp32) = softmax(q.k / sqrt(d)) v over
  * the valid tokens of those blocks; 0 when none is attended. */
 int oasis_sparse_attn(oasis_t *h, const void *q_dev, float *out_dev, hipStream_t stream);
 
-/* Attention over the normal and draft queries together (OasisKV page, Fig. 7
- * right: the attention kernel runs the normal and draft queries over the
- * sparse KV), as speculative decoding verifies drafts.  q_dev [B][Hq][d] is
+/* Verification attention (OasisKV page, Fig. 7 right): the current query
+ * and every draft query attend over the sparse KV in one pass, as
+ * speculative decoding verifies drafts.  q_dev [B][Hq][d] is
  * the current query (position T-1); drafts_dev [n_drafts][B][Hq][d] the draft
  * queries, draft j at position T-1+j; k_drafts_dev / v_drafts_dev
  * [n_drafts][B][Hkv][d] the draft tokens' keys and values (not appended to
@@ -193,7 +222,10 @@ int oasis_sparse_attn(oasis_t *h, const void *q_dev, float *out_dev, hipStream_t
  * of q; set j attends over the attended blocks of the last select (tokens
  * < T) and draft tokens 1..j (causal).  Fetches pending from the last select
  * are copied first.  bf16 layouts with d = 128 and block_size 16 only
- * (OASIS_E_INVAL otherwise); allocates its scratch on first use. */
+ * (OASIS_E_INVAL otherwise); its scratch is allocated with the handle, for
+ * max_drafts drafts, and shared by the handle's verify calls, which run in
+ * the order they were issued (a call on another stream waits for the last
+ * attention or verify). */
 int oasis_sparse_attn_verify(oasis_t *h, const void *q_dev, const void *drafts_dev,
                              int32_t n_drafts, const void *k_drafts_dev,
                              const void *v_drafts_dev, float *out_dev, hipStream_t stream);
@@ -225,8 +257,8 @@ int oasis_decode_layers(oasis_t *const *layers, const oasis_layer_io *io, int32_
                         int32_t n_drafts, int32_t cap, hipStream_t stream, hipStream_t side);
 
 /* One decode step over the layers in the lookahead order (OasisKV page,
- * Fig. 8: the draft query of step t drives top-K prediction, KV selection and
- * KV transfer before the layer's attention at step t+1).  Per layer l, in
+ * Fig. 8: what step t's drafts predict is selected and moved to HBM before
+ * that layer attends at step t+1).  Per layer l, in
  * order: on `stream`, append io[l].k_new/v_new (when not NULL) and, when the
  * layer has selected before and io[l].q and io[l].out are not NULL, attend
  * with io[l].q over the set the previous call selected; then on `side`,
@@ -287,6 +319,17 @@ typedef struct {
     int64_t fetch_fused;      /* 1: blocks are copied host -> HBM inside oasis_sparse_attn's
                                  kernel; 0: by a copy kernel on the handle's copy stream */
 } oasis_stats;
+
+/* Residency state after the last call (synchronous; waits for the device).
+ * Each pointer may be NULL to skip it; all are host memory owned by the
+ * caller.  slot_block [B][Hkv][S]: block held by each slot, -1 empty;
+ * last_used [B][Hkv][S]: step its block was last selected or fetched;
+ * fetch_list [B][Hkv][K][2]: (block, slot) pairs fetched by the last select,
+ * -1 past fetch_n; fetch_n [B][Hkv]; attended [B][Hkv][K]: the attended
+ * blocks of the last select (hits in top-K order, then fetched), -1 past
+ * their number.  Before any select the lists are all -1 and fetch_n 0. */
+int oasis_get_state(oasis_t *h, int32_t *slot_block, int32_t *last_used, int32_t *fetch_list,
+                    int32_t *fetch_n, int32_t *attended);
 
 /* Cumulative counters (synchronous). */
 int oasis_get_stats(oasis_t *h, oasis_stats *out);

@@ -30,7 +30,7 @@ EXPORTS = [
     "oasis_create", "oasis_create_shared", "oasis_destroy", "oasis_load_prefix",
     "oasis_set_state", "oasis_decode_layers", "oasis_decode_layers_ahead",
     "oasis_append_kv", "oasis_predict", "oasis_topk_from_scores", "oasis_select_and_fetch",
-    "oasis_evict", "oasis_sparse_attn", "oasis_sparse_attn_verify", "oasis_buffer_bytes", "oasis_read", "oasis_get_stats",
+    "oasis_evict", "oasis_evict_attended", "oasis_get_state", "oasis_sparse_attn", "oasis_sparse_attn_verify", "oasis_buffer_bytes", "oasis_read", "oasis_get_stats",
     "oasis_check", "oasis_set_timing", "oasis_set_timing_period",
     "oasis_set_score_topk_fusion", "oasis_set_fetch_in_attention", "oasis_set_attend_all_resident", "oasis_get_timing", "oasis_get_dims", "oasis_tokens",
     "oasis_copy_stream", "oasis_stream_read", "oasis_kv_bytes_per_token", "oasis_cap_from_ratio",
@@ -95,13 +95,15 @@ def lib():
                                                          ctypes.POINTER(oasis_layer_io), i32, i32,
                                                          i32, i32, vp, vp, vp]),
             "oasis_destroy": (ctypes.c_int, [H]),
-            "oasis_load_prefix": (ctypes.c_int, [H, vp, vp, i64]),
+            "oasis_load_prefix": (ctypes.c_int, [H, vp, vp, i64, vp]),
             "oasis_set_state": (ctypes.c_int, [H, vp, vp]),
             "oasis_append_kv": (ctypes.c_int, [H, vp, vp, vp]),
             "oasis_predict": (ctypes.c_int, [H, vp, vp, i32, vp, vp, vp]),
             "oasis_topk_from_scores": (ctypes.c_int, [H, vp, vp, vp]),
-            "oasis_select_and_fetch": (ctypes.c_int, [H, i32, vp]),
+            "oasis_select_and_fetch": (ctypes.c_int, [H, i32, vp, vp]),
             "oasis_evict": (ctypes.c_int, [H, vp, vp, i32, vp]),
+            "oasis_evict_attended": (ctypes.c_int, [H, vp, ctypes.c_double, vp]),
+            "oasis_get_state": (ctypes.c_int, [H, vp, vp, vp, vp, vp]),
             "oasis_sparse_attn": (ctypes.c_int, [H, vp, vp, vp]),
             "oasis_sparse_attn_verify": (ctypes.c_int, [H, vp, vp, i32, vp, vp, vp, vp]),
             "oasis_buffer_bytes": (i64, [H, i32]),
@@ -152,6 +154,10 @@ def _stream(stream):
     if isinstance(stream, int):
         return stream
     return stream.cuda_stream
+
+
+# oasis_select_and_fetch's copy argument: the handle's own placement of the copy
+COPY_DEFAULT = ctypes.c_void_p(-1).value
 
 
 def kv_bytes_per_token(layers, kv_heads, head_dim, dtype_bytes) -> int:
@@ -222,10 +228,10 @@ class Oasis:
 
     # -- C-ABI calls
     def oasis_load_prefix(self, k_host: np.ndarray | None, v_host: np.ndarray | None,
-                          length: int):
+                          length: int, stream=None):
         """k_host = v_host = None: start over from the prompt already in the host KV."""
-        self._check(lib().oasis_load_prefix(self.h, _ptr(k_host), _ptr(v_host), length),
-                    "oasis_load_prefix")
+        self._check(lib().oasis_load_prefix(self.h, _ptr(k_host), _ptr(v_host), length,
+                                            _stream(stream)), "oasis_load_prefix")
 
     def oasis_set_state(self, slot_block: np.ndarray, last_used: np.ndarray):
         sb = np.ascontiguousarray(slot_block, np.int32)
@@ -245,9 +251,30 @@ class Oasis:
         self._check(lib().oasis_topk_from_scores(self.h, _ptr(scores), _ptr(block_ids),
                                                  _stream(stream)), "oasis_topk_from_scores")
 
-    def oasis_select_and_fetch(self, cap=-1, stream=None):
-        self._check(lib().oasis_select_and_fetch(self.h, cap, _stream(stream)),
+    def oasis_select_and_fetch(self, cap=-1, stream=None, copy=None):
+        """copy: the stream of the host -> HBM copy; None leaves it where the
+        handle puts it (inside the next attention by default)."""
+        cp = COPY_DEFAULT if copy is None else _stream(copy)
+        self._check(lib().oasis_select_and_fetch(self.h, cap, _stream(stream), cp),
                     "oasis_select_and_fetch")
+
+    def oasis_evict_attended(self, draws, fraction: float, stream=None):
+        """draws: float64 device tensor [B][Hkv][K]."""
+        self._check(lib().oasis_evict_attended(self.h, _ptr(draws), float(fraction),
+                                               _stream(stream)), "oasis_evict_attended")
+
+    def oasis_get_state(self) -> dict:
+        """slot_block, last_used [units][S]; fetch_list [units][K][2]; fetch_n
+        [units]; attended [units][K] (host arrays)."""
+        u = self.batch * self.kv_heads
+        sb = np.empty((u, self.slots), np.int32)
+        lu = np.empty((u, self.slots), np.int32)
+        fl = np.empty((u, self.k_blocks, 2), np.int32)
+        fn = np.empty(u, np.int32)
+        at = np.empty((u, self.k_blocks), np.int32)
+        self._check(lib().oasis_get_state(self.h, _ptr(sb), _ptr(lu), _ptr(fl), _ptr(fn),
+                                          _ptr(at)), "oasis_get_state")
+        return dict(slot_block=sb, last_used=lu, fetch_list=fl, fetch_n=fn, attended=at)
 
     def oasis_evict(self, blocks: np.ndarray, counts: np.ndarray, stream=None):
         blocks = np.ascontiguousarray(blocks, np.int32)

@@ -118,6 +118,9 @@ struct oasis_handle {
     DevStats *stats = nullptr;
     int32_t *evict_buf = nullptr;
     size_t evict_cap = 0;
+    // oasis_set_state's device copy of the held blocks: [units][S] blocks,
+    // [units][S] slots, [units] counts (allocated with the handle)
+    int32_t *set_buf = nullptr;
     // verification attention: packed query rows and per-row partials
     void *vq = nullptr;
     float *vpart_m = nullptr, *vpart_l = nullptr, *vpart_acc = nullptr;
@@ -305,6 +308,7 @@ void free_all(oasis_t *h) {
     (void)hipFree(h->err);
     (void)hipFree(h->stats);
     (void)hipFree(h->evict_buf);
+    (void)hipFree(h->set_buf);
     (void)hipFree(h->vq);
     (void)hipFree(h->vpart_m);
     (void)hipFree(h->vpart_l);
@@ -543,7 +547,18 @@ int create_handle(const oasis_layout *layout, int32_t block_size, int32_t budget
               dmal((void **)&h->part_l, sizeof(float) * units * NS * G) &&
               dmal((void **)&h->part_acc, sizeof(float) * units * NS * G * D.d) &&
               dmal((void **)&h->err, sizeof(uint32_t)) &&
-              dmal((void **)&h->stats, sizeof(DevStats) * units);
+              dmal((void **)&h->stats, sizeof(DevStats) * units) &&
+              dmal((void **)&h->set_buf, sizeof(int32_t) * units * (2 * (size_t)S + 1)) &&
+              dmal((void **)&h->evict_buf, sizeof(int32_t) * units * ((size_t)K + 1));
+    h->evict_cap = (size_t)units * (K + 1);
+    if (ok && h->plan.mfma) {
+        // verification attention scratch, sized for max_drafts
+        const size_t rows = (size_t)units * verify_rows(D, L.max_drafts);
+        ok = dmal(&h->vq, rows * 128 * sizeof(uint16_t)) &&
+             dmal((void **)&h->vpart_m, rows * h->plan.ns1 * sizeof(float)) &&
+             dmal((void **)&h->vpart_l, rows * h->plan.ns1 * sizeof(float)) &&
+             dmal((void **)&h->vpart_acc, rows * h->plan.ns1 * 128 * sizeof(float));
+    }
     if (!ok) return bail(OASIS_E_NOMEM);
     if (hipMemset(h->summ, 0, summ_bytes) != hipSuccess ||
         hipMemset(h->slots, 0, (size_t)units * S * D.block_elems() * e) != hipSuccess ||
@@ -600,7 +615,7 @@ extern "C" int oasis_destroy(oasis_t *h) {
 // ------------------------------------------------------------------ setup
 
 extern "C" int oasis_load_prefix(oasis_t *h, const void *k_host, const void *v_host,
-                                 int64_t len) {
+                                 int64_t len, hipStream_t stream) {
     if (!h) return OASIS_E_INVAL;
     if (len < 0 || len > h->L.max_tokens)
         return fail(h, OASIS_E_CAPACITY, "prefix of %lld tokens exceeds max_tokens %lld",
@@ -642,8 +657,8 @@ extern "C" int oasis_load_prefix(oasis_t *h, const void *k_host, const void *v_h
     hkv.loaded = len;
     hkv.high = len;
     h->T = h->T_prefix = len;
-    HIP_OK(h, launch_summary_build(D, h->host_kv_dev, len, h->summ, h->copy));
-    HIP_OK(h, hipStreamSynchronize(h->copy));
+    HIP_OK(h, launch_summary_build(D, h->host_kv_dev, len, h->summ, stream));
+    HIP_OK(h, hipStreamSynchronize(stream));
     TRY(reset_tables(h));
     HIP_OK(h, hipDeviceSynchronize());
     return OASIS_OK;
@@ -682,21 +697,15 @@ extern "C" int oasis_set_state(oasis_t *h, const int32_t *slot_block_host,
     HIP_OK(h, hipMemcpy(h->last_used, last_used_host, sizeof(int32_t) * units * D.S,
                         hipMemcpyHostToDevice));
     HIP_OK(h, launch_rebuild_block_slot(D, h->slot_block, h->block_slot, h->copy));
-    int32_t *dlb = nullptr, *dls = nullptr, *dcnt = nullptr;
+    int32_t *dlb = h->set_buf, *dls = dlb + lb.size(), *dcnt = dls + ls.size();
     int rc = OASIS_OK;
-    if (hipMalloc(&dlb, sizeof(int32_t) * lb.size()) != hipSuccess ||
-        hipMalloc(&dls, sizeof(int32_t) * ls.size()) != hipSuccess ||
-        hipMalloc(&dcnt, sizeof(int32_t) * cnt.size()) != hipSuccess ||
-        hipMemcpy(dlb, lb.data(), sizeof(int32_t) * lb.size(), hipMemcpyHostToDevice) != hipSuccess ||
+    if (hipMemcpy(dlb, lb.data(), sizeof(int32_t) * lb.size(), hipMemcpyHostToDevice) != hipSuccess ||
         hipMemcpy(dls, ls.data(), sizeof(int32_t) * ls.size(), hipMemcpyHostToDevice) != hipSuccess ||
         hipMemcpy(dcnt, cnt.data(), sizeof(int32_t) * cnt.size(), hipMemcpyHostToDevice) != hipSuccess ||
         launch_gather(D, h->host_kv_dev, h->slots, dlb, dls, D.S, dcnt, 1, 0, maxn, h->copy) !=
             hipSuccess ||
         hipStreamSynchronize(h->copy) != hipSuccess)
         rc = fail(h, OASIS_E_HIP, "set_state upload or payload copy failed");
-    (void)hipFree(dlb);
-    (void)hipFree(dls);
-    (void)hipFree(dcnt);
     h->selected = false;
     return rc;
 }
@@ -864,8 +873,30 @@ int select_impl(oasis_t *h, int32_t cap, hipStream_t stream, bool eager, hipStre
 
 }  // namespace
 
-extern "C" int oasis_select_and_fetch(oasis_t *h, int32_t cap, hipStream_t stream) {
-    return select_impl(h, cap, stream, false, nullptr);
+extern "C" int oasis_select_and_fetch(oasis_t *h, int32_t cap, hipStream_t stream,
+                                      hipStream_t copy) {
+    if (copy == OASIS_COPY_DEFAULT) return select_impl(h, cap, stream, false, nullptr);
+    return select_impl(h, cap, stream, true, copy);
+}
+
+extern "C" int oasis_evict_attended(oasis_t *h, const double *draws_dev, double fraction,
+                                    hipStream_t stream) {
+    if (!h || !draws_dev || !(fraction >= 0.0) || !(fraction <= 1.0))
+        return h ? fail(h, OASIS_E_INVAL, "evict_attended: bad arguments") : OASIS_E_INVAL;
+    if (((uintptr_t)draws_dev & 7u) != 0)
+        return fail(h, OASIS_E_INVAL, "evict_attended: draws not 8-byte aligned");
+    if (!h->selected) return fail(h, OASIS_E_STATE, "evict_attended before select");
+    TRY(use_stream(h, stream));
+    TRY(after(h, stream, h->m_select));  // the attended list and the tables it rewrites
+    TRY(after(h, stream, h->m_gather));
+    TRY(after(h, stream, h->m_attn));
+    TRY(after(h, stream, h->m_append));  // an append reads block_slot for its write-through
+    TRY(flush_fetch(h, stream));  // a pending copy lands before its slot is emptied
+    HIP_OK(h, launch_evict_attended(h->D, draws_dev, fraction, h->att_block, h->counts,
+                                    h->slot_block, h->block_slot, stream));
+    // later appends, selects and attentions on other streams wait for the tables
+    TRY(mark(h, h->m_select, stream));
+    return OASIS_OK;
 }
 
 extern "C" int oasis_evict(oasis_t *h, const int32_t *blocks_host, const int32_t *counts_host,
@@ -946,20 +977,13 @@ extern "C" int oasis_sparse_attn_verify(oasis_t *h, const void *q_dev, const voi
         return fail(h, OASIS_E_INVAL, "verify: needs the bf16, d = 128, block 16 layout");
     if (!h->selected) return fail(h, OASIS_E_STATE, "verify attention before select");
     const Dims &D = h->D;
-    if (!h->vq) {  // sized for max_drafts on first use
-        const int M = verify_rows(D, h->L.max_drafts);
-        const size_t rows = (size_t)D.units() * M;
-        if (hipMalloc(&h->vq, rows * 128 * sizeof(uint16_t)) != hipSuccess ||
-            hipMalloc((void **)&h->vpart_m, rows * h->plan.ns1 * sizeof(float)) != hipSuccess ||
-            hipMalloc((void **)&h->vpart_l, rows * h->plan.ns1 * sizeof(float)) != hipSuccess ||
-            hipMalloc((void **)&h->vpart_acc, rows * h->plan.ns1 * 128 * sizeof(float)) !=
-                hipSuccess)
-            return fail(h, OASIS_E_NOMEM, "verify: scratch allocation failed");
-    }
     TRY(use_stream(h, stream));
     TRY(after(h, stream, h->m_select));
     TRY(after(h, stream, h->m_gather));
     TRY(after(h, stream, h->m_append));  // the last token, written through into its slot
+    // the previous attention: its fetch waves write the slots read here, and
+    // an earlier verify on another stream uses the same scratch
+    TRY(after(h, stream, h->m_attn));
     TRY(flush_fetch(h, stream));  // every attended block resident before the passes
     // several launches: not a class of the per-kernel timers
     HIP_OK(h, launch_verify(D, h->plan, n_drafts, q_dev, drafts_dev, k_drafts_dev, v_drafts_dev,
@@ -1005,7 +1029,7 @@ extern "C" int oasis_decode_layers(oasis_t *const *layers, const oasis_layer_io 
         if (io[l].k_new) rc = oasis_append_kv(h, io[l].k_new, io[l].v_new, pre);
         if (rc == OASIS_OK)
             rc = oasis_predict(h, io[l].q, io[l].drafts, n_drafts, nullptr, nullptr, pre);
-        if (rc == OASIS_OK) rc = oasis_select_and_fetch(h, cap, pre);
+        if (rc == OASIS_OK) rc = oasis_select_and_fetch(h, cap, pre, OASIS_COPY_DEFAULT);
         if (rc == OASIS_OK && !overlap) rc = oasis_sparse_attn(h, io[l].q, io[l].out, stream);
         if (rc != OASIS_OK) bad = l;
     }
@@ -1174,6 +1198,48 @@ extern "C" int oasis_read(oasis_t *h, int32_t which, int64_t offset, int64_t nby
     }
     HIP_OK(h, hipMemcpy(dst_host, (const char *)src + offset, (size_t)nbytes,
                         hipMemcpyDeviceToHost));
+    return OASIS_OK;
+}
+
+extern "C" int oasis_get_state(oasis_t *h, int32_t *slot_block, int32_t *last_used,
+                               int32_t *fetch_list, int32_t *fetch_n, int32_t *attended) {
+    if (!h) return OASIS_E_INVAL;
+    const Dims &D = h->D;
+    const int64_t units = D.units();
+    HIP_OK(h, hipDeviceSynchronize());
+    if (slot_block)
+        HIP_OK(h, hipMemcpy(slot_block, h->slot_block, sizeof(int32_t) * units * D.S,
+                            hipMemcpyDeviceToHost));
+    if (last_used)
+        HIP_OK(h, hipMemcpy(last_used, h->last_used, sizeof(int32_t) * units * D.S,
+                            hipMemcpyDeviceToHost));
+    if (!fetch_list && !fetch_n && !attended) return OASIS_OK;
+    std::vector<int32_t> cnt((size_t)units * 4, 0);
+    if (h->selected)
+        HIP_OK(h, hipMemcpy(cnt.data(), h->counts, sizeof(int32_t) * cnt.size(),
+                            hipMemcpyDeviceToHost));
+    std::vector<int32_t> a((size_t)units * D.K), b((size_t)units * D.K);
+    if (fetch_list) {
+        HIP_OK(h, hipMemcpy(a.data(), h->fetch_block, sizeof(int32_t) * a.size(),
+                            hipMemcpyDeviceToHost));
+        HIP_OK(h, hipMemcpy(b.data(), h->fetch_slot, sizeof(int32_t) * b.size(),
+                            hipMemcpyDeviceToHost));
+        for (int64_t u = 0; u < units; ++u)
+            for (int i = 0; i < D.K; ++i) {
+                const bool v = i < cnt[u * 4 + 2];
+                fetch_list[(u * D.K + i) * 2 + 0] = v ? a[u * D.K + i] : -1;
+                fetch_list[(u * D.K + i) * 2 + 1] = v ? b[u * D.K + i] : -1;
+            }
+    }
+    if (fetch_n)
+        for (int64_t u = 0; u < units; ++u) fetch_n[u] = cnt[u * 4 + 2];
+    if (attended) {
+        HIP_OK(h, hipMemcpy(a.data(), h->att_block, sizeof(int32_t) * a.size(),
+                            hipMemcpyDeviceToHost));
+        for (int64_t u = 0; u < units; ++u)
+            for (int i = 0; i < D.K; ++i)
+                attended[u * D.K + i] = i < cnt[u * 4 + 0] ? a[u * D.K + i] : -1;
+    }
     return OASIS_OK;
 }
 

@@ -112,6 +112,13 @@ hipError_t launch_evict(const Dims &D, const int32_t *blocks, const int32_t *cou
                         int max_per_unit, int32_t *slot_block, int32_t *block_slot,
                         hipStream_t st);
 
+// Forced non-residency from seeded draws [units][K]: unit u empties the slots
+// of floor(fraction * n_att) entries of its attended list, those with the
+// smallest draws (ties to the lower position).  K <= 1024.
+hipError_t launch_evict_attended(const Dims &D, const double *draws, double fraction,
+                                const int32_t *att_block, const int32_t *counts,
+                                int32_t *slot_block, int32_t *block_slot, hipStream_t st);
+
 // Rebuild block_slot from slot_block (after oasis_set_state).
 hipError_t launch_rebuild_block_slot(const Dims &D, const int32_t *slot_block,
                                      int32_t *block_slot, hipStream_t st);

@@ -562,7 +562,15 @@ __device__ void select_unit(int64_t u, const int32_t *sel, const int32_t *sb_in,
     for (int s = lane; s < S; s += 64) nvict += vkey[s] != ~0ull ? 1 : 0;
     nvict = wave_sum_i(nvict);
     if (nfree + nvict < n) {  // cannot happen with S >= K
-        if (lane == 0) atomicOr(err, kErrSlots);
+        // tables untouched; the lists of this step are empty, so the next
+        // attention attends nothing instead of the previous step's list
+        if (lane == 0) {
+            atomicOr(err, kErrSlots);
+            counts[u * 4 + 0] = 0;
+            counts[u * 4 + 1] = 0;
+            counts[u * 4 + 2] = 0;
+            counts[u * 4 + 3] = nm;
+        }
         return;
     }
 
@@ -814,6 +822,39 @@ __global__ __launch_bounds__(64) void evict_kernel(const int32_t *__restrict__ b
     }
 }
 
+// Forced non-residency from seeded draws: unit u empties the slots of
+// floor(fraction * n_att) entries of its last attended list, the entries whose
+// draws[u][i] are smallest (ties to the lower list position); recency is left
+// as it is.  The count uses a separately rounded product and sum (no fused
+// multiply-add), as the draws' consumer on the host computes it.
+__global__ __launch_bounds__(256) void evict_attended_kernel(
+    const double *__restrict__ draws, double fraction, const int32_t *__restrict__ att_block,
+    const int32_t *__restrict__ counts, int32_t *__restrict__ slot_block,
+    int32_t *__restrict__ block_slot, int K, int S, int64_t NBmax) {
+    __shared__ double dr[1024];
+    const int64_t u = blockIdx.x;
+    const int na = __builtin_amdgcn_readfirstlane(counts[u * 4]);
+    const int n = (int)floor(__dadd_rn(__dmul_rn(fraction, (double)na), 1e-9));
+    if (n <= 0) return;
+    for (int i = threadIdx.x; i < na; i += 256) dr[i] = draws[u * K + i];
+    __syncthreads();
+    for (int i = threadIdx.x; i < na; i += 256) {
+        const double di = dr[i];
+        int rank = 0;
+        for (int j = 0; j < na; ++j) {
+            const double dj = dr[j];
+            rank += (dj < di || (dj == di && j < i)) ? 1 : 0;
+        }
+        if (rank >= n) continue;
+        const int32_t blk = att_block[u * K + i];
+        if (blk < 0 || blk >= NBmax) continue;
+        const int32_t s = block_slot[u * NBmax + blk];
+        if (s < 0) continue;
+        slot_block[u * S + s] = -1;
+        block_slot[u * NBmax + blk] = -1;
+    }
+}
+
 __global__ __launch_bounds__(256) void rebuild_block_slot_kernel(
     const int32_t *__restrict__ slot_block, int32_t *__restrict__ block_slot, int S,
     int64_t NBmax) {
@@ -980,6 +1021,15 @@ hipError_t launch_evict(const Dims &D, const int32_t *blocks, const int32_t *cou
                         hipStream_t st) {
     OASIS_LAUNCH(evict_kernel, dim3((unsigned)D.units()), dim3(64), 0, st, blocks, counts,
                        max_per_unit, slot_block, block_slot, D.S, D.NBmax);
+    return hipGetLastError();
+}
+
+hipError_t launch_evict_attended(const Dims &D, const double *draws, double fraction,
+                                const int32_t *att_block, const int32_t *counts,
+                                int32_t *slot_block, int32_t *block_slot, hipStream_t st) {
+    if (D.K > 1024) return hipErrorInvalidValue;
+    OASIS_LAUNCH(evict_attended_kernel, dim3((unsigned)D.units()), dim3(256), 0, st, draws,
+                 fraction, att_block, counts, slot_block, block_slot, D.K, D.S, D.NBmax);
     return hipGetLastError();
 }
 

@@ -12,6 +12,8 @@ Tolerances (written here, used by every parity test):
 """
 from __future__ import annotations
 
+from concurrent.futures import ThreadPoolExecutor
+
 import numpy as np
 import torch
 
@@ -27,6 +29,47 @@ ATTN_TOL = 2e-3
 
 def log(msg):
     print(msg, flush=True)
+
+
+_POOL = None
+
+
+def pool():
+    """Host threads for the oracle units (its C calls release the GIL)."""
+    global _POOL
+    if _POOL is None:
+        import os
+        _POOL = ThreadPoolExecutor(max(1, min(16, len(os.sched_getaffinity(0)))))
+    return _POOL
+
+
+def every_unit(w):
+    return [(b, h) for b in range(w.batch) for h in range(w.kv_heads)]
+
+
+def device_evictions(w, h, t, layer):
+    """Forced evictions of step t applied on the device (oasis_evict_attended)
+    from the seeded draws.  Checks the slot table afterwards against the
+    harness rule applied to the GPU's own previous attended lists, for every
+    unit (bit-exact), and returns the evicted blocks per unit."""
+    K, S = h.k_blocks, h.slots
+    ab, cnt, sb0 = h.read("ATT_BLOCK"), h.read("COUNTS"), h.read("SLOT_BLOCK")
+    draws = synth.evict_draws(w, t, layer)
+    h.oasis_evict_attended(torch.from_numpy(np.ascontiguousarray(draws)).cuda(),
+                           w.forced_evict_frac)
+    sb1 = h.read("SLOT_BLOCK")
+    out = {}
+    for b in range(w.batch):
+        for hh in range(w.kv_heads):
+            u = b * w.kv_heads + hh
+            na = int(cnt[u * 4])
+            ev = synth.forced_evictions(w, ab[u * K:u * K + na], na, draws[b, hh])
+            exp = sb0[u * S:(u + 1) * S].copy()
+            exp[np.isin(exp, ev)] = -1
+            assert np.array_equal(sb1[u * S:(u + 1) * S], exp), \
+                f"step {t} unit {(b, hh)}: device evictions differ"
+            out[(b, hh)] = ev
+    return out
 
 
 def score_scale(unit: oracle.Unit, x_rows: np.ndarray) -> np.ndarray:
@@ -57,8 +100,8 @@ class Parity:
         self.K, self.V = K, V
         self.run = LayerRunner(w, n_steps, layer, kv=(K, V))
         self.cap = workload_cap(w)
-        self.oru = {(b, h): initial_unit(w, b, h, n_steps, layer, kv=(K[b, h], V[b, h]))
-                    for (b, h) in self.units}
+        mk = lambda k: initial_unit(w, k[0], k[1], n_steps, layer, kv=(K[k[0], k[1]], V[k[0], k[1]]))
+        self.oru = dict(zip(self.units, pool().map(mk, self.units)))
         self.qf = oracle.to_f64(synth.queries(w, layer), w.dtype)
         self.G = w.group
         h = self.run.h
@@ -101,9 +144,20 @@ class Parity:
         ab, ast = h.read("ATT_BLOCK"), h.read("ATT_SLOT")
         cnt = h.read("COUNTS")
         bsl = h.read("BLOCK_SLOT")
+        st = h.oasis_get_state()   # the same state through oasis_get_state
         for (b, hh) in self.units:
             r = rec[(b, hh)]
             tag = f"step {t} unit {(b, hh)}"
+            u = b * w.kv_heads + hh
+            nf_o, na_o = len(r["fetch_block"]), len(r["att_block"])
+            assert np.array_equal(st["slot_block"][u], r["slot_block"]), tag + " get_state slots"
+            assert np.array_equal(st["last_used"][u], r["last_used"]), tag + " get_state lru"
+            assert st["fetch_n"][u] == nf_o, tag + " get_state fetch_n"
+            assert np.array_equal(st["fetch_list"][u, :nf_o, 0], r["fetch_block"]), tag
+            assert np.array_equal(st["fetch_list"][u, :nf_o, 1], r["fetch_slot"]), tag
+            assert np.all(st["fetch_list"][u, nf_o:] == -1), tag + " get_state fetch pad"
+            assert np.array_equal(st["attended"][u, :na_o], r["att_block"]), tag
+            assert np.all(st["attended"][u, na_o:] == -1), tag + " get_state attended pad"
             assert np.array_equal(self._unit_slice(ids, b, hh, K), r["ids"]), tag + " ids"
             c = self._unit_slice(cnt, b, hh, 4)
             na, nh, nf = int(c[0]), int(c[1]), int(c[2])
@@ -154,15 +208,19 @@ class Parity:
 
     # ------------------------------------------------------------ stepping
     def _oracle_step(self, t, append, cap, evictions=None):
-        rec = {}
-        worst_rel = 0.0
         drafts = oracle.to_f64(synth.drafts(self.w, t, self.layer), self.w.dtype)
-        for (b, hh) in self.units:
+
+        def one(key):
+            b, hh = key
             x, cur = oracle.unit_rows(self.qf, drafts, b, hh, self.G)
-            ev = None if evictions is None else evictions[(b, hh)]
-            rec[(b, hh)] = self.oru[(b, hh)].step(t, x, cur, cap, append=append, evict_blocks=ev)
-            rec[(b, hh)]["x"] = x
-        return rec
+            ev = None if evictions is None else evictions[key]
+            r = self.oru[key].step(t, x, cur, cap, append=append, evict_blocks=ev)
+            r["x"] = x
+            return r
+
+        if len(self.units) > 4:
+            return dict(zip(self.units, pool().map(one, self.units)))
+        return {k: one(k) for k in self.units}
 
     def _compare_scores(self, t, rec):
         gpu = self.scores_dev.cpu().numpy()
@@ -184,10 +242,24 @@ class Parity:
             fed[b, hh, :nb] = rec[(b, hh)]["scores32"]
         self.run.h.oasis_topk_from_scores(torch.from_numpy(fed).cuda())
 
+    device_evict = False   # apply forced evictions with oasis_evict_attended
+
     def forced_evictions(self, t):
         """Host-side draws of the stress workload applied to the GPU's own
-        previous attended lists (read back), same rule as the oracle."""
+        previous attended lists (read back), same rule as the oracle; by the
+        host-built block lists (oasis_evict) or on the device from the draws
+        (oasis_evict_attended)."""
         w, h = self.w, self.run.h
+        if self.device_evict:
+            per_unit = device_evictions(w, h, t, self.layer)
+            draws = synth.evict_draws(w, t, self.layer)
+            out = {}
+            for key in self.units:
+                prev = self.prev_att.get(key, np.zeros(0, np.int32))
+                mine = synth.forced_evictions(w, prev, len(prev), draws[key[0], key[1]])
+                assert np.array_equal(mine, per_unit[key]), f"step {t} unit {key} evictions differ"
+                out[key] = mine
+            return out
         K = h.k_blocks
         ab, cnt = h.read("ATT_BLOCK"), h.read("COUNTS")
         draws = synth.evict_draws(w, t, self.layer)
@@ -262,6 +334,7 @@ class FreeRunning(Parity):
 
     q_layer = None   # layer whose query the drafts perturb (None: self.layer)
     attend_all = False  # attended set: every block held after the step
+    copy_stream = None  # select_and_fetch's copy stream (None: the handle's placement)
 
     def _tables(self):
         h = self.run.h
@@ -346,7 +419,12 @@ class FreeRunning(Parity):
         else:
             prev = self._tables()
         for t in range(1, steps + 1):
-            if w.forced_evict_frac > 0:
+            if w.forced_evict_frac > 0 and self.device_evict:
+                for key, ev in device_evictions(w, h, t, self.layer).items():
+                    if key in prev:
+                        sb0 = prev[key][0]
+                        sb0[np.isin(sb0, ev)] = -1
+            elif w.forced_evict_frac > 0:
                 ab, cnt = h.read("ATT_BLOCK"), h.read("COUNTS")
                 draws = synth.evict_draws(w, t, self.layer)
                 blocks = np.full((w.batch * w.kv_heads, K), -1, np.int32)
@@ -366,7 +444,7 @@ class FreeRunning(Parity):
             h.oasis_append_kv(run.app_k[t - 1], run.app_v[t - 1])
             h.oasis_predict(run.q, run.drafts[t], w.drafts,
                             scores=None if fuse else self.scores_dev)
-            h.oasis_select_and_fetch(self.cap)
+            h.oasis_select_and_fetch(self.cap, copy=self.copy_stream)
             h.oasis_sparse_attn(run.q, run.out)
             torch.cuda.synchronize()
             h.oasis_check()

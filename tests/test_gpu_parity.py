@@ -112,6 +112,33 @@ def test_qwen3_32b_forced_eviction_full_size_sampled_units():
     log(f"{w.name}: {rep}")
 
 
+# Every (batch row, KV head) unit at full size: the admission step and two
+# decode steps, each unit recomputed by the oracle on host threads.
+
+def _every_unit(w, steps=2, device_evict=False):
+    from tests.gpu_parity import Parity, every_unit, log
+    p = Parity(w, steps, every_unit(w))
+    p.device_evict = device_evict
+    rep = p.run_all(check_payload_every=1)
+    log(f"{w.name}, all {len(p.units)} units: {rep}")
+    assert rep["steps"] == steps
+
+
+def test_qwen3_8b_layer_full_size_every_unit():
+    _every_unit(synth.QWEN3_8B)
+
+
+def test_llama31_8b_long_context_full_size_every_unit():
+    _every_unit(synth.LLAMA31_8B_LONG)
+
+
+def test_qwen3_32b_full_size_every_unit_device_evictions():
+    """The forced evictions applied by oasis_evict_attended from the seeded
+    draws, checked on every unit against the harness rule on the GPU's own
+    attended lists and against the oracle's."""
+    _every_unit(synth.QWEN3_32B, device_evict=True)
+
+
 # ------------------------------------------------------------------ free-running
 # The GPU selects on its own scores with the fused top-K + select kernel;
 # every step is checked against the oracle functions applied to its state.
@@ -134,6 +161,59 @@ def test_qwen3_32b_free_running_with_forced_evictions():
     w = synth.QWEN3_32B
     rep = FreeRunning(w, 16, [(0, 0), (7, 5), (15, 7)]).run_free(check_payload_every=4)
     log(f"{w.name} free: {rep}")
+
+
+def test_llama31_8b_long_context_free_running_sampled_units():
+    """128K context (8,196 blocks per KV head): the production selection path,
+    the top-K + select kernel at 1,024 threads, on the GPU's own scores."""
+    from tests.gpu_parity import FreeRunning, log
+    w = synth.LLAMA31_8B_LONG
+    rep = FreeRunning(w, 12, [(0, 3), (4, 6), (7, 7)]).run_free(check_payload_every=6)
+    log(f"{w.name} free: {rep}")
+
+
+def test_qwen3_32b_free_running_device_evictions():
+    from tests.gpu_parity import FreeRunning, log
+    w = synth.QWEN3_32B
+    p = FreeRunning(w, 16, [(0, 0), (7, 5), (15, 7)])
+    p.device_evict = True
+    rep = p.run_free(check_payload_every=4)
+    log(f"{w.name} free, device evictions: {rep}")
+
+
+def test_select_and_fetch_on_an_explicit_copy_stream():
+    """oasis_select_and_fetch(cap, stream, copy) with a copy stream of the
+    caller's: the fetched blocks are copied there after the table update and
+    the attention waits for them.  Checked free-running against the oracle,
+    and equal (tables, payloads bit-exact; outputs up to the split-K merge
+    order) to the default placement inside the attention."""
+    from lookahead_sparse_kv_oasis_amd.runner import LayerRunner
+    from tests.gpu_parity import FreeRunning, log
+    w = synth.QWEN3_8B.with_(batch=4, prefix_tokens=16 * 600 + 9)
+    p = FreeRunning(w, 6, [(0, 0), (3, 7), (2, 4)])
+    p.copy_stream = torch.cuda.Stream()
+    rep = p.run_free(check_payload_every=2)
+    log(f"explicit copy stream: {rep}")
+    a, b = LayerRunner(w, 4), LayerRunner(w, 4)
+    st = a.h.oasis_get_state()
+    assert np.all(st["fetch_list"] == -1) and np.all(st["fetch_n"] == 0)
+    assert np.all(st["attended"] == -1) and np.all(st["slot_block"] == -1)
+    cp = torch.cuda.Stream()
+    for r in (a, b):
+        r.admission()
+    for t in range(1, 5):
+        for r, copy in ((a, cp), (b, None)):
+            r.h.oasis_append_kv(r.app_k[t - 1], r.app_v[t - 1])
+            r.h.oasis_predict(r.q, r.drafts[t], w.drafts)
+            r.h.oasis_select_and_fetch(r.cap, copy=copy)
+            r.h.oasis_sparse_attn(r.q, r.out)
+        torch.cuda.synchronize()
+        assert float((a.out - b.out).abs().max()) <= 1e-5, f"step {t}"
+        sa, sb = a.h.oasis_get_state(), b.h.oasis_get_state()
+        for k in sa:
+            assert np.array_equal(sa[k], sb[k]), f"step {t}: {k}"
+    assert np.array_equal(a.h.read("SLOTS", np.uint8), b.h.read("SLOTS", np.uint8))
+    a.h.oasis_check()
 
 
 # ------------------------------------------------------------------ lookahead ordering

@@ -127,17 +127,47 @@ def test_decode_layers_rejects_bad_arguments():
     mr.close()
 
 
-@pytest.mark.slow
-def test_qwen3_8b_36_layers_full_size_sampled_layers():
-    """The 36-layer model at batch 64 and 64K context (two data layers),
-    overlapped schedule, fetch ratio 0.02."""
+@pytest.fixture(scope="module")
+def full_model():
+    """The 36-layer model at batch 64 and 64K context (two data layers)."""
     w = synth.QWEN3_8B_36L
     mr = _runner(w, w.steps)
+    yield mr
+    mr.close()
+
+
+@pytest.mark.slow
+def test_qwen3_8b_36_layers_full_size_sampled_layers(full_model):
+    """Overlapped schedule, fetch ratio 0.02 (cap 2), every step."""
+    mr, w = full_model, full_model.w
+    mr.reset()
     side = torch.cuda.Stream()
     rep = _check_layers(mr, [0, 19, 35], [(0, 0), (37, 3), (63, 7)], w.steps, side,
                         check_payload_every=8)
     _log(f"{w.name}: {rep}")
-    mr.close()
+
+
+@pytest.mark.slow
+def test_qwen3_8b_36_layers_full_size_fetch_ratio_sweep(full_model):
+    """The fetch-ratio sweep of the 36-layer workload (ratios 0.01, 0.02, 0.05,
+    0.10, 0.20 and fetch-all: caps 1, 2, 6, 12, 25, 128 per KV head), each
+    from the prompt (reset) for 4 decode steps, layers 0, 19 and 35 checked
+    free-running against the oracle at every step."""
+    mr, w = full_model, full_model.w
+    side = torch.cuda.Stream()
+    units = [(0, 0), (37, 3), (63, 7)]
+    caps = [oracle_cap(r, w.k_blocks) for r in synth.FETCH_RATIO_SWEEP]
+    assert caps == [1, 2, 6, 12, 25, 128]
+    for cap in caps:
+        mr.reset()
+        rep = _check_layers(mr, [0, 19, 35], units, 4, side, cap=cap, check_payload_every=2)
+        _log(f"{w.name}, cap {cap}: {rep}")
+        assert all(r["steps"] == 4 for r in rep)
+
+
+def oracle_cap(ratio, k):
+    import oracle
+    return oracle.cap_from_ratio(ratio, k)
 
 
 AHEAD_SMALL = synth.QWEN3_8B_36L_AHEAD.with_(batch=4, prefix_tokens=16 * 300 + 5, layers=5,
@@ -334,6 +364,54 @@ def test_select_after_append_and_attention_twice_on_other_streams():
         torch.cuda.synchronize()
         assert torch.equal(a.out, b.out), f"step {t}: first attention differs"
         assert torch.equal(out2[id(a)], out2[id(b)]), f"step {t}: second attention differs"
+    for buf in STATE_BUFS:
+        assert np.array_equal(a.h.read(buf), b.h.read(buf)), buf
+    assert np.array_equal(a.h.read("SLOTS", np.uint8), b.h.read("SLOTS", np.uint8))
+    a.h.oasis_check()
+
+
+def test_verify_and_device_evictions_on_other_streams():
+    """Per step: forced evictions (oasis_evict_attended) on a second stream,
+    then append, predict, select and attention on the first, then the
+    verification attention on the second stream again, nothing synchronising
+    in between.  The evictions wait for the previous attention and the append
+    for them; the verify waits for the attention's fetch.  Everything equals
+    the same calls on one stream bit for bit, and set 0 of the verify equals
+    the attention up to the split-K merge order."""
+    from lookahead_sparse_kv_oasis_amd.runner import LayerRunner, to_device
+    w = synth.QWEN3_32B.with_(batch=4, prefix_tokens=16 * 400 + 5, budget_tokens=16 * 64)
+    n = 6
+    a, b = LayerRunner(w, n), LayerRunner(w, n)
+    cur, s2 = torch.cuda.current_stream(), torch.cuda.Stream()
+    D, B, Hkv, d = w.drafts, w.batch, w.kv_heads, w.head_dim
+    rng = np.random.default_rng(3)
+    vout = {id(r): torch.empty((1 + D, B, w.q_heads, d), dtype=torch.float32, device="cuda")
+            for r in (a, b)}
+    draws = [torch.from_numpy(np.ascontiguousarray(synth.evict_draws(w, t))).cuda()
+             for t in range(n + 1)]
+    kd = [to_device(synth.encode(rng.standard_normal((D, B, Hkv, d)).astype(np.float32),
+                                 w.dtype)) for _ in range(n + 1)]
+    vd = [to_device(synth.encode(rng.standard_normal((D, B, Hkv, d)).astype(np.float32),
+                                 w.dtype)) for _ in range(n + 1)]
+    a.admission()
+    b.admission()
+    torch.cuda.synchronize()
+    for t in range(1, n + 1):
+        for r, other in ((a, s2), (b, cur)):
+            h = r.h
+            h.oasis_evict_attended(draws[t], w.forced_evict_frac, stream=other)
+            h.oasis_append_kv(r.app_k[t - 1], r.app_v[t - 1], stream=cur)
+            h.oasis_predict(r.q, r.drafts[t], w.drafts, stream=cur)
+            h.oasis_select_and_fetch(r.cap, stream=cur)
+            h.oasis_sparse_attn(r.q, r.out, stream=cur)
+            h.oasis_sparse_attn_verify(r.q, r.drafts[t], D, kd[t], vd[t], vout[id(r)],
+                                       stream=other)
+        torch.cuda.synchronize()
+        assert torch.equal(a.out, b.out), f"step {t}: outputs differ"
+        assert torch.equal(vout[id(a)], vout[id(b)]), f"step {t}: verify differs"
+        assert float((vout[id(a)][0] - a.out).abs().max()) < 1e-5, f"step {t}: set 0"
+        st = a.h.oasis_get_stats()
+        assert st["misses"] > 0
     for buf in STATE_BUFS:
         assert np.array_equal(a.h.read(buf), b.h.read(buf)), buf
     assert np.array_equal(a.h.read("SLOTS", np.uint8), b.h.read("SLOTS", np.uint8))
