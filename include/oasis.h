@@ -94,7 +94,9 @@ typedef struct oasis_handle oasis_t;
  * Environment, read here: OASIS_SCORE_IMPL=valu keeps bf16 summaries
  * block-major and scores them on the vector ALU instead of the matrix cores;
  * OASIS_GATHER=stream starts the handle with the fetch outside the attention
- * (as oasis_set_fetch_in_attention(h, 0)). */
+ * (as oasis_set_fetch_in_attention(h, 0)); OASIS_ATTN_SPLIT=1 runs the
+ * attention over the resident blocks as fixed splits per (b, KV head)
+ * instead of runs balanced over all of them (for comparisons). */
 int oasis_create(const oasis_layout *layout, int32_t block_size, int32_t budget_tokens,
                  float fetch_ratio, oasis_t **out);
 

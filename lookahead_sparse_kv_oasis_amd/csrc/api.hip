@@ -529,7 +529,7 @@ int create_handle(const oasis_layout *layout, int32_t block_size, int32_t budget
     h->host_kv_dev = h->hkv->dev;
 
     auto dmal = [&](void **p, size_t bytes) { return hipMalloc(p, bytes ? bytes : 16) == hipSuccess; };
-    const int NS = h->plan.nsa;
+    const int64_t PR = attn_partial_rows(D, h->plan);
     const size_t summ_bytes = (size_t)units * D.summ_unit_elems() * e;
     bool ok = dmal(&h->summ, summ_bytes) &&
               dmal(&h->slots, (size_t)units * S * D.block_elems() * e) &&
@@ -543,9 +543,9 @@ int create_handle(const oasis_layout *layout, int32_t block_size, int32_t budget
               dmal((void **)&h->att_block, sizeof(int32_t) * units * K) &&
               dmal((void **)&h->att_slot, sizeof(int32_t) * units * K) &&
               dmal((void **)&h->counts, sizeof(int32_t) * units * 4) &&
-              dmal((void **)&h->part_m, sizeof(float) * units * NS * G) &&
-              dmal((void **)&h->part_l, sizeof(float) * units * NS * G) &&
-              dmal((void **)&h->part_acc, sizeof(float) * units * NS * G * D.d) &&
+              dmal((void **)&h->part_m, sizeof(float) * PR) &&
+              dmal((void **)&h->part_l, sizeof(float) * PR) &&
+              dmal((void **)&h->part_acc, sizeof(float) * PR * D.d) &&
               dmal((void **)&h->err, sizeof(uint32_t)) &&
               dmal((void **)&h->stats, sizeof(DevStats) * units) &&
               dmal((void **)&h->set_buf, sizeof(int32_t) * units * (2 * (size_t)S + 1)) &&

@@ -13,6 +13,8 @@
 // combine kernel merges the partials of a unit.
 #include <stdlib.h>
 
+#include <algorithm>
+
 #include "kernels.h"
 
 namespace oasis {
@@ -124,14 +126,19 @@ template <int G> struct AttnWave {
     }
     // Queries of unit (b, h) and a cleared softmax state.
     __device__ __forceinline__ void init(const uint16_t *q, int64_t b, int Hq, int h) {
+        load_q(qb, q, b, Hq, h);
+        reset();
+    }
+    // The query rows of unit (b, h) in the B-operand order (heads past G zero).
+    __device__ __forceinline__ void load_q(bf16x8 (&dst)[4], const uint16_t *q, int64_t b, int Hq,
+                                           int h) const {
         const uint16_t *qr = q + (b * Hq + h * G + (col < G ? col : 0)) * D + 8 * kg;
 #pragma unroll
         for (int i = 0; i < 4; ++i) {
             uint4 w = *reinterpret_cast<const uint4 *>(qr + 32 * i);
             if (col >= G) w = make_uint4(0, 0, 0, 0);
-            qb[i] = __builtin_bit_cast(bf16x8, w);
+            dst[i] = __builtin_bit_cast(bf16x8, w);
         }
-        reset();
     }
     __device__ __forceinline__ void reset() {
         m = -INFINITY;
@@ -280,11 +287,15 @@ template <int G> struct AttnWaveM {
         voff = BS * D + 4 * kg * D + 8 * col;
     }
     __device__ __forceinline__ void init(const uint16_t *q, int64_t b, int Hq, int h) {
+        load_q(qb, q, b, Hq, h);
+        reset();
+    }
+    __device__ __forceinline__ void load_q(bf16x8 (&dst)[4], const uint16_t *q, int64_t b, int Hq,
+                                           int h) const {
         const uint16_t *qr = q + (b * Hq + h * G + col) * D + 8 * kg;
 #pragma unroll
         for (int i = 0; i < 4; ++i)
-            qb[i] = __builtin_bit_cast(bf16x8, *reinterpret_cast<const uint4 *>(qr + 32 * i));
-        reset();
+            dst[i] = __builtin_bit_cast(bf16x8, *reinterpret_cast<const uint4 *>(qr + 32 * i));
     }
     __device__ __forceinline__ void reset() {
         m = -INFINITY;
@@ -400,6 +411,85 @@ __device__ __forceinline__ int block_valid(int64_t T, int32_t blk) {
     return (int)((T - first) < 16 ? (T - first) : 16);
 }
 
+// Fetch waves of a fused launch (mode 1): item i of unit u, i < cap, is the
+// i-th block fetched for u this step (attended entry n_att - n_fetch + i: the
+// fetched blocks end the list).  Wave f of the F = 4 n_fetch_wg fetch waves
+// takes items f, f + F, ...: it reads the block from the pinned host KV over
+// the host link, writes it into its slot (the copy later steps will hit),
+// attends to it from registers and writes partial i of the unit; an item past
+// the unit's fetch count writes an empty partial.  A few such waves keep the
+// host link saturated while holding only a small share of the CU slots.
+template <int G, typename W>
+__device__ __forceinline__ void fetch_waves(
+    W &st, int wave, const uint16_t *__restrict__ q, uint16_t *__restrict__ slots,
+    const uint16_t *__restrict__ host_kv, const int32_t *__restrict__ att_block,
+    const int32_t *__restrict__ att_slot, const int32_t *__restrict__ counts, int64_t T_, int Hq,
+    int Hkv, int K, int S, int64_t NBmax, int cap, int n_fetch_wg, int nsa, int64_t units,
+    float scale_log2, float *__restrict__ part_m, float *__restrict__ part_l,
+    float *__restrict__ part_acc) {
+    const int64_t F = 4LL * n_fetch_wg;
+    const int64_t n_items = units * cap;
+    int64_t it = (int64_t)blockIdx.x * 4 + wave;
+    int64_t cur_u = -1;
+    uint4 kr[2][4], vr[2][4];
+    // item -> (unit, i, entry); returns the source block pointer or null
+    auto locate = [&](int64_t item, int64_t &u, int &i, int32_t &blk, int32_t &slot) -> bool {
+        u = item / cap;
+        i = (int)(item % cap);
+        const int n_att = __builtin_amdgcn_readfirstlane(counts[u * 4 + 0]);
+        const int n_fetch = __builtin_amdgcn_readfirstlane(counts[u * 4 + 2]);
+        if (i >= n_fetch) return false;
+        const int e = n_att - n_fetch + i;  // the fetched blocks end the list
+        blk = __builtin_amdgcn_readfirstlane(att_block[u * K + e]);
+        slot = __builtin_amdgcn_readfirstlane(att_slot[u * K + e]);
+        return true;
+    };
+    int64_t u0;
+    int i0;
+    int32_t blk0 = 0, slot0 = 0;
+    bool have0 = it < n_items && locate(it, u0, i0, blk0, slot0);
+    if (it < n_items && have0) st.load(kr[0], vr[0], host_kv + (u0 * NBmax + blk0) * W::BLK);
+    int buf = 0;
+    for (; it < n_items; it += F) {
+        // prefetch the next item while this one is processed
+        const int64_t nx = it + F;
+        int64_t u1 = 0;
+        int i1 = 0;
+        int32_t blk1 = 0, slot1 = 0;
+        const bool have1 = nx < n_items && locate(nx, u1, i1, blk1, slot1);
+        if (have1) {
+            if (buf == 0) st.load(kr[1], vr[1], host_kv + (u1 * NBmax + blk1) * W::BLK);
+            else st.load(kr[0], vr[0], host_kv + (u1 * NBmax + blk1) * W::BLK);
+        }
+        __builtin_amdgcn_sched_barrier(0);  // keep the prefetch ahead of the compute
+        if (u0 != cur_u) {
+            const int64_t b = u0 / Hkv;
+            st.init(q, b, Hq, (int)(u0 % Hkv));
+            cur_u = u0;
+        } else {
+            st.reset();
+        }
+        if (have0) {
+            uint16_t *dst = slots + (u0 * S + slot0) * (int64_t)W::BLK;
+            if (buf == 0) {
+                st.store(dst, kr[0], vr[0]);
+                st.block(kr[0], vr[0], block_valid(T_, blk0), scale_log2);
+            } else {
+                st.store(dst, kr[1], vr[1]);
+                st.block(kr[1], vr[1], block_valid(T_, blk0), scale_log2);
+            }
+        }
+        st.reduce();
+        st.write_partial((u0 * nsa + i0) * G, part_m, part_l, part_acc);
+        u0 = u1;
+        i0 = i1;
+        blk0 = blk1;
+        slot0 = slot1;
+        have0 = have1;
+        buf ^= 1;
+    }
+}
+
 // Grid (1-D, 256 threads = 4 waves per workgroup):
 //   workgroups [0, n_fetch_wg): fetch waves (mode 1 only).  Item i of unit u,
 //     i < cap, is the i-th block fetched for u this step (attended entry
@@ -431,67 +521,9 @@ __global__ __launch_bounds__(256) void attn_mfma_kernel(
     st.vst = vstage[wave];
 
     if ((int64_t)blockIdx.x < n_fetch_wg) {
-        const int64_t F = 4LL * n_fetch_wg;
-        const int64_t n_items = units * cap;
-        int64_t it = (int64_t)blockIdx.x * 4 + wave;
-        int64_t cur_u = -1;
-        uint4 kr[2][4], vr[2][4];
-        // item -> (unit, i, entry); returns the source block pointer or null
-        auto locate = [&](int64_t item, int64_t &u, int &i, int32_t &blk, int32_t &slot) -> bool {
-            u = item / cap;
-            i = (int)(item % cap);
-            const int n_att = __builtin_amdgcn_readfirstlane(counts[u * 4 + 0]);
-            const int n_fetch = __builtin_amdgcn_readfirstlane(counts[u * 4 + 2]);
-            if (i >= n_fetch) return false;
-            const int e = n_att - n_fetch + i;  // the fetched blocks end the list
-            blk = __builtin_amdgcn_readfirstlane(att_block[u * K + e]);
-            slot = __builtin_amdgcn_readfirstlane(att_slot[u * K + e]);
-            return true;
-        };
-        int64_t u0;
-        int i0;
-        int32_t blk0 = 0, slot0 = 0;
-        bool have0 = it < n_items && locate(it, u0, i0, blk0, slot0);
-        if (it < n_items && have0) st.load(kr[0], vr[0], host_kv + (u0 * NBmax + blk0) * W::BLK);
-        int buf = 0;
-        for (; it < n_items; it += F) {
-            // prefetch the next item while this one is processed
-            const int64_t nx = it + F;
-            int64_t u1 = 0;
-            int i1 = 0;
-            int32_t blk1 = 0, slot1 = 0;
-            const bool have1 = nx < n_items && locate(nx, u1, i1, blk1, slot1);
-            if (have1) {
-                if (buf == 0) st.load(kr[1], vr[1], host_kv + (u1 * NBmax + blk1) * W::BLK);
-                else st.load(kr[0], vr[0], host_kv + (u1 * NBmax + blk1) * W::BLK);
-            }
-            __builtin_amdgcn_sched_barrier(0);  // keep the prefetch ahead of the compute
-            if (u0 != cur_u) {
-                const int64_t b = u0 / Hkv;
-                st.init(q, b, Hq, (int)(u0 % Hkv));
-                cur_u = u0;
-            } else {
-                st.reset();
-            }
-            if (have0) {
-                uint16_t *dst = slots + (u0 * S + slot0) * (int64_t)W::BLK;
-                if (buf == 0) {
-                    st.store(dst, kr[0], vr[0]);
-                    st.block(kr[0], vr[0], block_valid(T_, blk0), scale_log2);
-                } else {
-                    st.store(dst, kr[1], vr[1]);
-                    st.block(kr[1], vr[1], block_valid(T_, blk0), scale_log2);
-                }
-            }
-            st.reduce();
-            st.write_partial((u0 * nsa + i0) * G, part_m, part_l, part_acc);
-            u0 = u1;
-            i0 = i1;
-            blk0 = blk1;
-            slot0 = slot1;
-            have0 = have1;
-            buf ^= 1;
-        }
+        fetch_waves<G>(st, wave, q, slots, host_kv, att_block, att_slot, counts, T_, Hq, Hkv, K,
+                       S, NBmax, cap, n_fetch_wg, nsa, units, scale_log2, part_m, part_l,
+                       part_acc);
         return;
     }
 
@@ -555,27 +587,152 @@ __global__ __launch_bounds__(256) void attn_mfma_kernel(
     }
 }
 
+// ---------------------------------------------------------------- balanced hit path
+
+// Exclusive prefix sums of the hit entries of every unit into pre[0..units]
+// (LDS), by the 256 threads of a workgroup: hit entries of unit u are its
+// attended list minus, in mode 1, the fetched blocks at its end.
+__device__ __forceinline__ void hit_prefix(const int32_t *__restrict__ counts, int units, int mode,
+                                           int32_t *pre, int32_t *red) {
+    const int t = threadIdx.x, lane = t & 63, wv = t >> 6;
+    const int chunk = (units + 255) / 256;
+    const int lo = t * chunk < units ? t * chunk : units;
+    const int hi = lo + chunk < units ? lo + chunk : units;
+    int sum = 0;
+    for (int u = lo; u < hi; ++u) {
+        const int e = counts[u * 4 + 0] - (mode == 1 ? counts[u * 4 + 2] : 0);
+        pre[u + 1] = e;
+        sum += e;
+    }
+    int x = sum;  // inclusive scan over the wave
+#pragma unroll
+    for (int o = 1; o < 64; o <<= 1) {
+        const int y = __shfl_up(x, o, 64);
+        if (lane >= o) x += y;
+    }
+    if (lane == 63) red[wv] = x;
+    __syncthreads();
+    int r = x - sum;
+    for (int i = 0; i < wv; ++i) r += red[i];
+    for (int u = lo; u < hi; ++u) {
+        r += pre[u + 1];
+        pre[u + 1] = r;
+    }
+    if (t == 0) pre[0] = 0;
+    __syncthreads();
+}
+
+// Sparse attention over the hit entries, with the work balanced over waves
+// rather than split per unit (a unit's hit entries range from about 40 to
+// 115 on the Qwen3-8B layer).  The hit entries of all units, concatenated in
+// unit order (E of them), are cut into runs of P = max(ceil(E / W), pmin)
+// entries; wave w streams run w and may cross from one unit into the next.
+// W is what the GPU holds at once, so the launch is one round with equal
+// work per wave.  A wave issues one block, waits for it and attends to it:
+// on this part scattered 8 KB reads ran fastest with one block per wave in
+// flight (a timing probe of the same access: 37.4 us with none ahead, 40.0
+// with one block ahead, 42.4 with two, for 210 MB), and a new unit's query
+// rows then travel with its first block at no extra wait.  For each unit it
+// touches, a wave writes its partial at row hp0 + u R + s, s = the wave's
+// rank among the waves of u (at most R = ceil(K / pmin) + 1 of them); the
+// unit's last wave marks rows s + 1 .. R - 1 empty (m = -inf), and units
+// without hit entries are marked by workgroup u mod the grid, so the
+// combine reads a fixed set of rows with no dependent load.  Fetch
+// workgroups (mode 1) come first in the grid, as in the split kernel.
+// Dynamic LDS: units + 1 ints.
+template <int G>
+__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2))) void attn_flat_kernel(
+    const uint16_t *__restrict__ q, uint16_t *__restrict__ slots,
+    const uint16_t *__restrict__ host_kv, const int32_t *__restrict__ att_block,
+    const int32_t *__restrict__ att_slot, const int32_t *__restrict__ counts, int64_t T_, int Hq,
+    int Hkv, int K, int S, int64_t NBmax, int mode, int cap, int n_fetch_wg, int nsa, int units,
+    int W, int R, int pmin, float scale_log2, float *__restrict__ part_m,
+    float *__restrict__ part_l, float *__restrict__ part_acc, int64_t hp0) {
+    using Wv = std::conditional_t<G == 16, AttnWaveM<G>, AttnWave<G>>;
+    __shared__ __attribute__((aligned(16))) uint16_t vstage[4][Wv::kStage];
+    __shared__ int32_t red[4];
+    extern __shared__ int32_t pre[];
+    const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+    const int lane = threadIdx.x & 63;
+    Wv st;
+    st.lanes();
+    st.vst = vstage[wave];
+    if ((int)blockIdx.x < n_fetch_wg) {
+        fetch_waves<G>(st, wave, q, slots, host_kv, att_block, att_slot, counts, T_, Hq, Hkv, K,
+                       S, NBmax, cap, n_fetch_wg, nsa, (int64_t)units, scale_log2, part_m,
+                       part_l, part_acc);
+        return;
+    }
+    hit_prefix(counts, units, mode, pre, red);
+    const int wg = (int)blockIdx.x - n_fetch_wg, nwg = (int)gridDim.x - n_fetch_wg;
+    auto mark_empty = [&](int64_t row0, int nrows, int t0, int nt) {  // rows of G partials
+        for (int i = t0; i < nrows * G; i += nt) {
+            part_m[row0 * G + i] = -INFINITY;
+            part_l[row0 * G + i] = 0.f;
+        }
+    };
+    for (int u = wg; u < units; u += nwg)
+        if (pre[u + 1] == pre[u]) mark_empty(hp0 + (int64_t)u * R, R, threadIdx.x, 256);
+    const int E = pre[units];
+    if (E == 0) return;
+    const int P0 = (E + W - 1) / W;
+    const int P = P0 > pmin ? P0 : pmin;  // <= 64 (W >= E_max / 64)
+    const int w = __builtin_amdgcn_readfirstlane(wg * 4 + wave);
+    const int f0 = w * P;
+    if (f0 >= E) return;
+    const int n = (E - f0) < P ? (E - f0) : P;
+
+    // lane i < n: unit, block and slot of entry f0 + i
+    int my_u = 0, my_blk = 0, my_slot = 0;
+    if (lane < n) {
+        const int f = f0 + lane;
+        int lo = 0, hi = units - 1;  // largest u with pre[u] <= f
+        while (lo < hi) {
+            const int mid = (lo + hi + 1) >> 1;
+            if (pre[mid] <= f) lo = mid;
+            else hi = mid - 1;
+        }
+        my_u = lo;
+        my_blk = att_block[(int64_t)lo * K + f - pre[lo]];
+        my_slot = att_slot[(int64_t)lo * K + f - pre[lo]];
+    }
+    auto rl = [](int v, int j) { return __builtin_amdgcn_readlane(v, j); };
+    // partial of unit u from this wave; the unit's last wave marks the rest
+    auto finish = [&](int u) {
+        st.reduce();
+        const int s0 = pre[u] / P, s1 = (pre[u + 1] - 1) / P;
+        st.write_partial((hp0 + (int64_t)u * R + (w - s0)) * G, part_m, part_l, part_acc);
+        if (w == s1) mark_empty(hp0 + (int64_t)u * R + (w - s0) + 1, R - 1 - (w - s0), lane, 64);
+    };
+    int cur_u = -1;
+    uint4 kk[4], vv[4];
+    for (int j = 0; j < n; ++j) {
+        const int u = rl(my_u, j);
+        if (u != cur_u) {
+            if (cur_u >= 0) finish(cur_u);
+            st.load_q(st.qb, q, u / Hkv, Hq, u % Hkv);  // waited for with the block
+            st.reset();
+            cur_u = u;
+        }
+        st.load_nt(kk, vv, slots + ((int64_t)u * S + rl(my_slot, j)) * Wv::BLK);
+        st.block(kk, vv, block_valid(T_, rl(my_blk, j)), scale_log2);
+    }
+    finish(cur_u);
+}
+
 // ---------------------------------------------------------------- combine
 
 // Partials merged from registers when there are at most this many.
 constexpr int kCombineRegs = 24;
 
-// One workgroup per (b, query head); thread c owns output dimension c.  The
-// partials of a unit are splits [0, n_a) and [off_b, off_b + n_b) of nsa.
-__global__ __launch_bounds__(256) void combine_kernel(const float *__restrict__ part_m,
-                                                      const float *__restrict__ part_l,
-                                                      const float *__restrict__ part_acc,
-                                                      float *__restrict__ out, int Hq, int Hkv,
-                                                      int G, int d, int nsa, int n_a, int off_b,
-                                                      int n_b) {
-    const int qh = blockIdx.x, b = blockIdx.y;
-    const int h = qh / G, g = qh % G;
-    const int64_t u = (int64_t)b * Hkv + h;
-    const int n = n_a + n_b;
-    auto pidx = [&](int i) -> int64_t {
-        const int s = i < n_a ? i : off_b + (i - n_a);
-        return (u * nsa + s) * G + g;
-    };
+// Output row (b, query head qh) from its n partials, partial i at row
+// pidx(i); thread c owns output dimension c.
+template <typename F>
+__device__ __forceinline__ void combine_row(const float *__restrict__ part_m,
+                                            const float *__restrict__ part_l,
+                                            const float *__restrict__ part_acc,
+                                            float *__restrict__ out, int Hq, int d, int b, int qh,
+                                            int n, F pidx) {
     if (n <= kCombineRegs && (int)blockDim.x >= d) {
         // every load issued up front (one round trip), then the same sums in
         // the same order as below
@@ -593,6 +750,14 @@ __global__ __launch_bounds__(256) void combine_kernel(const float *__restrict__ 
                 if (c < d) pa[i] = part_acc[pi * d + c];
             }
         }
+        // a partial marked empty (m = -inf) contributes nothing; its sums may
+        // be stale
+#pragma unroll
+        for (int i = 0; i < kCombineRegs; ++i)
+            if (pm[i] == -INFINITY) {
+                pl[i] = 0.f;
+                pa[i] = 0.f;
+            }
         float M = -INFINITY;
 #pragma unroll
         for (int i = 0; i < kCombineRegs; ++i) M = fmaxf(M, pm[i]);
@@ -616,17 +781,50 @@ __global__ __launch_bounds__(256) void combine_kernel(const float *__restrict__ 
     if (M != -INFINITY)
         for (int i = 0; i < n; ++i) {
             const int64_t pi = pidx(i);
-            L += exp2f(part_m[pi] - M) * part_l[pi];
+            if (part_m[pi] != -INFINITY) L += exp2f(part_m[pi] - M) * part_l[pi];
         }
     for (int c = threadIdx.x; c < d; c += blockDim.x) {
         float a = 0.f;
         if (M != -INFINITY)
             for (int i = 0; i < n; ++i) {
                 const int64_t pi = pidx(i);
-                a += exp2f(part_m[pi] - M) * part_acc[pi * d + c];
+                if (part_m[pi] != -INFINITY) a += exp2f(part_m[pi] - M) * part_acc[pi * d + c];
             }
         out[((int64_t)b * Hq + qh) * d + c] = (L > 0.f) ? a / L : 0.f;
     }
+}
+
+// One workgroup per (b, query head).  The partials of a unit are splits
+// [0, n_a) and [off_b, off_b + n_b) of nsa.
+__global__ __launch_bounds__(256) void combine_kernel(const float *__restrict__ part_m,
+                                                      const float *__restrict__ part_l,
+                                                      const float *__restrict__ part_acc,
+                                                      float *__restrict__ out, int Hq, int Hkv,
+                                                      int G, int d, int nsa, int n_a, int off_b,
+                                                      int n_b) {
+    const int qh = blockIdx.x, b = blockIdx.y;
+    const int h = qh / G, g = qh % G;
+    const int64_t u = (int64_t)b * Hkv + h;
+    combine_row(part_m, part_l, part_acc, out, Hq, d, b, qh, n_a + n_b, [&](int i) -> int64_t {
+        const int s = i < n_a ? i : off_b + (i - n_a);
+        return (u * nsa + s) * G + g;
+    });
+}
+
+// The same after the balanced hit path: the unit's n_f fetch partials (splits
+// [0, n_f) of nsa), then its R hit partial rows hp0 + u R + s, the unused
+// ones marked empty.
+__global__ __launch_bounds__(256) void combine_flat_kernel(
+    const float *__restrict__ part_m, const float *__restrict__ part_l,
+    const float *__restrict__ part_acc, float *__restrict__ out, int Hq, int Hkv, int G, int d,
+    int nsa, int n_f, int R, int64_t hp0) {
+    const int qh = blockIdx.x, b = blockIdx.y;
+    const int h = qh / G, g = qh % G;
+    const int u = b * Hkv + h;
+    combine_row(part_m, part_l, part_acc, out, Hq, d, b, qh, n_f + R, [&](int i) -> int64_t {
+        if (i < n_f) return ((int64_t)u * nsa + i) * G + g;
+        return (hp0 + (int64_t)u * R + (i - n_f)) * G + g;
+    });
 }
 
 // ---------------------------------------------------------------- verification attention
@@ -753,6 +951,7 @@ hipError_t launch_verify(const Dims &D, const AttnPlan &P, int n_drafts, const v
     AttnPlan Pc = P;
     Pc.nsf_max = 0;
     Pc.nsa = P.ns1;
+    Pc.flat = false;  // per-chunk passes keep the per-unit split kernel
     for (int k = 0; k < ch.n; ++k) {
         Dims Dc = D;
         Dc.G = ch.rows[k];
@@ -778,8 +977,19 @@ static bool mfma_ok(const Dims &D) {
     return D.dtype == kBF16 && D.d == 128 && D.bs == 16 && g_ok;
 }
 
+// Units whose hit-entry prefix sums the balanced kernel keeps in LDS.
+constexpr int kFlatMaxUnits = 4096;
+
+template <int G> static int flat_wgs_per_cu(int units) {
+    int n = 0;
+    if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&n, attn_flat_kernel<G>, 256,
+                                                     sizeof(int32_t) * (units + 1)) != hipSuccess)
+        n = 0;
+    return n;
+}
+
 AttnPlan plan_attention(const Dims &D) {
-    AttnPlan P;
+    AttnPlan P{};
     P.mfma = mfma_ok(D);
     const int64_t units = D.units();
     if (P.mfma) {
@@ -789,6 +999,40 @@ AttnPlan plan_attention(const Dims &D) {
         P.blocks_per_wave = bpw;
         P.ns1 = (D.K + 4 * bpw - 1) / (4 * bpw);
         P.nsf_max = D.K;
+        // Balanced hit path: as many waves as the GPU holds at once, but no
+        // run shorter than 8 entries at full lists, and runs of at most 64
+        // entries (one list entry per lane).
+        if (units <= kFlatMaxUnits && !getenv("OASIS_ATTN_SPLIT")) {
+            int dev = 0, cus = 0, per_cu = 0;
+            if (hipGetDevice(&dev) == hipSuccess &&
+                hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) ==
+                    hipSuccess) {
+                const int u = (int)units;
+                switch (D.G) {
+                case 1: per_cu = flat_wgs_per_cu<1>(u); break;
+                case 2: per_cu = flat_wgs_per_cu<2>(u); break;
+                case 4: per_cu = flat_wgs_per_cu<4>(u); break;
+                case 8: per_cu = flat_wgs_per_cu<8>(u); break;
+                default: per_cu = flat_wgs_per_cu<16>(u); break;
+                }
+            }
+            const int64_t emax = units * D.K;
+            // at most two workgroups (eight waves) per CU: more concurrent
+            // block streams read slower (a timing probe of the access: 37.3
+            // us with 8 waves per CU, 39.2 with 12, for 210 MB)
+            int64_t w = (int64_t)cus * std::min(per_cu, 2) * 4;
+            w = std::min<int64_t>(w, std::max<int64_t>(4, (emax + 7) / 8));
+            w = (w + 3) / 4 * 4;
+            if (per_cu > 0 && w * 64 >= emax && w <= (1 << 20)) {
+                P.flat = true;
+                P.flat_waves = (int)w;
+                // runs of at least pmin entries: a unit's K entries then meet
+                // at most R waves
+                const int segs = (D.K + 7) / 8;
+                P.flat_pmin = (D.K + segs - 1) / segs;
+                P.flat_rows = segs + 1;
+            }
+        }
     } else {
         int bps = 8;
         while (bps > 1 && units * ((D.K + bps - 1) / bps) < 1024) bps /= 2;
@@ -796,8 +1040,14 @@ AttnPlan plan_attention(const Dims &D) {
         P.ns1 = (D.K + bps - 1) / bps;
         P.nsf_max = 0;
     }
-    P.nsa = P.nsf_max + P.ns1;
+    P.nsa = P.nsf_max + (P.flat ? 0 : P.ns1);
     return P;
+}
+
+int64_t attn_partial_rows(const Dims &D, const AttnPlan &P) {
+    int64_t rows = D.units() * P.nsa * D.G;
+    if (P.flat) rows += D.units() * P.flat_rows * D.G;
+    return rows;
 }
 
 int attention_fetch_splits(const Dims &D, const AttnPlan &P, int cap) {
@@ -836,11 +1086,43 @@ static void launch_mfma_g(const AttnPlan &P, dim3 grid, hipStream_t st, const ui
 #undef OASIS_ATTN
 }
 
+template <int G>
+static void launch_flat_g(const AttnPlan &P, dim3 grid, size_t lds, hipStream_t st,
+                          const uint16_t *q, uint16_t *slots, const uint16_t *host_kv,
+                          const int32_t *ab, const int32_t *as, const int32_t *counts, int64_t T,
+                          const Dims &D, int mode, int cap, int n_fetch_wg, float sc, float *pm,
+                          float *pl, float *pa) {
+    OASIS_LAUNCH((attn_flat_kernel<G>), grid, dim3(256), lds, st, q, slots, host_kv, ab, as,
+                 counts, T, D.Hq, D.Hkv, D.K, D.S, D.NBmax, mode, cap, n_fetch_wg, P.nsa,
+                 (int)D.units(), P.flat_waves, P.flat_rows, P.flat_pmin, sc, pm, pl, pa,
+                 D.units() * P.nsa);
+}
+
 hipError_t launch_attention(const Dims &D, const AttnPlan &P, int mode, int nsf, const void *q,
                             void *slots, const void *host_kv, const int32_t *att_block,
                             const int32_t *att_slot, const int32_t *counts, int64_t T,
                             float *part_m, float *part_l, float *part_acc, hipStream_t st) {
     const float sc = kLog2e / sqrtf((float)D.d);
+    if (P.mfma && P.flat) {
+        if (mode == 0) nsf = 0;
+        const int n_fetch_wg = nsf > 0 ? fetch_workgroups(D.units() * nsf) : 0;
+        const dim3 grid((unsigned)(n_fetch_wg + P.flat_waves / 4));
+        const size_t lds = sizeof(int32_t) * (D.units() + 1);
+        const uint16_t *qq = (const uint16_t *)q, *hk = (const uint16_t *)host_kv;
+        uint16_t *sl = (uint16_t *)slots;
+#define OASIS_FLAT(GG)                                                                          \
+    launch_flat_g<GG>(P, grid, lds, st, qq, sl, hk, att_block, att_slot, counts, T, D, mode, nsf, \
+                      n_fetch_wg, sc, part_m, part_l, part_acc)
+        switch (D.G) {
+        case 1: OASIS_FLAT(1); break;
+        case 2: OASIS_FLAT(2); break;
+        case 4: OASIS_FLAT(4); break;
+        case 8: OASIS_FLAT(8); break;
+        default: OASIS_FLAT(16); break;
+        }
+#undef OASIS_FLAT
+        return hipGetLastError();
+    }
     if (P.mfma) {
         if (mode == 0) nsf = 0;
         const int n_fetch_wg = nsf > 0 ? fetch_workgroups(D.units() * nsf) : 0;
@@ -879,6 +1161,12 @@ hipError_t launch_attention(const Dims &D, const AttnPlan &P, int mode, int nsf,
 hipError_t launch_combine(const Dims &D, const AttnPlan &P, int nsf, const float *part_m,
                           const float *part_l, const float *part_acc, float *out,
                           hipStream_t st) {
+    if (P.flat) {
+        OASIS_LAUNCH(combine_flat_kernel, dim3(D.Hq, D.B), dim3(D.d <= 256 ? D.d : 256), 0, st,
+                     part_m, part_l, part_acc, out, D.Hq, D.Hkv, D.G, D.d, P.nsa, nsf,
+                     P.flat_rows, D.units() * P.nsa);
+        return hipGetLastError();
+    }
     OASIS_LAUNCH(combine_kernel, dim3(D.Hq, D.B), dim3(D.d <= 256 ? D.d : 256), 0, st,
                        part_m, part_l, part_acc, out, D.Hq, D.Hkv, D.G, D.d, P.nsa, nsf,
                        P.nsf_max, P.ns1);

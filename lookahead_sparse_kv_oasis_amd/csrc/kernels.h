@@ -129,11 +129,19 @@ hipError_t launch_rebuild_block_slot(const Dims &D, const int32_t *slot_block,
 struct AttnPlan {
     bool mfma;             // bf16, d = 128, block 16, G in {1, 2, 4, 8, 16}
     int blocks_per_wave;   // hit entries per wave (MFMA: 4 waves per split)
-    int ns1;               // hit splits per unit
+    int ns1;               // hit splits per unit (split kernel; verification attention)
     int nsf_max;           // fetch splits per unit at cap = K (MFMA only)
     int nsa;               // partial stride per unit
+    // Balanced hit path (MFMA layouts whose units fit its LDS prefix sums):
+    // flat_waves waves stream equal runs (at least flat_pmin entries) of all
+    // units' hit entries and write their partials after the per-unit region,
+    // flat_rows per unit.
+    bool flat;
+    int flat_waves, flat_pmin, flat_rows;
 };
 AttnPlan plan_attention(const Dims &D);
+// Rows (G floats of m and l, G x d of acc each) of the partial buffers.
+int64_t attn_partial_rows(const Dims &D, const AttnPlan &P);
 // Fetch splits for a cap (fused mode), 0 when the kernel cannot fuse.
 int attention_fetch_splits(const Dims &D, const AttnPlan &P, int cap);
 // mode 0: every attended entry from its slot.  mode 1 (MFMA only): entries
