@@ -722,7 +722,7 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2))) void a
 
 // ---------------------------------------------------------------- combine
 
-// Partials merged from registers when there are at most this many.
+// Partials merged per round trip of the combine.
 constexpr int kCombineRegs = 24;
 
 // Output row (b, query head qh) from its n partials, partial i at row
@@ -733,63 +733,49 @@ __device__ __forceinline__ void combine_row(const float *__restrict__ part_m,
                                             const float *__restrict__ part_acc,
                                             float *__restrict__ out, int Hq, int d, int b, int qh,
                                             int n, F pidx) {
-    if (n <= kCombineRegs && (int)blockDim.x >= d) {
-        // every load issued up front (one round trip), then the same sums in
-        // the same order as below
-        const int c = threadIdx.x;
-        float pm[kCombineRegs], pl[kCombineRegs], pa[kCombineRegs];
+    // Chunks of kCombineRegs partials: every load of a chunk issued up front
+    // (one round trip per chunk), merged into a running (max, sum, acc).  A
+    // single chunk is the plain max-subtracted merge.
+    for (int c = threadIdx.x; c < d; c += blockDim.x) {
+        float M = -INFINITY, L = 0.f, a = 0.f;
+        for (int i0 = 0; i0 < n; i0 += kCombineRegs) {
+            float pm[kCombineRegs], pl[kCombineRegs], pa[kCombineRegs];
 #pragma unroll
-        for (int i = 0; i < kCombineRegs; ++i) {
-            pm[i] = -INFINITY;
-            pl[i] = 0.f;
-            pa[i] = 0.f;
-            if (i < n) {
-                const int64_t pi = pidx(i);
-                pm[i] = part_m[pi];
-                pl[i] = part_l[pi];
-                if (c < d) pa[i] = part_acc[pi * d + c];
-            }
-        }
-        // a partial marked empty (m = -inf) contributes nothing; its sums may
-        // be stale
-#pragma unroll
-        for (int i = 0; i < kCombineRegs; ++i)
-            if (pm[i] == -INFINITY) {
-                pl[i] = 0.f;
-                pa[i] = 0.f;
-            }
-        float M = -INFINITY;
-#pragma unroll
-        for (int i = 0; i < kCombineRegs; ++i) M = fmaxf(M, pm[i]);
-        float L = 0.f, a = 0.f;
-        if (M != -INFINITY) {
-#pragma unroll
-            for (int i = 0; i < kCombineRegs; ++i) {
-                if (i < n) {
-                    const float wgt = exp2f(pm[i] - M);
-                    L += wgt * pl[i];
-                    a += wgt * pa[i];
+            for (int k = 0; k < kCombineRegs; ++k) {
+                pm[k] = -INFINITY;
+                pl[k] = 0.f;
+                pa[k] = 0.f;
+                if (i0 + k < n) {
+                    const int64_t pi = pidx(i0 + k);
+                    pm[k] = part_m[pi];
+                    pl[k] = part_l[pi];
+                    pa[k] = part_acc[pi * d + c];
                 }
             }
-        }
-        if (c < d) out[((int64_t)b * Hq + qh) * d + c] = (L > 0.f) ? a / L : 0.f;
-        return;
-    }
-    float M = -INFINITY;
-    for (int i = 0; i < n; ++i) M = fmaxf(M, part_m[pidx(i)]);
-    float L = 0.f;
-    if (M != -INFINITY)
-        for (int i = 0; i < n; ++i) {
-            const int64_t pi = pidx(i);
-            if (part_m[pi] != -INFINITY) L += exp2f(part_m[pi] - M) * part_l[pi];
-        }
-    for (int c = threadIdx.x; c < d; c += blockDim.x) {
-        float a = 0.f;
-        if (M != -INFINITY)
-            for (int i = 0; i < n; ++i) {
-                const int64_t pi = pidx(i);
-                if (part_m[pi] != -INFINITY) a += exp2f(part_m[pi] - M) * part_acc[pi * d + c];
+            // a partial marked empty (m = -inf) contributes nothing; its sums
+            // may be stale
+            float cm = -INFINITY;
+#pragma unroll
+            for (int k = 0; k < kCombineRegs; ++k) {
+                if (pm[k] == -INFINITY) {
+                    pl[k] = 0.f;
+                    pa[k] = 0.f;
+                }
+                cm = fmaxf(cm, pm[k]);
             }
+            if (cm == -INFINITY) continue;
+            const float nm = fmaxf(M, cm);
+            const float r = exp2f(M - nm);  // 0 while nothing was merged
+            L *= r;
+            a *= r;
+#pragma unroll
+            for (int k = 0; k < kCombineRegs; ++k) {
+                const float wgt = exp2f(pm[k] - nm);
+                L += wgt * pl[k];
+                a += wgt * pa[k];
+            }
+            M = nm;
+        }
         out[((int64_t)b * Hq + qh) * d + c] = (L > 0.f) ? a / L : 0.f;
     }
 }
@@ -999,9 +985,8 @@ AttnPlan plan_attention(const Dims &D) {
         P.blocks_per_wave = bpw;
         P.ns1 = (D.K + 4 * bpw - 1) / (4 * bpw);
         P.nsf_max = D.K;
-        // Balanced hit path: as many waves as the GPU holds at once, but no
-        // run shorter than 8 entries at full lists, and runs of at most 64
-        // entries (one list entry per lane).
+        // Balanced hit path: as many waves as the GPU holds at once, runs of
+        // at most 64 entries (one list entry per lane).
         if (units <= kFlatMaxUnits && !getenv("OASIS_ATTN_SPLIT")) {
             int dev = 0, cus = 0, per_cu = 0;
             if (hipGetDevice(&dev) == hipSuccess &&
@@ -1021,14 +1006,19 @@ AttnPlan plan_attention(const Dims &D) {
             // block streams read slower (a timing probe of the access: 37.3
             // us with 8 waves per CU, 39.2 with 12, for 210 MB)
             int64_t w = (int64_t)cus * std::min(per_cu, 2) * 4;
-            w = std::min<int64_t>(w, std::max<int64_t>(4, (emax + 7) / 8));
+            w = std::min<int64_t>(w, std::max<int64_t>(4, (emax + 1) / 2));
             w = (w + 3) / 4 * 4;
             if (per_cu > 0 && w * 64 >= emax && w <= (1 << 20)) {
                 P.flat = true;
                 P.flat_waves = (int)w;
-                // runs of at least pmin entries: a unit's K entries then meet
-                // at most R waves
-                const int segs = (D.K + 7) / 8;
+                // runs of at least pmin entries, so that a unit's K entries
+                // meet at most R waves (the combine reads R rows per unit):
+                // 8 where full lists give each wave 8 or more entries, down to
+                // 2 for small batches (64 units), which would otherwise leave
+                // most waves idle
+                const int64_t per = (emax * 2 + 3 * w - 1) / (3 * w);  // ~ emax / 1.5 W
+                const int pm = (int)std::max<int64_t>(2, std::min<int64_t>(8, per));
+                const int segs = (D.K + pm - 1) / pm;
                 P.flat_pmin = (D.K + segs - 1) / segs;
                 P.flat_rows = segs + 1;
             }

@@ -52,6 +52,12 @@ class LayerRunner:
         if w.initial_resident_frac > 0:
             sb, lu = synth.initial_slots(w, layer)
             self.h.oasis_set_state(sb, lu)
+        # the GQA-8 stress workload forces part of the previous attended set out
+        # of HBM at each step start: its seeded draws, every step, on the device
+        self.evict_draws = None
+        if w.forced_evict_frac > 0:
+            self.evict_draws = torch.from_numpy(np.ascontiguousarray(np.stack(
+                [synth.evict_draws(w, t, layer) for t in range(n_steps + 1)]))).to(device)
         self.t = 0
 
     def admission(self, stream=None):
@@ -62,11 +68,14 @@ class LayerRunner:
         h.oasis_sparse_attn(self.q, self.out, stream=stream)
 
     def step(self, t: int, stream=None, scores_hook=None):
-        """Decode step t (1-based): append token T0 + t - 1, predict, select, attend.
+        """Decode step t (1-based): forced evictions (stress workload), append
+        token T0 + t - 1, predict, select, attend.
 
         scores_hook(t) may return device scores [B][Hkv][NBmax] to select on
         instead of the library's own (parity runs)."""
         h = self.h
+        if self.evict_draws is not None:
+            h.oasis_evict_attended(self.evict_draws[t], self.w.forced_evict_frac, stream=stream)
         h.oasis_append_kv(self.app_k[t - 1], self.app_v[t - 1], stream=stream)
         q = self.q_steps[t]
         h.oasis_predict(q, self.drafts[t], self.w.drafts, stream=stream)
