@@ -232,6 +232,45 @@ int oasis_sparse_attn_verify(oasis_t *h, const void *q_dev, const void *drafts_d
                              int32_t n_drafts, const void *k_drafts_dev,
                              const void *v_drafts_dev, float *out_dev, hipStream_t stream);
 
+/* Shape of oasis_sparse_attn_noalloc's inputs. */
+typedef struct {
+    int32_t batch;           /* B */
+    int32_t num_q_heads;     /* Hq, a multiple of Hkv with Hq / Hkv in {1, 2, 4, 8, 16} */
+    int32_t num_kv_heads;    /* Hkv */
+    int32_t head_dim;        /* 128 */
+    int32_t block_size;      /* 16 */
+    int32_t list_stride;     /* K: entries per (b, KV head) row of the lists, 1..1024 */
+    int32_t slots_per_head;  /* S: block slots per (b, KV head) in the slot pool */
+    int32_t reserved;
+} oasis_attn_desc;
+
+/* For callers that cannot allocate device memory (code under HIP graph
+ * capture, serving loops that forbid hipMalloc): oasis_sparse_attn over
+ * caller-owned buffers, with no handle and no allocation.  Its split-K
+ * partials live in an array of device memory that the library holds, one
+ * per GPU, for the life of the process: 61,440 partial rows of 130 fp32
+ * (31.9 MB).  A call needs G rows for each (b, KV head) and each of its run
+ * segments, B * Hkv * G * (K / 8 + 1) rows at full lists of the Qwen3-8B
+ * layer shape (17,408 at B = 32, K = 128; up to B * Hkv * G * (K / 2 + 1)
+ * for small batches); a shape needing more than the array holds returns
+ * OASIS_E_CAPACITY and launches nothing.  Every call on a GPU uses that GPU's one array: calls that overlap
+ * in time on one GPU (different streams, no ordering) race and give wrong
+ * results; calls ordered on a stream do not (each call writes every row it
+ * reads).  Inputs, all bf16 bit patterns or int32, device memory, 16-byte
+ * aligned:
+ *   q_dev [B][Hq][128]; slots_dev [B][Hkv][S][K|V][16][128] (the slot pool
+ *   layout of a handle); att_block_dev / att_slot_dev [B][Hkv][list_stride]:
+ *   the attended blocks and the slots holding them; counts_dev [B][Hkv][4]:
+ *   element 0 = number of attended entries of the row (the COUNTS layout of a
+ *   handle); tokens: the sequence length T (a block's tokens at or past T are
+ *   masked).  out_dev [B][Hq][128] fp32 = softmax(q.k / sqrt(128)) v over the
+ *   valid tokens of the attended blocks, 0 for an empty list.  Asynchronous on
+ *   `stream`; OASIS_E_INVAL for other shapes or null / misaligned pointers. */
+int oasis_sparse_attn_noalloc(const oasis_attn_desc *desc, const void *q_dev,
+                              const void *slots_dev, const int32_t *att_block_dev,
+                              const int32_t *att_slot_dev, const int32_t *counts_dev,
+                              int64_t tokens, float *out_dev, hipStream_t stream);
+
 /* ---------------------------------------------------------------- layer pipeline */
 
 typedef struct {

@@ -30,7 +30,8 @@ EXPORTS = [
     "oasis_create", "oasis_create_shared", "oasis_destroy", "oasis_load_prefix",
     "oasis_set_state", "oasis_decode_layers", "oasis_decode_layers_ahead",
     "oasis_append_kv", "oasis_predict", "oasis_topk_from_scores", "oasis_select_and_fetch",
-    "oasis_evict", "oasis_evict_attended", "oasis_get_state", "oasis_sparse_attn", "oasis_sparse_attn_verify", "oasis_buffer_bytes", "oasis_read", "oasis_get_stats",
+    "oasis_evict", "oasis_evict_attended", "oasis_get_state", "oasis_sparse_attn",
+    "oasis_sparse_attn_noalloc", "oasis_sparse_attn_verify", "oasis_buffer_bytes", "oasis_read", "oasis_get_stats",
     "oasis_check", "oasis_set_timing", "oasis_set_timing_period",
     "oasis_set_score_topk_fusion", "oasis_set_fetch_in_attention", "oasis_set_attend_all_resident", "oasis_get_timing", "oasis_get_dims", "oasis_tokens",
     "oasis_copy_stream", "oasis_stream_read", "oasis_kv_bytes_per_token", "oasis_cap_from_ratio",
@@ -51,6 +52,12 @@ class oasis_layout(ctypes.Structure):
                 ("dtype", ctypes.c_int32), ("max_drafts", ctypes.c_int32),
                 ("slots_per_head", ctypes.c_int32), ("reserved", ctypes.c_int32),
                 ("max_tokens", ctypes.c_int64)]
+
+
+class oasis_attn_desc(ctypes.Structure):
+    _fields_ = [(n, ctypes.c_int32) for n in
+                ("batch", "num_q_heads", "num_kv_heads", "head_dim", "block_size",
+                 "list_stride", "slots_per_head", "reserved")]
 
 
 class oasis_layer_io(ctypes.Structure):
@@ -106,6 +113,8 @@ def lib():
             "oasis_get_state": (ctypes.c_int, [H, vp, vp, vp, vp, vp]),
             "oasis_sparse_attn": (ctypes.c_int, [H, vp, vp, vp]),
             "oasis_sparse_attn_verify": (ctypes.c_int, [H, vp, vp, i32, vp, vp, vp, vp]),
+            "oasis_sparse_attn_noalloc": (ctypes.c_int, [ctypes.POINTER(oasis_attn_desc), vp, vp,
+                                                         vp, vp, vp, i64, vp, vp]),
             "oasis_buffer_bytes": (i64, [H, i32]),
             "oasis_read": (ctypes.c_int, [H, i32, i64, i64, vp]),
             "oasis_get_stats": (ctypes.c_int, [H, ctypes.POINTER(oasis_stats)]),
@@ -172,6 +181,14 @@ def stream_read(buf, sink, workgroups: int, stream=None) -> None:
     rc = lib().oasis_stream_read(_ptr(buf), nbytes, _ptr(sink), workgroups, _stream(stream))
     if rc != OASIS_OK:
         raise OasisError(rc, "oasis_stream_read")
+
+
+def sparse_attn_noalloc(desc: oasis_attn_desc, q, slots, att_block, att_slot, counts,
+                        tokens: int, out, stream=None) -> int:
+    """oasis_sparse_attn_noalloc on device tensors; returns the status."""
+    return lib().oasis_sparse_attn_noalloc(ctypes.byref(desc), _ptr(q), _ptr(slots),
+                                           _ptr(att_block), _ptr(att_slot), _ptr(counts),
+                                           int(tokens), _ptr(out), _stream(stream))
 
 
 def cap_from_ratio(ratio, k_blocks) -> int:
