@@ -46,9 +46,9 @@ PCIE_GEN5_X16_GBPS = 64.0   # host link, one direction
 
 KERNEL_SOURCES = {
     "oasis_score": ["score.hip", "score_tile.h"],
-    "oasis_sparse_attn": ["attention.hip"],
-    "oasis_sparse_attn_hbm": ["attention.hip"],
-    "oasis_combine": ["attention.hip"],
+    "oasis_sparse_attn": ["attention.hip", "combine.h"],
+    "oasis_sparse_attn_hbm": ["attention.hip", "combine.h"],
+    "oasis_combine": ["attention.hip", "combine.h"],
     "oasis_topk_select": ["selection.hip"],
     "oasis_score_topk_select": ["selection.hip", "score_tile.h"],
 }
@@ -406,7 +406,7 @@ def bench_layer(args, w, steps, warmup, main_leg=True, shared=None):
     stats1 = h.oasis_get_stats()
     h.oasis_check()
     verify = None
-    if main_leg and mfma_layout and not w.lookahead:
+    if main_leg and mfma_layout and not w.lookahead and not args.no_kernel_timing:
         verify = time_verify(run, w)
     K = steps
     e = w.elem_bytes

@@ -485,6 +485,7 @@ int create_handle(const oasis_layout *layout, int32_t block_size, int32_t budget
     D.S = S;
     D.NBmax = NBmax;
     h->plan = plan_attention(D);
+    h->plan.vns = verify_stride(D);
     h->use_mfma_score = D.dtype == kBF16 && (D.d == 64 || D.d == 128 || D.d == 256) && Q <= 128;
     if (const char *e = getenv("OASIS_SCORE_IMPL"))
         if (!strcmp(e, "valu")) h->use_mfma_score = false;
@@ -555,9 +556,9 @@ int create_handle(const oasis_layout *layout, int32_t block_size, int32_t budget
         // verification attention scratch, sized for max_drafts
         const size_t rows = (size_t)units * verify_rows(D, L.max_drafts);
         ok = dmal(&h->vq, rows * 128 * sizeof(uint16_t)) &&
-             dmal((void **)&h->vpart_m, rows * h->plan.ns1 * sizeof(float)) &&
-             dmal((void **)&h->vpart_l, rows * h->plan.ns1 * sizeof(float)) &&
-             dmal((void **)&h->vpart_acc, rows * h->plan.ns1 * 128 * sizeof(float));
+             dmal((void **)&h->vpart_m, rows * h->plan.vns * sizeof(float)) &&
+             dmal((void **)&h->vpart_l, rows * h->plan.vns * sizeof(float)) &&
+             dmal((void **)&h->vpart_acc, rows * h->plan.vns * 128 * sizeof(float));
     }
     if (!ok) return bail(OASIS_E_NOMEM);
     if (hipMemset(h->summ, 0, summ_bytes) != hipSuccess ||

@@ -15,6 +15,7 @@
 
 #include <algorithm>
 
+#include "combine.h"
 #include "kernels.h"
 
 namespace oasis {
@@ -722,9 +723,6 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2))) void a
 
 // ---------------------------------------------------------------- combine
 
-// Partials merged per round trip of the combine.
-constexpr int kCombineRegs = 24;
-
 // Output row (b, query head qh) from its n partials, partial i at row
 // pidx(i); thread c owns output dimension c.
 template <typename F>
@@ -733,49 +731,9 @@ __device__ __forceinline__ void combine_row(const float *__restrict__ part_m,
                                             const float *__restrict__ part_acc,
                                             float *__restrict__ out, int Hq, int d, int b, int qh,
                                             int n, F pidx) {
-    // Chunks of kCombineRegs partials: every load of a chunk issued up front
-    // (one round trip per chunk), merged into a running (max, sum, acc).  A
-    // single chunk is the plain max-subtracted merge.
     for (int c = threadIdx.x; c < d; c += blockDim.x) {
         float M = -INFINITY, L = 0.f, a = 0.f;
-        for (int i0 = 0; i0 < n; i0 += kCombineRegs) {
-            float pm[kCombineRegs], pl[kCombineRegs], pa[kCombineRegs];
-#pragma unroll
-            for (int k = 0; k < kCombineRegs; ++k) {
-                pm[k] = -INFINITY;
-                pl[k] = 0.f;
-                pa[k] = 0.f;
-                if (i0 + k < n) {
-                    const int64_t pi = pidx(i0 + k);
-                    pm[k] = part_m[pi];
-                    pl[k] = part_l[pi];
-                    pa[k] = part_acc[pi * d + c];
-                }
-            }
-            // a partial marked empty (m = -inf) contributes nothing; its sums
-            // may be stale
-            float cm = -INFINITY;
-#pragma unroll
-            for (int k = 0; k < kCombineRegs; ++k) {
-                if (pm[k] == -INFINITY) {
-                    pl[k] = 0.f;
-                    pa[k] = 0.f;
-                }
-                cm = fmaxf(cm, pm[k]);
-            }
-            if (cm == -INFINITY) continue;
-            const float nm = fmaxf(M, cm);
-            const float r = exp2f(M - nm);  // 0 while nothing was merged
-            L *= r;
-            a *= r;
-#pragma unroll
-            for (int k = 0; k < kCombineRegs; ++k) {
-                const float wgt = exp2f(pm[k] - nm);
-                L += wgt * pl[k];
-                a += wgt * pa[k];
-            }
-            M = nm;
-        }
+        merge_partials(part_m, part_l, part_acc, d, c, n, pidx, M, L, a);
         out[((int64_t)b * Hq + qh) * d + c] = (L > 0.f) ? a / L : 0.f;
     }
 }
@@ -811,149 +769,6 @@ __global__ __launch_bounds__(256) void combine_flat_kernel(
         if (i < n_f) return ((int64_t)u * nsa + i) * G + g;
         return (hp0 + (int64_t)u * R + (i - n_f)) * G + g;
     });
-}
-
-// ---------------------------------------------------------------- verification attention
-
-// OasisKV page, Fig. 7 (right): the attention kernel runs the normal and the
-// draft queries over the sparse KV together.  Query set j (0: the current
-// query, j >= 1: draft j) of every head of the group attends over the attended
-// blocks and, causally, over draft tokens 1..j.  The M = G (1 + D) rows of a
-// unit are split into chunks of 16, 8, 4, 2 or 1 rows; each chunk is one pass
-// of the block attention kernel above with G = chunk rows (one pass reads the
-// attended KV once for all of its rows), and the combine below merges a row's
-// partials with its draft tokens.
-struct VerifyChunks {
-    int n;
-    int r0[12];
-    int rows[12];
-};
-
-static VerifyChunks verify_chunks(int M) {
-    VerifyChunks c{};
-    int r = 0;
-    while (r < M && c.n < 12) {
-        int g = 16;
-        while (g > M - r) g >>= 1;
-        c.r0[c.n] = r;
-        c.rows[c.n] = g;
-        ++c.n;
-        r += g;
-    }
-    return c;
-}
-
-__device__ __forceinline__ int verify_chunk_of(const VerifyChunks &c, int r) {
-    int k = 0;
-    while (k + 1 < c.n && c.r0[k + 1] <= r) ++k;
-    return k;
-}
-
-// Row r of unit u -> chunk buffer [units][rows][D] of its chunk.
-__global__ __launch_bounds__(64) void verify_pack_kernel(const uint16_t *__restrict__ q,
-                                                         const uint16_t *__restrict__ drafts,
-                                                         uint16_t *__restrict__ qpack, int B,
-                                                         int Hq, int Hkv, int G,
-                                                         VerifyChunks ch, int64_t units) {
-    constexpr int D = 128;
-    const int r = blockIdx.x;
-    const int64_t u = blockIdx.y;
-    const int b = (int)(u / Hkv), h = (int)(u % Hkv);
-    const int j = r / G, g = r % G;
-    const int k = verify_chunk_of(ch, r);
-    const uint16_t *src = j == 0 ? q + ((int64_t)b * Hq + h * G + g) * D
-                                 : drafts + (((int64_t)(j - 1) * B + b) * Hq + h * G + g) * D;
-    uint16_t *dst = qpack + units * ch.r0[k] * D + (u * ch.rows[k] + (r - ch.r0[k])) * D;
-    const int c = threadIdx.x * 8;
-    if (c < D) gstore16(dst + c, gload16(src + c));
-}
-
-// One workgroup (128 threads, thread c = output dim c) per (row, unit).
-__global__ __launch_bounds__(128) void verify_combine_kernel(
-    const float *__restrict__ vpart_m, const float *__restrict__ vpart_l,
-    const float *__restrict__ vpart_acc, const uint16_t *__restrict__ q,
-    const uint16_t *__restrict__ drafts, const uint16_t *__restrict__ kd,
-    const uint16_t *__restrict__ vd, float *__restrict__ out, int B, int Hq, int Hkv, int G,
-    int ns, VerifyChunks ch, int64_t units, float scale_log2) {
-    constexpr int D = 128;
-    __shared__ float red[2];
-    const int r = blockIdx.x;
-    const int64_t u = blockIdx.y;
-    const int b = (int)(u / Hkv), h = (int)(u % Hkv);
-    const int j = r / G, g = r % G;
-    const int k = verify_chunk_of(ch, r);
-    const int rows = ch.rows[k], rr = r - ch.r0[k];
-    const int64_t base = units * ns * ch.r0[k];  // this chunk's partial rows
-    const int c = threadIdx.x;
-    auto pidx = [&](int s) -> int64_t { return base + (u * ns + s) * rows + rr; };
-    float M = -INFINITY;
-    for (int s = 0; s < ns; ++s) M = fmaxf(M, vpart_m[pidx(s)]);
-    float L = 0.f, a = 0.f;
-    if (M != -INFINITY)
-        for (int s = 0; s < ns; ++s) {
-            const int64_t pi = pidx(s);
-            const float w = exp2f(vpart_m[pi] - M);
-            L += w * vpart_l[pi];
-            a += w * vpart_acc[pi * D + c];
-        }
-    if (j > 0) {
-        const uint16_t *qr = drafts + (((int64_t)(j - 1) * B + b) * Hq + h * G + g) * D;
-        const float qv = __uint_as_float((uint32_t)qr[c] << 16);
-        for (int i = 0; i < j; ++i) {  // draft tokens 1..j
-            const int64_t kv = (((int64_t)i * B + b) * Hkv + h) * D + c;
-            float dot = qv * __uint_as_float((uint32_t)kd[kv] << 16);
-            dot = wave_sum(dot);
-            if ((threadIdx.x & 63) == 0) red[threadIdx.x >> 6] = dot;
-            __syncthreads();
-            const float x = (red[0] + red[1]) * scale_log2;
-            __syncthreads();
-            const float mn = fmaxf(M, x);
-            const float alpha = exp2f(M - mn), p = exp2f(x - mn);
-            L = L * alpha + p;
-            a = a * alpha + p * __uint_as_float((uint32_t)vd[kv] << 16);
-            M = mn;
-        }
-    }
-    (void)q;
-    out[(((int64_t)j * B + b) * Hq + h * G + g) * D + c] = L > 0.f ? a / L : 0.f;
-}
-
-int verify_rows(const Dims &D, int n_drafts) { return D.G * (1 + n_drafts); }
-
-hipError_t launch_verify(const Dims &D, const AttnPlan &P, int n_drafts, const void *q,
-                         const void *drafts, const void *kd, const void *vd, void *slots,
-                         const int32_t *att_block, const int32_t *att_slot,
-                         const int32_t *counts, int64_t T, void *qpack, float *vpart_m,
-                         float *vpart_l, float *vpart_acc, float *out, hipStream_t st) {
-    const int M = verify_rows(D, n_drafts);
-    const VerifyChunks ch = verify_chunks(M);
-    const int64_t units = D.units();
-    OASIS_LAUNCH(verify_pack_kernel, dim3((unsigned)M, (unsigned)units), dim3(64), 0, st,
-                 (const uint16_t *)q, (const uint16_t *)drafts, (uint16_t *)qpack, D.B, D.Hq,
-                 D.Hkv, D.G, ch, units);
-    hipError_t e = hipGetLastError();
-    if (e != hipSuccess) return e;
-    // one block-attention pass per chunk, every attended block from its slot
-    AttnPlan Pc = P;
-    Pc.nsf_max = 0;
-    Pc.nsa = P.ns1;
-    Pc.flat = false;  // per-chunk passes keep the per-unit split kernel
-    for (int k = 0; k < ch.n; ++k) {
-        Dims Dc = D;
-        Dc.G = ch.rows[k];
-        Dc.Hq = D.Hkv * ch.rows[k];
-        const int64_t rows0 = units * (int64_t)ch.r0[k];
-        e = launch_attention(Dc, Pc, 0, 0, (const uint16_t *)qpack + rows0 * 128, slots, nullptr,
-                             att_block, att_slot, counts, T, vpart_m + rows0 * Pc.nsa,
-                             vpart_l + rows0 * Pc.nsa, vpart_acc + rows0 * Pc.nsa * 128, st);
-        if (e != hipSuccess) return e;
-    }
-    const float scale_log2 = kLog2e / sqrtf(128.f);
-    OASIS_LAUNCH(verify_combine_kernel, dim3((unsigned)M, (unsigned)units), dim3(128), 0, st,
-                 vpart_m, vpart_l, vpart_acc, (const uint16_t *)q, (const uint16_t *)drafts,
-                 (const uint16_t *)kd, (const uint16_t *)vd, out, D.B, D.Hq, D.Hkv, D.G,
-                 Pc.nsa, ch, units, scale_log2);
-    return hipGetLastError();
 }
 
 // ---------------------------------------------------------------- host side
@@ -1031,7 +846,21 @@ AttnPlan plan_attention(const Dims &D) {
         P.nsf_max = 0;
     }
     P.nsa = P.nsf_max + (P.flat ? 0 : P.ns1);
+    P.vns = P.ns1;
     return P;
+}
+
+int verify_stride(const Dims &D) {
+    int v = plan_attention(D).ns1;
+    if (!mfma_ok(D)) return v;
+    for (int g : {1, 2, 4, 8, 16}) {
+        Dims Dc = D;
+        Dc.G = g;
+        Dc.Hq = D.Hkv * g;
+        const AttnPlan Pc = plan_attention(Dc);
+        v = std::max(v, Pc.flat ? Pc.flat_rows : Pc.ns1);
+    }
+    return v;
 }
 
 int64_t attn_partial_rows(const Dims &D, const AttnPlan &P) {

@@ -138,6 +138,9 @@ struct AttnPlan {
     // flat_rows per unit.
     bool flat;
     int flat_waves, flat_pmin, flat_rows;
+    // verification attention: partial rows per (unit, query row) of its
+    // buffers (at least the split and balanced strides of every chunk size)
+    int vns;
 };
 AttnPlan plan_attention(const Dims &D);
 // Rows (G floats of m and l, G x d of acc each) of the partial buffers.
@@ -152,6 +155,9 @@ hipError_t launch_attention(const Dims &D, const AttnPlan &P, int mode, int nsf,
                             void *slots, const void *host_kv, const int32_t *att_block,
                             const int32_t *att_slot, const int32_t *counts, int64_t T,
                             float *part_m, float *part_l, float *part_acc, hipStream_t st);
+// Partial rows per (unit, query row) the verification attention's buffers
+// need for every chunk size.
+int verify_stride(const Dims &D);
 // Verification attention (normal and draft query sets together, causal over
 // the draft tokens): rows per unit, and the whole pass (pack, one block
 // attention per chunk of rows, combine).  bf16, d = 128, bs = 16.
