@@ -417,9 +417,15 @@ __device__ __forceinline__ int block_valid(int64_t T, int32_t blk) {
 // fetched blocks end the list).  Wave f of the F = 4 n_fetch_wg fetch waves
 // takes items f, f + F, ...: it reads the block from the pinned host KV over
 // the host link, writes it into its slot (the copy later steps will hit),
-// attends to it from registers and writes partial i of the unit; an item past
-// the unit's fetch count writes an empty partial.  A few such waves keep the
-// host link saturated while holding only a small share of the CU slots.
+// attends to it from registers and writes partial i of the unit; items past
+// their unit's fetch count get an empty partial (m = -inf).  A wave first
+// reads the list entries of up to 64 of its items at once, one per lane, and
+// then streams the existing ones one after the other: with the entries in
+// registers, no dependent list read sits between two host reads.  Keeping a
+// second item's host loads in flight (two register buffers) measured slower
+// on the host link here: the extra registers cost the resident waves of the
+// same launch one wave per SIMD.  A few such waves keep the host link
+// saturated while holding only a small share of the CU slots.
 template <int G, typename W>
 __device__ __forceinline__ void fetch_waves(
     W &st, int wave, const uint16_t *__restrict__ q, uint16_t *__restrict__ slots,
@@ -428,66 +434,54 @@ __device__ __forceinline__ void fetch_waves(
     int Hkv, int K, int S, int64_t NBmax, int cap, int n_fetch_wg, int nsa, int64_t units,
     float scale_log2, float *__restrict__ part_m, float *__restrict__ part_l,
     float *__restrict__ part_acc) {
+    const int lane = threadIdx.x & 63;
     const int64_t F = 4LL * n_fetch_wg;
     const int64_t n_items = units * cap;
-    int64_t it = (int64_t)blockIdx.x * 4 + wave;
-    int64_t cur_u = -1;
-    uint4 kr[2][4], vr[2][4];
-    // item -> (unit, i, entry); returns the source block pointer or null
-    auto locate = [&](int64_t item, int64_t &u, int &i, int32_t &blk, int32_t &slot) -> bool {
-        u = item / cap;
-        i = (int)(item % cap);
-        const int n_att = __builtin_amdgcn_readfirstlane(counts[u * 4 + 0]);
-        const int n_fetch = __builtin_amdgcn_readfirstlane(counts[u * 4 + 2]);
-        if (i >= n_fetch) return false;
-        const int e = n_att - n_fetch + i;  // the fetched blocks end the list
-        blk = __builtin_amdgcn_readfirstlane(att_block[u * K + e]);
-        slot = __builtin_amdgcn_readfirstlane(att_slot[u * K + e]);
-        return true;
-    };
-    int64_t u0;
-    int i0;
-    int32_t blk0 = 0, slot0 = 0;
-    bool have0 = it < n_items && locate(it, u0, i0, blk0, slot0);
-    if (it < n_items && have0) st.load(kr[0], vr[0], host_kv + (u0 * NBmax + blk0) * W::BLK);
-    int buf = 0;
-    for (; it < n_items; it += F) {
-        // prefetch the next item while this one is processed
-        const int64_t nx = it + F;
-        int64_t u1 = 0;
-        int i1 = 0;
-        int32_t blk1 = 0, slot1 = 0;
-        const bool have1 = nx < n_items && locate(nx, u1, i1, blk1, slot1);
-        if (have1) {
-            if (buf == 0) st.load(kr[1], vr[1], host_kv + (u1 * NBmax + blk1) * W::BLK);
-            else st.load(kr[0], vr[0], host_kv + (u1 * NBmax + blk1) * W::BLK);
-        }
-        __builtin_amdgcn_sched_barrier(0);  // keep the prefetch ahead of the compute
-        if (u0 != cur_u) {
-            const int64_t b = u0 / Hkv;
-            st.init(q, b, Hq, (int)(u0 % Hkv));
-            cur_u = u0;
-        } else {
-            st.reset();
-        }
-        if (have0) {
-            uint16_t *dst = slots + (u0 * S + slot0) * (int64_t)W::BLK;
-            if (buf == 0) {
-                st.store(dst, kr[0], vr[0]);
-                st.block(kr[0], vr[0], block_valid(T_, blk0), scale_log2);
+    const int64_t it0 = (int64_t)blockIdx.x * 4 + wave;
+    if (it0 >= n_items) return;
+    const int64_t n_my = (n_items - it0 + F - 1) / F;
+    auto rl = [](int v, int l) { return __builtin_amdgcn_readlane(v, l); };
+    for (int64_t c0 = 0; c0 < n_my; c0 += 64) {
+        // lane l: item it0 + (c0 + l) F = (unit u, index i)
+        const int64_t item = it0 + (c0 + lane) * F;
+        const bool in = c0 + lane < n_my;
+        const int u = in ? (int)(item / cap) : 0, i = in ? (int)(item % cap) : 0;
+        bool ok = false;
+        int blk = 0, slot = 0;
+        if (in) {
+            const int n_att = counts[(int64_t)u * 4 + 0], n_fetch = counts[(int64_t)u * 4 + 2];
+            if (i < n_fetch) {
+                const int e = n_att - n_fetch + i;
+                blk = att_block[(int64_t)u * K + e];
+                slot = att_slot[(int64_t)u * K + e];
+                ok = true;
             } else {
-                st.store(dst, kr[1], vr[1]);
-                st.block(kr[1], vr[1], block_valid(T_, blk0), scale_log2);
+                for (int g = 0; g < G; ++g) {
+                    part_m[((int64_t)u * nsa + i) * G + g] = -INFINITY;
+                    part_l[((int64_t)u * nsa + i) * G + g] = 0.f;
+                }
             }
         }
-        st.reduce();
-        st.write_partial((u0 * nsa + i0) * G, part_m, part_l, part_acc);
-        u0 = u1;
-        i0 = i1;
-        blk0 = blk1;
-        slot0 = slot1;
-        have0 = have1;
-        buf ^= 1;
+        const uint64_t mask = __ballot(ok);
+        if (mask == 0) continue;
+        auto src = [&](int l) {
+            const int ul = rl(u, l);
+            return host_kv + ((int64_t)ul * NBmax + rl(blk, l)) * W::BLK;
+        };
+        // lane l's item: read it from the host, store it into its slot,
+        // attend, write partial i of its unit
+        for (uint64_t m = mask; m; m &= m - 1) {
+            const int l = __builtin_ctzll(m);
+            const int ul = rl(u, l);
+            uint4 kk[4], vv[4];
+            st.load_q(st.qb, q, ul / Hkv, Hq, ul % Hkv);
+            st.load(kk, vv, src(l));
+            st.reset();
+            st.block(kk, vv, block_valid(T_, rl(blk, l)), scale_log2);
+            st.store(slots + ((int64_t)ul * S + rl(slot, l)) * (int64_t)W::BLK, kk, vv);
+            st.reduce();
+            st.write_partial(((int64_t)ul * nsa + rl(i, l)) * G, part_m, part_l, part_acc);
+        }
     }
 }
 
