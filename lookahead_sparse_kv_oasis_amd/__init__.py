@@ -15,7 +15,9 @@ import os
 import numpy as np
 
 _PKG = os.path.dirname(os.path.abspath(__file__))
-LIB_PATH = os.path.join(_PKG, "liboasis.so")
+# OASIS_LIBRARY names another build of the same library (the host-sanitized
+# one that tests/test_sanitizers.py runs the host-side tests against).
+LIB_PATH = os.environ.get("OASIS_LIBRARY") or os.path.join(_PKG, "liboasis.so")
 
 OASIS_OK, OASIS_E_INVAL, OASIS_E_NOMEM, OASIS_E_HIP = 0, -1, -2, -3
 OASIS_E_CAPACITY, OASIS_E_STATE, OASIS_E_NONFINITE, OASIS_E_DEVICE = -4, -5, -6, -7

@@ -25,9 +25,17 @@ def sources():
     return sorted(glob.glob(os.path.join(CSRC, "*.hip")))
 
 
-def _compile(src):
-    obj = os.path.join(OBJ, os.path.basename(src) + ".o")
-    cmd = [HIPCC, *FLAGS, "-c", src, "-o", obj]
+# Host-side AddressSanitizer + UndefinedBehaviorSanitizer build (device code
+# unchanged): each sanitizer flag applies to the host pass only.
+SAN_HOST = ["-Xarch_host", "-fsanitize=address", "-Xarch_host", "-fsanitize=undefined",
+            "-Xarch_host", "-fno-omit-frame-pointer", "-Xarch_host", "-g"]
+SAN_OBJ = os.path.join(ROOT, "_build", "liboasis_san")
+SAN_LIB = os.path.join(ROOT, "_build", "san", "liboasis_san.so")
+
+
+def _compile(src, san=False):
+    obj = os.path.join(SAN_OBJ if san else OBJ, os.path.basename(src) + ".o")
+    cmd = [HIPCC, *FLAGS, *(SAN_HOST if san else []), "-c", src, "-o", obj]
     r = subprocess.run(cmd, capture_output=True, text=True)
     noise = "is not a recognized feature for this target"
     msg = "\n".join(l for l in (r.stdout + r.stderr).splitlines() if noise not in l)
@@ -36,22 +44,28 @@ def _compile(src):
     return obj, msg
 
 
-def build(verbose: bool = False) -> str:
-    """Compile every HIP source for gfx950 and link liboasis.so."""
-    os.makedirs(OBJ, exist_ok=True)
+def build(verbose: bool = False, sanitize: bool = False) -> str:
+    """Compile every HIP source for gfx950 and link liboasis.so.
+
+    sanitize=True links the host-sanitized variant into _build/san/ instead
+    (loaded only through OASIS_LIBRARY, in a process that preloads clang's
+    AddressSanitizer runtime)."""
+    os.makedirs(SAN_OBJ if sanitize else OBJ, exist_ok=True)
     with ThreadPoolExecutor(min(8, os.cpu_count() or 4)) as ex:
-        results = list(ex.map(_compile, sources()))
+        results = list(ex.map(lambda s: _compile(s, sanitize), sources()))
     for obj, msg in results:
         if verbose and msg.strip():
             print(msg)
-    tmp = LIB + ".tmp%d" % os.getpid()
+    out = SAN_LIB if sanitize else LIB
+    os.makedirs(os.path.dirname(out), exist_ok=True)
+    tmp = out + ".tmp%d" % os.getpid()
     cmd = [HIPCC, "--offload-arch=gfx950", "-shared", "-fPIC", "-o", tmp,
            *[o for o, _ in results], "-lpthread"]
     r = subprocess.run(cmd, capture_output=True, text=True)
     if r.returncode != 0:
         raise RuntimeError("link failed:\n" + r.stdout + r.stderr)
-    os.replace(tmp, LIB)
-    return LIB
+    os.replace(tmp, out)
+    return out
 
 
 if __name__ == "__main__":

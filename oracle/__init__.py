@@ -28,19 +28,31 @@ import numpy as np
 _HERE = os.path.dirname(os.path.abspath(__file__))
 _SRC = os.path.join(_HERE, "oasis_oracle.c")
 _LIB = os.path.join(_HERE, "liboasis_oracle.so")
+# OASIS_ORACLE_SANITIZE=1 loads an AddressSanitizer + UndefinedBehaviorSanitizer
+# build instead (the process must preload gcc's libasan; tests/test_sanitizers.py
+# runs the oracle tests that way in a child process).
+_SAN_LIB = os.path.join(os.path.dirname(_HERE), "_build", "san", "liboasis_oracle_san.so")
+SAN_FLAGS = ["-O1", "-g", "-fsanitize=address,undefined", "-fno-omit-frame-pointer",
+             "-fno-sanitize-recover=undefined"]
 
 F32 = 0
 BF16 = 1
 
 
-def build(force: bool = True) -> str:
-    """Compile the oracle with plain gcc (no fast-math, no shared headers)."""
-    if force or not os.path.exists(_LIB) or os.path.getmtime(_LIB) < os.path.getmtime(_SRC):
-        tmp = _LIB + ".tmp%d" % os.getpid()
-        subprocess.check_call(["gcc", "-O2", "-std=c11", "-fPIC", "-shared", "-Wall", "-Wextra",
+def build(force: bool = True, sanitize: bool = False) -> str:
+    """Compile the oracle with plain gcc (no fast-math, no shared headers).
+
+    sanitize=True builds the AddressSanitizer + UndefinedBehaviorSanitizer
+    variant (same source, -O1 -g) into _build/san/."""
+    out = _SAN_LIB if sanitize else _LIB
+    if force or not os.path.exists(out) or os.path.getmtime(out) < os.path.getmtime(_SRC):
+        os.makedirs(os.path.dirname(out), exist_ok=True)
+        tmp = out + ".tmp%d" % os.getpid()
+        opt = SAN_FLAGS if sanitize else ["-O2"]
+        subprocess.check_call(["gcc", *opt, "-std=c11", "-fPIC", "-shared", "-Wall", "-Wextra",
                                "-o", tmp, _SRC, "-lm"])
-        os.replace(tmp, _LIB)
-    return _LIB
+        os.replace(tmp, out)
+    return out
 
 
 _lib = None
@@ -49,9 +61,9 @@ _lib = None
 def lib():
     global _lib
     if _lib is None:
-        if not os.path.exists(_LIB) or os.path.getmtime(_LIB) < os.path.getmtime(_SRC):
-            build(force=True)
-        L = ctypes.CDLL(_LIB)
+        san = os.environ.get("OASIS_ORACLE_SANITIZE") == "1"
+        path = build(force=False, sanitize=san)
+        L = ctypes.CDLL(path)
         vp, dp, ip, fp = ctypes.c_void_p, ctypes.POINTER(ctypes.c_double), \
             ctypes.POINTER(ctypes.c_int32), ctypes.POINTER(ctypes.c_float)
         i64, i32 = ctypes.c_int64, ctypes.c_int
