@@ -586,7 +586,9 @@ def bench_layer(args, w, steps, warmup, main_leg=True, shared=None):
                 "frac_of_same_size_read": frac_of(sa3, same(score_bytes + attn_bytes))}
     if verify is not None:
         verify["attended_blocks"] = attended
+        # bytes the passes read, and the attended KV once (what the call needs)
         verify["hbm_gbps"] = (verify["passes"] * attended * blk_bytes) / (verify["avg_ms"] * 1e-3) / 1e9
+        verify["attended_kv_gbps"] = attended * blk_bytes / (verify["avg_ms"] * 1e-3) / 1e9
         line["verify_attention"] = verify
     if rec is not None:
         line["ordering"] = "lookahead"
@@ -622,16 +624,21 @@ def time_verify(run, w, calls=20):
         run.h.oasis_sparse_attn_verify(run.q, run.drafts[t], D, kd, vd, out)
     b.record()
     torch.cuda.synchronize()
+    # passes of the library's cut: 32 rows while 32 remain, then the next
+    # power of two at or above the rest (padded)
     rows = w.group * (1 + D)
-    passes, r = 0, rows
+    passes, padded, r = 0, 0, rows
     while r > 0:
-        g = 16
-        while g > r:
-            g //= 2
-        r -= g
+        g = 32
+        if r < 32:
+            g = 1
+            while g < r:
+                g *= 2
+        r -= min(r, g)
+        padded += g
         passes += 1
     return {"avg_ms": a.elapsed_time(b) / calls, "query_sets": 1 + D, "rows_per_kv_head": rows,
-            "passes": passes, "calls": calls}
+            "padded_rows_per_kv_head": padded, "passes": passes, "calls": calls}
 
 
 def warmup_ahead_with_recall(run, warmup, stream, cap_correct=0):

@@ -222,12 +222,15 @@ int oasis_sparse_attn(oasis_t *h, const void *q_dev, float *out_dev, hipStream_t
  * [n_drafts][B][Hkv][d] the draft tokens' keys and values (not appended to
  * the cache).  out_dev [1+n_drafts][B][Hq][d] fp32: set 0 = oasis_sparse_attn
  * of q; set j attends over the attended blocks of the last select (tokens
- * < T) and draft tokens 1..j (causal).  Fetches pending from the last select
- * are copied first.  bf16 layouts with d = 128 and block_size 16 only
- * (OASIS_E_INVAL otherwise); its scratch is allocated with the handle, for
- * max_drafts drafts, and shared by the handle's verify calls, which run in
- * the order they were issued (a call on another stream waits for the last
- * attention or verify). */
+ * < T) and draft tokens 1..j (causal).  The G (1 + n_drafts) query rows per
+ * KV head go through the KV in passes of 32 rows, the last one padded to a
+ * power of two (20 rows: one pass); more than 12 passes is OASIS_E_INVAL.
+ * Fetches pending from the last select are copied first.  bf16 layouts with
+ * d = 128 and block_size 16 only, all pointers 16-byte aligned (OASIS_E_INVAL
+ * otherwise); its scratch is allocated with the handle, for max_drafts
+ * drafts, and shared by the handle's verify calls, which run in the order
+ * they were issued (a call on another stream waits for the last attention or
+ * verify). */
 int oasis_sparse_attn_verify(oasis_t *h, const void *q_dev, const void *drafts_dev,
                              int32_t n_drafts, const void *k_drafts_dev,
                              const void *v_drafts_dev, float *out_dev, hipStream_t stream);

@@ -552,9 +552,10 @@ int create_handle(const oasis_layout *layout, int32_t block_size, int32_t budget
               dmal((void **)&h->set_buf, sizeof(int32_t) * units * (2 * (size_t)S + 1)) &&
               dmal((void **)&h->evict_buf, sizeof(int32_t) * units * ((size_t)K + 1));
     h->evict_cap = (size_t)units * (K + 1);
-    if (ok && h->plan.mfma) {
+    const int vrows = verify_rows(D, L.max_drafts);  // padded rows per unit, -1: too many
+    if (ok && h->plan.mfma && vrows > 0) {
         // verification attention scratch, sized for max_drafts
-        const size_t rows = (size_t)units * verify_rows(D, L.max_drafts);
+        const size_t rows = (size_t)units * vrows;
         ok = dmal(&h->vq, rows * 128 * sizeof(uint16_t)) &&
              dmal((void **)&h->vpart_m, rows * h->plan.vns * sizeof(float)) &&
              dmal((void **)&h->vpart_l, rows * h->plan.vns * sizeof(float)) &&
@@ -972,10 +973,14 @@ extern "C" int oasis_sparse_attn_verify(oasis_t *h, const void *q_dev, const voi
     if (n_drafts < 0 || n_drafts > h->L.max_drafts)
         return fail(h, OASIS_E_INVAL, "verify: n_drafts %d outside [0, %d]", n_drafts,
                     h->L.max_drafts);
-    if (n_drafts > 0 && (!drafts_dev || !k_drafts_dev || !v_drafts_dev || !aligned16(drafts_dev)))
-        return fail(h, OASIS_E_INVAL, "verify: null drafts or draft K/V");
+    if (n_drafts > 0 && (!drafts_dev || !k_drafts_dev || !v_drafts_dev || !aligned16(drafts_dev) ||
+                         !aligned16(k_drafts_dev) || !aligned16(v_drafts_dev)))
+        return fail(h, OASIS_E_INVAL, "verify: null or misaligned drafts or draft K/V");
     if (!h->plan.mfma)
         return fail(h, OASIS_E_INVAL, "verify: needs the bf16, d = 128, block 16 layout");
+    if (!h->vq || verify_rows(h->D, n_drafts) < 0)
+        return fail(h, OASIS_E_INVAL, "verify: %d query rows per KV head exceed the verify passes",
+                    h->D.G * (1 + n_drafts));
     if (!h->selected) return fail(h, OASIS_E_STATE, "verify attention before select");
     const Dims &D = h->D;
     TRY(use_stream(h, stream));

@@ -259,25 +259,28 @@ template <int G> struct AttnWave {
     }
 };
 
-// 16 heads per KV head (and the 16-row chunks of the verification
-// attention): P V on the matrix cores as well, v_mfma_f32_16x16x16_bf16 per
-// 16 output dimensions.  The probabilities of S^T already sit in the A-operand
-// order (lane l: head l % 16, tokens 4 (l / 16) + r); each is split into a
-// bf16 high part and the bf16 of the remainder, two products whose sum keeps
-// the relative error near 2^-16.  The B operand (lane l: dimension 16 n +
-// l % 16, tokens 4 (l / 16) + r) comes from the block's V rows staged in
-// LDS, rows past the valid tokens zeroed.  The output O[head][dim] sits in 8
-// accumulators per lane (lane l: dimension 16 n + l % 16, heads 4 (l / 16) +
-// r), 32 registers instead of the 128 the vector-ALU form needs for 16
-// heads, which had left one wave per SIMD.
+// 16 or 32 query rows per KV head (16 heads per KV head, and the 16- and
+// 32-row chunks of the verification attention): P V on the matrix cores as
+// well, v_mfma_f32_16x16x16_bf16 per 16 rows and 16 output dimensions.  The
+// rows form NT = G / 16 tiles of 16; S^T of tile t is its own
+// v_mfma_f32_16x16x32_bf16 chain.  The probabilities of S^T already sit in
+// the A-operand order (lane l: row 16 t + l % 16, tokens 4 (l / 16) + r);
+// each is split into a bf16 high part and the bf16 of the remainder, two
+// products whose sum keeps the relative error near 2^-16.  The B operand
+// (lane l: dimension 16 n + l % 16, tokens 4 (l / 16) + r) comes from the
+// block's V rows staged in LDS once for all tiles, rows past the valid tokens
+// zeroed.  The output O[row][dim] of tile t sits in 8 accumulators per lane
+// (lane l: dimension 16 n + l % 16, rows 16 t + 4 (l / 16) + r): 32 registers
+// per tile instead of the 128 the vector-ALU form needs for 16 rows.
 template <int G> struct AttnWaveM {
-    static_assert(G == 16, "16 heads fill the matrix rows");
+    static_assert(G == 16 || G == 32, "whole 16-row tiles");
+    static constexpr int NT = G / 16;
     static constexpr int D = 128, BS = 16, BLK = 2 * BS * D;
     static constexpr int kStage = BS * D;  // bf16 elements staged per wave
     int col, kg, koff, voff;
-    bf16x8 qb[4];
-    float m, lsum;
-    f32x4 o[8];
+    bf16x8 qb[4 * NT];
+    float m[NT], lsum[NT];
+    f32x4 o[NT][8];
     uint16_t *vst = nullptr;  // this wave's staging area in LDS
 
     __device__ __forceinline__ void lanes() {
@@ -291,18 +294,25 @@ template <int G> struct AttnWaveM {
         load_q(qb, q, b, Hq, h);
         reset();
     }
-    __device__ __forceinline__ void load_q(bf16x8 (&dst)[4], const uint16_t *q, int64_t b, int Hq,
-                                           int h) const {
-        const uint16_t *qr = q + (b * Hq + h * G + col) * D + 8 * kg;
+    __device__ __forceinline__ void load_q(bf16x8 (&dst)[4 * NT], const uint16_t *q, int64_t b,
+                                           int Hq, int h) const {
 #pragma unroll
-        for (int i = 0; i < 4; ++i)
-            dst[i] = __builtin_bit_cast(bf16x8, *reinterpret_cast<const uint4 *>(qr + 32 * i));
+        for (int t = 0; t < NT; ++t) {
+            const uint16_t *qr = q + (b * Hq + h * G + 16 * t + col) * D + 8 * kg;
+#pragma unroll
+            for (int i = 0; i < 4; ++i)
+                dst[4 * t + i] =
+                    __builtin_bit_cast(bf16x8, *reinterpret_cast<const uint4 *>(qr + 32 * i));
+        }
     }
     __device__ __forceinline__ void reset() {
-        m = -INFINITY;
-        lsum = 0.f;
 #pragma unroll
-        for (int n = 0; n < 8; ++n) o[n] = f32x4{0.f, 0.f, 0.f, 0.f};
+        for (int t = 0; t < NT; ++t) {
+            m[t] = -INFINITY;
+            lsum[t] = 0.f;
+#pragma unroll
+            for (int n = 0; n < 8; ++n) o[t][n] = f32x4{0.f, 0.f, 0.f, 0.f};
+        }
     }
     __device__ __forceinline__ void load(uint4 (&kk)[4], uint4 (&vv)[4], const uint16_t *p) const {
 #pragma unroll
@@ -326,31 +336,45 @@ template <int G> struct AttnWaveM {
     }
     __device__ __forceinline__ void block(const uint4 (&kk)[4], const uint4 (&vv)[4], int valid,
                                           float scale_log2) {
-        f32x4 s4 = {0.f, 0.f, 0.f, 0.f};
+        s16x4 ahi[NT], alo[NT];
 #pragma unroll
-        for (int c = 0; c < 4; ++c)
-            s4 = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, kk[c]), qb[c],
-                                                         s4, 0, 0, 0);
-        float sr[4];
+        for (int t = 0; t < NT; ++t) {
+            f32x4 s4 = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-        for (int r = 0; r < 4; ++r) sr[r] = (4 * kg + r < valid) ? s4[r] * scale_log2 : -INFINITY;
-        float bm = fmaxf(fmaxf(sr[0], sr[1]), fmaxf(sr[2], sr[3]));
-        bm = fmaxf(bm, __shfl_xor(bm, 16, 64));
-        bm = fmaxf(bm, __shfl_xor(bm, 32, 64));
-        const float mn = fmaxf(m, bm);
-        const bool live = mn != -INFINITY;
-        const float alpha = live ? exp2f(m - mn) : 1.f;
-        float p[4];
+            for (int c = 0; c < 4; ++c)
+                s4 = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, kk[c]),
+                                                             qb[4 * t + c], s4, 0, 0, 0);
+            float sr[4];
 #pragma unroll
-        for (int r = 0; r < 4; ++r) p[r] = live ? exp2f(sr[r] - mn) : 0.f;
-        lsum = lsum * alpha + ((p[0] + p[1]) + (p[2] + p[3]));
-        m = mn;
-        // rescale the rows of O (heads 4 kg + r); head h's factor is in lane h
+            for (int r = 0; r < 4; ++r)
+                sr[r] = (4 * kg + r < valid) ? s4[r] * scale_log2 : -INFINITY;
+            float bm = fmaxf(fmaxf(sr[0], sr[1]), fmaxf(sr[2], sr[3]));
+            bm = fmaxf(bm, __shfl_xor(bm, 16, 64));
+            bm = fmaxf(bm, __shfl_xor(bm, 32, 64));
+            const float mn = fmaxf(m[t], bm);
+            const bool live = mn != -INFINITY;
+            const float alpha = live ? exp2f(m[t] - mn) : 1.f;
+            float p[4];
 #pragma unroll
-        for (int r = 0; r < 4; ++r) {
-            const float ar = __shfl(alpha, 4 * kg + r, 64);
+            for (int r = 0; r < 4; ++r) p[r] = live ? exp2f(sr[r] - mn) : 0.f;
+            lsum[t] = lsum[t] * alpha + ((p[0] + p[1]) + (p[2] + p[3]));
+            m[t] = mn;
+            // rescale the rows of O (rows 4 kg + r of the tile); row h's
+            // factor is in lane h
 #pragma unroll
-            for (int n = 0; n < 8; ++n) o[n][r] *= ar;
+            for (int r = 0; r < 4; ++r) {
+                const float ar = __shfl(alpha, 4 * kg + r, 64);
+#pragma unroll
+                for (int n = 0; n < 8; ++n) o[t][n][r] *= ar;
+            }
+            // P as bf16 high part + bf16 of the remainder
+#pragma unroll
+            for (int r = 0; r < 4; ++r) {
+                const uint32_t hb = __float_as_uint(p[r]) & 0xFFFF0000u;
+                const float rest = p[r] - __uint_as_float(hb);
+                ahi[t][r] = (short)(hb >> 16);
+                alo[t][r] = (short)(__float_as_uint(rest) >> 16);
+            }
         }
         // stage V (rows past the valid tokens zeroed: probability 0, bytes
         // possibly anything); the previous block's reads are done first
@@ -361,48 +385,52 @@ template <int G> struct AttnWaveM {
             *reinterpret_cast<uint4 *>(vst + (4 * kg + r) * D + 8 * col) = w;
         }
         wave_sync();
-        // P as bf16 high part + bf16 of the remainder
-        s16x4 ahi, alo;
-#pragma unroll
-        for (int r = 0; r < 4; ++r) {
-            const uint32_t hb = __float_as_uint(p[r]) & 0xFFFF0000u;
-            const float rest = p[r] - __uint_as_float(hb);
-            ahi[r] = (short)(hb >> 16);
-            alo[r] = (short)(__float_as_uint(rest) >> 16);
-        }
 #pragma unroll
         for (int n = 0; n < 8; ++n) {
             s16x4 bv;
 #pragma unroll
             for (int r = 0; r < 4; ++r) bv[r] = (short)vst[(4 * kg + r) * D + 16 * n + col];
-            o[n] = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(ahi, bv, o[n], 0, 0, 0);
-            o[n] = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(alo, bv, o[n], 0, 0, 0);
+#pragma unroll
+            for (int t = 0; t < NT; ++t) {
+                o[t][n] = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(ahi[t], bv, o[t][n], 0, 0, 0);
+                o[t][n] = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(alo[t], bv, o[t][n], 0, 0, 0);
+            }
         }
     }
     // Sum the four token groups of lsum; O already holds all the tokens.
     __device__ __forceinline__ void reduce() {
-        lsum += __shfl_xor(lsum, 16, 64);
-        lsum += __shfl_xor(lsum, 32, 64);
+#pragma unroll
+        for (int t = 0; t < NT; ++t) {
+            lsum[t] += __shfl_xor(lsum[t], 16, 64);
+            lsum[t] += __shfl_xor(lsum[t], 32, 64);
+        }
     }
     __device__ __forceinline__ void write_partial(int64_t pi0, float *part_m, float *part_l,
                                                   float *part_acc) const {
 #pragma unroll
-        for (int n = 0; n < 8; ++n)
+        for (int t = 0; t < NT; ++t) {
 #pragma unroll
-            for (int r = 0; r < 4; ++r) part_acc[(pi0 + 4 * kg + r) * D + 16 * n + col] = o[n][r];
-        if (kg == 0) {
-            part_m[pi0 + col] = m;
-            part_l[pi0 + col] = lsum;
+            for (int n = 0; n < 8; ++n)
+#pragma unroll
+                for (int r = 0; r < 4; ++r)
+                    part_acc[(pi0 + 16 * t + 4 * kg + r) * D + 16 * n + col] = o[t][n][r];
+            if (kg == 0) {
+                part_m[pi0 + 16 * t + col] = m[t];
+                part_l[pi0 + 16 * t + col] = lsum[t];
+            }
         }
     }
     __device__ __forceinline__ void stash(float (*sacc)[D], float *sm, float *sl) const {
 #pragma unroll
-        for (int n = 0; n < 8; ++n)
+        for (int t = 0; t < NT; ++t) {
 #pragma unroll
-            for (int r = 0; r < 4; ++r) sacc[4 * kg + r][16 * n + col] = o[n][r];
-        if (kg == 0) {
-            sm[col] = m;
-            sl[col] = lsum;
+            for (int n = 0; n < 8; ++n)
+#pragma unroll
+                for (int r = 0; r < 4; ++r) sacc[16 * t + 4 * kg + r][16 * n + col] = o[t][n][r];
+            if (kg == 0) {
+                sm[16 * t + col] = m[t];
+                sl[16 * t + col] = lsum[t];
+            }
         }
     }
 };
@@ -506,6 +534,7 @@ __global__ __launch_bounds__(256) void attn_mfma_kernel(
     int Hkv, int K, int S, int64_t NBmax, int mode, int cap, int n_fetch_wg, int nsf_max,
     int ns1, int nsa, int64_t units, float scale_log2, float *__restrict__ part_m,
     float *__restrict__ part_l, float *__restrict__ part_acc) {
+    static_assert(G <= 16, "the split path serves up to 16 rows per KV head");
     using W = std::conditional_t<G == 16, AttnWaveM<G>, AttnWave<G>>;
     constexpr int D = W::D;
     __shared__ __attribute__((aligned(16))) uint16_t vstage[4][W::kStage];
@@ -643,7 +672,7 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2))) void a
     int Hkv, int K, int S, int64_t NBmax, int mode, int cap, int n_fetch_wg, int nsa, int units,
     int W, int R, int pmin, float scale_log2, float *__restrict__ part_m,
     float *__restrict__ part_l, float *__restrict__ part_acc, int64_t hp0) {
-    using Wv = std::conditional_t<G == 16, AttnWaveM<G>, AttnWave<G>>;
+    using Wv = std::conditional_t<(G >= 16), AttnWaveM<G>, AttnWave<G>>;
     __shared__ __attribute__((aligned(16))) uint16_t vstage[4][Wv::kStage];
     __shared__ int32_t red[4];
     extern __shared__ int32_t pre[];
@@ -749,20 +778,28 @@ __global__ __launch_bounds__(256) void combine_kernel(const float *__restrict__ 
     });
 }
 
-// The same after the balanced hit path: the unit's n_f fetch partials (splits
-// [0, n_f) of nsa), then its R hit partial rows hp0 + u R + s, the unused
-// ones marked empty.
+// The same after the balanced hit path, d = 128: the unit's n_f fetch
+// partials (splits [0, n_f) of nsa), then its R hit partial rows
+// hp0 + u R + s, the unused ones marked empty.  One wave per output row (four
+// per workgroup), merging with merge_row_wave: the m and l of every partial
+// in one round trip, then the sums of the live ones only.
 __global__ __launch_bounds__(256) void combine_flat_kernel(
     const float *__restrict__ part_m, const float *__restrict__ part_l,
-    const float *__restrict__ part_acc, float *__restrict__ out, int Hq, int Hkv, int G, int d,
+    const float *__restrict__ part_acc, float *__restrict__ out, int Hq, int Hkv, int G,
     int nsa, int n_f, int R, int64_t hp0) {
-    const int qh = blockIdx.x, b = blockIdx.y;
+    const int qh = __builtin_amdgcn_readfirstlane((int)blockIdx.x * 4 + (int)(threadIdx.x >> 6));
+    const int b = blockIdx.y;
+    if (qh >= Hq) return;
     const int h = qh / G, g = qh % G;
     const int u = b * Hkv + h;
-    combine_row(part_m, part_l, part_acc, out, Hq, d, b, qh, n_f + R, [&](int i) -> int64_t {
+    float M = -INFINITY, L = 0.f;
+    float2 a = make_float2(0.f, 0.f);
+    merge_row_wave(part_m, part_l, part_acc, n_f + R, [&](int i) -> int64_t {
         if (i < n_f) return ((int64_t)u * nsa + i) * G + g;
         return (hp0 + (int64_t)u * R + (i - n_f)) * G + g;
-    });
+    }, M, L, a);
+    const float2 o = L > 0.f ? make_float2(a.x / L, a.y / L) : make_float2(0.f, 0.f);
+    *reinterpret_cast<float2 *>(out + ((int64_t)b * Hq + qh) * 128 + 2 * (threadIdx.x & 63)) = o;
 }
 
 // ---------------------------------------------------------------- host side
@@ -770,6 +807,12 @@ __global__ __launch_bounds__(256) void combine_flat_kernel(
 static bool mfma_ok(const Dims &D) {
     const bool g_ok = D.G == 1 || D.G == 2 || D.G == 4 || D.G == 8 || D.G == 16;
     return D.dtype == kBF16 && D.d == 128 && D.bs == 16 && g_ok;
+}
+
+// 32 rows per KV head (32 heads per KV head, or a 32-row verification chunk)
+// run on the balanced kernel only.
+static bool mfma32_ok(const Dims &D) {
+    return D.dtype == kBF16 && D.d == 128 && D.bs == 16 && D.G == 32;
 }
 
 // Units whose hit-entry prefix sums the balanced kernel keeps in LDS.
@@ -785,7 +828,7 @@ template <int G> static int flat_wgs_per_cu(int units) {
 
 AttnPlan plan_attention(const Dims &D) {
     AttnPlan P{};
-    P.mfma = mfma_ok(D);
+    P.mfma = mfma_ok(D) || mfma32_ok(D);
     const int64_t units = D.units();
     if (P.mfma) {
         // largest blocks-per-wave that still gives >= 1024 workgroups
@@ -807,7 +850,8 @@ AttnPlan plan_attention(const Dims &D) {
                 case 2: per_cu = flat_wgs_per_cu<2>(u); break;
                 case 4: per_cu = flat_wgs_per_cu<4>(u); break;
                 case 8: per_cu = flat_wgs_per_cu<8>(u); break;
-                default: per_cu = flat_wgs_per_cu<16>(u); break;
+                case 16: per_cu = flat_wgs_per_cu<16>(u); break;
+                default: per_cu = flat_wgs_per_cu<32>(u); break;
                 }
             }
             const int64_t emax = units * D.K;
@@ -832,7 +876,9 @@ AttnPlan plan_attention(const Dims &D) {
                 P.flat_rows = segs + 1;
             }
         }
-    } else {
+        if (D.G == 32 && !P.flat) P = AttnPlan{};  // the generic kernel instead
+    }
+    if (!P.mfma) {
         int bps = 8;
         while (bps > 1 && units * ((D.K + bps - 1) / bps) < 1024) bps /= 2;
         P.blocks_per_wave = bps;
@@ -847,7 +893,7 @@ AttnPlan plan_attention(const Dims &D) {
 int verify_stride(const Dims &D) {
     int v = plan_attention(D).ns1;
     if (!mfma_ok(D)) return v;
-    for (int g : {1, 2, 4, 8, 16}) {
+    for (int g : {1, 2, 4, 8, 16, 32}) {
         Dims Dc = D;
         Dc.G = g;
         Dc.Hq = D.Hkv * g;
@@ -931,12 +977,14 @@ hipError_t launch_attention(const Dims &D, const AttnPlan &P, int mode, int nsf,
         case 2: OASIS_FLAT(2); break;
         case 4: OASIS_FLAT(4); break;
         case 8: OASIS_FLAT(8); break;
-        default: OASIS_FLAT(16); break;
+        case 16: OASIS_FLAT(16); break;
+        default: OASIS_FLAT(32); break;
         }
 #undef OASIS_FLAT
         return hipGetLastError();
     }
     if (P.mfma) {
+        if (D.G > 16) return hipErrorInvalidValue;  // planned on the balanced kernel only
         if (mode == 0) nsf = 0;
         const int n_fetch_wg = nsf > 0 ? fetch_workgroups(D.units() * nsf) : 0;
         dim3 grid((unsigned)(n_fetch_wg + D.units() * P.ns1));
@@ -974,10 +1022,10 @@ hipError_t launch_attention(const Dims &D, const AttnPlan &P, int mode, int nsf,
 hipError_t launch_combine(const Dims &D, const AttnPlan &P, int nsf, const float *part_m,
                           const float *part_l, const float *part_acc, float *out,
                           hipStream_t st) {
-    if (P.flat) {
-        OASIS_LAUNCH(combine_flat_kernel, dim3(D.Hq, D.B), dim3(D.d <= 256 ? D.d : 256), 0, st,
-                     part_m, part_l, part_acc, out, D.Hq, D.Hkv, D.G, D.d, P.nsa, nsf,
-                     P.flat_rows, D.units() * P.nsa);
+    if (P.flat) {  // d = 128
+        OASIS_LAUNCH(combine_flat_kernel, dim3((D.Hq + 3) / 4, D.B), dim3(256), 0, st, part_m,
+                     part_l, part_acc, out, D.Hq, D.Hkv, D.G, P.nsa, nsf, P.flat_rows,
+                     D.units() * P.nsa);
         return hipGetLastError();
     }
     OASIS_LAUNCH(combine_kernel, dim3(D.Hq, D.B), dim3(D.d <= 256 ? D.d : 256), 0, st,

@@ -5,6 +5,8 @@
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
+#include "common.h"
+
 namespace oasis {
 
 // Partials merged per round trip of the combine.
@@ -56,6 +58,63 @@ __device__ __forceinline__ void merge_partials(const float *__restrict__ part_m,
             a += wgt * pa[k];
         }
         M = nm;
+    }
+}
+
+// Partial sums loaded per round trip by merge_row_wave.
+constexpr int kWaveMergeRegs = 16;
+
+// One wave merges the n partials of one output row of 128 dimensions (partial
+// i at row pidx(i); lane l owns dimensions 2 l and 2 l + 1) into a running
+// (M, L, a).  Per group of 64 partials, lane s first reads partial s's m and
+// l (one round trip for all of them); the weights and the normaliser follow
+// by wave reductions, and only the sums of the live partials (m > -inf) are
+// read, kWaveMergeRegs per round trip, as 512-byte rows.  Partials marked
+// empty cost no sum read, which matters where a unit's fixed set of partial
+// rows is mostly unused.
+template <typename F>
+__device__ __forceinline__ void merge_row_wave(const float *__restrict__ part_m,
+                                               const float *__restrict__ part_l,
+                                               const float *__restrict__ part_acc, int n, F pidx,
+                                               float &M, float &L, float2 &a) {
+    const int lane = threadIdx.x & 63;
+    for (int i0 = 0; i0 < n; i0 += 64) {
+        float pm = -INFINITY, pl = 0.f;
+        if (i0 + lane < n) {
+            const int64_t pi = pidx(i0 + lane);
+            pm = part_m[pi];
+            pl = part_l[pi];
+        }
+        uint64_t live = __ballot(pm != -INFINITY);
+        if (live == 0) continue;
+        const float nm = fmaxf(M, wave_max(pm));
+        const float r = exp2f(M - nm);  // 0 while nothing was merged
+        const float w = pm != -INFINITY ? exp2f(pm - nm) : 0.f;
+        // a partial marked empty adds nothing, whatever its l holds
+        L = L * r + wave_sum(pm != -INFINITY ? w * pl : 0.f);
+        a.x *= r;
+        a.y *= r;
+        M = nm;
+        const int s_first = __builtin_ctzll(live);
+        while (live) {
+            // every load issued before any is used; past the last live
+            // partial the first one is read again with weight 0
+            float2 v[kWaveMergeRegs];
+            int wk[kWaveMergeRegs];  // weight bits
+#pragma unroll
+            for (int k = 0; k < kWaveMergeRegs; ++k) {
+                const int s = live ? __builtin_ctzll(live) : s_first;
+                wk[k] = live ? __builtin_amdgcn_readlane(__float_as_int(w), s) : 0;
+                live &= live - 1;
+                v[k] = *reinterpret_cast<const float2 *>(part_acc + pidx(i0 + s) * 128 + 2 * lane);
+            }
+#pragma unroll
+            for (int k = 0; k < kWaveMergeRegs; ++k) {
+                const float wf = __int_as_float(wk[k]);
+                a.x += wf * v[k].x;
+                a.y += wf * v[k].y;
+            }
+        }
     }
 }
 

@@ -159,8 +159,9 @@ hipError_t launch_attention(const Dims &D, const AttnPlan &P, int mode, int nsf,
 // need for every chunk size.
 int verify_stride(const Dims &D);
 // Verification attention (normal and draft query sets together, causal over
-// the draft tokens): rows per unit, and the whole pass (pack, one block
-// attention per chunk of rows, combine).  bf16, d = 128, bs = 16.
+// the draft tokens): query rows per unit padded to whole passes (-1 when they
+// need more than 12 passes), and the whole call (pack, one block attention
+// per chunk of rows, combine).  bf16, d = 128, bs = 16.
 int verify_rows(const Dims &D, int n_drafts);
 hipError_t launch_verify(const Dims &D, const AttnPlan &P, int n_drafts, const void *q,
                          const void *drafts, const void *kd, const void *vd, void *slots,

@@ -38,12 +38,15 @@ def test_tiny_workload_bf16_variant():
     log(f"tiny bf16 d128: {p.run_all()}")
 
 
-@pytest.mark.parametrize("q_heads,kv_heads", [(8, 8), (16, 8), (32, 4), (64, 4)])
+@pytest.mark.parametrize("q_heads,kv_heads", [(8, 8), (16, 8), (32, 4), (64, 4), (32, 1)])
 def test_group_sizes_reduced_context(q_heads, kv_heads):
-    """G = 1, 2, 8, 16 on a reduced context with a ragged prefix."""
+    """G = 1, 2, 8, 16, 32 on a reduced context with a ragged prefix (32
+    heads per KV head: two 16-row tiles on the matrix cores; 2 drafts, so the
+    96 query rows of the score fit the handle's limit)."""
     Parity, log = _parity()
+    extra = {"drafts": 2} if q_heads // kv_heads == 32 else {}
     w = synth.QWEN3_8B.with_(batch=2, q_heads=q_heads, kv_heads=kv_heads,
-                             prefix_tokens=16 * 300 + 7, budget_tokens=16 * 64)
+                             prefix_tokens=16 * 300 + 7, budget_tokens=16 * 64, **extra)
     units = [(0, 0), (1, kv_heads - 1)]
     p = Parity(w, 6, units)
     log(f"G={q_heads // kv_heads}: {p.run_all()}")
@@ -300,12 +303,13 @@ def test_miss_correction_reduced_context():
 
 # ------------------------------------------------------------------ verification attention
 
-@pytest.mark.parametrize("q_heads,n_steps", [(32, 4), (64, 3)])
+@pytest.mark.parametrize("q_heads,n_steps", [(32, 4), (64, 3), (128, 2)])
 def test_verification_attention_against_oracle(q_heads, n_steps):
     """Normal and draft queries together with causal draft tokens ([OASIS]
     Fig. 7 right) after each step of the free-running path: every set of
     sampled units against the oracle over the GPU's attended list; set 0
-    equal to oasis_sparse_attn up to summation order."""
+    equal to oasis_sparse_attn up to summation order.  20 rows per KV head
+    run as one padded 32-row pass, 40 as 32 + 8, 80 as 32 + 32 + 16."""
     from lookahead_sparse_kv_oasis_amd.runner import LayerRunner, to_device
     from tests.gpu_parity import ATTN_TOL, log
     w = synth.QWEN3_8B.with_(batch=3, q_heads=q_heads, prefix_tokens=16 * 300 + 9,
