@@ -122,7 +122,6 @@ struct oasis_handle {
     // [units][S] slots, [units] counts (allocated with the handle)
     int32_t *set_buf = nullptr;
     // verification attention: packed query rows and per-row partials
-    void *vq = nullptr;
     float *vpart_m = nullptr, *vpart_l = nullptr, *vpart_acc = nullptr;
 
     hipStream_t copy = nullptr;
@@ -309,7 +308,6 @@ void free_all(oasis_t *h) {
     (void)hipFree(h->stats);
     (void)hipFree(h->evict_buf);
     (void)hipFree(h->set_buf);
-    (void)hipFree(h->vq);
     (void)hipFree(h->vpart_m);
     (void)hipFree(h->vpart_l);
     (void)hipFree(h->vpart_acc);
@@ -556,8 +554,7 @@ int create_handle(const oasis_layout *layout, int32_t block_size, int32_t budget
     if (ok && h->plan.mfma && vrows > 0) {
         // verification attention scratch, sized for max_drafts
         const size_t rows = (size_t)units * vrows;
-        ok = dmal(&h->vq, rows * 128 * sizeof(uint16_t)) &&
-             dmal((void **)&h->vpart_m, rows * h->plan.vns * sizeof(float)) &&
+        ok = dmal((void **)&h->vpart_m, rows * h->plan.vns * sizeof(float)) &&
              dmal((void **)&h->vpart_l, rows * h->plan.vns * sizeof(float)) &&
              dmal((void **)&h->vpart_acc, rows * h->plan.vns * 128 * sizeof(float));
     }
@@ -978,7 +975,7 @@ extern "C" int oasis_sparse_attn_verify(oasis_t *h, const void *q_dev, const voi
         return fail(h, OASIS_E_INVAL, "verify: null or misaligned drafts or draft K/V");
     if (!h->plan.mfma)
         return fail(h, OASIS_E_INVAL, "verify: needs the bf16, d = 128, block 16 layout");
-    if (!h->vq || verify_rows(h->D, n_drafts) < 0)
+    if (!h->vpart_m || verify_rows(h->D, n_drafts) < 0)
         return fail(h, OASIS_E_INVAL, "verify: %d query rows per KV head exceed the verify passes",
                     h->D.G * (1 + n_drafts));
     if (!h->selected) return fail(h, OASIS_E_STATE, "verify attention before select");
@@ -993,7 +990,7 @@ extern "C" int oasis_sparse_attn_verify(oasis_t *h, const void *q_dev, const voi
     TRY(flush_fetch(h, stream));  // every attended block resident before the passes
     // several launches: not a class of the per-kernel timers
     HIP_OK(h, launch_verify(D, h->plan, n_drafts, q_dev, drafts_dev, k_drafts_dev, v_drafts_dev,
-                            h->slots, h->att_block, h->att_slot, h->counts, h->T, h->vq,
+                            h->slots, h->att_block, h->att_slot, h->counts, h->T,
                             h->vpart_m, h->vpart_l, h->vpart_acc, out_dev, stream));
     TRY(mark(h, h->m_attn, stream));
     return OASIS_OK;

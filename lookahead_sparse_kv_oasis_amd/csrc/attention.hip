@@ -97,6 +97,15 @@ template <int g> __device__ __forceinline__ float row_bcast(float x) {
                                            false));
 }
 
+// Row r of a pass over unit (b, h): its query row r0 + r (r0 past `real`),
+// query row j G + g = head h G + g of set j.
+__device__ __forceinline__ const uint16_t *query_row(const QRows &qr, int64_t b, int h, int r) {
+    const int R = qr.r0 + (r < qr.real ? r : 0);
+    const int j = R / qr.G, g = R - j * qr.G;
+    const uint16_t *base = j == 0 ? qr.q : qr.drafts + (int64_t)(j - 1) * qr.set_stride;
+    return base + (b * qr.Hq + (int64_t)h * qr.G + g) * 128;
+}
+
 // Per 16-token block of one unit, in one wave:
 //   S^T = K . Q^T on v_mfma_f32_16x16x32_bf16 (tokens are the M rows, the G
 //   heads of the group the N columns, zero-padded to 16).  Lane l supplies
@@ -125,18 +134,19 @@ template <int G> struct AttnWave {
         koff = col * D + 8 * kg;
         voff = BS * D + 4 * kg * D + 8 * col;
     }
+    int nreal = G;  // rows whose partials are written
     // Queries of unit (b, h) and a cleared softmax state.
-    __device__ __forceinline__ void init(const uint16_t *q, int64_t b, int Hq, int h) {
-        load_q(qb, q, b, Hq, h);
+    __device__ __forceinline__ void init(const QRows &qr, int64_t b, int h) {
+        load_q(qb, qr, b, h);
         reset();
     }
-    // The query rows of unit (b, h) in the B-operand order (heads past G zero).
-    __device__ __forceinline__ void load_q(bf16x8 (&dst)[4], const uint16_t *q, int64_t b, int Hq,
+    // The query rows of unit (b, h) in the B-operand order (rows past G zero).
+    __device__ __forceinline__ void load_q(bf16x8 (&dst)[4], const QRows &qr, int64_t b,
                                            int h) const {
-        const uint16_t *qr = q + (b * Hq + h * G + (col < G ? col : 0)) * D + 8 * kg;
+        const uint16_t *qp = query_row(qr, b, h, col < G ? col : 0) + 8 * kg;
 #pragma unroll
         for (int i = 0; i < 4; ++i) {
-            uint4 w = *reinterpret_cast<const uint4 *>(qr + 32 * i);
+            uint4 w = *reinterpret_cast<const uint4 *>(qp + 32 * i);
             if (col >= G) w = make_uint4(0, 0, 0, 0);
             dst[i] = __builtin_bit_cast(bf16x8, w);
         }
@@ -236,11 +246,12 @@ template <int G> struct AttnWave {
         if (kg == 0) {
 #pragma unroll
             for (int g = 0; g < G; ++g) {
+                if (g >= nreal) break;
                 float4 *dst = reinterpret_cast<float4 *>(part_acc + (pi0 + g) * D + 8 * col);
                 dst[0] = make_float4(acc[g][0], acc[g][1], acc[g][2], acc[g][3]);
                 dst[1] = make_float4(acc[g][4], acc[g][5], acc[g][6], acc[g][7]);
             }
-            if (col < G) {
+            if (col < nreal) {
                 part_m[pi0 + col] = m;
                 part_l[pi0 + col] = lsum;
             }
@@ -290,19 +301,20 @@ template <int G> struct AttnWaveM {
         koff = col * D + 8 * kg;
         voff = BS * D + 4 * kg * D + 8 * col;
     }
-    __device__ __forceinline__ void init(const uint16_t *q, int64_t b, int Hq, int h) {
-        load_q(qb, q, b, Hq, h);
+    int nreal = G;  // rows whose partials are written
+    __device__ __forceinline__ void init(const QRows &qr, int64_t b, int h) {
+        load_q(qb, qr, b, h);
         reset();
     }
-    __device__ __forceinline__ void load_q(bf16x8 (&dst)[4 * NT], const uint16_t *q, int64_t b,
-                                           int Hq, int h) const {
+    __device__ __forceinline__ void load_q(bf16x8 (&dst)[4 * NT], const QRows &qr, int64_t b,
+                                           int h) const {
 #pragma unroll
         for (int t = 0; t < NT; ++t) {
-            const uint16_t *qr = q + (b * Hq + h * G + 16 * t + col) * D + 8 * kg;
+            const uint16_t *qp = query_row(qr, b, h, 16 * t + col) + 8 * kg;
 #pragma unroll
             for (int i = 0; i < 4; ++i)
                 dst[4 * t + i] =
-                    __builtin_bit_cast(bf16x8, *reinterpret_cast<const uint4 *>(qr + 32 * i));
+                    __builtin_bit_cast(bf16x8, *reinterpret_cast<const uint4 *>(qp + 32 * i));
         }
     }
     __device__ __forceinline__ void reset() {
@@ -409,12 +421,15 @@ template <int G> struct AttnWaveM {
                                                   float *part_acc) const {
 #pragma unroll
         for (int t = 0; t < NT; ++t) {
+            if (16 * t >= nreal) break;
 #pragma unroll
-            for (int n = 0; n < 8; ++n)
+            for (int r = 0; r < 4; ++r) {
+                if (16 * t + 4 * kg + r >= nreal) continue;
 #pragma unroll
-                for (int r = 0; r < 4; ++r)
+                for (int n = 0; n < 8; ++n)
                     part_acc[(pi0 + 16 * t + 4 * kg + r) * D + 16 * n + col] = o[t][n][r];
-            if (kg == 0) {
+            }
+            if (kg == 0 && 16 * t + col < nreal) {
                 part_m[pi0 + 16 * t + col] = m[t];
                 part_l[pi0 + 16 * t + col] = lsum[t];
             }
@@ -456,7 +471,7 @@ __device__ __forceinline__ int block_valid(int64_t T, int32_t blk) {
 // saturated while holding only a small share of the CU slots.
 template <int G, typename W>
 __device__ __forceinline__ void fetch_waves(
-    W &st, int wave, const uint16_t *__restrict__ q, uint16_t *__restrict__ slots,
+    W &st, int wave, const QRows &qr, uint16_t *__restrict__ slots,
     const uint16_t *__restrict__ host_kv, const int32_t *__restrict__ att_block,
     const int32_t *__restrict__ att_slot, const int32_t *__restrict__ counts, int64_t T_, int Hq,
     int Hkv, int K, int S, int64_t NBmax, int cap, int n_fetch_wg, int nsa, int64_t units,
@@ -502,7 +517,7 @@ __device__ __forceinline__ void fetch_waves(
             const int l = __builtin_ctzll(m);
             const int ul = rl(u, l);
             uint4 kk[4], vv[4];
-            st.load_q(st.qb, q, ul / Hkv, Hq, ul % Hkv);
+            st.load_q(st.qb, qr, ul / Hkv, ul % Hkv);
             st.load(kk, vv, src(l));
             st.reset();
             st.block(kk, vv, block_valid(T_, rl(blk, l)), scale_log2);
@@ -528,8 +543,7 @@ __device__ __forceinline__ void fetch_waves(
 //     in LDS into partial nsf_max + s.
 template <int G, int BPW>
 __global__ __launch_bounds__(256) void attn_mfma_kernel(
-    const uint16_t *__restrict__ q, uint16_t *__restrict__ slots,
-    const uint16_t *__restrict__ host_kv, const int32_t *__restrict__ att_block,
+    const QRows qr, uint16_t *__restrict__ slots, const uint16_t *__restrict__ host_kv, const int32_t *__restrict__ att_block,
     const int32_t *__restrict__ att_slot, const int32_t *__restrict__ counts, int64_t T_, int Hq,
     int Hkv, int K, int S, int64_t NBmax, int mode, int cap, int n_fetch_wg, int nsf_max,
     int ns1, int nsa, int64_t units, float scale_log2, float *__restrict__ part_m,
@@ -543,9 +557,10 @@ __global__ __launch_bounds__(256) void attn_mfma_kernel(
     W st;
     st.lanes();
     st.vst = vstage[wave];
+    st.nreal = qr.real;
 
     if ((int64_t)blockIdx.x < n_fetch_wg) {
-        fetch_waves<G>(st, wave, q, slots, host_kv, att_block, att_slot, counts, T_, Hq, Hkv, K,
+        fetch_waves<G>(st, wave, qr, slots, host_kv, att_block, att_slot, counts, T_, Hq, Hkv, K,
                        S, NBmax, cap, n_fetch_wg, nsa, units, scale_log2, part_m, part_l,
                        part_acc);
         return;
@@ -559,7 +574,7 @@ __global__ __launch_bounds__(256) void attn_mfma_kernel(
     const int e_end = __builtin_amdgcn_readfirstlane(
         mode == 1 ? counts[u * 4 + 0] - counts[u * 4 + 2] : counts[u * 4 + 0]);
     const int e_first = 4 * BPW * s + wave;
-    st.init(q, u / Hkv, Hq, (int)(u % Hkv));
+    st.init(qr, u / Hkv, (int)(u % Hkv));
     const int ne = e_first >= e_end ? 0 : (e_end - e_first + 3) / 4 < BPW ? (e_end - e_first + 3) / 4 : BPW;
 
     uint4 kr[2][4], vr[2][4];
@@ -588,7 +603,7 @@ __global__ __launch_bounds__(256) void attn_mfma_kernel(
     __syncthreads();
 
     // merge the four waves into this workgroup's partial
-    for (int idx = threadIdx.x; idx < G * D; idx += 256) {
+    for (int idx = threadIdx.x; idx < qr.real * D; idx += 256) {
         const int gg = idx / D, c = idx % D;
         float M = -INFINITY;
 #pragma unroll
@@ -666,8 +681,7 @@ __device__ __forceinline__ void hit_prefix(const int32_t *__restrict__ counts, i
 // Dynamic LDS: units + 1 ints.
 template <int G>
 __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2))) void attn_flat_kernel(
-    const uint16_t *__restrict__ q, uint16_t *__restrict__ slots,
-    const uint16_t *__restrict__ host_kv, const int32_t *__restrict__ att_block,
+    const QRows qr, uint16_t *__restrict__ slots, const uint16_t *__restrict__ host_kv, const int32_t *__restrict__ att_block,
     const int32_t *__restrict__ att_slot, const int32_t *__restrict__ counts, int64_t T_, int Hq,
     int Hkv, int K, int S, int64_t NBmax, int mode, int cap, int n_fetch_wg, int nsa, int units,
     int W, int R, int pmin, float scale_log2, float *__restrict__ part_m,
@@ -681,8 +695,9 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2))) void a
     Wv st;
     st.lanes();
     st.vst = vstage[wave];
+    st.nreal = qr.real;
     if ((int)blockIdx.x < n_fetch_wg) {
-        fetch_waves<G>(st, wave, q, slots, host_kv, att_block, att_slot, counts, T_, Hq, Hkv, K,
+        fetch_waves<G>(st, wave, qr, slots, host_kv, att_block, att_slot, counts, T_, Hq, Hkv, K,
                        S, NBmax, cap, n_fetch_wg, nsa, (int64_t)units, scale_log2, part_m,
                        part_l, part_acc);
         return;
@@ -734,7 +749,7 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2))) void a
         const int u = rl(my_u, j);
         if (u != cur_u) {
             if (cur_u >= 0) finish(cur_u);
-            st.load_q(st.qb, q, u / Hkv, Hq, u % Hkv);  // waited for with the block
+            st.load_q(st.qb, qr, u / Hkv, u % Hkv);  // waited for with the block
             st.reset();
             cur_u = u;
         }
@@ -927,7 +942,7 @@ static int fetch_workgroups(int64_t items) {
 }
 
 template <int G>
-static void launch_mfma_g(const AttnPlan &P, dim3 grid, hipStream_t st, const uint16_t *q,
+static void launch_mfma_g(const AttnPlan &P, dim3 grid, hipStream_t st, const QRows &q,
                           uint16_t *slots, const uint16_t *host_kv, const int32_t *ab,
                           const int32_t *as, const int32_t *counts, int64_t T, const Dims &D,
                           int mode, int cap, int n_fetch_wg, float sc, float *pm, float *pl,
@@ -947,7 +962,7 @@ static void launch_mfma_g(const AttnPlan &P, dim3 grid, hipStream_t st, const ui
 
 template <int G>
 static void launch_flat_g(const AttnPlan &P, dim3 grid, size_t lds, hipStream_t st,
-                          const uint16_t *q, uint16_t *slots, const uint16_t *host_kv,
+                          const QRows &q, uint16_t *slots, const uint16_t *host_kv,
                           const int32_t *ab, const int32_t *as, const int32_t *counts, int64_t T,
                           const Dims &D, int mode, int cap, int n_fetch_wg, float sc, float *pm,
                           float *pl, float *pa) {
@@ -960,14 +975,16 @@ static void launch_flat_g(const AttnPlan &P, dim3 grid, size_t lds, hipStream_t 
 hipError_t launch_attention(const Dims &D, const AttnPlan &P, int mode, int nsf, const void *q,
                             void *slots, const void *host_kv, const int32_t *att_block,
                             const int32_t *att_slot, const int32_t *counts, int64_t T,
-                            float *part_m, float *part_l, float *part_acc, hipStream_t st) {
+                            float *part_m, float *part_l, float *part_acc, hipStream_t st,
+                            const QRows *qrows) {
     const float sc = kLog2e / sqrtf((float)D.d);
+    const QRows qq = qrows ? *qrows : QRows{(const uint16_t *)q, nullptr, 0, D.Hq, D.G, 0, D.G};
     if (P.mfma && P.flat) {
         if (mode == 0) nsf = 0;
         const int n_fetch_wg = nsf > 0 ? fetch_workgroups(D.units() * nsf) : 0;
         const dim3 grid((unsigned)(n_fetch_wg + P.flat_waves / 4));
         const size_t lds = sizeof(int32_t) * (D.units() + 1);
-        const uint16_t *qq = (const uint16_t *)q, *hk = (const uint16_t *)host_kv;
+        const uint16_t *hk = (const uint16_t *)host_kv;
         uint16_t *sl = (uint16_t *)slots;
 #define OASIS_FLAT(GG)                                                                          \
     launch_flat_g<GG>(P, grid, lds, st, qq, sl, hk, att_block, att_slot, counts, T, D, mode, nsf, \
@@ -988,7 +1005,7 @@ hipError_t launch_attention(const Dims &D, const AttnPlan &P, int mode, int nsf,
         if (mode == 0) nsf = 0;
         const int n_fetch_wg = nsf > 0 ? fetch_workgroups(D.units() * nsf) : 0;
         dim3 grid((unsigned)(n_fetch_wg + D.units() * P.ns1));
-        const uint16_t *qq = (const uint16_t *)q, *hk = (const uint16_t *)host_kv;
+        const uint16_t *hk = (const uint16_t *)host_kv;
         uint16_t *sl = (uint16_t *)slots;
         switch (D.G) {
         case 1: launch_mfma_g<1>(P, grid, st, qq, sl, hk, att_block, att_slot, counts, T, D, mode, nsf, n_fetch_wg, sc, part_m, part_l, part_acc); break;

@@ -127,7 +127,7 @@ hipError_t launch_rebuild_block_slot(const Dims &D, const int32_t *slot_block,
 // unit are indexed [0, nsa): fetch splits at [0, nsf), hit splits at
 // [nsf_max, nsf_max + ns1).
 struct AttnPlan {
-    bool mfma;             // bf16, d = 128, block 16, G in {1, 2, 4, 8, 16}
+    bool mfma;             // bf16, d = 128, block 16, G in {1, 2, 4, 8, 16}, or 32 when flat
     int blocks_per_wave;   // hit entries per wave (MFMA: 4 waves per split)
     int ns1;               // hit splits per unit (split kernel; verification attention)
     int nsf_max;           // fetch splits per unit at cap = K (MFMA only)
@@ -147,27 +147,41 @@ AttnPlan plan_attention(const Dims &D);
 int64_t attn_partial_rows(const Dims &D, const AttnPlan &P);
 // Fetch splits for a cap (fused mode), 0 when the kernel cannot fuse.
 int attention_fetch_splits(const Dims &D, const AttnPlan &P, int cap);
+// Where the matrix-core attention kernels take the query rows of a unit.
+// Row r of a pass over G_pass rows is the unit's query row r0 + r (r0 again
+// for r >= real, whose partials are not written); query row j G + g of unit
+// (b, h) is head h G + g of query set j: q [B][Hq][d] for j = 0, drafts set
+// j - 1 ([n][B][Hq][d], set_stride elements apart) for j >= 1.  The decode
+// attention's rows are {q, -, -, Hq, G, 0, G}.
+struct QRows {
+    const uint16_t *q, *drafts;
+    int64_t set_stride;
+    int Hq, G;
+    int r0, real;
+};
 // mode 0: every attended entry from its slot.  mode 1 (MFMA only): entries
 // [n_hit, n_att) are read from the host KV and written into their slots in
 // the same kernel, using nsf fetch splits.  launch_combine merges the
-// partials into the output.
+// partials into the output.  qr (MFMA only; null: the rows of q) gives the
+// query rows of a verification pass.
 hipError_t launch_attention(const Dims &D, const AttnPlan &P, int mode, int nsf, const void *q,
                             void *slots, const void *host_kv, const int32_t *att_block,
                             const int32_t *att_slot, const int32_t *counts, int64_t T,
-                            float *part_m, float *part_l, float *part_acc, hipStream_t st);
+                            float *part_m, float *part_l, float *part_acc, hipStream_t st,
+                            const QRows *qr = nullptr);
 // Partial rows per (unit, query row) the verification attention's buffers
 // need for every chunk size.
 int verify_stride(const Dims &D);
 // Verification attention (normal and draft query sets together, causal over
 // the draft tokens): query rows per unit padded to whole passes (-1 when they
-// need more than 12 passes), and the whole call (pack, one block attention
-// per chunk of rows, combine).  bf16, d = 128, bs = 16.
+// need more than 12 passes), and the whole call (one block attention per
+// chunk of rows, combine).  bf16, d = 128, bs = 16.
 int verify_rows(const Dims &D, int n_drafts);
 hipError_t launch_verify(const Dims &D, const AttnPlan &P, int n_drafts, const void *q,
                          const void *drafts, const void *kd, const void *vd, void *slots,
                          const int32_t *att_block, const int32_t *att_slot,
-                         const int32_t *counts, int64_t T, void *qpack, float *vpart_m,
-                         float *vpart_l, float *vpart_acc, float *out, hipStream_t st);
+                         const int32_t *counts, int64_t T, float *vpart_m, float *vpart_l,
+                         float *vpart_acc, float *out, hipStream_t st);
 
 hipError_t launch_combine(const Dims &D, const AttnPlan &P, int nsf, const float *part_m,
                           const float *part_l, const float *part_acc, float *out,

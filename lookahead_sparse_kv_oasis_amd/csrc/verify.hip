@@ -18,11 +18,12 @@ constexpr float kLog2eV = 1.4426950408889634f;
 // blocks and, causally, over draft tokens 1..j.  The M = G (1 + D) rows of a
 // unit are cut into chunks of 32 rows while 32 or more remain, then one chunk
 // of the next power of two at or above the rest (its extra rows repeat the
-// chunk's first row and are never combined).  Each chunk is one pass of the
-// block attention kernel with G = chunk rows: one pass reads the attended KV
-// once for all of its rows, so the Qwen3-8B layer's 20 rows per KV head
-// (4 heads x 5 query sets) take a single 32-row pass on the matrix cores.
-// The combine below merges a row's partials with its draft tokens.
+// chunk's first row; their partials are not written).  Each chunk is one
+// pass of the block attention kernel with G = chunk rows, reading its query
+// rows in place from q and the drafts: one pass reads the attended KV once for
+// all of its rows, so the Qwen3-8B layer's 20 rows per KV head (4 heads x 5
+// query sets) take a single 32-row pass on the matrix cores.  The combine
+// below merges a row's partials with its draft tokens.
 constexpr int kMaxChunks = 12;
 constexpr int kChunkRows = 32;
 
@@ -31,7 +32,7 @@ struct VerifyChunks {
     int r0[kMaxChunks];    // first query row of chunk k
     int real[kMaxChunks];  // query rows of chunk k
     int rows[kMaxChunks];  // rows of its pass: real rows and padding
-    int p0[kMaxChunks];    // first padded row of chunk k
+    int p0[kMaxChunks];    // first padded row of chunk k (its partials' offset)
     int ns[kMaxChunks];    // partial rows per (unit, row) of the chunk's pass
 };
 
@@ -59,37 +60,10 @@ static bool verify_chunks(int M, int wmax, VerifyChunks &c) {
     return true;
 }
 
-__device__ __forceinline__ int chunk_of_padded(const VerifyChunks &c, int p) {
-    int k = 0;
-    while (k + 1 < c.n && c.p0[k + 1] <= p) ++k;
-    return k;
-}
-
 __device__ __forceinline__ int chunk_of_row(const VerifyChunks &c, int r) {
     int k = 0;
     while (k + 1 < c.n && c.r0[k + 1] <= r) ++k;
     return k;
-}
-
-// Padded row p of unit u -> the buffer [units][rows][D] of its chunk.
-__global__ __launch_bounds__(64) void verify_pack_kernel(const uint16_t *__restrict__ q,
-                                                         const uint16_t *__restrict__ drafts,
-                                                         uint16_t *__restrict__ qpack, int B,
-                                                         int Hq, int Hkv, int G,
-                                                         VerifyChunks ch, int64_t units) {
-    constexpr int D = 128;
-    const int p = blockIdx.x;
-    const int64_t u = blockIdx.y;
-    const int b = (int)(u / Hkv), h = (int)(u % Hkv);
-    const int k = chunk_of_padded(ch, p);
-    const int rr = p - ch.p0[k];
-    const int r = ch.r0[k] + (rr < ch.real[k] ? rr : 0);  // padding repeats a real row
-    const int j = r / G, g = r % G;
-    const uint16_t *src = j == 0 ? q + ((int64_t)b * Hq + h * G + g) * D
-                                 : drafts + (((int64_t)(j - 1) * B + b) * Hq + h * G + g) * D;
-    uint16_t *dst = qpack + units * ch.p0[k] * D + (u * ch.rows[k] + rr) * D;
-    const int c = threadIdx.x * 8;
-    if (c < D) gstore16(dst + c, gload16(src + c));
 }
 
 constexpr int kDraftBatch = 8;  // draft tokens whose loads go out together
@@ -169,8 +143,8 @@ int verify_rows(const Dims &D, int n_drafts) {
 hipError_t launch_verify(const Dims &D, const AttnPlan &P, int n_drafts, const void *q,
                          const void *drafts, const void *kd, const void *vd, void *slots,
                          const int32_t *att_block, const int32_t *att_slot,
-                         const int32_t *counts, int64_t T, void *qpack, float *vpart_m,
-                         float *vpart_l, float *vpart_acc, float *out, hipStream_t st) {
+                         const int32_t *counts, int64_t T, float *vpart_m, float *vpart_l,
+                         float *vpart_acc, float *out, hipStream_t st) {
     const int M = D.G * (1 + n_drafts);
     // 32-row passes need the balanced kernel (the split kernel serves up to
     // 16 rows); its partial rows per unit must fit the stride P.vns
@@ -181,7 +155,6 @@ hipError_t launch_verify(const Dims &D, const AttnPlan &P, int n_drafts, const v
     const int wmax = P32.flat && P32.flat_rows <= P.vns ? kChunkRows : 16;
     VerifyChunks ch;
     if (!verify_chunks(M, wmax, ch)) return hipErrorInvalidValue;
-    const int Mp = ch.p0[ch.n - 1] + ch.rows[ch.n - 1];
     const int64_t units = D.units();
     // one pass per chunk over the attended blocks, each with the plan of its
     // row count: the balanced kernel where it applies (its partial rows per
@@ -198,11 +171,6 @@ hipError_t launch_verify(const Dims &D, const AttnPlan &P, int n_drafts, const v
         Pk[k].nsa = Pk[k].flat ? 0 : Pk[k].ns1;
         ch.ns[k] = Pk[k].flat ? Pk[k].flat_rows : Pk[k].ns1;
     }
-    OASIS_LAUNCH(verify_pack_kernel, dim3((unsigned)Mp, (unsigned)units), dim3(64), 0, st,
-                 (const uint16_t *)q, (const uint16_t *)drafts, (uint16_t *)qpack, D.B, D.Hq,
-                 D.Hkv, D.G, ch, units);
-    hipError_t e = hipGetLastError();
-    if (e != hipSuccess) return e;
     // every attended block from its slot; chunk k's partials start at row
     // units p0 vns
     for (int k = 0; k < ch.n; ++k) {
@@ -210,9 +178,12 @@ hipError_t launch_verify(const Dims &D, const AttnPlan &P, int n_drafts, const v
         Dc.G = ch.rows[k];
         Dc.Hq = D.Hkv * ch.rows[k];
         const int64_t rows0 = units * (int64_t)ch.p0[k];
-        e = launch_attention(Dc, Pk[k], 0, 0, (const uint16_t *)qpack + rows0 * 128, slots,
-                             nullptr, att_block, att_slot, counts, T, vpart_m + rows0 * P.vns,
-                             vpart_l + rows0 * P.vns, vpart_acc + rows0 * P.vns * 128, st);
+        const QRows qr{(const uint16_t *)q, (const uint16_t *)drafts, (int64_t)D.B * D.Hq * 128,
+                       D.Hq, D.G, ch.r0[k], ch.real[k]};
+        const hipError_t e =
+            launch_attention(Dc, Pk[k], 0, 0, q, slots, nullptr, att_block, att_slot, counts, T,
+                             vpart_m + rows0 * P.vns, vpart_l + rows0 * P.vns,
+                             vpart_acc + rows0 * P.vns * 128, st, &qr);
         if (e != hipSuccess) return e;
     }
     const float scale_log2 = kLog2eV / sqrtf(128.f);
