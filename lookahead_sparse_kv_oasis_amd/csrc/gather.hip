@@ -9,28 +9,52 @@
 // needed, and it runs on its own stream.
 //
 // A few waves stream the whole list: wave w copies items w, w + W, ... of the
-// units x max_n (unit, i) pairs (item i of a unit exists when i < its count).
-// A wave reads the list entries of up to 64 of its items at once, one per
-// lane.  8 KB blocks (8 16-byte loads per lane) are then copied with the next
-// block's host loads issued before the current one is stored; those loads go
-// out unconditionally (after the last block, a discarded read of slot 0) and
-// the loop's one branch is its exit after the stores: with a load under a
-// branch, or a list entry read between blocks, the compiler's wait before each
-// store covered the block in flight as well, and the copy ran one block per
-// host round trip.  Blocks of any other size are copied one at a time.  Host
-// reads by shader loads run best with about 64 waves in flight (about
-// 55 GB/s alone); one workgroup per block (thousands of waves) lowers the
-// link rate and takes CU slots from the kernels running beside the copy.
+// units x max_n (unit, i) pairs (item i of a unit exists when i < its count),
+// in chunks of 8 16-byte loads per lane (8 KB).  A wave keeps two chunks in
+// flight: the next chunk's list entries are read (scalar loads) and its host
+// loads issued before the current chunk is stored, so neither the list reads
+// nor the slot stores leave the host link idle.  Host reads by shader loads
+// run best with about 64 waves in flight (about 55 GB/s alone); one workgroup
+// per block (thousands of waves) lowers the link rate and takes CU slots from
+// the kernels running beside the copy.  A variant reading the list entries of
+// 64 items at once (one per lane) and keeping the next block's loads in
+// flight without branches copied no faster alone and made the 36-layer
+// lookahead step slower (10.5 -> 11.8 ms): its copies pressed harder on the
+// HBM-bound kernels running beside them.
 #include "kernels.h"
 
 namespace oasis {
 
-// Lane l's 64-bit value, read by the whole wave.
-__device__ __forceinline__ int64_t lane_i64(int64_t v, int l) {
-    const uint32_t lo = (uint32_t)__builtin_amdgcn_readlane((int)(uint32_t)v, l);
-    const uint32_t hi = (uint32_t)__builtin_amdgcn_readlane((int)(uint32_t)((uint64_t)v >> 32), l);
-    return (int64_t)(((uint64_t)hi << 32) | lo);
+namespace {
+
+constexpr int kChunk = 64 * 8;  // 16-byte vectors per wave chunk
+
+struct GatherCursor {
+    const u32x4 *src;
+    u32x4 *dst;
+    int64_t item;
+    int c0;
+};
+
+__device__ __forceinline__ void load_chunk(u32x4 (&r)[8], const GatherCursor &g, int block_vec,
+                                           int lane) {
+#pragma unroll
+    for (int k = 0; k < 8; ++k) {
+        const int c = g.c0 + k * 64 + lane;
+        if (c < block_vec) r[k] = __builtin_nontemporal_load(g.src + c);
+    }
 }
+
+__device__ __forceinline__ void store_chunk(const u32x4 (&r)[8], const GatherCursor &g,
+                                            int block_vec, int lane) {
+#pragma unroll
+    for (int k = 0; k < 8; ++k) {
+        const int c = g.c0 + k * 64 + lane;
+        if (c < block_vec) g.dst[c] = r[k];
+    }
+}
+
+}  // namespace
 
 __global__ __launch_bounds__(256) void gather_kernel(const u32x4 *__restrict__ host_kv,
                                                      u32x4 *__restrict__ slots,
@@ -45,73 +69,51 @@ __global__ __launch_bounds__(256) void gather_kernel(const u32x4 *__restrict__ h
     const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
     const int64_t W = (int64_t)gridDim.x * 4;
     const int64_t n_items = units * max_n;
-    const int64_t it0 = (int64_t)blockIdx.x * 4 + wave;
-    if (it0 >= n_items) return;
-    const int64_t n_my = (n_items - it0 + W - 1) / W;  // this wave's items
-    for (int64_t c0 = 0; c0 < n_my; c0 += 64) {
-        // lane l: item it0 + (c0 + l) W, its source and destination blocks
-        const int64_t item = it0 + (c0 + lane) * W;
-        bool ok = false;
-        int64_t src = 0, dst = 0;
-        if (c0 + lane < n_my) {
+    // The first existing item at or after `item` (stride W): fills g and
+    // returns true, or returns false when the list is exhausted.
+    auto seek = [&](int64_t item, GatherCursor &g) -> bool {
+        for (; item < n_items; item += W) {
             const int64_t u = item / max_n;
             const int i = (int)(item % max_n);
-            if (i < counts[u * count_stride + count_index]) {
-                src = (u * NBmax + blocks[u * list_stride + i]) * (int64_t)block_vec;
-                dst = (u * S + slot_ids[u * list_stride + i]) * (int64_t)block_vec;
-                ok = true;
-            }
+            const int n = __builtin_amdgcn_readfirstlane(counts[u * count_stride + count_index]);
+            if (i >= n) continue;
+            const int32_t blk = __builtin_amdgcn_readfirstlane(blocks[u * list_stride + i]);
+            const int32_t s = __builtin_amdgcn_readfirstlane(slot_ids[u * list_stride + i]);
+            g.src = host_kv + (u * NBmax + blk) * (int64_t)block_vec;
+            g.dst = slots + (u * S + s) * (int64_t)block_vec;
+            g.item = item;
+            g.c0 = 0;
+            return true;
         }
-        const uint64_t mask = __ballot(ok);
-        if (mask == 0) continue;
-        if (block_vec == 512) {
-            // 8 KB blocks (16 tokens x 128 dims of bf16 K and V): the
-            // pipelined copy, 8 vectors per lane; the discarded read stays
-            // inside slot 0, which is a whole block
-            int l_cur = __builtin_ctzll(mask);
-            uint64_t rest = mask & (mask - 1);  // set lanes after the current one
-            u32x4 ra[8], rb[8];
-            {
-                const u32x4 *sp = host_kv + lane_i64(src, l_cur);
-#pragma unroll
-                for (int k = 0; k < 8; ++k) ra[k] = __builtin_nontemporal_load(sp + k * 64 + lane);
-            }
-            for (;;) {
-                // the current item is in ra; issue the next (or a discarded read)
-                bool more = rest != 0;
-                int l_nx = __builtin_ctzll(rest | (1ull << 63));
-                const u32x4 *sp = more ? host_kv + lane_i64(src, l_nx) : (const u32x4 *)slots;
-#pragma unroll
-                for (int k = 0; k < 8; ++k) rb[k] = __builtin_nontemporal_load(sp + k * 64 + lane);
-                __builtin_amdgcn_sched_barrier(0);  // the next item's loads go out first
-                u32x4 *dp = slots + lane_i64(dst, l_cur);
-#pragma unroll
-                for (int k = 0; k < 8; ++k) dp[k * 64 + lane] = ra[k];
-                if (!more) break;
-                l_cur = l_nx;
-                rest &= rest - 1;
-                more = rest != 0;
-                l_nx = __builtin_ctzll(rest | (1ull << 63));
-                sp = more ? host_kv + lane_i64(src, l_nx) : (const u32x4 *)slots;
-#pragma unroll
-                for (int k = 0; k < 8; ++k) ra[k] = __builtin_nontemporal_load(sp + k * 64 + lane);
-                __builtin_amdgcn_sched_barrier(0);
-                dp = slots + lane_i64(dst, l_cur);
-#pragma unroll
-                for (int k = 0; k < 8; ++k) dp[k * 64 + lane] = rb[k];
-                if (!more) break;
-                l_cur = l_nx;
-                rest &= rest - 1;
-            }
-        } else {
-            // other block sizes: one block at a time, every vector guarded
-            for (uint64_t m = mask; m; m &= m - 1) {
-                const int l = __builtin_ctzll(m);
-                const u32x4 *sp = host_kv + lane_i64(src, l);
-                u32x4 *dp = slots + lane_i64(dst, l);
-                for (int c = lane; c < block_vec; c += 64) dp[c] = __builtin_nontemporal_load(sp + c);
-            }
+        return false;
+    };
+    // The chunk after g: the next chunk of the same block, else the next item.
+    auto advance = [&](const GatherCursor &g, GatherCursor &nx) -> bool {
+        if (g.c0 + kChunk < block_vec) {
+            nx = g;
+            nx.c0 = g.c0 + kChunk;
+            return true;
         }
+        return seek(g.item + W, nx);
+    };
+    GatherCursor cur, nx;
+    if (!seek((int64_t)blockIdx.x * 4 + wave, cur)) return;
+    u32x4 ra[8], rb[8];
+    load_chunk(ra, cur, block_vec, lane);
+    // two register buffers in turn, so a chunk in flight is never copied
+    for (;;) {
+        bool more = advance(cur, nx);
+        if (more) load_chunk(rb, nx, block_vec, lane);
+        __builtin_amdgcn_sched_barrier(0);  // the next chunk's loads go out first
+        store_chunk(ra, cur, block_vec, lane);
+        if (!more) break;
+        cur = nx;
+        more = advance(cur, nx);
+        if (more) load_chunk(ra, nx, block_vec, lane);
+        __builtin_amdgcn_sched_barrier(0);
+        store_chunk(rb, cur, block_vec, lane);
+        if (!more) break;
+        cur = nx;
     }
 }
 
