@@ -795,13 +795,13 @@ __global__ __launch_bounds__(256) void combine_kernel(const float *__restrict__ 
 
 // The same after the balanced hit path, d = 128: the unit's n_f fetch
 // partials (splits [0, n_f) of nsa), then its R hit partial rows
-// hp0 + u R + s, the unused ones marked empty.  One wave per output row (four
+// hp0 + u R + s, the unused ones marked empty; gt query rows per partial.  One wave per output row (four
 // per workgroup), merging with merge_row_wave: the m and l of every partial
 // in one round trip, then the sums of the live ones only.
 __global__ __launch_bounds__(256) void combine_flat_kernel(
     const float *__restrict__ part_m, const float *__restrict__ part_l,
     const float *__restrict__ part_acc, float *__restrict__ out, int Hq, int Hkv, int G,
-    int nsa, int n_f, int R, int64_t hp0) {
+    int gt, int nsa, int n_f, int R, int64_t hp0) {
     const int qh = __builtin_amdgcn_readfirstlane((int)blockIdx.x * 4 + (int)(threadIdx.x >> 6));
     const int b = blockIdx.y;
     if (qh >= Hq) return;
@@ -810,8 +810,8 @@ __global__ __launch_bounds__(256) void combine_flat_kernel(
     float M = -INFINITY, L = 0.f;
     float2 a = make_float2(0.f, 0.f);
     merge_row_wave(part_m, part_l, part_acc, n_f + R, [&](int i) -> int64_t {
-        if (i < n_f) return ((int64_t)u * nsa + i) * G + g;
-        return (hp0 + (int64_t)u * R + (i - n_f)) * G + g;
+        if (i < n_f) return ((int64_t)u * nsa + i) * gt + g;
+        return (hp0 + (int64_t)u * R + (i - n_f)) * gt + g;
     }, M, L, a);
     const float2 o = L > 0.f ? make_float2(a.x / L, a.y / L) : make_float2(0.f, 0.f);
     *reinterpret_cast<float2 *>(out + ((int64_t)b * Hq + qh) * 128 + 2 * (threadIdx.x & 63)) = o;
@@ -822,6 +822,23 @@ __global__ __launch_bounds__(256) void combine_flat_kernel(
 static bool mfma_ok(const Dims &D) {
     const bool g_ok = D.G == 1 || D.G == 2 || D.G == 4 || D.G == 8 || D.G == 16;
     return D.dtype == kBF16 && D.d == 128 && D.bs == 16 && g_ok;
+}
+
+// Rows of the balanced kernel's tile for G query rows per KV head.  Eight
+// rows run on the 16-row matrix-core tile (P V on the matrix cores, 142
+// VGPRs against 206): with 64 accumulators per lane the vector-ALU form's P V
+// arithmetic, not HBM, set that kernel's time.  Four rows stay on the
+// vector ALU: the 16-row tile made the Qwen3-8B layer's fused attention
+// slower (82 -> 89 us) for no gain over resident blocks.
+static int tile_rows(int G) { return G == 8 ? 16 : G; }
+
+// Query rows per unit of one balanced launch: a launch that also fetches
+// (nsf > 0) keeps the vector-ALU form for G = 8, whose fetch waves kept the
+// host link busier (51.5 against 50.9 GB/s on the Qwen3-32B layer); a
+// launch over resident blocks only takes the plan's tile (Qwen3-32B layer:
+// 26.3 -> 22.8 us).  The partial buffers hold the larger of the two.
+static int flat_rows_of_call(const Dims &D, const AttnPlan &P, int nsf) {
+    return nsf > 0 ? D.G : P.gt;
 }
 
 // 32 rows per KV head (32 heads per KV head, or a 32-row verification chunk)
@@ -860,7 +877,7 @@ AttnPlan plan_attention(const Dims &D) {
                 hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) ==
                     hipSuccess) {
                 const int u = (int)units;
-                switch (D.G) {
+                switch (tile_rows(D.G)) {
                 case 1: per_cu = flat_wgs_per_cu<1>(u); break;
                 case 2: per_cu = flat_wgs_per_cu<2>(u); break;
                 case 4: per_cu = flat_wgs_per_cu<4>(u); break;
@@ -892,6 +909,7 @@ AttnPlan plan_attention(const Dims &D) {
             }
         }
         if (D.G == 32 && !P.flat) P = AttnPlan{};  // the generic kernel instead
+        P.gt = P.flat ? tile_rows(D.G) : D.G;
     }
     if (!P.mfma) {
         int bps = 8;
@@ -900,6 +918,7 @@ AttnPlan plan_attention(const Dims &D) {
         P.ns1 = (D.K + bps - 1) / bps;
         P.nsf_max = 0;
     }
+    if (!P.mfma) P.gt = D.G;
     P.nsa = P.nsf_max + (P.flat ? 0 : P.ns1);
     P.vns = P.ns1;
     return P;
@@ -919,8 +938,8 @@ int verify_stride(const Dims &D) {
 }
 
 int64_t attn_partial_rows(const Dims &D, const AttnPlan &P) {
-    int64_t rows = D.units() * P.nsa * D.G;
-    if (P.flat) rows += D.units() * P.flat_rows * D.G;
+    int64_t rows = D.units() * P.nsa * P.gt;
+    if (P.flat) rows += D.units() * P.flat_rows * P.gt;
     return rows;
 }
 
@@ -989,7 +1008,7 @@ hipError_t launch_attention(const Dims &D, const AttnPlan &P, int mode, int nsf,
 #define OASIS_FLAT(GG)                                                                          \
     launch_flat_g<GG>(P, grid, lds, st, qq, sl, hk, att_block, att_slot, counts, T, D, mode, nsf, \
                       n_fetch_wg, sc, part_m, part_l, part_acc)
-        switch (D.G) {
+        switch (flat_rows_of_call(D, P, nsf)) {
         case 1: OASIS_FLAT(1); break;
         case 2: OASIS_FLAT(2); break;
         case 4: OASIS_FLAT(4); break;
@@ -1041,7 +1060,8 @@ hipError_t launch_combine(const Dims &D, const AttnPlan &P, int nsf, const float
                           hipStream_t st) {
     if (P.flat) {  // d = 128
         OASIS_LAUNCH(combine_flat_kernel, dim3((D.Hq + 3) / 4, D.B), dim3(256), 0, st, part_m,
-                     part_l, part_acc, out, D.Hq, D.Hkv, D.G, P.nsa, nsf, P.flat_rows,
+                     part_l, part_acc, out, D.Hq, D.Hkv, D.G, flat_rows_of_call(D, P, nsf), P.nsa,
+                     nsf, P.flat_rows,
                      D.units() * P.nsa);
         return hipGetLastError();
     }

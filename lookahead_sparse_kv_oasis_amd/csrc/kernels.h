@@ -138,6 +138,11 @@ struct AttnPlan {
     // flat_rows per unit.
     bool flat;
     int flat_waves, flat_pmin, flat_rows;
+    // Query rows per unit in the kernels and the partials (the row stride of
+    // the partial buffers): G, or 16 where the balanced kernel runs G = 8 on
+    // the 16-row matrix-core tile (rows past G repeat row 0, their partials
+    // unwritten).
+    int gt;
     // verification attention: partial rows per (unit, query row) of its
     // buffers (at least the split and balanced strides of every chunk size)
     int vns;

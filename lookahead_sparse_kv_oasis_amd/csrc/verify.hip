@@ -165,6 +165,7 @@ hipError_t launch_verify(const Dims &D, const AttnPlan &P, int n_drafts, const v
         Dc.G = ch.rows[k];
         Dc.Hq = D.Hkv * ch.rows[k];
         Pk[k] = plan_attention(Dc);
+        Pk[k].gt = ch.rows[k];  // partial rows of the chunk's own width
         Pk[k].nsf_max = 0;
         if (Pk[k].flat && Pk[k].flat_rows > P.vns) Pk[k].flat = false;
         if (!Pk[k].flat && ch.rows[k] > 16) return hipErrorInvalidValue;
