@@ -983,12 +983,34 @@ template <int G>
 static void launch_flat_g(const AttnPlan &P, dim3 grid, size_t lds, hipStream_t st,
                           const QRows &q, uint16_t *slots, const uint16_t *host_kv,
                           const int32_t *ab, const int32_t *as, const int32_t *counts, int64_t T,
-                          const Dims &D, int mode, int cap, int n_fetch_wg, float sc, float *pm,
-                          float *pl, float *pa) {
+                          const Dims &D, int mode, int cap, int n_fetch_wg, int hit_waves,
+                          float sc, float *pm, float *pl, float *pa) {
     OASIS_LAUNCH((attn_flat_kernel<G>), grid, dim3(256), lds, st, q, slots, host_kv, ab, as,
                  counts, T, D.Hq, D.Hkv, D.K, D.S, D.NBmax, mode, cap, n_fetch_wg, P.nsa,
-                 (int)D.units(), P.flat_waves, P.flat_rows, P.flat_pmin, sc, pm, pl, pa,
+                 (int)D.units(), hit_waves, P.flat_rows, P.flat_pmin, sc, pm, pl, pa,
                  D.units() * P.nsa);
+}
+
+// Hit waves of a balanced launch.  Alone, all the GPU holds at once.  In a
+// launch that also fetches, the hits only have to be done when the transfer
+// is: fewer hit waves, each with a longer run, then press less on the host
+// reads, and leave CUs free of hit waves for the fetch workgroups (a CU's
+// vector-memory loads complete at the pace of its slowest outstanding load,
+// so hit waves beside a fetch wave wait on the host round trip).  The count
+// paces the largest hit list (K per unit, about 1.5 us per block for a wave
+// at this concurrency) to the transfer of nsf blocks per unit at 50 GB/s;
+// the units cancel.  Qwen3-8B layer at cap 2: 584 waves instead of 2,048,
+// fused attention 82.5 -> 78.5 us (host link 50.8 -> 53.4 GB/s); a quarter
+// of them on every CU (1,024 waves) was slower, 98 us.
+static int flat_hit_waves(const Dims &D, const AttnPlan &P, int nsf) {
+    if (nsf <= 0) return P.flat_waves;
+    const double t_block = 1.5e-6, host_rate = 50e9, blk = 8192.0;
+    const double w = (double)D.K * t_block * host_rate / ((double)nsf * blk);
+    const int64_t lo = (D.units() * D.K + 63) / 64;  // runs of at most 64 entries
+    int64_t hw = (int64_t)w / 4 * 4;
+    if (hw < lo) hw = (lo + 3) / 4 * 4;
+    if (hw > P.flat_waves) hw = P.flat_waves;
+    return (int)hw;
 }
 
 hipError_t launch_attention(const Dims &D, const AttnPlan &P, int mode, int nsf, const void *q,
@@ -1001,13 +1023,14 @@ hipError_t launch_attention(const Dims &D, const AttnPlan &P, int mode, int nsf,
     if (P.mfma && P.flat) {
         if (mode == 0) nsf = 0;
         const int n_fetch_wg = nsf > 0 ? fetch_workgroups(D.units() * nsf) : 0;
-        const dim3 grid((unsigned)(n_fetch_wg + P.flat_waves / 4));
+        const int hw = flat_hit_waves(D, P, nsf);
+        const dim3 grid((unsigned)(n_fetch_wg + hw / 4));
         const size_t lds = sizeof(int32_t) * (D.units() + 1);
         const uint16_t *hk = (const uint16_t *)host_kv;
         uint16_t *sl = (uint16_t *)slots;
 #define OASIS_FLAT(GG)                                                                          \
     launch_flat_g<GG>(P, grid, lds, st, qq, sl, hk, att_block, att_slot, counts, T, D, mode, nsf, \
-                      n_fetch_wg, sc, part_m, part_l, part_acc)
+                      n_fetch_wg, hw, sc, part_m, part_l, part_acc)
         switch (flat_rows_of_call(D, P, nsf)) {
         case 1: OASIS_FLAT(1); break;
         case 2: OASIS_FLAT(2); break;

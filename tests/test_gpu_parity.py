@@ -38,6 +38,11 @@ def test_tiny_workload_bf16_variant():
     log(f"tiny bf16 d128: {p.run_all()}")
 
 
+def _all_units(w):
+    from tests.gpu_parity import every_unit
+    return every_unit(w)
+
+
 @pytest.mark.parametrize("q_heads,kv_heads", [(8, 8), (16, 8), (32, 4), (64, 4), (32, 1)])
 def test_group_sizes_reduced_context(q_heads, kv_heads):
     """G = 1, 2, 8, 16, 32 on a reduced context with a ragged prefix (32
@@ -47,8 +52,7 @@ def test_group_sizes_reduced_context(q_heads, kv_heads):
     extra = {"drafts": 2} if q_heads // kv_heads == 32 else {}
     w = synth.QWEN3_8B.with_(batch=2, q_heads=q_heads, kv_heads=kv_heads,
                              prefix_tokens=16 * 300 + 7, budget_tokens=16 * 64, **extra)
-    units = [(0, 0), (1, kv_heads - 1)]
-    p = Parity(w, 6, units)
+    p = Parity(w, 6, _all_units(w))
     log(f"G={q_heads // kv_heads}: {p.run_all()}")
 
 
@@ -59,7 +63,7 @@ def test_head_dims_reduced_context(head_dim):
     Parity, log = _parity()
     w = synth.QWEN3_8B.with_(batch=2, head_dim=head_dim, prefix_tokens=16 * 200 + 3,
                              budget_tokens=16 * 64)
-    p = Parity(w, 5, [(0, 0), (1, 7)])
+    p = Parity(w, 5, _all_units(w))
     log(f"d={head_dim}: {p.run_all()}")
 
 
@@ -74,7 +78,7 @@ def test_block_sizes_reduced_context(block_size, budget_blocks):
     w = synth.QWEN3_8B.with_(batch=2, block_size=block_size,
                              prefix_tokens=block_size * 120 + block_size // 2 + 1,
                              budget_tokens=block_size * budget_blocks)
-    p = Parity(w, 6, [(0, 0), (1, 7)])
+    p = Parity(w, 6, _all_units(w))
     log(f"block size {block_size}: {p.run_all()}")
 
 
@@ -83,7 +87,7 @@ def test_tiny_workload_one_token_blocks():
     the generic attention at the smallest block."""
     Parity, log = _parity()
     w = synth.TINY.with_(block_size=1, prefix_tokens=200, budget_tokens=8, slots=16)
-    p = Parity(w, 8, [(0, 0), (0, 1)])
+    p = Parity(w, 8, _all_units(w))
     log(f"tiny, one-token blocks: {p.run_all()}")
 
 
