@@ -238,9 +238,12 @@ int tbegin(oasis_t *h, int cls, hipStream_t st) {
         fold_timer(t);
     }
     if (t.used == t.start.size()) {
+        // read by the host only, after the stop event completes: no system
+        // fence (with one, the timed launches ran 2-5 us longer than the
+        // others: the fence flushed the caches around them)
         hipEvent_t a, b;
-        HIP_OK(h, hipEventCreate(&a));
-        HIP_OK(h, hipEventCreate(&b));
+        HIP_OK(h, hipEventCreateWithFlags(&a, hipEventDisableSystemFence));
+        HIP_OK(h, hipEventCreateWithFlags(&b, hipEventDisableSystemFence));
         t.start.push_back(a);
         t.stop.push_back(b);
     }
