@@ -795,9 +795,11 @@ __global__ __launch_bounds__(256) void combine_kernel(const float *__restrict__ 
 
 // The same after the balanced hit path, d = 128: the unit's n_f fetch
 // partials (splits [0, n_f) of nsa), then its R hit partial rows
-// hp0 + u R + s, the unused ones marked empty; gt query rows per partial.  One wave per output row (four
-// per workgroup), merging with merge_row_wave: the m and l of every partial
-// in one round trip, then the sums of the live ones only.
+// hp0 + u R + s, the unused ones marked empty; gt query rows per partial.
+// One wave per output row (four per workgroup), merging with merge_row_wave:
+// the m and l of every partial and the sums of the first 16 in one round
+// trip, the sums of later live ones after (4.58 -> 4.46 us on the Qwen3-8B
+// layer against reading the m and l first).
 __global__ __launch_bounds__(256) void combine_flat_kernel(
     const float *__restrict__ part_m, const float *__restrict__ part_l,
     const float *__restrict__ part_acc, float *__restrict__ out, int Hq, int Hkv, int G,
@@ -809,7 +811,7 @@ __global__ __launch_bounds__(256) void combine_flat_kernel(
     const int u = b * Hkv + h;
     float M = -INFINITY, L = 0.f;
     float2 a = make_float2(0.f, 0.f);
-    merge_row_wave(part_m, part_l, part_acc, n_f + R, [&](int i) -> int64_t {
+    merge_row_wave<true>(part_m, part_l, part_acc, n_f + R, [&](int i) -> int64_t {
         if (i < n_f) return ((int64_t)u * nsa + i) * gt + g;
         return (hp0 + (int64_t)u * R + (i - n_f)) * gt + g;
     }, M, L, a);

@@ -66,24 +66,35 @@ constexpr int kWaveMergeRegs = 16;
 
 // One wave merges the n partials of one output row of 128 dimensions (partial
 // i at row pidx(i); lane l owns dimensions 2 l and 2 l + 1) into a running
-// (M, L, a).  Per group of 64 partials, lane s first reads partial s's m and
-// l (one round trip for all of them); the weights and the normaliser follow
-// by wave reductions, and only the sums of the live partials (m > -inf) are
-// read, kWaveMergeRegs per round trip, as 512-byte rows.  Partials marked
-// empty cost no sum read, which matters where a unit's fixed set of partial
-// rows is mostly unused.
-template <typename F>
+// (M, L, a).  Per group of 64 partials, lane s reads partial s's m and l; the
+// weights and the normaliser follow by wave reductions, and then only the
+// sums (512-byte rows) of the live partials (m > -inf) are read,
+// kWaveMergeRegs per round trip: partials marked empty cost no sum read,
+// which matters where a unit's fixed set of partial rows is mostly unused.
+// With Spec, the sums of the first kWaveMergeRegs partials are read together
+// with the first group's m and l, live or not, so that the common case takes
+// one round trip at the price of the dead rows' bytes (a gain for the decode
+// combine's 4 rows per unit, a loss for the verification's 20).
+template <bool Spec = false, typename F>
 __device__ __forceinline__ void merge_row_wave(const float *__restrict__ part_m,
                                                const float *__restrict__ part_l,
                                                const float *__restrict__ part_acc, int n, F pidx,
                                                float &M, float &L, float2 &a) {
     const int lane = threadIdx.x & 63;
+    float2 v0[kWaveMergeRegs];  // sums of partials 0 .. kWaveMergeRegs - 1 (0 again past n)
+    if constexpr (Spec) {
+#pragma unroll
+        for (int k = 0; k < kWaveMergeRegs; ++k)
+            v0[k] =
+                *reinterpret_cast<const float2 *>(part_acc + pidx(k < n ? k : 0) * 128 + 2 * lane);
+    }
     for (int i0 = 0; i0 < n; i0 += 64) {
-        float pm = -INFINITY, pl = 0.f;
-        if (i0 + lane < n) {
-            const int64_t pi = pidx(i0 + lane);
-            pm = part_m[pi];
-            pl = part_l[pi];
+        // lanes past n read partial i0 again and count as empty
+        const int64_t pi = pidx(i0 + lane < n ? i0 + lane : i0);
+        float pm = part_m[pi], pl = part_l[pi];
+        if (i0 + lane >= n) {
+            pm = -INFINITY;
+            pl = 0.f;
         }
         uint64_t live = __ballot(pm != -INFINITY);
         if (live == 0) continue;
@@ -95,7 +106,19 @@ __device__ __forceinline__ void merge_row_wave(const float *__restrict__ part_m,
         a.x *= r;
         a.y *= r;
         M = nm;
-        const int s_first = __builtin_ctzll(live);
+        if (Spec && i0 == 0) {
+#pragma unroll
+            for (int k = 0; k < kWaveMergeRegs; ++k) {
+                // an empty partial's sums may hold anything (NaN included):
+                // selected away, not multiplied by 0
+                const bool lk = (live >> k) & 1;
+                const float wf = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(w), k));
+                a.x += lk ? wf * v0[k].x : 0.f;
+                a.y += lk ? wf * v0[k].y : 0.f;
+            }
+            live &= ~((1ull << kWaveMergeRegs) - 1);
+        }
+        const int s_first = live ? __builtin_ctzll(live) : 0;
         while (live) {
             // every load issued before any is used; past the last live
             // partial the first one is read again with weight 0
