@@ -87,7 +87,7 @@ def _workloads():
     return {w.name: w for w in synth.WORKLOADS}
 
 
-def pinned_h2d_peak_gbps(nbytes=1 << 30, reps=5):
+def pinned_h2d_peak_gbps(nbytes=1 << 30, reps=10):
     """Best pinned host -> device copy rate (hipMemcpyAsync through torch)."""
     import torch
     src = torch.empty(nbytes, dtype=torch.uint8, pin_memory=True)
@@ -155,6 +155,17 @@ def hbm_read_peak(same_sizes=(), nbytes=2 << 30, reps=5):
     return out
 
 
+def _cpu_model():
+    try:
+        with open("/proc/cpuinfo") as fh:
+            for line in fh:
+                if line.startswith("model name"):
+                    return line.split(":", 1)[1].strip()
+    except OSError:
+        pass
+    return None
+
+
 def cpu_baseline(w, target_s=12.0, max_threads=16, bytes_per_step=None):
     """The fp64 oracle (as it stands) on a bounded sample of the workload: up
     to 64 (b, KV head) units stepped through the same decode steps (appended
@@ -214,6 +225,7 @@ def cpu_baseline(w, target_s=12.0, max_threads=16, bytes_per_step=None):
         "value": value,
         "unit": "layer-steps/s",
         "cores": threads,
+        "cpu_model": _cpu_model(),
         "kind": "oracle",
         "effective_gbps": value * bytes_per_step / 1e9 if bytes_per_step else None,
         "phase_share": {k: v / tsum for k, v in total.items()},
