@@ -805,6 +805,11 @@ def bench_model(args, w):
                     "measured_read_peak_gbps": rpk["gbps"] if rpk else None,
                     "frac_of_measured_read_peak": score_gbps / rpk["gbps"] if rpk else None}
         link_gbps = r["fetched"] * blk_bytes / (dt / K) / 1e9
+        # the metric's HBM figure with the layers pipelined: every layer's
+        # score and attention bytes of a step over the step's wall time
+        pipe_bytes = L * score_bytes + r["attended"] * blk_bytes + \
+            L * (q_bytes + w.batch * w.q_heads * d * 4)
+        pipe_gbps = pipe_bytes / (dt / K) / 1e9
         line = {
             "metric": METRIC,
             "value": L * K / dt,
@@ -824,6 +829,10 @@ def bench_model(args, w):
                        "host_kv_buffers": mr.H},
             "model_steps_per_s": K / dt,
             "roofline": roof,
+            "pipelined_score_attn": {"hbm_bytes_per_step": pipe_bytes, "gbps": pipe_gbps,
+                                     "frac": pipe_gbps / HBM_PEAK_GBPS,
+                                     "note": "score + attention bytes of all layers per step "
+                                             "over the step's wall time (kernels overlapped)"},
             "host_link": {"achieved_gbps_step_avg": link_gbps, "pinned_h2d_peak_gbps": h2d,
                           "blocks_per_step": r["fetched"],
                           "bytes_per_step": r["fetched"] * blk_bytes},
