@@ -18,11 +18,17 @@ def _dev(a):
     return torch.from_numpy(np.ascontiguousarray(a)).cuda()
 
 
-def test_noalloc_attention_matches_the_handle_on_two_calls():
+@pytest.mark.parametrize("shape", ["qwen3_8b", "qwen3_32b"])
+def test_noalloc_attention_matches_the_handle_on_two_calls(shape):
+    """4 heads per KV head (vector-ALU P V) and 8 (the 16-row matrix-core
+    tile over resident blocks, twice the partial rows)."""
     import lookahead_sparse_kv_oasis_amd as L
     from lookahead_sparse_kv_oasis_amd.runner import LayerRunner
     L.lib()
-    w = synth.QWEN3_8B.with_(batch=8, prefix_tokens=16 * 600 + 9)
+    if shape == "qwen3_8b":
+        w = synth.QWEN3_8B.with_(batch=8, prefix_tokens=16 * 600 + 9)
+    else:
+        w = synth.QWEN3_32B.with_(batch=4, prefix_tokens=16 * 600 + 9)
     run = LayerRunner(w, 3)
     h = run.h
     run.admission()
