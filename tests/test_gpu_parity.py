@@ -307,20 +307,23 @@ def test_miss_correction_reduced_context():
 
 # ------------------------------------------------------------------ verification attention
 
-@pytest.mark.parametrize("q_heads,n_steps", [(32, 4), (64, 3), (128, 2)])
-def test_verification_attention_against_oracle(q_heads, n_steps):
+@pytest.mark.parametrize("q_heads,n_steps,fewer", [(32, 4, 0), (64, 3, 0), (128, 2, 0),
+                                                   (8, 2, 0), (16, 2, 1)])
+def test_verification_attention_against_oracle(q_heads, n_steps, fewer):
     """Normal and draft queries together with causal draft tokens ([OASIS]
     Fig. 7 right) after each step of the free-running path: every set of
     sampled units against the oracle over the GPU's attended list; set 0
     equal to oasis_sparse_attn up to summation order.  20 rows per KV head
-    run as one padded 32-row pass, 40 as 32 + 8, 80 as 32 + 32 + 16."""
+    run as one padded 32-row pass, 40 as 32 + 8, 80 as 32 + 32 + 16, 5 as
+    one padded 8-row pass; `fewer` drafts than the handle was sized for
+    (2 heads x 4 sets: one 8-row pass)."""
     from lookahead_sparse_kv_oasis_amd.runner import LayerRunner, to_device
     from tests.gpu_parity import ATTN_TOL, log
     w = synth.QWEN3_8B.with_(batch=3, q_heads=q_heads, prefix_tokens=16 * 300 + 9,
                              budget_tokens=16 * 64)
     run = LayerRunner(w, n_steps)
     h = run.h
-    D, B, Hkv, d, G = w.drafts, w.batch, w.kv_heads, w.head_dim, w.group
+    D, B, Hkv, d, G = w.drafts - fewer, w.batch, w.kv_heads, w.head_dim, w.group
     rng = np.random.default_rng(7)
     out = torch.empty((1 + D, B, w.q_heads, d), dtype=torch.float32, device="cuda")
     run.admission()
@@ -332,14 +335,15 @@ def test_verification_attention_against_oracle(q_heads, n_steps):
         run.step(t)
         kd = synth.encode(rng.standard_normal((D, B, Hkv, d)).astype(np.float32), w.dtype)
         vd = synth.encode(rng.standard_normal((D, B, Hkv, d)).astype(np.float32), w.dtype)
-        h.oasis_sparse_attn_verify(run.q, run.drafts[t], D, to_device(kd), to_device(vd), out)
+        h.oasis_sparse_attn_verify(run.q, run.drafts[t][:D].contiguous() if fewer else run.drafts[t],
+                                   D, to_device(kd), to_device(vd), out)
         torch.cuda.synchronize()
         got = out.cpu().numpy()
         # set 0 is the plain attention, summed in other splits (fetched blocks
         # are read from their slots here, inside the fetch waves there)
         assert np.max(np.abs(got[0] - run.out.cpu().numpy())) < 1e-5, f"step {t}: set 0"
         ab, cnt = h.read("ATT_BLOCK"), h.read("COUNTS")
-        dr = oracle.to_f64(synth.drafts(w, t), w.dtype)
+        dr = oracle.to_f64(synth.drafts(w, t), w.dtype)[:D]
         T = w.prefix_tokens + t
         for (b, hh) in units:
             u = b * Hkv + hh
