@@ -591,6 +591,21 @@ def test_free_running_full_slot_pools(slots):
     log(f"{slots}-slot pool: {rep}")
 
 
+@pytest.mark.parametrize("fetch_ratio", [0.02, 1.0])
+def test_free_running_largest_budget(fetch_ratio):
+    """The largest budget the handle takes, 16,384 tokens (K = 1,024 blocks
+    per KV head) with 1,024 slots, on a 1,600-block context: the top-K places
+    its winners by rank counting (more than 128 of them), the select and the
+    balanced attention run K-entry lists (its partial rows per unit grow with
+    K), and fetch-all moves up to 1,024 blocks per KV head in one step.  Every
+    unit, every step, against the oracle."""
+    from tests.gpu_parity import FreeRunning, every_unit, log
+    w = synth.QWEN3_8B.with_(batch=2, prefix_tokens=16 * 1600 + 11, budget_tokens=16 * 1024,
+                             fetch_ratio=fetch_ratio)
+    rep = FreeRunning(w, 4, every_unit(w)).run_free()
+    log(f"K = 1024, ratio {fetch_ratio}: {rep}")
+
+
 def test_free_running_past_the_direct_lookup_table():
     """More than 16,384 blocks per KV head (272K tokens): the select's
     resident-block lookup falls back to the LDS hash; checked step by step
