@@ -148,6 +148,43 @@ def test_error_paths():
     h.oasis_check()
 
 
+@pytest.mark.parametrize("hq", [32, 64, 128])
+def test_empty_attended_sets_give_zero_output_on_the_matrix_core_path(hq):
+    """bf16, d = 128 (the balanced attention kernel, 4, 8 and 16 heads per KV
+    head): nothing resident and cap 0, so every unit's attended list is empty;
+    the kernel marks every partial row empty and the combine writes exact
+    zeros (the rows' sums, never written, are selected away).  Verification
+    attention over the same empty lists leaves set 0 at zero and attends set
+    j to draft tokens 1..j only."""
+    B, hkv, d, T = 4, 8, 128, 16 * 100 + 3
+    h = _handle(batch=B, hq=hq, hkv=hkv, d=d, dtype=1, drafts=2, max_tokens=T + 8,
+                budget=16 * 64)
+    z = np.zeros((B, hkv, T, d), np.uint16)
+    h.oasis_load_prefix(z, z, T)
+    q = torch.ones((B, hq, d), dtype=torch.int16, device="cuda") * 0x3F80  # bf16 1.0
+    out = torch.full((B, hq, d), float("nan"), dtype=torch.float32, device="cuda")
+    h.oasis_predict(q, None, 0)
+    h.oasis_select_and_fetch(0)
+    h.oasis_sparse_attn(q, out)
+    torch.cuda.synchronize()
+    assert torch.all(out == 0)
+    assert int(h.read("COUNTS").reshape(-1, 4)[:, 0].max()) == 0
+    # verification: set 0 has nothing to attend; draft j attends to draft
+    # tokens 1..j, whose values are v_i = i + 1 in every dimension
+    D = 2
+    drafts = q.unsqueeze(0).repeat(D, 1, 1, 1).contiguous()
+    kd = torch.zeros((D, B, hkv, d), dtype=torch.int16, device="cuda")
+    vals = [0x3F80, 0x4000]  # bf16 1.0, 2.0
+    vd = torch.stack([torch.full((B, hkv, d), v, dtype=torch.int16, device="cuda") for v in vals])
+    vout = torch.full((1 + D, B, hq, d), float("nan"), dtype=torch.float32, device="cuda")
+    h.oasis_sparse_attn_verify(q, drafts, D, kd, vd, vout)
+    torch.cuda.synchronize()
+    assert torch.all(vout[0] == 0)
+    assert torch.all(vout[1] == 1.0)          # one token, value 1
+    assert torch.allclose(vout[2], torch.full_like(vout[2], 1.5), atol=1e-6)  # equal logits
+    h.oasis_check()
+
+
 def test_runs_are_bitwise_deterministic():
     from lookahead_sparse_kv_oasis_amd.runner import LayerRunner
     w = synth.QWEN3_8B.with_(batch=4, prefix_tokens=16 * 400 + 3)
