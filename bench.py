@@ -459,8 +459,12 @@ def bench_layer(args, w, steps, warmup, main_leg=True, shared=None):
     # (the append before it leaves it pending)
     fused = bool(stats1["fetch_fused"]) and not correcting
     # with the fetch fused into the attention kernel the host-link transfer
-    # runs inside it: its rate is bounded below by bytes / attention time
-    g_ms = ms_attn if fused else ms_gather
+    # runs inside it: its rate is bounded below by bytes / attention time.
+    # With miss correction the corrective fetch runs inside the attention and
+    # the prefetch in the standalone gather, so the step's fetched bytes span
+    # both launches.
+    g_ms = ms_attn if fused else (ms_attn + ms_gather if correcting else ms_gather)
+    fetch_in_attn = fused or correcting
     gather_gbps = fetched * blk_bytes / (g_ms * 1e-3) / 1e9 if g_ms > 0 else None
     h2d = shared.get("h2d") if not main_leg else (
         None if args.no_h2d_peak else pinned_h2d_peak_gbps())
@@ -469,7 +473,7 @@ def bench_layer(args, w, steps, warmup, main_leg=True, shared=None):
         rpk = hbm_read_peak((score_bytes, attn_bytes, score_bytes + attn_bytes))
     read_peak = rpk["gbps"] if rpk else shared.get("read_peak")
     link_gbps = h2d if h2d is not None else PCIE_GEN5_X16_GBPS
-    attn_link_bound = (fused and fetched * blk_bytes / (link_gbps * 1e9) >=
+    attn_link_bound = (fetch_in_attn and fetched * blk_bytes / (link_gbps * 1e9) >=
                        attn_bytes / ((read_peak or 6500.0) * 1e9))
 
     def same(n):
@@ -494,8 +498,10 @@ def bench_layer(args, w, steps, warmup, main_leg=True, shared=None):
                       "hbm_frac_of_measured_read_peak": frac_of(attn_gbps, read_peak),
                       "same_size_read_gbps": same(attn_bytes),
                       "bound": "host_link" if attn_link_bound else "hbm",
-                      "fetch_inside": fused},
-        "host_link": {"kernel": "oasis_sparse_attn (fused fetch)" if fused else "oasis_gather",
+                      "fetch_inside": fetch_in_attn},
+        "host_link": {"kernel": "oasis_sparse_attn (fused fetch)" if fused else
+                      "oasis_sparse_attn (corrective fetch) + oasis_gather (prefetch)"
+                      if correcting else "oasis_gather",
                       "achieved_gbps": gather_gbps, "pinned_h2d_peak_gbps": h2d,
                       "frac": frac_of(gather_gbps, h2d),
                       "pcie_gen5_x16_gbps": PCIE_GEN5_X16_GBPS,

@@ -744,17 +744,53 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2))) void a
         if (w == s1) mark_empty(hp0 + (int64_t)u * R + (w - s0) + 1, R - 1 - (w - s0), lane, 64);
     };
     int cur_u = -1;
-    uint4 kk[4], vv[4];
-    for (int j = 0; j < n; ++j) {
-        const int u = rl(my_u, j);
-        if (u != cur_u) {
-            if (cur_u >= 0) finish(cur_u);
-            st.load_q(st.qb, qr, u / Hkv, u % Hkv);  // waited for with the block
-            st.reset();
-            cur_u = u;
+    auto src = [&](int j) {
+        return slots + ((int64_t)rl(my_u, j) * S + rl(my_slot, j)) * Wv::BLK;
+    };
+    auto enter = [&](int u) {  // a new unit: its query rows, waited for with its block
+        if (u == cur_u) return;
+        if (cur_u >= 0) finish(cur_u);
+        st.load_q(st.qb, qr, u / Hkv, u % Hkv);
+        st.reset();
+        cur_u = u;
+    };
+    if constexpr (G < 32) {
+        uint4 kk[4], vv[4];
+        for (int j = 0; j < n; ++j) {
+            enter(rl(my_u, j));
+            st.load_nt(kk, vv, src(j));
+            st.block(kk, vv, block_valid(T_, rl(my_blk, j)), scale_log2);
         }
-        st.load_nt(kk, vv, slots + ((int64_t)u * S + rl(my_slot, j)) * Wv::BLK);
-        st.block(kk, vv, block_valid(T_, rl(my_blk, j)), scale_log2);
+    } else {
+        // 32 rows: a block's matrix work (two query tiles, V through LDS) is
+        // long enough to hide part of the next block's round trip, so the
+        // next block's loads are issued before it (two register buffers,
+        // alternating).  A new unit's query loads go out before them, so
+        // the wait for the current block and its query leaves the next
+        // block in flight.  Every load in the loop is unconditional (the
+        // last one or two blocks are peeled off), so that wait is never a
+        // wait for everything.
+        uint4 ka[4], va[4], kb[4], vb[4];
+        auto valid = [&](int j) { return block_valid(T_, rl(my_blk, j)); };
+        st.load_nt(ka, va, src(0));
+        int j = 0;
+        for (; j + 2 < n; j += 2) {
+            enter(rl(my_u, j));
+            st.load_nt(kb, vb, src(j + 1));
+            st.block(ka, va, valid(j), scale_log2);
+            enter(rl(my_u, j + 1));
+            st.load_nt(ka, va, src(j + 2));
+            st.block(kb, vb, valid(j + 1), scale_log2);
+        }
+        enter(rl(my_u, j));  // block j is in (ka, va); one more may follow
+        if (j + 1 < n) {
+            st.load_nt(kb, vb, src(j + 1));
+            st.block(ka, va, valid(j), scale_log2);
+            enter(rl(my_u, j + 1));
+            st.block(kb, vb, valid(j + 1), scale_log2);
+        } else {
+            st.block(ka, va, valid(j), scale_log2);
+        }
     }
     finish(cur_u);
 }
