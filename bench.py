@@ -279,6 +279,9 @@ def main():
                     help="default run: timed steps of each extra workload (36-layer model: 3)")
     ap.add_argument("--no-extra-workloads", action="store_true",
                     help="default run: the Qwen3-8B layer alone")
+    ap.add_argument("--copy-cus", type=int, default=0,
+                    help="partition the CUs: copy stream on CUs [0, N), compute (and side) "
+                         "streams on the rest, handles sized for them (0: no partition)")
     args = ap.parse_args()
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
         print("bench.py measures one GPU only: every (batch row, KV head) unit of the decode "
@@ -297,6 +300,37 @@ def main():
         torch.cuda.synchronize()
         print(json.dumps({"copy_calibration_bytes": n, "launches": 5}))
         return
+
+    if args.copy_cus > 0:
+        _partition(args.copy_cus)
+        with torch.cuda.stream(_PART["compute"]):
+            _run(args)
+        torch.cuda.synchronize()
+        return
+    _run(args)
+
+
+# CU partition of the run (--copy-cus): compute units of the compute streams
+# and the streams themselves
+_PART = {}
+
+
+def _partition(n_copy):
+    import torch
+
+    from lookahead_sparse_kv_oasis_amd import stream_create_cus
+    ncu = torch.cuda.get_device_properties(0).multi_processor_count
+    if not 0 < n_copy < ncu:
+        raise SystemExit(f"--copy-cus must be in 1..{ncu - 1}")
+    ext = torch.cuda.ExternalStream
+    _PART.update(cus=ncu - n_copy, copy_cus=n_copy,
+                 compute=ext(stream_create_cus(n_copy, ncu - n_copy)),
+                 side=ext(stream_create_cus(n_copy, ncu - n_copy)),
+                 copy=ext(stream_create_cus(0, n_copy)))
+
+
+def _run(args):
+    import torch
 
     default_run = args.workload is None
     w = _workloads()[args.workload or "qwen3_8b_layer_b32_t32k_bf16"]
@@ -374,7 +408,7 @@ def bench_layer(args, w, steps, warmup, main_leg=True, shared=None):
     n_fused_end = n_main + (steps if fused_leg else 0)
     n_steps = n_fused_end + (steps if split_leg else 0)
     t_setup = time.perf_counter()
-    run = LayerRunner(w, n_steps)
+    run = LayerRunner(w, n_steps, compute_units=_PART.get("cus", 0))
     h = run.h
     if args.fuse_score_topk:
         h.oasis_set_score_topk_fusion(True)
@@ -443,7 +477,8 @@ def bench_layer(args, w, steps, warmup, main_leg=True, shared=None):
                        "budget_tokens": w.budget_tokens, "drafts": w.drafts,
                        "fetch_ratio": w.fetch_ratio, "cap_per_kv_head": run.cap,
                        "forced_evict_frac": w.forced_evict_frac,
-                       "fuse_score_topk": bool(args.fuse_score_topk)},
+                       "fuse_score_topk": bool(args.fuse_score_topk),
+                       **({"copy_cus": _PART["copy_cus"]} if _PART else {})},
             "_bytes_per_step": score_bytes + attn_bytes}
     if args.no_kernel_timing:
         base.update(roofline=None, cpu_baseline=None)
@@ -718,7 +753,8 @@ def bench_model(args, w):
         w = w.with_(steps=n_steps)
     t_setup = time.perf_counter()
     log = lambda m: print("# " + m, file=sys.stderr, flush=True)
-    mr = ModelRunner(w, n_steps, data_layers=args.data_layers, log=log)
+    mr = ModelRunner(w, n_steps, data_layers=args.data_layers, log=log,
+                     compute_units=_PART.get("cus", 0))
     if args.fuse_score_topk:
         for h in mr.handles:
             h.oasis_set_score_topk_fusion(True)
@@ -732,8 +768,8 @@ def bench_model(args, w):
         ratios = [w.fetch_ratio]
     schedules = ["overlap", "serial"] if args.schedule == "both" else [args.schedule]
     stream = torch.cuda.current_stream()
-    side = torch.cuda.Stream()
-    xfer = torch.cuda.Stream()
+    side = _PART.get("side") or torch.cuda.Stream()
+    xfer = _PART.get("copy") or torch.cuda.Stream()
     h2d = None if args.no_h2d_peak else pinned_h2d_peak_gbps()
     rpk = None if args.no_read_peak else hbm_read_peak()
     cpu = None if args.no_cpu_baseline else cpu_baseline(w.with_(layers=1))
@@ -832,7 +868,8 @@ def bench_model(args, w):
                        "cap_per_kv_head": cap, "schedule": main_sched,
                        "ordering": "lookahead" if w.lookahead else "within step",
                        "correct_cap": args.correct_cap if w.lookahead else None,
-                       "host_kv_buffers": mr.H},
+                       "host_kv_buffers": mr.H,
+                       **({"copy_cus": _PART["copy_cus"]} if _PART else {})},
             "model_steps_per_s": K / dt,
             "roofline": roof,
             "pipelined_score_attn": {"hbm_bytes_per_step": pipe_bytes, "gbps": pipe_gbps,

@@ -75,7 +75,10 @@ typedef struct {
     int32_t max_drafts;     /* largest n_drafts passed to oasis_predict */
     int32_t slots_per_head; /* HBM block slots per (b, KV head); 0 -> budget blocks;
                                budget blocks <= slots <= 2048 */
-    int32_t reserved;
+    int32_t compute_units;  /* CUs the handle's launches are sized to fill; 0 -> all
+                               of the device's.  Set it to n_cus when the handle's
+                               compute work runs on a stream from
+                               oasis_stream_create_cus (0 or 1..device CUs) */
     int64_t max_tokens;     /* capacity of the host KV per sequence */
 } oasis_layout;
 
@@ -454,6 +457,20 @@ int64_t oasis_tokens(const oasis_t *h);
 /* The handle's copy stream (gather); for callers that order their own work
  * after it. */
 hipStream_t oasis_copy_stream(const oasis_t *h);
+
+/* A stream of the current device (default priority) whose kernels run only
+ * on compute units [first_cu, first_cu + n_cus) of the runtime's CU mask
+ * (hipExtStreamCreateWithCUMask).  Streams made from disjoint ranges never
+ * share a CU.  The OasisKV page puts the host -> HBM transfer on a stream of
+ * its own beside the attention (Fig. 8); on this GPU a CU's vector loads
+ * return at the pace of its slowest outstanding load, so HBM reads on a CU
+ * that also runs host reads wait for the host link's round trip.  Giving the
+ * copy stream a few CUs of its own and the compute streams the rest keeps
+ * both at full rate.  OASIS_E_INVAL when the range is empty or past the
+ * device's CUs, OASIS_E_HIP when the runtime refuses.  Release with
+ * oasis_stream_destroy. */
+int oasis_stream_create_cus(int32_t first_cu, int32_t n_cus, hipStream_t *out);
+int oasis_stream_destroy(hipStream_t stream);
 
 /* ------------------------------------------------------------------ helpers */
 

@@ -36,7 +36,8 @@ EXPORTS = [
     "oasis_sparse_attn_noalloc", "oasis_sparse_attn_verify", "oasis_buffer_bytes", "oasis_read", "oasis_get_stats",
     "oasis_check", "oasis_set_timing", "oasis_set_timing_period",
     "oasis_set_score_topk_fusion", "oasis_set_fetch_in_attention", "oasis_set_attend_all_resident", "oasis_get_timing", "oasis_get_dims", "oasis_tokens",
-    "oasis_copy_stream", "oasis_stream_read", "oasis_kv_bytes_per_token", "oasis_cap_from_ratio",
+    "oasis_copy_stream", "oasis_stream_create_cus", "oasis_stream_destroy",
+    "oasis_stream_read", "oasis_kv_bytes_per_token", "oasis_cap_from_ratio",
     "oasis_strerror",
     "oasis_last_error",
 ]
@@ -52,7 +53,7 @@ class oasis_layout(ctypes.Structure):
     _fields_ = [("batch", ctypes.c_int32), ("num_q_heads", ctypes.c_int32),
                 ("num_kv_heads", ctypes.c_int32), ("head_dim", ctypes.c_int32),
                 ("dtype", ctypes.c_int32), ("max_drafts", ctypes.c_int32),
-                ("slots_per_head", ctypes.c_int32), ("reserved", ctypes.c_int32),
+                ("slots_per_head", ctypes.c_int32), ("compute_units", ctypes.c_int32),
                 ("max_tokens", ctypes.c_int64)]
 
 
@@ -132,6 +133,8 @@ def lib():
             "oasis_tokens": (i64, [H]),
             "oasis_copy_stream": (vp, [H]),
             "oasis_stream_read": (ctypes.c_int, [vp, i64, vp, i32, vp]),
+            "oasis_stream_create_cus": (ctypes.c_int, [i32, i32, ctypes.POINTER(ctypes.c_void_p)]),
+            "oasis_stream_destroy": (ctypes.c_int, [vp]),
             "oasis_kv_bytes_per_token": (ctypes.c_uint64, [i32, i32, i32, i32]),
             "oasis_cap_from_ratio": (i32, [f32, i32]),
             "oasis_strerror": (ctypes.c_char_p, [ctypes.c_int]),
@@ -185,6 +188,23 @@ def stream_read(buf, sink, workgroups: int, stream=None) -> None:
         raise OasisError(rc, "oasis_stream_read")
 
 
+def stream_create_cus(first_cu: int, n_cus: int) -> int:
+    """oasis_stream_create_cus: a HIP stream (as an int handle, for
+    torch.cuda.ExternalStream) whose kernels run on CUs [first_cu, first_cu +
+    n_cus) only; release it with stream_destroy."""
+    s = ctypes.c_void_p()
+    rc = lib().oasis_stream_create_cus(first_cu, n_cus, ctypes.byref(s))
+    if rc != OASIS_OK:
+        raise OasisError(rc, "oasis_stream_create_cus")
+    return s.value
+
+
+def stream_destroy(stream: int) -> None:
+    rc = lib().oasis_stream_destroy(stream)
+    if rc != OASIS_OK:
+        raise OasisError(rc, "oasis_stream_destroy")
+
+
 def sparse_attn_noalloc(desc: oasis_attn_desc, q, slots, att_block, att_slot, counts,
                         tokens: int, out, stream=None) -> int:
     """oasis_sparse_attn_noalloc on device tensors; returns the status."""
@@ -202,12 +222,14 @@ class Oasis:
 
     def __init__(self, batch, num_q_heads, num_kv_heads, head_dim, dtype, max_drafts,
                  max_tokens, block_size=16, budget_tokens=2048, fetch_ratio=0.02,
-                 slots_per_head=0, share_host_with: "Oasis | None" = None):
+                 slots_per_head=0, share_host_with: "Oasis | None" = None,
+                 compute_units=0):
         """share_host_with: another handle whose host KV this layer reuses
-        (oasis_create_shared); otherwise oasis_create."""
+        (oasis_create_shared); otherwise oasis_create.  compute_units: the
+        layout field of that name (0: every CU)."""
         L = lib()
         self.layout = oasis_layout(batch, num_q_heads, num_kv_heads, head_dim, dtype,
-                                   max_drafts, slots_per_head, 0, max_tokens)
+                                   max_drafts, slots_per_head, compute_units, max_tokens)
         h = ctypes.c_void_p()
         if share_host_with is None:
             rc = L.oasis_create(ctypes.byref(self.layout), block_size, budget_tokens,

@@ -467,6 +467,9 @@ int create_handle(const oasis_layout *layout, int32_t block_size, int32_t budget
     const int G = L.num_q_heads / L.num_kv_heads;
     const int64_t NBmax = (L.max_tokens + block_size - 1) / block_size;
     if (K > 1024 || S < K || S > 2048 || NBmax > 65536) return OASIS_E_INVAL;
+    Dims probe{};
+    const int dev_cus = compute_units(probe);  // the current device's CUs
+    if (L.compute_units < 0 || L.compute_units > dev_cus) return OASIS_E_INVAL;
     const int Q = G * (1 + L.max_drafts);
     if ((int64_t)Q * L.head_dim * 4 > 64 * 1024) return OASIS_E_INVAL;
 
@@ -485,6 +488,7 @@ int create_handle(const oasis_layout *layout, int32_t block_size, int32_t budget
     D.K = K;
     D.S = S;
     D.NBmax = NBmax;
+    D.cus = L.compute_units > 0 ? L.compute_units : dev_cus;
     h->plan = plan_attention(D);
     h->plan.vns = verify_stride(D);
     h->use_mfma_score = D.dtype == kBF16 && (D.d == 64 || D.d == 128 || D.d == 256) && Q <= 128;
@@ -1380,3 +1384,23 @@ extern "C" int oasis_get_dims(const oasis_t *h, int32_t *k_blocks, int32_t *slot
 extern "C" int64_t oasis_tokens(const oasis_t *h) { return h ? h->T : OASIS_E_INVAL; }
 
 extern "C" hipStream_t oasis_copy_stream(const oasis_t *h) { return h ? h->copy : nullptr; }
+
+extern "C" int oasis_stream_create_cus(int32_t first_cu, int32_t n_cus, hipStream_t *out) {
+    if (!out) return OASIS_E_INVAL;
+    *out = nullptr;
+    Dims probe{};
+    const int ncu = compute_units(probe);
+    if (first_cu < 0 || n_cus < 1 || (int64_t)first_cu + n_cus > ncu) return OASIS_E_INVAL;
+    std::vector<uint32_t> mask((size_t)(ncu + 31) / 32, 0u);
+    for (int i = first_cu; i < first_cu + n_cus; ++i) mask[(size_t)i / 32] |= 1u << (i % 32);
+    if (hipExtStreamCreateWithCUMask(out, (uint32_t)mask.size(), mask.data()) != hipSuccess) {
+        *out = nullptr;
+        return OASIS_E_HIP;
+    }
+    return OASIS_OK;
+}
+
+extern "C" int oasis_stream_destroy(hipStream_t stream) {
+    if (!stream) return OASIS_E_INVAL;
+    return hipStreamDestroy(stream) == hipSuccess ? OASIS_OK : OASIS_E_HIP;
+}

@@ -910,10 +910,9 @@ AttnPlan plan_attention(const Dims &D) {
         // Balanced hit path: as many waves as the GPU holds at once, runs of
         // at most 64 entries (one list entry per lane).
         if (units <= kFlatMaxUnits && !getenv("OASIS_ATTN_SPLIT")) {
-            int dev = 0, cus = 0, per_cu = 0;
-            if (hipGetDevice(&dev) == hipSuccess &&
-                hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) ==
-                    hipSuccess) {
+            const int cus = compute_units(D);
+            int per_cu = 0;
+            {
                 const int u = (int)units;
                 switch (tile_rows(D.G)) {
                 case 1: per_cu = flat_wgs_per_cu<1>(u); break;

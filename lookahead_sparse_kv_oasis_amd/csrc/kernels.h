@@ -42,12 +42,30 @@ struct Dims {
     // Attended set: the selected blocks now held (false), or every block held
     // after the step (true; needs S <= K so the list fits K entries).
     bool attend_all = false;
+    // Compute units the handle's kernels may occupy (0: every CU of the
+    // current device).  Launches are sized to fill this many CUs: where the
+    // caller runs the handle on a stream limited to a subset of the CUs, a
+    // grid planned for the whole chip would leave part of each launch to a
+    // second round.
+    int cus = 0;
     int64_t units() const { return (int64_t)B * Hkv; }
     int esize() const { return dtype == kF32 ? 4 : 2; }
     int64_t block_elems() const { return 2LL * bs * d; }  // K and V of one block
     int64_t summ_tiles() const { return (NBmax + 31) / 32; }
     int64_t summ_unit_elems() const { return tiled ? summ_tiles() * 64LL * d : NBmax * 2LL * d; }
 };
+
+// Compute units a launch of the handle should fill (Dims::cus, else the
+// current device's count).
+inline int compute_units(const Dims &D) {
+    if (D.cus > 0) return D.cus;
+    int dev = 0, n = 0;
+    if (hipGetDevice(&dev) == hipSuccess &&
+        hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev) == hipSuccess &&
+        n > 0)
+        return n;
+    return 256;
+}
 
 // Element offset of dims [c, c + 8) of the maxima (half 0) or minima (half 1)
 // of block j in a unit's summary region (see Dims).
@@ -90,8 +108,8 @@ hipError_t launch_gather(const Dims &D, const void *host_kv, void *slots, const 
 // Top-K and diff / cap / LRU of every unit in one kernel (the ids are also
 // written to ids).
 // Score, top-K and select fused in one workgroup per unit (tiled bf16
-// summaries, d = 128, at least 256 units, NB <= 8192); score_topk_fusable
-// says whether a shape qualifies.
+// summaries, d = 128, at least as many units as compute units, NB <= 8192);
+// score_topk_fusable says whether a shape qualifies.
 bool score_topk_fusable(const Dims &D, int64_t NB, int n_rows);
 hipError_t launch_score_topk_select(const Dims &D, const void *summ, const void *q,
                                     const void *drafts, int n_drafts, int64_t NB, float *scores,

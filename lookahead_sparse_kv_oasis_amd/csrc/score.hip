@@ -162,8 +162,10 @@ hipError_t launch_score(const Dims &D, const void *summ, const void *q, const vo
     if (D.tiled) {
         const int QT = (Q + 31) / 32;
         const int64_t ntiles = (NB + 31) / 32;
-        // at least 256 workgroups, and at most 256 tiles (32 KB of scores) per workgroup
-        const int64_t want = (256 + D.units() - 1) / D.units();
+        // at least one workgroup per CU, and at most 256 tiles (32 KB of
+        // scores) per workgroup
+        const int cus = compute_units(D);
+        const int64_t want = (cus + D.units() - 1) / D.units();
         int64_t tpw = (ntiles + want - 1) / want;
         if (tpw > 256) tpw = 256;
         if (tpw < 1) tpw = 1;
@@ -173,9 +175,6 @@ hipError_t launch_score(const Dims &D, const void *summ, const void *q, const vo
         const uint16_t *s = (const uint16_t *)summ, *qq = (const uint16_t *)q,
                        *dr = (const uint16_t *)drafts;
         // the extra-tile buffer where each CU holds at most one workgroup
-        int dev = 0, cus = 256;
-        if (hipGetDevice(&dev) == hipSuccess)
-            (void)hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev);
         const bool xt = (int64_t)grid.x <= cus;
         if (D.d == 64)
             launch_tiled<64>(QT, xt, grid, lds, st, s, qq, dr, n_drafts, qskip, scores, D, NB,

@@ -948,7 +948,7 @@ static size_t fused_lds_bytes(const Dims &D, int64_t NB) {
 bool score_topk_fusable(const Dims &D, int64_t NB, int n_rows) {
     // one workgroup per unit must still fill the GPU, and the unit's scores
     // must fit in LDS next to the select's tables
-    return D.tiled && D.d == 128 && n_rows <= 128 && D.units() >= 256 && NB >= 1 &&
+    return D.tiled && D.d == 128 && n_rows <= 128 && D.units() >= compute_units(D) && NB >= 1 &&
            NB <= 8192 && fused_lds_bytes(D, NB) <= 64 * 1024;
 }
 
@@ -973,10 +973,7 @@ hipError_t launch_score_topk_select(const Dims &D, const void *summ, const void 
     // (51.6 against 53.6 us on the Qwen3-8B layer); with two or more per CU
     // every wave scores (10.30 against 10.83 ms per 36-layer step, where the
     // kernel shares the GPU with other layers' attention).
-    int dev = 0, cus = 256;
-    if (hipGetDevice(&dev) == hipSuccess)
-        (void)hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev);
-    const int nws = D.units() <= cus ? 4 : nt / 64;
+    const int nws = D.units() <= compute_units(D) ? 4 : nt / 64;
     const int C = (int)((NB + nt - 1) / nt);
     const bool xt = nws == 4 && QT == 1;  // one workgroup per CU
 #define OASIS_STS_X(QT_, CM_, NT_, XT_)                                                          \

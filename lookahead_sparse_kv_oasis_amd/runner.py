@@ -24,7 +24,7 @@ def to_device(a: np.ndarray, device="cuda") -> torch.Tensor:
 
 class LayerRunner:
     def __init__(self, w: synth.Workload, n_steps: int, layer: int = 0, device: str = "cuda",
-                 kv=None, cap: int | None = None):
+                 kv=None, cap: int | None = None, compute_units: int = 0):
         self.w, self.layer, self.n_steps = w, layer, n_steps
         self.T0 = w.prefix_tokens
         n_tok = w.prefix_tokens + n_steps
@@ -34,7 +34,8 @@ class LayerRunner:
         self.h = Oasis(w.batch, w.q_heads, w.kv_heads, w.head_dim,
                        OASIS_F32 if w.dtype == synth.F32 else OASIS_BF16, w.drafts, n_tok,
                        block_size=w.block_size, budget_tokens=w.budget_tokens,
-                       fetch_ratio=w.fetch_ratio, slots_per_head=w.n_slots)
+                       fetch_ratio=w.fetch_ratio, slots_per_head=w.n_slots,
+                       compute_units=compute_units)
         self.h.oasis_load_prefix(np.ascontiguousarray(K[:, :, :self.T0]),
                                  np.ascontiguousarray(V[:, :, :self.T0]), self.T0)
         # appended tokens, one [B][Hkv][d] slab per step
@@ -136,7 +137,8 @@ class ModelRunner:
     """
 
     def __init__(self, w: synth.Workload, n_steps: int, data_layers: int = 2,
-                 device: str = "cuda", cap: int | None = None, threads: int = 16, log=None):
+                 device: str = "cuda", cap: int | None = None, threads: int = 16, log=None,
+                 compute_units: int = 0):
         from . import LayerStep
         self.w, self.n_steps = w, n_steps
         self.n_layers = w.layers
@@ -149,7 +151,8 @@ class ModelRunner:
         mk = lambda owner=None: Oasis(w.batch, w.q_heads, w.kv_heads, w.head_dim, dt, w.drafts,
                                       n_tok, block_size=w.block_size,
                                       budget_tokens=w.budget_tokens, fetch_ratio=w.fetch_ratio,
-                                      slots_per_head=w.n_slots, share_host_with=owner)
+                                      slots_per_head=w.n_slots, share_host_with=owner,
+                                      compute_units=compute_units)
         self.handles = [None] * self.n_layers
         self.app_k, self.app_v, self.q, self.q_steps = [], [], [], []
         for g in range(self.H):
