@@ -302,10 +302,13 @@ def main():
         return
 
     if args.copy_cus > 0:
+        from lookahead_sparse_kv_oasis_amd import stream_destroy
         _partition(args.copy_cus)
         with torch.cuda.stream(_PART["compute"]):
             _run(args)
         torch.cuda.synchronize()
+        for k in ("compute", "side", "copy"):
+            stream_destroy(_PART[k].cuda_stream)
         return
     _run(args)
 
@@ -416,11 +419,19 @@ def bench_layer(args, w, steps, warmup, main_leg=True, shared=None):
     print(f"# setup {time.perf_counter() - t_setup:.1f}s: {w.name}, {n_steps} steps",
           file=sys.stderr, flush=True)
     rec = None
+    # lookahead order on a CU partition (--copy-cus): each select's blocks are
+    # copied on the copy stream while the next step runs on this one
+    beside = bool(_PART) and w.lookahead and args.correct_cap == 0
     if w.lookahead:
         # [OASIS] Fig. 8 ordering; the warmup steps also measure prediction recall
         rec = warmup_ahead_with_recall(run, warmup, stream, args.correct_cap)
         if args.correct_cap > 0:
             step = lambda t, st: run.step_corrected(t, args.correct_cap, st)
+        elif beside:
+            # the transfer on the copy stream's own CUs, beside the next
+            # step's scoring and attention over held blocks
+            h.oasis_set_attention_beside_copy(True)
+            step = lambda t, st: run.step_beside(t, st, _PART["copy"])
         else:
             step = run.step_ahead
     else:
@@ -438,7 +449,8 @@ def bench_layer(args, w, steps, warmup, main_leg=True, shared=None):
     # combine of its partials), sampled, to keep the step itself unperturbed
     h.oasis_set_timing(0 if args.no_kernel_timing else
                        TIME["score"] | TIME["attn"] | TIME["combine"] |
-                       (0 if stats0["fetch_fused"] and not correcting else TIME["gather"]))
+                       (0 if stats0["fetch_fused"] and not correcting and not beside
+                        else TIME["gather"]))
     h.oasis_set_timing_period(args.timing_period)
 
     torch.cuda.synchronize()
@@ -466,7 +478,9 @@ def bench_layer(args, w, steps, warmup, main_leg=True, shared=None):
     score_bytes = units * nb_avg * 2 * d * e + q_bytes * (1 + w.drafts) + units * nb_avg * 4
     attended = (stats1["attended"] - stats0["attended"]) / K
     fetched = (stats1["fetched"] - stats0["fetched"]) / K
-    attn_bytes = attended * blk_bytes + q_bytes + out_bytes
+    # with the copy beside, the timed attention launch reads the held blocks
+    # only (the fetched ones follow in a second, untimed launch)
+    attn_bytes = (attended - (fetched if beside else 0)) * blk_bytes + q_bytes + out_bytes
     base = {"metric": METRIC, "value": K / dt, "unit": "layer-steps/s", "n_gpus": 1,
             "steps": K, "warmup": warmup, "ms_per_step": dt / K * 1e3,
             "higher_is_better": True, "scaling": "weak", "vs_baseline": None,
@@ -492,7 +506,7 @@ def bench_layer(args, w, steps, warmup, main_leg=True, shared=None):
     hbm_gbps = (score_bytes + attn_bytes) / ((ms_score + ms_attn + ms_comb) * 1e-3) / 1e9
     # the fetch runs inside the next attention, in the lookahead order too
     # (the append before it leaves it pending)
-    fused = bool(stats1["fetch_fused"]) and not correcting
+    fused = bool(stats1["fetch_fused"]) and not correcting and not beside
     # with the fetch fused into the attention kernel the host-link transfer
     # runs inside it: its rate is bounded below by bytes / attention time.
     # With miss correction the corrective fetch runs inside the attention and
@@ -536,7 +550,8 @@ def bench_layer(args, w, steps, warmup, main_leg=True, shared=None):
                       "fetch_inside": fetch_in_attn},
         "host_link": {"kernel": "oasis_sparse_attn (fused fetch)" if fused else
                       "oasis_sparse_attn (corrective fetch) + oasis_gather (prefetch)"
-                      if correcting else "oasis_gather",
+                      if correcting else "oasis_gather (copy stream, CUs of its own)"
+                      if beside else "oasis_gather",
                       "achieved_gbps": gather_gbps, "pinned_h2d_peak_gbps": h2d,
                       "frac": frac_of(gather_gbps, h2d),
                       "pcie_gen5_x16_gbps": PCIE_GEN5_X16_GBPS,

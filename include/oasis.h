@@ -179,8 +179,9 @@ int oasis_topk_from_scores(oasis_t *h, const float *scores_dev, int32_t *block_i
  * copy: the stream of the host -> HBM block copies (OasisKV Fig. 8: the
  * transfer on a stream of its own).  A stream: the gather kernel copies the
  * fetched blocks there right after the table update (it waits for `stream`),
- * and the next call that reads the slots (attention, append, select, evict)
- * waits for it.  OASIS_COPY_DEFAULT: the handle's own placement, by default
+ * and the next call that reads the slots (attention, select, evict, verify)
+ * waits for it; the copy takes the rows of the tokens held now, so an append
+ * (which writes the next token's row) runs beside it.  OASIS_COPY_DEFAULT: the handle's own placement, by default
  * inside the next oasis_sparse_attn's kernel (bf16, d = 128, block 16:
  * fetch waves read the host blocks while the other workgroups attend to the
  * hits, which measured faster than a separate copy the attention waits for),
@@ -446,6 +447,16 @@ int oasis_set_score_topk_fusion(oasis_t *h, int32_t on);
  * before the switch (synchronous).  OASIS_E_INVAL when on is asked for
  * another layout. */
 int oasis_set_fetch_in_attention(oasis_t *h, int32_t on);
+
+/* on != 0: when the last oasis_select_and_fetch copied its blocks on a copy
+ * stream other than the stream of the next oasis_sparse_attn (and the
+ * layout is bf16, d = 128, block 16), that attention starts on the blocks
+ * held before the select while the copy runs and waits for the copy only
+ * before the fetched blocks (two launches, then the combine), so the copy
+ * overlaps the attention instead of preceding it (OasisKV Fig. 8: the
+ * transfer beside the compute).  The output equals the one-launch form's up
+ * to the order of the floating-point sums.  Default off. */
+int oasis_set_attention_beside_copy(oasis_t *h, int32_t on);
 
 /* Shape of a handle: K (top-K blocks), S (slots), NBmax, block size. */
 int oasis_get_dims(const oasis_t *h, int32_t *k_blocks, int32_t *slots, int64_t *nb_max,

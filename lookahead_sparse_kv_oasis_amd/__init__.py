@@ -35,7 +35,9 @@ EXPORTS = [
     "oasis_evict", "oasis_evict_attended", "oasis_get_state", "oasis_sparse_attn",
     "oasis_sparse_attn_noalloc", "oasis_sparse_attn_verify", "oasis_buffer_bytes", "oasis_read", "oasis_get_stats",
     "oasis_check", "oasis_set_timing", "oasis_set_timing_period",
-    "oasis_set_score_topk_fusion", "oasis_set_fetch_in_attention", "oasis_set_attend_all_resident", "oasis_get_timing", "oasis_get_dims", "oasis_tokens",
+    "oasis_set_score_topk_fusion", "oasis_set_fetch_in_attention",
+    "oasis_set_attention_beside_copy", "oasis_set_attend_all_resident", "oasis_get_timing",
+    "oasis_get_dims", "oasis_tokens",
     "oasis_copy_stream", "oasis_stream_create_cus", "oasis_stream_destroy",
     "oasis_stream_read", "oasis_kv_bytes_per_token", "oasis_cap_from_ratio",
     "oasis_strerror",
@@ -126,6 +128,7 @@ def lib():
             "oasis_set_timing_period": (ctypes.c_int, [H, i32]),
             "oasis_set_score_topk_fusion": (ctypes.c_int, [H, i32]),
             "oasis_set_fetch_in_attention": (ctypes.c_int, [H, i32]),
+            "oasis_set_attention_beside_copy": (ctypes.c_int, [H, i32]),
             "oasis_set_attend_all_resident": (ctypes.c_int, [H, i32]),
             "oasis_get_timing": (ctypes.c_int, [H, ctypes.POINTER(oasis_timing)]),
             "oasis_get_dims": (ctypes.c_int, [H, ctypes.POINTER(i32), ctypes.POINTER(i32),
@@ -351,6 +354,11 @@ class Oasis:
         gather kernel on the copy stream right after the select (False)."""
         self._check(lib().oasis_set_fetch_in_attention(self.h, int(bool(on))),
                     "oasis_set_fetch_in_attention")
+
+    def oasis_set_attention_beside_copy(self, on: bool):
+        """Attend to the held blocks while a copy on another stream runs."""
+        self._check(lib().oasis_set_attention_beside_copy(self.h, int(bool(on))),
+                    "oasis_set_attention_beside_copy")
 
     def oasis_set_score_topk_fusion(self, on: bool):
         """Fuse score, top-K and select into one kernel (when the shape allows)."""

@@ -104,6 +104,12 @@ struct oasis_handle {
     const void *score_q = nullptr, *score_drafts = nullptr;
     int score_nd = 0;
     int last_cap = 0;
+    // The last select's blocks are being copied by a gather on another
+    // stream (m_gather) that no attention has waited for yet; with
+    // split_beside_copy the next attention attends to the other blocks
+    // before it waits for that copy.
+    bool copy_open = false;
+    bool split_beside_copy = false;
 
     std::shared_ptr<HostKV> hkv;
     void *host_kv = nullptr;      // host pointer (pinned), hkv->host
@@ -340,6 +346,7 @@ int reset_tables(oasis_t *h) {
     h->fetch_pending = false;
     h->topk_pending = false;
     h->score_pending = false;
+    h->copy_open = false;
     return OASIS_OK;
 }
 
@@ -394,7 +401,7 @@ int flush_fetch(oasis_t *h, hipStream_t st) {
     h->fetch_pending = false;
     LAUNCH(h, TM_GATHER, st,
            launch_gather(h->D, h->host_kv_dev, h->slots, h->fetch_block, h->fetch_slot, h->D.K,
-                         h->counts, 4, 2, h->last_cap, st));
+                         h->counts, 4, 2, h->last_cap, h->T, st));
     return OASIS_OK;
 }
 
@@ -697,6 +704,7 @@ extern "C" int oasis_set_state(oasis_t *h, const int32_t *slot_block_host,
         maxn = std::max(maxn, n);
     }
     h->fetch_pending = false;   // the tables are replaced wholesale
+    h->copy_open = false;
     HIP_OK(h, hipDeviceSynchronize());
     HIP_OK(h, hipMemcpy(h->slot_block, slot_block_host, sizeof(int32_t) * units * D.S,
                         hipMemcpyHostToDevice));
@@ -708,7 +716,8 @@ extern "C" int oasis_set_state(oasis_t *h, const int32_t *slot_block_host,
     if (hipMemcpy(dlb, lb.data(), sizeof(int32_t) * lb.size(), hipMemcpyHostToDevice) != hipSuccess ||
         hipMemcpy(dls, ls.data(), sizeof(int32_t) * ls.size(), hipMemcpyHostToDevice) != hipSuccess ||
         hipMemcpy(dcnt, cnt.data(), sizeof(int32_t) * cnt.size(), hipMemcpyHostToDevice) != hipSuccess ||
-        launch_gather(D, h->host_kv_dev, h->slots, dlb, dls, D.S, dcnt, 1, 0, maxn, h->copy) !=
+        launch_gather(D, h->host_kv_dev, h->slots, dlb, dls, D.S, dcnt, 1, 0, maxn, h->T,
+                      h->copy) !=
             hipSuccess ||
         hipStreamSynchronize(h->copy) != hipSuccess)
         rc = fail(h, OASIS_E_HIP, "set_state upload or payload copy failed");
@@ -726,15 +735,18 @@ extern "C" int oasis_append_kv(oasis_t *h, const void *k_dev, const void *v_dev,
         return fail(h, OASIS_E_CAPACITY, "append: sequence already holds max_tokens = %lld",
                     (long long)h->L.max_tokens);
     TRY(use_stream(h, stream));
-    TRY(after(h, stream, h->m_gather));
     TRY(after(h, stream, h->m_attn));
     TRY(after(h, stream, h->m_select));  // and the score the select ranked
-    // A fetch left pending by the last select stays pending: it copies whole
-    // host blocks later on this stream, after this token is in the host KV, so
-    // a fetched block's slot ends up with the token whether or not the write-
-    // through below reaches it first.  In the lookahead order (append, attend,
-    // predict, select) the next attention thus streams its hits from HBM
-    // while its fetch waves read the host link.
+    // No wait for a gather still copying the last select's blocks on another
+    // stream: it copies the rows of the tokens held at that select only, and
+    // this token's row is written here (into the host KV, and into the slot,
+    // the block being resident since the select), so the two touch disjoint
+    // bytes.  A fetch left pending by the last select stays pending: it
+    // copies the host blocks later on this stream, after this token is in
+    // the host KV, so a fetched block's slot ends up with the token whether
+    // or not the write-through below reaches it first.  In the lookahead
+    // order (append, attend, predict, select) the next attention thus
+    // streams its hits from HBM while its fetch waves read the host link.
     TRY(flush_score(h, stream));  // a deferred predict scores the summaries before this token
     TRY(after_predict(h, stream));  // a score on another stream may still read the summaries
     LAUNCH(h, TM_APPEND, stream,
@@ -861,6 +873,7 @@ int select_impl(oasis_t *h, int32_t cap, hipStream_t stream, bool eager, hipStre
     // predict's kernels.
     h->pred_open = false;
     TRY(mark(h, h->m_select, stream));
+    h->copy_open = false;
     if (h->fused && !eager) {
         h->fetch_pending = cap > 0;
     } else if (cap > 0) {
@@ -869,8 +882,9 @@ int select_impl(oasis_t *h, int32_t cap, hipStream_t stream, bool eager, hipStre
         TRY(after(h, g, h->m_select));
         LAUNCH(h, TM_GATHER, g,
                launch_gather(D, h->host_kv_dev, h->slots, h->fetch_block, h->fetch_slot, D.K,
-                             h->counts, 4, 2, cap, g));
+                             h->counts, 4, 2, cap, h->T, g));
         TRY(mark(h, h->m_gather, g));
+        h->copy_open = true;
     }
     ++h->n_select;
     h->selected = true;
@@ -941,12 +955,35 @@ extern "C" int oasis_sparse_attn(oasis_t *h, const void *q_dev, float *out_dev,
     const Dims &D = h->D;
     TRY(use_stream(h, stream));
     TRY(after(h, stream, h->m_select));
-    TRY(after(h, stream, h->m_gather));
     // the last append: its write-through into resident slots, and the host
     // token a pending fetch copies
     TRY(after(h, stream, h->m_append));
     // the previous attention: the same partials, and the slots its fetch wrote
     TRY(after(h, stream, h->m_attn));
+    const bool split = h->split_beside_copy && h->copy_open && h->m_gather.set &&
+                       h->m_gather.st != stream && h->plan.mfma && h->plan.flat &&
+                       h->last_cap > 0 && !h->fetch_pending;
+    h->copy_open = false;
+    if (split) {
+        // the blocks held before the select while the copy runs, the fetched
+        // ones from their slots once it has landed (their partials in the
+        // fetch splits, as the fused form writes them)
+        const int nsf = attention_fetch_splits(D, h->plan, h->last_cap);
+        LAUNCH(h, TM_ATTN, stream,
+               launch_attention(D, h->plan, 2, nsf, q_dev, h->slots, h->host_kv_dev,
+                                h->att_block, h->att_slot, h->counts, h->T, h->part_m,
+                                h->part_l, h->part_acc, stream));
+        TRY(after(h, stream, h->m_gather));
+        HIP_OK(h, launch_attention(D, h->plan, 3, nsf, q_dev, h->slots, h->host_kv_dev,
+                                   h->att_block, h->att_slot, h->counts, h->T, h->part_m,
+                                   h->part_l, h->part_acc, stream));
+        LAUNCH(h, TM_COMBINE, stream,
+               launch_combine(D, h->plan, nsf, h->part_m, h->part_l, h->part_acc, out_dev,
+                              stream));
+        TRY(mark(h, h->m_attn, stream));
+        return OASIS_OK;
+    }
+    TRY(after(h, stream, h->m_gather));
     int mode = 0, nsf = 0;
     if (h->fetch_pending) {
         if (h->plan.mfma) {
@@ -1334,6 +1371,12 @@ extern "C" int oasis_set_fetch_in_attention(oasis_t *h, int32_t on) {
         HIP_OK(h, hipStreamSynchronize(h->copy));
     }
     h->fused = on != 0;
+    return OASIS_OK;
+}
+
+extern "C" int oasis_set_attention_beside_copy(oasis_t *h, int32_t on) {
+    if (!h) return OASIS_E_INVAL;
+    h->split_beside_copy = on != 0;
     return OASIS_OK;
 }
 

@@ -173,12 +173,17 @@ template <int G> struct AttnWave {
 #pragma unroll
         for (int r = 0; r < 4; ++r) vv[r] = gload16_nt(p + voff + r * D);
     }
-    __device__ __forceinline__ void store(uint16_t *p, const uint4 (&kk)[4],
-                                          const uint4 (&vv)[4]) const {
+    // Into a slot, the rows of the `valid` tokens only (K row col, V rows
+    // 4 kg + r of this lane): rows past them are left as they are.
+    __device__ __forceinline__ void store(uint16_t *p, const uint4 (&kk)[4], const uint4 (&vv)[4],
+                                          int valid) const {
+        if (col < valid) {
 #pragma unroll
-        for (int c = 0; c < 4; ++c) gstore16(p + koff + 32 * c, kk[c]);
+            for (int c = 0; c < 4; ++c) gstore16(p + koff + 32 * c, kk[c]);
+        }
 #pragma unroll
-        for (int r = 0; r < 4; ++r) gstore16(p + voff + r * D, vv[r]);
+        for (int r = 0; r < 4; ++r)
+            if (4 * kg + r < valid) gstore16(p + voff + r * D, vv[r]);
     }
     // Online-softmax update with one block of `valid` tokens.
     __device__ __forceinline__ void block(const uint4 (&kk)[4], const uint4 (&vv)[4], int valid,
@@ -339,12 +344,17 @@ template <int G> struct AttnWaveM {
 #pragma unroll
         for (int r = 0; r < 4; ++r) vv[r] = gload16_nt(p + voff + r * D);
     }
-    __device__ __forceinline__ void store(uint16_t *p, const uint4 (&kk)[4],
-                                          const uint4 (&vv)[4]) const {
+    // Into a slot, the rows of the `valid` tokens only (K row col, V rows
+    // 4 kg + r of this lane): rows past them are left as they are.
+    __device__ __forceinline__ void store(uint16_t *p, const uint4 (&kk)[4], const uint4 (&vv)[4],
+                                          int valid) const {
+        if (col < valid) {
 #pragma unroll
-        for (int c = 0; c < 4; ++c) gstore16(p + koff + 32 * c, kk[c]);
+            for (int c = 0; c < 4; ++c) gstore16(p + koff + 32 * c, kk[c]);
+        }
 #pragma unroll
-        for (int r = 0; r < 4; ++r) gstore16(p + voff + r * D, vv[r]);
+        for (int r = 0; r < 4; ++r)
+            if (4 * kg + r < valid) gstore16(p + voff + r * D, vv[r]);
     }
     __device__ __forceinline__ void block(const uint4 (&kk)[4], const uint4 (&vv)[4], int valid,
                                           float scale_log2) {
@@ -476,7 +486,7 @@ __device__ __forceinline__ void fetch_waves(
     const int32_t *__restrict__ att_slot, const int32_t *__restrict__ counts, int64_t T_, int Hq,
     int Hkv, int K, int S, int64_t NBmax, int cap, int n_fetch_wg, int nsa, int64_t units,
     float scale_log2, float *__restrict__ part_m, float *__restrict__ part_l,
-    float *__restrict__ part_acc) {
+    float *__restrict__ part_acc, bool from_slots = false) {
     const int lane = threadIdx.x & 63;
     const int64_t F = 4LL * n_fetch_wg;
     const int64_t n_items = units * cap;
@@ -509,10 +519,12 @@ __device__ __forceinline__ void fetch_waves(
         if (mask == 0) continue;
         auto src = [&](int l) {
             const int ul = rl(u, l);
-            return host_kv + ((int64_t)ul * NBmax + rl(blk, l)) * W::BLK;
+            return from_slots ? slots + ((int64_t)ul * S + rl(slot, l)) * (int64_t)W::BLK
+                              : host_kv + ((int64_t)ul * NBmax + rl(blk, l)) * W::BLK;
         };
         // lane l's item: read it from the host, store it into its slot,
-        // attend, write partial i of its unit
+        // attend, write partial i of its unit (from_slots: the block is in
+        // its slot already, copied there by a gather)
         for (uint64_t m = mask; m; m &= m - 1) {
             const int l = __builtin_ctzll(m);
             const int ul = rl(u, l);
@@ -520,8 +532,11 @@ __device__ __forceinline__ void fetch_waves(
             st.load_q(st.qb, qr, ul / Hkv, ul % Hkv);
             st.load(kk, vv, src(l));
             st.reset();
-            st.block(kk, vv, block_valid(T_, rl(blk, l)), scale_log2);
-            st.store(slots + ((int64_t)ul * S + rl(slot, l)) * (int64_t)W::BLK, kk, vv);
+            const int valid = block_valid(T_, rl(blk, l));
+            st.block(kk, vv, valid, scale_log2);
+            if (!from_slots)
+                st.store(slots + ((int64_t)ul * S + rl(slot, l)) * (int64_t)W::BLK, kk, vv,
+                         valid);
             st.reduce();
             st.write_partial(((int64_t)ul * nsa + rl(i, l)) * G, part_m, part_l, part_acc);
         }
@@ -639,7 +654,7 @@ __device__ __forceinline__ void hit_prefix(const int32_t *__restrict__ counts, i
     const int hi = lo + chunk < units ? lo + chunk : units;
     int sum = 0;
     for (int u = lo; u < hi; ++u) {
-        const int e = counts[u * 4 + 0] - (mode == 1 ? counts[u * 4 + 2] : 0);
+        const int e = counts[u * 4 + 0] - (mode != 0 ? counts[u * 4 + 2] : 0);
         pre[u + 1] = e;
         sum += e;
     }
@@ -676,9 +691,12 @@ __device__ __forceinline__ void hit_prefix(const int32_t *__restrict__ counts, i
 // rank among the waves of u (at most R = ceil(K / pmin) + 1 of them); the
 // unit's last wave marks rows s + 1 .. R - 1 empty (m = -inf), and units
 // without hit entries are marked by workgroup u mod the grid, so the
-// combine reads a fixed set of rows with no dependent load.  Fetch
-// workgroups (mode 1) come first in the grid, as in the split kernel.
-// Dynamic LDS: units + 1 ints.
+// combine reads a fixed set of rows with no dependent load.  Modes: 0, the
+// hit waves over every attended entry; 1, fetch workgroups first in the grid
+// (host reads, as in the split kernel), hit waves over the entries before
+// the fetched ones; 2, those hit waves alone; 3, fetch workgroups alone,
+// reading the fetched blocks from their slots (a gather on another stream
+// copied them while a mode-2 launch ran).  Dynamic LDS: units + 1 ints.
 template <int G>
 __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2))) void attn_flat_kernel(
     const QRows qr, uint16_t *__restrict__ slots, const uint16_t *__restrict__ host_kv, const int32_t *__restrict__ att_block,
@@ -699,7 +717,7 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2))) void a
     if ((int)blockIdx.x < n_fetch_wg) {
         fetch_waves<G>(st, wave, qr, slots, host_kv, att_block, att_slot, counts, T_, Hq, Hkv, K,
                        S, NBmax, cap, n_fetch_wg, nsa, (int64_t)units, scale_log2, part_m,
-                       part_l, part_acc);
+                       part_l, part_acc, mode == 3);
         return;
     }
     hit_prefix(counts, units, mode, pre, red);
@@ -1059,8 +1077,18 @@ hipError_t launch_attention(const Dims &D, const AttnPlan &P, int mode, int nsf,
     const QRows qq = qrows ? *qrows : QRows{(const uint16_t *)q, nullptr, 0, D.Hq, D.G, 0, D.G};
     if (P.mfma && P.flat) {
         if (mode == 0) nsf = 0;
-        const int n_fetch_wg = nsf > 0 ? fetch_workgroups(D.units() * nsf) : 0;
-        const int hw = flat_hit_waves(D, P, nsf);
+        int n_fetch_wg = 0, hw = 0;
+        if (mode == 3) {
+            // the fetched blocks from HBM: a wave per block, up to 8 per CU
+            if (nsf <= 0) return hipSuccess;
+            const int64_t waves = std::min<int64_t>(D.units() * nsf, 8LL * compute_units(D));
+            n_fetch_wg = (int)((waves + 3) / 4);
+        } else if (mode == 2) {
+            hw = P.flat_waves;
+        } else {
+            n_fetch_wg = nsf > 0 ? fetch_workgroups(D.units() * nsf) : 0;
+            hw = flat_hit_waves(D, P, nsf);
+        }
         const dim3 grid((unsigned)(n_fetch_wg + hw / 4));
         const size_t lds = sizeof(int32_t) * (D.units() + 1);
         const uint16_t *hk = (const uint16_t *)host_kv;

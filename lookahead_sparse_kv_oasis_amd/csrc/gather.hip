@@ -21,6 +21,12 @@
 // flight without branches copied no faster alone and made the 36-layer
 // lookahead step slower (10.5 -> 11.8 ms): its copies pressed harder on the
 // HBM-bound kernels running beside them.
+//
+// Only the tokens the sequences hold when the list is copied (T) are copied:
+// rows at or past T of the last, partial block stay as they are in the slot.
+// An append running beside the copy (on another stream) writes token T into
+// the host KV and, the block being resident by then, into its slot; the two
+// never touch the same bytes, so the append need not wait for the copy.
 #include "kernels.h"
 
 namespace oasis {
@@ -34,14 +40,23 @@ struct GatherCursor {
     u32x4 *dst;
     int64_t item;
     int c0;
+    int valid_vec;  // vectors of the K (and of the V) half that hold tokens < T
 };
+
+// Vector c of a block (K half, then V half of block_vec / 2 vectors each) is
+// copied when it lies in a row of a token < T.
+__device__ __forceinline__ bool vec_copied(int c, const GatherCursor &g, int block_vec) {
+    const int half = block_vec >> 1;
+    const int cc = c >= half ? c - half : c;
+    return c < block_vec && cc < g.valid_vec;
+}
 
 __device__ __forceinline__ void load_chunk(u32x4 (&r)[8], const GatherCursor &g, int block_vec,
                                            int lane) {
 #pragma unroll
     for (int k = 0; k < 8; ++k) {
         const int c = g.c0 + k * 64 + lane;
-        if (c < block_vec) r[k] = __builtin_nontemporal_load(g.src + c);
+        if (vec_copied(c, g, block_vec)) r[k] = __builtin_nontemporal_load(g.src + c);
     }
 }
 
@@ -50,7 +65,7 @@ __device__ __forceinline__ void store_chunk(const u32x4 (&r)[8], const GatherCur
 #pragma unroll
     for (int k = 0; k < 8; ++k) {
         const int c = g.c0 + k * 64 + lane;
-        if (c < block_vec) g.dst[c] = r[k];
+        if (vec_copied(c, g, block_vec)) g.dst[c] = r[k];
     }
 }
 
@@ -64,7 +79,8 @@ __global__ __launch_bounds__(256) void gather_kernel(const u32x4 *__restrict__ h
                                                      const int32_t *__restrict__ counts,
                                                      int count_stride, int count_index,
                                                      int64_t NBmax, int S, int block_vec,
-                                                     int max_n, int64_t units) {
+                                                     int max_n, int64_t units, int64_t T,
+                                                     int bs) {
     const int lane = threadIdx.x & 63;
     const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
     const int64_t W = (int64_t)gridDim.x * 4;
@@ -83,6 +99,8 @@ __global__ __launch_bounds__(256) void gather_kernel(const u32x4 *__restrict__ h
             g.dst = slots + (u * S + s) * (int64_t)block_vec;
             g.item = item;
             g.c0 = 0;
+            const int64_t rows = T - (int64_t)blk * bs;
+            g.valid_vec = (int)(rows < bs ? rows : bs) * (block_vec / (2 * bs));
             return true;
         }
         return false;
@@ -119,7 +137,8 @@ __global__ __launch_bounds__(256) void gather_kernel(const u32x4 *__restrict__ h
 
 hipError_t launch_gather(const Dims &D, const void *host_kv, void *slots, const int32_t *blocks,
                          const int32_t *slot_ids, int list_stride, const int32_t *counts,
-                         int count_stride, int count_index, int max_n, hipStream_t st) {
+                         int count_stride, int count_index, int max_n, int64_t T,
+                         hipStream_t st) {
     if (max_n <= 0) return hipSuccess;
     const int block_vec = (int)(D.block_elems() * D.esize() / 16);
     const int64_t items = D.units() * max_n;
@@ -128,7 +147,7 @@ hipError_t launch_gather(const Dims &D, const void *host_kv, void *slots, const 
     const dim3 grid((unsigned)((waves + 3) / 4));
     OASIS_LAUNCH(gather_kernel, grid, dim3(256), 0, st, (const u32x4 *)host_kv, (u32x4 *)slots,
                  blocks, slot_ids, list_stride, counts, count_stride, count_index, D.NBmax, D.S,
-                 block_vec, max_n, D.units());
+                 block_vec, max_n, D.units(), T, D.bs);
     return hipGetLastError();
 }
 

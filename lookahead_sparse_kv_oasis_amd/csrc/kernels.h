@@ -98,12 +98,13 @@ hipError_t launch_select(const Dims &D, const int32_t *ids, int32_t *slot_block,
                          int32_t *att_slot, int32_t *counts, DevStats *stats, uint32_t *err,
                          hipStream_t st);
 
-// Copy listed blocks from the host KV into their slots.  Unit u copies
-// n = counts[u * count_stride + count_index] entries of
-// (blocks, slots)[u * list_stride ...].  max_n bounds n for the grid.
+// Copy listed blocks from the host KV into their slots, the rows of tokens
+// < T only.  Unit u copies n = counts[u * count_stride + count_index] entries
+// of (blocks, slots)[u * list_stride ...].  max_n bounds n for the grid.
 hipError_t launch_gather(const Dims &D, const void *host_kv, void *slots, const int32_t *blocks,
                          const int32_t *slot_ids, int list_stride, const int32_t *counts,
-                         int count_stride, int count_index, int max_n, hipStream_t st);
+                         int count_stride, int count_index, int max_n, int64_t T,
+                         hipStream_t st);
 
 // Top-K and diff / cap / LRU of every unit in one kernel (the ids are also
 // written to ids).
@@ -184,8 +185,12 @@ struct QRows {
 };
 // mode 0: every attended entry from its slot.  mode 1 (MFMA only): entries
 // [n_hit, n_att) are read from the host KV and written into their slots in
-// the same kernel, using nsf fetch splits.  launch_combine merges the
-// partials into the output.  qr (MFMA only; null: the rows of q) gives the
+// the same kernel, using nsf fetch splits.  Balanced plans only: mode 2, the
+// entries [0, n_hit) alone; mode 3, entries [n_hit, n_att) alone, from their
+// slots (into the nsf fetch splits, as mode 1 writes them), so that a mode-2
+// launch can run while a gather on another stream fills the slots and a
+// mode-3 launch after it.  launch_combine merges the partials into the
+// output.  qr (MFMA only; null: the rows of q) gives the
 // query rows of a verification pass.
 hipError_t launch_attention(const Dims &D, const AttnPlan &P, int mode, int nsf, const void *q,
                             void *slots, const void *host_kv, const int32_t *att_block,

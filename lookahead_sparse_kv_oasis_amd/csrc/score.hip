@@ -163,9 +163,14 @@ hipError_t launch_score(const Dims &D, const void *summ, const void *q, const vo
         const int QT = (Q + 31) / 32;
         const int64_t ntiles = (NB + 31) / 32;
         // at least one workgroup per CU, and at most 256 tiles (32 KB of
-        // scores) per workgroup
+        // scores) per workgroup.  Where the workgroups do not spread evenly
+        // over the CUs (a CU subset of 240 for 256 units), at least four per
+        // unit, so that CUs that finish early take more: one per unit left
+        // 16 CUs with two and took 56.7 us on the Qwen3-8B layer, four per
+        // unit 45.9 us (42.1 us on all 256 CUs).
         const int cus = compute_units(D);
-        const int64_t want = (cus + D.units() - 1) / D.units();
+        int64_t want = (cus + D.units() - 1) / D.units();
+        if ((D.units() * want) % cus != 0 && want < 4) want = 4;
         int64_t tpw = (ntiles + want - 1) / want;
         if (tpw > 256) tpw = 256;
         if (tpw < 1) tpw = 1;

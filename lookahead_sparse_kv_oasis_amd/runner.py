@@ -106,6 +106,27 @@ class LayerRunner:
         h.oasis_select_and_fetch(self.cap if cap is None else cap, stream=stream)
         self.t = t
 
+    def admission_beside(self, stream, copy):
+        """admission_ahead with the copy on its own stream."""
+        h = self.h
+        h.oasis_set_attention_beside_copy(True)
+        h.oasis_predict(None, self.drafts[0], self.w.drafts, stream=stream)
+        h.oasis_select_and_fetch(self.w.k_blocks, stream=stream, copy=copy)
+
+    def step_beside(self, t: int, stream, copy, cap: int | None = None):
+        """Lookahead step with the transfer on a copy stream of its own
+        ([OASIS] Fig. 8): append token T0 + t - 1, score the step-t drafts,
+        attend with the step-t query (the blocks held before the last select
+        while the copy of its fetched blocks runs, those once it has landed),
+        then select step t+1's set, whose copy starts on `copy`.  The scoring
+        and the attention over held blocks hide the transfer."""
+        h = self.h
+        h.oasis_append_kv(self.app_k[t - 1], self.app_v[t - 1], stream=stream)
+        h.oasis_predict(None, self.drafts[t], self.w.drafts, stream=stream)
+        h.oasis_sparse_attn(self.q_steps[t], self.out, stream=stream)
+        h.oasis_select_and_fetch(self.cap if cap is None else cap, stream=stream, copy=copy)
+        self.t = t
+
     def step_corrected(self, t: int, cap_correct: int, stream=None, cap: int | None = None):
         """Lookahead step with decode-time miss correction: append; the step-t
         query's own top-K selected with cap_correct (missed blocks fetched

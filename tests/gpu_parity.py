@@ -79,26 +79,26 @@ def score_scale(unit: oracle.Unit, x_rows: np.ndarray) -> np.ndarray:
 
 
 def slot_payload_expected(keys, vals, blk, T, bs, dtype):
-    """Bytes a slot holding block blk must contain: valid rows, zeros past T."""
-    d = keys.shape[1]
-    dt = np.float32 if dtype == synth.F32 else np.uint16
-    out = np.zeros((2, bs, d), dt)
+    """Rows a slot holding block blk must contain: the K and V rows of its
+    tokens < T ([2][n][d]).  Rows of tokens not yet appended are never read
+    (the attention bounds every block by T) and copies leave them as they
+    are, so they are not compared."""
     p0 = blk * bs
     n = max(0, min(bs, T - p0))
-    out[0, :n] = keys[p0:p0 + n]
-    out[1, :n] = vals[p0:p0 + n]
-    return out
+    dt = np.float32 if dtype == synth.F32 else np.uint16
+    return np.stack([keys[p0:p0 + n], vals[p0:p0 + n]]).astype(dt, copy=False)
 
 
 class Parity:
     """GPU runner + oracle units for a sample of (b, h) units of a workload."""
 
-    def __init__(self, w: synth.Workload, n_steps: int, units, layer: int = 0):
+    def __init__(self, w: synth.Workload, n_steps: int, units, layer: int = 0,
+                 compute_units: int = 0):
         self.w, self.n_steps, self.units, self.layer = w, n_steps, list(units), layer
         n_tok = w.prefix_tokens + n_steps
         K, V = synth.layer_kv(w, n_tok, layer)
         self.K, self.V = K, V
-        self.run = LayerRunner(w, n_steps, layer, kv=(K, V))
+        self.run = LayerRunner(w, n_steps, layer, kv=(K, V), compute_units=compute_units)
         self.cap = workload_cap(w)
         mk = lambda k: initial_unit(w, k[0], k[1], n_steps, layer, kv=(K[k[0], k[1]], V[k[0], k[1]]))
         self.oru = dict(zip(self.units, pool().map(mk, self.units)))
@@ -192,7 +192,7 @@ class Parity:
                 if usb[s] < 0:
                     continue
                 exp = slot_payload_expected(self.K[b, hh], self.V[b, hh], usb[s], T, bs, w.dtype)
-                assert np.array_equal(got[s], exp), \
+                assert np.array_equal(got[s][:, :exp.shape[1]], exp), \
                     f"step {t} unit {(b, hh)} slot {s} block {usb[s]} payload differs"
 
     def check_out(self, t, rec):
@@ -521,7 +521,10 @@ class AheadRunning(FreeRunning):
         report["steps"] = t
         return now, att_now
 
-    def run_ahead(self, steps=None, check_payload_every=4):
+    def run_ahead(self, steps=None, check_payload_every=4, beside=None):
+        """beside = (stream, copy): the runner's step_beside, the copy of each
+        select's blocks on `copy` while the next step scores and attends on
+        `stream`."""
         w, run = self.w, self.run
         steps = self.n_steps if steps is None else steps
         report = dict(score_err=0.0, attn_err=0.0, steps=0, fetched=0)
@@ -529,11 +532,18 @@ class AheadRunning(FreeRunning):
                  for k in self.units}
         for k in self.units:
             self.oru[k].slot_block[:] = -1
-        run.admission_ahead()
+        if beside is None:
+            run.admission_ahead()
+        else:
+            torch.cuda.synchronize()  # inputs were made on torch's stream
+            run.admission_beside(*beside)
         torch.cuda.synchronize()
         prev, att = self.verify_ahead(0, empty, None, report, w.k_blocks)
         for t in range(1, steps + 1):
-            run.step_ahead(t)
+            if beside is None:
+                run.step_ahead(t)
+            else:
+                run.step_beside(t, *beside)
             torch.cuda.synchronize()
             run.h.oasis_check()
             prev, att = self.verify_ahead(t, prev, att, report, self.cap,

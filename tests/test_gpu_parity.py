@@ -256,6 +256,84 @@ def test_lookahead_append_into_a_block_whose_fetch_is_pending():
     assert rep["fetched"] > 0
 
 
+@pytest.fixture
+def cu_streams():
+    """A compute stream on all CUs but the first 16 and a copy stream on those
+    16 (oasis_stream_create_cus), and the compute stream's CU count."""
+    import lookahead_sparse_kv_oasis_amd as L
+    ncu = torch.cuda.get_device_properties(0).multi_processor_count
+    n_copy = 16
+    raw = [L.stream_create_cus(n_copy, ncu - n_copy), L.stream_create_cus(0, n_copy)]
+    yield ncu - n_copy, torch.cuda.ExternalStream(raw[0]), torch.cuda.ExternalStream(raw[1])
+    torch.cuda.synchronize()
+    for r in raw:
+        L.stream_destroy(r)
+
+
+@pytest.mark.parametrize("case", ["reduced", "fetch_all", "full_size"])
+def test_lookahead_with_the_copy_on_its_own_cus(case, cu_streams):
+    """[OASIS] Fig. 8 placement: each select's blocks are copied on a copy
+    stream with CUs of its own while the next step appends, scores the drafts
+    and attends to the held blocks on the compute stream (sized for the
+    remaining CUs); the fetched blocks are attended once the copy lands.
+    fetch_all: the budget and cap cover every block, so an append writes its
+    token into a block whose copy is still running.  Checked against the
+    oracle as the one-stream lookahead run is, slot payloads included."""
+    from tests.gpu_parity import AheadRunning, log
+    cus, comp, copy = cu_streams
+    if case == "reduced":
+        w = synth.QWEN3_8B_AHEAD.with_(batch=2, prefix_tokens=16 * 300 + 7,
+                                       budget_tokens=16 * 64)
+        p, every = AheadRunning(w, 10, [(0, 0), (1, 7), (0, 4)], compute_units=cus), 2
+    elif case == "fetch_all":
+        w = synth.QWEN3_8B_AHEAD.with_(batch=2, prefix_tokens=16 * 40 + 5,
+                                       budget_tokens=16 * 48, cap=48)
+        p, every = AheadRunning(w, 16, [(0, 0), (1, 7), (0, 4)], compute_units=cus), 1
+    else:
+        w = synth.QWEN3_8B_AHEAD
+        p, every = AheadRunning(w, 12, [(0, 0), (17, 5), (31, 7)], compute_units=cus), 6
+    rep = p.run_ahead(check_payload_every=every, beside=(comp, copy))
+    log(f"lookahead, copy on {torch.cuda.get_device_properties(0).multi_processor_count - cus}"
+        f" CUs of its own ({case}): {rep}")
+    assert rep["fetched"] > 0
+
+
+def test_lookahead_copy_beside_matches_one_stream(cu_streams):
+    """The same lookahead run on one stream and with the copy on its own CUs:
+    ids, tables and slot payloads bit-identical every step; outputs equal up
+    to the order of the sums (the attention runs as two launches)."""
+    from lookahead_sparse_kv_oasis_amd.runner import LayerRunner
+    cus, comp, copy = cu_streams
+    w = synth.QWEN3_8B_AHEAD.with_(batch=4, prefix_tokens=16 * 500 + 3, budget_tokens=16 * 64)
+    a = LayerRunner(w, 12)
+    b = LayerRunner(w, 12, compute_units=cus)
+    torch.cuda.synchronize()  # inputs were made on torch's stream
+    a.admission_ahead()
+    b.admission_beside(comp, copy)
+    worst = 0.0
+    for t in range(1, 13):
+        a.step_ahead(t)
+        b.step_beside(t, comp, copy)
+        torch.cuda.synchronize()
+        for name in ("IDS", "SLOT_BLOCK", "LAST_USED", "ATT_BLOCK", "COUNTS", "FETCH_BLOCK"):
+            assert np.array_equal(a.h.read(name), b.h.read(name)), f"step {t}: {name}"
+        oa, ob = a.out.cpu().numpy(), b.out.cpu().numpy()
+        worst = max(worst, float(np.max(np.abs(oa - ob))))
+        assert worst <= 1e-5, f"step {t}: outputs differ by {worst:.3g}"
+    # every slot's rows of tokens < T
+    T, bs, S, d = a.h.oasis_tokens(), w.block_size, a.h.slots, w.head_dim
+    sa = a.h.read("SLOTS", np.uint16).reshape(-1, S, 2, bs, d)
+    sb = b.h.read("SLOTS", np.uint16).reshape(-1, S, 2, bs, d)
+    blk = a.h.read("SLOT_BLOCK").reshape(-1, S)
+    for u in range(sa.shape[0]):
+        for s_ in range(S):
+            if blk[u, s_] >= 0:
+                n = max(0, min(bs, T - blk[u, s_] * bs))
+                assert np.array_equal(sa[u, s_, :, :n], sb[u, s_, :, :n]), (u, s_)
+    from tests.gpu_parity import log
+    log(f"lookahead one stream vs copy beside: outputs within {worst:.3g}")
+
+
 def test_lookahead_recall_measurement():
     """Recall of the drafts' prediction and of the previous query's top-K
     against the exact top-K of the step's own query; the exact ids are checked
