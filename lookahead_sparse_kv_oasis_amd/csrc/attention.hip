@@ -173,17 +173,12 @@ template <int G> struct AttnWave {
 #pragma unroll
         for (int r = 0; r < 4; ++r) vv[r] = gload16_nt(p + voff + r * D);
     }
-    // Into a slot, the rows of the `valid` tokens only (K row col, V rows
-    // 4 kg + r of this lane): rows past them are left as they are.
-    __device__ __forceinline__ void store(uint16_t *p, const uint4 (&kk)[4], const uint4 (&vv)[4],
-                                          int valid) const {
-        if (col < valid) {
+    __device__ __forceinline__ void store(uint16_t *p, const uint4 (&kk)[4],
+                                          const uint4 (&vv)[4]) const {
 #pragma unroll
-            for (int c = 0; c < 4; ++c) gstore16(p + koff + 32 * c, kk[c]);
-        }
+        for (int c = 0; c < 4; ++c) gstore16(p + koff + 32 * c, kk[c]);
 #pragma unroll
-        for (int r = 0; r < 4; ++r)
-            if (4 * kg + r < valid) gstore16(p + voff + r * D, vv[r]);
+        for (int r = 0; r < 4; ++r) gstore16(p + voff + r * D, vv[r]);
     }
     // Online-softmax update with one block of `valid` tokens.
     __device__ __forceinline__ void block(const uint4 (&kk)[4], const uint4 (&vv)[4], int valid,
@@ -344,17 +339,12 @@ template <int G> struct AttnWaveM {
 #pragma unroll
         for (int r = 0; r < 4; ++r) vv[r] = gload16_nt(p + voff + r * D);
     }
-    // Into a slot, the rows of the `valid` tokens only (K row col, V rows
-    // 4 kg + r of this lane): rows past them are left as they are.
-    __device__ __forceinline__ void store(uint16_t *p, const uint4 (&kk)[4], const uint4 (&vv)[4],
-                                          int valid) const {
-        if (col < valid) {
+    __device__ __forceinline__ void store(uint16_t *p, const uint4 (&kk)[4],
+                                          const uint4 (&vv)[4]) const {
 #pragma unroll
-            for (int c = 0; c < 4; ++c) gstore16(p + koff + 32 * c, kk[c]);
-        }
+        for (int c = 0; c < 4; ++c) gstore16(p + koff + 32 * c, kk[c]);
 #pragma unroll
-        for (int r = 0; r < 4; ++r)
-            if (4 * kg + r < valid) gstore16(p + voff + r * D, vv[r]);
+        for (int r = 0; r < 4; ++r) gstore16(p + voff + r * D, vv[r]);
     }
     __device__ __forceinline__ void block(const uint4 (&kk)[4], const uint4 (&vv)[4], int valid,
                                           float scale_log2) {
@@ -479,14 +469,14 @@ __device__ __forceinline__ int block_valid(int64_t T, int32_t blk) {
 // on the host link here: the extra registers cost the resident waves of the
 // same launch one wave per SIMD.  A few such waves keep the host link
 // saturated while holding only a small share of the CU slots.
-template <int G, typename W>
+template <int G, bool FromSlots = false, typename W>
 __device__ __forceinline__ void fetch_waves(
     W &st, int wave, const QRows &qr, uint16_t *__restrict__ slots,
     const uint16_t *__restrict__ host_kv, const int32_t *__restrict__ att_block,
     const int32_t *__restrict__ att_slot, const int32_t *__restrict__ counts, int64_t T_, int Hq,
     int Hkv, int K, int S, int64_t NBmax, int cap, int n_fetch_wg, int nsa, int64_t units,
     float scale_log2, float *__restrict__ part_m, float *__restrict__ part_l,
-    float *__restrict__ part_acc, bool from_slots = false) {
+    float *__restrict__ part_acc) {
     const int lane = threadIdx.x & 63;
     const int64_t F = 4LL * n_fetch_wg;
     const int64_t n_items = units * cap;
@@ -517,10 +507,14 @@ __device__ __forceinline__ void fetch_waves(
         }
         const uint64_t mask = __ballot(ok);
         if (mask == 0) continue;
-        auto src = [&](int l) {
+        // (a compile-time choice: with the slots a possible source, the host
+        // reads could no longer be scheduled across the slot stores)
+        auto src = [&](int l) -> const uint16_t * {
             const int ul = rl(u, l);
-            return from_slots ? slots + ((int64_t)ul * S + rl(slot, l)) * (int64_t)W::BLK
-                              : host_kv + ((int64_t)ul * NBmax + rl(blk, l)) * W::BLK;
+            if constexpr (FromSlots)
+                return slots + ((int64_t)ul * S + rl(slot, l)) * (int64_t)W::BLK;
+            else
+                return host_kv + ((int64_t)ul * NBmax + rl(blk, l)) * W::BLK;
         };
         // lane l's item: read it from the host, store it into its slot,
         // attend, write partial i of its unit (from_slots: the block is in
@@ -532,11 +526,12 @@ __device__ __forceinline__ void fetch_waves(
             st.load_q(st.qb, qr, ul / Hkv, ul % Hkv);
             st.load(kk, vv, src(l));
             st.reset();
-            const int valid = block_valid(T_, rl(blk, l));
-            st.block(kk, vv, valid, scale_log2);
-            if (!from_slots)
-                st.store(slots + ((int64_t)ul * S + rl(slot, l)) * (int64_t)W::BLK, kk, vv,
-                         valid);
+            st.block(kk, vv, block_valid(T_, rl(blk, l)), scale_log2);
+            // the whole host block (rows past T hold the host KV's zeros);
+            // storing only the held rows cost this kernel 3% (78 -> 81 us
+            // on the Qwen3-8B layer)
+            if constexpr (!FromSlots)
+                st.store(slots + ((int64_t)ul * S + rl(slot, l)) * (int64_t)W::BLK, kk, vv);
             st.reduce();
             st.write_partial(((int64_t)ul * nsa + rl(i, l)) * G, part_m, part_l, part_acc);
         }
@@ -694,9 +689,9 @@ __device__ __forceinline__ void hit_prefix(const int32_t *__restrict__ counts, i
 // combine reads a fixed set of rows with no dependent load.  Modes: 0, the
 // hit waves over every attended entry; 1, fetch workgroups first in the grid
 // (host reads, as in the split kernel), hit waves over the entries before
-// the fetched ones; 2, those hit waves alone; 3, fetch workgroups alone,
-// reading the fetched blocks from their slots (a gather on another stream
-// copied them while a mode-2 launch ran).  Dynamic LDS: units + 1 ints.
+// the fetched ones; 2, those hit waves alone (attn_fetched_kernel below then
+// attends to the fetched blocks from their slots).  Dynamic LDS: units + 1
+// ints.
 template <int G>
 __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2))) void attn_flat_kernel(
     const QRows qr, uint16_t *__restrict__ slots, const uint16_t *__restrict__ host_kv, const int32_t *__restrict__ att_block,
@@ -717,7 +712,7 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2))) void a
     if ((int)blockIdx.x < n_fetch_wg) {
         fetch_waves<G>(st, wave, qr, slots, host_kv, att_block, att_slot, counts, T_, Hq, Hkv, K,
                        S, NBmax, cap, n_fetch_wg, nsa, (int64_t)units, scale_log2, part_m,
-                       part_l, part_acc, mode == 3);
+                       part_l, part_acc);
         return;
     }
     hit_prefix(counts, units, mode, pre, red);
@@ -811,6 +806,29 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2))) void a
         }
     }
     finish(cur_u);
+}
+
+// The fetched entries of a mode-2 launch, from their slots once a gather on
+// another stream has copied them: the fetch waves' item loop (one wave per
+// item, partial i of the unit as mode 1 writes it) with the slots as the
+// source and no store.  A kernel of its own, so that the host-reading fetch
+// waves keep their code and schedule.
+template <int G>
+__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2))) void attn_fetched_kernel(
+    const QRows qr, uint16_t *__restrict__ slots, const int32_t *__restrict__ att_block,
+    const int32_t *__restrict__ att_slot, const int32_t *__restrict__ counts, int64_t T_, int Hq,
+    int Hkv, int K, int S, int cap, int nsa, int units, float scale_log2,
+    float *__restrict__ part_m, float *__restrict__ part_l, float *__restrict__ part_acc) {
+    using Wv = std::conditional_t<(G >= 16), AttnWaveM<G>, AttnWave<G>>;
+    __shared__ __attribute__((aligned(16))) uint16_t vstage[4][Wv::kStage];
+    const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+    Wv st;
+    st.lanes();
+    st.vst = vstage[wave];
+    st.nreal = qr.real;
+    fetch_waves<G, true>(st, wave, qr, slots, nullptr, att_block, att_slot, counts, T_, Hq, Hkv,
+                         K, S, 0, cap, (int)gridDim.x, nsa, (int64_t)units, scale_log2, part_m,
+                         part_l, part_acc);
 }
 
 // ---------------------------------------------------------------- combine
@@ -1075,15 +1093,31 @@ hipError_t launch_attention(const Dims &D, const AttnPlan &P, int mode, int nsf,
                             const QRows *qrows) {
     const float sc = kLog2e / sqrtf((float)D.d);
     const QRows qq = qrows ? *qrows : QRows{(const uint16_t *)q, nullptr, 0, D.Hq, D.G, 0, D.G};
+    if (P.mfma && P.flat && mode == 3) {
+        // the fetched blocks from HBM: a wave per block, up to 8 per CU
+        if (nsf <= 0) return hipSuccess;
+        const int64_t waves = std::min<int64_t>(D.units() * nsf, 8LL * compute_units(D));
+        const dim3 grid((unsigned)((waves + 3) / 4));
+        uint16_t *sl = (uint16_t *)slots;
+#define OASIS_FETCHED(GG)                                                                        \
+    OASIS_LAUNCH((attn_fetched_kernel<GG>), grid, dim3(256), 0, st, qq, sl, att_block, att_slot, \
+                 counts, T, D.Hq, D.Hkv, D.K, D.S, nsf, P.nsa, (int)D.units(), sc, part_m,       \
+                 part_l, part_acc)
+        switch (flat_rows_of_call(D, P, nsf)) {
+        case 1: OASIS_FETCHED(1); break;
+        case 2: OASIS_FETCHED(2); break;
+        case 4: OASIS_FETCHED(4); break;
+        case 8: OASIS_FETCHED(8); break;
+        case 16: OASIS_FETCHED(16); break;
+        default: OASIS_FETCHED(32); break;
+        }
+#undef OASIS_FETCHED
+        return hipGetLastError();
+    }
     if (P.mfma && P.flat) {
         if (mode == 0) nsf = 0;
         int n_fetch_wg = 0, hw = 0;
-        if (mode == 3) {
-            // the fetched blocks from HBM: a wave per block, up to 8 per CU
-            if (nsf <= 0) return hipSuccess;
-            const int64_t waves = std::min<int64_t>(D.units() * nsf, 8LL * compute_units(D));
-            n_fetch_wg = (int)((waves + 3) / 4);
-        } else if (mode == 2) {
+        if (mode == 2) {
             hw = P.flat_waves;
         } else {
             n_fetch_wg = nsf > 0 ? fetch_workgroups(D.units() * nsf) : 0;

@@ -89,6 +89,24 @@ def slot_payload_expected(keys, vals, blk, T, bs, dtype):
     return np.stack([keys[p0:p0 + n], vals[p0:p0 + n]]).astype(dt, copy=False)
 
 
+def assert_held_rows_equal(ha, hb, what=""):
+    """Two handles hold the same blocks in the same slots, with the same bytes
+    in the rows of the tokens held (rows past T are never read: the fetch
+    inside the attention copies whole host blocks, the gather kernel the
+    held rows only)."""
+    assert np.array_equal(ha.read("SLOT_BLOCK"), hb.read("SLOT_BLOCK")), what + " slot tables"
+    T, S, bs = ha.oasis_tokens(), ha.slots, ha.block_size
+    assert T == hb.oasis_tokens()
+    blk = ha.read("SLOT_BLOCK").reshape(-1, S)
+    sa = ha.read("SLOTS", np.uint8).reshape(blk.shape[0], S, 2, bs, -1)
+    sb = hb.read("SLOTS", np.uint8).reshape(blk.shape[0], S, 2, bs, -1)
+    rows = np.clip(T - blk.astype(np.int64) * bs, 0, bs)  # held rows per slot
+    keep = np.arange(bs)[None, None, :] < rows[:, :, None]  # [units][S][bs]
+    keep &= (blk >= 0)[:, :, None]
+    m = np.broadcast_to(keep[:, :, None, :, None], sa.shape)
+    assert np.array_equal(sa[m], sb[m]), what + " slot payloads"
+
+
 class Parity:
     """GPU runner + oracle units for a sample of (b, h) units of a workload."""
 
