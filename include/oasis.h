@@ -477,7 +477,9 @@ hipStream_t oasis_copy_stream(const oasis_t *h);
  * return at the pace of its slowest outstanding load, so HBM reads on a CU
  * that also runs host reads wait for the host link's round trip.  Giving the
  * copy stream a few CUs of its own and the compute streams the rest keeps
- * both at full rate.  OASIS_E_INVAL when the range is empty or past the
+ * both at full rate.  Like a stream from hipStreamCreate it synchronizes
+ * with the null stream, so the other streams of such a schedule should be
+ * created streams too.  OASIS_E_INVAL when the range is empty or past the
  * device's CUs, OASIS_E_HIP when the runtime refuses.  Release with
  * oasis_stream_destroy. */
 int oasis_stream_create_cus(int32_t first_cu, int32_t n_cus, hipStream_t *out);
