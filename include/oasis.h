@@ -181,14 +181,15 @@ int oasis_topk_from_scores(oasis_t *h, const float *scores_dev, int32_t *block_i
  * fetched blocks there right after the table update (it waits for `stream`),
  * and the next call that reads the slots (attention, select, evict, verify)
  * waits for it; the copy takes the rows of the tokens held now, so an append
- * (which writes the next token's row) runs beside it.  OASIS_COPY_DEFAULT: the handle's own placement, by default
- * inside the next oasis_sparse_attn's kernel (bf16, d = 128, block 16:
+ * (which writes the next token's row) runs beside it.  OASIS_COPY_DEFAULT:
+ * the handle's own placement, by default inside the next oasis_sparse_attn's
+ * kernel (bf16, d = 128, block 16:
  * fetch waves read the host blocks while the other workgroups attend to the
  * hits, which measured faster than a separate copy the attention waits for),
  * else the handle's copy stream.  A copy left for the attention is made
  * earlier by any call that needs the slots first (evict, select, reading
  * SLOTS, verify); an append in between leaves it pending, and the copy then
- * takes the whole host block, appended token included. */
+ * takes the host block with the appended token. */
 int oasis_select_and_fetch(oasis_t *h, int32_t cap, hipStream_t stream, hipStream_t copy);
 
 /* Force blocks out of HBM (synchronous on `stream`): blocks_host
@@ -312,8 +313,9 @@ int oasis_decode_layers(oasis_t *const *layers, const oasis_layer_io *io, int32_
  * with io[l].q over the set the previous call selected; then on `side`,
  * predict from io[l].drafts alone (n_drafts >= 1) and select_and_fetch(cap);
  * the selected misses are copied host -> HBM on `xfer`.  The next call's
- * append and attention of that layer wait for the copy; the call itself does
- * not: `stream` does not wait for `side` or `xfer`, so transfers run under
+ * attention and select of that layer wait for the copy (its append runs
+ * beside it); the call itself does not: `stream` does not wait for `side`
+ * or `xfer`, so transfers run under
  * the attention of the following layers.  Synchronize all three streams (or
  * the device) before reusing the call's inputs.  Call it with every q = NULL
  * and cap = K for the admission step (predict and fetch only).
