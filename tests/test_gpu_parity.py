@@ -299,6 +299,21 @@ def test_lookahead_with_the_copy_on_its_own_cus(case, cu_streams):
     assert rep["fetched"] > 0
 
 
+@pytest.mark.parametrize("q_heads", [8, 64, 128])
+def test_lookahead_with_the_copy_on_its_own_cus_other_group_sizes(q_heads, cu_streams):
+    """The copy-beside lookahead for 1, 8 and 16 query heads per KV head (the
+    held-block and fetched-block launches and the combine on the G-row
+    partials of each), against the oracle with slot payloads."""
+    from tests.gpu_parity import AheadRunning, log
+    cus, comp, copy = cu_streams
+    w = synth.QWEN3_8B_AHEAD.with_(batch=2, q_heads=q_heads, prefix_tokens=16 * 200 + 11,
+                                   budget_tokens=16 * 32, cap=4)
+    p = AheadRunning(w, 6, [(0, 0), (1, 7), (0, 5)], compute_units=cus)
+    rep = p.run_ahead(check_payload_every=2, beside=(comp, copy))
+    log(f"lookahead, copy beside, G = {q_heads // 8}: {rep}")
+    assert rep["fetched"] > 0
+
+
 def test_lookahead_copy_beside_matches_one_stream(cu_streams):
     """The same lookahead run on one stream and with the copy on its own CUs:
     ids, tables and slot payloads bit-identical every step; outputs equal up
