@@ -21,10 +21,11 @@ def _gpu():
 
 
 def _handle(batch=1, hq=2, hkv=1, d=64, dtype=0, drafts=0, max_tokens=1024, bs=16, budget=128,
-            ratio=0.02, slots=0):
+            ratio=0.02, slots=0, compute_units=0):
     from lookahead_sparse_kv_oasis_amd import Oasis
     return Oasis(batch, hq, hkv, d, dtype, drafts, max_tokens, block_size=bs,
-                 budget_tokens=budget, fetch_ratio=ratio, slots_per_head=slots)
+                 budget_tokens=budget, fetch_ratio=ratio, slots_per_head=slots,
+                 compute_units=compute_units)
 
 
 def _zeros_prefix(h, T, d, batch=1, hkv=1, dtype=np.float32):
@@ -146,6 +147,38 @@ def test_error_paths():
     torch.cuda.synchronize()
     assert torch.all(out == 0)
     h.oasis_check()
+
+
+def test_cu_partition_arguments():
+    """oasis_stream_create_cus rejects empty ranges and ranges past the
+    device's CUs; a handle's compute_units must be 0 or a CU count of the
+    device; a valid partition stream runs the handle's work."""
+    import lookahead_sparse_kv_oasis_amd as L
+    ncu = torch.cuda.get_device_properties(0).multi_processor_count
+    for first, n in [(0, 0), (-1, 4), (ncu - 8, 16), (0, ncu + 1)]:
+        with pytest.raises(L.OasisError) as e:
+            L.stream_create_cus(first, n)
+        assert e.value.status == L.OASIS_E_INVAL, (first, n)
+    for cus in [-1, ncu + 1]:
+        with pytest.raises(L.OasisError) as e:
+            _handle(max_tokens=33, drafts=1, compute_units=cus)
+        assert e.value.status == L.OASIS_E_INVAL, cus
+    s = L.stream_create_cus(8, ncu - 8)
+    try:
+        h = _handle(max_tokens=33, drafts=1, compute_units=ncu - 8)
+        _zeros_prefix(h, 32, 64)
+        q = torch.zeros((1, 2, 64), dtype=torch.float32, device="cuda")
+        out = torch.full((1, 2, 64), float("nan"), dtype=torch.float32, device="cuda")
+        torch.cuda.synchronize()
+        h.oasis_predict(q, None, 0, stream=s)
+        h.oasis_select_and_fetch(2, stream=s)
+        h.oasis_sparse_attn(q, out, stream=s)
+        torch.cuda.synchronize()
+        assert torch.all(out == 0)   # zero keys and values
+        h.oasis_check()
+    finally:
+        torch.cuda.synchronize()
+        L.stream_destroy(s)
 
 
 @pytest.mark.parametrize("hq", [32, 64, 128])
