@@ -316,6 +316,8 @@ def main():
 # CU partition of the run (--copy-cus): compute units of the compute streams
 # and the streams themselves
 _PART = {}
+# side and transfer streams of the multi-layer executors
+_MODEL_STREAMS = {}
 
 
 def _partition(n_copy):
@@ -354,7 +356,8 @@ def _run(args):
         shared = dict(h2d=line["host_link"]["pinned_h2d_peak_gbps"],
                       read_peak=(line["hbm_read_peak"] or {}).get("gbps"))
         import gc
-        for name in ("llama31_8b_layer_b8_t128k_bf16", "qwen3_32b_layer_b16_t32k_bf16"):
+        for name in ("llama31_8b_layer_b8_t128k_bf16", "qwen3_32b_layer_b16_t32k_bf16",
+                     "qwen3_8b_layer_b32_t32k_bf16_lookahead"):
             print(f"# extra workload {name}", file=sys.stderr, flush=True)
             sub = bench_layer(args, _workloads()[name], args.extra_steps, 2, main_leg=False,
                               shared=shared)
@@ -364,17 +367,24 @@ def _run(args):
             line["workloads"][name] = sub
             gc.collect()
             torch.cuda.empty_cache()
-        m = _workloads()["qwen3_8b_36layer_b64_t64k_bf16"]
-        print(f"# extra workload {m.name}", file=sys.stderr, flush=True)
-        margs = argparse.Namespace(**vars(args))
-        margs.steps, margs.warmup, margs.sweep, margs.fetch_ratio = 3, 1, False, None
-        margs.no_cpu_baseline, margs.no_h2d_peak, margs.no_read_peak = True, True, True
-        margs.schedule = "overlap"
-        sub = bench_model(margs, m)[0]
-        for k in ("metric", "n_gpus", "higher_is_better", "scaling", "vs_baseline", "data",
-                  "cpu_baseline"):
-            sub.pop(k, None)
-        line["workloads"][m.name] = sub
+        # the 36-layer model within the step (the layer overlap), then in the
+        # lookahead order with score, top-K and select fused (its fastest form)
+        for mname, fuse in (("qwen3_8b_36layer_b64_t64k_bf16", False),
+                            ("qwen3_8b_36layer_b64_t64k_bf16_lookahead", True)):
+            m = _workloads()[mname]
+            print(f"# extra workload {m.name}", file=sys.stderr, flush=True)
+            margs = argparse.Namespace(**vars(args))
+            margs.steps, margs.warmup, margs.sweep, margs.fetch_ratio = 3, 1, False, None
+            margs.no_cpu_baseline, margs.no_h2d_peak, margs.no_read_peak = True, True, True
+            margs.schedule = "overlap"
+            margs.fuse_score_topk = fuse
+            sub = bench_model(margs, m)[0]
+            for k in ("metric", "n_gpus", "higher_is_better", "scaling", "vs_baseline", "data",
+                      "cpu_baseline"):
+                sub.pop(k, None)
+            line["workloads"][m.name] = sub
+            gc.collect()
+            torch.cuda.empty_cache()
     if not args.no_cpu_baseline:
         print("# cpu baseline (oracle) ...", file=sys.stderr, flush=True)
         line["cpu_baseline"] = cpu_baseline(w, bytes_per_step=line["_bytes_per_step"])
@@ -783,8 +793,16 @@ def bench_model(args, w):
         ratios = [w.fetch_ratio]
     schedules = ["overlap", "serial"] if args.schedule == "both" else [args.schedule]
     stream = torch.cuda.current_stream()
-    side = _PART.get("side") or torch.cuda.Stream()
-    xfer = _PART.get("copy") or torch.cuda.Stream()
+    side, xfer = _PART.get("side"), _PART.get("copy")
+    if side is None:
+        # made once per process: the runtime spreads streams over a few
+        # hardware queues (4 here) in creation order, and a later pair of
+        # pool streams can land on the queue of the caller's stream, which
+        # then serializes the overlap (17.2 against 10.9 ms per 36-layer
+        # lookahead step when a second model ran with new streams)
+        if "side" not in _MODEL_STREAMS:
+            _MODEL_STREAMS.update(side=torch.cuda.Stream(), xfer=torch.cuda.Stream())
+        side, xfer = _MODEL_STREAMS["side"], _MODEL_STREAMS["xfer"]
     h2d = None if args.no_h2d_peak else pinned_h2d_peak_gbps()
     rpk = None if args.no_read_peak else hbm_read_peak()
     cpu = None if args.no_cpu_baseline else cpu_baseline(w.with_(layers=1))
@@ -883,6 +901,7 @@ def bench_model(args, w):
                        "cap_per_kv_head": cap, "schedule": main_sched,
                        "ordering": "lookahead" if w.lookahead else "within step",
                        "correct_cap": args.correct_cap if w.lookahead else None,
+                       "fuse_score_topk": bool(args.fuse_score_topk),
                        "host_kv_buffers": mr.H,
                        **({"copy_cus": _PART["copy_cus"]} if _PART else {})},
             "model_steps_per_s": K / dt,

@@ -315,8 +315,10 @@ int oasis_decode_layers(oasis_t *const *layers, const oasis_layer_io *io, int32_
  * the selected misses are copied host -> HBM on `xfer`.  The next call's
  * attention and select of that layer wait for the copy (its append runs
  * beside it); the call itself does not: `stream` does not wait for `side`
- * or `xfer`, so transfers run under
- * the attention of the following layers.  Synchronize all three streams (or
+ * or `xfer`, so transfers run under the attention of the following layers
+ * (provided the three streams sit on different hardware queues: the HIP
+ * runtime spreads a process's streams over a few queues in creation order,
+ * and streams sharing one run in order).  Synchronize all three streams (or
  * the device) before reusing the call's inputs.  Call it with every q = NULL
  * and cap = K for the admission step (predict and fetch only).
  * cap_correct > 0 adds decode-time miss correction (the corrective transfers
