@@ -18,10 +18,11 @@
 // append does not: the gather copies the rows of the tokens held at its
 // select, the append writes the next one); attention, append and evict wait
 // for the select; attention and select wait for the last append; attention
-// waits for the previous attention.  A select, an append or a new predict also waits for score /
-// top-K kernels that a predict queued on another stream.  A wait is issued only when the
-// producing call ran on another stream (one stream is in order by itself).
-// No call synchronises the host except the inspection calls.
+// waits for the previous attention.  A select, an append or a new predict
+// also waits for score / top-K kernels that a predict queued on another
+// stream.  A wait is issued only when the producing call ran on another
+// stream (one stream is in order by itself).  No call synchronises the host
+// except the inspection calls.
 #include <stdarg.h>
 #include <stdio.h>
 #include <string.h>
