@@ -271,7 +271,7 @@ def cu_streams():
         L.stream_destroy(r)
 
 
-@pytest.mark.parametrize("case", ["reduced", "fetch_all", "full_size"])
+@pytest.mark.parametrize("case", ["reduced", "fetch_all", "full_size", "full_size_fused"])
 def test_lookahead_with_the_copy_on_its_own_cus(case, cu_streams):
     """[OASIS] Fig. 8 placement: each select's blocks are copied on a copy
     stream with CUs of its own while the next step appends, scores the drafts
@@ -279,7 +279,9 @@ def test_lookahead_with_the_copy_on_its_own_cus(case, cu_streams):
     remaining CUs); the fetched blocks are attended once the copy lands.
     fetch_all: the budget and cap cover every block, so an append writes its
     token into a block whose copy is still running.  Checked against the
-    oracle as the one-stream lookahead run is, slot payloads included."""
+    oracle as the one-stream lookahead run is, slot payloads included (at full
+    size also with score, top-K and select fused: 256 units fill the 240 CUs'
+    one-workgroup-per-unit kernel)."""
     from tests.gpu_parity import AheadRunning, log
     cus, comp, copy = cu_streams
     if case == "reduced":
@@ -293,6 +295,8 @@ def test_lookahead_with_the_copy_on_its_own_cus(case, cu_streams):
     else:
         w = synth.QWEN3_8B_AHEAD
         p, every = AheadRunning(w, 12, [(0, 0), (17, 5), (31, 7)], compute_units=cus), 6
+        if case == "full_size_fused":   # score, top-K and select in one kernel
+            p.run.h.oasis_set_score_topk_fusion(True)
     rep = p.run_ahead(check_payload_every=every, beside=(comp, copy))
     log(f"lookahead, copy on {torch.cuda.get_device_properties(0).multi_processor_count - cus}"
         f" CUs of its own ({case}): {rep}")
